@@ -1,0 +1,200 @@
+/*
+ * octopus.h -- C ABI of the OCTOPUS KV-cache codec and the attention kernels
+ * that read it (gfx950 / MI355X).
+ *
+ * The method is the one of "OCTOPUS: Optimized KV Cache for Transformers via
+ * Octahedral Parametrization Under optimal Squared error quantization"
+ * (arXiv 2605.21226).  A key (or value) k in R^d is stored as the compressed
+ * state S(k) = (gamma, I_dir, I_nrm) of its Sec. 3: the norm gamma, a packed
+ * stream of octahedral-coordinate indices and a packed stream of triplet-norm
+ * indices, optionally plus the 1-bit QJL residual (sigma, gamma_r) of Sec. 3.6.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronizes inside these calls and keeps no
+ *     mutable global state; calls are asynchronous on `stream` and re-entrant.
+ *   - Every argument that can be checked on the host is checked before any
+ *     launch; on failure nothing is launched and a status other than OCTO_OK is
+ *     returned.  octo_last_error() then returns a thread-local message.
+ *     No exception crosses this boundary.
+ *   - Device-resident lengths (seq_lens) cannot be checked on the host; the
+ *     kernels clamp them to [0, min(max_seq_len, capacity)].
+ *   - Outputs are bitwise deterministic for identical inputs (no atomics in any
+ *     reduction; the split-K merge order is fixed).
+ *   - Supported now: head_dim = 128; (b_dir, b_nrm) in {(3,1), (4,2), (5,3)}
+ *     (the paper's (b+1, b-1) split for b = 2, 3, 4; Sec. 3.3) and the uniform
+ *     splits {(2,2), (3,3), (4,4)}; query heads per KV head in {1, 2, 4, 7, 8};
+ *     QJL on keys only.  Anything else returns OCTO_ERR_UNSUPPORTED.
+ *
+ * Cache layout (OCTO_LAYOUT_TILE64).  The paper fixes no bit layout; this one
+ * is this library's.  A stream is a little-endian LSB-first bit string: field
+ * j of width w occupies bits [j*w, (j+1)*w).  I_dir holds 2*n_tri fields of
+ * b_dir bits ordered xi_0, eta_0, xi_1, eta_1, ...; I_nrm holds n_tri fields of
+ * b_nrm bits; the QJL stream holds d one-bit fields (1 where sigma_j = -1).
+ * Each stream is zero-padded to whole 32-bit words (W words per token).  In a
+ * (batch b, kv head h) plane of `capacity` tokens (a multiple of 64), word w
+ * of token t is stored at word index
+ *     ((b*kv_heads + h)*(capacity/64) + t/64)*W*64 + w*64 + t%64,
+ * i.e. each 64-token tile keeps its W words as W rows of 64 consecutive words,
+ * so that one wavefront reading word w of 64 tokens reads 256 contiguous bytes.
+ * gamma (fp32) and gamma_r (fp16 bit pattern) are plain [B][H][capacity].
+ */
+#ifndef OCTOPUS_H
+#define OCTOPUS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OCTO_ABI_VERSION 1u
+
+typedef enum {
+  OCTO_OK = 0,
+  OCTO_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad enum   */
+  OCTO_ERR_UNSUPPORTED = 2,        /* valid but not implemented (d, bits, G)  */
+  OCTO_ERR_ALIGNMENT = 3,          /* pointer or stride not suitably aligned  */
+  OCTO_ERR_CAPACITY = 4,           /* token range beyond the cache capacity   */
+  OCTO_ERR_WORKSPACE_TOO_SMALL = 5,
+  OCTO_ERR_VERSION = 6,            /* descriptor built for another ABI        */
+  OCTO_ERR_HIP = 7                 /* a HIP launch reported an error          */
+} octo_status;
+
+typedef enum { OCTO_DTYPE_F32 = 0, OCTO_DTYPE_BF16 = 1 } octo_dtype;
+
+/* Encoder rounding (OCTOPUS paper Sec. 3.5; App. A/E summaries).
+ * LOCAL3X3: the 3x3 joint rounding around the scalar Lloyd seed (default).
+ * SCALAR:   Delta = {(0,0)}: independent nearest-centroid xi, eta and rho.   */
+typedef enum { OCTO_ROUND_LOCAL3X3 = 0, OCTO_ROUND_SCALAR = 1 } octo_rounding;
+
+typedef enum { OCTO_LAYOUT_TILE64 = 0 } octo_layout;
+
+/* One codec (one for K, one for V).  Sec. 3.3-3.4: the triplet budget is
+ * B_tri = 2*b_dir + b_nrm; codebooks depend only on (d, b_dir, b_nrm).
+ * The rotation R = H diag(s) (Sec. 3.1, App. C.2) takes its signs s_j,
+ * j < d, from the j-th output of SplitMix64 seeded with `seed` (bit 63 set ->
+ * -1); the QJL rotation R' uses outputs d..2d-1.                             */
+typedef struct {
+  uint32_t abi_version;   /* must be OCTO_ABI_VERSION                          */
+  int32_t head_dim;       /* d (power of two; 128 supported)                   */
+  int32_t bits;           /* b; with b_dir = b_nrm = 0 selects (b+1, b-1)      */
+  int32_t b_dir;          /* explicit bits per octahedral coordinate, or 0     */
+  int32_t b_nrm;          /* explicit bits per triplet norm, or 0              */
+  int32_t rounding;       /* octo_rounding                                     */
+  int32_t qjl;            /* 1: keys carry the QJL sign sketch (Sec. 3.6)      */
+  int32_t reserved;
+  uint64_t seed;          /* rotation seed                                     */
+  const float* c_xi;      /* device, 2^b_dir fp32 centroids, ascending         */
+  const float* c_rho;     /* device, 2^b_nrm fp32 centroids, ascending         */
+} octo_codec_desc;
+
+/* A packed cache for one tensor (K or V), layout OCTO_LAYOUT_TILE64.        */
+typedef struct {
+  uint32_t* dir;          /* B*H*capacity*W_dir words                          */
+  uint32_t* nrm;          /* B*H*capacity*W_nrm words (may be NULL if W_nrm=0) */
+  float* gamma;           /* B*H*capacity                                      */
+  uint32_t* qjl;          /* B*H*capacity*W_qjl words, NULL unless codec.qjl   */
+  uint16_t* gamma_r;      /* B*H*capacity fp16 bits, NULL unless codec.qjl     */
+  int32_t batch;          /* B                                                 */
+  int32_t kv_heads;       /* H                                                 */
+  int32_t capacity;       /* tokens per (b, h) plane, multiple of 64           */
+  int32_t layout;         /* octo_layout                                       */
+} octo_cache_view;
+
+/* 32-bit words per token of each stream for a codec.                        */
+typedef struct {
+  int32_t dir_words;
+  int32_t nrm_words;
+  int32_t qjl_words;
+  int32_t n_triplets;     /* ceil(d / 3)                                       */
+  int32_t b_dir;          /* the resolved split                                */
+  int32_t b_nrm;
+} octo_stream_sizes;
+
+uint32_t octo_abi_version(void);
+const char* octo_status_string(octo_status s);
+/* Message of the last failing call on this thread ("" if none).             */
+const char* octo_last_error(void);
+
+/* Resolves the bit split and fills `out`.  Host only.                        */
+octo_status octo_record_sizes(const octo_codec_desc* codec, octo_stream_sizes* out);
+
+/* octo_encode -- OCTOPUS encoder (paper Sec. 3.1-3.6; App. A summary).
+ * For every b < B, h < H, t < T encodes x[b,h,t,:] and writes token
+ * token_offset + t of plane (b, h) of `dst`: gamma = ||x||_2, u = R x/gamma,
+ * zero-pad to 3*ceil(d/3), triplets, octahedral map (Eq. 5), Lloyd seeds,
+ * 3x3 joint rounding (or scalar rounding), packing; with codec.qjl also the
+ * QJL signs of R'(u - u^) and gamma_r = fp16(||u - u^||).
+ *   x          device, element (b,h,t,e) at x + b*s0 + h*s1 + t*s2 + e*s3,
+ *              x_strides = {s0,s1,s2,s3} in elements; s3 must be 1 and rows
+ *              16-byte aligned.
+ *   x_dtype    OCTO_DTYPE_F32 or OCTO_DTYPE_BF16.
+ *   dst        cache with batch == B, kv_heads == H and
+ *              token_offset + T <= capacity (else OCTO_ERR_CAPACITY).
+ * Zero vectors encode as gamma = 0 with the placeholder direction (0, 0).   */
+octo_status octo_encode(const octo_codec_desc* codec, const void* x, octo_dtype x_dtype,
+                        int32_t B, int32_t H, int32_t T, const int64_t x_strides[4],
+                        const octo_cache_view* dst, int32_t token_offset,
+                        hipStream_t stream);
+
+/* Workspace bytes needed by octo_attend_decode for these shapes.            */
+octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
+                                        int32_t num_q_heads, int32_t kv_heads,
+                                        int32_t max_seq_len, size_t* bytes);
+
+/* octo_attend_decode -- one query per sequence over the packed cache
+ * (paper Sec. 3.6 Eq. 13 score factorization; App. A summary: split-K
+ * flash decoding with fused unpack, centroid lookup, octahedral decode,
+ * value dequantization and online softmax).  For query head h on KV head
+ * g = h / (num_q_heads / kv_heads):
+ *   score_j = gamma_j * (R q_h) . u^_j  [+ gamma_j sqrt(pi/(2d)) gamma_r,j (R'R q_h).sigma_j]
+ *   out[b,h,:] = R_v^T sum_j softmax(softmax_scale * score)_j gamma_v,j u^_v,j
+ * over tokens j < min(seq_lens[b], max_seq_len, capacity).  K^ is never
+ * materialized.  An empty context gives a zero output row.
+ *   q          device [B, num_q_heads, d], fp32 or bf16, contiguous.
+ *   seq_lens   device int32 [B].
+ *   softmax_scale  <= 0 selects 1/sqrt(d).
+ *   out        device fp32 [B, num_q_heads, d].
+ *   workspace  device, >= octo_decode_workspace_bytes(...), 256-byte aligned.
+ * K and V caches must share B, kv_heads, capacity and (b_dir, b_nrm);
+ * V must not carry QJL.                                                      */
+octo_status octo_attend_decode(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
+                               const octo_cache_view* k_cache, const octo_cache_view* v_cache,
+                               const void* q, octo_dtype q_dtype, int32_t num_q_heads,
+                               const int32_t* seq_lens, int32_t max_seq_len,
+                               float softmax_scale, float* out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by octo_attend_chunk for these shapes.             */
+octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
+                                       int32_t num_q_heads, int32_t Tq, int32_t cached_tokens,
+                                       int32_t Tc, size_t* bytes);
+
+/* octo_attend_chunk -- chunk-wise attention ("Quantized Keys Steal Attention",
+ * Sec. 3, Token Structure and Attention Decomposition; OCTOPUS paper Sec. 4.3
+ * chunk-wise video diffusion): every one of the Tq queries of the current
+ * chunk attends, in one softmax and without a mask, to the first
+ * `cached_tokens` tokens of the packed cache and to the Tc current-chunk keys
+ * and values held at full precision.  QK^T and PV run on MFMA with fp16
+ * operands (cached u^ and current tokens rotated into R's frame) and fp32
+ * accumulation; the epilogue applies R^T.
+ *   q          device bf16 [B, num_q_heads, Tq, d] contiguous.
+ *   k_cur,v_cur device bf16 [B, kv_heads, Tc, d] contiguous.
+ *   out        device fp32 [B, num_q_heads, Tq, d].
+ * Keys must not carry QJL in this path.  Operand range: fp16 staging of the
+ * rotated queries, keys and values requires |entries| < 65504.              */
+octo_status octo_attend_chunk(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
+                              const octo_cache_view* k_cache, const octo_cache_view* v_cache,
+                              int32_t cached_tokens, const void* q, const void* k_cur,
+                              const void* v_cur, int32_t num_q_heads, int32_t Tq, int32_t Tc,
+                              float softmax_scale, float* out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OCTOPUS_H */

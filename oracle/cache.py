@@ -1,0 +1,105 @@
+"""Encode into, and decode out of, the packed cache layout (oracle side).
+
+A cache for one tensor (K or V) of shape [B, H, capacity, d] is a dict of
+flat host arrays in the layout documented in oracle.pack:
+  "dir"    uint32, B*H*capacity*W_dir words (tile-64)
+  "nrm"    uint32, B*H*capacity*W_nrm words (tile-64)
+  "gamma"  float32, [B, H, capacity]
+  "qjl"    uint32, B*H*capacity*W_sig words (tile-64)   (only with QJL)
+  "gamma_r" uint16, [B, H, capacity] fp16 bit patterns  (only with QJL)
+
+The codec is described by a plain dict:
+  d, b_dir, b_nrm, seed, qjl (bool), c_xi, c_rho (float32 arrays), rounding.
+"""
+import numpy as np
+
+from . import pack
+from .encode import encode, n_triplets
+from .octahedral import oct_decode
+
+
+def stream_sizes(codec):
+    nt = n_triplets(codec["d"])
+    return {
+        "dir": pack.stream_words(2 * nt, codec["b_dir"]),
+        "nrm": pack.stream_words(nt, codec["b_nrm"]),
+        "qjl": pack.stream_words(codec["d"], 1) if codec.get("qjl") else 0,
+    }
+
+
+def empty_cache(codec, B, H, capacity):
+    if capacity % 64:
+        raise ValueError("capacity must be a multiple of 64")
+    w = stream_sizes(codec)
+    c = {
+        "dir": np.zeros(B * H * capacity * w["dir"], dtype=np.uint32),
+        "nrm": np.zeros(B * H * capacity * w["nrm"], dtype=np.uint32),
+        "gamma": np.zeros((B, H, capacity), dtype=np.float32),
+        "B": B, "H": H, "capacity": capacity,
+    }
+    if codec.get("qjl"):
+        c["qjl"] = np.zeros(B * H * capacity * w["qjl"], dtype=np.uint32)
+        c["gamma_r"] = np.zeros((B, H, capacity), dtype=np.uint16)
+    return c
+
+
+def encode_into(cache, codec, x, token_offset=0):
+    """Encode x[B, H, T, d] into tokens [token_offset, token_offset+T).
+
+    Returns the per-vector encoder outputs (indices, margins, ...) reshaped to
+    [B, H, T, ...] so that tests can compare decisions and margins."""
+    B, H, T, d = x.shape
+    flat = np.asarray(x, dtype=np.float64).reshape(B * H * T, d)
+    enc = encode(flat, codec["c_xi"], codec["c_rho"], codec["seed"],
+                 rounding=codec.get("rounding", "local3x3"), qjl=codec.get("qjl", False))
+    w = stream_sizes(codec)
+    cap = cache["capacity"]
+    dirw = pack.pack_fields(pack.dir_fields(enc["i_xi"], enc["i_eta"]), codec["b_dir"])
+    nrmw = pack.pack_fields(enc["i_rho"], codec["b_nrm"])
+    if codec.get("qjl"):
+        sigw = pack.pack_fields(enc["sigma_neg"].astype(np.int64), 1)
+    for b in range(B):
+        for h in range(H):
+            sl = slice((b * H + h) * T, (b * H + h + 1) * T)
+            pack.scatter_tokens(cache["dir"], dirw[sl].reshape(T, w["dir"]), b, h, token_offset, H, cap)
+            if w["nrm"]:
+                pack.scatter_tokens(cache["nrm"], nrmw[sl].reshape(T, w["nrm"]), b, h, token_offset, H, cap)
+            cache["gamma"][b, h, token_offset:token_offset + T] = enc["gamma_f32"][sl]
+            if codec.get("qjl"):
+                pack.scatter_tokens(cache["qjl"], sigw[sl], b, h, token_offset, H, cap)
+                cache["gamma_r"][b, h, token_offset:token_offset + T] = enc["gamma_r_f16"][sl].view(np.uint16)
+    return {k: (v.reshape((B, H, T) + v.shape[1:]) if isinstance(v, np.ndarray) else v)
+            for k, v in enc.items()}
+
+
+def read_tokens(cache, codec, b, h, t0, T):
+    """Indices and side data of tokens [t0, t0+T) of plane (b, h)."""
+    nt = n_triplets(codec["d"])
+    w = stream_sizes(codec)
+    H, cap = cache["H"], cache["capacity"]
+    dirw = pack.gather_tokens(cache["dir"], b, h, t0, T, H, cap, w["dir"])
+    f = pack.unpack_fields(dirw, 2 * nt, codec["b_dir"])
+    if w["nrm"]:
+        nrmw = pack.gather_tokens(cache["nrm"], b, h, t0, T, H, cap, w["nrm"])
+        i_rho = pack.unpack_fields(nrmw, nt, codec["b_nrm"])
+    else:
+        i_rho = np.zeros((T, nt), dtype=np.int64)
+    out = {
+        "i_xi": f[:, 0::2], "i_eta": f[:, 1::2], "i_rho": i_rho,
+        "gamma": cache["gamma"][b, h, t0:t0 + T].astype(np.float64),
+        "dir_words": dirw,
+    }
+    if codec.get("qjl"):
+        sigw = pack.gather_tokens(cache["qjl"], b, h, t0, T, H, cap, w["qjl"])
+        out["sigma_neg"] = pack.unpack_fields(sigw, codec["d"], 1).astype(bool)
+        out["gamma_r"] = cache["gamma_r"][b, h, t0:t0 + T].view(np.float16).astype(np.float64)
+    return out
+
+
+def u_hat_from_indices(codec, i_xi, i_eta, i_rho):
+    """Rotated-frame reconstruction u^ = rho^ n^(xi^, eta^) per triplet."""
+    c_xi = np.asarray(codec["c_xi"], dtype=np.float64)
+    c_rho = np.asarray(codec["c_rho"], dtype=np.float64)
+    n_hat = oct_decode(c_xi[i_xi], c_xi[i_eta])
+    u_hat = c_rho[i_rho][..., None] * n_hat
+    return u_hat.reshape(u_hat.shape[:-2] + (-1,))

@@ -1,0 +1,200 @@
+"""Pins for oracle.encode (CPU).
+
+  * bit budget B_tri = 2 b_dir + b_nrm is 3b for the uniform reference and
+    3b + 1 for the implemented (b+1, b-1) split (OCTOPUS paper Sec. 3.3).
+  * sum_i rho_i^2 = 1 (App. C.4); u^ = rho^ n^ per triplet.
+  * tiny d exhaustive: full-grid joint rounding reaches the brute-force minimum
+    of l = ||t - rho^ n(xi^, eta^)||^2 over every (i_xi, i_eta, i_rho), and per
+    triplet l_full <= l_3x3 <= l_scalar (Sec. 3.5, Eq. 11/12).
+  * the argmax-s / nearest-rho rule equals the literal minimum of Eq. 12 over
+    the nine clamped candidates and all C_rho centroids.
+  * zero vector -> gamma = 0, placeholder direction, deterministic indices.
+  * statistical claims printed in the paper on Gaussian keys at d = 128:
+    the (b+delta, b-delta) sweep (Sec. 3.3), the rounding ablation (Sec. 3.5,
+    App. E summary), full-grid agreement of the 3x3 search.
+  * QJL (Sec. 3.6): the corrected dot product is unbiased (slope 1) where the
+    MSE-only reconstruction shrinks it.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import encode as E
+from oracle.octahedral import oct_decode
+from oracle.rotation import rotation_matrix, qjl_rotation_matrix
+from tests.oracle_codecs import ROOT, codec
+
+CLAIMS = json.load(open(os.path.join(ROOT, "tests", "golden", "paper_claims.json")))
+
+
+def gauss(n, d=128, seed=0):
+    return np.random.default_rng(seed).standard_normal((n, d))
+
+
+def tri_loss(enc, d):
+    t = E.split_triplets(enc["u"])
+    uh = enc["u_hat"].reshape(t.shape)
+    return ((t - uh) ** 2).sum(-1)
+
+
+def recon(enc, seed, d=128):
+    return enc["gamma"][:, None] * (enc["u_hat"][:, :d] @ rotation_matrix(d, seed))
+
+
+def test_bit_budget():
+    off = CLAIMS["bit_budget"]["default_split_offset"]
+    for b in (2, 3, 4):
+        c = codec(b)
+        assert 2 * c["b_dir"] + c["b_nrm"] == 3 * b + off
+        u = codec(b, b_dir=b, b_nrm=b)
+        assert 2 * u["b_dir"] + u["b_nrm"] == 3 * b
+
+
+def test_triplet_norms_and_reconstruction_shape():
+    c = codec(3)
+    x = gauss(64)
+    enc = E.encode(x, c["c_xi"], c["c_rho"], 0)
+    t = E.split_triplets(enc["u"])
+    assert np.allclose((t ** 2).sum((-1, -2)), 1.0, atol=1e-13)
+    assert np.allclose(enc["gamma"], np.linalg.norm(x, axis=1))
+    c_rho = c["c_rho"].astype(float)
+    uh = enc["u_hat"].reshape(t.shape)
+    assert np.allclose(np.linalg.norm(uh, axis=-1), c_rho[enc["i_rho"]], atol=1e-12)
+
+
+@pytest.mark.parametrize("bd,bn", [(2, 1), (3, 1), (2, 2), (3, 2)])
+def test_tiny_d_exhaustive(bd, bn):
+    d = 8
+    c = codec(b_dir=bd, b_nrm=bn, d=d)
+    x = gauss(300, d, seed=bd * 10 + bn)
+    K = c["c_xi"].size
+    cx = c["c_xi"].astype(float)
+    cr = c["c_rho"].astype(float)
+    dirs = oct_decode(np.repeat(cx, K), np.tile(cx, K))               # [K*K, 3]
+    loss = {}
+    for mode in ("full", "local3x3", "scalar"):
+        enc = E.encode(x, c["c_xi"], c["c_rho"], 1, rounding=mode)
+        loss[mode] = tri_loss(enc, d)
+        if mode == "full":
+            t = E.split_triplets(enc["u"])
+            cand = cr[None, None, :, None, None] * dirs[None, None, None, :, :]   # [1,1,R,KK,3]
+            brute = ((t[:, :, None, None, :] - cand) ** 2).sum(-1).min(axis=(-1, -2))
+            assert np.allclose(loss[mode], brute, atol=1e-14)
+    assert np.all(loss["full"] <= loss["local3x3"] + 1e-15)
+    assert np.all(loss["local3x3"] <= loss["scalar"] + 1e-15)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_joint_rounding_is_eq12_minimum_over_local_set(bits):
+    c = codec(bits)
+    x = gauss(200, seed=bits)
+    enc = E.encode(x, c["c_xi"], c["c_rho"], 0)
+    cx = c["c_xi"].astype(float)
+    cr = c["c_rho"].astype(float)
+    K = cx.size
+    t = E.split_triplets(enc["u"])
+    # seeds recomputed here from the midpoints of C_xi
+    from oracle.octahedral import oct_encode
+    xi, eta, _ = oct_encode(t)
+    mids = 0.5 * (cx[:-1] + cx[1:])
+    sx = np.searchsorted(mids, xi, side="left")
+    sy = np.searchsorted(mids, eta, side="left")
+    best = np.full(t.shape[:2], np.inf)
+    rho = np.sqrt((t ** 2).sum(-1))
+    for a, b in itertools.product((-1, 0, 1), repeat=2):
+        n = oct_decode(cx[np.clip(sx + a, 0, K - 1)], cx[np.clip(sy + b, 0, K - 1)])
+        s = (t * n).sum(-1)
+        l = rho[..., None] ** 2 - 2 * cr[None, None, :] * s[..., None] + cr[None, None, :] ** 2
+        best = np.minimum(best, l.min(-1))
+    got = tri_loss(enc, 128)
+    assert np.abs(got - best).max() < 1e-14
+
+
+def test_zero_vector_placeholder():
+    c = codec(3)
+    x = np.zeros((2, 128))
+    enc = E.encode(x, c["c_xi"], c["c_rho"], 0)
+    K = c["c_xi"].size
+    assert np.all(enc["gamma"] == 0)
+    assert np.all(enc["i_xi"] == K // 2 - 1) and np.all(enc["i_eta"] == K // 2 - 1)
+    assert np.all(enc["i_rho"] == 0)
+    assert np.all(enc["margin"] == 0)
+
+
+def sweep_mse(b, delta, x):
+    bd, bn = b + delta, b - delta
+    c = codec(b_dir=bd, b_nrm=bn)
+    enc = E.encode(x, c["c_xi"], c["c_rho"], 0)
+    return ((x - recon(enc, 0)) ** 2).mean()
+
+
+def test_bit_split_sweep_reproduces_paper():
+    cl = CLAIMS["bit_split_sweep"]
+    x = gauss(2048, seed=11)
+    for b in (2, 3, 4):
+        mse = {dl: sweep_mse(b, dl, x) for dl in (-2, -1, 0, 1, 2)}
+        assert min(mse, key=mse.get) == cl["argmin_delta"], (b, mse)
+        red = 100 * (1 - mse[1] / mse[0])
+        lo, hi = cl["delta_plus1_mse_reduction_pct"]
+        assert lo - 3 <= red <= hi + 3, (b, red)
+        assert mse[2] > mse[1] and mse[2] > mse[0]
+        if b > 2:
+            inc = 100 * (mse[2] / mse[0] - 1)
+            lo2, hi2 = cl["delta_plus2_mse_increase_pct"]
+            assert lo2 - 5 <= inc <= hi2 + 5, (b, inc)
+        assert mse[-2] / mse[0] >= 5.0, (b, mse[-2] / mse[0])
+
+
+def test_rounding_ablation_reproduces_paper():
+    lo, hi = CLAIMS["rounding_ablation"]["mse_reduction_pct"]
+    x = gauss(2048, seed=12)
+    for b in (2, 3, 4):
+        c = codec(b)
+        m = {}
+        for mode in ("local3x3", "scalar"):
+            enc = E.encode(x, c["c_xi"], c["c_rho"], 0, rounding=mode)
+            m[mode] = ((x - recon(enc, 0)) ** 2).mean()
+        red = 100 * (1 - m["local3x3"] / m["scalar"])
+        assert lo - 3 <= red <= hi + 2, (b, red)
+
+
+@pytest.mark.parametrize("b_dir", [2, 3, 4, 5])
+def test_local3x3_agrees_with_full_grid(b_dir):
+    n_trip = CLAIMS["rounding_ablation"]["full_grid_equal_triplets"]
+    c = codec(b_dir=b_dir, b_nrm=max(b_dir - 2, 1))
+    x = gauss(-(-n_trip // 43), seed=20 + b_dir)
+    a = E.encode(x, c["c_xi"], c["c_rho"], 0, rounding="local3x3")
+    f = E.encode(x, c["c_xi"], c["c_rho"], 0, rounding="full")
+    same = (a["i_xi"] == f["i_xi"]) & (a["i_eta"] == f["i_eta"]) & (a["i_rho"] == f["i_rho"])
+    assert same.mean() >= 0.999
+    assert np.all(tri_loss(f, 128) <= tri_loss(a, 128) + 1e-15)
+
+
+def test_qjl_dot_product_unbiased():
+    n = 3000
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((n, 128))
+    k = rng.standard_normal((n, 128))
+    c = codec(2, qjl=True)
+    true, mse_only, corrected = [], [], []
+    for i in range(0, n, 100):
+        seed = 1000 + i
+        enc = E.encode(k[i:i + 100], c["c_xi"], c["c_rho"], seed, qjl=True)
+        R = rotation_matrix(128, seed)
+        Rp = qjl_rotation_matrix(128, seed)
+        q_rot = q[i:i + 100] @ R.T
+        base = enc["gamma"] * (q_rot * enc["u_hat"][:, :128]).sum(1)
+        sig = np.where(enc["sigma_neg"], -1.0, 1.0)
+        r_norm = enc["gamma_r_f16"].astype(float)
+        est = np.sqrt(np.pi / 256) * r_norm * ((q_rot @ Rp.T) * sig).sum(1)
+        true.append((q[i:i + 100] * k[i:i + 100]).sum(1))
+        mse_only.append(base)
+        corrected.append(base + enc["gamma"] * est)
+    true, mse_only, corrected = map(np.concatenate, (true, mse_only, corrected))
+    slope = lambda y: (y * true).sum() / (true * true).sum()
+    assert slope(mse_only) < 0.985
+    assert abs(slope(corrected) - 1.0) < 0.01
+    assert np.all(np.abs(corrected - true).mean() < 1.2 * np.abs(mse_only - true).mean())
