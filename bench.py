@@ -1,0 +1,283 @@
+"""Benchmark of the OCTOPUS hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa32k]
+
+A step is one pass of the whole hot path over one batch of synthetic input
+with everything already resident in HBM:
+  decode workloads  encode the full context (K and V) into the packed cache,
+                    then single-query decode attention over it;
+  chunk workload    encode the current chunk (K and V) into the cache slots
+                    after the cached window, then chunk attention of its
+                    queries over the window and the chunk.
+The timed region brackets exactly K steps with torch.cuda.synchronize();
+HIP events recorded on the stream the kernels run on give the per-call
+durations.  One JSON line is printed.
+
+value      cached KV-tokens/s of the attention call: tokens attended per
+           step (sum of the sequence lengths; for the chunk workload the
+           window plus the chunk) divided by its mean duration.
+roofline   for the attention call: algorithmic bytes (packed cache of the
+           attended tokens, K and V) per launch over the mean duration,
+           against 8 TB/s (decode), or algorithmic MFMA flops against the
+           fp16 dense peak (chunk).
+cpu_baseline  the float64 oracle on a bounded sample (one KV-head plane of
+           the decode workload; a few query rows for the chunk workload),
+           on one host thread, scaled to the same unit.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import quantized_decode_attention_octo_amd as octo  # noqa: E402
+from quantized_decode_attention_octo_amd.workloads import WORKLOADS, make_inputs  # noqa: E402
+
+METRIC = "decode-attn cached KV-tokens/s + % of HBM peak on packed cache; encode tokens/s"
+HBM_PEAK_GBS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def packed_bytes_per_token(codec):
+    s = codec.sizes()
+    b = 4 * (s.dir_words + s.nrm_words) + 4           # streams + gamma
+    if codec.qjl:
+        b += 4 * s.qjl_words + 2                      # sigma + fp16 gamma_r
+    return b
+
+
+class Timer:
+    """HIP events on the current stream around each call of one kind."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def run_decode(w, steps, warmup):
+    inp = make_inputs(w)
+    kc = octo.Codec(bits=w.bits, qjl=w.qjl)
+    vc = octo.Codec(bits=w.bits)
+    K, V = inp["K"].cuda(), inp["V"].cuda()
+    q, seq = inp["q"].cuda(), inp["seq_lens"].cuda()
+    cap = w.capacity
+    kcache = octo.PackedCache(kc, w.B, w.Hkv, cap)
+    vcache = octo.PackedCache(vc, w.B, w.Hkv, cap)
+    max_len = int(inp["seq_lens"].max())
+    ws = octo.workspace(octo.octo_decode_workspace_bytes(kc, w.B, w.Hq, w.Hkv, max_len), "cuda")
+    out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    t_enc, t_att = Timer(), Timer()
+
+    def step(timed):
+        e0 = t_enc.start() if timed else None
+        octo.octo_encode(kc, K, kcache)
+        octo.octo_encode(vc, V, vcache)
+        if timed:
+            t_enc.stop(e0)
+            e0 = t_att.start()
+        octo.octo_attend_decode(kc, vc, kcache, vcache, q, seq, max_len, out=out, ws=ws)
+        if timed:
+            t_att.stop(e0)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tokens = int(inp["seq_lens"].sum())
+    att_ms, enc_ms = t_att.mean_ms(), t_enc.mean_ms()
+    kv_bytes = tokens * w.Hkv * (packed_bytes_per_token(kc) + packed_bytes_per_token(vc))
+    achieved = kv_bytes / (att_ms * 1e-3) / 1e9
+    enc_tokens = w.B * w.T
+    res = {
+        "value": tokens / (att_ms * 1e-3),
+        "unit": "cached KV-tokens/s",
+        "ms_per_step": wall / steps * 1e3,
+        "dtype": "f32",
+        "attention_us": att_ms * 1e3,
+        "encode_us": enc_ms * 1e3,
+        "encode_tokens_per_s": enc_tokens / (enc_ms * 1e-3),
+        "token_kv_heads_per_s": tokens * w.Hkv / (att_ms * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "octo_attend_decode (split-K scan + merge)",
+                     "algorithmic_bytes_per_launch": kv_bytes},
+    }
+    return res, (inp, kc, vc, kcache, vcache)
+
+
+def run_chunk(w, steps, warmup):
+    inp = make_inputs(w)
+    kc = octo.Codec(bits=w.bits)
+    vc = octo.Codec(bits=w.bits)
+    cached, Tq = w.T, w.chunk_q
+    kcache = octo.PackedCache(kc, w.B, w.Hkv, w.capacity)
+    vcache = octo.PackedCache(vc, w.B, w.Hkv, w.capacity)
+    octo.octo_encode(kc, inp["K"].cuda(), kcache)
+    octo.octo_encode(vc, inp["V"].cuda(), vcache)
+    q, kcur, vcur = inp["q"].cuda(), inp["K_cur"].cuda(), inp["V_cur"].cuda()
+    ws = octo.workspace(octo.octo_chunk_workspace_bytes(kc, w.B, w.Hq, w.Hkv, Tq, cached, Tq), "cuda")
+    out = torch.empty(w.B, w.Hq, Tq, 128, dtype=torch.float32, device="cuda")
+    t_enc, t_att = Timer(), Timer()
+
+    def step(timed):
+        e0 = t_enc.start() if timed else None
+        octo.octo_encode(kc, kcur, kcache, token_offset=cached)
+        octo.octo_encode(vc, vcur, vcache, token_offset=cached)
+        if timed:
+            t_enc.stop(e0)
+            e0 = t_att.start()
+        octo.octo_attend_chunk(kc, vc, kcache, vcache, cached, q, kcur, vcur, out=out, ws=ws)
+        if timed:
+            t_att.stop(e0)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    att_ms, enc_ms = t_att.mean_ms(), t_enc.mean_ms()
+    keys = cached + Tq
+    flops = 4.0 * w.B * w.Hq * Tq * keys * 128
+    achieved = flops / (att_ms * 1e-3) / 1e12
+    res = {
+        "value": w.B * keys / (att_ms * 1e-3),
+        "unit": "cached KV-tokens/s",
+        "ms_per_step": wall / steps * 1e3,
+        "dtype": "f16-mfma/f32-acc",
+        "attention_us": att_ms * 1e3,
+        "encode_us": enc_ms * 1e3,
+        "encode_tokens_per_s": w.B * Tq / (enc_ms * 1e-3),
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "octo_attend_chunk (rotate + decode pre-passes + MFMA attention)",
+                     "algorithmic_flops_per_launch": flops},
+    }
+    return res, (inp, kc, vc, kcache, vcache)
+
+
+def cpu_baseline(w, state):
+    """The oracle on one host thread over a bounded sample, in the same unit."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import attention as oatt
+    from oracle_codecs import codec as oracle_codec
+    inp, kc, vc, kcache, vcache = state
+    hk = oracle_codec(bits=w.bits, qjl=w.qjl)
+    hv = oracle_codec(bits=w.bits)
+    hkc, hvc = kcache.to_host(), vcache.to_host()
+    G = w.Hq // w.Hkv
+    n = w.B * w.Hkv
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        if not w.chunk_q:
+            L = int(inp["seq_lens"][0])
+            pk = {"B": 1, "H": 1, "capacity": hkc["capacity"],
+                  "dir": hkc["dir"].reshape(n, -1)[0], "nrm": hkc["nrm"].reshape(n, -1)[0],
+                  "gamma": hkc["gamma"][:1, :1]}
+            if "qjl" in hkc:
+                pk["qjl"] = hkc["qjl"].reshape(n, -1)[0]
+                pk["gamma_r"] = hkc["gamma_r"][:1, :1]
+            pv = {"B": 1, "H": 1, "capacity": hvc["capacity"],
+                  "dir": hvc["dir"].reshape(n, -1)[0], "nrm": hvc["nrm"].reshape(n, -1)[0],
+                  "gamma": hvc["gamma"][:1, :1]}
+            qn = inp["q"][:1, :G].double().numpy()
+            t0 = time.perf_counter()
+            oatt.decode_attention(qn, pk, pv, hk, hv, np.array([L]))
+            dt = time.perf_counter() - t0
+            # the step attends sum(len) tokens on each of the Hkv planes; the
+            # sample is L tokens of one plane: tokens/s = L / (dt * Hkv)
+            value = L / (dt * w.Hkv)
+            sample = f"oracle decode attention of batch 0, KV head 0 ({L} tokens, {G} query heads), scaled by the {w.Hkv} KV heads"
+        else:
+            rows = np.arange(8)
+            pk = {"B": 1, "H": 1, "capacity": hkc["capacity"], "dir": hkc["dir"].reshape(n, -1)[0],
+                  "nrm": hkc["nrm"].reshape(n, -1)[0], "gamma": hkc["gamma"][:1, :1]}
+            pv = {"B": 1, "H": 1, "capacity": hvc["capacity"], "dir": hvc["dir"].reshape(n, -1)[0],
+                  "nrm": hvc["nrm"].reshape(n, -1)[0], "gamma": hvc["gamma"][:1, :1]}
+            t0 = time.perf_counter()
+            oatt.chunk_attention(inp["q"][:, :1].double().numpy(), pk, pv, hk, hv, w.T,
+                                 inp["K_cur"][:, :1].double().numpy(),
+                                 inp["V_cur"][:, :1].double().numpy(), q_rows=rows)
+            dt = time.perf_counter() - t0
+            keys = w.T + w.chunk_q
+            # full step = Hq heads x Tq rows; the sample = 1 head x 8 rows
+            t_full = dt * w.Hq * w.chunk_q / len(rows)
+            value = keys / t_full
+            sample = f"oracle chunk attention of head 0, {len(rows)} query rows over {keys} keys, scaled to {w.Hq} heads x {w.chunk_q} rows"
+    return {"value": value, "unit": "cached KV-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa32k", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the workloads fit one MI355X and no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+    octo.lib()
+    w = WORKLOADS[a.workload]
+    log(f"bench {a.workload}: {w.name}; warmup {a.warmup}, steps {a.steps}")
+    if w.chunk_q:
+        res, state = run_chunk(w, a.steps, a.warmup)
+    else:
+        res, state = run_decode(w, a.steps, a.warmup)
+    log(f"attention {res['attention_us']:.1f} us, encode {res['encode_us']:.1f} us")
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(w, state)
+        log(f"cpu baseline {cpu['value']:.3g} {cpu['unit']} in {cpu['seconds']:.1f} s")
+    line = {
+        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": res["dtype"], "data": "synthetic (seeded Gaussian, see workloads.py)",
+        "config": {"workload": f"{a.workload}: {w.name}", "batch": w.B, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.d, "context": w.T, "bits": w.bits,
+                   "qjl": w.qjl, "chunk_queries": w.chunk_q},
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+        "attention_us": res["attention_us"], "encode_us": res["encode_us"],
+        "encode_tokens_per_s": res["encode_tokens_per_s"],
+    }
+    if "token_kv_heads_per_s" in res:
+        line["token_kv_heads_per_s"] = res["token_kv_heads_per_s"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,8 +23,9 @@
  *     reduction; the split-K merge order is fixed).
  *   - Supported now: head_dim = 128; (b_dir, b_nrm) in {(3,1), (4,2), (5,3)}
  *     (the paper's (b+1, b-1) split for b = 2, 3, 4; Sec. 3.3) and the uniform
- *     splits {(2,2), (3,3), (4,4)}; query heads per KV head in {1, 2, 4, 7, 8};
- *     QJL on keys only.  Anything else returns OCTO_ERR_UNSUPPORTED.
+ *     splits {(2,2), (3,3), (4,4)}; for decode, query heads per KV head in
+ *     {1, 2, 4, 7, 8}; QJL on keys only, in the decode path only.  Anything
+ *     else returns OCTO_ERR_UNSUPPORTED.
  *
  * Cache layout (OCTO_LAYOUT_TILE64).  The paper fixes no bit layout; this one
  * is this library's.  A stream is a little-endian LSB-first bit string: field
@@ -129,8 +130,8 @@ octo_status octo_record_sizes(const octo_codec_desc* codec, octo_stream_sizes* o
  * 3x3 joint rounding (or scalar rounding), packing; with codec.qjl also the
  * QJL signs of R'(u - u^) and gamma_r = fp16(||u - u^||).
  *   x          device, element (b,h,t,e) at x + b*s0 + h*s1 + t*s2 + e*s3,
- *              x_strides = {s0,s1,s2,s3} in elements; s3 must be 1 and rows
- *              16-byte aligned.
+ *              x_strides = {s0,s1,s2,s3} in elements, s3 must be 1, the
+ *              others >= 0; x aligned to its element size.
  *   x_dtype    OCTO_DTYPE_F32 or OCTO_DTYPE_BF16.
  *   dst        cache with batch == B, kv_heads == H and
  *              token_offset + T <= capacity (else OCTO_ERR_CAPACITY).
@@ -170,22 +171,30 @@ octo_status octo_attend_decode(const octo_codec_desc* k_codec, const octo_codec_
 
 /* Workspace bytes needed by octo_attend_chunk for these shapes.             */
 octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
-                                       int32_t num_q_heads, int32_t Tq, int32_t cached_tokens,
-                                       int32_t Tc, size_t* bytes);
+                                       int32_t num_q_heads, int32_t kv_heads, int32_t Tq,
+                                       int32_t cached_tokens, int32_t Tc, size_t* bytes);
 
 /* octo_attend_chunk -- chunk-wise attention ("Quantized Keys Steal Attention",
  * Sec. 3, Token Structure and Attention Decomposition; OCTOPUS paper Sec. 4.3
  * chunk-wise video diffusion): every one of the Tq queries of the current
  * chunk attends, in one softmax and without a mask, to the first
  * `cached_tokens` tokens of the packed cache and to the Tc current-chunk keys
- * and values held at full precision.  QK^T and PV run on MFMA with fp16
- * operands (cached u^ and current tokens rotated into R's frame) and fp32
- * accumulation; the epilogue applies R^T.
+ * and values held at full precision.  Query head h uses KV head
+ * h / (num_q_heads / kv_heads).  QK^T and PV run on MFMA with fp16 operands
+ * and fp32 accumulation, everything in the rotated frames: R_k q, R_k k_cur,
+ * R_v v_cur and gamma u^ of the cached tokens (Eq. 13); the epilogue applies
+ * R_v^T.  The workspace receives the fp16 rotated queries and the fp16
+ * rotated key and value rows of the whole window (cached then current).
  *   q          device bf16 [B, num_q_heads, Tq, d] contiguous.
- *   k_cur,v_cur device bf16 [B, kv_heads, Tc, d] contiguous.
+ *   k_cur,v_cur device bf16 [B, kv_heads, Tc, d] contiguous (may be NULL if
+ *              Tc == 0).
  *   out        device fp32 [B, num_q_heads, Tq, d].
- * Keys must not carry QJL in this path.  Operand range: fp16 staging of the
- * rotated queries, keys and values requires |entries| < 65504.              */
+ *   workspace  device, >= octo_chunk_workspace_bytes(...), 256-byte aligned.
+ * Keys must not carry QJL in this path.  Operand range and precision: the
+ * fp16 staging requires |rotated entries| < 65504 and rounds each operand to
+ * 11 significant bits, so this path is meant for inputs without large
+ * outlier channels (the decode path computes in fp32).  Tq == 0 is a no-op;
+ * an empty window gives zero output rows.                                  */
 octo_status octo_attend_chunk(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
                               const octo_cache_view* k_cache, const octo_cache_view* v_cache,
                               int32_t cached_tokens, const void* q, const void* k_cur,

@@ -16,7 +16,8 @@ Chunk attention (the cached / current decomposition of the second page,
 "Quantized Keys Steal Attention", Sec. 3 "Token Structure and Attention
 Decomposition"): every query of the current chunk attends, in one softmax and
 without a mask, to all cached (packed) tokens and to all current-chunk tokens,
-the latter at full precision.
+the latter at full precision.  An empty window (no cached and no current
+tokens) gives zero output rows, as an empty decode context does (reading).
 
 Parity: pinned by the score factorization of Eq. 13 against the explicit
 reconstruction, by torch's scaled_dot_product_attention on the explicit K^, V^,
@@ -91,12 +92,17 @@ def chunk_attention(q, k_cache, v_cache, k_codec, v_codec, cached_tokens,
     out = np.zeros((B, Hq, Tq, d))
     for b in range(B):
         for g in range(Hkv):
-            k_hat, krec = reconstruct(k_cache, k_codec, b, g, 0, cached_tokens)
-            v_hat, _ = reconstruct(v_cache, v_codec, b, g, 0, cached_tokens)
-            kc = np.asarray(k_cur[b, g], dtype=np.float64)
-            vc = np.asarray(v_cur[b, g], dtype=np.float64)
+            if cached_tokens:
+                k_hat, krec = reconstruct(k_cache, k_codec, b, g, 0, cached_tokens)
+                v_hat, _ = reconstruct(v_cache, v_codec, b, g, 0, cached_tokens)
+            else:
+                k_hat = v_hat = np.zeros((0, d))
+            kc = np.asarray(k_cur[b, g], dtype=np.float64).reshape(-1, d)
+            vc = np.asarray(v_cur[b, g], dtype=np.float64).reshape(-1, d)
             keys = np.concatenate([k_hat, kc], axis=0)
             vals = np.concatenate([v_hat, vc], axis=0)
+            if keys.shape[0] == 0:
+                continue            # nothing to attend to: zero rows (reading)
             for hh in range(G):
                 h = g * G + hh
                 qh = q[b, h][rows]

@@ -1,0 +1,262 @@
+"""ctypes binding of liboctopus.so (include/octopus.h).
+
+Argument marshalling only: the functions below turn torch tensors into device
+pointers, pass the current HIP stream and raise OctoError on a non-OK status.
+Every step of the codec and of attention runs in the library's kernels; there
+is no fallback of any kind.  torch provides device memory and streams.
+
+Names follow the C ABI: octo_encode, octo_attend_decode, octo_attend_chunk,
+octo_record_sizes, octo_decode_workspace_bytes, octo_chunk_workspace_bytes.
+The helper classes Codec and PackedCache allocate the codebook tables and the
+packed streams with torch and build the descriptor structs.
+"""
+import ctypes
+import json
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liboctopus.so")
+CODEBOOKS = os.path.join(PKG, "codebooks", "octopus_d{d}.json")
+
+ABI_VERSION = 1
+STATUS = ["OCTO_OK", "OCTO_ERR_INVALID_ARGUMENT", "OCTO_ERR_UNSUPPORTED", "OCTO_ERR_ALIGNMENT",
+          "OCTO_ERR_CAPACITY", "OCTO_ERR_WORKSPACE_TOO_SMALL", "OCTO_ERR_VERSION", "OCTO_ERR_HIP"]
+DTYPE_F32, DTYPE_BF16 = 0, 1
+ROUND_LOCAL3X3, ROUND_SCALAR = 0, 1
+LAYOUT_TILE64 = 0
+
+
+class OctoError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS[status] if 0 <= status < len(STATUS) else status}: {message}")
+        self.status = status
+
+
+class CodecDesc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("head_dim", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("b_dir", ctypes.c_int32), ("b_nrm", ctypes.c_int32),
+                ("rounding", ctypes.c_int32), ("qjl", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("c_xi", ctypes.c_void_p), ("c_rho", ctypes.c_void_p)]
+
+
+class CacheView(ctypes.Structure):
+    _fields_ = [("dir", ctypes.c_void_p), ("nrm", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("qjl", ctypes.c_void_p), ("gamma_r", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+class StreamSizes(ctypes.Structure):
+    _fields_ = [("dir_words", ctypes.c_int32), ("nrm_words", ctypes.c_int32),
+                ("qjl_words", ctypes.c_int32), ("n_triplets", ctypes.c_int32),
+                ("b_dir", ctypes.c_int32), ("b_nrm", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+
+def lib():
+    """The loaded library.  Raises if it has not been built: nothing runs without it."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m quantized_decode_attention_octo_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.octo_abi_version.restype = ctypes.c_uint32
+        L.octo_status_string.restype = ctypes.c_char_p
+        L.octo_status_string.argtypes = [ctypes.c_int]
+        L.octo_last_error.restype = ctypes.c_char_p
+        L.octo_record_sizes.argtypes = [ctypes.POINTER(CodecDesc), ctypes.POINTER(StreamSizes)]
+        L.octo_encode.argtypes = [ctypes.POINTER(CodecDesc), _P, ctypes.c_int, _I, _I, _I,
+                                  ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(CacheView), _I, _P]
+        L.octo_decode_workspace_bytes.argtypes = [ctypes.POINTER(CodecDesc), _I, _I, _I, _I,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+        L.octo_attend_decode.argtypes = [ctypes.POINTER(CodecDesc), ctypes.POINTER(CodecDesc),
+                                         ctypes.POINTER(CacheView), ctypes.POINTER(CacheView),
+                                         _P, ctypes.c_int, _I, _P, _I, ctypes.c_float, _P, _P,
+                                         ctypes.c_size_t, _P]
+        L.octo_chunk_workspace_bytes.argtypes = [ctypes.POINTER(CodecDesc), _I, _I, _I, _I, _I, _I,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+        L.octo_attend_chunk.argtypes = [ctypes.POINTER(CodecDesc), ctypes.POINTER(CodecDesc),
+                                        ctypes.POINTER(CacheView), ctypes.POINTER(CacheView), _I,
+                                        _P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P,
+                                        ctypes.c_size_t, _P]
+        for f in ("octo_record_sizes", "octo_encode", "octo_decode_workspace_bytes",
+                  "octo_attend_decode", "octo_chunk_workspace_bytes", "octo_attend_chunk"):
+            getattr(L, f).restype = ctypes.c_int
+        if L.octo_abi_version() != ABI_VERSION:
+            raise RuntimeError("liboctopus.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise OctoError(status, lib().octo_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def load_codebooks(d=128):
+    with open(CODEBOOKS.format(d=d)) as f:
+        return json.load(f)
+
+
+class Codec:
+    """A codec descriptor with its fp32 codebook tables on `device`.
+
+    bits: b; the split defaults to the paper's (b+1, b-1) (b_dir, b_nrm).
+    The codebook values come from the shipped artifact (Lloyd-Max tables,
+    Sec. 3.4 of the OCTOPUS paper)."""
+
+    def __init__(self, bits=3, seed=0, qjl=False, b_dir=None, b_nrm=None,
+                 rounding=ROUND_LOCAL3X3, device="cuda", d=128, tables=None):
+        if b_dir is None:
+            b_dir, b_nrm = bits + 1, bits - 1
+        art = tables or load_codebooks(d)
+        self.c_xi = torch.tensor(art["c_xi"][str(b_dir)], dtype=torch.float32, device=device)
+        self.c_rho = torch.tensor(art["c_rho"][str(b_nrm)], dtype=torch.float32, device=device)
+        self.desc = CodecDesc(ABI_VERSION, d, bits, b_dir, b_nrm, rounding, int(bool(qjl)), 0,
+                              seed, self.c_xi.data_ptr(), self.c_rho.data_ptr())
+        self.bits, self.b_dir, self.b_nrm, self.seed, self.qjl = bits, b_dir, b_nrm, seed, bool(qjl)
+        self.rounding, self.d, self.device = rounding, d, device
+
+    def sizes(self):
+        return octo_record_sizes(self.desc)
+
+
+class PackedCache:
+    """The packed streams of one tensor (K or V) in the tile-64 layout."""
+
+    def __init__(self, codec, B, H, capacity, device="cuda"):
+        s = codec.sizes()
+        n = B * H * capacity
+        i32 = dict(dtype=torch.int32, device=device)
+        self.dir = torch.zeros(n * s.dir_words, **i32)
+        self.nrm = torch.zeros(max(1, n * s.nrm_words), **i32)
+        self.gamma = torch.zeros(B, H, capacity, dtype=torch.float32, device=device)
+        self.qjl = torch.zeros(n * s.qjl_words, **i32) if codec.qjl else None
+        self.gamma_r = torch.zeros(B, H, capacity, dtype=torch.int16, device=device) if codec.qjl else None
+        self.B, self.H, self.capacity, self.sizes = B, H, capacity, s
+        self.view = CacheView(self.dir.data_ptr(), self.nrm.data_ptr(), self.gamma.data_ptr(),
+                              self.qjl.data_ptr() if self.qjl is not None else None,
+                              self.gamma_r.data_ptr() if self.gamma_r is not None else None,
+                              B, H, capacity, LAYOUT_TILE64)
+
+    def nbytes(self):
+        t = [self.dir, self.nrm, self.gamma, self.qjl, self.gamma_r]
+        return sum(x.numel() * x.element_size() for x in t if x is not None)
+
+    def to_host(self):
+        """Host copies of the streams (numpy) in the layout the oracle reads."""
+        out = {"dir": self.dir.cpu().numpy().view("<u4"),
+               "nrm": self.nrm.cpu().numpy().view("<u4"),
+               "gamma": self.gamma.cpu().numpy(),
+               "B": self.B, "H": self.H, "capacity": self.capacity}
+        if self.qjl is not None:
+            out["qjl"] = self.qjl.cpu().numpy().view("<u4")
+            out["gamma_r"] = self.gamma_r.cpu().numpy().view("<u2")
+        return out
+
+
+# ------------------------------------------------------------------ entry points
+def octo_record_sizes(desc):
+    out = StreamSizes()
+    _check(lib().octo_record_sizes(ctypes.byref(desc), ctypes.byref(out)))
+    return out
+
+
+def octo_encode(codec, x, cache, token_offset=0):
+    """Encodes x[B, H, T, d] (fp32 or bf16, any strides with unit last stride)
+    into tokens [token_offset, token_offset + T) of `cache`."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    B, H, T, d = x.shape
+    strides = (ctypes.c_int64 * 4)(*x.stride())
+    dt = DTYPE_F32 if x.dtype == torch.float32 else DTYPE_BF16
+    _check(lib().octo_encode(ctypes.byref(codec.desc), _ptr(x), dt, B, H, T, strides,
+                             ctypes.byref(cache.view), token_offset, _stream(x.device)))
+
+
+def octo_decode_workspace_bytes(k_codec, B, num_q_heads, kv_heads, max_seq_len):
+    n = ctypes.c_size_t()
+    _check(lib().octo_decode_workspace_bytes(ctypes.byref(k_codec.desc), B, num_q_heads,
+                                             kv_heads, max_seq_len, ctypes.byref(n)))
+    return n.value
+
+
+def workspace(nbytes, device):
+    """A 256-byte aligned device buffer of at least nbytes."""
+    return torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
+
+
+def _aligned_ptr(ws):
+    p = ws.data_ptr()
+    return (p + 255) // 256 * 256
+
+
+def octo_attend_decode(k_codec, v_codec, k_cache, v_cache, q, seq_lens, max_seq_len=None,
+                       softmax_scale=0.0, out=None, ws=None):
+    """q[B, H_q, d] (fp32 or bf16, contiguous), seq_lens int32 [B] on the device.
+    Returns out[B, H_q, d] fp32."""
+    if q.dtype not in (torch.float32, torch.bfloat16) or not q.is_contiguous():
+        raise TypeError("q must be a contiguous float32 or bfloat16 tensor")
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    B, Hq, d = q.shape
+    max_seq_len = k_cache.capacity if max_seq_len is None else int(max_seq_len)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    need = octo_decode_workspace_bytes(k_codec, B, Hq, k_cache.H, max_seq_len)
+    if ws is None or ws.numel() < need + 256:
+        ws = workspace(need, q.device)
+    dt = DTYPE_F32 if q.dtype == torch.float32 else DTYPE_BF16
+    _check(lib().octo_attend_decode(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
+                                    ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
+                                    _ptr(q), dt, Hq, _ptr(seq_lens), max_seq_len,
+                                    float(softmax_scale), _ptr(out),
+                                    ctypes.c_void_p(_aligned_ptr(ws)), ws.numel() - 256,
+                                    _stream(q.device)))
+    return out
+
+
+def octo_chunk_workspace_bytes(k_codec, B, num_q_heads, kv_heads, Tq, cached_tokens, Tc):
+    n = ctypes.c_size_t()
+    _check(lib().octo_chunk_workspace_bytes(ctypes.byref(k_codec.desc), B, num_q_heads,
+                                            kv_heads, Tq, cached_tokens, Tc, ctypes.byref(n)))
+    return n.value
+
+
+def octo_attend_chunk(k_codec, v_codec, k_cache, v_cache, cached_tokens, q, k_cur, v_cur,
+                      softmax_scale=0.0, out=None, ws=None):
+    """q[B, H_q, Tq, d], k_cur/v_cur[B, H_kv, Tc, d] (bf16, contiguous).
+    Returns out[B, H_q, Tq, d] fp32."""
+    for t in (q, k_cur, v_cur):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError("q, k_cur and v_cur must be contiguous bfloat16 tensors")
+    B, Hq, Tq, d = q.shape
+    Tc = k_cur.shape[2]
+    if out is None:
+        out = torch.empty(B, Hq, Tq, d, dtype=torch.float32, device=q.device)
+    need = octo_chunk_workspace_bytes(k_codec, B, Hq, k_cache.H, Tq, cached_tokens, Tc)
+    if ws is None or ws.numel() < need + 256:
+        ws = workspace(need, q.device)
+    _check(lib().octo_attend_chunk(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
+                                   ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
+                                   cached_tokens, _ptr(q), _ptr(k_cur), _ptr(v_cur), Hq, Tq, Tc,
+                                   float(softmax_scale), _ptr(out),
+                                   ctypes.c_void_p(_aligned_ptr(ws)), ws.numel() - 256,
+                                   _stream(q.device)))
+    return out

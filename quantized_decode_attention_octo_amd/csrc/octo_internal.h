@@ -1,0 +1,115 @@
+// Internal declarations shared by the OCTOPUS HIP library sources.
+//
+// The method is the one of "OCTOPUS: Optimized KV Cache for Transformers via
+// Octahedral Parametrization Under optimal Squared error quantization"
+// (arXiv 2605.21226), Sec. 3.  This header holds the resolved codec
+// parameters, the host-side status plumbing and the small device helpers
+// (sign generator, wavefront Walsh-Hadamard transform, bit-field access) that
+// the encode, decode and chunk kernels share.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "octopus.h"
+
+namespace octo {
+
+constexpr int kHeadDim = 128;            // d supported by the kernels
+constexpr int kNTri = 43;                // ceil(128 / 3) triplets (Sec. 3.2)
+constexpr int kPadDim = 3 * kNTri;       // 129: u zero-padded to whole triplets
+constexpr float kEps = 1e-20f;           // the eps-safe divisor of Sec. 3.1 / 3.2
+constexpr int kWave = 64;
+
+// A codec with its bit split resolved (Sec. 3.3: B_tri = 2 b_dir + b_nrm).
+struct Codec {
+  int b_dir, b_nrm;     // bits per octahedral coordinate / per triplet norm
+  int K;                // 2^b_dir entries of C_xi
+  int R;                // 2^b_nrm entries of C_rho
+  int w_dir, w_nrm, w_qjl;  // 32-bit words per token of each stream
+  int qjl;
+  int rounding;
+  uint64_t seed;
+  const float* c_xi;
+  const float* c_rho;
+};
+
+// ---------------------------------------------------------------- host side
+// Thread-local message behind octo_last_error(); returns `s` for chaining.
+octo_status fail(octo_status s, const char* fmt, ...);
+void clear_error();
+// Validates a descriptor and resolves its split; nothing on the device is read.
+// need_tables: the codebook pointers must be set (every compute entry point).
+octo_status resolve_codec(const octo_codec_desc* desc, const char* what, Codec* out,
+                          bool need_tables = true);
+// Validates a cache view against a codec (pointers, sizes, alignment).
+octo_status check_cache(const octo_cache_view* v, const Codec& c, const char* what);
+// Maps the last HIP launch error to OCTO_ERR_HIP.
+octo_status check_launch(const char* what);
+
+inline int words_for_bits(int bits) { return (bits + 31) / 32; }
+
+// ---------------------------------------------------------------- device side
+// SplitMix64 output j of the generator started at `seed` (Steele, Lea and
+// Flood, OOPSLA 2014): the sign s_j of the rotation R = H diag(s) is -1 when
+// bit 63 is set.  j < d gives s, d <= j < 2d gives the QJL signs s'.
+__host__ __device__ inline float splitmix_sign(uint64_t seed, uint32_t j) {
+  uint64_t z = seed + (uint64_t)(j + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z = z ^ (z >> 31);
+  return (z >> 63) ? -1.0f : 1.0f;
+}
+
+// Unnormalized Walsh-Hadamard transform of a 128-vector held by one
+// wavefront, lane l owning coordinates l (a) and l + 64 (b).  Natural
+// (Sylvester) order: H[i][j] = (-1)^popcount(i & j).  The stride-64 butterfly
+// is lane-local, strides 32..1 exchange across lanes.
+__device__ inline void wht128(float& a, float& b) {
+  const int lane = threadIdx.x & 63;
+  float s = a + b, t = a - b;
+  a = s;
+  b = t;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    float pa = __shfl_xor(a, m, 64);
+    float pb = __shfl_xor(b, m, 64);
+    const bool upper = lane & m;
+    a = upper ? (pa - a) : (a + pa);
+    b = upper ? (pb - b) : (b + pb);
+  }
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits.
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Field of WIDTH bits at bit offset POS of a little-endian LSB-first stream
+// held in registers (POS and WIDTH become constants after unrolling).
+template <int WIDTH>
+__device__ inline uint32_t field(const uint32_t* w, int pos) {
+  const int wi = pos >> 5, sh = pos & 31;
+  uint32_t v = w[wi] >> sh;
+  if (sh + WIDTH > 32) v |= w[wi + 1] << (32 - sh);
+  return v & ((1u << WIDTH) - 1u);
+}
+
+// Word index of word `w` of token `t` in plane `plane` of a tile-64 stream
+// with W words per token: each 64-token tile stores W rows of 64 words.
+__host__ __device__ inline size_t tile_word(size_t plane, int capacity, int t, int w, int W) {
+  return ((plane * (size_t)(capacity >> 6) + (size_t)(t >> 6)) * (size_t)W + (size_t)w) * 64 +
+         (size_t)(t & 63);
+}
+
+}  // namespace octo

@@ -1,0 +1,167 @@
+"""C-ABI contract of liboctopus.so, on the host only (no kernel launch).
+
+Checks that the library loads, exports every function include/octopus.h
+declares, reports the record sizes of the bit splits (OCTOPUS paper Sec. 3.3:
+B_tri = 2 b_dir + b_nrm bits per triplet, 43 triplets at d = 128), and that
+every host-checkable error is reported before anything is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_decode_attention_octo_amd import binding as ob
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "octopus.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ob.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return ob.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(octo_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert {"octo_encode", "octo_attend_decode", "octo_attend_chunk"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.octo_abi_version() == ob.ABI_VERSION
+    for i, name in enumerate(ob.STATUS):
+        assert L.octo_status_string(i).decode() == name
+    assert L.octo_status_string(99).decode() == "OCTO_ERR_UNKNOWN"
+
+
+def desc(bits=3, b_dir=0, b_nrm=0, qjl=0, head_dim=128, version=ob.ABI_VERSION, tables=True,
+         rounding=0):
+    p = 4096 if tables else 0
+    return ob.CodecDesc(version, head_dim, bits, b_dir, b_nrm, rounding, qjl, 0, 0, p, p)
+
+
+# bytes per token of each stream with words padded to 4 B (dir, nrm) and the
+# QJL sketch of d = 128 bits
+@pytest.mark.parametrize("bits,bd,bn,dir_w,nrm_w", [
+    (4, 5, 3, 14, 5), (3, 4, 2, 11, 3), (2, 3, 1, 9, 2),
+    (4, 4, 4, 11, 6), (3, 3, 3, 9, 5), (2, 2, 2, 6, 3)])
+def test_record_sizes(L, bits, bd, bn, dir_w, nrm_w):
+    explicit = (bd, bn) != (bits + 1, bits - 1)
+    d = desc(bits, bd if explicit else 0, bn if explicit else 0, qjl=1, tables=False)
+    s = ob.octo_record_sizes(d)
+    assert (s.b_dir, s.b_nrm, s.n_triplets) == (bd, bn, 43)
+    assert s.dir_words == dir_w == -(-(2 * 43 * bd) // 32)
+    assert s.nrm_words == nrm_w == -(-(43 * bn) // 32)
+    assert s.qjl_words == 4
+
+
+def test_record_bytes_of_default_splits(L):
+    # K record = dir + nrm + gamma: 80 / 60 / 48 bytes at b = 4 / 3 / 2
+    for bits, nbytes in ((4, 80), (3, 60), (2, 48)):
+        s = ob.octo_record_sizes(desc(bits, tables=False))
+        assert 4 * (s.dir_words + s.nrm_words + 1) == nbytes
+
+
+def test_codec_errors(L):
+    out = ob.StreamSizes()
+    assert L.octo_record_sizes(None, ctypes.byref(out)) == 1
+    assert L.octo_record_sizes(ctypes.byref(desc(version=7)), ctypes.byref(out)) == 6
+    assert b"abi_version" in L.octo_last_error()
+    assert L.octo_record_sizes(ctypes.byref(desc(head_dim=96)), ctypes.byref(out)) == 1
+    assert L.octo_record_sizes(ctypes.byref(desc(head_dim=64)), ctypes.byref(out)) == 2
+    assert L.octo_record_sizes(ctypes.byref(desc(bits=6)), ctypes.byref(out)) == 2
+    assert L.octo_record_sizes(ctypes.byref(desc(b_dir=5, b_nrm=1)), ctypes.byref(out)) == 2
+    assert L.octo_record_sizes(ctypes.byref(desc(rounding=5)), ctypes.byref(out)) == 1
+    assert L.octo_record_sizes(ctypes.byref(desc(qjl=2)), ctypes.byref(out)) == 1
+    assert L.octo_record_sizes(ctypes.byref(desc()), ctypes.byref(out)) == 0
+    assert L.octo_last_error() == b""
+
+
+def view(B=1, H=1, cap=128, ptr=4096, layout=0, qjl=False):
+    q = ptr if qjl else None
+    return ob.CacheView(ptr, ptr, ptr, q, q, B, H, cap, layout)
+
+
+def enc(L, d, x, B, H, T, v, off, strides=(128 * 256, 128 * 256, 128, 1), dt=1):
+    s = (ctypes.c_int64 * 4)(*strides)
+    return L.octo_encode(ctypes.byref(d), x, dt, B, H, T, s, ctypes.byref(v) if v else None,
+                         off, None)
+
+
+def test_encode_errors(L):
+    d = desc()
+    x = ctypes.c_void_p(8192)
+    assert enc(L, desc(tables=False), x, 1, 1, 64, view(), 0) == 1
+    assert enc(L, d, x, 1, 1, 64, None, 0) == 1
+    assert enc(L, d, x, 1, 1, 64, view(cap=100), 0) == 1
+    assert enc(L, d, x, 1, 1, 64, view(layout=3), 0) == 1
+    assert enc(L, d, x, 1, 1, 64, view(ptr=4100), 0) == 3
+    assert enc(L, d, x, 2, 1, 64, view(), 0) == 1          # batch mismatch
+    assert enc(L, d, x, 1, 1, 64, view(cap=128), 100) == 4  # beyond capacity
+    assert enc(L, d, x, 1, 1, 64, view(), -1) == 1
+    assert enc(L, d, x, 1, 1, 64, view(), 0, dt=5) == 1
+    assert enc(L, d, x, 1, 1, 64, view(), 0, strides=(0, 0, 128, 2)) == 1
+    assert enc(L, d, ctypes.c_void_p(8193), 1, 1, 64, view(), 0) == 3
+    assert enc(L, desc(qjl=1), x, 1, 1, 64, view(), 0) == 1  # QJL needs its streams
+    assert enc(L, d, x, 1, 1, 0, view(), 0) == 0            # T = 0: nothing to do
+
+
+def dec(L, kd, vd, kv, vv, Hq=4, lens=4096, max_len=128, out=4096, ws=4096, ws_bytes=1 << 20,
+        q=4096, qdt=0):
+    return L.octo_attend_decode(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(kv),
+                                ctypes.byref(vv), q, qdt, Hq, lens, max_len, 0.0, out, ws,
+                                ws_bytes, None)
+
+
+def test_decode_errors(L):
+    kd, vd = desc(), desc()
+    kv, vv = view(H=2), view(H=2)
+    assert dec(L, kd, vd, kv, vv, ws_bytes=0) == 5
+    assert dec(L, kd, vd, kv, vv, ws=4097) == 3
+    assert dec(L, kd, vd, kv, vv, Hq=3) == 1                 # not a multiple of kv_heads
+    assert dec(L, kd, vd, kv, vv, Hq=6) == 2                 # G = 3 not compiled
+    assert dec(L, kd, vd, kv, vv, max_len=256) == 4          # beyond capacity
+    assert dec(L, kd, desc(qjl=1), kv, view(H=2, qjl=True)) == 2   # QJL values
+    assert dec(L, kd, desc(bits=2), kv, vv) == 2             # K/V split differ
+    assert dec(L, kd, vd, kv, view(H=3)) == 1                # K/V shapes differ
+    assert dec(L, kd, vd, kv, vv, q=None) == 1
+    assert dec(L, kd, vd, kv, vv, qdt=7) == 1
+    assert dec(L, kd, vd, kv, vv, lens=4098) == 3
+    n = ctypes.c_size_t()
+    assert L.octo_decode_workspace_bytes(ctypes.byref(kd), 1, 28, 4, 32768, ctypes.byref(n)) == 0
+    assert n.value >= 28 * 130 * 4
+    assert L.octo_decode_workspace_bytes(ctypes.byref(kd), 0, 28, 4, 32768, ctypes.byref(n)) == 1
+
+
+def test_chunk_errors(L):
+    kd, vd = desc(bits=2), desc(bits=2)
+    kv, vv = view(H=2, cap=256), view(H=2, cap=256)
+    n = ctypes.c_size_t()
+    assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, ctypes.byref(n)) == 0
+    need = n.value
+    # fp16 rotated queries [1, 2, 64, 128] and key / value rows [1, 2, 192, 128]
+    assert need == (64 * 2 + 2 * 2 * 192) * 256
+
+    def ch(kd=kd, vd=vd, kv=kv, vv=vv, cached=128, Hq=2, Tq=64, Tc=64, ws=4096, ws_bytes=need):
+        p = ctypes.c_void_p(4096)
+        return L.octo_attend_chunk(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(kv),
+                                   ctypes.byref(vv), cached, p, p, p, Hq, Tq, Tc, 0.0, p, ws,
+                                   ws_bytes, None)
+    assert ch(ws_bytes=need - 1) == 5
+    assert ch(ws=4352 + 1) == 3
+    assert ch(cached=300) == 4
+    assert ch(Hq=3) == 1
+    assert ch(Tq=-1) == 1
+    assert ch(kd=desc(bits=2, qjl=1), kv=view(H=2, cap=256, qjl=True)) == 2
+    assert ch(Tq=0) == 0                                     # nothing to do

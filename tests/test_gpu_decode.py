@@ -1,0 +1,132 @@
+"""GPU parity of octo_attend_decode against the oracle's float64 attention on
+the GPU-written packed cache (max-abs 2e-3).
+
+Small cases span several 64-token tiles, several splits and ragged tails;
+the full-size cases are the benchmark's configurations (all outputs for the
+32k-context and batched workloads, sampled planes at 128k context).  Edge
+cases: empty sequences, lengths clipped by max_seq_len, fp32 queries, every
+compiled GQA group size, determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_parity import ATOL, codecs, encode_gpu, make_inputs, oatt, octo, say, workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_case(w, T=None, seq_override=None, max_len=None, q_f32=False, planes=None):
+    inp = make_inputs(w, scale_T=T)
+    kc, hk = codecs(w.bits, qjl=w.qjl)
+    vc, hv = codecs(w.bits)
+    K, V, q = inp["K"], inp["V"], inp["q"]
+    seq = inp["seq_lens"].clone() if seq_override is None else torch.tensor(seq_override, dtype=torch.int32)
+    cap = -(-K.shape[2] // 64) * 64
+    kcache = encode_gpu(K, kc, capacity=cap)
+    vcache = encode_gpu(V, vc, capacity=cap)
+    qd = q.float() if q_f32 else q
+    out = octo.octo_attend_decode(kc, vc, kcache, vcache, qd.cuda(), seq.cuda(), max_len)
+    torch.cuda.synchronize()
+    out = out.cpu().double().numpy()
+    hkc, hvc = kcache.to_host(), vcache.to_host()
+    lens = seq.numpy().copy()
+    if max_len is not None:
+        lens = np.minimum(lens, max_len)
+    lens = np.clip(lens, 0, cap)
+    qn = qd.double().numpy()
+    if planes is None:
+        ref = oatt.decode_attention(qn, hkc, hvc, hk, hv, lens)
+        err = np.abs(out - ref).max()
+    else:
+        # only the query heads of the sampled (batch, kv head) planes
+        G = w.Hq // w.Hkv
+        err = 0.0
+        for b, g in planes:
+            ref = oatt.decode_attention(qn[b:b + 1, g * G:(g + 1) * G], _plane(hkc, b, g),
+                                        _plane(hvc, b, g), hk, hv, lens[b:b + 1])
+            err = max(err, np.abs(out[b, g * G:(g + 1) * G] - ref[0]).max())
+    return err, out, lens
+
+
+def _plane(h, b, g):
+    """The host cache of plane (b, g) alone (same layout with B = H = 1)."""
+    n = h["B"] * h["H"]
+    p = b * h["H"] + g
+    out = {"B": 1, "H": 1, "capacity": h["capacity"],
+           "dir": h["dir"].reshape(n, -1)[p], "nrm": h["nrm"].reshape(n, -1)[p],
+           "gamma": h["gamma"][b:b + 1, g:g + 1]}
+    if "qjl" in h:
+        out["qjl"] = h["qjl"].reshape(n, -1)[p]
+        out["gamma_r"] = h["gamma_r"][b:b + 1, g:g + 1]
+    return out
+
+
+@pytest.mark.parametrize("key,T", [("tiny", None), ("gqa32k", 1000), ("batch16", 777),
+                                   ("long128k", 1500)])
+def test_decode_small(key, T):
+    w = workload(key)
+    if key == "batch16":
+        w = workload(key, B=5, len_lo=1, len_hi=T)
+    say(f"decode {key} T={T}")
+    err, _, lens = run_case(w, T)
+    say(f"  lens {lens.tolist()} max-abs err {err:.3e}")
+    assert err <= ATOL
+
+
+@pytest.mark.parametrize("key", ["gqa32k", "batch16"])
+def test_decode_full_size(key):
+    w = workload(key)
+    say(f"decode full {key}")
+    err, _, lens = run_case(w)
+    say(f"  lens {lens.tolist()} max-abs err {err:.3e}")
+    assert err <= ATOL
+
+
+def test_decode_full_size_long_context_sampled():
+    w = workload("long128k")
+    say("decode full long128k (planes (0,0) and (3,3))")
+    err, _, _ = run_case(w, planes=[(0, 0), (3, 3)])
+    say(f"  max-abs err {err:.3e}")
+    assert err <= ATOL
+
+
+def test_decode_edge_lengths():
+    """Empty sequence -> zero row; max_seq_len clips the context; lengths that
+    end inside a tile and inside a split."""
+    w = workload("gqa32k", B=4)
+    err, out, lens = run_case(w, T=600, seq_override=[0, 1, 599, 600], max_len=590)
+    say(f"  edge lens {lens.tolist()} err {err:.3e}")
+    assert err <= ATOL
+    assert np.all(out[0] == 0.0)
+
+
+def test_decode_fp32_queries():
+    err, _, _ = run_case(workload("gqa32k"), T=300, q_f32=True)
+    assert err <= ATOL
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (4, 2), (8, 2), (16, 2), (7, 1)])
+def test_decode_group_sizes(Hq, Hkv):
+    w = workload("gqa32k", Hq=Hq, Hkv=Hkv, outliers=False)
+    err, _, _ = run_case(w, T=260)
+    assert err <= ATOL
+
+
+def test_decode_deterministic():
+    w = workload("gqa32k")
+    inp = make_inputs(w, scale_T=2000)
+    kc, _ = codecs(4)
+    vc, _ = codecs(4)
+    kcache = encode_gpu(inp["K"], kc)
+    vcache = encode_gpu(inp["V"], vc)
+    q, seq = inp["q"].cuda(), inp["seq_lens"].cuda()
+    a = octo.octo_attend_decode(kc, vc, kcache, vcache, q, seq).cpu()
+    b = octo.octo_attend_decode(kc, vc, kcache, vcache, q, seq).cpu()
+    assert torch.equal(a, b)

@@ -101,3 +101,26 @@ def test_approaches_exact_attention_and_empty_context():
     assert errs[0] > errs[1] > errs[2] and errs[2] < 0.05
     out = A.decode_attention(q, kk, vv, kc, vc, [0])
     assert np.all(out == 0)
+
+
+def test_chunk_edge_windows():
+    """No cached tokens: plain attention over the current chunk (SDPA); no
+    current tokens: attention over the reconstructed window; neither: zeros."""
+    K, V, kc, vc, kk, vv = build(2, B=1, H=1, T=40, cap=64)
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((1, 1, 3, 128))
+    kcur = rng.standard_normal((1, 1, 6, 128))
+    vcur = rng.standard_normal((1, 1, 6, 128))
+    out = A.chunk_attention(q, kk, vv, kc, vc, 0, kcur, vcur)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q[0]), torch.tensor(kcur[0]), torch.tensor(vcur[0]))
+    assert np.allclose(out[0], ref.numpy(), atol=1e-12)
+    empty = np.zeros((1, 1, 0, 128))
+    out = A.chunk_attention(q, kk, vv, kc, vc, 40, empty, empty)
+    kh, _ = A.reconstruct(kk, kc, 0, 0, 0, 40)
+    vh, _ = A.reconstruct(vv, vc, 0, 0, 0, 40)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q[0]), torch.tensor(kh)[None], torch.tensor(vh)[None])
+    assert np.allclose(out[0], ref.numpy(), atol=1e-12)
+    out = A.chunk_attention(q, kk, vv, kc, vc, 0, empty, empty)
+    assert np.all(out == 0)
