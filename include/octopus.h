@@ -23,9 +23,9 @@
  *     reduction; the split-K merge order is fixed).
  *   - Supported now: head_dim = 128; (b_dir, b_nrm) in {(3,1), (4,2), (5,3)}
  *     (the paper's (b+1, b-1) split for b = 2, 3, 4; Sec. 3.3) and the uniform
- *     splits {(2,2), (3,3), (4,4)}; for decode, query heads per KV head in
- *     {1, 2, 4, 7, 8}; QJL on keys only, in the decode path only.  Anything
- *     else returns OCTO_ERR_UNSUPPORTED.
+ *     splits {(2,2), (3,3), (4,4)}; for decode, 1 to 16 query heads per KV
+ *     head; QJL on keys only, in the decode path only.  Anything else returns
+ *     OCTO_ERR_UNSUPPORTED.
  *
  * Cache layout (OCTO_LAYOUT_TILE64).  The paper fixes no bit layout; this one
  * is this library's.  A stream is a little-endian LSB-first bit string: field
@@ -159,9 +159,13 @@ octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_codec, int32_t 
  *   seq_lens   device int32 [B].
  *   softmax_scale  <= 0 selects 1/sqrt(d).
  *   out        device fp32 [B, num_q_heads, d].
- *   workspace  device, >= octo_decode_workspace_bytes(...), 256-byte aligned.
- * K and V caches must share B, kv_heads, capacity and (b_dir, b_nrm);
- * V must not carry QJL.                                                      */
+ *   workspace  device, >= octo_decode_workspace_bytes(...), 256-byte aligned;
+ *              holds the per-split partial results (no state between calls).
+ *              Calls that share a workspace must not overlap in time.
+ * Both contractions run on MFMA with fp16 hi/lo operand pairs and fp32
+ * accumulation (about 2^-20 relative per product); softmax and the merge of
+ * the splits are fp32.  K and V caches must share B, kv_heads, capacity and
+ * (b_dir, b_nrm); V must not carry QJL.                                      */
 octo_status octo_attend_decode(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
                                const octo_cache_view* k_cache, const octo_cache_view* v_cache,
                                const void* q, octo_dtype q_dtype, int32_t num_q_heads,

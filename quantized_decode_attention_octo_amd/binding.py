@@ -198,7 +198,7 @@ def octo_decode_workspace_bytes(k_codec, B, num_q_heads, kv_heads, max_seq_len):
 
 
 def workspace(nbytes, device):
-    """A 256-byte aligned device buffer of at least nbytes."""
+    """A device buffer with at least nbytes from a 256-byte aligned start."""
     return torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
 
 

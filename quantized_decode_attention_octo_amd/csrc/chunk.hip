@@ -151,18 +151,29 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(ChunkArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;   // of query q0 + col
 
   const size_t kv_base = ((size_t)b * a.Hkv + hk) * a.Tk_pad * kHeadDim;
+  // The next tile is loaded into registers while the current one is used.
+  half8 kreg[4], vreg[4];
+  auto load_tile = [&](int kt0) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = it * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
+      const size_t g = kv_base + (size_t)(kt0 + row) * kHeadDim + c8;
+      kreg[it] = *reinterpret_cast<const half8*>(a.k + g);
+      vreg[it] = *reinterpret_cast<const half8*>(a.v + g);
+    }
+  };
+  if (a.Tk > 0) load_tile(0);
   for (int kt0 = 0; kt0 < a.Tk; kt0 += kBN) {
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int idx = it * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
-      const size_t g = kv_base + (size_t)(kt0 + row) * kHeadDim + c8;
-      *reinterpret_cast<half8*>(&ks[row * kKStride + c8]) = *reinterpret_cast<const half8*>(a.k + g);
-      const half8 vv = *reinterpret_cast<const half8*>(a.v + g);
+      *reinterpret_cast<half8*>(&ks[row * kKStride + c8]) = kreg[it];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(c8 + e) * kVStride + row] = vv[e];
+      for (int e = 0; e < 8; ++e) vt[(c8 + e) * kVStride + row] = vreg[it][e];
     }
     __syncthreads();
+    if (kt0 + kBN < a.Tk) load_tile(kt0 + kBN);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       floatx4 st[2];

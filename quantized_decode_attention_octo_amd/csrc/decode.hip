@@ -1,23 +1,42 @@
 // octo_attend_decode: single-query attention over the packed OCTOPUS cache.
 //
 // Split-K flash decoding (OCTOPUS paper, arXiv 2605.21226, Sec. 3.6 and the
-// App. A summary of the fused decode kernel): each workgroup scans one token
-// range ("split") of one (batch, KV head) plane for the G query heads that
-// share that KV head, and keeps a running maximum, normalizer and value sum
-// per head (online softmax).  A second kernel merges the splits by their
-// log-sum-exp and applies the inverse value rotation.
+// App. A summary of the fused decode kernel) with the two contractions on
+// the matrix cores.  Each workgroup scans one token range ("split") of one
+// (batch, KV head) plane for the G query heads sharing that KV head.  Keys
+// are never reconstructed in memory: each wavefront unpacks a 32-token block
+// straight into MFMA operand registers,
+//   u^_j = rho^_ji n^_ji   (Eq. 13: n^ from an LDS table of the decoded
+//                           direction of every code pair, rho^ from C_rho),
+// and the score of Eq. 13, gamma_j (R q) . u^_j, is one MFMA product of the
+// block's u^ with the rotated queries.  With QJL the estimator of Sec. 3.6,
+// gamma_j sqrt(pi/(2d)) gamma_r,j (R' R q) . sigma_j, is a second product
+// with sigma_j = +-1 as an exact fp16 operand.  Values stay in the rotated
+// frame: O += P (gamma_v u^_v), and R_v^T is applied once per head when the
+// splits are merged.
 //
-// Keys are never reconstructed in memory: the score of token j is the
-// factorized form of Eq. 13, gamma_j * sum_i rho^_ji (q_rot,i . n^_ji), with
-// q_rot = R q computed once per workgroup, n^ read from an LDS table of the
-// decoded direction of every code pair, and rho^ from C_rho.  With QJL the
-// estimator of Sec. 3.6, gamma_j sqrt(pi/(2d)) gamma_r,j (R' q_rot) . sigma_j,
-// is added.  Values are accumulated in the rotated frame,
-// acc += p_j gamma_v,j u^_v,j, and the merge applies R_v^T once per head.
+// Precision.  The operands are split as x = hi + lo with hi, lo in fp16
+// (hi = x rounded toward zero, lo = the fp32 residual rounded toward zero) and
+// every product is formed as hi*hi + hi*lo + lo*hi with fp32 accumulation,
+// about 2^-20 relative: single fp16 operands are not accurate enough for the
+// peaked softmax that outlier channels produce.  u^ is scaled by 64 (exact)
+// so that the residuals stay in the fp16 normal range.
 //
-// Lane mapping: the score phase puts one token on each lane; the value phase
-// puts one triplet (43 of the 64 lanes) on each lane and walks the 64 tokens
-// of the tile, whose packed words are staged in LDS.
+// MFMA lane layout of v_mfma_f32_16x16x32_f16 (L = lane):
+//   A[i][k]: i = L % 16, k-slot 8 (L / 16) + e;  B[k][j]: j = L % 16, same k
+//   D[i][j]: i = 4 (L / 16) + r, j = L % 16.
+// Scores are S^T = U Q^T (tokens as rows), so each lane ends up with 4 keys
+// of one query head, which is the A-operand layout P needs in O = P V.
+// Key-side coordinates: lane group g = L / 16 of token row t holds, for
+// call (grp, c), slot e = component c of triplet 32 grp + 4 e + g.
+// Value-side columns: tile (grp, c), column j = component c of triplet
+// 16 grp + j; slot e of lane group g = token 16 (e / 4) + 4 g + e % 4 of the
+// 32-token block, matching the score layout.
+//
+// A second launch merges the splits by their log-sum-exp in split order and
+// applies R_v^T, so results do not depend on scheduling.  (Merging inside the
+// first launch needs device-scope fences, which on this chip write back and
+// invalidate a whole L2 per workgroup and cost far more than a launch.)
 #include <math.h>
 
 #include "octo_internal.h"
@@ -25,15 +44,23 @@
 namespace octo {
 namespace {
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kSplitQuantum = 256;   // split lengths are multiples of this
-constexpr int kTargetBlocks = 1024;  // about four workgroups per CU
+constexpr int kBlock = 32;            // tokens per wavefront iteration
+constexpr int kSplitQuantum = 128;    // split lengths are multiples of this
+constexpr int kMaxG = 16;             // query heads per KV head (MFMA columns)
+constexpr float kUScale = 64.0f;      // exact scale of u^ in the operands
+constexpr float kInvSqrtD = 0.08838834764831845f;
+constexpr int kStageStride = 33;      // words per staged row (32 tokens + pad)
 
 struct DecodeArgs {
   const void* q;
   int q_bf16;
-  int B, Hq, Hkv;
+  int B, Hq, Hkv, G;
   const int* seq_lens;
   int max_len;
   float scale;
@@ -44,8 +71,9 @@ struct DecodeArgs {
   const uint16_t* kgamma_r;
   int capacity;
   int n_split, split_len;
-  float2* ws_ml;   // [B][Hq][n_split] (running max, normalizer)
-  float* ws_acc;   // [B][Hq][n_split][128] rotated-frame value sums
+  float2* ws_ml;       // [B][Hq][n_split] (running max, normalizer)
+  float* ws_acc;       // [B][Hq][n_split][128] rotated-frame value sums (x64)
+  float* out;          // [B][Hq][128]
 };
 
 __device__ inline void wave_sync() {
@@ -54,37 +82,60 @@ __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// x = hi + lo for 8 slots: hi rounded toward zero to fp16, lo the residual.
+__device__ inline void split8(const float* x, half8& hi, half8& lo) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(x[2 * k], x[2 * k + 1]);
+    const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(x[2 * k] - (float)h.x, x[2 * k + 1] - (float)h.y);
+    hi[2 * k] = (_Float16)h.x;
+    hi[2 * k + 1] = (_Float16)h.y;
+    lo[2 * k] = (_Float16)l.x;
+    lo[2 * k + 1] = (_Float16)l.y;
+  }
+}
+
+__device__ inline floatx4 mfma(const half8& a, const half8& b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// hi*hi + hi*lo + lo*hi
+__device__ inline floatx4 mfma3(const half8& ah, const half8& al, const half8& bh,
+                                const half8& bl, floatx4 c) {
+  c = mfma(al, bh, c);
+  c = mfma(ah, bl, c);
+  return mfma(ah, bh, c);
+}
+
 __device__ inline float4 decode_dir(float xi, float eta) {
-  // Eq. 6 / App. C.7: unfold, then normalize onto S^2.
+  // Eq. 6 / App. C.7: unfold, normalize onto S^2; scaled by 64.
   const float z = 1.0f - fabsf(xi) - fabsf(eta);
   float x = xi, y = eta;
   if (z < 0.0f) {
     x = (xi >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(eta));
     y = (eta >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(xi));
   }
-  const float n = fmaxf(sqrtf(x * x + y * y + z * z), kEps);
-  return make_float4(x / n, y / n, z / n, 0.0f);
+  const float n = kUScale / fmaxf(sqrtf(x * x + y * y + z * z), kEps);
+  return make_float4(x * n, y * n, z * n, 0.0f);
 }
 
-template <int BD, int BN, int G, bool QJL>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
-  constexpr int K = 1 << BD, R = 1 << BN;
-  constexpr int FWD = 2 * BD;
+template <int BD, int BN, bool QJL>
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
+  constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD;
   constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32, WV = WD + WN;
-  constexpr int kStage = 65;                       // padded row of staged words
-  constexpr int kStageWords = kWaves * WV * kStage;
-  constexpr int kRedWords = kWaves * G * 2 + kWaves * G * kPadDim;
-  constexpr int kUnion = kStageWords > kRedWords ? kStageWords : kRedWords;
+  constexpr uint32_t kDirMask = (1u << FWD) - 1u, kNrmMask = (1u << BN) - 1u;
 
   __shared__ float4 lutk[K * K], lutv[K * K];
-  __shared__ float crk[R], crv[R];
-  __shared__ float4 qrot[G * kNTri];               // (R q)_i triplets, pad coordinate 0
-  __shared__ float qprime[QJL ? G * kHeadDim : 1]; // R' R q
-  __shared__ float pbuf[kWaves * 64 * 8];          // p_h * gamma_v per token
-  __shared__ uint32_t uni[kUnion];                 // staged V words, later the reduction
+  __shared__ float crk[R], crv[R], cxk[K], cxv[K];
+  __shared__ float qs[kMaxG * 132];                      // R q, then R' R q (QJL)
+  __shared__ uint32_t stage[kWaves * WV * kStageStride];  // value words of a block
+  __shared__ float red_ml[kWaves * kMaxG * 2];
+  __shared__ float red_o[kWaves * 8 * kHeadDim];          // [wave][8 heads][128]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
+  const int col = L & 15, grp4 = L >> 4;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = a.G;
   const size_t plane = (size_t)b * a.Hkv + g;
 
   int len = a.seq_lens[b];
@@ -92,221 +143,366 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int t_begin = split * a.split_len;
   const int t_end = min(len, t_begin + a.split_len);
 
-  // ---- tables
-  for (int e = tid; e < K * K; e += kThreads) {
-    lutk[e] = decode_dir(a.kc_xi[e % K], a.kc_xi[e / K]);
-    lutv[e] = decode_dir(a.vc_xi[e % K], a.vc_xi[e / K]);
+  // ---- tables: codebooks to LDS first, then the decoded directions
+  if (tid < K) {
+    cxk[tid] = a.kc_xi[tid];
+    cxv[tid] = a.vc_xi[tid];
   }
   if (tid < R) {
     crk[tid] = a.kc_rho[tid];
     crv[tid] = a.vc_rho[tid];
   }
-  // ---- query rotation q_rot = H diag(s) q / sqrt(d) (Sec. 3.1, Eq. 13)
-  float* qr_flat = reinterpret_cast<float*>(uni);  // scratch before the loop
-  for (int hh = wave; hh < G; hh += kWaves) {
-    const size_t qo = ((size_t)b * a.Hq + (size_t)g * G + hh) * kHeadDim;
-    float q0, q1;
-    if (a.q_bf16) {
-      q0 = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qo + lane]);
-      q1 = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qo + lane + 64]);
-    } else {
-      q0 = static_cast<const float*>(a.q)[qo + lane];
-      q1 = static_cast<const float*>(a.q)[qo + lane + 64];
+  // q of this wave's heads, all loads issued before any use
+  constexpr int kHeadsPerWave = kMaxG / kWaves;
+  float qv[kHeadsPerWave][2];
+#pragma unroll
+  for (int k = 0; k < kHeadsPerWave; ++k) {
+    const int hh = wave + kWaves * k;
+    qv[k][0] = qv[k][1] = 0.0f;
+    if (hh < G) {
+      const size_t qo = ((size_t)b * a.Hq + (size_t)g * G + hh) * kHeadDim;
+      if (a.q_bf16) {
+        qv[k][0] = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qo + L]);
+        qv[k][1] = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qo + L + 64]);
+      } else {
+        qv[k][0] = static_cast<const float*>(a.q)[qo + L];
+        qv[k][1] = static_cast<const float*>(a.q)[qo + L + 64];
+      }
     }
-    q0 *= splitmix_sign(a.kseed, lane);
-    q1 *= splitmix_sign(a.kseed, lane + 64);
+  }
+  __syncthreads();
+  for (int e = tid; e < K * K; e += kThreads) {
+    lutk[e] = decode_dir(cxk[e % K], cxk[e / K]);
+    lutv[e] = decode_dir(cxv[e % K], cxv[e / K]);
+  }
+  // ---- q_rot = H diag(s) q / sqrt(d) for the G heads (rows >= G are zero)
+  const float s_lo = splitmix_sign(a.kseed, L), s_hi = splitmix_sign(a.kseed, L + 64);
+#pragma unroll
+  for (int k = 0; k < kHeadsPerWave; ++k) {
+    const int hh = wave + kWaves * k;
+    float q0 = qv[k][0] * s_lo, q1 = qv[k][1] * s_hi;
     wht128(q0, q1);
-    q0 *= 0.08838834764831845f;
-    q1 *= 0.08838834764831845f;
-    qr_flat[hh * 132 + lane] = q0;
-    qr_flat[hh * 132 + lane + 64] = q1;
-    if (lane == 0) qr_flat[hh * 132 + 128] = 0.0f;
-    if (QJL) {
-      float p0 = q0 * splitmix_sign(a.kseed, kHeadDim + lane);
-      float p1 = q1 * splitmix_sign(a.kseed, kHeadDim + lane + 64);
+    qs[hh * 132 + L] = q0 * kInvSqrtD;
+    qs[hh * 132 + L + 64] = q1 * kInvSqrtD;
+    if (L < 4) qs[hh * 132 + 128 + L] = 0.0f;   // pad coordinate 128 (and slack)
+  }
+  __syncthreads();
+
+  // Q^T operands (B): column col = head, call (grp, c), slot e = component c
+  // of triplet 32 grp + 4 e + grp4 (zero beyond the 128 real coordinates).
+  half8 qh[2][3], ql[2][3];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tri = 32 * gi + 4 * e + grp4;
+        const int coord = 3 * tri + c;
+        x[e] = coord < kHeadDim ? qs[col * 132 + coord] : 0.0f;
+      }
+      split8(x, qh[gi][c], ql[gi][c]);
+    }
+  // QJL operands: call k, slot e of group grp4 = bit 32 k + 8 grp4 + e.
+  half8 ph[QJL ? 4 : 1], pl[QJL ? 4 : 1];
+  if (QJL) {
+    __syncthreads();
+    for (int hh = wave; hh < kMaxG; hh += kWaves) {
+      float p0 = qs[hh * 132 + L] * splitmix_sign(a.kseed, kHeadDim + L);
+      float p1 = qs[hh * 132 + L + 64] * splitmix_sign(a.kseed, kHeadDim + L + 64);
       wht128(p0, p1);
-      qprime[hh * kHeadDim + lane] = p0 * 0.08838834764831845f;
-      qprime[hh * kHeadDim + lane + 64] = p1 * 0.08838834764831845f;
+      wave_sync();
+      qs[hh * 132 + L] = p0 * kInvSqrtD;
+      qs[hh * 132 + L + 64] = p1 * kInvSqrtD;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < (QJL ? 4 : 1); ++k) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = qs[col * 132 + 32 * k + 8 * grp4 + e];
+      split8(x, ph[k], pl[k]);
     }
   }
-  __syncthreads();
-  for (int e = tid; e < G * kNTri; e += kThreads) {
-    const int hh = e / kNTri, i = e - hh * kNTri;
-    const float* src = &qr_flat[hh * 132 + 3 * i];
-    qrot[e] = make_float4(src[0], src[1], src[2], 0.0f);
-  }
-  __syncthreads();
 
-  // ---- main loop: wave w takes tiles w, w+4, ... of the split
-  float m_run[G], l_run[G], acc[G][3];
+  // ---- main loop: wave w takes blocks w, w+4, ... of the split
+  floatx4 o[3][3];                                   // value tiles (grp, c)
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.0f;
-    acc[h][0] = acc[h][1] = acc[h][2] = 0.0f;
-  }
-  uint32_t* stage = &uni[wave * WV * kStage];
-  float* pb = &pbuf[wave * 64 * 8];
-  const float qjl_c = 1.2533141373155003f * 0.08838834764831845f;  // sqrt(pi/2) / sqrt(d)
-  const int tri = lane < kNTri ? lane : kNTri - 1;
-  const int dpos = tri * FWD, npos = tri * BN;
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) o[i][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;            // of head `col`
+  uint32_t* st = &stage[wave * WV * kStageStride];
+  const float qjl_c = 1.2533141373155003f * kInvSqrtD;   // sqrt(pi / 2) / sqrt(d)
 
-  for (int t0 = t_begin + wave * 64; t0 < t_end; t0 += kWaves * 64) {
-    const int t = t0 + lane;
-    const bool valid = t < t_end;
-    const int tl = valid ? t : t0;  // in-bounds token for the loads
-    // -- score phase: one token per lane
-    uint32_t dw[WD], nw[WN > 0 ? WN : 1];
+  // value-side positions of this lane's triplets 16 grp + col
+  int vdw[3], vdsh[3], vnw[3], vnsh[3];
 #pragma unroll
-    for (int w = 0; w < WD; ++w) dw[w] = a.kdir[tile_word(plane, a.capacity, tl, w, WD)];
+  for (int i = 0; i < 3; ++i) {
+    const int tri = min(16 * i + col, kNTri - 1);
+    vdw[i] = (tri * FWD) >> 5;
+    vdsh[i] = (tri * FWD) & 31;
+    vnw[i] = WD + ((tri * BN) >> 5);
+    vnsh[i] = (tri * BN) & 31;
+  }
+
+  for (int t0 = t_begin + wave * kBlock; t0 < t_end; t0 += kWaves * kBlock) {
+    // -- stage the block's value words (word w of 32 tokens is 128 B)
+    for (int e = L; e < WV * kBlock; e += 64) {
+      const int w = e >> 5, tk = e & 31;
+      st[w * kStageStride + tk] =
+          w < WD ? a.vdir[tile_word(plane, a.capacity, t0 + tk, w, WD)]
+                 : a.vnrm[tile_word(plane, a.capacity, t0 + tk, w - WD, WN)];
+    }
+    // -- scores, two 16-token tiles
+    floatx4 sc[2];
 #pragma unroll
-    for (int w = 0; w < WN; ++w) nw[w] = a.knrm[tile_word(plane, a.capacity, tl, w, WN)];
-    const float gk = a.kgamma[plane * a.capacity + tl];
-    const float gv = a.vgamma[plane * a.capacity + tl];
-    float dot[G];
+    for (int kt = 0; kt < 2; ++kt) {
+      const int tok = t0 + 16 * kt + col;
+      uint32_t dw[WD + 1], nw[WN + 1];
 #pragma unroll
-    for (int h = 0; h < G; ++h) dot[h] = 0.0f;
+      for (int w = 0; w < WD; ++w) dw[w] = a.kdir[tile_word(plane, a.capacity, tok, w, WD)];
 #pragma unroll
-    for (int i = 0; i < kNTri; ++i) {
-      const float4 n = lutk[field<FWD>(dw, i * FWD)];
-      const float rho = crk[field<BN>(nw, i * BN)];
-      const float ux = rho * n.x, uy = rho * n.y, uz = rho * n.z;
+      for (int w = 0; w < WN; ++w) nw[w] = a.knrm[tile_word(plane, a.capacity, tok, w, WN)];
+      dw[WD] = 0u;
+      nw[WN] = 0u;
+      // shift the record so that triplet 4 e + grp4 starts at bit 4 e FWD
+      const uint32_t dsh = grp4 * FWD, nsh = grp4 * BN;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float4 qv = qrot[h * kNTri + i];
-        dot[h] = fmaf(qv.x, ux, fmaf(qv.y, uy, fmaf(qv.z, uz, dot[h])));
+      for (int w = 0; w < WD; ++w) dw[w] = __builtin_amdgcn_alignbit(dw[w + 1], dw[w], dsh);
+#pragma unroll
+      for (int w = 0; w < WN; ++w) nw[w] = __builtin_amdgcn_alignbit(nw[w + 1], nw[w], nsh);
+      floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        float ux[8], uy[8], uz[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tri = 32 * gi + 4 * e;       // relative triplet index
+          if (gi == 1 && e >= 3) {
+            ux[e] = uy[e] = uz[e] = 0.0f;
+            continue;
+          }
+          const float4 n = lutk[field<FWD>(dw, tri * FWD)];
+          const float rho = crk[field<BN>(nw, tri * BN)];
+          ux[e] = rho * n.x;
+          uy[e] = rho * n.y;
+          uz[e] = rho * n.z;
+        }
+        half8 ah, al;
+        split8(ux, ah, al);
+        acc = mfma3(ah, al, qh[gi][0], ql[gi][0], acc);
+        split8(uy, ah, al);
+        acc = mfma3(ah, al, qh[gi][1], ql[gi][1], acc);
+        split8(uz, ah, al);
+        acc = mfma3(ah, al, qh[gi][2], ql[gi][2], acc);
+      }
+      // this lane's 4 tokens: t0 + 16 kt + 4 grp4 + r, head col
+      const int tb = t0 + 16 * kt + 4 * grp4;
+      const float4 gk = *reinterpret_cast<const float4*>(&a.kgamma[plane * a.capacity + tb]);
+      const float gka[4] = {gk.x, gk.y, gk.z, gk.w};
+      float s4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s4[r] = acc[r] * (1.0f / kUScale);
+      if (QJL) {
+        uint32_t sw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sw[k] = a.kqjl[tile_word(plane, a.capacity, tok, k, 4)];
+        floatx4 qa = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // sigma_j = -1 where the bit is set: fp16 +-1 = 0x3C00 | bit << 15
+          const uint32_t byte = (sw[k] >> (8 * grp4)) & 0xffu;
+          half8 sg;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            sg[e] = ((byte >> e) & 1u) ? (_Float16)-1.0f : (_Float16)1.0f;
+          qa = mfma(sg, pl[k], qa);
+          qa = mfma(sg, ph[k], qa);
+        }
+        const uint16_t* grp_r = &a.kgamma_r[plane * a.capacity + tb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s4[r] += qjl_c * (float)__builtin_bit_cast(_Float16, grp_r[r]) * qa[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool valid = tb + r < t_end;
+        sc[kt][r] = valid ? s4[r] * gka[r] * a.scale : -INFINITY;
       }
     }
-    float s[G];
+    // -- online softmax over the 32 tokens, head col (Sec. 3.6 / App. A)
+    float mx = -INFINITY;
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = dot[h] * gk;
-    if (QJL) {
-      uint32_t sw[4];
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) sw[w] = a.kqjl[tile_word(plane, a.capacity, tl, w, 4)];
-      const float gr = (float)__builtin_bit_cast(_Float16, a.kgamma_r[plane * a.capacity + tl]);
-      float qs[G];
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_run == m_new ? 1.0f : __expf(m_run - m_new);
+    float pw[8], psum = 0.0f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) qs[h] = 0.0f;
+    for (int kt = 0; kt < 2; ++kt) {
+      const int tb = t0 + 16 * kt + 4 * grp4;
+      const float4 gv = *reinterpret_cast<const float4*>(&a.vgamma[plane * a.capacity + tb]);
+      const float gva[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-      for (int j = 0; j < kHeadDim; ++j) {
-        const float sg = ((sw[j >> 5] >> (j & 31)) & 1u) ? -1.0f : 1.0f;
-#pragma unroll
-        for (int h = 0; h < G; ++h) qs[h] = fmaf(sg, qprime[h * kHeadDim + j], qs[h]);
+      for (int r = 0; r < 4; ++r) {
+        const float p = sc[kt][r] == -INFINITY ? 0.0f : __expf(sc[kt][r] - m_new);
+        psum += p;
+        pw[4 * kt + r] = p * gva[r];
       }
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[h] += gk * qjl_c * gr * qs[h];
     }
-    // -- online softmax over the tile (Sec. 3.6 / App. A: split-K decoding)
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    half8 pah, pal;
+    split8(pw, pah, pal);
+    // rescale O rows (heads 4 grp4 + r)
+    float al[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float sc = valid ? s[h] * a.scale : -INFINITY;
-      const float m_new = fmaxf(m_run[h], wave_max(sc));
-      const float alpha = m_run[h] == -INFINITY ? 0.0f : __expf(m_run[h] - m_new);
-      const float p = valid ? __expf(sc - m_new) : 0.0f;
-      l_run[h] = l_run[h] * alpha + wave_sum(p);
-      m_run[h] = m_new;
-      acc[h][0] *= alpha;
-      acc[h][1] *= alpha;
-      acc[h][2] *= alpha;
-      pb[lane * 8 + h] = p * gv;
-    }
-    // -- stage the tile's V words (coalesced), then the value phase
+    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp4 + r, 64);
 #pragma unroll
-    for (int w = 0; w < WD; ++w) stage[w * kStage + lane] = a.vdir[tile_word(plane, a.capacity, tl, w, WD)];
+    for (int i = 0; i < 3; ++i)
 #pragma unroll
-    for (int w = 0; w < WN; ++w)
-      stage[(WD + w) * kStage + lane] = a.vnrm[tile_word(plane, a.capacity, tl, w, WN)];
+      for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[i][c][r] *= al[r];
+    // -- values: triplet 16 grp + col for this lane group's 8 tokens
     wave_sync();
-    const int nt = min(64, t_end - t0);
-    if (lane < kNTri) {
-      const int dwi = dpos >> 5, dsh = dpos & 31;
-      const int dwi1 = min(dwi + 1, WD - 1);
-      const int nwi = WD + (npos >> 5), nsh = npos & 31;
-      const int nwi1 = min(nwi + 1, WV - 1);
-      for (int k = 0; k < nt; ++k) {
-        const uint64_t dwd = (uint64_t)stage[dwi * kStage + k] |
-                             ((uint64_t)stage[dwi1 * kStage + k] << 32);
-        const uint64_t nwd = (uint64_t)stage[nwi * kStage + k] |
-                             ((uint64_t)stage[nwi1 * kStage + k] << 32);
-        const float4 n = lutv[(uint32_t)(dwd >> dsh) & ((1u << FWD) - 1u)];
-        const float rho = crv[(uint32_t)(nwd >> nsh) & ((1u << BN) - 1u)];
-        const float vx = rho * n.x, vy = rho * n.y, vz = rho * n.z;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = pb[k * 8 + h];
-          acc[h][0] = fmaf(p, vx, acc[h][0]);
-          acc[h][1] = fmaf(p, vy, acc[h][1]);
-          acc[h][2] = fmaf(p, vz, acc[h][2]);
+    for (int i = 0; i < 3; ++i) {
+      float vx[8], vy[8], vz[8];
+      const bool tri_ok = 16 * i + col < kNTri;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tk = 16 * (e >> 2) + 4 * grp4 + (e & 3);
+        const uint32_t d0 = st[vdw[i] * kStageStride + tk];
+        const uint32_t d1 = st[min(vdw[i] + 1, WV - 1) * kStageStride + tk];
+        const uint32_t n0 = st[vnw[i] * kStageStride + tk];
+        const uint32_t n1 = st[min(vnw[i] + 1, WV - 1) * kStageStride + tk];
+        const uint32_t code = __builtin_amdgcn_alignbit(d1, d0, vdsh[i]) & kDirMask;
+        const uint32_t ir = __builtin_amdgcn_alignbit(n1, n0, vnsh[i]) & kNrmMask;
+        const float4 n = lutv[code];
+        const float rho = tri_ok ? crv[ir] : 0.0f;
+        vx[e] = rho * n.x;
+        vy[e] = rho * n.y;
+        vz[e] = rho * n.z;
+      }
+      half8 bh, bl;
+      split8(vx, bh, bl);
+      o[i][0] = mfma3(pah, pal, bh, bl, o[i][0]);
+      split8(vy, bh, bl);
+      o[i][1] = mfma3(pah, pal, bh, bl, o[i][1]);
+      split8(vz, bh, bl);
+      o[i][2] = mfma3(pah, pal, bh, bl, o[i][2]);
+    }
+    wave_sync();
+  }
+
+  // ---- merge the waves: partial (m, l, O) of this split
+  __syncthreads();
+  for (int h0 = 0; h0 < G; h0 += 8) {              // eight heads at a time
+
+    const int hn = min(8, G - h0);
+    if (grp4 == 0 && col >= h0 && col < h0 + hn) {
+      red_ml[(wave * kMaxG + col) * 2] = m_run;
+      red_ml[(wave * kMaxG + col) * 2 + 1] = l_run;
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        const int coord = 3 * (16 * i + col) + c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * grp4 + r;
+          if (coord < kHeadDim && h >= h0 && h < h0 + hn)
+            red_o[(wave * 8 + (h - h0)) * kHeadDim + coord] = o[i][c][r];
         }
       }
-    }
-    wave_sync();
-  }
-
-  // ---- merge the four waves and write this split's partials
-  __syncthreads();
-  float* red_ml = reinterpret_cast<float*>(uni);           // [wave][G][2]
-  float* red_acc = red_ml + kWaves * G * 2;                 // [wave][G][129]
+    __syncthreads();
+    for (int e = tid; e < hn * kHeadDim; e += kThreads) {
+      const int hl = e >> 7, c = e & 127, h = h0 + hl;
+      float M = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (lane == 0) {
-      red_ml[(wave * G + h) * 2] = m_run[h];
-      red_ml[(wave * G + h) * 2 + 1] = l_run[h];
-    }
-    if (lane < kNTri) {
-      float* dst = &red_acc[(wave * G + h) * kPadDim + 3 * lane];
-      dst[0] = acc[h][0];
-      dst[1] = acc[h][1];
-      dst[2] = acc[h][2];
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < G * kHeadDim; e += kThreads) {
-    const int h = e >> 7, c = e & 127;
-    float M = -INFINITY;
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[(w * kMaxG + h) * 2]);
+      float Lsum = 0.0f, A = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[(w * G + h) * 2]);
-    float L = 0.0f, A = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = red_ml[(w * G + h) * 2];
-      const float f = mw == -INFINITY ? 0.0f : __expf(mw - M);
-      L += f * red_ml[(w * G + h) * 2 + 1];
-      A += f * red_acc[(w * G + h) * kPadDim + c];
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = red_ml[(w * kMaxG + h) * 2];
+        const float f = mw == -INFINITY ? 0.0f : __expf(mw - M);
+        Lsum += f * red_ml[(w * kMaxG + h) * 2 + 1];
+        A += f * red_o[(w * 8 + hl) * kHeadDim + c];
+      }
+      const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_split + split;
+      a.ws_acc[row * kHeadDim + c] = A;
+      if (c == 0) a.ws_ml[row] = make_float2(M, Lsum);
     }
-    const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_split + split;
-    a.ws_acc[row * kHeadDim + c] = A;
-    if (c == 0) a.ws_ml[row] = make_float2(M, L);
+    __syncthreads();
   }
 }
 
-// Merges the splits of one (batch, query head) and applies R_v^T = diag(s) H.
-__global__ __launch_bounds__(64) void decode_merge_kernel(const float2* ws_ml, const float* ws_acc,
-                                                          int n_split, int Hq, uint64_t vseed,
-                                                          float* out) {
-  const int lane = threadIdx.x;
+// Merges the splits of one (batch, query head) by their log-sum-exp, in split
+// order, and applies R_v^T = diag(s_v) H / sqrt(d).  Four wavefronts take the
+// splits round-robin; the partial sums meet in LDS.
+__global__ __launch_bounds__(256) void merge_kernel(const float2* __restrict__ ws_ml,
+                                                    const float* __restrict__ ws_acc,
+                                                    int n_split, int Hq, uint64_t vseed,
+                                                    float* __restrict__ out) {
+  __shared__ float part[kWaves][2 * 64 + 1];
+  const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
   const size_t row0 = ((size_t)blockIdx.y * Hq + blockIdx.x) * n_split;
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, ws_ml[row0 + s].x);
-  float L = 0.0f, a0 = 0.0f, a1 = 0.0f;
+  for (int s0 = 0; s0 < n_split; s0 += 64) {
+    const int s = s0 + L;
+    M = fmaxf(M, s < n_split ? ws_ml[row0 + s].x : -INFINITY);
+  }
+  M = wave_max(M);
+  float Lsum = 0.0f, a0 = 0.0f, a1 = 0.0f;
   if (M != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float2 ml = ws_ml[row0 + s];
-      if (ml.x == -INFINITY) continue;
-      const float f = __expf(ml.x - M);
-      L += f * ml.y;
-      a0 += f * ws_acc[(row0 + s) * kHeadDim + lane];
-      a1 += f * ws_acc[(row0 + s) * kHeadDim + lane + 64];
+    for (int s0 = wave; s0 < n_split; s0 += 4 * kWaves) {
+      float2 ml[4];
+      float x0[4], x1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = min(s0 + u * kWaves, n_split - 1);
+        ml[u] = ws_ml[row0 + s];
+        x0[u] = ws_acc[(row0 + s) * kHeadDim + L];
+        x1[u] = ws_acc[(row0 + s) * kHeadDim + L + 64];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool in = s0 + u * kWaves < n_split && ml[u].x != -INFINITY;
+        const float f = in ? __expf(ml[u].x - M) : 0.0f;
+        Lsum += f * ml[u].y;
+        a0 += f * x0[u];
+        a1 += f * x1[u];
+      }
     }
   }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  a0 *= inv;
-  a1 *= inv;
-  wht128(a0, a1);
+  part[wave][L] = a0;
+  part[wave][64 + L] = a1;
+  if (L == 0) part[wave][128] = Lsum;
+  __syncthreads();
+  if (wave != 0) return;
+  float t0 = 0.0f, t1 = 0.0f, tl = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    t0 += part[w][L];
+    t1 += part[w][64 + L];
+    tl += part[w][128];
+  }
+  const float inv = tl > 0.0f ? 1.0f / (tl * kUScale) : 0.0f;
+  t0 *= inv;
+  t1 *= inv;
+  wht128(t0, t1);
   const size_t o = ((size_t)blockIdx.y * Hq + blockIdx.x) * kHeadDim;
-  out[o + lane] = a0 * 0.08838834764831845f * splitmix_sign(vseed, lane);
-  out[o + lane + 64] = a1 * 0.08838834764831845f * splitmix_sign(vseed, lane + 64);
+  out[o + L] = t0 * kInvSqrtD * splitmix_sign(vseed, L);
+  out[o + L + 64] = t1 * kInvSqrtD * splitmix_sign(vseed, L + 64);
 }
 
 struct Plan {
@@ -317,7 +513,8 @@ struct Plan {
 Plan make_plan(int B, int Hq, int Hkv, int max_len) {
   Plan p;
   const int units = B * Hkv;
-  const int per_unit = max(1, kTargetBlocks / max(1, units));
+  const int target_blocks = 512;                 // two workgroups per CU
+  const int per_unit = max(1, target_blocks / max(1, units));
   int sl = (max(max_len, 1) + per_unit - 1) / per_unit;
   sl = (sl + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
   p.split_len = max(sl, kSplitQuantum);
@@ -329,25 +526,13 @@ Plan make_plan(int B, int Hq, int Hkv, int max_len) {
   return p;
 }
 
-template <int BD, int BN, int G>
-void launch_g(const DecodeArgs& a, bool qjl, hipStream_t st) {
+template <int BD, int BN>
+void launch(const DecodeArgs& a, bool qjl, hipStream_t st) {
   dim3 grid(a.n_split, a.Hkv, a.B);
   if (qjl)
-    hipLaunchKernelGGL((decode_split_kernel<BD, BN, G, true>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<BD, BN, true>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<BD, BN, G, false>), grid, dim3(kThreads), 0, st, a);
-}
-
-template <int BD, int BN>
-bool launch_split(const DecodeArgs& a, int G, bool qjl, hipStream_t st) {
-  switch (G) {
-    case 1: launch_g<BD, BN, 1>(a, qjl, st); return true;
-    case 2: launch_g<BD, BN, 2>(a, qjl, st); return true;
-    case 4: launch_g<BD, BN, 4>(a, qjl, st); return true;
-    case 7: launch_g<BD, BN, 7>(a, qjl, st); return true;
-    case 8: launch_g<BD, BN, 8>(a, qjl, st); return true;
-  }
-  return false;
+    hipLaunchKernelGGL((decode_kernel<BD, BN, false>), grid, dim3(kThreads), 0, st, a);
 }
 
 }  // namespace
@@ -411,13 +596,14 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: %d query heads on %d KV heads", what,
                 num_q_heads, Hkv);
   const int G = num_q_heads / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 7 && G != 8)
-    return fail(OCTO_ERR_UNSUPPORTED, "%s: %d query heads per KV head not compiled", what, G);
+  if (G > kMaxG)
+    return fail(OCTO_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most %d)", what, G,
+                kMaxG);
   if (max_seq_len < 0 || max_seq_len > k_cache->capacity)
     return fail(OCTO_ERR_CAPACITY, "%s: max_seq_len %d outside [0, capacity %d]", what,
                 max_seq_len, k_cache->capacity);
-  if (B > 65535 || Hkv > 65535)
-    return fail(OCTO_ERR_UNSUPPORTED, "%s: batch and kv_heads must be <= 65535", what);
+  if (B > 65535 || Hkv > 65535 || num_q_heads > 65535)
+    return fail(OCTO_ERR_UNSUPPORTED, "%s: batch and heads must be <= 65535", what);
   const Plan p = make_plan(B, num_q_heads, Hkv, max_seq_len);
   if (!workspace || workspace_bytes < p.total)
     return fail(OCTO_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", what,
@@ -431,9 +617,10 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
   a.B = B;
   a.Hq = num_q_heads;
   a.Hkv = Hkv;
+  a.G = G;
   a.seq_lens = seq_lens;
   a.max_len = max_seq_len;
-  a.scale = softmax_scale > 0.0f ? softmax_scale : 0.08838834764831845f;
+  a.scale = softmax_scale > 0.0f ? softmax_scale : kInvSqrtD;
   a.kc_xi = kc.c_xi;
   a.kc_rho = kc.c_rho;
   a.vc_xi = vc.c_xi;
@@ -451,21 +638,22 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
   a.capacity = k_cache->capacity;
   a.n_split = p.n_split;
   a.split_len = p.split_len;
-  a.ws_ml = reinterpret_cast<float2*>(workspace);
-  a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ml_bytes);
+  char* ws = static_cast<char*>(workspace);
+  a.ws_ml = reinterpret_cast<float2*>(ws);
+  a.ws_acc = reinterpret_cast<float*>(ws + p.ml_bytes);
+  a.out = out;
 
-  bool ok = false;
   switch (kc.b_dir * 10 + kc.b_nrm) {
-    case 31: ok = launch_split<3, 1>(a, G, kc.qjl, stream); break;
-    case 42: ok = launch_split<4, 2>(a, G, kc.qjl, stream); break;
-    case 53: ok = launch_split<5, 3>(a, G, kc.qjl, stream); break;
-    case 22: ok = launch_split<2, 2>(a, G, kc.qjl, stream); break;
-    case 33: ok = launch_split<3, 3>(a, G, kc.qjl, stream); break;
-    case 44: ok = launch_split<4, 4>(a, G, kc.qjl, stream); break;
+    case 31: launch<3, 1>(a, kc.qjl, stream); break;
+    case 42: launch<4, 2>(a, kc.qjl, stream); break;
+    case 53: launch<5, 3>(a, kc.qjl, stream); break;
+    case 22: launch<2, 2>(a, kc.qjl, stream); break;
+    case 33: launch<3, 3>(a, kc.qjl, stream); break;
+    case 44: launch<4, 4>(a, kc.qjl, stream); break;
+    default: return fail(OCTO_ERR_UNSUPPORTED, "%s: configuration not compiled", what);
   }
-  if (!ok) return fail(OCTO_ERR_UNSUPPORTED, "%s: configuration not compiled", what);
   if ((s = check_launch(what)) != OCTO_OK) return s;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, B), dim3(64), 0, stream, a.ws_ml,
-                     a.ws_acc, a.n_split, num_q_heads, vc.seed, out);
+  hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, B), dim3(256), 0, stream, a.ws_ml, a.ws_acc,
+                     a.n_split, num_q_heads, vc.seed, out);
   return check_launch(what);
 }

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32;
 
   __shared__ float4 lut[K * K];                       // n(c_xi[i], c_xi[j]) at i + K j
-  __shared__ float mid_xi[K], crho[R], mid_rho[R];
+  __shared__ float cxi[K], mid_xi[K], crho[R], mid_rho[R];
   __shared__ float sgn[2 * kHeadDim];                 // s then s'
   __shared__ float u[kTok * kUStride];
   __shared__ uint16_t code_dir[kTok * kNTri];
@@ -94,14 +94,18 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   const int h = blockIdx.y, b = blockIdx.z;
   const int t0 = blockIdx.x * kTok;
 
-  // ---- tables: signs, midpoints, the decoded direction of every code pair
+  // ---- tables: signs, codebooks, midpoints, the decoded direction of every
+  // code pair (codebooks go through LDS so that the table loop reads no
+  // global memory)
   for (int j = tid; j < 2 * kHeadDim; j += kThreads) sgn[j] = splitmix_sign(a.seed, j);
-  if (tid < K - 1) mid_xi[tid] = 0.5f * (a.c_xi[tid] + a.c_xi[tid + 1]);
+  if (tid < K) cxi[tid] = a.c_xi[tid];
   if (tid < R) crho[tid] = a.c_rho[tid];
-  if (tid < R - 1) mid_rho[tid] = 0.5f * (a.c_rho[tid] + a.c_rho[tid + 1]);
+  __syncthreads();
+  if (tid < K - 1) mid_xi[tid] = 0.5f * (cxi[tid] + cxi[tid + 1]);
+  if (tid < R - 1) mid_rho[tid] = 0.5f * (crho[tid] + crho[tid + 1]);
   for (int e = tid; e < K * K; e += kThreads) {
     // Eq. 6 with the fold of App. C.7, then normalization onto S^2.
-    const float xi = a.c_xi[e % K], eta = a.c_xi[e / K];
+    const float xi = cxi[e % K], eta = cxi[e / K];
     const float z = 1.0f - fabsf(xi) - fabsf(eta);
     float x = xi, y = eta;
     if (z < 0.0f) {
@@ -117,16 +121,26 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   const size_t plane = (size_t)b * a.H + h;
   const int64_t base = (int64_t)b * a.s0 + (int64_t)h * a.s1;
   const float inv_sqrt_d = 0.08838834764831845f;     // 1/sqrt(128)
-  for (int k = wave; k < kTok; k += 4) {
-    const int t = t0 + k;
-    float x0 = 0.0f, x1 = 0.0f;
+  // each wave takes 16 tokens, loading all of them before any use
+  constexpr int kPerWave = kTok / 4;
+  float xs[kPerWave][2];
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int t = t0 + wave + 4 * j;
+    xs[j][0] = xs[j][1] = 0.0f;
     if (t < a.T) {
       const int64_t off = base + (int64_t)t * a.s2;
-      x0 = load_x(a, off + lane);
-      x1 = load_x(a, off + lane + 64);
+      xs[j][0] = load_x(a, off + lane);
+      xs[j][1] = load_x(a, off + lane + 64);
     }
+  }
+  const float s_lo = sgn[lane], s_hi = sgn[lane + 64];
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int k = wave + 4 * j, t = t0 + k;
+    const float x0 = xs[j][0], x1 = xs[j][1];
     const float gamma = sqrtf(wave_sum(x0 * x0 + x1 * x1));
-    float v0 = x0 * sgn[lane], v1 = x1 * sgn[lane + 64];
+    float v0 = x0 * s_lo, v1 = x1 * s_hi;
     wht128(v0, v1);
     const float scale = inv_sqrt_d / fmaxf(gamma, kEps);
     u[k * kUStride + lane] = v0 * scale;

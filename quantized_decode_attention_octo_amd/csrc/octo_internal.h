@@ -21,6 +21,7 @@ constexpr int kPadDim = 3 * kNTri;       // 129: u zero-padded to whole triplets
 constexpr float kEps = 1e-20f;           // the eps-safe divisor of Sec. 3.1 / 3.2
 constexpr int kWave = 64;
 
+
 // A codec with its bit split resolved (Sec. 3.3: B_tri = 2 b_dir + b_nrm).
 struct Codec {
   int b_dir, b_nrm;     // bits per octahedral coordinate / per triplet norm

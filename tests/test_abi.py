@@ -130,7 +130,7 @@ def test_decode_errors(L):
     assert dec(L, kd, vd, kv, vv, ws_bytes=0) == 5
     assert dec(L, kd, vd, kv, vv, ws=4097) == 3
     assert dec(L, kd, vd, kv, vv, Hq=3) == 1                 # not a multiple of kv_heads
-    assert dec(L, kd, vd, kv, vv, Hq=6) == 2                 # G = 3 not compiled
+    assert dec(L, kd, vd, kv, vv, Hq=34) == 2                # G = 17 > 16 MFMA columns
     assert dec(L, kd, vd, kv, vv, max_len=256) == 4          # beyond capacity
     assert dec(L, kd, desc(qjl=1), kv, view(H=2, qjl=True)) == 2   # QJL values
     assert dec(L, kd, desc(bits=2), kv, vv) == 2             # K/V split differ

@@ -5,7 +5,7 @@ Small cases span several 64-token tiles, several splits and ragged tails;
 the full-size cases are the benchmark's configurations (all outputs for the
 32k-context and batched workloads, sampled planes at 128k context).  Edge
 cases: empty sequences, lengths clipped by max_seq_len, fp32 queries, every
-compiled GQA group size, determinism.
+GQA group size from 1 to 16, determinism, repeated calls on one workspace.
 """
 import numpy as np
 import pytest
@@ -112,7 +112,7 @@ def test_decode_fp32_queries():
     assert err <= ATOL
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (4, 2), (8, 2), (16, 2), (7, 1)])
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (4, 2), (6, 2), (8, 2), (16, 2), (7, 1), (32, 2)])
 def test_decode_group_sizes(Hq, Hkv):
     w = workload("gqa32k", Hq=Hq, Hkv=Hkv, outliers=False)
     err, _, _ = run_case(w, T=260)
@@ -130,3 +130,21 @@ def test_decode_deterministic():
     a = octo.octo_attend_decode(kc, vc, kcache, vcache, q, seq).cpu()
     b = octo.octo_attend_decode(kc, vc, kcache, vcache, q, seq).cpu()
     assert torch.equal(a, b)
+
+
+def test_decode_reuses_workspace():
+    """The completion counters return to zero: back-to-back calls on one
+    workspace, with different shapes, keep matching the oracle."""
+    ws = octo.workspace(1 << 22, "cuda")
+    for T, key in ((700, "gqa32k"), (300, "long128k"), (700, "gqa32k")):
+        w = workload(key)
+        inp = make_inputs(w, scale_T=T)
+        kc, hk = codecs(w.bits, qjl=w.qjl)
+        vc, hv = codecs(w.bits)
+        kcache = encode_gpu(inp["K"], kc)
+        vcache = encode_gpu(inp["V"], vc)
+        out = octo.octo_attend_decode(kc, vc, kcache, vcache, inp["q"].cuda(),
+                                      inp["seq_lens"].cuda(), ws=ws)
+        ref = oatt.decode_attention(inp["q"].double().numpy(), kcache.to_host(),
+                                    vcache.to_host(), hk, hv, inp["seq_lens"].numpy())
+        assert np.abs(out.cpu().double().numpy() - ref).max() <= ATOL
