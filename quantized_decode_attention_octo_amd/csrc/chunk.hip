@@ -12,11 +12,14 @@
 // (R_k q) . (gamma u^) is the score of the factorized form.  The output is
 // R_v^T applied to the softmax-weighted rotated values.
 //
-// Three launches on one stream:
-//   1. rotate_rows: q, k_cur, v_cur -> fp16 rotated rows in the workspace
-//   2. decode_rows: cached tokens -> fp16 gamma * u^ rows in the workspace
-//   3. chunk_attn:  fp16 MFMA flash attention (fp32 accumulation, online
-//                   softmax), epilogue R_v^T.
+// Launches on one stream:
+//   1. rotate_rows (x3): q, k_cur -> fp16 rotated rows; v_cur -> fp16 rotated
+//      columns of the transposed value matrix
+//   2. decode_rows (x2): cached keys -> fp16 gamma u^ rows; cached values ->
+//      columns of the transposed value matrix
+//   3. chunk_attn: fp16 MFMA flash attention (fp32 accumulation, online
+//      softmax), epilogue 1/l and R_v^T; XCD-aware workgroup order.
+// The window is decoded once per call and shared by every query tile.
 #include <math.h>
 
 #include "octo_internal.h"
@@ -29,28 +32,60 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr float kInvSqrtD = 0.08838834764831845f;
+constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- pre-passes
-// One wavefront per row: out = fp16(H diag(s) x / sqrt(d)).  Rows t >= T of
-// the output range [0, T_out) are written as zeros (tile padding).
+// Rows t < T_out of a plane: fp16(H diag(s) x_t / sqrt(d)), zero for t >= T
+// (tile padding).  Row-major output: row out_off + t of a [out_rows][128]
+// plane.  Transposed output: column out_off + t of a [128][out_rows] plane.
+// One workgroup takes 64 rows, one wavefront per row for the transform; the
+// transposed store goes through LDS so that 64 consecutive columns are
+// written together.
+template <bool TRANSPOSED>
 __global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __restrict__ in,
                                                           int T, int T_out, uint64_t seed,
                                                           _Float16* __restrict__ out,
                                                           int out_rows, int out_off) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ _Float16 tile[TRANSPOSED ? 64 * 130 : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int plane = blockIdx.y;
-  if (t >= T_out) return;
-  float a = 0.0f, b = 0.0f;
-  if (t < T) {
-    const uint16_t* src = in + ((size_t)plane * T + t) * kHeadDim;
-    a = bf16_to_f32(src[lane]) * splitmix_sign(seed, lane);
-    b = bf16_to_f32(src[lane + 64]) * splitmix_sign(seed, lane + 64);
+  const int t0 = blockIdx.x * 64;
+  const float s0 = splitmix_sign(seed, lane), s1 = splitmix_sign(seed, lane + 64);
+#pragma unroll 1
+  for (int j0 = 0; j0 < 16; j0 += 4) {
+    float xa[4], xb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + wave + 4 * (j0 + j);
+      xa[j] = xb[j] = 0.0f;
+      if (t < T) {
+        const uint16_t* src = in + ((size_t)plane * T + t) * kHeadDim;
+        xa[j] = bf16_to_f32(src[lane]);
+        xb[j] = bf16_to_f32(src[lane + 64]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = wave + 4 * (j0 + j), t = t0 + k;
+      float a = xa[j] * s0, b = xb[j] * s1;
+      wht128(a, b);
+      if (TRANSPOSED) {
+        tile[k * 130 + lane] = (_Float16)(a * kInvSqrtD);
+        tile[k * 130 + lane + 64] = (_Float16)(b * kInvSqrtD);
+      } else if (t < T_out) {
+        _Float16* dst = out + ((size_t)plane * out_rows + out_off + t) * kHeadDim;
+        dst[lane] = (_Float16)(a * kInvSqrtD);
+        dst[lane + 64] = (_Float16)(b * kInvSqrtD);
+      }
+    }
   }
-  wht128(a, b);
-  _Float16* dst = out + ((size_t)plane * out_rows + out_off + t) * kHeadDim;
-  dst[lane] = (_Float16)(a * kInvSqrtD);
-  dst[lane + 64] = (_Float16)(b * kInvSqrtD);
+  if (TRANSPOSED) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * kHeadDim; e += 256) {
+      const int c = e >> 6, k = e & 63, t = t0 + k;
+      if (t < T_out) out[((size_t)plane * kHeadDim + c) * out_rows + out_off + t] = tile[k * 130 + c];
+    }
+  }
 }
 
 __device__ inline float4 oct_dir(float xi, float eta) {
@@ -64,9 +99,12 @@ __device__ inline float4 oct_dir(float xi, float eta) {
   return make_float4(x / n, y / n, z / n, 0.0f);
 }
 
-// One workgroup per 64 cached tokens of a plane, one lane per (token,
-// triplet), token-fastest: out row t = fp16(gamma_t * u^_t[0:128]).
-template <int BD, int BN>
+// One workgroup per 64 cached tokens of a plane: lanes take (token, triplet)
+// items token-fastest (coalesced reads of the tile-64 words) and write
+// fp16(gamma_t u^_t[0:128]) into an LDS tile, which is then stored as rows t
+// of a [out_rows][128] plane (16-byte chunks) or as columns t of a
+// [128][out_rows] plane (64 consecutive columns per row).
+template <int BD, int BN, bool TRANSPOSED>
 __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __restrict__ dir,
                                                           const uint32_t* __restrict__ nrm,
                                                           const float* __restrict__ gamma,
@@ -77,18 +115,23 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
                                                           int out_rows) {
   constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD;
   constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32;
+  constexpr int kRow = 136;                        // halves per token row in LDS
   __shared__ float4 lut[K * K];
-  __shared__ float crho[R];
+  __shared__ float crho[R], cxi[K];
+  __shared__ __attribute__((aligned(16))) _Float16 tile[64 * kRow];
   const int tid = threadIdx.x;
-  for (int e = tid; e < K * K; e += 256) lut[e] = oct_dir(c_xi[e % K], c_xi[e / K]);
+  if (tid < K) cxi[tid] = c_xi[tid];
   if (tid < R) crho[tid] = c_rho[tid];
+  __syncthreads();
+  for (int e = tid; e < K * K; e += 256) lut[e] = oct_dir(cxi[e % K], cxi[e / K]);
   __syncthreads();
   const size_t plane = blockIdx.y;
   const int t0 = blockIdx.x * 64;
+  const int nt = min(64, cached - t0);
   for (int e = tid; e < 64 * kNTri; e += 256) {
     const int k = e & 63, i = e >> 6;
     const int t = t0 + k;
-    if (t >= cached) continue;
+    if (k >= nt) continue;
     const int dp = i * FWD, np = i * BN;
     uint32_t lo = dir[tile_word(plane, capacity, t, dp >> 5, WD)];
     uint32_t hi = ((dp & 31) + FWD > 32) ? dir[tile_word(plane, capacity, t, (dp >> 5) + 1, WD)] : 0u;
@@ -98,26 +141,46 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
     const uint32_t ir = (uint32_t)((((uint64_t)hi << 32) | lo) >> (np & 31)) & ((1u << BN) - 1u);
     const float s = crho[ir] * gamma[plane * capacity + t];
     const float4 n = lut[code];
-    _Float16* dst = out + (plane * out_rows + t) * kHeadDim + 3 * i;
+    _Float16* dst = &tile[k * kRow + 3 * i];
     dst[0] = (_Float16)(s * n.x);
     dst[1] = (_Float16)(s * n.y);
     if (i < kNTri - 1) dst[2] = (_Float16)(s * n.z);   // coordinate 128 is the pad
   }
+  __syncthreads();
+  if (TRANSPOSED) {
+    for (int e = tid; e < 64 * kHeadDim; e += 256) {
+      const int c = e >> 6, k = e & 63;
+      if (k < nt) out[(plane * kHeadDim + c) * out_rows + t0 + k] = tile[k * kRow + c];
+    }
+  } else {
+    typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+    for (int e = tid; e < 64 * 16; e += 256) {
+      const int k = e >> 4, c8 = (e & 15) * 8;
+      if (k < nt)
+        *reinterpret_cast<half8v*>(out + (plane * out_rows + t0 + k) * kHeadDim + c8) =
+            *reinterpret_cast<const half8v*>(&tile[k * kRow + c8]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- attention
-constexpr int kBM = 64;        // queries per workgroup (16 per wavefront)
-constexpr int kBN = 64;        // keys per LDS tile
-constexpr int kKStride = 136;  // halves per K row in LDS (128 + 8 pad)
-constexpr int kVStride = 72;   // halves per transposed V row in LDS (64 + 8 pad)
+constexpr int kRG = 2;          // 16-query row groups per wavefront
+constexpr int kCWaves = 2;
+constexpr int kCThreads = 64 * kCWaves;
+constexpr int kBM = 16 * kRG * kCWaves;   // 64 queries per workgroup
+constexpr int kXcds = 8;        // workgroups are dealt round-robin to the XCDs
+constexpr int kBN = 64;         // keys per LDS tile
+constexpr int kKStride = 136;   // halves per key row in LDS (128 + 8 pad)
+constexpr int kVStride = 72;    // halves per transposed value row in LDS (64 + 8 pad)
 
 struct ChunkArgs {
   const _Float16* q;   // [B][Hq][Tq][128] rotated
   const _Float16* k;   // [B][Hkv][Tk_pad][128] rotated
-  const _Float16* v;   // [B][Hkv][Tk_pad][128] rotated
+  const _Float16* vt;  // [B][Hkv][128][Tk_pad] rotated, transposed
   float* out;          // [B][Hq][Tq][128]
   int Hq, Hkv, Tq, Tk, Tk_pad;
-  float scale;
+  int q_tiles;         // query tiles per (batch, head)
+  float scale2;        // softmax scale * log2(e)
   uint64_t vseed;
 };
 
@@ -127,154 +190,188 @@ struct ChunkArgs {
 //   D[i][j]: i = 4 (L / 16) + r, j = L % 16  (r = register 0..3)
 // Scores are computed transposed, S^T = K Q^T (keys are rows), so that each
 // lane ends up with 4 keys of one query, which is exactly the A operand
-// layout P needs for O = P V with keys as the contraction index.
-__global__ __launch_bounds__(256) void chunk_attn_kernel(ChunkArgs a) {
+// layout P needs for O = P V with keys as the contraction index.  Each
+// wavefront owns two 16-query row groups, so every key / value fragment read
+// from LDS feeds two MFMAs.  The softmax state is updated once per 64-key
+// tile.  Small workgroups (64 queries) keep four resident per CU, which
+// hides the tile loads and leaves no lone final round of workgroups.
+//
+// XCD-aware order: the hardware deals consecutive workgroup ids to the 8
+// XCDs in turn, so the linear id is mapped such that all query tiles of one
+// (batch, head) run on the same XCD and stream its keys and values through
+// that XCD's L2 together.
+__global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
   __shared__ _Float16 ks[kBN * kKStride];
-  __shared__ _Float16 vt[kHeadDim * kVStride];
+  __shared__ _Float16 vs[kHeadDim * kVStride];
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
   const int col = L & 15, grp = L >> 4;
-  const int hq = blockIdx.y, b = blockIdx.z;
+  const int n_units = gridDim.x;
+  const int id = blockIdx.x;
+  // id -> (xcd, local); units (head-major, tile-minor) are split into 8
+  // contiguous ranges, range x running on XCD x.
+  const int per_xcd = (n_units + kXcds - 1) / kXcds;
+  const int xcd = id % kXcds, local = id / kXcds;
+  const int full_xcds = n_units - (per_xcd - 1) * kXcds;   // XCDs with per_xcd units
+  const int unit = xcd < full_xcds ? xcd * per_xcd + local
+                                   : full_xcds * per_xcd + (xcd - full_xcds) * (per_xcd - 1) + local;
+  const int tile = unit % a.q_tiles, bh = unit / a.q_tiles;
+  const int hq = bh % a.Hq, b = bh / a.Hq;
   const int hk = hq / (a.Hq / a.Hkv);
-  const int q0 = blockIdx.x * kBM + wave * 16;
+  const int q0 = tile * kBM + wave * 16 * kRG;
 
-  // Q^T fragments (B operand): query q0 + col, dims 32 s + 8 grp + e.
-  half8 qf[4];
-  {
-    const int qrow = min(q0 + col, a.Tq - 1);
+  // Q^T fragments (B operand): query q0 + 16 rg + col, dims 32 s + 8 grp + e.
+  half8 qf[kRG][4];
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
+    const int qrow = min(q0 + 16 * rg + col, a.Tq - 1);
     const _Float16* src = a.q + (((size_t)b * a.Hq + hq) * a.Tq + qrow) * kHeadDim;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const half8*>(src + 32 * s + 8 * grp);
+    for (int s = 0; s < 4; ++s) qf[rg][s] = *reinterpret_cast<const half8*>(src + 32 * s + 8 * grp);
   }
-  floatx4 o[8];
+  floatx4 o[kRG][8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) o[c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;   // of query q0 + col
+  for (int rg = 0; rg < kRG; ++rg)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[rg][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run[kRG], l_run[kRG];   // of query q0 + 16 rg + col, log2 units
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
+    m_run[rg] = -INFINITY;
+    l_run[rg] = 0.0f;
+  }
 
-  const size_t kv_base = ((size_t)b * a.Hkv + hk) * a.Tk_pad * kHeadDim;
-  // The next tile is loaded into registers while the current one is used.
-  half8 kreg[4], vreg[4];
-  auto load_tile = [&](int kt0) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = it * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
-      const size_t g = kv_base + (size_t)(kt0 + row) * kHeadDim + c8;
-      kreg[it] = *reinterpret_cast<const half8*>(a.k + g);
-      vreg[it] = *reinterpret_cast<const half8*>(a.v + g);
-    }
-  };
-  if (a.Tk > 0) load_tile(0);
+  const size_t kbase = ((size_t)b * a.Hkv + hk) * a.Tk_pad * kHeadDim;
+  const size_t vbase = ((size_t)b * a.Hkv + hk) * kHeadDim * a.Tk_pad;
   for (int kt0 = 0; kt0 < a.Tk; kt0 += kBN) {
     __syncthreads();
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = it * 256 + tid, row = idx >> 4, c8 = (idx & 15) * 8;
-      *reinterpret_cast<half8*>(&ks[row * kKStride + c8]) = kreg[it];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(c8 + e) * kVStride + row] = vreg[it][e];
+    // 64 keys x 128 dims of K and 128 dims x 64 keys of V^T: 1024 16-byte
+    // chunks each.
+#pragma unroll 4
+    for (int idx = tid; idx < 1024; idx += kCThreads) {
+      *reinterpret_cast<half8*>(&ks[(idx >> 4) * kKStride + (idx & 15) * 8]) =
+          *reinterpret_cast<const half8*>(a.k + kbase + (size_t)(kt0 + (idx >> 4)) * kHeadDim +
+                                          (idx & 15) * 8);
+      *reinterpret_cast<half8*>(&vs[(idx >> 3) * kVStride + (idx & 7) * 8]) =
+          *reinterpret_cast<const half8*>(a.vt + vbase + (size_t)(idx >> 3) * a.Tk_pad + kt0 +
+                                          (idx & 7) * 8);
     }
     __syncthreads();
-    if (kt0 + kBN < a.Tk) load_tile(kt0 + kBN);
+
+    // scores of the 64 keys: st[kt][rg][r] = key kt0 + 16 kt + 4 grp + r
+    floatx4 st[4][kRG];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      floatx4 st[2];
+    for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        st[kt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        const _Float16* kr = &ks[(32 * sub + 16 * kt + col) * kKStride + 8 * grp];
+      for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      const _Float16* kr = &ks[(16 * kt + col) * kKStride + 8 * grp];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const half8 kf = *reinterpret_cast<const half8*>(kr + 32 * s);
-          st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[s], st[kt], 0, 0, 0);
-        }
+      for (int s = 0; s < 4; ++s) {
+        const half8 kf = *reinterpret_cast<const half8*>(kr + 32 * s);
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg)
+          st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[rg][s], st[kt][rg], 0, 0, 0);
       }
-      // st[kt][r] = score of key kt0 + 32 sub + 16 kt + 4 grp + r, query q0 + col
-      float sc[8];
+    }
+    const bool full = kt0 + kBN <= a.Tk;
+    half8 pf[kRG][2];
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) {
+      float x[16];
       float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = kt0 + 32 * sub + 16 * (e >> 2) + 4 * grp + (e & 3);
-        sc[e] = key < a.Tk ? st[e >> 2][e & 3] * a.scale : -INFINITY;
-        mx = fmaxf(mx, sc[e]);
+      for (int e = 0; e < 16; ++e) {
+        const int kt = e >> 2, r = e & 3;
+        x[e] = st[kt][rg][r] * a.scale2;
+        if (!full && kt0 + 16 * kt + 4 * grp + r >= a.Tk) x[e] = -INFINITY;
+        mx = fmaxf(mx, x[e]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == -INFINITY ? 0.0f : __expf(m_run - m_new);
-      half8 pf;
+      const float m_new = fmaxf(m_run[rg], mx);
+      const float alpha = m_run[rg] == m_new ? 1.0f : exp2f(m_run[rg] - m_new);
       float ps = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = sc[e] == -INFINITY ? 0.0f : __expf(sc[e] - m_new);
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2f(x[e] - m_new);
         ps += p;
-        pf[e] = (_Float16)p;
+        pf[rg][e >> 3][e & 7] = (_Float16)p;
       }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-      // rescale O rows: lane holds queries q0 + 4 grp + r
+      l_run[rg] = l_run[rg] * alpha + ps;
+      m_run[rg] = m_new;
+      // rescale O rows (queries q0 + 16 rg + 4 grp + r)
       float al[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[c][r] *= al[r];
-        // V operand: keys 32 sub + 4 grp + 0..3 and 32 sub + 16 + 4 grp + 0..3, dim 16 c + col
-        const _Float16* vr = &vt[(16 * c + col) * kVStride + 32 * sub + 4 * grp];
+        for (int r = 0; r < 4; ++r) o[rg][c][r] *= al[r];
+    }
+    // O += P V: slot e of sub-block sb is key kt0 + 32 sb + 16 (e / 4) + 4 grp + e % 4
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const _Float16* vr = &vs[(16 * c + col) * kVStride + 32 * sb + 4 * grp];
         const half4 v0 = *reinterpret_cast<const half4*>(vr);
         const half4 v1 = *reinterpret_cast<const half4*>(vr + 16);
         const half8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vf, o[c], 0, 0, 0);
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg)
+          o[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg][sb], vf, o[rg][c], 0, 0, 0);
       }
-    }
   }
 
   // ---- epilogue: 1/l, then R_v^T = diag(s_v) H / sqrt(d) on every query row.
-  // Lane holds coordinate 16 c + col of queries q0 + 4 grp + r: the Hadamard
-  // butterflies on coordinate bits 4..6 are register-local, bits 0..3 cross
-  // lanes within each 16-lane group.
-  float li[4];
+  // Lane holds coordinate 16 c + col of queries q0 + 16 rg + 4 grp + r: the
+  // Hadamard butterflies on coordinate bits 4..6 are register-local, bits
+  // 0..3 cross lanes within each 16-lane group.
+  float sv[8];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float l = __shfl(l_run, 4 * grp + r, 64);
-    li[r] = l > 0.0f ? 1.0f / l : 0.0f;
-  }
-  float v[8][4];
+  for (int c = 0; c < 8; ++c) sv[c] = kInvSqrtD * splitmix_sign(a.vseed, 16 * c + col);
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+  for (int rg = 0; rg < kRG; ++rg) {
+    float li[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[c][r] = o[c][r] * li[r];
-#pragma unroll
-  for (int m = 4; m >= 1; m >>= 1)
+    for (int r = 0; r < 4; ++r) {
+      const float l = __shfl(l_run[rg], 4 * grp + r, 64);
+      li[r] = l > 0.0f ? 1.0f / l : 0.0f;
+    }
+    float v[8][4];
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      if (!(c & m)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[c][r] = o[rg][c][r] * li[r];
+#pragma unroll
+    for (int m = 4; m >= 1; m >>= 1)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (!(c & m)) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = v[c][r], y = v[c | m][r];
+            v[c][r] = x + y;
+            v[c | m][r] = x - y;
+          }
+        }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float x = v[c][r], y = v[c | m][r];
-          v[c][r] = x + y;
-          v[c | m][r] = x - y;
+          const float p = __shfl_xor(v[c][r], m, 64);
+          v[c][r] = (col & m) ? (p - v[c][r]) : (v[c][r] + p);
         }
-      }
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1)
+    for (int r = 0; r < 4; ++r) {
+      const int q = q0 + 16 * rg + 4 * grp + r;
+      if (q >= a.Tq) continue;
+      float* dst = a.out + (((size_t)b * a.Hq + hq) * a.Tq + q) * kHeadDim;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __shfl_xor(v[c][r], m, 64);
-        v[c][r] = (col & m) ? (p - v[c][r]) : (v[c][r] + p);
-      }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int q = q0 + 4 * grp + r;
-    if (q >= a.Tq) continue;
-    float* dst = a.out + (((size_t)b * a.Hq + hq) * a.Tq + q) * kHeadDim;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int d = 16 * c + col;
-      dst[d] = v[c][r] * kInvSqrtD * splitmix_sign(a.vseed, d);
+      for (int c = 0; c < 8; ++c) dst[16 * c + col] = v[c][r] * sv[c];
     }
   }
 }
@@ -299,21 +396,25 @@ ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Tq, int cached, int Tc) {
 
 template <int BD, int BN>
 void launch_decode_rows(const octo_cache_view* c, const Codec& cd, int cached, _Float16* out,
-                        int out_rows, hipStream_t st) {
+                        int out_rows, bool transposed, hipStream_t st) {
   dim3 grid((cached + 63) / 64, c->batch * c->kv_heads);
-  hipLaunchKernelGGL((decode_rows_kernel<BD, BN>), grid, dim3(256), 0, st, c->dir, c->nrm,
-                     c->gamma, cd.c_xi, cd.c_rho, c->capacity, cached, out, out_rows);
+  if (transposed)
+    hipLaunchKernelGGL((decode_rows_kernel<BD, BN, true>), grid, dim3(256), 0, st, c->dir,
+                       c->nrm, c->gamma, cd.c_xi, cd.c_rho, c->capacity, cached, out, out_rows);
+  else
+    hipLaunchKernelGGL((decode_rows_kernel<BD, BN, false>), grid, dim3(256), 0, st, c->dir,
+                       c->nrm, c->gamma, cd.c_xi, cd.c_rho, c->capacity, cached, out, out_rows);
 }
 
 bool decode_rows(const octo_cache_view* c, const Codec& cd, int cached, _Float16* out,
-                 int out_rows, hipStream_t st) {
+                 int out_rows, bool transposed, hipStream_t st) {
   switch (cd.b_dir * 10 + cd.b_nrm) {
-    case 31: launch_decode_rows<3, 1>(c, cd, cached, out, out_rows, st); return true;
-    case 42: launch_decode_rows<4, 2>(c, cd, cached, out, out_rows, st); return true;
-    case 53: launch_decode_rows<5, 3>(c, cd, cached, out, out_rows, st); return true;
-    case 22: launch_decode_rows<2, 2>(c, cd, cached, out, out_rows, st); return true;
-    case 33: launch_decode_rows<3, 3>(c, cd, cached, out, out_rows, st); return true;
-    case 44: launch_decode_rows<4, 4>(c, cd, cached, out, out_rows, st); return true;
+    case 31: launch_decode_rows<3, 1>(c, cd, cached, out, out_rows, transposed, st); return true;
+    case 42: launch_decode_rows<4, 2>(c, cd, cached, out, out_rows, transposed, st); return true;
+    case 53: launch_decode_rows<5, 3>(c, cd, cached, out, out_rows, transposed, st); return true;
+    case 22: launch_decode_rows<2, 2>(c, cd, cached, out, out_rows, transposed, st); return true;
+    case 33: launch_decode_rows<3, 3>(c, cd, cached, out, out_rows, transposed, st); return true;
+    case 44: launch_decode_rows<4, 4>(c, cd, cached, out, out_rows, transposed, st); return true;
   }
   return false;
 }
@@ -387,36 +488,39 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   _Float16* vr = reinterpret_cast<_Float16*>(ws + p.v_off);
   const int planes_q = B * num_q_heads, planes_kv = B * Hkv;
 
-  hipLaunchKernelGGL(rotate_rows_kernel, dim3((Tq + 3) / 4, planes_q), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(q), Tq, Tq, kc.seed, qr, Tq, 0);
+  hipLaunchKernelGGL(rotate_rows_kernel<false>, dim3((Tq + 63) / 64, planes_q), dim3(256), 0,
+                     stream, static_cast<const uint16_t*>(q), Tq, Tq, kc.seed, qr, Tq, 0);
   const int cur_out = p.Tk_pad - cached_tokens;  // current rows plus the zero tile padding
   if (cur_out > 0) {
-    hipLaunchKernelGGL(rotate_rows_kernel, dim3((cur_out + 3) / 4, planes_kv), dim3(256), 0,
-                       stream, static_cast<const uint16_t*>(k_cur), Tc, cur_out, kc.seed, kr,
+    hipLaunchKernelGGL(rotate_rows_kernel<false>, dim3((cur_out + 63) / 64, planes_kv), dim3(256),
+                       0, stream, static_cast<const uint16_t*>(k_cur), Tc, cur_out, kc.seed, kr,
                        p.Tk_pad, cached_tokens);
-    hipLaunchKernelGGL(rotate_rows_kernel, dim3((cur_out + 3) / 4, planes_kv), dim3(256), 0,
-                       stream, static_cast<const uint16_t*>(v_cur), Tc, cur_out, vc.seed, vr,
+    hipLaunchKernelGGL(rotate_rows_kernel<true>, dim3((cur_out + 63) / 64, planes_kv), dim3(256),
+                       0, stream, static_cast<const uint16_t*>(v_cur), Tc, cur_out, vc.seed, vr,
                        p.Tk_pad, cached_tokens);
   }
   if (cached_tokens > 0) {
-    if (!decode_rows(k_cache, kc, cached_tokens, kr, p.Tk_pad, stream) ||
-        !decode_rows(v_cache, vc, cached_tokens, vr, p.Tk_pad, stream))
+    if (!decode_rows(k_cache, kc, cached_tokens, kr, p.Tk_pad, false, stream) ||
+        !decode_rows(v_cache, vc, cached_tokens, vr, p.Tk_pad, true, stream))
       return fail(OCTO_ERR_UNSUPPORTED, "%s: split not compiled", what);
   }
   if ((s = check_launch(what)) != OCTO_OK) return s;
   ChunkArgs a;
   a.q = qr;
   a.k = kr;
-  a.v = vr;
+  a.vt = vr;
   a.out = out;
   a.Hq = num_q_heads;
   a.Hkv = Hkv;
   a.Tq = Tq;
   a.Tk = p.Tk;
   a.Tk_pad = p.Tk_pad;
-  a.scale = softmax_scale > 0.0f ? softmax_scale : kInvSqrtD;
+  a.q_tiles = (Tq + kBM - 1) / kBM;
+  a.scale2 = (softmax_scale > 0.0f ? softmax_scale : kInvSqrtD) * kLog2e;
   a.vseed = vc.seed;
-  hipLaunchKernelGGL(chunk_attn_kernel, dim3((Tq + kBM - 1) / kBM, num_q_heads, B), dim3(256), 0,
-                     stream, a);
+  const long long units = (long long)a.q_tiles * num_q_heads * B;
+  if (units > 0x7fffffffLL)
+    return fail(OCTO_ERR_UNSUPPORTED, "%s: too many query tiles", what);
+  hipLaunchKernelGGL(chunk_attn_kernel, dim3((unsigned)units), dim3(kCThreads), 0, stream, a);
   return check_launch(what);
 }

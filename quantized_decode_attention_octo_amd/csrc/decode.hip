@@ -6,8 +6,8 @@
 // (batch, KV head) plane for the G query heads sharing that KV head.  Keys
 // are never reconstructed in memory: each wavefront unpacks a 32-token block
 // straight into MFMA operand registers,
-//   u^_j = rho^_ji n^_ji   (Eq. 13: n^ from an LDS table of the decoded
-//                           direction of every code pair, rho^ from C_rho),
+//   u^_j = rho^_ji n^_ji   (Eq. 13: n^ the decoded direction of the code
+//                           pair, rho^ the C_rho centroid),
 // and the score of Eq. 13, gamma_j (R q) . u^_j, is one MFMA product of the
 // block's u^ with the rotated queries.  With QJL the estimator of Sec. 3.6,
 // gamma_j sqrt(pi/(2d)) gamma_r,j (R' R q) . sigma_j, is a second product
@@ -21,6 +21,13 @@
 // about 2^-20 relative: single fp16 operands are not accurate enough for the
 // peaked softmax that outlier channels produce.  u^ is scaled by 64 (exact)
 // so that the residuals stay in the fp16 normal range.
+//
+// Tables in LDS, built per workgroup from the codebooks.  When the split is
+// small (2^(2 b_dir + b_nrm) <= 1024 entries: b_dir <= 4 with b_nrm <= 2, or
+// the uniform (2,2), (3,3)), the table holds 64 rho^ n^ for every (code pair,
+// norm index), already split into fp16 hi/lo halves, so unpacking a triplet
+// is two field extractions, one LDS read and byte permutes.  Otherwise it
+// holds 64 n^ per code pair in fp32 and rho^ is applied and split on the fly.
 //
 // MFMA lane layout of v_mfma_f32_16x16x32_f16 (L = lane):
 //   A[i][k]: i = L % 16, k-slot 8 (L / 16) + e;  B[k][j]: j = L % 16, same k
@@ -47,6 +54,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -55,7 +63,7 @@ constexpr int kSplitQuantum = 128;    // split lengths are multiples of this
 constexpr int kMaxG = 16;             // query heads per KV head (MFMA columns)
 constexpr float kUScale = 64.0f;      // exact scale of u^ in the operands
 constexpr float kInvSqrtD = 0.08838834764831845f;
-constexpr int kStageStride = 33;      // words per staged row (32 tokens + pad)
+constexpr int kMaxPre = 1024;         // largest pre-split table (entries)
 
 struct DecodeArgs {
   const void* q;
@@ -65,6 +73,7 @@ struct DecodeArgs {
   int max_len;
   float scale;
   const float *kc_xi, *kc_rho, *vc_xi, *vc_rho;
+  int shared_tables;   // K and V use the same codebooks
   uint64_t kseed, vseed;
   const uint32_t *kdir, *knrm, *kqjl, *vdir, *vnrm;
   const float *kgamma, *vgamma;
@@ -73,7 +82,6 @@ struct DecodeArgs {
   int n_split, split_len;
   float2* ws_ml;       // [B][Hq][n_split] (running max, normalizer)
   float* ws_acc;       // [B][Hq][n_split][128] rotated-frame value sums (x64)
-  float* out;          // [B][Hq][128]
 };
 
 __device__ inline void wave_sync() {
@@ -82,17 +90,19 @@ __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+__device__ inline uint32_t pk(fp16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+
 // x = hi + lo for 8 slots: hi rounded toward zero to fp16, lo the residual.
 __device__ inline void split8(const float* x, half8& hi, half8& lo) {
+  u32x4 h, l;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(x[2 * k], x[2 * k + 1]);
-    const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(x[2 * k] - (float)h.x, x[2 * k + 1] - (float)h.y);
-    hi[2 * k] = (_Float16)h.x;
-    hi[2 * k + 1] = (_Float16)h.y;
-    lo[2 * k] = (_Float16)l.x;
-    lo[2 * k + 1] = (_Float16)l.y;
+    const fp16x2 a = __builtin_amdgcn_cvt_pkrtz(x[2 * k], x[2 * k + 1]);
+    h[k] = pk(a);
+    l[k] = pk(__builtin_amdgcn_cvt_pkrtz(x[2 * k] - (float)a.x, x[2 * k + 1] - (float)a.y));
   }
+  hi = __builtin_bit_cast(half8, h);
+  lo = __builtin_bit_cast(half8, l);
 }
 
 __device__ inline floatx4 mfma(const half8& a, const half8& b, floatx4 c) {
@@ -119,31 +129,80 @@ __device__ inline float4 decode_dir(float xi, float eta) {
   return make_float4(x * n, y * n, z * n, 0.0f);
 }
 
+// Pre-split entry of 64 rho^ n^: {hx|hy, hz|0, lx|ly, lz|0} as fp16 pairs.
+__device__ inline uint4 presplit_entry(float4 n, float rho) {
+  const float x = rho * n.x, y = rho * n.y, z = rho * n.z;
+  const fp16x2 hxy = __builtin_amdgcn_cvt_pkrtz(x, y);
+  const fp16x2 hz = __builtin_amdgcn_cvt_pkrtz(z, 0.0f);
+  const fp16x2 lxy = __builtin_amdgcn_cvt_pkrtz(x - (float)hxy.x, y - (float)hxy.y);
+  const fp16x2 lz = __builtin_amdgcn_cvt_pkrtz(z - (float)hz.x, 0.0f);
+  return make_uint4(pk(hxy), pk(hz), pk(lxy), pk(lz));
+}
+
+// Operand pair of slots (e, e+1) for one component from two pre-split
+// entries: low or high fp16 half of the same word of each.
+__device__ inline uint32_t pair_lo(uint32_t e0, uint32_t e1) {
+  return __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+}
+__device__ inline uint32_t pair_hi(uint32_t e0, uint32_t e1) {
+  return __builtin_amdgcn_perm(e1, e0, 0x07060302u);
+}
+
+// Operands of 8 slots from pre-split entries: component c hi / lo.
+__device__ inline void operands_pre(const uint4* E, half8 (&hi)[3], half8 (&lo)[3]) {
+  u32x4 hx, hy, hz, lx, ly, lz;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint4 a = E[2 * m], b = E[2 * m + 1];
+    hx[m] = pair_lo(a.x, b.x);
+    hy[m] = pair_hi(a.x, b.x);
+    hz[m] = pair_lo(a.y, b.y);
+    lx[m] = pair_lo(a.z, b.z);
+    ly[m] = pair_hi(a.z, b.z);
+    lz[m] = pair_lo(a.w, b.w);
+  }
+  hi[0] = __builtin_bit_cast(half8, hx);
+  hi[1] = __builtin_bit_cast(half8, hy);
+  hi[2] = __builtin_bit_cast(half8, hz);
+  lo[0] = __builtin_bit_cast(half8, lx);
+  lo[1] = __builtin_bit_cast(half8, ly);
+  lo[2] = __builtin_bit_cast(half8, lz);
+}
+
 template <int BD, int BN, bool QJL>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD;
   constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32, WV = WD + WN;
   constexpr uint32_t kDirMask = (1u << FWD) - 1u, kNrmMask = (1u << BN) - 1u;
+  constexpr bool PRE = K * K * R <= kMaxPre;       // pre-split (code, rho) table
+  constexpr int kTab = PRE ? K * K * R : K * K;    // entries per table (16 B each)
+  constexpr int kTabBytes = 2 * kTab * 16;
+  constexpr int kRedBytes = kWaves * kMaxG * kHeadDim * 4;
+  constexpr int kUnion = kTabBytes > kRedBytes ? kTabBytes : kRedBytes;
+  constexpr int kStageRow = WV + 1;                // words per staged token (+ pad)
 
-  __shared__ float4 lutk[K * K], lutv[K * K];
+  // tables during the scan, the per-wave partial sums afterwards
+  __shared__ __attribute__((aligned(16))) char smem[kUnion];
   __shared__ float crk[R], crv[R], cxk[K], cxv[K];
-  __shared__ float qs[kMaxG * 132];                      // R q, then R' R q (QJL)
-  __shared__ uint32_t stage[kWaves * WV * kStageStride];  // value words of a block
+  __shared__ float qs[kMaxG * 132];                       // R q, then R' R q (QJL)
+  __shared__ uint32_t stage[kWaves * kBlock * kStageRow];  // value words of a block
   __shared__ float red_ml[kWaves * kMaxG * 2];
-  __shared__ float red_o[kWaves * 8 * kHeadDim];          // [wave][8 heads][128]
 
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
   const int col = L & 15, grp4 = L >> 4;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
   const size_t plane = (size_t)b * a.Hkv + g;
+  uint4* tabk = reinterpret_cast<uint4*>(smem);
+  uint4* tabv = a.shared_tables ? tabk : tabk + kTab;
+  float* red_o = reinterpret_cast<float*>(smem);          // [wave][head][128]
 
   int len = a.seq_lens[b];
   len = max(0, min(len, min(a.max_len, a.capacity)));
   const int t_begin = split * a.split_len;
   const int t_end = min(len, t_begin + a.split_len);
 
-  // ---- tables: codebooks to LDS first, then the decoded directions
+  // ---- tables: codebooks to LDS first, then the table entries
   if (tid < K) {
     cxk[tid] = a.kc_xi[tid];
     cxv[tid] = a.vc_xi[tid];
@@ -171,9 +230,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  for (int e = tid; e < K * K; e += kThreads) {
-    lutk[e] = decode_dir(cxk[e % K], cxk[e / K]);
-    lutv[e] = decode_dir(cxv[e % K], cxv[e / K]);
+  const int n_tables = a.shared_tables ? 1 : 2;
+  for (int e = tid; e < n_tables * kTab; e += kThreads) {
+    const bool v = e >= kTab;
+    const int i = v ? e - kTab : e;
+    const float* cx = v ? cxv : cxk;
+    if (PRE) {
+      const int code = i / R, r = i - code * R;
+      tabk[e] = presplit_entry(decode_dir(cx[code % K], cx[code / K]), (v ? crv : crk)[r]);
+    } else {
+      const float4 n = decode_dir(cx[i % K], cx[i / K]);
+      tabk[e] = make_uint4(__float_as_uint(n.x), __float_as_uint(n.y), __float_as_uint(n.z), 0u);
+    }
   }
   // ---- q_rot = H diag(s) q / sqrt(d) for the G heads (rows >= G are zero)
   const float s_lo = splitmix_sign(a.kseed, L), s_hi = splitmix_sign(a.kseed, L + 64);
@@ -181,10 +249,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   for (int k = 0; k < kHeadsPerWave; ++k) {
     const int hh = wave + kWaves * k;
     float q0 = qv[k][0] * s_lo, q1 = qv[k][1] * s_hi;
-    wht128(q0, q1);
+    if (wave + kWaves * k < G) wht128(q0, q1);
     qs[hh * 132 + L] = q0 * kInvSqrtD;
     qs[hh * 132 + L + 64] = q1 * kInvSqrtD;
-    if (L < 4) qs[hh * 132 + 128 + L] = 0.0f;   // pad coordinate 128 (and slack)
   }
   __syncthreads();
 
@@ -233,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < 3; ++c) o[i][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;            // of head `col`
-  uint32_t* st = &stage[wave * WV * kStageStride];
+  uint32_t* st = &stage[wave * kBlock * kStageRow];
   const float qjl_c = 1.2533141373155003f * kInvSqrtD;   // sqrt(pi / 2) / sqrt(d)
 
   // value-side positions of this lane's triplets 16 grp + col
@@ -247,26 +314,55 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     vnsh[i] = (tri * BN) & 31;
   }
 
+  constexpr int kVW = (WV * kBlock + 63) / 64;     // staged value words per lane
   for (int t0 = t_begin + wave * kBlock; t0 < t_end; t0 += kWaves * kBlock) {
-    // -- stage the block's value words (word w of 32 tokens is 128 B)
-    for (int e = L; e < WV * kBlock; e += 64) {
-      const int w = e >> 5, tk = e & 31;
-      st[w * kStageStride + tk] =
-          w < WD ? a.vdir[tile_word(plane, a.capacity, t0 + tk, w, WD)]
-                 : a.vnrm[tile_word(plane, a.capacity, t0 + tk, w - WD, WN)];
+    // -- every global load of the block is issued before any of them is used,
+    //    so the block waits for memory once
+    uint32_t vw[kVW];
+#pragma unroll
+    for (int j = 0; j < kVW; ++j) {
+      const int e = L + 64 * j, w = e >> 5, tk = e & 31;
+      vw[j] = 0u;
+      if (e < WV * kBlock)
+        vw[j] = w < WD ? a.vdir[tile_word(plane, a.capacity, t0 + tk, w, WD)]
+                       : a.vnrm[tile_word(plane, a.capacity, t0 + tk, w - WD, WN)];
+    }
+    uint32_t dws[2][WD + 1], nws[2][WN + 1], sws[2][QJL ? 4 : 1];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int tok = t0 + 16 * kt + col;
+#pragma unroll
+      for (int w = 0; w < WD; ++w) dws[kt][w] = a.kdir[tile_word(plane, a.capacity, tok, w, WD)];
+#pragma unroll
+      for (int w = 0; w < WN; ++w) nws[kt][w] = a.knrm[tile_word(plane, a.capacity, tok, w, WN)];
+      dws[kt][WD] = 0u;
+      nws[kt][WN] = 0u;
+      if (QJL) {
+#pragma unroll
+        for (int k = 0; k < (QJL ? 4 : 1); ++k) sws[kt][k] = a.kqjl[tile_word(plane, a.capacity, tok, k, 4)];
+      }
+    }
+    float4 gk4[2], gv4[2];
+    uint2 grs[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int tb = t0 + 16 * kt + 4 * grp4;
+      gk4[kt] = *reinterpret_cast<const float4*>(&a.kgamma[plane * a.capacity + tb]);
+      gv4[kt] = *reinterpret_cast<const float4*>(&a.vgamma[plane * a.capacity + tb]);
+      if (QJL) grs[kt] = *reinterpret_cast<const uint2*>(&a.kgamma_r[plane * a.capacity + tb]);
+    }
+    // -- stage the block's value words, token-major
+#pragma unroll
+    for (int j = 0; j < kVW; ++j) {
+      const int e = L + 64 * j, w = e >> 5, tk = e & 31;
+      if (e < WV * kBlock) st[tk * kStageRow + w] = vw[j];
     }
     // -- scores, two 16-token tiles
     floatx4 sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int tok = t0 + 16 * kt + col;
-      uint32_t dw[WD + 1], nw[WN + 1];
-#pragma unroll
-      for (int w = 0; w < WD; ++w) dw[w] = a.kdir[tile_word(plane, a.capacity, tok, w, WD)];
-#pragma unroll
-      for (int w = 0; w < WN; ++w) nw[w] = a.knrm[tile_word(plane, a.capacity, tok, w, WN)];
-      dw[WD] = 0u;
-      nw[WN] = 0u;
+      uint32_t* dw = dws[kt];
+      uint32_t* nw = nws[kt];
       // shift the record so that triplet 4 e + grp4 starts at bit 4 e FWD
       const uint32_t dsh = grp4 * FWD, nsh = grp4 * BN;
 #pragma unroll
@@ -276,55 +372,70 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
-        float ux[8], uy[8], uz[8];
+        half8 ah[3], al[3];
+        if (PRE) {
+          uint4 E[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tri = 32 * gi + 4 * e;       // relative triplet index
-          if (gi == 1 && e >= 3) {
-            ux[e] = uy[e] = uz[e] = 0.0f;
-            continue;
+          for (int e = 0; e < 8; ++e) {
+            const int tri = 32 * gi + 4 * e;       // relative triplet index
+            if (gi == 1 && e >= 3) {
+              E[e] = make_uint4(0u, 0u, 0u, 0u);
+              continue;
+            }
+            E[e] = tabk[field<FWD>(dw, tri * FWD) * R + field<BN>(nw, tri * BN)];
           }
-          const float4 n = lutk[field<FWD>(dw, tri * FWD)];
-          const float rho = crk[field<BN>(nw, tri * BN)];
-          ux[e] = rho * n.x;
-          uy[e] = rho * n.y;
-          uz[e] = rho * n.z;
+          operands_pre(E, ah, al);
+        } else {
+          float ux[8], uy[8], uz[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int tri = 32 * gi + 4 * e;
+            if (gi == 1 && e >= 3) {
+              ux[e] = uy[e] = uz[e] = 0.0f;
+              continue;
+            }
+            const uint4 n = tabk[field<FWD>(dw, tri * FWD)];
+            const float rho = crk[field<BN>(nw, tri * BN)];
+            ux[e] = rho * __uint_as_float(n.x);
+            uy[e] = rho * __uint_as_float(n.y);
+            uz[e] = rho * __uint_as_float(n.z);
+          }
+          split8(ux, ah[0], al[0]);
+          split8(uy, ah[1], al[1]);
+          split8(uz, ah[2], al[2]);
         }
-        half8 ah, al;
-        split8(ux, ah, al);
-        acc = mfma3(ah, al, qh[gi][0], ql[gi][0], acc);
-        split8(uy, ah, al);
-        acc = mfma3(ah, al, qh[gi][1], ql[gi][1], acc);
-        split8(uz, ah, al);
-        acc = mfma3(ah, al, qh[gi][2], ql[gi][2], acc);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) acc = mfma3(ah[c], al[c], qh[gi][c], ql[gi][c], acc);
       }
       // this lane's 4 tokens: t0 + 16 kt + 4 grp4 + r, head col
       const int tb = t0 + 16 * kt + 4 * grp4;
-      const float4 gk = *reinterpret_cast<const float4*>(&a.kgamma[plane * a.capacity + tb]);
-      const float gka[4] = {gk.x, gk.y, gk.z, gk.w};
+      const float gka[4] = {gk4[kt].x, gk4[kt].y, gk4[kt].z, gk4[kt].w};
       float s4[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) s4[r] = acc[r] * (1.0f / kUScale);
       if (QJL) {
-        uint32_t sw[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) sw[k] = a.kqjl[tile_word(plane, a.capacity, tok, k, 4)];
+        const uint32_t* sw = sws[kt];
         floatx4 qa = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           // sigma_j = -1 where the bit is set: fp16 +-1 = 0x3C00 | bit << 15
           const uint32_t byte = (sw[k] >> (8 * grp4)) & 0xffu;
-          half8 sg;
+          u32x4 sg;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            sg[e] = ((byte >> e) & 1u) ? (_Float16)-1.0f : (_Float16)1.0f;
-          qa = mfma(sg, pl[k], qa);
-          qa = mfma(sg, ph[k], qa);
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t bits = byte >> (2 * m);
+            sg[m] = 0x3C003C00u | ((bits & 1u) << 15) | ((bits & 2u) << 30);
+          }
+          const half8 sgh = __builtin_bit_cast(half8, sg);
+          qa = mfma(sgh, pl[k], qa);
+          qa = mfma(sgh, ph[k], qa);
         }
-        const uint16_t* grp_r = &a.kgamma_r[plane * a.capacity + tb];
+        const uint32_t gr2[2] = {grs[kt].x, grs[kt].y};
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          s4[r] += qjl_c * (float)__builtin_bit_cast(_Float16, grp_r[r]) * qa[r];
+        for (int r = 0; r < 4; ++r) {
+          const uint16_t h = (uint16_t)(gr2[r >> 1] >> (16 * (r & 1)));
+          s4[r] += qjl_c * (float)__builtin_bit_cast(_Float16, h) * qa[r];
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -345,9 +456,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     float pw[8], psum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int tb = t0 + 16 * kt + 4 * grp4;
-      const float4 gv = *reinterpret_cast<const float4*>(&a.vgamma[plane * a.capacity + tb]);
-      const float gva[4] = {gv.x, gv.y, gv.z, gv.w};
+      const float gva[4] = {gv4[kt].x, gv4[kt].y, gv4[kt].z, gv4[kt].w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = sc[kt][r] == -INFINITY ? 0.0f : __expf(sc[kt][r] - m_new);
@@ -361,98 +470,103 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     m_run = m_new;
     half8 pah, pal;
     split8(pw, pah, pal);
-    // rescale O rows (heads 4 grp4 + r)
-    float al[4];
+    // rescale O rows (heads 4 grp4 + r) unless no running maximum moved
+    if (__ballot(alpha != 1.0f)) {
+      float al[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp4 + r, 64);
+      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp4 + r, 64);
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
+      for (int i = 0; i < 3; ++i)
 #pragma unroll
-      for (int c = 0; c < 3; ++c)
+        for (int c = 0; c < 3; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[i][c][r] *= al[r];
+          for (int r = 0; r < 4; ++r) o[i][c][r] *= al[r];
+    }
     // -- values: triplet 16 grp + col for this lane group's 8 tokens
     wave_sync();
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      float vx[8], vy[8], vz[8];
       const bool tri_ok = 16 * i + col < kNTri;
+      half8 bh[3], bl[3];
+      if (PRE) {
+        uint4 E[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tk = 16 * (e >> 2) + 4 * grp4 + (e & 3);
-        const uint32_t d0 = st[vdw[i] * kStageStride + tk];
-        const uint32_t d1 = st[min(vdw[i] + 1, WV - 1) * kStageStride + tk];
-        const uint32_t n0 = st[vnw[i] * kStageStride + tk];
-        const uint32_t n1 = st[min(vnw[i] + 1, WV - 1) * kStageStride + tk];
-        const uint32_t code = __builtin_amdgcn_alignbit(d1, d0, vdsh[i]) & kDirMask;
-        const uint32_t ir = __builtin_amdgcn_alignbit(n1, n0, vnsh[i]) & kNrmMask;
-        const float4 n = lutv[code];
-        const float rho = tri_ok ? crv[ir] : 0.0f;
-        vx[e] = rho * n.x;
-        vy[e] = rho * n.y;
-        vz[e] = rho * n.z;
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t* sr = &st[(16 * (e >> 2) + 4 * grp4 + (e & 3)) * kStageRow];
+          const uint32_t code = __builtin_amdgcn_alignbit(sr[vdw[i] + 1], sr[vdw[i]], vdsh[i]) & kDirMask;
+          const uint32_t ir = __builtin_amdgcn_alignbit(sr[vnw[i] + 1], sr[vnw[i]], vnsh[i]) & kNrmMask;
+          E[e] = tri_ok ? tabv[code * R + ir] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        operands_pre(E, bh, bl);
+      } else {
+        float vx[8], vy[8], vz[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t* sr = &st[(16 * (e >> 2) + 4 * grp4 + (e & 3)) * kStageRow];
+          const uint32_t code = __builtin_amdgcn_alignbit(sr[vdw[i] + 1], sr[vdw[i]], vdsh[i]) & kDirMask;
+          const uint32_t ir = __builtin_amdgcn_alignbit(sr[vnw[i] + 1], sr[vnw[i]], vnsh[i]) & kNrmMask;
+          const uint4 n = tabv[code];
+          const float rho = tri_ok ? crv[ir] : 0.0f;
+          vx[e] = rho * __uint_as_float(n.x);
+          vy[e] = rho * __uint_as_float(n.y);
+          vz[e] = rho * __uint_as_float(n.z);
+        }
+        split8(vx, bh[0], bl[0]);
+        split8(vy, bh[1], bl[1]);
+        split8(vz, bh[2], bl[2]);
       }
-      half8 bh, bl;
-      split8(vx, bh, bl);
-      o[i][0] = mfma3(pah, pal, bh, bl, o[i][0]);
-      split8(vy, bh, bl);
-      o[i][1] = mfma3(pah, pal, bh, bl, o[i][1]);
-      split8(vz, bh, bl);
-      o[i][2] = mfma3(pah, pal, bh, bl, o[i][2]);
+#pragma unroll
+      for (int c = 0; c < 3; ++c) o[i][c] = mfma3(pah, pal, bh[c], bl[c], o[i][c]);
     }
     wave_sync();
   }
 
-  // ---- merge the waves: partial (m, l, O) of this split
+  // ---- merge the waves: partial (m, l, O) of this split.  The tables are
+  // dead now; their LDS holds the per-wave value sums.
   __syncthreads();
-  for (int h0 = 0; h0 < G; h0 += 8) {              // eight heads at a time
-
-    const int hn = min(8, G - h0);
-    if (grp4 == 0 && col >= h0 && col < h0 + hn) {
-      red_ml[(wave * kMaxG + col) * 2] = m_run;
-      red_ml[(wave * kMaxG + col) * 2 + 1] = l_run;
-    }
+  if (grp4 == 0 && col < G) {
+    red_ml[(wave * kMaxG + col) * 2] = m_run;
+    red_ml[(wave * kMaxG + col) * 2 + 1] = l_run;
+  }
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < 3; ++i)
 #pragma unroll
-      for (int c = 0; c < 3; ++c) {
-        const int coord = 3 * (16 * i + col) + c;
+    for (int c = 0; c < 3; ++c) {
+      const int coord = 3 * (16 * i + col) + c;
+      if (coord < kHeadDim) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int h = 4 * grp4 + r;
-          if (coord < kHeadDim && h >= h0 && h < h0 + hn)
-            red_o[(wave * 8 + (h - h0)) * kHeadDim + coord] = o[i][c][r];
-        }
+        for (int r = 0; r < 4; ++r) red_o[(wave * kMaxG + 4 * grp4 + r) * kHeadDim + coord] = o[i][c][r];
       }
-    __syncthreads();
-    for (int e = tid; e < hn * kHeadDim; e += kThreads) {
-      const int hl = e >> 7, c = e & 127, h = h0 + hl;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[(w * kMaxG + h) * 2]);
-      float Lsum = 0.0f, A = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = red_ml[(w * kMaxG + h) * 2];
-        const float f = mw == -INFINITY ? 0.0f : __expf(mw - M);
-        Lsum += f * red_ml[(w * kMaxG + h) * 2 + 1];
-        A += f * red_o[(w * 8 + hl) * kHeadDim + c];
-      }
-      const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_split + split;
-      a.ws_acc[row * kHeadDim + c] = A;
-      if (c == 0) a.ws_ml[row] = make_float2(M, Lsum);
     }
-    __syncthreads();
+  __syncthreads();
+  for (int e = tid; e < G * kHeadDim; e += kThreads) {
+    const int h = e >> 7, c = e & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[(w * kMaxG + h) * 2]);
+    float Lsum = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = red_ml[(w * kMaxG + h) * 2];
+      const float f = mw == -INFINITY ? 0.0f : __expf(mw - M);
+      Lsum += f * red_ml[(w * kMaxG + h) * 2 + 1];
+      A += f * red_o[(w * kMaxG + h) * kHeadDim + c];
+    }
+    const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_split + split;
+    a.ws_acc[row * kHeadDim + c] = A;
+    if (c == 0) a.ws_ml[row] = make_float2(M, Lsum);
   }
 }
 
 // Merges the splits of one (batch, query head) by their log-sum-exp, in split
-// order, and applies R_v^T = diag(s_v) H / sqrt(d).  Four wavefronts take the
-// splits round-robin; the partial sums meet in LDS.
+// order, and applies R_v^T = diag(s_v) H / sqrt(d).  Four wavefronts take
+// the splits round-robin, eight loads in flight per lane; the partial sums
+// meet in LDS.
 __global__ __launch_bounds__(256) void merge_kernel(const float2* __restrict__ ws_ml,
                                                     const float* __restrict__ ws_acc,
                                                     int n_split, int Hq, uint64_t vseed,
                                                     float* __restrict__ out) {
+  constexpr int kU = 8;
   __shared__ float part[kWaves][2 * 64 + 1];
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
   const size_t row0 = ((size_t)blockIdx.y * Hq + blockIdx.x) * n_split;
@@ -464,18 +578,18 @@ __global__ __launch_bounds__(256) void merge_kernel(const float2* __restrict__ w
   M = wave_max(M);
   float Lsum = 0.0f, a0 = 0.0f, a1 = 0.0f;
   if (M != -INFINITY) {
-    for (int s0 = wave; s0 < n_split; s0 += 4 * kWaves) {
-      float2 ml[4];
-      float x0[4], x1[4];
+    for (int s0 = wave; s0 < n_split; s0 += kU * kWaves) {
+      float2 ml[kU];
+      float x0[kU], x1[kU];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const int s = min(s0 + u * kWaves, n_split - 1);
         ml[u] = ws_ml[row0 + s];
         x0[u] = ws_acc[(row0 + s) * kHeadDim + L];
         x1[u] = ws_acc[(row0 + s) * kHeadDim + L + 64];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const bool in = s0 + u * kWaves < n_split && ml[u].x != -INFINITY;
         const float f = in ? __expf(ml[u].x - M) : 0.0f;
         Lsum += f * ml[u].y;
@@ -625,6 +739,7 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
   a.kc_rho = kc.c_rho;
   a.vc_xi = vc.c_xi;
   a.vc_rho = vc.c_rho;
+  a.shared_tables = kc.c_xi == vc.c_xi && kc.c_rho == vc.c_rho;
   a.kseed = kc.seed;
   a.vseed = vc.seed;
   a.kdir = k_cache->dir;
@@ -641,7 +756,6 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
   char* ws = static_cast<char*>(workspace);
   a.ws_ml = reinterpret_cast<float2*>(ws);
   a.ws_acc = reinterpret_cast<float*>(ws + p.ml_bytes);
-  a.out = out;
 
   switch (kc.b_dir * 10 + kc.b_nrm) {
     case 31: launch<3, 1>(a, kc.qjl, stream); break;
