@@ -1,11 +1,11 @@
 // octo_encode: the OCTOPUS encoder on gfx950.
 //
-// One workgroup (4 wavefronts) encodes 64 consecutive tokens of one
-// (batch, head) plane, following the OCTOPUS paper (arXiv 2605.21226):
-//   Sec. 3.1      gamma = ||x||_2 and u = R x / gamma with R = H diag(s), the
-//                 normalized Walsh-Hadamard transform after a sign flip; one
-//                 wavefront per token, the transform as in-register and
-//                 cross-lane butterflies;
+// One lane encodes one token, entirely in registers, following the OCTOPUS
+// paper (arXiv 2605.21226):
+//   Sec. 3.1      gamma = ||x||_2 and u = R x / gamma with R = H diag(s): the
+//                 sign flip is an xor with a 128-bit mask (wave ballots of
+//                 the SplitMix64 signs), the Walsh-Hadamard transform is the
+//                 7-stage butterfly on the lane's 128 registers;
 //   Sec. 3.2      u zero-padded to 129 coordinates, 43 triplets t_i, the
 //                 octahedral coordinates (xi, eta) of Eq. 5;
 //   Sec. 3.5      scalar Lloyd seeds, then the local 3x3 joint rounding: the
@@ -15,25 +15,29 @@
 //                 rho = ||t||;
 //   Sec. 3.6      with QJL: r = u - u^, sigma = sign(H diag(s') r) and
 //                 gamma_r = fp16(||r||);
-//   Sec. 3      the packed index streams I_dir, I_nrm.
-// Phase 2 spreads the 64 x 43 triplets of the workgroup over all 256 lanes.
-// The decoded unit directions n(xi^, eta^) of every code pair live in LDS,
-// built once per workgroup from C_xi.
+//   Sec. 3        the packed index streams I_dir, I_nrm, assembled in
+//                 registers at constant bit offsets.
+// A workgroup of 256 lanes takes 256 consecutive tokens of one (batch, head)
+// plane; in the tile-64 layout word w of 64 consecutive tokens is 256
+// contiguous bytes, so every word store of a wavefront is one coalesced
+// 256-byte write.  LDS holds the codebooks, their cell boundaries and the
+// decoded unit direction n(xi^, eta^) of every code pair.
 #include <math.h>
+
+#include <type_traits>
 
 #include "octo_internal.h"
 
 namespace octo {
 namespace {
 
-constexpr int kTok = 64;          // tokens per workgroup
-constexpr int kThreads = 256;
-constexpr int kUStride = 132;     // floats per token row of u in LDS
+constexpr int kThreads = 256;     // tokens per workgroup, one per lane
+constexpr float kInvSqrtD = 0.08838834764831845f;
 
 struct EncodeArgs {
   const void* x;
   int64_t s0, s1, s2;             // element strides of b, h, t
-  int is_bf16;
+  int is_bf16, vec16;             // vec16: every row starts 16-byte aligned
   int B, H, T;
   const float* c_xi;
   const float* c_rho;
@@ -47,34 +51,76 @@ struct EncodeArgs {
   int capacity, token_offset;
 };
 
-__device__ inline float load_x(const EncodeArgs& a, int64_t off) {
-  if (a.is_bf16) return bf16_to_f32(static_cast<const uint16_t*>(a.x)[off]);
-  return static_cast<const float*>(a.x)[off];
-}
-
-// Index of the nearest of the N sorted centroids whose N-1 cell boundaries
-// (midpoints) are `mid`: the number of boundaries below x.
-template <int N>
-__device__ inline int nearest(const float* mid, float x) {
+// Nearest of the K sorted centroids of C_xi: the number of the K-1 cell
+// boundaries `mid` below x.  The Lloyd-Max centroids on [-1, 1] lie close to
+// a uniform grid; when every boundary is within one grid cell of the
+// uniform one (`guess_ok`, checked per workgroup), the grid cell of x is at
+// most one index off and two boundary reads give the exact count.
+// Otherwise a binary search does.
+template <int K>
+__device__ inline int seed_index(const float* mid, float x, bool guess_ok) {
+  if (guess_ok) {
+    int g = (int)((x + 1.0f) * (0.5f * K));
+    g = min(max(g, 0), K - 1);
+    const float up = g < K - 1 ? mid[g] : INFINITY;
+    const float dn = g > 0 ? mid[g - 1] : -INFINITY;
+    const int r = x > up ? g + 1 : (x > dn ? g : g - 1);
+    return min(max(r, 0), K - 1);      // (only a NaN input could leave the range)
+  }
   int idx = 0;
 #pragma unroll
-  for (int step = N >> 1; step > 0; step >>= 1)
+  for (int step = K >> 1; step > 0; step >>= 1)
     if (x > mid[idx + step - 1]) idx += step;
   return idx;
 }
 
-// Packs word w of a stream of kNTri fields of FW bits (LSB-first).
-template <int FW, typename Get>
-__device__ inline uint32_t pack_word(int w, Get get) {
-  const int lo = (32 * w) / FW;
-  int hi = (32 * w + 31) / FW;
-  if (hi > kNTri - 1) hi = kNTri - 1;
-  uint32_t out = 0;
-  for (int i = lo; i <= hi; ++i) {
-    const int shift = i * FW - 32 * w + 32;  // in [33 - FW, 63]
-    out |= (uint32_t)(((uint64_t)get(i) << shift) >> 32);
+// The same count for the few C_rho boundaries held in registers.
+template <int R>
+__device__ inline int rho_index(const float (&mid)[R > 1 ? R - 1 : 1], float x) {
+  int idx = 0;
+#pragma unroll
+  for (int k = 0; k < R - 1; ++k) idx += x > mid[k] ? 1 : 0;
+  return idx;
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1: the register
+// array indices in the body stay compile-time constants however large the
+// body is (a pragma unroll gives up on the 43 encoder triplets).
+template <int B, int E>
+struct StaticFor {
+  template <class F>
+  __device__ static inline void run(F&& f) {
+    f(std::integral_constant<int, B>{});
+    StaticFor<B + 1, E>::run(f);
   }
-  return out;
+};
+template <int E>
+struct StaticFor<E, E> {
+  template <class F>
+  __device__ static inline void run(F&&) {}
+};
+
+// Unnormalized Walsh-Hadamard transform of 128 registers (Sylvester order).
+__device__ inline void wht128_regs(float (&v)[128]) {
+#pragma unroll
+  for (int h = 1; h < 128; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 128; ++i)
+      if (!(i & h)) {
+        const float p = v[i], q = v[i + h];
+        v[i] = p + q;
+        v[i + h] = p - q;
+      }
+}
+
+// Flips the sign of v[j] where bit j of the 128-bit mask (m0: j < 64) is set.
+__device__ inline void flip_signs(float (&v)[128], uint64_t m0, uint64_t m1) {
+#pragma unroll
+  for (int j = 0; j < 128; ++j) {
+    const uint64_t m = j < 64 ? m0 : m1;
+    const uint32_t bit = (uint32_t)(m >> (j & 63)) & 1u;
+    v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (bit << 31));
+  }
 }
 
 template <int BD, int BN>
@@ -85,23 +131,79 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
 
   __shared__ float4 lut[K * K];                       // n(c_xi[i], c_xi[j]) at i + K j
   __shared__ float cxi[K], mid_xi[K], crho[R], mid_rho[R];
-  __shared__ float sgn[2 * kHeadDim];                 // s then s'
-  __shared__ float u[kTok * kUStride];
-  __shared__ uint16_t code_dir[kTok * kNTri];
-  __shared__ uint8_t code_nrm[kTok * kNTri];
+  __shared__ int guess_bad;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int t0 = blockIdx.x * kTok;
+  const int t = blockIdx.x * kThreads + tid;
+  const bool valid = t < a.T;
+  const size_t plane = (size_t)b * a.H + h;
 
-  // ---- tables: signs, codebooks, midpoints, the decoded direction of every
-  // code pair (codebooks go through LDS so that the table loop reads no
-  // global memory)
-  for (int j = tid; j < 2 * kHeadDim; j += kThreads) sgn[j] = splitmix_sign(a.seed, j);
+  // ---- signs of R (and R') as 128-bit masks, identical in every lane
+  const int ln = tid & 63;
+  const uint64_t sm0 = __ballot(splitmix_sign(a.seed, ln) < 0.0f);
+  const uint64_t sm1 = __ballot(splitmix_sign(a.seed, ln + 64) < 0.0f);
+  const uint64_t qm0 = __ballot(splitmix_sign(a.seed, kHeadDim + ln) < 0.0f);
+  const uint64_t qm1 = __ballot(splitmix_sign(a.seed, kHeadDim + ln + 64) < 0.0f);
+
+  // ---- the row of this token, issued before the tables are built
+  float v[128];
+  {
+    const int64_t off = (int64_t)b * a.s0 + (int64_t)h * a.s1 + (int64_t)(valid ? t : 0) * a.s2;
+    if (a.is_bf16) {
+      const uint16_t* row = static_cast<const uint16_t*>(a.x) + off;
+      if (a.vec16) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const uint4 w = reinterpret_cast<const uint4*>(row)[k];
+          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            v[8 * k + 2 * m] = __uint_as_float(ws[m] << 16);
+            v[8 * k + 2 * m + 1] = __uint_as_float(ws[m] & 0xffff0000u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 128; ++j) v[j] = bf16_to_f32(row[j]);
+      }
+    } else {
+      const float* row = static_cast<const float*>(a.x) + off;
+      if (a.vec16) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const float4 w = reinterpret_cast<const float4*>(row)[k];
+          v[4 * k] = w.x;
+          v[4 * k + 1] = w.y;
+          v[4 * k + 2] = w.z;
+          v[4 * k + 3] = w.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 128; ++j) v[j] = row[j];
+      }
+    }
+    if (!valid) {
+#pragma unroll
+      for (int j = 0; j < 128; ++j) v[j] = 0.0f;
+    }
+  }
+
+  // ---- tables: codebooks, cell boundaries, decoded directions
   if (tid < K) cxi[tid] = a.c_xi[tid];
   if (tid < R) crho[tid] = a.c_rho[tid];
+  if (tid == 0) guess_bad = 0;
   __syncthreads();
-  if (tid < K - 1) mid_xi[tid] = 0.5f * (cxi[tid] + cxi[tid + 1]);
+  if (tid < K - 1) {
+    const float m = 0.5f * (cxi[tid] + cxi[tid + 1]);
+    mid_xi[tid] = m;
+    // uniform grid boundaries b_k = -1 + 2 (k + 1) / K; the one-step
+    // correction is exact when b_(k-1) <= mid_k < b_(k+1) (with a margin
+    // for the rounding of the grid index)
+    const float lo = tid > 0 ? -1.0f + 2.0f * tid / K : -INFINITY;
+    const float hi = tid + 2 < K ? -1.0f + 2.0f * (tid + 2) / K : INFINITY;
+    if (!(m >= lo + 1e-5f && m < hi - 1e-5f)) guess_bad = 1;
+  }
   if (tid < R - 1) mid_rho[tid] = 0.5f * (crho[tid] + crho[tid + 1]);
   for (int e = tid; e < K * K; e += kThreads) {
     // Eq. 6 with the fold of App. C.7, then normalization onto S^2.
@@ -116,135 +218,127 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     lut[e] = make_float4(x / n, y / n, z / n, 0.0f);
   }
   __syncthreads();
-
-  // ---- phase 1: gamma and the rotation, one wavefront per token
-  const size_t plane = (size_t)b * a.H + h;
-  const int64_t base = (int64_t)b * a.s0 + (int64_t)h * a.s1;
-  const float inv_sqrt_d = 0.08838834764831845f;     // 1/sqrt(128)
-  // each wave takes 16 tokens, loading all of them before any use
-  constexpr int kPerWave = kTok / 4;
-  float xs[kPerWave][2];
+  const bool guess_ok = guess_bad == 0;
+  float mr[R > 1 ? R - 1 : 1];
 #pragma unroll
-  for (int j = 0; j < kPerWave; ++j) {
-    const int t = t0 + wave + 4 * j;
-    xs[j][0] = xs[j][1] = 0.0f;
-    if (t < a.T) {
-      const int64_t off = base + (int64_t)t * a.s2;
-      xs[j][0] = load_x(a, off + lane);
-      xs[j][1] = load_x(a, off + lane + 64);
-    }
-  }
-  const float s_lo = sgn[lane], s_hi = sgn[lane + 64];
-#pragma unroll
-  for (int j = 0; j < kPerWave; ++j) {
-    const int k = wave + 4 * j, t = t0 + k;
-    const float x0 = xs[j][0], x1 = xs[j][1];
-    const float gamma = sqrtf(wave_sum(x0 * x0 + x1 * x1));
-    float v0 = x0 * s_lo, v1 = x1 * s_hi;
-    wht128(v0, v1);
-    const float scale = inv_sqrt_d / fmaxf(gamma, kEps);
-    u[k * kUStride + lane] = v0 * scale;
-    u[k * kUStride + lane + 64] = v1 * scale;
-    if (lane == 0) {
-      u[k * kUStride + kHeadDim] = 0.0f;              // the zero pad (Sec. 3.2)
-      if (t < a.T) a.gamma[plane * a.capacity + a.token_offset + t] = gamma;
-    }
-  }
-  __syncthreads();
+  for (int k = 0; k < R - 1; ++k) mr[k] = mid_rho[k];
 
-  // ---- phase 2: per triplet, octahedral map, seeds, joint rounding
-  for (int e = tid; e < kTok * kNTri; e += kThreads) {
-    const int k = e / kNTri, i = e - k * kNTri;
-    float* tp = &u[k * kUStride + 3 * i];
-    const float tx = tp[0], ty = tp[1], tz = tp[2];
+  // ---- gamma, sign flip, rotation (Sec. 3.1)
+  float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 128; ++j) ss[j & 3] = fmaf(v[j], v[j], ss[j & 3]);
+  const float gamma = sqrtf((ss[0] + ss[1]) + (ss[2] + ss[3]));
+  flip_signs(v, sm0, sm1);
+  wht128_regs(v);
+  const float scale = kInvSqrtD / fmaxf(gamma, kEps);
+#pragma unroll
+  for (int j = 0; j < 128; ++j) v[j] *= scale;
+
+  // ---- triplets: octahedral map, seeds, joint rounding, packing
+  uint32_t dw[WD + 1], nw[WN + 1];
+#pragma unroll
+  for (int w = 0; w <= WD; ++w) dw[w] = 0u;
+#pragma unroll
+  for (int w = 0; w <= WN; ++w) nw[w] = 0u;
+  const bool scalar = a.rounding == OCTO_ROUND_SCALAR;
+  StaticFor<0, kNTri>::run([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    // one triplet at a time: keeps the scheduler from interleaving the 43
+    // iterations (and their table reads) into a register spill
+    __builtin_amdgcn_sched_barrier(0);
+    const float tx = v[3 * i], ty = v[3 * i + 1];
+    const float tz = 3 * i + 2 < kHeadDim ? v[3 * i + 2] : 0.0f;   // the zero pad
     // Eq. 5 on the L1-normalized direction, sign(0) = +1.
-    const float l1 = fmaxf(fabsf(tx) + fabsf(ty) + fabsf(tz), kEps);
-    const float px = tx / l1, py = ty / l1, pz = tz / l1;
+    const float inv_l1 = 1.0f / fmaxf(fabsf(tx) + fabsf(ty) + fabsf(tz), kEps);
+    const float px = tx * inv_l1, py = ty * inv_l1, pz = tz * inv_l1;
     float xi = px, eta = py;
     if (pz < 0.0f) {
       xi = (px >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(py));
       eta = (py >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(px));
     }
-    const int sx = nearest<K>(mid_xi, xi), sy = nearest<K>(mid_xi, eta);
+    const int sx = seed_index<K>(mid_xi, xi, guess_ok);
+    const int sy = seed_index<K>(mid_xi, eta, guess_ok);
     int bx = sx, by = sy, ir;
-    if (a.rounding == OCTO_ROUND_SCALAR) {
-      ir = nearest<R>(mid_rho, sqrtf(tx * tx + ty * ty + tz * tz));
+    float4 nb;
+    if (scalar) {
+      ir = rho_index<R>(mr, sqrtf(tx * tx + ty * ty + tz * tz));
+      nb = lut[sx + K * sy];
     } else {
       // Seed first, then the other eight neighbours row-major (dx outer);
       // only a strictly larger s replaces the incumbent.
-      float4 n = lut[sx + K * sy];
-      float best = tx * n.x + ty * n.y + tz * n.z;
+      nb = lut[sx + K * sy];
+      float best = tx * nb.x + ty * nb.y + tz * nb.z;
 #pragma unroll
       for (int dx = -1; dx <= 1; ++dx)
 #pragma unroll
         for (int dy = -1; dy <= 1; ++dy) {
           if (dx == 0 && dy == 0) continue;
           const int cx = min(max(sx + dx, 0), K - 1), cy = min(max(sy + dy, 0), K - 1);
-          n = lut[cx + K * cy];
+          const float4 n = lut[cx + K * cy];
           const float s = tx * n.x + ty * n.y + tz * n.z;
           if (s > best) {
             best = s;
             bx = cx;
             by = cy;
+            nb = n;
           }
         }
-      ir = nearest<R>(mid_rho, best);
+      ir = rho_index<R>(mr, best);
     }
-    code_dir[k * kNTri + i] = (uint16_t)(bx | (by << BD));
-    code_nrm[k * kNTri + i] = (uint8_t)ir;
+    // pack at constant bit offsets (LSB-first streams)
+    const uint32_t code = (uint32_t)(bx | (by << BD));
+    {
+      constexpr int pos = i * FWD, w = pos >> 5, sh = pos & 31;
+      dw[w] |= code << sh;
+      if (sh + FWD > 32) dw[w + 1] |= code >> ((32 - sh) & 31);
+    }
+    {
+      constexpr int pos = i * BN, w = pos >> 5, sh = pos & 31;
+      nw[w] |= (uint32_t)ir << sh;
+      if (sh + BN > 32) nw[w + 1] |= (uint32_t)ir >> ((32 - sh) & 31);
+    }
     if (a.qjl) {
-      // Rotated-frame residual r = u - u^ written over u (Sec. 3.6).
-      const float4 n = lut[bx + K * by];
+      // rotated-frame residual r = u - u^ (Sec. 3.6), over the real coordinates
       const float rho = crho[ir];
-      tp[0] = tx - rho * n.x;
-      tp[1] = ty - rho * n.y;
-      tp[2] = tz - rho * n.z;
+      v[3 * i] = tx - rho * nb.x;
+      v[3 * i + 1] = ty - rho * nb.y;
+      if (3 * i + 2 < kHeadDim) v[3 * i + 2] = tz - rho * nb.z;
     }
-  }
-  __syncthreads();
+  });
 
-  // ---- phase 3: pack I_dir and I_nrm (token-fastest items: coalesced stores)
-  const int t_valid = min(kTok, a.T - t0);
-  for (int e = tid; e < kTok * (WD + WN); e += kThreads) {
-    const int k = e & 63, w = e >> 6;
-    if (k >= t_valid) continue;
-    const int tc = a.token_offset + t0 + k;
-    if (w < WD) {
-      const uint16_t* cd = &code_dir[k * kNTri];
-      a.dir[tile_word(plane, a.capacity, tc, w, WD)] =
-          pack_word<FWD>(w, [&](int i) { return (uint32_t)cd[i]; });
-    } else {
-      const uint8_t* cn = &code_nrm[k * kNTri];
-      a.nrm[tile_word(plane, a.capacity, tc, w - WD, WN)] =
-          pack_word<BN>(w - WD, [&](int i) { return (uint32_t)cn[i]; });
-    }
+  // ---- stores: word w of 64 consecutive tokens is 256 contiguous bytes
+  const int tc = a.token_offset + t;
+  if (valid) {
+#pragma unroll
+    for (int w = 0; w < WD; ++w) a.dir[tile_word(plane, a.capacity, tc, w, WD)] = dw[w];
+#pragma unroll
+    for (int w = 0; w < WN; ++w) a.nrm[tile_word(plane, a.capacity, tc, w, WN)] = nw[w];
+    a.gamma[plane * a.capacity + tc] = gamma;
   }
 
-  // ---- phase 4 (QJL): sigma = sign(H diag(s') r), gamma_r = fp16(||r||)
+  // ---- QJL: sigma = sign(H diag(s') r), gamma_r = fp16(||r||)
   if (a.qjl) {
-    for (int k = wave; k < t_valid; k += 4) {
-      const float r0 = u[k * kUStride + lane], r1 = u[k * kUStride + lane + 64];
-      const float rn = sqrtf(wave_sum(r0 * r0 + r1 * r1));
-      float v0 = r0 * sgn[kHeadDim + lane], v1 = r1 * sgn[kHeadDim + lane + 64];
-      wht128(v0, v1);
-      const uint64_t m0 = __ballot(v0 < 0.0f), m1 = __ballot(v1 < 0.0f);
-      const int tc = a.token_offset + t0 + k;
-      if (lane < 4) {
-        const uint64_t m = lane < 2 ? m0 : m1;
-        a.qjl_bits[tile_word(plane, a.capacity, tc, lane, 4)] =
-            (uint32_t)(m >> (32 * (lane & 1)));
-      }
-      if (lane == 0) {
-        const _Float16 hr = (_Float16)rn;
-        a.gamma_r[plane * a.capacity + tc] = __builtin_bit_cast(uint16_t, hr);
-      }
+    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 128; ++j) rs[j & 3] = fmaf(v[j], v[j], rs[j & 3]);
+    const float rn = sqrtf((rs[0] + rs[1]) + (rs[2] + rs[3]));
+    flip_signs(v, qm0, qm1);
+    wht128_regs(v);
+    uint32_t sw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 128; ++j) sw[j >> 5] |= (uint32_t)(v[j] < 0.0f) << (j & 31);
+    if (valid) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) a.qjl_bits[tile_word(plane, a.capacity, tc, w, 4)] = sw[w];
+      const _Float16 hr = (_Float16)rn;
+      a.gamma_r[plane * a.capacity + tc] = __builtin_bit_cast(uint16_t, hr);
     }
   }
 }
 
 template <int BD, int BN>
 void launch(const EncodeArgs& a, hipStream_t st) {
-  dim3 grid((a.T + kTok - 1) / kTok, a.H, a.B);
+  dim3 grid((a.T + kThreads - 1) / kThreads, a.H, a.B);
   hipLaunchKernelGGL((encode_kernel<BD, BN>), grid, dim3(kThreads), 0, st, a);
 }
 
@@ -288,6 +382,8 @@ extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, 
   a.s1 = x_strides[1];
   a.s2 = x_strides[2];
   a.is_bf16 = x_dtype == OCTO_DTYPE_BF16;
+  a.vec16 = ((uintptr_t)x % 16 == 0) && ((x_strides[0] * esz) % 16 == 0) &&
+            ((x_strides[1] * esz) % 16 == 0) && ((x_strides[2] * esz) % 16 == 0);
   a.B = B;
   a.H = H;
   a.T = T;
