@@ -20,8 +20,11 @@
 // A workgroup of 256 lanes takes 256 consecutive tokens of one (batch, head)
 // plane; in the tile-64 layout word w of 64 consecutive tokens is 256
 // contiguous bytes, so every word store of a wavefront is one coalesced
-// 256-byte write.  LDS holds the codebooks, their cell boundaries and the
-// decoded unit direction n(xi^, eta^) of every code pair.
+// 256-byte write.  LDS holds the codebooks, their cell boundaries and, for
+// every code pair, the decoded unit direction n(xi^, eta^) with the pair's
+// code, in a table padded by one clamped cell per side so that the 3x3
+// search is nine reads at constant offsets and two selects per candidate.
+// The kernel is bound for two wavefronts per SIMD (at most 256 VGPRs).
 #include <math.h>
 
 #include <type_traits>
@@ -52,25 +55,27 @@ struct EncodeArgs {
 };
 
 // Nearest of the K sorted centroids of C_xi: the number of the K-1 cell
-// boundaries `mid` below x.  The Lloyd-Max centroids on [-1, 1] lie close to
-// a uniform grid; when every boundary is within one grid cell of the
-// uniform one (`guess_ok`, checked per workgroup), the grid cell of x is at
-// most one index off and two boundary reads give the exact count.
-// Otherwise a binary search does.
+// boundaries below x.  `midp` holds them padded, midp[0] = -inf,
+// midp[k] = (c_(k-1) + c_k) / 2, midp[K] = +inf.  The Lloyd-Max centroids on
+// [-1, 1] lie close to a uniform grid; when every boundary is within one grid
+// cell of the uniform one (checked per workgroup), the grid cell g of x is at
+// most one index off and the two boundaries around g give the exact count.
 template <int K>
-__device__ inline int seed_index(const float* mid, float x, bool guess_ok) {
-  if (guess_ok) {
-    int g = (int)((x + 1.0f) * (0.5f * K));
-    g = min(max(g, 0), K - 1);
-    const float up = g < K - 1 ? mid[g] : INFINITY;
-    const float dn = g > 0 ? mid[g - 1] : -INFINITY;
-    const int r = x > up ? g + 1 : (x > dn ? g : g - 1);
-    return min(max(r, 0), K - 1);      // (only a NaN input could leave the range)
-  }
+__device__ inline int seed_guess(const float* midp, float x) {
+  int g = (int)fmaf(x, 0.5f * K, 0.5f * K);
+  g = min(max(g, 0), K - 1);
+  const float dn = midp[g], up = midp[g + 1];
+  const int r = g - 1 + (x > dn ? 1 : 0) + (x > up ? 1 : 0);
+  return min(max(r, 0), K - 1);      // (only a NaN input could leave the range)
+}
+
+// The same count by binary search, for codebooks far from the uniform grid.
+template <int K>
+__device__ inline int seed_search(const float* midp, float x) {
   int idx = 0;
 #pragma unroll
   for (int step = K >> 1; step > 0; step >>= 1)
-    if (x > mid[idx + step - 1]) idx += step;
+    if (x > midp[idx + step]) idx += step;
   return idx;
 }
 
@@ -100,10 +105,18 @@ struct StaticFor<E, E> {
   __device__ static inline void run(F&&) {}
 };
 
+// Materializes x in a register at this point.  The compiler otherwise sinks
+// the rotation into the triplet loop and turns the table selects below into
+// branches around partial loads.
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+__device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ inline void pin(floatx4& x) { asm volatile("" : "+v"(x)); }
+
 // Unnormalized Walsh-Hadamard transform of 128 registers (Sylvester order).
+// One stage at a time: interleaving the stages only lengthens live ranges.
 __device__ inline void wht128_regs(float (&v)[128]) {
 #pragma unroll
-  for (int h = 1; h < 128; h <<= 1)
+  for (int h = 1; h < 128; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < 128; ++i)
       if (!(i & h)) {
@@ -111,6 +124,8 @@ __device__ inline void wht128_regs(float (&v)[128]) {
         v[i] = p + q;
         v[i + h] = p - q;
       }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Flips the sign of v[j] where bit j of the 128-bit mask (m0: j < 64) is set.
@@ -124,13 +139,19 @@ __device__ inline void flip_signs(float (&v)[128], uint64_t m0, uint64_t m1) {
 }
 
 template <int BD, int BN>
-__global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
   constexpr int K = 1 << BD, R = 1 << BN;
   constexpr int FWD = 2 * BD;                         // xi | eta << BD
   constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32;
 
-  __shared__ float4 lut[K * K];                       // n(c_xi[i], c_xi[j]) at i + K j
-  __shared__ float cxi[K], mid_xi[K], crho[R], mid_rho[R];
+  constexpr int KP = K + 2;                           // padded side of the direction table
+  // Direction table, padded by one cell on every side: entry (i, j), i, j in
+  // [-1, K], at (i + 1) + KP (j + 1) holds n(c_xi[i'], c_xi[j']) and the code
+  // pair i' | j' << BD of the clamped cell (i', j'), so the 3x3 neighbourhood
+  // of a seed is nine reads at constant offsets, and a clamped neighbour is
+  // the same candidate as the cell it clamps to.
+  __shared__ floatx4 lut[KP * KP];
+  __shared__ float cxi[K], midp[K + 1], crho[R], mid_rho[R];
   __shared__ int guess_bad;
 
   const int tid = threadIdx.x;
@@ -192,11 +213,15 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   // ---- tables: codebooks, cell boundaries, decoded directions
   if (tid < K) cxi[tid] = a.c_xi[tid];
   if (tid < R) crho[tid] = a.c_rho[tid];
-  if (tid == 0) guess_bad = 0;
+  if (tid == 0) {
+    guess_bad = 0;
+    midp[0] = -INFINITY;
+    midp[K] = INFINITY;
+  }
   __syncthreads();
   if (tid < K - 1) {
     const float m = 0.5f * (cxi[tid] + cxi[tid + 1]);
-    mid_xi[tid] = m;
+    midp[tid + 1] = m;
     // uniform grid boundaries b_k = -1 + 2 (k + 1) / K; the one-step
     // correction is exact when b_(k-1) <= mid_k < b_(k+1) (with a margin
     // for the rounding of the grid index)
@@ -205,9 +230,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     if (!(m >= lo + 1e-5f && m < hi - 1e-5f)) guess_bad = 1;
   }
   if (tid < R - 1) mid_rho[tid] = 0.5f * (crho[tid] + crho[tid + 1]);
-  for (int e = tid; e < K * K; e += kThreads) {
+  for (int e = tid; e < KP * KP; e += kThreads) {
     // Eq. 6 with the fold of App. C.7, then normalization onto S^2.
-    const float xi = cxi[e % K], eta = cxi[e / K];
+    const int ci = min(max(e % KP - 1, 0), K - 1), cj = min(max(e / KP - 1, 0), K - 1);
+    const float xi = cxi[ci], eta = cxi[cj];
     const float z = 1.0f - fabsf(xi) - fabsf(eta);
     float x = xi, y = eta;
     if (z < 0.0f) {
@@ -215,10 +241,11 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
       y = (eta >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(xi));
     }
     const float n = fmaxf(sqrtf(x * x + y * y + z * z), kEps);
-    lut[e] = make_float4(x / n, y / n, z / n, 0.0f);
+    lut[e] = floatx4{x / n, y / n, z / n, __uint_as_float((uint32_t)(ci | (cj << BD)))};
   }
   __syncthreads();
-  const bool guess_ok = guess_bad == 0;
+  // uniform: a scalar branch, not a masked one
+  const bool guess_ok = __builtin_amdgcn_readfirstlane(guess_bad) == 0;
   float mr[R > 1 ? R - 1 : 1];
 #pragma unroll
   for (int k = 0; k < R - 1; ++k) mr[k] = mid_rho[k];
@@ -232,7 +259,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   wht128_regs(v);
   const float scale = kInvSqrtD / fmaxf(gamma, kEps);
 #pragma unroll
-  for (int j = 0; j < 128; ++j) v[j] *= scale;
+  for (int j = 0; j < 128; ++j) {
+    v[j] *= scale;
+    pin(v[j]);
+  }
 
   // ---- triplets: octahedral map, seeds, joint rounding, packing
   uint32_t dw[WD + 1], nw[WN + 1];
@@ -240,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   for (int w = 0; w <= WD; ++w) dw[w] = 0u;
 #pragma unroll
   for (int w = 0; w <= WN; ++w) nw[w] = 0u;
-  const bool scalar = a.rounding == OCTO_ROUND_SCALAR;
+  const bool scalar = a.rounding == OCTO_ROUND_SCALAR;     // kernel argument: uniform
   StaticFor<0, kNTri>::run([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     // one triplet at a time: keeps the scheduler from interleaving the 43
@@ -249,44 +279,49 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     const float tx = v[3 * i], ty = v[3 * i + 1];
     const float tz = 3 * i + 2 < kHeadDim ? v[3 * i + 2] : 0.0f;   // the zero pad
     // Eq. 5 on the L1-normalized direction, sign(0) = +1.
-    const float inv_l1 = 1.0f / fmaxf(fabsf(tx) + fabsf(ty) + fabsf(tz), kEps);
+    const float inv_l1 = __builtin_amdgcn_rcpf(fmaxf(fabsf(tx) + fabsf(ty) + fabsf(tz), kEps));
     const float px = tx * inv_l1, py = ty * inv_l1, pz = tz * inv_l1;
     float xi = px, eta = py;
     if (pz < 0.0f) {
       xi = (px >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(py));
       eta = (py >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(px));
     }
-    const int sx = seed_index<K>(mid_xi, xi, guess_ok);
-    const int sy = seed_index<K>(mid_xi, eta, guess_ok);
-    int bx = sx, by = sy, ir;
-    float4 nb;
+    int sx, sy;
+    if (guess_ok) {
+      sx = seed_guess<K>(midp, xi);
+      sy = seed_guess<K>(midp, eta);
+    } else {
+      sx = seed_search<K>(midp, xi);
+      sy = seed_search<K>(midp, eta);
+    }
+    // corner (-1, -1) of the seed's neighbourhood; candidate (dx, dy) sits at
+    // offset (dx + 1) + KP (dy + 1)
+    const floatx4* nbh = &lut[sx + KP * sy];
+    floatx4 n0 = nbh[1 + KP];
+    pin(n0);
+    uint32_t code = __float_as_uint(n0.w);
+    int ir;
     if (scalar) {
       ir = rho_index<R>(mr, sqrtf(tx * tx + ty * ty + tz * tz));
-      nb = lut[sx + K * sy];
     } else {
       // Seed first, then the other eight neighbours row-major (dx outer);
       // only a strictly larger s replaces the incumbent.
-      nb = lut[sx + K * sy];
-      float best = tx * nb.x + ty * nb.y + tz * nb.z;
+      float best = tx * n0.x + ty * n0.y + tz * n0.z;
 #pragma unroll
-      for (int dx = -1; dx <= 1; ++dx)
+      for (int dx = 0; dx < 3; ++dx)
 #pragma unroll
-        for (int dy = -1; dy <= 1; ++dy) {
-          if (dx == 0 && dy == 0) continue;
-          const int cx = min(max(sx + dx, 0), K - 1), cy = min(max(sy + dy, 0), K - 1);
-          const float4 n = lut[cx + K * cy];
+        for (int dy = 0; dy < 3; ++dy) {
+          if (dx == 1 && dy == 1) continue;
+          floatx4 n = nbh[dx + KP * dy];
+          pin(n);
           const float s = tx * n.x + ty * n.y + tz * n.z;
-          if (s > best) {
-            best = s;
-            bx = cx;
-            by = cy;
-            nb = n;
-          }
+          const bool up = s > best;
+          best = up ? s : best;
+          code = up ? __float_as_uint(n.w) : code;
         }
       ir = rho_index<R>(mr, best);
     }
     // pack at constant bit offsets (LSB-first streams)
-    const uint32_t code = (uint32_t)(bx | (by << BD));
     {
       constexpr int pos = i * FWD, w = pos >> 5, sh = pos & 31;
       dw[w] |= code << sh;
@@ -299,6 +334,11 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     }
     if (a.qjl) {
       // rotated-frame residual r = u - u^ (Sec. 3.6), over the real coordinates
+      floatx4 nb = n0;
+      if (!scalar) {
+        nb = lut[(code & (K - 1)) + 1 + KP * ((code >> BD) + 1)];
+        pin(nb);
+      }
       const float rho = crho[ir];
       v[3 * i] = tx - rho * nb.x;
       v[3 * i + 1] = ty - rho * nb.y;
