@@ -114,6 +114,9 @@ def load_codebooks(d=128):
         return json.load(f)
 
 
+_shared_tables = {}
+
+
 class Codec:
     """A codec descriptor with its fp32 codebook tables on `device`.
 
@@ -125,9 +128,20 @@ class Codec:
                  rounding=ROUND_LOCAL3X3, device="cuda", d=128, tables=None):
         if b_dir is None:
             b_dir, b_nrm = bits + 1, bits - 1
-        art = tables or load_codebooks(d)
-        self.c_xi = torch.tensor(art["c_xi"][str(b_dir)], dtype=torch.float32, device=device)
-        self.c_rho = torch.tensor(art["c_rho"][str(b_nrm)], dtype=torch.float32, device=device)
+        if tables is None:
+            # codecs of one (d, split, device) share their device tables, so a
+            # K and a V codec of the same split pass the same pointers and the
+            # attention kernels build one LDS table for both
+            key = (d, b_dir, b_nrm, str(device))
+            if key not in _shared_tables:
+                art = load_codebooks(d)
+                _shared_tables[key] = (
+                    torch.tensor(art["c_xi"][str(b_dir)], dtype=torch.float32, device=device),
+                    torch.tensor(art["c_rho"][str(b_nrm)], dtype=torch.float32, device=device))
+            self.c_xi, self.c_rho = _shared_tables[key]
+        else:
+            self.c_xi = torch.tensor(tables["c_xi"][str(b_dir)], dtype=torch.float32, device=device)
+            self.c_rho = torch.tensor(tables["c_rho"][str(b_nrm)], dtype=torch.float32, device=device)
         self.desc = CodecDesc(ABI_VERSION, d, bits, b_dir, b_nrm, rounding, int(bool(qjl)), 0,
                               seed, self.c_xi.data_ptr(), self.c_rho.data_ptr())
         self.bits, self.b_dir, self.b_nrm, self.seed, self.qjl = bits, b_dir, b_nrm, seed, bool(qjl)

@@ -34,8 +34,11 @@
 //   D[i][j]: i = 4 (L / 16) + r, j = L % 16.
 // Scores are S^T = U Q^T (tokens as rows), so each lane ends up with 4 keys
 // of one query head, which is the A-operand layout P needs in O = P V.
-// Key-side coordinates: lane group g = L / 16 of token row t holds, for
-// call (grp, c), slot e = component c of triplet 32 grp + 4 e + g.
+// Key-side coordinates: lane group g = L / 16 of token row t owns the 11
+// consecutive triplets 11 g .. 11 g + 10 (10 for g = 3) and holds, for call
+// (gi, c), slot e = component c of triplet 11 g + 8 gi + e, so that it reads
+// only the few record words that cover its triplets; with QJL, call k,
+// slot e = sign bit 32 g + 8 k + e, one word of the sign record.
 // Value-side columns: tile (grp, c), column j = component c of triplet
 // 16 grp + j; slot e of lane group g = token 16 (e / 4) + 4 g + e % 4 of the
 // 32-token block, matching the score layout.
@@ -56,14 +59,18 @@ typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWavesSmall = 4;        // waves per workgroup with small tables
+constexpr int kWavesBig = 8;          // ... with the big pre-split table (one per CU)
 constexpr int kBlock = 32;            // tokens per wavefront iteration
-constexpr int kSplitQuantum = 128;    // split lengths are multiples of this
 constexpr int kMaxG = 16;             // query heads per KV head (MFMA columns)
 constexpr float kUScale = 64.0f;      // exact scale of u^ in the operands
 constexpr float kInvSqrtD = 0.08838834764831845f;
-constexpr int kMaxPre = 1024;         // largest pre-split table (entries)
+constexpr int kMaxSmallPre = 1024;    // largest pre-split table beside a second
+                                      // workgroup on the CU (entries)
+
+// Table modes: PRE holds rho^ n^ for every (code pair, norm index), split
+// into fp16 hi/lo; FP32 holds n^ per code pair and rho^ is applied on the fly.
+enum TableMode { kPre = 0, kFp32 = 1 };
 
 struct DecodeArgs {
   const void* q;
@@ -125,7 +132,8 @@ __device__ inline float4 decode_dir(float xi, float eta) {
     x = (xi >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(eta));
     y = (eta >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(xi));
   }
-  const float n = kUScale / fmaxf(sqrtf(x * x + y * y + z * z), kEps);
+  // |x| + |y| + |z| = 1 here, so the squared norm is at least 1/3
+  const float n = kUScale * __builtin_amdgcn_rsqf(x * x + y * y + z * z);
   return make_float4(x * n, y * n, z * n, 0.0f);
 }
 
@@ -169,14 +177,74 @@ __device__ inline void operands_pre(const uint4* E, half8 (&hi)[3], half8 (&lo)[
   lo[2] = __builtin_bit_cast(half8, lz);
 }
 
+constexpr int kTriPerGroup = 11;      // triplets of one key-side lane group
+
+// Record words that cover the bits of 11 triplets of FW bits from any shift.
+constexpr int group_words(int FW) { return (31 + kTriPerGroup * FW + 31) / 32; }
+
+// The global words of one 32-token block of a wavefront.  Key side: lane
+// (col, grp4) holds, for tile kt, the record words of token 16 kt + col that
+// cover the triplets of lane group grp4 (and word grp4 of its sign record);
+// value side: lane L holds word 2 j + L / 32 of token L % 32, for staging in
+// LDS.
 template <int BD, int BN, bool QJL>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
+struct BlockWords {
+  static constexpr int FWD = 2 * BD;
+  static constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32;
+  static constexpr int KWD = group_words(FWD), KWN = group_words(BN);
+  static constexpr int kVD = (WD + 1) / 2, kVN = (WN + 1) / 2;
+  uint32_t dw[2][KWD], nw[2][KWN], sw[2];
+  uint32_t vd[kVD], vn[kVN];
+  float4 gk[2], gv[2];
+  uint2 gr[2];
+};
+
+// Issues every load of the block at t0 (a multiple of 32, below the
+// capacity, which is a multiple of 64, so that the 32 tokens share one
+// 64-token tile).  Words of one token are 256 bytes apart: one base address
+// per stream and immediate offsets; a group's window is clamped to the
+// record (the words past its end only ever feed bits above the last field).
+template <int BD, int BN, bool QJL>
+__device__ inline void load_block(BlockWords<BD, BN, QJL>& r, const DecodeArgs& a, size_t plane,
+                                  int t0, int L) {
+  using BW = BlockWords<BD, BN, QJL>;
+  constexpr int FWD = BW::FWD, WD = BW::WD, WN = BW::WN;
+  const int col = L & 15, grp4 = L >> 4, w0 = L >> 5, tk = L & 31;
+  const int dwo = (kTriPerGroup * FWD * grp4) >> 5, nwo = (kTriPerGroup * BN * grp4) >> 5;
+  const size_t tile = plane * (size_t)(a.capacity >> 6) + (size_t)(t0 >> 6);
+  const int tin = t0 & 63;
+  const size_t gbase = plane * (size_t)a.capacity + (size_t)t0 + 4 * grp4;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const uint32_t* pd = a.kdir + tile * (WD * 64) + tin + 16 * kt + col;
+    const uint32_t* pn = a.knrm + tile * (WN * 64) + tin + 16 * kt + col;
+#pragma unroll
+    for (int w = 0; w < BW::KWD; ++w) r.dw[kt][w] = pd[64 * min(dwo + w, WD - 1)];
+#pragma unroll
+    for (int w = 0; w < BW::KWN; ++w) r.nw[kt][w] = pn[64 * min(nwo + w, WN - 1)];
+    if (QJL) r.sw[kt] = a.kqjl[tile * (4 * 64) + tin + 16 * kt + col + 64 * grp4];
+    r.gk[kt] = *reinterpret_cast<const float4*>(a.kgamma + gbase + 16 * kt);
+    r.gv[kt] = *reinterpret_cast<const float4*>(a.vgamma + gbase + 16 * kt);
+    if (QJL) r.gr[kt] = *reinterpret_cast<const uint2*>(a.kgamma_r + gbase + 16 * kt);
+  }
+  const uint32_t* pvd = a.vdir + tile * (WD * 64) + tin + tk + 64 * w0;
+  const uint32_t* pvn = a.vnrm + tile * (WN * 64) + tin + tk + 64 * w0;
+#pragma unroll
+  for (int j = 0; j < BW::kVD; ++j) r.vd[j] = (2 * j + w0 < WD) ? pvd[128 * j] : 0u;
+#pragma unroll
+  for (int j = 0; j < BW::kVN; ++j) r.vn[j] = (2 * j + w0 < WN) ? pvn[128 * j] : 0u;
+}
+
+template <int BD, int BN, bool QJL, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
+  constexpr int kThreads = 64 * NW, kWaves = NW;
   constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD;
   constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32, WV = WD + WN;
   constexpr uint32_t kDirMask = (1u << FWD) - 1u, kNrmMask = (1u << BN) - 1u;
-  constexpr bool PRE = K * K * R <= kMaxPre;       // pre-split (code, rho) table
-  constexpr int kTab = PRE ? K * K * R : K * K;    // entries per table (16 B each)
-  constexpr int kTabBytes = 2 * kTab * 16;
+  constexpr bool PRE = MODE == kPre;                // pre-split (code, rho) table
+  constexpr bool BIG = K * K * R > kMaxSmallPre;    // one shared table, one WG per CU
+  constexpr int kTab = PRE ? K * K * R : K * K;     // entries per table (16 B each)
+  constexpr int kTabBytes = (PRE && BIG ? 1 : 2) * kTab * 16;
   constexpr int kRedBytes = kWaves * kMaxG * kHeadDim * 4;
   constexpr int kUnion = kTabBytes > kRedBytes ? kTabBytes : kRedBytes;
   constexpr int kStageRow = WV + 1;                // words per staged token (+ pad)
@@ -195,23 +263,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   const size_t plane = (size_t)b * a.Hkv + g;
   uint4* tabk = reinterpret_cast<uint4*>(smem);
   uint4* tabv = a.shared_tables ? tabk : tabk + kTab;
+  static_assert(!(PRE && BIG) || kWaves * kBlock * kStageRow >= 4 * K * K,
+                "the stage area holds the per-code directions while the table is built");
   float* red_o = reinterpret_cast<float*>(smem);          // [wave][head][128]
 
-  int len = a.seq_lens[b];
-  len = max(0, min(len, min(a.max_len, a.capacity)));
-  const int t_begin = split * a.split_len;
-  const int t_end = min(len, t_begin + a.split_len);
-
-  // ---- tables: codebooks to LDS first, then the table entries
+  // ---- every global load of the prologue goes out first, none waiting for
+  // another: codebooks, q, the first block (speculatively: any t0 below the
+  // capacity is in bounds, whatever seq_lens holds) and seq_lens.
+  float cx_k = 0.0f, cx_v = 0.0f, cr_k = 0.0f, cr_v = 0.0f;
   if (tid < K) {
-    cxk[tid] = a.kc_xi[tid];
-    cxv[tid] = a.vc_xi[tid];
+    cx_k = a.kc_xi[tid];
+    cx_v = a.vc_xi[tid];
   }
   if (tid < R) {
-    crk[tid] = a.kc_rho[tid];
-    crv[tid] = a.vc_rho[tid];
+    cr_k = a.kc_rho[tid];
+    cr_v = a.vc_rho[tid];
   }
-  // q of this wave's heads, all loads issued before any use
   constexpr int kHeadsPerWave = kMaxG / kWaves;
   float qv[kHeadsPerWave][2];
 #pragma unroll
@@ -229,18 +296,46 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       }
     }
   }
+  const int t_begin = split * a.split_len;
+  int t0 = t_begin + wave * kBlock;
+  BlockWords<BD, BN, QJL> blk;
+  if (!QJL && t0 < min(a.max_len, a.capacity)) load_block(blk, a, plane, t0, L);
+  int len = a.seq_lens[b];
+  len = max(0, min(len, min(a.max_len, a.capacity)));
+  // uniform: the loop and its prefetch test become scalar branches
+  const int t_end = __builtin_amdgcn_readfirstlane(min(len, t_begin + a.split_len));
+
+  // ---- tables: codebooks to LDS first, then the table entries
+  if (tid < K) {
+    cxk[tid] = cx_k;
+    cxv[tid] = cx_v;
+  }
+  if (tid < R) {
+    crk[tid] = cr_k;
+    crv[tid] = cr_v;
+  }
   __syncthreads();
   const int n_tables = a.shared_tables ? 1 : 2;
-  for (int e = tid; e < n_tables * kTab; e += kThreads) {
-    const bool v = e >= kTab;
-    const int i = v ? e - kTab : e;
-    const float* cx = v ? cxv : cxk;
-    if (PRE) {
-      const int code = i / R, r = i - code * R;
-      tabk[e] = presplit_entry(decode_dir(cx[code % K], cx[code / K]), (v ? crv : crk)[r]);
-    } else {
-      const float4 n = decode_dir(cx[i % K], cx[i / K]);
-      tabk[e] = make_uint4(__float_as_uint(n.x), __float_as_uint(n.y), __float_as_uint(n.z), 0u);
+  if (PRE && BIG) {
+    // the (shared) table has K^2 R entries: n^ of every code pair first, in
+    // the stage area, then one entry per lane and step, consecutive lanes on
+    // consecutive entries
+    float4* ncode = reinterpret_cast<float4*>(stage);
+    for (int c = tid; c < K * K; c += kThreads) ncode[c] = decode_dir(cxk[c % K], cxk[c / K]);
+    __syncthreads();
+    for (int e = tid; e < kTab; e += kThreads) tabk[e] = presplit_entry(ncode[e / R], crk[e % R]);
+  } else {
+    for (int e = tid; e < n_tables * kTab; e += kThreads) {
+      const bool v = e >= kTab;
+      const int i = v ? e - kTab : e;
+      const float* cx = v ? cxv : cxk;
+      if (PRE) {
+        const int code = i / R, r = i - code * R;
+        tabk[e] = presplit_entry(decode_dir(cx[code % K], cx[code / K]), (v ? crv : crk)[r]);
+      } else {
+        const float4 n = decode_dir(cx[i % K], cx[i / K]);
+        tabk[e] = make_uint4(__float_as_uint(n.x), __float_as_uint(n.y), __float_as_uint(n.z), 0u);
+      }
     }
   }
   // ---- q_rot = H diag(s) q / sqrt(d) for the G heads (rows >= G are zero)
@@ -255,8 +350,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // Q^T operands (B): column col = head, call (grp, c), slot e = component c
-  // of triplet 32 grp + 4 e + grp4 (zero beyond the 128 real coordinates).
+  // Q^T operands (B): column col = head, call (gi, c), slot e = component c
+  // of triplet 11 grp4 + 8 gi + e (zero outside the group's triplets and
+  // beyond the 128 real coordinates).
   half8 qh[2][3], ql[2][3];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi)
@@ -265,13 +361,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int tri = 32 * gi + 4 * e + grp4;
-        const int coord = 3 * tri + c;
-        x[e] = coord < kHeadDim ? qs[col * 132 + coord] : 0.0f;
+        const int j = 8 * gi + e;
+        const int coord = 3 * (kTriPerGroup * grp4 + j) + c;
+        x[e] = j < kTriPerGroup && coord < kHeadDim ? qs[col * 132 + coord] : 0.0f;
       }
       split8(x, qh[gi][c], ql[gi][c]);
     }
-  // QJL operands: call k, slot e of group grp4 = bit 32 k + 8 grp4 + e.
+  // QJL operands: call k, slot e of group grp4 = bit 32 grp4 + 8 k + e.
   half8 ph[QJL ? 4 : 1], pl[QJL ? 4 : 1];
   if (QJL) {
     __syncthreads();
@@ -288,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     for (int k = 0; k < (QJL ? 4 : 1); ++k) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = qs[col * 132 + 32 * k + 8 * grp4 + e];
+      for (int e = 0; e < 8; ++e) x[e] = qs[col * 132 + 32 * grp4 + 8 * k + e];
       split8(x, ph[k], pl[k]);
     }
   }
@@ -314,61 +410,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     vnsh[i] = (tri * BN) & 31;
   }
 
-  constexpr int kVW = (WV * kBlock + 63) / 64;     // staged value words per lane
-  for (int t0 = t_begin + wave * kBlock; t0 < t_end; t0 += kWaves * kBlock) {
-    // -- every global load of the block is issued before any of them is used,
-    //    so the block waits for memory once
-    uint32_t vw[kVW];
+  if (QJL && t0 < t_end) load_block(blk, a, plane, t0, L);   // (registers are short)
+  for (; t0 < t_end; t0 += kWaves * kBlock) {
+    // -- stage the block's value words, token-major (the previous block's
+    //    reads of the stage ended at the wave_sync closing its iteration)
+    {
+      const int w0 = L >> 5, tk = L & 31;
 #pragma unroll
-    for (int j = 0; j < kVW; ++j) {
-      const int e = L + 64 * j, w = e >> 5, tk = e & 31;
-      vw[j] = 0u;
-      if (e < WV * kBlock)
-        vw[j] = w < WD ? a.vdir[tile_word(plane, a.capacity, t0 + tk, w, WD)]
-                       : a.vnrm[tile_word(plane, a.capacity, t0 + tk, w - WD, WN)];
-    }
-    uint32_t dws[2][WD + 1], nws[2][WN + 1], sws[2][QJL ? 4 : 1];
+      for (int j = 0; j < blk.kVD; ++j)
+        if (2 * j + w0 < WD) st[tk * kStageRow + 2 * j + w0] = blk.vd[j];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int tok = t0 + 16 * kt + col;
-#pragma unroll
-      for (int w = 0; w < WD; ++w) dws[kt][w] = a.kdir[tile_word(plane, a.capacity, tok, w, WD)];
-#pragma unroll
-      for (int w = 0; w < WN; ++w) nws[kt][w] = a.knrm[tile_word(plane, a.capacity, tok, w, WN)];
-      dws[kt][WD] = 0u;
-      nws[kt][WN] = 0u;
-      if (QJL) {
-#pragma unroll
-        for (int k = 0; k < (QJL ? 4 : 1); ++k) sws[kt][k] = a.kqjl[tile_word(plane, a.capacity, tok, k, 4)];
-      }
-    }
-    float4 gk4[2], gv4[2];
-    uint2 grs[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int tb = t0 + 16 * kt + 4 * grp4;
-      gk4[kt] = *reinterpret_cast<const float4*>(&a.kgamma[plane * a.capacity + tb]);
-      gv4[kt] = *reinterpret_cast<const float4*>(&a.vgamma[plane * a.capacity + tb]);
-      if (QJL) grs[kt] = *reinterpret_cast<const uint2*>(&a.kgamma_r[plane * a.capacity + tb]);
-    }
-    // -- stage the block's value words, token-major
-#pragma unroll
-    for (int j = 0; j < kVW; ++j) {
-      const int e = L + 64 * j, w = e >> 5, tk = e & 31;
-      if (e < WV * kBlock) st[tk * kStageRow + w] = vw[j];
+      for (int j = 0; j < blk.kVN; ++j)
+        if (2 * j + w0 < WN) st[tk * kStageRow + WD + 2 * j + w0] = blk.vn[j];
     }
     // -- scores, two 16-token tiles
     floatx4 sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      uint32_t* dw = dws[kt];
-      uint32_t* nw = nws[kt];
-      // shift the record so that triplet 4 e + grp4 starts at bit 4 e FWD
-      const uint32_t dsh = grp4 * FWD, nsh = grp4 * BN;
+      // shift the group's window so that its triplet j starts at bit j FWD
+      using BW = BlockWords<BD, BN, QJL>;
+      const uint32_t dsh = (kTriPerGroup * FWD * grp4) & 31, nsh = (kTriPerGroup * BN * grp4) & 31;
+      uint32_t dw[BW::KWD], nw[BW::KWN];
 #pragma unroll
-      for (int w = 0; w < WD; ++w) dw[w] = __builtin_amdgcn_alignbit(dw[w + 1], dw[w], dsh);
+      for (int w = 0; w < BW::KWD; ++w)
+        dw[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KWD ? blk.dw[kt][w + 1] : 0u, blk.dw[kt][w], dsh);
 #pragma unroll
-      for (int w = 0; w < WN; ++w) nw[w] = __builtin_amdgcn_alignbit(nw[w + 1], nw[w], nsh);
+      for (int w = 0; w < BW::KWN; ++w)
+        nw[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KWN ? blk.nw[kt][w + 1] : 0u, blk.nw[kt][w], nsh);
       floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
@@ -377,25 +445,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
           uint4 E[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int tri = 32 * gi + 4 * e;       // relative triplet index
-            if (gi == 1 && e >= 3) {
+            const int j = 8 * gi + e;               // the group's triplet
+            if (j >= kTriPerGroup) {
               E[e] = make_uint4(0u, 0u, 0u, 0u);
               continue;
             }
-            E[e] = tabk[field<FWD>(dw, tri * FWD) * R + field<BN>(nw, tri * BN)];
+            E[e] = tabk[field<FWD>(dw, j * FWD) * R + field<BN>(nw, j * BN)];
           }
           operands_pre(E, ah, al);
         } else {
           float ux[8], uy[8], uz[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int tri = 32 * gi + 4 * e;
-            if (gi == 1 && e >= 3) {
+            const int j = 8 * gi + e;
+            if (j >= kTriPerGroup) {
               ux[e] = uy[e] = uz[e] = 0.0f;
               continue;
             }
-            const uint4 n = tabk[field<FWD>(dw, tri * FWD)];
-            const float rho = crk[field<BN>(nw, tri * BN)];
+            const uint4 n = tabk[field<FWD>(dw, j * FWD)];
+            const float rho = crk[field<BN>(nw, j * BN)];
             ux[e] = rho * __uint_as_float(n.x);
             uy[e] = rho * __uint_as_float(n.y);
             uz[e] = rho * __uint_as_float(n.z);
@@ -409,17 +477,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       }
       // this lane's 4 tokens: t0 + 16 kt + 4 grp4 + r, head col
       const int tb = t0 + 16 * kt + 4 * grp4;
-      const float gka[4] = {gk4[kt].x, gk4[kt].y, gk4[kt].z, gk4[kt].w};
+      const float gka[4] = {blk.gk[kt].x, blk.gk[kt].y, blk.gk[kt].z, blk.gk[kt].w};
       float s4[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) s4[r] = acc[r] * (1.0f / kUScale);
       if (QJL) {
-        const uint32_t* sw = sws[kt];
+        const uint32_t sw = blk.sw[kt];
         floatx4 qa = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           // sigma_j = -1 where the bit is set: fp16 +-1 = 0x3C00 | bit << 15
-          const uint32_t byte = (sw[k] >> (8 * grp4)) & 0xffu;
+          const uint32_t byte = (sw >> (8 * k)) & 0xffu;
           u32x4 sg;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
@@ -430,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
           qa = mfma(sgh, pl[k], qa);
           qa = mfma(sgh, ph[k], qa);
         }
-        const uint32_t gr2[2] = {grs[kt].x, grs[kt].y};
+        const uint32_t gr2[2] = {blk.gr[kt].x, blk.gr[kt].y};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const uint16_t h = (uint16_t)(gr2[r >> 1] >> (16 * (r & 1)));
@@ -443,6 +511,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
         sc[kt][r] = valid ? s4[r] * gka[r] * a.scale : -INFINITY;
       }
     }
+    // -- the key words are consumed: the next block's loads go out now and
+    //    land while this block's softmax and values are computed
+    //    (with QJL the registers are short: the loads go out after the values)
+    const float4 gv4[2] = {blk.gv[0], blk.gv[1]};
+    if (!QJL && t0 + kWaves * kBlock < t_end) load_block(blk, a, plane, t0 + kWaves * kBlock, L);
     // -- online softmax over the 32 tokens, head col (Sec. 3.6 / App. A)
     float mx = -INFINITY;
 #pragma unroll
@@ -486,7 +559,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     wave_sync();
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const bool tri_ok = 16 * i + col < kNTri;
+      // with QJL the registers are short: one value tile at a time
+      if (QJL) __builtin_amdgcn_sched_barrier(0);
+      // lanes past the last triplet decode a clamped copy of it: finite
+      // values in output columns the epilogue never writes
       half8 bh[3], bl[3];
       if (PRE) {
         uint4 E[8];
@@ -495,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
           const uint32_t* sr = &st[(16 * (e >> 2) + 4 * grp4 + (e & 3)) * kStageRow];
           const uint32_t code = __builtin_amdgcn_alignbit(sr[vdw[i] + 1], sr[vdw[i]], vdsh[i]) & kDirMask;
           const uint32_t ir = __builtin_amdgcn_alignbit(sr[vnw[i] + 1], sr[vnw[i]], vnsh[i]) & kNrmMask;
-          E[e] = tri_ok ? tabv[code * R + ir] : make_uint4(0u, 0u, 0u, 0u);
+          E[e] = tabv[code * R + ir];
         }
         operands_pre(E, bh, bl);
       } else {
@@ -506,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
           const uint32_t code = __builtin_amdgcn_alignbit(sr[vdw[i] + 1], sr[vdw[i]], vdsh[i]) & kDirMask;
           const uint32_t ir = __builtin_amdgcn_alignbit(sr[vnw[i] + 1], sr[vnw[i]], vnsh[i]) & kNrmMask;
           const uint4 n = tabv[code];
-          const float rho = tri_ok ? crv[ir] : 0.0f;
+          const float rho = crv[ir];
           vx[e] = rho * __uint_as_float(n.x);
           vy[e] = rho * __uint_as_float(n.y);
           vz[e] = rho * __uint_as_float(n.z);
@@ -518,6 +594,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < 3; ++c) o[i][c] = mfma3(pah, pal, bh[c], bl[c], o[i][c]);
     }
+    if (QJL && t0 + kWaves * kBlock < t_end) load_block(blk, a, plane, t0 + kWaves * kBlock, L);
     wave_sync();
   }
 
@@ -558,57 +635,74 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// Merges the splits of one (batch, query head) by their log-sum-exp, in split
-// order, and applies R_v^T = diag(s_v) H / sqrt(d).  Four wavefronts take
-// the splits round-robin, eight loads in flight per lane; the partial sums
-// meet in LDS.
-__global__ __launch_bounds__(256) void merge_kernel(const float2* __restrict__ ws_ml,
-                                                    const float* __restrict__ ws_acc,
-                                                    int n_split, int Hq, uint64_t vseed,
-                                                    float* __restrict__ out) {
-  constexpr int kU = 8;
-  __shared__ float part[kWaves][2 * 64 + 1];
+// Merges the splits of one (batch, query head) by their log-sum-exp and
+// applies R_v^T = diag(s_v) H / sqrt(d).  Eight wavefronts take 16
+// consecutive splits each per round, every load of the round in flight at
+// once, with a running maximum (an online rescale) so that no pass over the
+// maxima has to come first; the wavefronts meet in LDS in a fixed order, so
+// the result does not depend on scheduling.
+constexpr int kMergeWaves = 8;
+constexpr int kMergeU = 16;
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float2* __restrict__ ws_ml,
+                                                                 const float* __restrict__ ws_acc,
+                                                                 int n_split, int Hq,
+                                                                 uint64_t vseed,
+                                                                 float* __restrict__ out) {
+  __shared__ float part[kMergeWaves][2 * 64 + 2];
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
   const size_t row0 = ((size_t)blockIdx.y * Hq + blockIdx.x) * n_split;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < n_split; s0 += 64) {
-    const int s = s0 + L;
-    M = fmaxf(M, s < n_split ? ws_ml[row0 + s].x : -INFINITY);
-  }
-  M = wave_max(M);
-  float Lsum = 0.0f, a0 = 0.0f, a1 = 0.0f;
-  if (M != -INFINITY) {
-    for (int s0 = wave; s0 < n_split; s0 += kU * kWaves) {
-      float2 ml[kU];
-      float x0[kU], x1[kU];
+  float M = -INFINITY, Lsum = 0.0f, a0 = 0.0f, a1 = 0.0f;
+  for (int s0 = wave * kMergeU; s0 < n_split; s0 += kMergeWaves * kMergeU) {
+    float2 ml[kMergeU];
+    float x0[kMergeU], x1[kMergeU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int s = min(s0 + u * kWaves, n_split - 1);
-        ml[u] = ws_ml[row0 + s];
-        x0[u] = ws_acc[(row0 + s) * kHeadDim + L];
-        x1[u] = ws_acc[(row0 + s) * kHeadDim + L + 64];
-      }
+    for (int u = 0; u < kMergeU; ++u) {
+      const size_t r = row0 + min(s0 + u, n_split - 1);
+      ml[u] = ws_ml[r];
+      x0[u] = ws_acc[r * kHeadDim + L];
+      x1[u] = ws_acc[r * kHeadDim + L + 64];
+    }
+    float m_new = M;
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const bool in = s0 + u * kWaves < n_split && ml[u].x != -INFINITY;
-        const float f = in ? __expf(ml[u].x - M) : 0.0f;
-        Lsum += f * ml[u].y;
-        a0 += f * x0[u];
-        a1 += f * x1[u];
+    for (int u = 0; u < kMergeU; ++u)
+      if (s0 + u < n_split) m_new = fmaxf(m_new, ml[u].x);
+    if (m_new != -INFINITY) {            // the same in every lane
+      const float f0 = M == -INFINITY ? 0.0f : __expf(M - m_new);
+      Lsum *= f0;
+      a0 *= f0;
+      a1 *= f0;
+#pragma unroll
+      for (int u = 0; u < kMergeU; ++u) {
+        const bool in = s0 + u < n_split && ml[u].x != -INFINITY;
+        const float f = in ? __expf(ml[u].x - m_new) : 0.0f;
+        Lsum = fmaf(f, ml[u].y, Lsum);
+        a0 = fmaf(f, x0[u], a0);
+        a1 = fmaf(f, x1[u], a1);
       }
+      M = m_new;
     }
   }
   part[wave][L] = a0;
   part[wave][64 + L] = a1;
-  if (L == 0) part[wave][128] = Lsum;
+  if (L == 0) {
+    part[wave][128] = M;
+    part[wave][129] = Lsum;
+  }
   __syncthreads();
   if (wave != 0) return;
-  float t0 = 0.0f, t1 = 0.0f, tl = 0.0f;
+  float Mt = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    t0 += part[w][L];
-    t1 += part[w][64 + L];
-    tl += part[w][128];
+  for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, part[w][128]);
+  float t0 = 0.0f, t1 = 0.0f, tl = 0.0f;
+  if (Mt != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+      const float mw = part[w][128];
+      const float f = mw == -INFINITY ? 0.0f : __expf(mw - Mt);
+      t0 = fmaf(f, part[w][L], t0);
+      t1 = fmaf(f, part[w][64 + L], t1);
+      tl = fmaf(f, part[w][129], tl);
+    }
   }
   const float inv = tl > 0.0f ? 1.0f / (tl * kUScale) : 0.0f;
   t0 *= inv;
@@ -624,14 +718,17 @@ struct Plan {
   size_t ml_bytes, acc_bytes, total;
 };
 
-Plan make_plan(int B, int Hq, int Hkv, int max_len) {
+// Splits of `nw`-wave workgroups: about eight waves per CU in all, each
+// split a multiple of nw 32-token blocks.
+Plan make_plan(int B, int Hq, int Hkv, int max_len, int nw) {
   Plan p;
   const int units = B * Hkv;
-  const int target_blocks = 512;                 // two workgroups per CU
+  const int target_blocks = 256 * (8 / nw);
+  const int quantum = nw * kBlock;
   const int per_unit = max(1, target_blocks / max(1, units));
   int sl = (max(max_len, 1) + per_unit - 1) / per_unit;
-  sl = (sl + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
-  p.split_len = max(sl, kSplitQuantum);
+  sl = (sl + quantum - 1) / quantum * quantum;
+  p.split_len = max(sl, quantum);
   p.n_split = max(1, (max_len + p.split_len - 1) / p.split_len);
   const size_t rows = (size_t)B * Hq * p.n_split;
   p.ml_bytes = (rows * sizeof(float2) + 255) / 256 * 256;
@@ -640,13 +737,33 @@ Plan make_plan(int B, int Hq, int Hkv, int max_len) {
   return p;
 }
 
+// Big tables (more than kMaxSmallPre entries) are pre-split only when K and
+// V share their codebooks (one table fills the CU's LDS); otherwise fp32.
+bool big_split(int b_dir, int b_nrm) { return (1 << (2 * b_dir + b_nrm)) > kMaxSmallPre; }
+int waves_for(int b_dir, int b_nrm, bool shared) {
+  return big_split(b_dir, b_nrm) && shared ? kWavesBig : kWavesSmall;
+}
+
+template <int BD, int BN, bool QJL>
+void launch_q(const DecodeArgs& a, hipStream_t st) {
+  dim3 grid(a.n_split, a.Hkv, a.B);
+  constexpr bool big = (1 << (2 * BD + BN)) > kMaxSmallPre;
+  if constexpr (!big) {
+    hipLaunchKernelGGL((decode_kernel<BD, BN, QJL, kPre, kWavesSmall>), grid, dim3(64 * kWavesSmall), 0, st, a);
+  } else {
+    if (a.shared_tables)
+      hipLaunchKernelGGL((decode_kernel<BD, BN, QJL, kPre, kWavesBig>), grid, dim3(64 * kWavesBig), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<BD, BN, QJL, kFp32, kWavesSmall>), grid, dim3(64 * kWavesSmall), 0, st, a);
+  }
+}
+
 template <int BD, int BN>
 void launch(const DecodeArgs& a, bool qjl, hipStream_t st) {
-  dim3 grid(a.n_split, a.Hkv, a.B);
   if (qjl)
-    hipLaunchKernelGGL((decode_kernel<BD, BN, true>), grid, dim3(kThreads), 0, st, a);
+    launch_q<BD, BN, true>(a, st);
   else
-    hipLaunchKernelGGL((decode_kernel<BD, BN, false>), grid, dim3(kThreads), 0, st, a);
+    launch_q<BD, BN, false>(a, st);
 }
 
 }  // namespace
@@ -681,7 +798,8 @@ extern "C" octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_code
   if (!bytes) return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_decode_workspace_bytes: bytes is NULL");
   if (B < 1 || num_q_heads < 1 || kv_heads < 1 || max_seq_len < 0)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_decode_workspace_bytes: bad sizes");
-  *bytes = make_plan(B, num_q_heads, kv_heads, max_seq_len).total;
+  // the small-workgroup plan has the most splits: enough for either
+  *bytes = make_plan(B, num_q_heads, kv_heads, max_seq_len, kWavesSmall).total;
   return OCTO_OK;
 }
 
@@ -718,7 +836,8 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
                 max_seq_len, k_cache->capacity);
   if (B > 65535 || Hkv > 65535 || num_q_heads > 65535)
     return fail(OCTO_ERR_UNSUPPORTED, "%s: batch and heads must be <= 65535", what);
-  const Plan p = make_plan(B, num_q_heads, Hkv, max_seq_len);
+  const bool shared = kc.c_xi == vc.c_xi && kc.c_rho == vc.c_rho;
+  const Plan p = make_plan(B, num_q_heads, Hkv, max_seq_len, waves_for(kc.b_dir, kc.b_nrm, shared));
   if (!workspace || workspace_bytes < p.total)
     return fail(OCTO_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", what,
                 workspace_bytes, p.total);
@@ -739,7 +858,7 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
   a.kc_rho = kc.c_rho;
   a.vc_xi = vc.c_xi;
   a.vc_rho = vc.c_rho;
-  a.shared_tables = kc.c_xi == vc.c_xi && kc.c_rho == vc.c_rho;
+  a.shared_tables = shared;
   a.kseed = kc.seed;
   a.vseed = vc.seed;
   a.kdir = k_cache->dir;
@@ -767,7 +886,7 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
     default: return fail(OCTO_ERR_UNSUPPORTED, "%s: configuration not compiled", what);
   }
   if ((s = check_launch(what)) != OCTO_OK) return s;
-  hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, B), dim3(256), 0, stream, a.ws_ml, a.ws_acc,
+  hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, B), dim3(kMergeWaves * 64), 0, stream, a.ws_ml, a.ws_acc,
                      a.n_split, num_q_heads, vc.seed, out);
   return check_launch(what);
 }

@@ -101,8 +101,7 @@ __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32
 template <int WIDTH>
 __device__ inline uint32_t field(const uint32_t* w, int pos) {
   const int wi = pos >> 5, sh = pos & 31;
-  uint32_t v = w[wi] >> sh;
-  if (sh + WIDTH > 32) v |= w[wi + 1] << (32 - sh);
+  const uint32_t v = sh + WIDTH > 32 ? __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) : w[wi] >> sh;
   return v & ((1u << WIDTH) - 1u);
 }
 

@@ -22,10 +22,15 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def run_case(w, T=None, seq_override=None, max_len=None, q_f32=False, planes=None):
+def run_case(w, T=None, seq_override=None, max_len=None, q_f32=False, planes=None,
+             split=(None, None), v_own_tables=False):
     inp = make_inputs(w, scale_T=T)
-    kc, hk = codecs(w.bits, qjl=w.qjl)
-    vc, hv = codecs(w.bits)
+    kc, hk = codecs(w.bits, qjl=w.qjl, b_dir=split[0], b_nrm=split[1])
+    vc, hv = codecs(w.bits, b_dir=split[0], b_nrm=split[1])
+    if v_own_tables:
+        # same values at other addresses: the kernels cannot share one table
+        vc = octo.Codec(bits=w.bits, b_dir=split[0], b_nrm=split[1],
+                        tables=octo.binding.load_codebooks(128))
     K, V, q = inp["K"], inp["V"], inp["q"]
     seq = inp["seq_lens"].clone() if seq_override is None else torch.tensor(seq_override, dtype=torch.int32)
     cap = -(-K.shape[2] // 64) * 64
@@ -77,6 +82,21 @@ def test_decode_small(key, T):
     say(f"decode {key} T={T}")
     err, _, lens = run_case(w, T)
     say(f"  lens {lens.tolist()} max-abs err {err:.3e}")
+    assert err <= ATOL
+
+
+@pytest.mark.parametrize("split", [(5, 3), (4, 4), (4, 2), (3, 3), (3, 1), (2, 2)])
+@pytest.mark.parametrize("own", [False, True])
+def test_decode_table_modes(split, own):
+    """Every bit split, with K and V sharing their codebook tables (one
+    pre-split LDS table, the one-workgroup-per-CU mode for the big splits) and
+    with V's tables at other addresses (separate tables; the fp32 table for
+    the big splits)."""
+    bits = (split[0] + split[1]) // 2
+    w = workload("gqa32k", bits=bits)
+    say(f"decode split {split} own V tables {own}")
+    err, _, _ = run_case(w, T=1100, split=split, v_own_tables=own)
+    say(f"  max-abs err {err:.3e}")
     assert err <= ATOL
 
 
@@ -133,7 +153,7 @@ def test_decode_deterministic():
 
 
 def test_decode_reuses_workspace():
-    """The completion counters return to zero: back-to-back calls on one
+    """The workspace holds no state between calls: back-to-back calls on one
     workspace, with different shapes, keep matching the oracle."""
     ws = octo.workspace(1 << 22, "cuda")
     for T, key in ((700, "gqa32k"), (300, "long128k"), (700, "gqa32k")):
