@@ -23,8 +23,19 @@ roofline   for the attention call: algorithmic bytes (packed cache of the
 cpu_baseline  the float64 oracle on a bounded sample (one KV-head plane of
            the decode workload; a few query rows for the chunk workload),
            on one host thread, scaled to the same unit.
+traffic    memory-side bytes per attention call, from rocprofv3 FETCH_SIZE and
+           WRITE_SIZE counters (one --pmc run each) scaled by what the same
+           counters read for a plain copy of known size; read from
+           profiles/traffic_<workload>.json and reported only while the
+           library sources hash to the value recorded there (else null).
+
+Counter helpers (run under rocprofv3 --pmc, then summarized here):
+    python bench.py --copy-calibration          # a 512 MiB device copy
+    python bench.py --pmc-summary WORKLOAD FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
 """
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -40,11 +51,89 @@ from quantized_decode_attention_octo_amd.workloads import WORKLOADS, make_inputs
 
 METRIC = "decode-attn cached KV-tokens/s + % of HBM peak on packed cache; encode tokens/s"
 HBM_PEAK_GBS = 8000.0
+COPY_MIB = 512                     # size of the counter calibration copy
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    """Hash of the library sources: recorded counters apply to these kernels only."""
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "quantized_decode_attention_octo_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    with open(os.path.join(ROOT, "include", "octopus.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def recorded_traffic(workload):
+    """Memory-side bytes per attention call from the recorded counters, or None."""
+    try:
+        with open(traffic_file(workload)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec["attention_bytes_per_call"]
+
+
+def copy_calibration(mib):
+    """A plain device copy of known size, for scaling the memory counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
+
+
+def _pmc_per_kernel(path, counter):
+    """Mean counter value per dispatch, by kernel name, from a rocprofv3 csv."""
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Writes profiles/traffic_<workload>.json from the four counter runs."""
+    fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+    cf = _pmc_per_kernel(copy_fetch_csv, "FETCH_SIZE")
+    cw = _pmc_per_kernel(copy_write_csv, "WRITE_SIZE")
+    # the copy kernel is the largest dispatch of the calibration run
+    ck = max(cf, key=cf.get)
+    copy_bytes = float(COPY_MIB * (1 << 20))
+    f_scale = copy_bytes / (cf[ck] * 1024.0)
+    w_scale = copy_bytes / (cw[ck] * 1024.0)
+    att = [k for k in fetch if ("decode_kernel" in k or "merge_kernel" in k or "chunk" in k
+                                or "rotate_rows" in k or "decode_rows" in k)]
+    kernels = {k: {"fetch_kib": fetch[k], "write_kib": write.get(k, 0.0),
+                   "bytes": fetch[k] * 1024.0 * f_scale + write.get(k, 0.0) * 1024.0 * w_scale}
+               for k in att}
+    rec = {"source_hash": source_hash(), "workload": workload,
+           "copy_kernel": ck, "copy_bytes": copy_bytes,
+           "copy_fetch_kib": cf[ck], "copy_write_kib": cw[ck],
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernels": kernels,
+           "attention_bytes_per_call": sum(v["bytes"] for v in kernels.values())}
+    with open(traffic_file(workload), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def packed_bytes_per_token(codec):
@@ -123,7 +212,7 @@ def run_decode(w, steps, warmup):
         "encode_tokens_per_s": enc_tokens / (enc_ms * 1e-3),
         "token_kv_heads_per_s": tokens * w.Hkv / (att_ms * 1e-3),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.key),
                      "kernel": "octo_attend_decode (split-K scan + merge)",
                      "algorithmic_bytes_per_launch": kv_bytes},
     }
@@ -176,15 +265,33 @@ def run_chunk(w, steps, warmup):
         "encode_us": enc_ms * 1e3,
         "encode_tokens_per_s": w.B * Tq / (enc_ms * 1e-3),
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_FP16_PEAK_TFLOPS,
+                     "traffic": recorded_traffic(w.key),
                      "kernel": "octo_attend_chunk (rotate + decode pre-passes + MFMA attention)",
                      "algorithmic_flops_per_launch": flops},
     }
     return res, (inp, kc, vc, kcache, vcache)
 
 
+CPU_SECONDS = 10.0                 # oracle work per baseline (bounded sample)
+
+
+def _host_plane(h, b, g):
+    """Host cache of plane (b, g) alone, in the same layout with B = H = 1."""
+    n = h["B"] * h["H"]
+    p = b * h["H"] + g
+    out = {"B": 1, "H": 1, "capacity": h["capacity"],
+           "dir": h["dir"].reshape(n, -1)[p], "nrm": h["nrm"].reshape(n, -1)[p],
+           "gamma": h["gamma"][b:b + 1, g:g + 1]}
+    if "qjl" in h:
+        out["qjl"] = h["qjl"].reshape(n, -1)[p]
+        out["gamma_r"] = h["gamma_r"][b:b + 1, g:g + 1]
+    return out
+
+
 def cpu_baseline(w, state):
-    """The oracle on one host thread over a bounded sample, in the same unit."""
+    """The oracle on one host thread over a bounded sample (about CPU_SECONDS
+    of work), in the same unit as the GPU value."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -195,44 +302,45 @@ def cpu_baseline(w, state):
     hv = oracle_codec(bits=w.bits)
     hkc, hvc = kcache.to_host(), vcache.to_host()
     G = w.Hq // w.Hkv
-    n = w.B * w.Hkv
+    lens = inp["seq_lens"].numpy()
     with threadpool_limits(limits=1):
         torch.set_num_threads(1)
+        done, dt, units = 0.0, 0.0, 0
         if not w.chunk_q:
-            L = int(inp["seq_lens"][0])
-            pk = {"B": 1, "H": 1, "capacity": hkc["capacity"],
-                  "dir": hkc["dir"].reshape(n, -1)[0], "nrm": hkc["nrm"].reshape(n, -1)[0],
-                  "gamma": hkc["gamma"][:1, :1]}
-            if "qjl" in hkc:
-                pk["qjl"] = hkc["qjl"].reshape(n, -1)[0]
-                pk["gamma_r"] = hkc["gamma_r"][:1, :1]
-            pv = {"B": 1, "H": 1, "capacity": hvc["capacity"],
-                  "dir": hvc["dir"].reshape(n, -1)[0], "nrm": hvc["nrm"].reshape(n, -1)[0],
-                  "gamma": hvc["gamma"][:1, :1]}
-            qn = inp["q"][:1, :G].double().numpy()
-            t0 = time.perf_counter()
-            oatt.decode_attention(qn, pk, pv, hk, hv, np.array([L]))
-            dt = time.perf_counter() - t0
-            # the step attends sum(len) tokens on each of the Hkv planes; the
-            # sample is L tokens of one plane: tokens/s = L / (dt * Hkv)
-            value = L / (dt * w.Hkv)
-            sample = f"oracle decode attention of batch 0, KV head 0 ({L} tokens, {G} query heads), scaled by the {w.Hkv} KV heads"
+            # (batch, KV head) planes in order, repeated if the workload is
+            # smaller than the budget; a plane of sequence b is len_b / Hkv of
+            # the step's cached KV-tokens
+            planes = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+            while dt < CPU_SECONDS:
+                b, g = planes[units % len(planes)]
+                qn = inp["q"][b:b + 1, g * G:(g + 1) * G].double().numpy()
+                t0 = time.perf_counter()
+                oatt.decode_attention(qn, _host_plane(hkc, b, g), _host_plane(hvc, b, g), hk, hv,
+                                      lens[b:b + 1])
+                dt += time.perf_counter() - t0
+                done += lens[b] / w.Hkv
+                units += 1
+            value = done / dt
+            sample = (f"oracle decode attention over {units} (batch, KV head) planes of the workload "
+                      f"({len(planes)} in all, taken in order and repeated), "
+                      f"{G} query heads each; each plane counts len_b / {w.Hkv} cached KV-tokens")
         else:
-            rows = np.arange(8)
-            pk = {"B": 1, "H": 1, "capacity": hkc["capacity"], "dir": hkc["dir"].reshape(n, -1)[0],
-                  "nrm": hkc["nrm"].reshape(n, -1)[0], "gamma": hkc["gamma"][:1, :1]}
-            pv = {"B": 1, "H": 1, "capacity": hvc["capacity"], "dir": hvc["dir"].reshape(n, -1)[0],
-                  "nrm": hvc["nrm"].reshape(n, -1)[0], "gamma": hvc["gamma"][:1, :1]}
-            t0 = time.perf_counter()
-            oatt.chunk_attention(inp["q"][:, :1].double().numpy(), pk, pv, hk, hv, w.T,
-                                 inp["K_cur"][:, :1].double().numpy(),
-                                 inp["V_cur"][:, :1].double().numpy(), q_rows=rows)
-            dt = time.perf_counter() - t0
+            # 8-row groups of head 0's queries; one row attends the whole window
+            # and chunk, 1 / (Hq Tq) of the step
+            pk, pv = _host_plane(hkc, 0, 0), _host_plane(hvc, 0, 0)
             keys = w.T + w.chunk_q
-            # full step = Hq heads x Tq rows; the sample = 1 head x 8 rows
-            t_full = dt * w.Hq * w.chunk_q / len(rows)
-            value = keys / t_full
-            sample = f"oracle chunk attention of head 0, {len(rows)} query rows over {keys} keys, scaled to {w.Hq} heads x {w.chunk_q} rows"
+            while dt < CPU_SECONDS and units * 8 < w.chunk_q:
+                rows = np.arange(units * 8, min(units * 8 + 8, w.chunk_q))
+                t0 = time.perf_counter()
+                oatt.chunk_attention(inp["q"][:, :1].double().numpy(), pk, pv, hk, hv, w.T,
+                                     inp["K_cur"][:, :1].double().numpy(),
+                                     inp["V_cur"][:, :1].double().numpy(), q_rows=rows)
+                dt += time.perf_counter() - t0
+                done += len(rows)
+                units += 1
+            value = keys * done / (dt * w.Hq * w.chunk_q)
+            sample = (f"oracle chunk attention of head 0, {int(done)} query rows over {keys} keys, "
+                      f"scaled to {w.Hq} heads x {w.chunk_q} rows")
     return {"value": value, "unit": "cached KV-tokens/s", "cores": 1, "kind": "oracle",
             "sample": sample, "seconds": dt}
 
@@ -244,7 +352,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa32k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=5,
+                    metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     a = ap.parse_args()
+    if a.pmc_summary:
+        pmc_summary(*a.pmc_summary)
+        return
+    if a.copy_calibration:
+        copy_calibration(COPY_MIB)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               "(the workloads fit one MI355X and no multi-GPU path is built)", file=sys.stderr)
