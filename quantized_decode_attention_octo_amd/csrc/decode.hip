@@ -22,23 +22,29 @@
 // peaked softmax that outlier channels produce.  u^ is scaled by 64 (exact)
 // so that the residuals stay in the fp16 normal range.
 //
-// Tables in LDS, built per workgroup from the codebooks.  When the split is
-// small (2^(2 b_dir + b_nrm) <= 1024 entries: b_dir <= 4 with b_nrm <= 2, or
-// the uniform (2,2), (3,3)), the table holds 64 rho^ n^ for every (code pair,
-// norm index), already split into fp16 hi/lo halves, so unpacking a triplet
-// is two field extractions, one LDS read and byte permutes.  Otherwise it
-// holds 64 n^ per code pair in fp32 and rho^ is applied and split on the fly.
-//
+// Tables in LDS, built per workgroup from the codebooks.  The pre-split
+// table holds 64 rho^ n^ for every (norm index, code pair), already split
+// into fp16 hi/lo halves, so unpacking a triplet is two field extractions
+// and one LDS read.  Up to 1024 entries (b_dir <= 4 with b_nrm <= 2, or the
+// uniform (2,2), (3,3)) two workgroups share a CU, each with its K and V
+// tables; the 4-bit splits (5,3) and (4,4) take 4096 or 8192 entries, one
+// table for K and V when they share their codebooks, in one eight-wave
+// workgroup per CU.  Otherwise the table holds 64 n^ per code pair in fp32
+// and rho^ is applied and split on the fly.
+
 // MFMA lane layout of v_mfma_f32_16x16x32_f16 (L = lane):
 //   A[i][k]: i = L % 16, k-slot 8 (L / 16) + e;  B[k][j]: j = L % 16, same k
 //   D[i][j]: i = 4 (L / 16) + r, j = L % 16.
 // Scores are S^T = U Q^T (tokens as rows), so each lane ends up with 4 keys
 // of one query head, which is the A-operand layout P needs in O = P V.
 // Key-side coordinates: lane group g = L / 16 of token row t owns the 11
-// consecutive triplets 11 g .. 11 g + 10 (10 for g = 3) and holds, for call
-// (gi, c), slot e = component c of triplet 11 g + 8 gi + e, so that it reads
-// only the few record words that cover its triplets; with QJL, call k,
-// slot e = sign bit 32 g + 8 k + e, one word of the sign record.
+// consecutive triplets 11 g .. 11 g + 10 (10 for g = 3), so that it reads
+// only the few record words that cover them.  With pre-split tables, slot e
+// of call m (six calls) is component e % 4 of triplet 2 m + e / 4 (component
+// 3 a zero pad): two table entries are the hi and lo operands as they stand.
+// With fp32 tables, call (gi, c) slot e is component c of triplet 8 gi + e.
+// With QJL, call k, slot e = sign bit 32 g + 8 k + e, one word of the sign
+// record.
 // Value-side columns: tile (grp, c), column j = component c of triplet
 // 16 grp + j; slot e of lane group g = token 16 (e / 4) + 4 g + e % 4 of the
 // 32-token block, matching the score layout.
@@ -98,6 +104,23 @@ __device__ inline void wave_sync() {
 }
 
 __device__ inline uint32_t pk(fp16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Reductions over the four 16-lane rows of a wavefront (lanes L, L ^ 16,
+// L ^ 32, L ^ 48) with the lane-half and row swaps, no LDS round trip.  Both
+// halves of each swap are combined in the same order in every lane, so all
+// four lanes hold the same bits.
+__device__ inline float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // x = hi + lo for 8 slots: hi rounded toward zero to fp16, lo the residual.
 __device__ inline void split8(const float* x, half8& hi, half8& lo) {
@@ -182,19 +205,27 @@ constexpr int kTriPerGroup = 11;      // triplets of one key-side lane group
 // Record words that cover the bits of 11 triplets of FW bits from any shift.
 constexpr int group_words(int FW) { return (31 + kTriPerGroup * FW + 31) / 32; }
 
+// Value side: lane L (token L % 32, half L / 32) extracts the table indices of
+// triplets 22 h .. 22 h + 21 of its token (the last one of half 1 is past the
+// 43 and lands in a spare row).
+constexpr int kValTri = 22;
+constexpr int value_words(int FW) { return (31 + kValTri * FW + 31) / 32; }
+constexpr int kIdxRow = 36;           // u16 per index row: 32 tokens + pad (bank spread)
+constexpr int kIdxRows = 44;          // 43 triplets + the spare
+
 // The global words of one 32-token block of a wavefront.  Key side: lane
 // (col, grp4) holds, for tile kt, the record words of token 16 kt + col that
 // cover the triplets of lane group grp4 (and word grp4 of its sign record);
-// value side: lane L holds word 2 j + L / 32 of token L % 32, for staging in
-// LDS.
+// value side: lane L holds the record words of token L % 32 that cover
+// triplets 22 (L / 32) .. + 21.
 template <int BD, int BN, bool QJL>
 struct BlockWords {
   static constexpr int FWD = 2 * BD;
   static constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32;
   static constexpr int KWD = group_words(FWD), KWN = group_words(BN);
-  static constexpr int kVD = (WD + 1) / 2, kVN = (WN + 1) / 2;
+  static constexpr int KVD = value_words(FWD), KVN = value_words(BN);
   uint32_t dw[2][KWD], nw[2][KWN], sw[2];
-  uint32_t vd[kVD], vn[kVN];
+  uint32_t vd[KVD], vn[KVN];
   float4 gk[2], gv[2];
   uint2 gr[2];
 };
@@ -227,33 +258,35 @@ __device__ inline void load_block(BlockWords<BD, BN, QJL>& r, const DecodeArgs& 
     r.gv[kt] = *reinterpret_cast<const float4*>(a.vgamma + gbase + 16 * kt);
     if (QJL) r.gr[kt] = *reinterpret_cast<const uint2*>(a.kgamma_r + gbase + 16 * kt);
   }
-  const uint32_t* pvd = a.vdir + tile * (WD * 64) + tin + tk + 64 * w0;
-  const uint32_t* pvn = a.vnrm + tile * (WN * 64) + tin + tk + 64 * w0;
+  const int vwo = (kValTri * FWD * w0) >> 5, vno = (kValTri * BN * w0) >> 5;
+  const uint32_t* pvd = a.vdir + tile * (WD * 64) + tin + tk;
+  const uint32_t* pvn = a.vnrm + tile * (WN * 64) + tin + tk;
 #pragma unroll
-  for (int j = 0; j < BW::kVD; ++j) r.vd[j] = (2 * j + w0 < WD) ? pvd[128 * j] : 0u;
+  for (int w = 0; w < BW::KVD; ++w) r.vd[w] = pvd[64 * min(vwo + w, WD - 1)];
 #pragma unroll
-  for (int j = 0; j < BW::kVN; ++j) r.vn[j] = (2 * j + w0 < WN) ? pvn[128 * j] : 0u;
+  for (int w = 0; w < BW::KVN; ++w) r.vn[w] = pvn[64 * min(vno + w, WN - 1)];
 }
 
 template <int BD, int BN, bool QJL, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * NW, kWaves = NW;
   constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD;
-  constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32, WV = WD + WN;
-  constexpr uint32_t kDirMask = (1u << FWD) - 1u, kNrmMask = (1u << BN) - 1u;
+  constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32;
   constexpr bool PRE = MODE == kPre;                // pre-split (code, rho) table
   constexpr bool BIG = K * K * R > kMaxSmallPre;    // one shared table, one WG per CU
   constexpr int kTab = PRE ? K * K * R : K * K;     // entries per table (16 B each)
   constexpr int kTabBytes = (PRE && BIG ? 1 : 2) * kTab * 16;
   constexpr int kRedBytes = kWaves * kMaxG * kHeadDim * 4;
   constexpr int kUnion = kTabBytes > kRedBytes ? kTabBytes : kRedBytes;
-  constexpr int kStageRow = WV + 1;                // words per staged token (+ pad)
 
   // tables during the scan, the per-wave partial sums afterwards
   __shared__ __attribute__((aligned(16))) char smem[kUnion];
   __shared__ float crk[R], crv[R], cxk[K], cxv[K];
-  __shared__ float qs[kMaxG * 132];                       // R q, then R' R q (QJL)
-  __shared__ uint32_t stage[kWaves * kBlock * kStageRow];  // value words of a block
+  // R q (then R' R q with QJL) during the set-up; the value-side table
+  // indices of each wavefront's block in the scan
+  constexpr int kQsBytes = kMaxG * 132 * 4, kIdxBytes = kWaves * kIdxRows * kIdxRow * 2;
+  __shared__ __attribute__((aligned(16))) char qbuf[kQsBytes > kIdxBytes ? kQsBytes : kIdxBytes];
+  float* qs = reinterpret_cast<float*>(qbuf);
   __shared__ float red_ml[kWaves * kMaxG * 2];
 
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
@@ -263,8 +296,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   const size_t plane = (size_t)b * a.Hkv + g;
   uint4* tabk = reinterpret_cast<uint4*>(smem);
   uint4* tabv = a.shared_tables ? tabk : tabk + kTab;
-  static_assert(!(PRE && BIG) || kWaves * kBlock * kStageRow >= 4 * K * K,
-                "the stage area holds the per-code directions while the table is built");
   float* red_o = reinterpret_cast<float*>(smem);          // [wave][head][128]
 
   // ---- every global load of the prologue goes out first, none waiting for
@@ -316,21 +347,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const int n_tables = a.shared_tables ? 1 : 2;
+  // pre-split tables are rho-major, entry rho_index K^2 + code pair, so that
+  // consecutive lanes write consecutive entries
+  constexpr int KK = K * K;
   if (PRE && BIG) {
-    // the (shared) table has K^2 R entries: n^ of every code pair first, in
-    // the stage area, then one entry per lane and step, consecutive lanes on
-    // consecutive entries
-    float4* ncode = reinterpret_cast<float4*>(stage);
-    for (int c = tid; c < K * K; c += kThreads) ncode[c] = decode_dir(cxk[c % K], cxk[c / K]);
-    __syncthreads();
-    for (int e = tid; e < kTab; e += kThreads) tabk[e] = presplit_entry(ncode[e / R], crk[e % R]);
+    // the (shared) table: each lane decodes the direction of its code pairs
+    // once, in registers, and writes the entries of every norm index
+    if constexpr (KK >= kThreads) {
+      for (int c = tid; c < KK; c += kThreads) {
+        const float4 n = decode_dir(cxk[c % K], cxk[c / K]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) tabk[r * KK + c] = presplit_entry(n, crk[r]);
+      }
+    } else {
+      constexpr int kSlices = kThreads / KK;        // lanes per code pair
+      const int c = tid % KK;
+      const float4 n = decode_dir(cxk[c % K], cxk[c / K]);
+#pragma unroll
+      for (int r = tid / KK; r < R; r += kSlices) tabk[r * KK + c] = presplit_entry(n, crk[r]);
+    }
   } else {
     for (int e = tid; e < n_tables * kTab; e += kThreads) {
       const bool v = e >= kTab;
       const int i = v ? e - kTab : e;
       const float* cx = v ? cxv : cxk;
       if (PRE) {
-        const int code = i / R, r = i - code * R;
+        const int code = i % KK, r = i / KK;
         tabk[e] = presplit_entry(decode_dir(cx[code % K], cx[code / K]), (v ? crv : crk)[r]);
       } else {
         const float4 n = decode_dir(cx[i % K], cx[i / K]);
@@ -350,23 +392,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // Q^T operands (B): column col = head, call (gi, c), slot e = component c
-  // of triplet 11 grp4 + 8 gi + e (zero outside the group's triplets and
-  // beyond the 128 real coordinates).
-  half8 qh[2][3], ql[2][3];
+  // Q^T operands (B), column col = head, six calls m.  Pre-split tables:
+  // slot e of call m = component e % 4 of the group's triplet 2 m + e / 4
+  // (component 3 is a zero pad), so a table entry {hx|hy, hz|0, lx|ly, lz|0}
+  // is, as it stands, half of an hi and half of an lo operand.  fp32 tables:
+  // call m = (gi, c) = (m / 3, m % 3), slot e = component c of triplet
+  // 8 gi + e.  Zero outside the group's triplets and the 128 coordinates.
+  half8 qh[6], ql[6];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi)
+  for (int m = 0; m < 6; ++m) {
+    float x[8];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 8 * gi + e;
-        const int coord = 3 * (kTriPerGroup * grp4 + j) + c;
-        x[e] = j < kTriPerGroup && coord < kHeadDim ? qs[col * 132 + coord] : 0.0f;
-      }
-      split8(x, qh[gi][c], ql[gi][c]);
+    for (int e = 0; e < 8; ++e) {
+      const int j = PRE ? 2 * m + (e >> 2) : 8 * (m / 3) + e;
+      const int c = PRE ? e & 3 : m % 3;
+      const int coord = 3 * (kTriPerGroup * grp4 + j) + c;
+      x[e] = c < 3 && j < kTriPerGroup && coord < kHeadDim ? qs[col * 132 + coord] : 0.0f;
     }
+    split8(x, qh[m], ql[m]);
+  }
   // QJL operands: call k, slot e of group grp4 = bit 32 grp4 + 8 k + e.
   half8 ph[QJL ? 4 : 1], pl[QJL ? 4 : 1];
   if (QJL) {
@@ -396,32 +440,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < 3; ++c) o[i][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;            // of head `col`
-  uint32_t* st = &stage[wave * kBlock * kStageRow];
   const float qjl_c = 1.2533141373155003f * kInvSqrtD;   // sqrt(pi / 2) / sqrt(d)
-
-  // value-side positions of this lane's triplets 16 grp + col
-  int vdw[3], vdsh[3], vnw[3], vnsh[3];
+  uint16_t* vidx = reinterpret_cast<uint16_t*>(qbuf) + wave * (kIdxRows * kIdxRow);
+  // value-side rows of this lane's triplets 16 i + col (lanes past the last
+  // triplet read a copy of it: finite values in columns never written out)
+  int vrow[3];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int tri = min(16 * i + col, kNTri - 1);
-    vdw[i] = (tri * FWD) >> 5;
-    vdsh[i] = (tri * FWD) & 31;
-    vnw[i] = WD + ((tri * BN) >> 5);
-    vnsh[i] = (tri * BN) & 31;
-  }
+  for (int i = 0; i < 3; ++i) vrow[i] = min(16 * i + col, kNTri - 1) * kIdxRow + 4 * grp4;
+  __syncthreads();                 // every wave is done with qs before it holds indices
 
   if (QJL && t0 < t_end) load_block(blk, a, plane, t0, L);   // (registers are short)
   for (; t0 < t_end; t0 += kWaves * kBlock) {
-    // -- stage the block's value words, token-major (the previous block's
-    //    reads of the stage ended at the wave_sync closing its iteration)
+    // -- value-side table indices, code | rho index << 2 b_dir (the entry of a
+    //    pre-split table), into this wavefront's rows (the previous block's
+    //    reads of them ended at the wave_sync closing its iteration)
     {
-      const int w0 = L >> 5, tk = L & 31;
+      using BW = BlockWords<BD, BN, QJL>;
+      const int h = L >> 5, tk = L & 31;
+      const uint32_t dsh = (kValTri * FWD * h) & 31, nsh = (kValTri * BN * h) & 31;
+      uint32_t rd[BW::KVD], rn[BW::KVN];
 #pragma unroll
-      for (int j = 0; j < blk.kVD; ++j)
-        if (2 * j + w0 < WD) st[tk * kStageRow + 2 * j + w0] = blk.vd[j];
+      for (int w = 0; w < BW::KVD; ++w)
+        rd[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KVD ? blk.vd[w + 1] : 0u, blk.vd[w], dsh);
 #pragma unroll
-      for (int j = 0; j < blk.kVN; ++j)
-        if (2 * j + w0 < WN) st[tk * kStageRow + WD + 2 * j + w0] = blk.vn[j];
+      for (int w = 0; w < BW::KVN; ++w)
+        rn[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KVN ? blk.vn[w + 1] : 0u, blk.vn[w], nsh);
+      uint16_t* row = vidx + kValTri * h * kIdxRow + tk;
+#pragma unroll
+      for (int j = 0; j < kValTri; ++j)
+        row[j * kIdxRow] = (uint16_t)(field<FWD>(rd, j * FWD) | (field<BN>(rn, j * BN) << FWD));
     }
     // -- scores, two 16-token tiles
     floatx4 sc[2];
@@ -438,22 +485,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
       for (int w = 0; w < BW::KWN; ++w)
         nw[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KWN ? blk.nw[kt][w + 1] : 0u, blk.nw[kt][w], nsh);
       floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (PRE) {
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-        half8 ah[3], al[3];
-        if (PRE) {
-          uint4 E[8];
+        for (int m = 0; m < 6; ++m) {
+          // triplets 2 m and 2 m + 1 of the group (the twelfth is padding)
+          const int j0 = 2 * m, j1 = 2 * m + 1;
+          const uint4 E0 = tabk[field<FWD>(dw, j0 * FWD) + field<BN>(nw, j0 * BN) * KK];
+          const uint4 E1 = j1 < kTriPerGroup
+                               ? tabk[field<FWD>(dw, j1 * FWD) + field<BN>(nw, j1 * BN) * KK]
+                               : make_uint4(0u, 0u, 0u, 0u);
+          const u32x4 h = {E0.x, E0.y, E1.x, E1.y}, l = {E0.z, E0.w, E1.z, E1.w};
+          acc = mfma3(__builtin_bit_cast(half8, h), __builtin_bit_cast(half8, l), qh[m], ql[m], acc);
+        }
+      } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 8 * gi + e;               // the group's triplet
-            if (j >= kTriPerGroup) {
-              E[e] = make_uint4(0u, 0u, 0u, 0u);
-              continue;
-            }
-            E[e] = tabk[field<FWD>(dw, j * FWD) * R + field<BN>(nw, j * BN)];
-          }
-          operands_pre(E, ah, al);
-        } else {
+        for (int gi = 0; gi < 2; ++gi) {
+          half8 ah[3], al[3];
           float ux[8], uy[8], uz[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -471,9 +518,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
           split8(ux, ah[0], al[0]);
           split8(uy, ah[1], al[1]);
           split8(uz, ah[2], al[2]);
-        }
 #pragma unroll
-        for (int c = 0; c < 3; ++c) acc = mfma3(ah[c], al[c], qh[gi][c], ql[gi][c], acc);
+          for (int c = 0; c < 3; ++c) acc = mfma3(ah[c], al[c], qh[3 * gi + c], ql[3 * gi + c], acc);
+        }
       }
       // this lane's 4 tokens: t0 + 16 kt + 4 grp4 + r, head col
       const int tb = t0 + 16 * kt + 4 * grp4;
@@ -522,8 +569,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = m_run == m_new ? 1.0f : __expf(m_run - m_new);
     float pw[8], psum = 0.0f;
@@ -537,8 +583,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
         pw[4 * kt + r] = p * gva[r];
       }
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = rows_sum(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
     half8 pah, pal;
@@ -561,28 +606,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     for (int i = 0; i < 3; ++i) {
       // with QJL the registers are short: one value tile at a time
       if (QJL) __builtin_amdgcn_sched_barrier(0);
-      // lanes past the last triplet decode a clamped copy of it: finite
-      // values in output columns the epilogue never writes
+      // indices of tokens 4 grp4 + (0..3) and 16 + 4 grp4 + (0..3): slots e
+      const uint2 p0 = *reinterpret_cast<const uint2*>(vidx + vrow[i]);
+      const uint2 p1 = *reinterpret_cast<const uint2*>(vidx + vrow[i] + 16);
+      const uint32_t pw2[4] = {p0.x, p0.y, p1.x, p1.y};
       half8 bh[3], bl[3];
       if (PRE) {
         uint4 E[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t* sr = &st[(16 * (e >> 2) + 4 * grp4 + (e & 3)) * kStageRow];
-          const uint32_t code = __builtin_amdgcn_alignbit(sr[vdw[i] + 1], sr[vdw[i]], vdsh[i]) & kDirMask;
-          const uint32_t ir = __builtin_amdgcn_alignbit(sr[vnw[i] + 1], sr[vnw[i]], vnsh[i]) & kNrmMask;
-          E[e] = tabv[code * R + ir];
-        }
+        for (int e = 0; e < 8; ++e) E[e] = tabv[(pw2[e >> 1] >> (16 * (e & 1))) & 0xffffu];
         operands_pre(E, bh, bl);
       } else {
         float vx[8], vy[8], vz[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t* sr = &st[(16 * (e >> 2) + 4 * grp4 + (e & 3)) * kStageRow];
-          const uint32_t code = __builtin_amdgcn_alignbit(sr[vdw[i] + 1], sr[vdw[i]], vdsh[i]) & kDirMask;
-          const uint32_t ir = __builtin_amdgcn_alignbit(sr[vnw[i] + 1], sr[vnw[i]], vnsh[i]) & kNrmMask;
-          const uint4 n = tabv[code];
-          const float rho = crv[ir];
+          const uint32_t idx = (pw2[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          const uint4 n = tabv[idx & (KK - 1)];
+          const float rho = crv[idx >> FWD];
           vx[e] = rho * __uint_as_float(n.x);
           vy[e] = rho * __uint_as_float(n.y);
           vz[e] = rho * __uint_as_float(n.z);
