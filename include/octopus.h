@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define OCTO_ABI_VERSION 1u
+#define OCTO_ABI_VERSION 2u
 
 typedef enum {
   OCTO_OK = 0,
@@ -88,8 +88,8 @@ typedef struct {
   int32_t qjl;            /* 1: keys carry the QJL sign sketch (Sec. 3.6)      */
   int32_t reserved;
   uint64_t seed;          /* rotation seed                                     */
-  const float* c_xi;      /* device, 2^b_dir fp32 centroids, ascending         */
-  const float* c_rho;     /* device, 2^b_nrm fp32 centroids, ascending         */
+  const float* c_xi;      /* host, 2^b_dir fp32 centroids, ascending           */
+  const float* c_rho;     /* host, 2^b_nrm fp32 centroids, ascending           */
 } octo_codec_desc;
 
 /* A packed cache for one tensor (K or V), layout OCTO_LAYOUT_TILE64.        */

@@ -7,20 +7,22 @@ is no fallback of any kind.  torch provides device memory and streams.
 
 Names follow the C ABI: octo_encode, octo_attend_decode, octo_attend_chunk,
 octo_record_sizes, octo_decode_workspace_bytes, octo_chunk_workspace_bytes.
-The helper classes Codec and PackedCache allocate the codebook tables and the
-packed streams with torch and build the descriptor structs.
+The helper classes Codec and PackedCache hold the codebook values (host
+arrays) and allocate the packed streams with torch, and build the descriptor
+structs.
 """
 import ctypes
 import json
 import os
 
+import numpy as np
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liboctopus.so")
 CODEBOOKS = os.path.join(PKG, "codebooks", "octopus_d{d}.json")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 STATUS = ["OCTO_OK", "OCTO_ERR_INVALID_ARGUMENT", "OCTO_ERR_UNSUPPORTED", "OCTO_ERR_ALIGNMENT",
           "OCTO_ERR_CAPACITY", "OCTO_ERR_WORKSPACE_TOO_SMALL", "OCTO_ERR_VERSION", "OCTO_ERR_HIP"]
 DTYPE_F32, DTYPE_BF16 = 0, 1
@@ -114,11 +116,8 @@ def load_codebooks(d=128):
         return json.load(f)
 
 
-_shared_tables = {}
-
-
 class Codec:
-    """A codec descriptor with its fp32 codebook tables on `device`.
+    """A codec descriptor with its fp32 codebook values (host arrays).
 
     bits: b; the split defaults to the paper's (b+1, b-1) (b_dir, b_nrm).
     The codebook values come from the shipped artifact (Lloyd-Max tables,
@@ -128,22 +127,13 @@ class Codec:
                  rounding=ROUND_LOCAL3X3, device="cuda", d=128, tables=None):
         if b_dir is None:
             b_dir, b_nrm = bits + 1, bits - 1
-        if tables is None:
-            # codecs of one (d, split, device) share their device tables, so a
-            # K and a V codec of the same split pass the same pointers and the
-            # attention kernels build one LDS table for both
-            key = (d, b_dir, b_nrm, str(device))
-            if key not in _shared_tables:
-                art = load_codebooks(d)
-                _shared_tables[key] = (
-                    torch.tensor(art["c_xi"][str(b_dir)], dtype=torch.float32, device=device),
-                    torch.tensor(art["c_rho"][str(b_nrm)], dtype=torch.float32, device=device))
-            self.c_xi, self.c_rho = _shared_tables[key]
-        else:
-            self.c_xi = torch.tensor(tables["c_xi"][str(b_dir)], dtype=torch.float32, device=device)
-            self.c_rho = torch.tensor(tables["c_rho"][str(b_nrm)], dtype=torch.float32, device=device)
+        art = tables or load_codebooks(d)
+        # host arrays: the library reads the values at each call and hands
+        # them to the kernels by value
+        self.c_xi = np.ascontiguousarray(art["c_xi"][str(b_dir)], dtype=np.float32)
+        self.c_rho = np.ascontiguousarray(art["c_rho"][str(b_nrm)], dtype=np.float32)
         self.desc = CodecDesc(ABI_VERSION, d, bits, b_dir, b_nrm, rounding, int(bool(qjl)), 0,
-                              seed, self.c_xi.data_ptr(), self.c_rho.data_ptr())
+                              seed, self.c_xi.ctypes.data, self.c_rho.ctypes.data)
         self.bits, self.b_dir, self.b_nrm, self.seed, self.qjl = bits, b_dir, b_nrm, seed, bool(qjl)
         self.rounding, self.d, self.device = rounding, d, device
 

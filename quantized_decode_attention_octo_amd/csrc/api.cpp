@@ -5,6 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
+#include <cstring>
+
 #include "octo_internal.h"
 
 namespace octo {
@@ -57,10 +60,22 @@ octo_status resolve_codec(const octo_codec_desc* d, const char* what, Codec* out
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: rounding %d unknown", what, d->rounding);
   if (d->qjl != 0 && d->qjl != 1)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: qjl must be 0 or 1", what);
-  if (need_tables && (!d->c_xi || !d->c_rho))
-    return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: codebook pointer is NULL", what);
-  if (((uintptr_t)d->c_xi | (uintptr_t)d->c_rho) & 3)
-    return fail(OCTO_ERR_ALIGNMENT, "%s: codebooks must be 4-byte aligned", what);
+  Codebook cb;
+  std::memset(&cb, 0, sizeof(cb));
+  if (need_tables) {
+    if (!d->c_xi || !d->c_rho)
+      return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: codebook pointer is NULL", what);
+    if (((uintptr_t)d->c_xi | (uintptr_t)d->c_rho) & 3)
+      return fail(OCTO_ERR_ALIGNMENT, "%s: codebooks must be 4-byte aligned", what);
+    std::memcpy(cb.xi, d->c_xi, sizeof(float) << bd);
+    std::memcpy(cb.rho, d->c_rho, sizeof(float) << bn);
+    for (int i = 0; i < (1 << bd); ++i)
+      if (!std::isfinite(cb.xi[i]) || (i > 0 && !(cb.xi[i] > cb.xi[i - 1])))
+        return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: c_xi is not finite and ascending", what);
+    for (int i = 0; i < (1 << bn); ++i)
+      if (!std::isfinite(cb.rho[i]) || (i > 0 && !(cb.rho[i] > cb.rho[i - 1])))
+        return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: c_rho is not finite and ascending", what);
+  }
   out->b_dir = bd;
   out->b_nrm = bn;
   out->K = 1 << bd;
@@ -71,8 +86,7 @@ octo_status resolve_codec(const octo_codec_desc* d, const char* what, Codec* out
   out->qjl = d->qjl;
   out->rounding = d->rounding;
   out->seed = d->seed;
-  out->c_xi = d->c_xi;
-  out->c_rho = d->c_rho;
+  out->cb = cb;
   return OCTO_OK;
 }
 

@@ -108,8 +108,7 @@ template <int BD, int BN, bool TRANSPOSED>
 __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __restrict__ dir,
                                                           const uint32_t* __restrict__ nrm,
                                                           const float* __restrict__ gamma,
-                                                          const float* __restrict__ c_xi,
-                                                          const float* __restrict__ c_rho,
+                                                          const Codebook cb,
                                                           int capacity, int cached,
                                                           _Float16* __restrict__ out,
                                                           int out_rows) {
@@ -120,8 +119,8 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
   __shared__ float crho[R], cxi[K];
   __shared__ __attribute__((aligned(16))) _Float16 tile[64 * kRow];
   const int tid = threadIdx.x;
-  if (tid < K) cxi[tid] = c_xi[tid];
-  if (tid < R) crho[tid] = c_rho[tid];
+  if (tid < K) cxi[tid] = cb.xi[tid];
+  if (tid < R) crho[tid] = cb.rho[tid];
   __syncthreads();
   for (int e = tid; e < K * K; e += 256) lut[e] = oct_dir(cxi[e % K], cxi[e / K]);
   __syncthreads();
@@ -400,10 +399,10 @@ void launch_decode_rows(const octo_cache_view* c, const Codec& cd, int cached, _
   dim3 grid((cached + 63) / 64, c->batch * c->kv_heads);
   if (transposed)
     hipLaunchKernelGGL((decode_rows_kernel<BD, BN, true>), grid, dim3(256), 0, st, c->dir,
-                       c->nrm, c->gamma, cd.c_xi, cd.c_rho, c->capacity, cached, out, out_rows);
+                       c->nrm, c->gamma, cd.cb, c->capacity, cached, out, out_rows);
   else
     hipLaunchKernelGGL((decode_rows_kernel<BD, BN, false>), grid, dim3(256), 0, st, c->dir,
-                       c->nrm, c->gamma, cd.c_xi, cd.c_rho, c->capacity, cached, out, out_rows);
+                       c->nrm, c->gamma, cd.cb, c->capacity, cached, out, out_rows);
 }
 
 bool decode_rows(const octo_cache_view* c, const Codec& cd, int cached, _Float16* out,

@@ -55,6 +55,8 @@
 // invalidate a whole L2 per workgroup and cost far more than a launch.)
 #include <math.h>
 
+#include <cstring>
+
 #include "octo_internal.h"
 
 namespace octo {
@@ -85,8 +87,8 @@ struct DecodeArgs {
   const int* seq_lens;
   int max_len;
   float scale;
-  const float *kc_xi, *kc_rho, *vc_xi, *vc_rho;
-  int shared_tables;   // K and V use the same codebooks
+  Codebook kcb, vcb;   // C_xi, C_rho of K and of V
+  int shared_tables;   // K and V use the same codebook values
   uint64_t kseed, vseed;
   const uint32_t *kdir, *knrm, *kqjl, *vdir, *vnrm;
   const float *kgamma, *vgamma;
@@ -303,12 +305,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   // capacity is in bounds, whatever seq_lens holds) and seq_lens.
   float cx_k = 0.0f, cx_v = 0.0f, cr_k = 0.0f, cr_v = 0.0f;
   if (tid < K) {
-    cx_k = a.kc_xi[tid];
-    cx_v = a.vc_xi[tid];
+    cx_k = a.kcb.xi[tid];
+    cx_v = a.vcb.xi[tid];
   }
   if (tid < R) {
-    cr_k = a.kc_rho[tid];
-    cr_v = a.vc_rho[tid];
+    cr_k = a.kcb.rho[tid];
+    cr_v = a.vcb.rho[tid];
   }
   constexpr int kHeadsPerWave = kMaxG / kWaves;
   float qv[kHeadsPerWave][2];
@@ -876,7 +878,7 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
                 max_seq_len, k_cache->capacity);
   if (B > 65535 || Hkv > 65535 || num_q_heads > 65535)
     return fail(OCTO_ERR_UNSUPPORTED, "%s: batch and heads must be <= 65535", what);
-  const bool shared = kc.c_xi == vc.c_xi && kc.c_rho == vc.c_rho;
+  const bool shared = std::memcmp(&kc.cb, &vc.cb, sizeof(Codebook)) == 0;
   const Plan p = make_plan(B, num_q_heads, Hkv, max_seq_len, waves_for(kc.b_dir, kc.b_nrm, shared));
   if (!workspace || workspace_bytes < p.total)
     return fail(OCTO_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", what,
@@ -894,10 +896,8 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
   a.seq_lens = seq_lens;
   a.max_len = max_seq_len;
   a.scale = softmax_scale > 0.0f ? softmax_scale : kInvSqrtD;
-  a.kc_xi = kc.c_xi;
-  a.kc_rho = kc.c_rho;
-  a.vc_xi = vc.c_xi;
-  a.vc_rho = vc.c_rho;
+  a.kcb = kc.cb;
+  a.vcb = vc.cb;
   a.shared_tables = shared;
   a.kseed = kc.seed;
   a.vseed = vc.seed;

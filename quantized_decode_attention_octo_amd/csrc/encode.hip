@@ -42,8 +42,7 @@ struct EncodeArgs {
   int64_t s0, s1, s2;             // element strides of b, h, t
   int is_bf16, vec16;             // vec16: every row starts 16-byte aligned
   int B, H, T;
-  const float* c_xi;
-  const float* c_rho;
+  Codebook cb;                    // C_xi, C_rho values
   uint64_t seed;
   int qjl, rounding;
   uint32_t* dir;
@@ -211,8 +210,8 @@ __global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
   }
 
   // ---- tables: codebooks, cell boundaries, decoded directions
-  if (tid < K) cxi[tid] = a.c_xi[tid];
-  if (tid < R) crho[tid] = a.c_rho[tid];
+  if (tid < K) cxi[tid] = a.cb.xi[tid];
+  if (tid < R) crho[tid] = a.cb.rho[tid];
   if (tid == 0) {
     guess_bad = 0;
     midp[0] = -INFINITY;
@@ -427,8 +426,7 @@ extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, 
   a.B = B;
   a.H = H;
   a.T = T;
-  a.c_xi = c.c_xi;
-  a.c_rho = c.c_rho;
+  a.cb = c.cb;
   a.seed = c.seed;
   a.qjl = c.qjl;
   a.rounding = c.rounding;

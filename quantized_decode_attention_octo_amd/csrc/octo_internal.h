@@ -22,6 +22,17 @@ constexpr float kEps = 1e-20f;           // the eps-safe divisor of Sec. 3.1 / 3
 constexpr int kWave = 64;
 
 
+constexpr int kMaxXi = 32;            // 2^b_dir centroids, b_dir <= 5
+constexpr int kMaxRho = 16;           // 2^b_nrm centroids, b_nrm <= 4
+
+// The codebook values, passed to the kernels by value (kernel arguments
+// arrive with the launch: no dependent load of a table before the kernels
+// can build their LDS tables).  Unused entries are zero.
+struct Codebook {
+  float xi[kMaxXi];
+  float rho[kMaxRho];
+};
+
 // A codec with its bit split resolved (Sec. 3.3: B_tri = 2 b_dir + b_nrm).
 struct Codec {
   int b_dir, b_nrm;     // bits per octahedral coordinate / per triplet norm
@@ -31,8 +42,7 @@ struct Codec {
   int qjl;
   int rounding;
   uint64_t seed;
-  const float* c_xi;
-  const float* c_rho;
+  Codebook cb;          // the C_xi, C_rho values read from the descriptor
 };
 
 // ---------------------------------------------------------------- host side
@@ -40,7 +50,8 @@ struct Codec {
 octo_status fail(octo_status s, const char* fmt, ...);
 void clear_error();
 // Validates a descriptor and resolves its split; nothing on the device is read.
-// need_tables: the codebook pointers must be set (every compute entry point).
+// need_tables: the codebook pointers must be set and are read (every compute
+// entry point): finite, ascending values.
 octo_status resolve_codec(const octo_codec_desc* desc, const char* what, Codec* out,
                           bool need_tables = true);
 // Validates a cache view against a codec (pointers, sizes, alignment).

@@ -6,6 +6,8 @@ B_tri = 2 b_dir + b_nrm bits per triplet, 43 triplets at d = 128), and that
 every host-checkable error is reported before anything is launched.
 """
 import ctypes
+
+import numpy as np
 import os
 import re
 
@@ -45,9 +47,12 @@ def test_version_and_status_strings(L):
     assert L.octo_status_string(99).decode() == "OCTO_ERR_UNKNOWN"
 
 
+_TABLE = np.linspace(-0.9, 0.9, 32).astype(np.float32)     # ascending, finite
+
+
 def desc(bits=3, b_dir=0, b_nrm=0, qjl=0, head_dim=128, version=ob.ABI_VERSION, tables=True,
-         rounding=0):
-    p = 4096 if tables else 0
+         rounding=0, table=_TABLE):
+    p = table.ctypes.data if tables else 0
     return ob.CodecDesc(version, head_dim, bits, b_dir, b_nrm, rounding, qjl, 0, 0, p, p)
 
 
@@ -115,6 +120,23 @@ def test_encode_errors(L):
     assert enc(L, d, ctypes.c_void_p(8193), 1, 1, 64, view(), 0) == 3
     assert enc(L, desc(qjl=1), x, 1, 1, 64, view(), 0) == 1  # QJL needs its streams
     assert enc(L, d, x, 1, 1, 0, view(), 0) == 0            # T = 0: nothing to do
+
+
+def test_codebook_values_are_checked(L):
+    """The codebooks are host arrays read at each call: finite and ascending."""
+    x = ctypes.c_void_p(8192)
+    bad = _TABLE.copy()
+    bad[3], bad[4] = bad[4], bad[3]                          # not ascending
+    assert enc(L, desc(table=bad), x, 1, 1, 64, view(), 0) == 1
+    assert b"ascending" in L.octo_last_error()
+    bad = _TABLE.copy()
+    bad[0] = np.nan
+    assert enc(L, desc(table=bad), x, 1, 1, 64, view(), 0) == 1
+    # only the 2^b_dir (2^b_nrm) leading values are read: a table whose tail is
+    # not ascending is accepted for a smaller split
+    tail = _TABLE.copy()
+    tail[20] = -5.0
+    assert enc(L, desc(table=tail), x, 1, 1, 0, view(), 0) == 0
 
 
 def dec(L, kd, vd, kv, vv, Hq=4, lens=4096, max_len=128, out=4096, ws=4096, ws_bytes=1 << 20,
