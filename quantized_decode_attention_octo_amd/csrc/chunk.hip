@@ -22,6 +22,8 @@
 // The window is decoded once per call and shared by every query tile.
 #include <math.h>
 
+#include <type_traits>
+
 #include "octo_internal.h"
 
 namespace octo {
@@ -34,16 +36,28 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr float kInvSqrtD = 0.08838834764831845f;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Column of key k in the transposed value matrix.  Within each 32-key block
+// the keys are stored in the order in which the score MFMA leaves them in a
+// lane's P slots (slot e of lane group g is key 16 (e / 4) + 4 g + e % 4), so
+// that a lane's eight value slots are eight consecutive halves: one 16-byte
+// LDS read.
+__device__ inline int key_column(int k) {
+  return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+}
+
 // ---------------------------------------------------------------- pre-passes
-// Rows t < T_out of a plane: fp16(H diag(s) x_t / sqrt(d)), zero for t >= T
-// (tile padding).  Row-major output: row out_off + t of a [out_rows][128]
-// plane.  Transposed output: column out_off + t of a [128][out_rows] plane.
+// Rows t < T_out of a plane: fp16(post H diag(s) x_t), zero for t >= T (tile
+// padding); post = 1 / sqrt(d), times the softmax scale and log2(e) for the
+// queries, so that scores come out of the MFMA in log2 units.  Row-major
+// output: row out_off + t of a [out_rows][128] plane.  Transposed output:
+// column key_column(out_off + t) of a [128][out_rows] plane.
 // One workgroup takes 64 rows, one wavefront per row for the transform; the
 // transposed store goes through LDS so that 64 consecutive columns are
 // written together.
 template <bool TRANSPOSED>
 __global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __restrict__ in,
                                                           int T, int T_out, uint64_t seed,
+                                                          float post,
                                                           _Float16* __restrict__ out,
                                                           int out_rows, int out_off) {
   __shared__ _Float16 tile[TRANSPOSED ? 64 * 130 : 1];
@@ -70,12 +84,12 @@ __global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __rest
       float a = xa[j] * s0, b = xb[j] * s1;
       wht128(a, b);
       if (TRANSPOSED) {
-        tile[k * 130 + lane] = (_Float16)(a * kInvSqrtD);
-        tile[k * 130 + lane + 64] = (_Float16)(b * kInvSqrtD);
+        tile[k * 130 + lane] = (_Float16)(a * post);
+        tile[k * 130 + lane + 64] = (_Float16)(b * post);
       } else if (t < T_out) {
         _Float16* dst = out + ((size_t)plane * out_rows + out_off + t) * kHeadDim;
-        dst[lane] = (_Float16)(a * kInvSqrtD);
-        dst[lane + 64] = (_Float16)(b * kInvSqrtD);
+        dst[lane] = (_Float16)(a * post);
+        dst[lane + 64] = (_Float16)(b * post);
       }
     }
   }
@@ -83,7 +97,8 @@ __global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __rest
     __syncthreads();
     for (int e = threadIdx.x; e < 64 * kHeadDim; e += 256) {
       const int c = e >> 6, k = e & 63, t = t0 + k;
-      if (t < T_out) out[((size_t)plane * kHeadDim + c) * out_rows + out_off + t] = tile[k * 130 + c];
+      if (t < T_out)
+        out[((size_t)plane * kHeadDim + c) * out_rows + key_column(out_off + t)] = tile[k * 130 + c];
     }
   }
 }
@@ -103,7 +118,7 @@ __device__ inline float4 oct_dir(float xi, float eta) {
 // items token-fastest (coalesced reads of the tile-64 words) and write
 // fp16(gamma_t u^_t[0:128]) into an LDS tile, which is then stored as rows t
 // of a [out_rows][128] plane (16-byte chunks) or as columns t of a
-// [128][out_rows] plane (64 consecutive columns per row).
+// [128][out_rows] plane (64 consecutive keys per row, at key_column).
 template <int BD, int BN, bool TRANSPOSED>
 __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __restrict__ dir,
                                                           const uint32_t* __restrict__ nrm,
@@ -149,7 +164,7 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
   if (TRANSPOSED) {
     for (int e = tid; e < 64 * kHeadDim; e += 256) {
       const int c = e >> 6, k = e & 63;
-      if (k < nt) out[(plane * kHeadDim + c) * out_rows + t0 + k] = tile[k * kRow + c];
+      if (k < nt) out[(plane * kHeadDim + c) * out_rows + key_column(t0 + k)] = tile[k * kRow + c];
     }
   } else {
     typedef _Float16 half8v __attribute__((ext_vector_type(8)));
@@ -173,13 +188,12 @@ constexpr int kKStride = 136;   // halves per key row in LDS (128 + 8 pad)
 constexpr int kVStride = 72;    // halves per transposed value row in LDS (64 + 8 pad)
 
 struct ChunkArgs {
-  const _Float16* q;   // [B][Hq][Tq][128] rotated
+  const _Float16* q;   // [B][Hq][Tq][128] rotated, times scale log2(e)
   const _Float16* k;   // [B][Hkv][Tk_pad][128] rotated
   const _Float16* vt;  // [B][Hkv][128][Tk_pad] rotated, transposed
   float* out;          // [B][Hq][Tq][128]
   int Hq, Hkv, Tq, Tk, Tk_pad;
   int q_tiles;         // query tiles per (batch, head)
-  float scale2;        // softmax scale * log2(e)
   uint64_t vseed;
 };
 
@@ -241,22 +255,31 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
 
   const size_t kbase = ((size_t)b * a.Hkv + hk) * a.Tk_pad * kHeadDim;
   const size_t vbase = ((size_t)b * a.Hkv + hk) * kHeadDim * a.Tk_pad;
-  for (int kt0 = 0; kt0 < a.Tk; kt0 += kBN) {
-    __syncthreads();
-    // 64 keys x 128 dims of K and 128 dims x 64 keys of V^T: 1024 16-byte
-    // chunks each.
+  // The 64-key tiles of K (64 rows x 128 dims, contiguous) and V^T (128 rows x
+  // 64 keys) travel in 16-byte chunks, chunk tid + 128 j of each: a uniform
+  // base per tile plus a lane offset.  (Holding the next tile in registers
+  // during the current one does not fit beside two row groups' state.)
+  const uint32_t koff = 16u * tid;
+  const uint32_t voff = (uint32_t)(((size_t)(tid >> 3) * a.Tk_pad + 8 * (tid & 7)) * 2);
+  _Float16* const ks_dst = &ks[(tid >> 4) * kKStride + (tid & 15) * 8];
+  _Float16* const vs_dst = &vs[(tid >> 3) * kVStride + (tid & 7) * 8];
+  constexpr int kChunks = 1024 / kCThreads;
+  auto copy_tile = [&](int kt0) {
+    const char* kb = reinterpret_cast<const char*>(a.k + kbase + (size_t)kt0 * kHeadDim);
+    const char* vb = reinterpret_cast<const char*>(a.vt + vbase + kt0);
 #pragma unroll 4
-    for (int idx = tid; idx < 1024; idx += kCThreads) {
-      *reinterpret_cast<half8*>(&ks[(idx >> 4) * kKStride + (idx & 15) * 8]) =
-          *reinterpret_cast<const half8*>(a.k + kbase + (size_t)(kt0 + (idx >> 4)) * kHeadDim +
-                                          (idx & 15) * 8);
-      *reinterpret_cast<half8*>(&vs[(idx >> 3) * kVStride + (idx & 7) * 8]) =
-          *reinterpret_cast<const half8*>(a.vt + vbase + (size_t)(idx >> 3) * a.Tk_pad + kt0 +
-                                          (idx & 7) * 8);
+    for (int j = 0; j < kChunks; ++j) {
+      *reinterpret_cast<half8*>(ks_dst + j * (kCThreads / 16) * kKStride) =
+          *reinterpret_cast<const half8*>(kb + (size_t)j * (kCThreads * 16) + koff);
+      *reinterpret_cast<half8*>(vs_dst + j * (kCThreads / 8) * kVStride) =
+          *reinterpret_cast<const half8*>(vb + (size_t)j * (kCThreads / 8) * a.Tk_pad * 2 + voff);
     }
-    __syncthreads();
+  };
 
-    // scores of the 64 keys: st[kt][rg][r] = key kt0 + 16 kt + 4 grp + r
+  // One 64-key tile from LDS; only the last, ragged tile masks keys past Tk.
+  auto tile_step = [&](int kt0, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    // scores of the 64 keys (log2 units): st[kt][rg][r] = key kt0 + 16 kt + 4 grp + r
     floatx4 st[4][kRG];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -271,7 +294,6 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
           st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[rg][s], st[kt][rg], 0, 0, 0);
       }
     }
-    const bool full = kt0 + kBN <= a.Tk;
     half8 pf[kRG][2];
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
@@ -280,47 +302,56 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kt = e >> 2, r = e & 3;
-        x[e] = st[kt][rg][r] * a.scale2;
-        if (!full && kt0 + 16 * kt + 4 * grp + r >= a.Tk) x[e] = -INFINITY;
+        x[e] = st[kt][rg][r];
+        if (MASKED && kt0 + 16 * kt + 4 * grp + r >= a.Tk) x[e] = -INFINITY;
         mx = fmaxf(mx, x[e]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = rows_max(mx);
       const float m_new = fmaxf(m_run[rg], mx);
-      const float alpha = m_run[rg] == m_new ? 1.0f : exp2f(m_run[rg] - m_new);
+      const float alpha = m_run[rg] == m_new ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
       float ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(x[e] - m_new);
+        // probabilities are at most 1: the raw exp2 (flushing results below
+        // the normal range to zero) is exact enough
+        const float p = __builtin_amdgcn_exp2f(x[e] - m_new);
         ps += p;
         pf[rg][e >> 3][e & 7] = (_Float16)p;
       }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
+      ps = rows_sum(ps);
       l_run[rg] = l_run[rg] * alpha + ps;
       m_run[rg] = m_new;
-      // rescale O rows (queries q0 + 16 rg + 4 grp + r)
-      float al[4];
+      // rescale O rows (queries q0 + 16 rg + 4 grp + r) unless no row moved
+      if (__ballot(alpha != 1.0f)) {
+        float al[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
+        for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[rg][c][r] *= al[r];
+          for (int r = 0; r < 4; ++r) o[rg][c][r] *= al[r];
+      }
     }
     // O += P V: slot e of sub-block sb is key kt0 + 32 sb + 16 (e / 4) + 4 grp + e % 4
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const _Float16* vr = &vs[(16 * c + col) * kVStride + 32 * sb + 4 * grp];
-        const half4 v0 = *reinterpret_cast<const half4*>(vr);
-        const half4 v1 = *reinterpret_cast<const half4*>(vr + 16);
-        const half8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const half8 vf = *reinterpret_cast<const half8*>(&vs[(16 * c + col) * kVStride + 32 * sb + 8 * grp]);
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg)
           o[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg][sb], vf, o[rg][c], 0, 0, 0);
       }
+  };
+  const int tk_full = a.Tk / kBN * kBN;
+  for (int kt0 = 0; kt0 < a.Tk; kt0 += kBN) {
+    __syncthreads();               // the previous tile's LDS reads are done
+    copy_tile(kt0);
+    __syncthreads();
+    if (kt0 < tk_full)
+      tile_step(kt0, std::false_type{});
+    else
+      tile_step(kt0, std::true_type{});
   }
 
   // ---- epilogue: 1/l, then R_v^T = diag(s_v) H / sqrt(d) on every query row.
@@ -487,16 +518,18 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   _Float16* vr = reinterpret_cast<_Float16*>(ws + p.v_off);
   const int planes_q = B * num_q_heads, planes_kv = B * Hkv;
 
+  const float scale2 = (softmax_scale > 0.0f ? softmax_scale : kInvSqrtD) * kLog2e;
   hipLaunchKernelGGL(rotate_rows_kernel<false>, dim3((Tq + 63) / 64, planes_q), dim3(256), 0,
-                     stream, static_cast<const uint16_t*>(q), Tq, Tq, kc.seed, qr, Tq, 0);
+                     stream, static_cast<const uint16_t*>(q), Tq, Tq, kc.seed, kInvSqrtD * scale2,
+                     qr, Tq, 0);
   const int cur_out = p.Tk_pad - cached_tokens;  // current rows plus the zero tile padding
   if (cur_out > 0) {
     hipLaunchKernelGGL(rotate_rows_kernel<false>, dim3((cur_out + 63) / 64, planes_kv), dim3(256),
-                       0, stream, static_cast<const uint16_t*>(k_cur), Tc, cur_out, kc.seed, kr,
-                       p.Tk_pad, cached_tokens);
+                       0, stream, static_cast<const uint16_t*>(k_cur), Tc, cur_out, kc.seed,
+                       kInvSqrtD, kr, p.Tk_pad, cached_tokens);
     hipLaunchKernelGGL(rotate_rows_kernel<true>, dim3((cur_out + 63) / 64, planes_kv), dim3(256),
-                       0, stream, static_cast<const uint16_t*>(v_cur), Tc, cur_out, vc.seed, vr,
-                       p.Tk_pad, cached_tokens);
+                       0, stream, static_cast<const uint16_t*>(v_cur), Tc, cur_out, vc.seed,
+                       kInvSqrtD, vr, p.Tk_pad, cached_tokens);
   }
   if (cached_tokens > 0) {
     if (!decode_rows(k_cache, kc, cached_tokens, kr, p.Tk_pad, false, stream) ||
@@ -515,7 +548,6 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   a.Tk = p.Tk;
   a.Tk_pad = p.Tk_pad;
   a.q_tiles = (Tq + kBM - 1) / kBM;
-  a.scale2 = (softmax_scale > 0.0f ? softmax_scale : kInvSqrtD) * kLog2e;
   a.vseed = vc.seed;
   const long long units = (long long)a.q_tiles * num_q_heads * B;
   if (units > 0x7fffffffLL)
