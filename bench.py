@@ -23,6 +23,10 @@ roofline   for the attention call: algorithmic bytes (packed cache of the
 cpu_baseline  the float64 oracle on a bounded sample (one KV-head plane of
            the decode workload; a few query rows for the chunk workload),
            on one host thread, scaled to the same unit.
+cold       (decode) the same call over cache replicas spanning 600 MB, taken in
+           turn, so each call reads from HBM rather than the 256 MB
+           Infinity Cache; achieved GB/s and fraction of 8 TB/s beside it.
+           stream_copy_ceiling_GBps: read + write rate of a 1 GiB device copy.
 traffic    memory-side bytes per attention call, from rocprofv3 FETCH_SIZE and
            WRITE_SIZE counters (one --pmc run each) scaled by what the same
            counters read for a plain copy of known size; read from
@@ -98,6 +102,57 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
 
 
+COLD_BYTES = 600 * (1 << 20)        # replicas span this, beyond the 256 MB MALL
+
+
+def stream_ceiling_gbs():
+    """Read + write GB/s of a plain 1 GiB device copy: a practical ceiling,
+    reported beside (never instead of) the 8 TB/s peak."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / 5
+    del src, dst
+    return 2 * n * 4 / t / 1e9
+
+
+def cold_decode(w, kc, vc, kcache, vcache, q, seq, max_len, ws, out, steps):
+    """Attention over replicas of the packed cache taken in turn, spanning
+    COLD_BYTES, so that each call reads a cache the previous calls have
+    pushed out of the Infinity Cache.  Returns (replicas, mean us, percentiles)."""
+    per = kcache.nbytes() + vcache.nbytes()
+    n = max(2, -(-COLD_BYTES // per))
+    reps = []
+    for _ in range(n):
+        kr = octo.PackedCache(kc, w.B, w.Hkv, w.capacity)
+        vr = octo.PackedCache(vc, w.B, w.Hkv, w.capacity)
+        for a, b in ((kr, kcache), (vr, vcache)):
+            for f in ("dir", "nrm", "gamma", "qjl", "gamma_r"):
+                if getattr(a, f) is not None:
+                    getattr(a, f).copy_(getattr(b, f))
+        reps.append((kr, vr))
+    t = Timer()
+    for i in range(steps + n):
+        kr, vr = reps[i % n]
+        e0 = t.start() if i >= n else None
+        octo.octo_attend_decode(kc, vc, kr, vr, q, seq, max_len, out=out, ws=ws)
+        if i >= n:
+            t.stop(e0)
+    torch.cuda.synchronize()
+    res = (n, t.mean_ms() * 1e3, t.percentiles_us())
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
 def _pmc_per_kernel(path, counter):
     """Mean counter value per dispatch, by kernel name, from a rocprofv3 csv."""
     acc = {}
@@ -163,6 +218,13 @@ class Timer:
     def mean_ms(self):
         return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
 
+    def percentiles_us(self):
+        d = sorted(a.elapsed_time(b) * 1e3 for a, b in self.pairs)
+        if not d:
+            return None
+        pick = lambda q: d[min(len(d) - 1, int(q * (len(d) - 1) + 0.5))]
+        return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
 
 def run_decode(w, steps, warmup):
     inp = make_inputs(w)
@@ -202,19 +264,27 @@ def run_decode(w, steps, warmup):
     kv_bytes = tokens * w.Hkv * (packed_bytes_per_token(kc) + packed_bytes_per_token(vc))
     achieved = kv_bytes / (att_ms * 1e-3) / 1e9
     enc_tokens = w.B * w.T
+    n_rep, cold_us, cold_pct = cold_decode(w, kc, vc, kcache, vcache, q, seq, max_len, ws, out,
+                                           steps)
+    ceiling = stream_ceiling_gbs()
     res = {
         "value": tokens / (att_ms * 1e-3),
         "unit": "cached KV-tokens/s",
         "ms_per_step": wall / steps * 1e3,
         "dtype": "f32",
         "attention_us": att_ms * 1e3,
+        "attention_us_percentiles": t_att.percentiles_us(),
+        "cold": {"attention_us": cold_us, "percentiles_us": cold_pct, "replicas": n_rep,
+                 "achieved_GBps": kv_bytes / (cold_us * 1e-6) / 1e9,
+                 "frac": kv_bytes / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
         "encode_us": enc_ms * 1e3,
         "encode_tokens_per_s": enc_tokens / (enc_ms * 1e-3),
         "token_kv_heads_per_s": tokens * w.Hkv / (att_ms * 1e-3),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.key),
                      "kernel": "octo_attend_decode (split-K scan + merge)",
-                     "algorithmic_bytes_per_launch": kv_bytes},
+                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "stream_copy_ceiling_GBps": ceiling},
     }
     return res, (inp, kc, vc, kcache, vcache)
 
@@ -262,6 +332,7 @@ def run_chunk(w, steps, warmup):
         "ms_per_step": wall / steps * 1e3,
         "dtype": "f16-mfma/f32-acc",
         "attention_us": att_ms * 1e3,
+        "attention_us_percentiles": t_att.percentiles_us(),
         "encode_us": enc_ms * 1e3,
         "encode_tokens_per_s": w.B * Tq / (enc_ms * 1e-3),
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP16_PEAK_TFLOPS,
@@ -342,7 +413,19 @@ def cpu_baseline(w, state):
             sample = (f"oracle chunk attention of head 0, {int(done)} query rows over {keys} keys, "
                       f"scaled to {w.Hq} heads x {w.chunk_q} rows")
     return {"value": value, "unit": "cached KV-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": sample, "seconds": dt}
+            "sample": sample, "seconds": dt, "cpu_model": _cpu_model(),
+            "host_cores_available": len(os.sched_getaffinity(0)), "blas_threads": 1}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -389,10 +472,13 @@ def main():
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "attention_us": res["attention_us"], "encode_us": res["encode_us"],
+        "attention_us_percentiles": res.get("attention_us_percentiles"),
         "encode_tokens_per_s": res["encode_tokens_per_s"],
     }
     if "token_kv_heads_per_s" in res:
         line["token_kv_heads_per_s"] = res["token_kv_heads_per_s"]
+    if "cold" in res:
+        line["cold"] = res["cold"]
     print(json.dumps(line), flush=True)
 
 

@@ -139,6 +139,16 @@ def test_decode_group_sizes(Hq, Hkv):
     assert err <= ATOL
 
 
+def test_decode_many_splits():
+    """One KV head over a long context: more splits than the merge takes in
+    one round (its running-maximum rescale across rounds), big-table mode."""
+    w = workload("gqa32k", Hq=7, Hkv=1)
+    say("decode 7/1 heads, 40000 tokens")
+    err, _, _ = run_case(w, T=40000)
+    say(f"  max-abs err {err:.3e}")
+    assert err <= ATOL
+
+
 def test_decode_deterministic():
     w = workload("gqa32k")
     inp = make_inputs(w, scale_T=2000)
