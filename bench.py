@@ -135,7 +135,7 @@ def cold_decode(w, kc, vc, kcache, vcache, q, seq, max_len, ws, out, steps):
         kr = octo.PackedCache(kc, w.B, w.Hkv, w.capacity)
         vr = octo.PackedCache(vc, w.B, w.Hkv, w.capacity)
         for a, b in ((kr, kcache), (vr, vcache)):
-            for f in ("dir", "nrm", "gamma", "qjl", "gamma_r"):
+            for f in ("idx", "gamma", "qjl", "gamma_r"):
                 if getattr(a, f) is not None:
                     getattr(a, f).copy_(getattr(b, f))
         reps.append((kr, vr))
@@ -193,7 +193,7 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
 
 def packed_bytes_per_token(codec):
     s = codec.sizes()
-    b = 4 * (s.dir_words + s.nrm_words) + 4           # streams + gamma
+    b = 4 * s.idx_words + 4                           # index stream + gamma
     if codec.qjl:
         b += 4 * s.qjl_words + 2                      # sigma + fp16 gamma_r
     return b
@@ -352,7 +352,7 @@ def _host_plane(h, b, g):
     n = h["B"] * h["H"]
     p = b * h["H"] + g
     out = {"B": 1, "H": 1, "capacity": h["capacity"],
-           "dir": h["dir"].reshape(n, -1)[p], "nrm": h["nrm"].reshape(n, -1)[p],
+           "idx": h["idx"].reshape(n, -1)[p],
            "gamma": h["gamma"][b:b + 1, g:g + 1]}
     if "qjl" in h:
         out["qjl"] = h["qjl"].reshape(n, -1)[p]

@@ -29,10 +29,13 @@
  *
  * Cache layout (OCTO_LAYOUT_TILE64).  The paper fixes no bit layout; this one
  * is this library's.  A stream is a little-endian LSB-first bit string: field
- * j of width w occupies bits [j*w, (j+1)*w).  I_dir holds 2*n_tri fields of
- * b_dir bits ordered xi_0, eta_0, xi_1, eta_1, ...; I_nrm holds n_tri fields of
- * b_nrm bits; the QJL stream holds d one-bit fields (1 where sigma_j = -1).
- * Each stream is zero-padded to whole 32-bit words (W words per token).  In a
+ * j of width w occupies bits [j*w, (j+1)*w).  The index stream `idx` holds the
+ * bits of I_dir and I_nrm interleaved per triplet: n_tri fields of
+ * B_tri = 2*b_dir + b_nrm bits (the triplet budget of Sec. 3.3), field i being
+ *     xi_i | eta_i << b_dir | rho_i << (2*b_dir)
+ * (the triplet's two octahedral-coordinate indices, then its norm index).  The
+ * QJL stream holds d one-bit fields (1 where sigma_j = -1).  Each stream is
+ * zero-padded to whole 32-bit words (W words per token).  In a
  * (batch b, kv head h) plane of `capacity` tokens (a multiple of 64), word w
  * of token t is stored at word index
  *     ((b*kv_heads + h)*(capacity/64) + t/64)*W*64 + w*64 + t%64,
@@ -51,7 +54,7 @@
 extern "C" {
 #endif
 
-#define OCTO_ABI_VERSION 2u
+#define OCTO_ABI_VERSION 3u
 
 typedef enum {
   OCTO_OK = 0,
@@ -94,8 +97,7 @@ typedef struct {
 
 /* A packed cache for one tensor (K or V), layout OCTO_LAYOUT_TILE64.        */
 typedef struct {
-  uint32_t* dir;          /* B*H*capacity*W_dir words                          */
-  uint32_t* nrm;          /* B*H*capacity*W_nrm words (may be NULL if W_nrm=0) */
+  uint32_t* idx;          /* B*H*capacity*W_idx words                          */
   float* gamma;           /* B*H*capacity                                      */
   uint32_t* qjl;          /* B*H*capacity*W_qjl words, NULL unless codec.qjl   */
   uint16_t* gamma_r;      /* B*H*capacity fp16 bits, NULL unless codec.qjl     */
@@ -107,8 +109,7 @@ typedef struct {
 
 /* 32-bit words per token of each stream for a codec.                        */
 typedef struct {
-  int32_t dir_words;
-  int32_t nrm_words;
+  int32_t idx_words;      /* ceil(n_triplets * (2*b_dir + b_nrm) / 32)         */
   int32_t qjl_words;
   int32_t n_triplets;     /* ceil(d / 3)                                       */
   int32_t b_dir;          /* the resolved split                                */

@@ -2,8 +2,7 @@
 
 A cache for one tensor (K or V) of shape [B, H, capacity, d] is a dict of
 flat host arrays in the layout documented in oracle.pack:
-  "dir"    uint32, B*H*capacity*W_dir words (tile-64)
-  "nrm"    uint32, B*H*capacity*W_nrm words (tile-64)
+  "idx"    uint32, B*H*capacity*W_idx words (tile-64): the index stream
   "gamma"  float32, [B, H, capacity]
   "qjl"    uint32, B*H*capacity*W_sig words (tile-64)   (only with QJL)
   "gamma_r" uint16, [B, H, capacity] fp16 bit patterns  (only with QJL)
@@ -21,8 +20,7 @@ from .octahedral import oct_decode
 def stream_sizes(codec):
     nt = n_triplets(codec["d"])
     return {
-        "dir": pack.stream_words(2 * nt, codec["b_dir"]),
-        "nrm": pack.stream_words(nt, codec["b_nrm"]),
+        "idx": pack.stream_words(nt, 2 * codec["b_dir"] + codec["b_nrm"]),
         "qjl": pack.stream_words(codec["d"], 1) if codec.get("qjl") else 0,
     }
 
@@ -32,8 +30,7 @@ def empty_cache(codec, B, H, capacity):
         raise ValueError("capacity must be a multiple of 64")
     w = stream_sizes(codec)
     c = {
-        "dir": np.zeros(B * H * capacity * w["dir"], dtype=np.uint32),
-        "nrm": np.zeros(B * H * capacity * w["nrm"], dtype=np.uint32),
+        "idx": np.zeros(B * H * capacity * w["idx"], dtype=np.uint32),
         "gamma": np.zeros((B, H, capacity), dtype=np.float32),
         "B": B, "H": H, "capacity": capacity,
     }
@@ -54,16 +51,14 @@ def encode_into(cache, codec, x, token_offset=0):
                  rounding=codec.get("rounding", "local3x3"), qjl=codec.get("qjl", False))
     w = stream_sizes(codec)
     cap = cache["capacity"]
-    dirw = pack.pack_fields(pack.dir_fields(enc["i_xi"], enc["i_eta"]), codec["b_dir"])
-    nrmw = pack.pack_fields(enc["i_rho"], codec["b_nrm"])
+    idxw = pack.pack_fields(pack.triplet_fields(enc["i_xi"], enc["i_eta"], enc["i_rho"], codec["b_dir"]),
+                            2 * codec["b_dir"] + codec["b_nrm"])
     if codec.get("qjl"):
         sigw = pack.pack_fields(enc["sigma_neg"].astype(np.int64), 1)
     for b in range(B):
         for h in range(H):
             sl = slice((b * H + h) * T, (b * H + h + 1) * T)
-            pack.scatter_tokens(cache["dir"], dirw[sl].reshape(T, w["dir"]), b, h, token_offset, H, cap)
-            if w["nrm"]:
-                pack.scatter_tokens(cache["nrm"], nrmw[sl].reshape(T, w["nrm"]), b, h, token_offset, H, cap)
+            pack.scatter_tokens(cache["idx"], idxw[sl].reshape(T, w["idx"]), b, h, token_offset, H, cap)
             cache["gamma"][b, h, token_offset:token_offset + T] = enc["gamma_f32"][sl]
             if codec.get("qjl"):
                 pack.scatter_tokens(cache["qjl"], sigw[sl], b, h, token_offset, H, cap)
@@ -77,17 +72,13 @@ def read_tokens(cache, codec, b, h, t0, T):
     nt = n_triplets(codec["d"])
     w = stream_sizes(codec)
     H, cap = cache["H"], cache["capacity"]
-    dirw = pack.gather_tokens(cache["dir"], b, h, t0, T, H, cap, w["dir"])
-    f = pack.unpack_fields(dirw, 2 * nt, codec["b_dir"])
-    if w["nrm"]:
-        nrmw = pack.gather_tokens(cache["nrm"], b, h, t0, T, H, cap, w["nrm"])
-        i_rho = pack.unpack_fields(nrmw, nt, codec["b_nrm"])
-    else:
-        i_rho = np.zeros((T, nt), dtype=np.int64)
+    idxw = pack.gather_tokens(cache["idx"], b, h, t0, T, H, cap, w["idx"])
+    f = pack.unpack_fields(idxw, nt, 2 * codec["b_dir"] + codec["b_nrm"])
+    i_xi, i_eta, i_rho = pack.split_triplet_fields(f, codec["b_dir"], codec["b_nrm"])
     out = {
-        "i_xi": f[:, 0::2], "i_eta": f[:, 1::2], "i_rho": i_rho,
+        "i_xi": i_xi, "i_eta": i_eta, "i_rho": i_rho,
         "gamma": cache["gamma"][b, h, t0:t0 + T].astype(np.float64),
-        "dir_words": dirw,
+        "idx_words": idxw,
     }
     if codec.get("qjl"):
         sigw = pack.gather_tokens(cache["qjl"], b, h, t0, T, H, cap, w["qjl"])

@@ -9,8 +9,11 @@ code from its description:
 
   * A stream is a little-endian, LSB-first bit string: field j of width w
     occupies bits [j*w, (j+1)*w), bit p is bit (p % 8) of byte p // 8.
-  * I_dir holds 2*n_tri fields of b_dir bits in the order
-    xi_0, eta_0, xi_1, eta_1, ...; I_nrm holds n_tri fields of b_nrm bits.
+  * The index stream I holds one field per triplet, n_tri fields of
+    B_tri = 2 b_dir + b_nrm bits (the per-triplet budget of Sec. 3.3): field i
+    is xi_i | eta_i << b_dir | rho_i << 2 b_dir, i.e. the triplet's I_dir
+    pair followed by its I_nrm entry.  (I_dir and I_nrm are the same bits,
+    interleaved per triplet rather than kept as two streams.)
     The sigma stream holds d one-bit fields, 1 where sigma_j = -1.
   * Every stream is zero-padded to whole 32-bit words; W = words per token.
   * gamma is fp32 and gamma_r the fp16 bit pattern, each one value per token
@@ -59,13 +62,17 @@ def unpack_fields(words, n_fields, width):
     return out
 
 
-def dir_fields(i_xi, i_eta):
-    """Interleave to xi_0, eta_0, xi_1, eta_1, ... : [N, 2*n_tri]."""
-    n, nt = i_xi.shape
-    f = np.empty((n, 2 * nt), dtype=np.int64)
-    f[:, 0::2] = i_xi
-    f[:, 1::2] = i_eta
-    return f
+def triplet_fields(i_xi, i_eta, i_rho, b_dir):
+    """One B_tri-bit field per triplet: xi | eta << b_dir | rho << 2 b_dir."""
+    i_xi, i_eta, i_rho = (np.asarray(a, dtype=np.int64) for a in (i_xi, i_eta, i_rho))
+    return i_xi | (i_eta << b_dir) | (i_rho << (2 * b_dir))
+
+
+def split_triplet_fields(f, b_dir, b_nrm):
+    """Inverse of triplet_fields: (i_xi, i_eta, i_rho)."""
+    f = np.asarray(f, dtype=np.int64)
+    m = (1 << b_dir) - 1
+    return f & m, (f >> b_dir) & m, (f >> (2 * b_dir)) & ((1 << b_nrm) - 1)
 
 
 def tile_index(b, h, t, w, H, capacity, W):

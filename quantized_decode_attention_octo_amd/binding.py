@@ -22,7 +22,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liboctopus.so")
 CODEBOOKS = os.path.join(PKG, "codebooks", "octopus_d{d}.json")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 STATUS = ["OCTO_OK", "OCTO_ERR_INVALID_ARGUMENT", "OCTO_ERR_UNSUPPORTED", "OCTO_ERR_ALIGNMENT",
           "OCTO_ERR_CAPACITY", "OCTO_ERR_WORKSPACE_TOO_SMALL", "OCTO_ERR_VERSION", "OCTO_ERR_HIP"]
 DTYPE_F32, DTYPE_BF16 = 0, 1
@@ -45,14 +45,14 @@ class CodecDesc(ctypes.Structure):
 
 
 class CacheView(ctypes.Structure):
-    _fields_ = [("dir", ctypes.c_void_p), ("nrm", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+    _fields_ = [("idx", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
                 ("qjl", ctypes.c_void_p), ("gamma_r", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 class StreamSizes(ctypes.Structure):
-    _fields_ = [("dir_words", ctypes.c_int32), ("nrm_words", ctypes.c_int32),
+    _fields_ = [("idx_words", ctypes.c_int32),
                 ("qjl_words", ctypes.c_int32), ("n_triplets", ctypes.c_int32),
                 ("b_dir", ctypes.c_int32), ("b_nrm", ctypes.c_int32)]
 
@@ -148,25 +148,23 @@ class PackedCache:
         s = codec.sizes()
         n = B * H * capacity
         i32 = dict(dtype=torch.int32, device=device)
-        self.dir = torch.zeros(n * s.dir_words, **i32)
-        self.nrm = torch.zeros(max(1, n * s.nrm_words), **i32)
+        self.idx = torch.zeros(n * s.idx_words, **i32)
         self.gamma = torch.zeros(B, H, capacity, dtype=torch.float32, device=device)
         self.qjl = torch.zeros(n * s.qjl_words, **i32) if codec.qjl else None
         self.gamma_r = torch.zeros(B, H, capacity, dtype=torch.int16, device=device) if codec.qjl else None
         self.B, self.H, self.capacity, self.sizes = B, H, capacity, s
-        self.view = CacheView(self.dir.data_ptr(), self.nrm.data_ptr(), self.gamma.data_ptr(),
+        self.view = CacheView(self.idx.data_ptr(), self.gamma.data_ptr(),
                               self.qjl.data_ptr() if self.qjl is not None else None,
                               self.gamma_r.data_ptr() if self.gamma_r is not None else None,
                               B, H, capacity, LAYOUT_TILE64)
 
     def nbytes(self):
-        t = [self.dir, self.nrm, self.gamma, self.qjl, self.gamma_r]
+        t = [self.idx, self.gamma, self.qjl, self.gamma_r]
         return sum(x.numel() * x.element_size() for x in t if x is not None)
 
     def to_host(self):
         """Host copies of the streams (numpy) in the layout the oracle reads."""
-        out = {"dir": self.dir.cpu().numpy().view("<u4"),
-               "nrm": self.nrm.cpu().numpy().view("<u4"),
+        out = {"idx": self.idx.cpu().numpy().view("<u4"),
                "gamma": self.gamma.cpu().numpy(),
                "B": self.B, "H": self.H, "capacity": self.capacity}
         if self.qjl is not None:

@@ -80,8 +80,7 @@ octo_status resolve_codec(const octo_codec_desc* d, const char* what, Codec* out
   out->b_nrm = bn;
   out->K = 1 << bd;
   out->R = 1 << bn;
-  out->w_dir = words_for_bits(2 * kNTri * bd);
-  out->w_nrm = words_for_bits(kNTri * bn);
+  out->w_idx = words_for_bits(kNTri * (2 * bd + bn));
   out->w_qjl = d->qjl ? words_for_bits(kHeadDim) : 0;
   out->qjl = d->qjl;
   out->rounding = d->rounding;
@@ -100,11 +99,11 @@ octo_status check_cache(const octo_cache_view* v, const Codec& c, const char* wh
   if (v->capacity % 64)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: capacity %d is not a multiple of 64", what,
                 v->capacity);
-  if (!v->dir || !v->gamma || (c.w_nrm && !v->nrm))
+  if (!v->idx || !v->gamma)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: stream pointer is NULL", what);
   if (c.qjl && (!v->qjl || !v->gamma_r))
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: QJL codec needs qjl and gamma_r streams", what);
-  uintptr_t a = (uintptr_t)v->dir | (uintptr_t)v->nrm | (uintptr_t)v->gamma;
+  uintptr_t a = (uintptr_t)v->idx | (uintptr_t)v->gamma;
   if (c.qjl) a |= (uintptr_t)v->qjl;
   if (a & 15) return fail(OCTO_ERR_ALIGNMENT, "%s: streams must be 16-byte aligned", what);
   if (c.qjl && ((uintptr_t)v->gamma_r & 1))
@@ -146,8 +145,7 @@ octo_status octo_record_sizes(const octo_codec_desc* codec, octo_stream_sizes* o
   octo::Codec c;
   octo_status s = octo::resolve_codec(codec, "octo_record_sizes", &c, false);
   if (s != OCTO_OK) return s;
-  out->dir_words = c.w_dir;
-  out->nrm_words = c.w_nrm;
+  out->idx_words = c.w_idx;
   out->qjl_words = c.w_qjl;
   out->n_triplets = octo::kNTri;
   out->b_dir = c.b_dir;

@@ -120,15 +120,14 @@ __device__ inline float4 oct_dir(float xi, float eta) {
 // of a [out_rows][128] plane (16-byte chunks) or as columns t of a
 // [128][out_rows] plane (64 consecutive keys per row, at key_column).
 template <int BD, int BN, bool TRANSPOSED>
-__global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __restrict__ dir,
-                                                          const uint32_t* __restrict__ nrm,
+__global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __restrict__ idx,
                                                           const float* __restrict__ gamma,
                                                           const Codebook cb,
                                                           int capacity, int cached,
                                                           _Float16* __restrict__ out,
                                                           int out_rows) {
-  constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD;
-  constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32;
+  constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD, BT = FWD + BN;
+  constexpr int WI = (kNTri * BT + 31) / 32;
   constexpr int kRow = 136;                        // halves per token row in LDS
   __shared__ float4 lut[K * K];
   __shared__ float crho[R], cxi[K];
@@ -146,13 +145,12 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
     const int k = e & 63, i = e >> 6;
     const int t = t0 + k;
     if (k >= nt) continue;
-    const int dp = i * FWD, np = i * BN;
-    uint32_t lo = dir[tile_word(plane, capacity, t, dp >> 5, WD)];
-    uint32_t hi = ((dp & 31) + FWD > 32) ? dir[tile_word(plane, capacity, t, (dp >> 5) + 1, WD)] : 0u;
-    const uint32_t code = (uint32_t)((((uint64_t)hi << 32) | lo) >> (dp & 31)) & ((1u << FWD) - 1u);
-    lo = nrm[tile_word(plane, capacity, t, np >> 5, WN)];
-    hi = ((np & 31) + BN > 32) ? nrm[tile_word(plane, capacity, t, (np >> 5) + 1, WN)] : 0u;
-    const uint32_t ir = (uint32_t)((((uint64_t)hi << 32) | lo) >> (np & 31)) & ((1u << BN) - 1u);
+    // triplet field i: code pair | rho index << 2 b_dir
+    const int p = i * BT;
+    const uint32_t lo = idx[tile_word(plane, capacity, t, p >> 5, WI)];
+    const uint32_t hi = ((p & 31) + BT > 32) ? idx[tile_word(plane, capacity, t, (p >> 5) + 1, WI)] : 0u;
+    const uint32_t f = (uint32_t)((((uint64_t)hi << 32) | lo) >> (p & 31)) & ((1u << BT) - 1u);
+    const uint32_t code = f & ((1u << FWD) - 1u), ir = f >> FWD;
     const float s = crho[ir] * gamma[plane * capacity + t];
     const float4 n = lut[code];
     _Float16* dst = &tile[k * kRow + 3 * i];
@@ -429,11 +427,11 @@ void launch_decode_rows(const octo_cache_view* c, const Codec& cd, int cached, _
                         int out_rows, bool transposed, hipStream_t st) {
   dim3 grid((cached + 63) / 64, c->batch * c->kv_heads);
   if (transposed)
-    hipLaunchKernelGGL((decode_rows_kernel<BD, BN, true>), grid, dim3(256), 0, st, c->dir,
-                       c->nrm, c->gamma, cd.cb, c->capacity, cached, out, out_rows);
+    hipLaunchKernelGGL((decode_rows_kernel<BD, BN, true>), grid, dim3(256), 0, st, c->idx,
+                       c->gamma, cd.cb, c->capacity, cached, out, out_rows);
   else
-    hipLaunchKernelGGL((decode_rows_kernel<BD, BN, false>), grid, dim3(256), 0, st, c->dir,
-                       c->nrm, c->gamma, cd.cb, c->capacity, cached, out, out_rows);
+    hipLaunchKernelGGL((decode_rows_kernel<BD, BN, false>), grid, dim3(256), 0, st, c->idx,
+                       c->gamma, cd.cb, c->capacity, cached, out, out_rows);
 }
 
 bool decode_rows(const octo_cache_view* c, const Codec& cd, int cached, _Float16* out,

@@ -17,15 +17,17 @@
 //
 // Precision.  The operands are split as x = hi + lo with hi, lo in fp16
 // (hi = x rounded toward zero, lo = the fp32 residual rounded toward zero) and
-// every product is formed as hi*hi + hi*lo + lo*hi with fp32 accumulation,
-// about 2^-20 relative: single fp16 operands are not accurate enough for the
+// every product is formed as hi*hi + hi*lo + lo*hi (the key side with
+// pre-split tables also adds lo*lo) with fp32 accumulation, about 2^-20
+// relative: single fp16 operands are not accurate enough for the
 // peaked softmax that outlier channels produce.  u^ is scaled by 64 (exact)
 // so that the residuals stay in the fp16 normal range.
 //
 // Tables in LDS, built per workgroup from the codebooks.  The pre-split
 // table holds 64 rho^ n^ for every (norm index, code pair), already split
-// into fp16 hi/lo halves, so unpacking a triplet is two field extractions
-// and one LDS read.  Up to 1024 entries (b_dir <= 4 with b_nrm <= 2, or the
+// into fp16 hi/lo halves, at index rho K^2 + code pair, which is the
+// triplet's field of the index stream as it is stored: unpacking a triplet
+// is one field extraction and one LDS read.  Up to 1024 entries (b_dir <= 4 with b_nrm <= 2, or the
 // uniform (2,2), (3,3)) two workgroups share a CU, each with its K and V
 // tables; the 4-bit splits (5,3) and (4,4) take 4096 or 8192 entries, one
 // table for K and V when they share their codebooks, in one eight-wave
@@ -39,10 +41,12 @@
 // of one query head, which is the A-operand layout P needs in O = P V.
 // Key-side coordinates: lane group g = L / 16 of token row t owns the 11
 // consecutive triplets 11 g .. 11 g + 10 (10 for g = 3), so that it reads
-// only the few record words that cover them.  With pre-split tables, slot e
-// of call m (six calls) is component e % 4 of triplet 2 m + e / 4 (component
-// 3 a zero pad): two table entries are the hi and lo operands as they stand.
-// With fp32 tables, call (gi, c) slot e is component c of triplet 8 gi + e.
+// only the few record words that cover them.  With pre-split tables, call m
+// (eleven calls, two products each) takes triplet 11 g + m: slots 0-3 are
+// its hi components (x, y, z, 0), slots 4-7 its lo components, which is the
+// table entry as it stands, against the query's components repeated, hi in
+// one product and lo in the other.  With fp32 tables, call (gi, c) slot e is
+// component c of triplet 8 gi + e.
 // With QJL, call k, slot e = sign bit 32 g + 8 k + e, one word of the sign
 // record.
 // Value-side columns: tile (grp, c), column j = component c of triplet
@@ -90,7 +94,7 @@ struct DecodeArgs {
   Codebook kcb, vcb;   // C_xi, C_rho of K and of V
   int shared_tables;   // K and V use the same codebook values
   uint64_t kseed, vseed;
-  const uint32_t *kdir, *knrm, *kqjl, *vdir, *vnrm;
+  const uint32_t *k_idx, *kqjl, *v_idx;   // index streams, K sign stream
   const float *kgamma, *vgamma;
   const uint16_t* kgamma_r;
   int capacity;
@@ -205,58 +209,63 @@ constexpr int kIdxRows = 44;          // 43 triplets + the spare
 // triplets 22 (L / 32) .. + 21.
 template <int BD, int BN, bool QJL>
 struct BlockWords {
-  static constexpr int FWD = 2 * BD;
-  static constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32;
-  static constexpr int KWD = group_words(FWD), KWN = group_words(BN);
-  static constexpr int KVD = value_words(FWD), KVN = value_words(BN);
-  uint32_t dw[2][KWD], nw[2][KWN], sw[2];
-  uint32_t vd[KVD], vn[KVN];
+  static constexpr int BT = 2 * BD + BN;            // bits of one triplet field
+  static constexpr int WI = (kNTri * BT + 31) / 32;
+  static constexpr int KWI = group_words(BT), KVI = value_words(BT);
+  uint32_t iw[2][KWI], sw[2];
+  uint32_t vi[KVI];
   float4 gk[2], gv[2];
   uint2 gr[2];
 };
 
 // Issues every load of the block at t0 (a multiple of 32, below the
 // capacity, which is a multiple of 64, so that the 32 tokens share one
-// 64-token tile).  Words of one token are 256 bytes apart: one base address
-// per stream and immediate offsets; a group's window is clamped to the
-// record (the words past its end only ever feed bits above the last field).
+// 64-token tile) but the value norms.  Words of one token are 256 bytes
+// apart: one base address per stream and immediate offsets; a group's window
+// is clamped to the record (the words past its end only ever feed bits above
+// the last field).
 template <int BD, int BN, bool QJL>
 __device__ inline void load_block(BlockWords<BD, BN, QJL>& r, const DecodeArgs& a, size_t plane,
                                   int t0, int L) {
   using BW = BlockWords<BD, BN, QJL>;
-  constexpr int FWD = BW::FWD, WD = BW::WD, WN = BW::WN;
+  constexpr int BT = BW::BT, WI = BW::WI;
   const int col = L & 15, grp4 = L >> 4, w0 = L >> 5, tk = L & 31;
-  const int dwo = (kTriPerGroup * FWD * grp4) >> 5, nwo = (kTriPerGroup * BN * grp4) >> 5;
+  const int iwo = (kTriPerGroup * BT * grp4) >> 5;
   const size_t tile = plane * (size_t)(a.capacity >> 6) + (size_t)(t0 >> 6);
   const int tin = t0 & 63;
   const size_t gbase = plane * (size_t)a.capacity + (size_t)t0 + 4 * grp4;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const uint32_t* pd = a.kdir + tile * (WD * 64) + tin + 16 * kt + col;
-    const uint32_t* pn = a.knrm + tile * (WN * 64) + tin + 16 * kt + col;
+    const uint32_t* pi = a.k_idx + tile * (WI * 64) + tin + 16 * kt + col;
 #pragma unroll
-    for (int w = 0; w < BW::KWD; ++w) r.dw[kt][w] = pd[64 * min(dwo + w, WD - 1)];
-#pragma unroll
-    for (int w = 0; w < BW::KWN; ++w) r.nw[kt][w] = pn[64 * min(nwo + w, WN - 1)];
+    for (int w = 0; w < BW::KWI; ++w) r.iw[kt][w] = pi[64 * min(iwo + w, WI - 1)];
     if (QJL) r.sw[kt] = a.kqjl[tile * (4 * 64) + tin + 16 * kt + col + 64 * grp4];
     r.gk[kt] = *reinterpret_cast<const float4*>(a.kgamma + gbase + 16 * kt);
-    r.gv[kt] = *reinterpret_cast<const float4*>(a.vgamma + gbase + 16 * kt);
     if (QJL) r.gr[kt] = *reinterpret_cast<const uint2*>(a.kgamma_r + gbase + 16 * kt);
   }
-  const int vwo = (kValTri * FWD * w0) >> 5, vno = (kValTri * BN * w0) >> 5;
-  const uint32_t* pvd = a.vdir + tile * (WD * 64) + tin + tk;
-  const uint32_t* pvn = a.vnrm + tile * (WN * 64) + tin + tk;
+  const int vwo = (kValTri * BT * w0) >> 5;
+  const uint32_t* pvi = a.v_idx + tile * (WI * 64) + tin + tk;
 #pragma unroll
-  for (int w = 0; w < BW::KVD; ++w) r.vd[w] = pvd[64 * min(vwo + w, WD - 1)];
+  for (int w = 0; w < BW::KVI; ++w) r.vi[w] = pvi[64 * min(vwo + w, WI - 1)];
+}
+
+// The value norms of the block at t0, loaded apart from the rest: the
+// softmax still reads the current block's norms when the next block's
+// words are requested, and a separate load keeps the two sets from being
+// live at once (which costs register copies at the end of every iteration).
+template <int BD, int BN, bool QJL>
+__device__ inline void load_gv(BlockWords<BD, BN, QJL>& r, const DecodeArgs& a, size_t plane,
+                               int t0, int L) {
+  const size_t gbase = plane * (size_t)a.capacity + (size_t)t0 + 4 * (L >> 4);
 #pragma unroll
-  for (int w = 0; w < BW::KVN; ++w) r.vn[w] = pvn[64 * min(vno + w, WN - 1)];
+  for (int kt = 0; kt < 2; ++kt)
+    r.gv[kt] = *reinterpret_cast<const float4*>(a.vgamma + gbase + 16 * kt);
 }
 
 template <int BD, int BN, bool QJL, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * NW, kWaves = NW;
-  constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD;
-  constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32;
+  constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD, BT = FWD + BN;
   constexpr bool PRE = MODE == kPre;                // pre-split (code, rho) table
   constexpr bool BIG = K * K * R > kMaxSmallPre;    // one shared table, one WG per CU
   constexpr int kTab = PRE ? K * K * R : K * K;     // entries per table (16 B each)
@@ -274,48 +283,61 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   float* qs = reinterpret_cast<float*>(qbuf);
   __shared__ float red_ml[kWaves * kMaxG * 2];
 
-  const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, L = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = L & 15, grp4 = L >> 4;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
   const size_t plane = (size_t)b * a.Hkv + g;
+  // The big pre-split table serves K and V; small pre-split tables are
+  // built twice (V's own copy even when the codebooks agree), so that the V
+  // table sits at a constant offset that the LDS reads take as an
+  // immediate.  fp32 tables are shared when the codebooks agree.
   uint4* tabk = reinterpret_cast<uint4*>(smem);
-  uint4* tabv = a.shared_tables ? tabk : tabk + kTab;
+  uint4* tabv = PRE ? (BIG ? tabk : tabk + kTab) : (a.shared_tables ? tabk : tabk + kTab);
   float* red_o = reinterpret_cast<float*>(smem);          // [wave][head][128]
 
   // ---- every global load of the prologue goes out first, none waiting for
   // another: codebooks, q, the first block (speculatively: any t0 below the
   // capacity is in bounds, whatever seq_lens holds) and seq_lens.
+  // The codebooks are read at constant indices (scalar loads of the kernel
+  // arguments), so that their LDS stores wait on no vector load; q is kept
+  // as raw bits until the tables are built.
   float cx_k = 0.0f, cx_v = 0.0f, cr_k = 0.0f, cr_v = 0.0f;
-  if (tid < K) {
-    cx_k = a.kcb.xi[tid];
-    cx_v = a.vcb.xi[tid];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    cx_k = L == i ? a.kcb.xi[i] : cx_k;
+    cx_v = L == i ? a.vcb.xi[i] : cx_v;
   }
-  if (tid < R) {
-    cr_k = a.kcb.rho[tid];
-    cr_v = a.vcb.rho[tid];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    cr_k = L == i ? a.kcb.rho[i] : cr_k;
+    cr_v = L == i ? a.vcb.rho[i] : cr_v;
   }
   constexpr int kHeadsPerWave = kMaxG / kWaves;
-  float qv[kHeadsPerWave][2];
+  uint32_t qraw[kHeadsPerWave][2];                 // bf16 or fp32 bits
 #pragma unroll
   for (int k = 0; k < kHeadsPerWave; ++k) {
     const int hh = wave + kWaves * k;
-    qv[k][0] = qv[k][1] = 0.0f;
+    qraw[k][0] = qraw[k][1] = 0u;
     if (hh < G) {
       const size_t qo = ((size_t)b * a.Hq + (size_t)g * G + hh) * kHeadDim;
       if (a.q_bf16) {
-        qv[k][0] = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qo + L]);
-        qv[k][1] = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qo + L + 64]);
+        qraw[k][0] = static_cast<const uint16_t*>(a.q)[qo + L];
+        qraw[k][1] = static_cast<const uint16_t*>(a.q)[qo + L + 64];
       } else {
-        qv[k][0] = static_cast<const float*>(a.q)[qo + L];
-        qv[k][1] = static_cast<const float*>(a.q)[qo + L + 64];
+        qraw[k][0] = static_cast<const uint32_t*>(a.q)[qo + L];
+        qraw[k][1] = static_cast<const uint32_t*>(a.q)[qo + L + 64];
       }
     }
   }
   const int t_begin = split * a.split_len;
   int t0 = t_begin + wave * kBlock;
   BlockWords<BD, BN, QJL> blk;
-  if (!QJL && t0 < min(a.max_len, a.capacity)) load_block(blk, a, plane, t0, L);
+  if (!QJL && t0 < min(a.max_len, a.capacity)) {
+    load_block(blk, a, plane, t0, L);
+    load_gv(blk, a, plane, t0, L);
+  }
   int len = a.seq_lens[b];
   len = max(0, min(len, min(a.max_len, a.capacity)));
   // uniform: the loop and its prefetch test become scalar branches
@@ -330,8 +352,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     crk[tid] = cr_k;
     crv[tid] = cr_v;
   }
-  __syncthreads();
-  const int n_tables = a.shared_tables ? 1 : 2;
+  lds_barrier();
+  const int n_tables = PRE || !a.shared_tables ? 2 : 1;
   // pre-split tables are rho-major, entry rho_index K^2 + code pair, so that
   // consecutive lanes write consecutive entries
   constexpr int KK = K * K;
@@ -370,36 +392,53 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < kHeadsPerWave; ++k) {
     const int hh = wave + kWaves * k;
-    float q0 = qv[k][0] * s_lo, q1 = qv[k][1] * s_hi;
+    const int qsh = a.q_bf16 ? 16 : 0;
+    float q0 = __uint_as_float(qraw[k][0] << qsh) * s_lo;
+    float q1 = __uint_as_float(qraw[k][1] << qsh) * s_hi;
     if (wave + kWaves * k < G) wht128(q0, q1);
     qs[hh * 132 + L] = q0 * kInvSqrtD;
     qs[hh * 132 + L + 64] = q1 * kInvSqrtD;
   }
-  __syncthreads();
+  lds_barrier();
 
-  // Q^T operands (B), column col = head, six calls m.  Pre-split tables:
-  // slot e of call m = component e % 4 of the group's triplet 2 m + e / 4
-  // (component 3 is a zero pad), so a table entry {hx|hy, hz|0, lx|ly, lz|0}
-  // is, as it stands, half of an hi and half of an lo operand.  fp32 tables:
-  // call m = (gi, c) = (m / 3, m % 3), slot e = component c of triplet
-  // 8 gi + e.  Zero outside the group's triplets and the 128 coordinates.
-  half8 qh[6], ql[6];
+  // Q^T operands (B), column col = head.  Pre-split tables: eleven calls m,
+  // one per triplet 11 grp4 + m of the lane group; slot e = component e % 4
+  // of that triplet (component 3 a zero pad), the same four values twice, so
+  // that against the table entry {hi | lo} as it stands one call with the hi
+  // operand and one with the lo operand give (hi + lo)(qh + ql).  fp32
+  // tables: six calls m = (gi, c) = (m / 3, m % 3), slot e = component c of
+  // triplet 8 gi + e.  Zero outside the group's triplets and the 128
+  // coordinates.
+  half8 qh[PRE ? kTriPerGroup : 6], ql[PRE ? kTriPerGroup : 6];
+  if constexpr (PRE) {
 #pragma unroll
-  for (int m = 0; m < 6; ++m) {
-    float x[8];
+    for (int m = 0; m < kTriPerGroup; ++m) {
+      float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = PRE ? 2 * m + (e >> 2) : 8 * (m / 3) + e;
-      const int c = PRE ? e & 3 : m % 3;
-      const int coord = 3 * (kTriPerGroup * grp4 + j) + c;
-      x[e] = c < 3 && j < kTriPerGroup && coord < kHeadDim ? qs[col * 132 + coord] : 0.0f;
+      for (int e = 0; e < 8; ++e) {
+        const int c = e & 3;
+        const int coord = 3 * (kTriPerGroup * grp4 + m) + c;
+        x[e] = c < 3 && coord < kHeadDim ? qs[col * 132 + coord] : 0.0f;
+      }
+      split8(x, qh[m], ql[m]);
     }
-    split8(x, qh[m], ql[m]);
+  } else {
+#pragma unroll
+    for (int m = 0; m < 6; ++m) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 8 * (m / 3) + e, c = m % 3;
+        const int coord = 3 * (kTriPerGroup * grp4 + j) + c;
+        x[e] = j < kTriPerGroup && coord < kHeadDim ? qs[col * 132 + coord] : 0.0f;
+      }
+      split8(x, qh[m], ql[m]);
+    }
   }
   // QJL operands: call k, slot e of group grp4 = bit 32 grp4 + 8 k + e.
   half8 ph[QJL ? 4 : 1], pl[QJL ? 4 : 1];
   if (QJL) {
-    __syncthreads();
+    lds_barrier();
     for (int hh = wave; hh < kMaxG; hh += kWaves) {
       float p0 = qs[hh * 132 + L] * splitmix_sign(a.kseed, kHeadDim + L);
       float p1 = qs[hh * 132 + L + 64] * splitmix_sign(a.kseed, kHeadDim + L + 64);
@@ -408,7 +447,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
       qs[hh * 132 + L] = p0 * kInvSqrtD;
       qs[hh * 132 + L + 64] = p1 * kInvSqrtD;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int k = 0; k < (QJL ? 4 : 1); ++k) {
       float x[8];
@@ -432,55 +471,50 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   int vrow[3];
 #pragma unroll
   for (int i = 0; i < 3; ++i) vrow[i] = min(16 * i + col, kNTri - 1) * kIdxRow + 4 * grp4;
-  __syncthreads();                 // every wave is done with qs before it holds indices
+  lds_barrier();                 // every wave is done with qs before it holds indices
 
-  if (QJL && t0 < t_end) load_block(blk, a, plane, t0, L);   // (registers are short)
+  if (QJL && t0 < t_end) {                                   // (registers are short)
+    load_block(blk, a, plane, t0, L);
+    load_gv(blk, a, plane, t0, L);
+  }
   for (; t0 < t_end; t0 += kWaves * kBlock) {
-    // -- value-side table indices, code | rho index << 2 b_dir (the entry of a
-    //    pre-split table), into this wavefront's rows (the previous block's
+    // -- value-side triplet fields, code | rho index << 2 b_dir (the entry of
+    //    a pre-split table), into this wavefront's rows (the previous block's
     //    reads of them ended at the wave_sync closing its iteration)
     {
       using BW = BlockWords<BD, BN, QJL>;
       const int h = L >> 5, tk = L & 31;
-      const uint32_t dsh = (kValTri * FWD * h) & 31, nsh = (kValTri * BN * h) & 31;
-      uint32_t rd[BW::KVD], rn[BW::KVN];
+      const uint32_t ish = (kValTri * BT * h) & 31;
+      uint32_t ri[BW::KVI];
 #pragma unroll
-      for (int w = 0; w < BW::KVD; ++w)
-        rd[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KVD ? blk.vd[w + 1] : 0u, blk.vd[w], dsh);
-#pragma unroll
-      for (int w = 0; w < BW::KVN; ++w)
-        rn[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KVN ? blk.vn[w + 1] : 0u, blk.vn[w], nsh);
+      for (int w = 0; w < BW::KVI; ++w)
+        ri[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KVI ? blk.vi[w + 1] : 0u, blk.vi[w], ish);
       uint16_t* row = vidx + kValTri * h * kIdxRow + tk;
 #pragma unroll
-      for (int j = 0; j < kValTri; ++j)
-        row[j * kIdxRow] = (uint16_t)(field<FWD>(rd, j * FWD) | (field<BN>(rn, j * BN) << FWD));
+      for (int j = 0; j < kValTri; ++j) row[j * kIdxRow] = (uint16_t)field<BT>(ri, j * BT);
     }
     // -- scores, two 16-token tiles
     floatx4 sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      // shift the group's window so that its triplet j starts at bit j FWD
+      // shift the group's window so that its triplet j starts at bit j B_tri
       using BW = BlockWords<BD, BN, QJL>;
-      const uint32_t dsh = (kTriPerGroup * FWD * grp4) & 31, nsh = (kTriPerGroup * BN * grp4) & 31;
-      uint32_t dw[BW::KWD], nw[BW::KWN];
+      const uint32_t ish = (kTriPerGroup * BT * grp4) & 31;
+      uint32_t iw[BW::KWI];
 #pragma unroll
-      for (int w = 0; w < BW::KWD; ++w)
-        dw[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KWD ? blk.dw[kt][w + 1] : 0u, blk.dw[kt][w], dsh);
-#pragma unroll
-      for (int w = 0; w < BW::KWN; ++w)
-        nw[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KWN ? blk.nw[kt][w + 1] : 0u, blk.nw[kt][w], nsh);
+      for (int w = 0; w < BW::KWI; ++w)
+        iw[w] = __builtin_amdgcn_alignbit(w + 1 < BW::KWI ? blk.iw[kt][w + 1] : 0u, blk.iw[kt][w], ish);
       floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (PRE) {
+      if constexpr (PRE) {
 #pragma unroll
-        for (int m = 0; m < 6; ++m) {
-          // triplets 2 m and 2 m + 1 of the group (the twelfth is padding)
-          const int j0 = 2 * m, j1 = 2 * m + 1;
-          const uint4 E0 = tabk[field<FWD>(dw, j0 * FWD) + field<BN>(nw, j0 * BN) * KK];
-          const uint4 E1 = j1 < kTriPerGroup
-                               ? tabk[field<FWD>(dw, j1 * FWD) + field<BN>(nw, j1 * BN) * KK]
-                               : make_uint4(0u, 0u, 0u, 0u);
-          const u32x4 h = {E0.x, E0.y, E1.x, E1.y}, l = {E0.z, E0.w, E1.z, E1.w};
-          acc = mfma3(__builtin_bit_cast(half8, h), __builtin_bit_cast(half8, l), qh[m], ql[m], acc);
+        for (int m = 0; m < kTriPerGroup; ++m) {
+          // triplet m of the group: its field is the entry index
+          // rho K^2 + code pair, and the entry {hx|hy, hz|0, lx|ly, lz|0},
+          // one 16-byte read (random gathers conflict least in wide reads),
+          // is the A operand as it stands
+          const half8 A = __builtin_bit_cast(half8, tabk[field<BT>(iw, m * BT)]);
+          acc = mfma(A, ql[m], acc);
+          acc = mfma(A, qh[m], acc);
         }
       } else {
 #pragma unroll
@@ -494,8 +528,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
               ux[e] = uy[e] = uz[e] = 0.0f;
               continue;
             }
-            const uint4 n = tabk[field<FWD>(dw, j * FWD)];
-            const float rho = crk[field<BN>(nw, j * BN)];
+            const uint32_t f = field<BT>(iw, j * BT);
+            const uint4 n = tabk[f & (KK - 1)];
+            const float rho = crk[f >> FWD];
             ux[e] = rho * __uint_as_float(n.x);
             uy[e] = rho * __uint_as_float(n.y);
             uz[e] = rho * __uint_as_float(n.z);
@@ -544,10 +579,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
       }
     }
     // -- the key words are consumed: the next block's loads go out now and
-    //    land while this block's softmax and values are computed
-    //    (with QJL the registers are short: the loads go out after the values)
-    const float4 gv4[2] = {blk.gv[0], blk.gv[1]};
-    if (!QJL && t0 + kWaves * kBlock < t_end) load_block(blk, a, plane, t0 + kWaves * kBlock, L);
+    //    land while this block's softmax and values are computed (the value
+    //    norms once the softmax has read them; with QJL the registers are
+    //    short: the loads go out after the values)
+    //    Past the end of the split the current block is requested again (it
+    //    is in cache): unconditional loads write the block's registers in
+    //    place, where loads under a branch leave copies at the loop's end
+    //    that wait for every outstanding load.
+    const int t_next = t0 + kWaves * kBlock < t_end ? t0 + kWaves * kBlock : t0;
+    if (!QJL) load_block(blk, a, plane, t_next, L);
     // -- online softmax over the 32 tokens, head col (Sec. 3.6 / App. A)
     float mx = -INFINITY;
 #pragma unroll
@@ -560,13 +600,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     float pw[8], psum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const float gva[4] = {gv4[kt].x, gv4[kt].y, gv4[kt].z, gv4[kt].w};
+      const float gva[4] = {blk.gv[kt].x, blk.gv[kt].y, blk.gv[kt].z, blk.gv[kt].w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = sc[kt][r] == -INFINITY ? 0.0f : __expf(sc[kt][r] - m_new);
         psum += p;
         pw[4 * kt + r] = p * gva[r];
       }
+    }
+    if (!QJL) {
+      // the weights are computed: the current norms are dead.  The empty asm
+      // keeps the scheduler from hoisting the next norms' load above them.
+      int tg = t_next;
+      asm volatile("" : "+s"(tg) : "v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]), "v"(pw[4]),
+                   "v"(pw[5]), "v"(pw[6]), "v"(pw[7]));
+      load_gv(blk, a, plane, tg, L);
     }
     psum = rows_sum(psum);
     l_run = l_run * alpha + psum;
@@ -619,13 +667,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < 3; ++c) o[i][c] = mfma3(pah, pal, bh[c], bl[c], o[i][c]);
     }
-    if (QJL && t0 + kWaves * kBlock < t_end) load_block(blk, a, plane, t0 + kWaves * kBlock, L);
+    if (QJL) {
+      load_block(blk, a, plane, t_next, L);
+      load_gv(blk, a, plane, t_next, L);
+    }
     wave_sync();
   }
 
   // ---- merge the waves: partial (m, l, O) of this split.  The tables are
   // dead now; their LDS holds the per-wave value sums.
-  __syncthreads();
+  lds_barrier();
   if (grp4 == 0 && col < G) {
     red_ml[(wave * kMaxG + col) * 2] = m_run;
     red_ml[(wave * kMaxG + col) * 2 + 1] = l_run;
@@ -640,7 +691,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
         for (int r = 0; r < 4; ++r) red_o[(wave * kMaxG + 4 * grp4 + r) * kHeadDim + coord] = o[i][c][r];
       }
     }
-  __syncthreads();
+  lds_barrier();
   for (int e = tid; e < G * kHeadDim; e += kThreads) {
     const int h = e >> 7, c = e & 127;
     float M = -INFINITY;
@@ -884,13 +935,11 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
   a.shared_tables = shared;
   a.kseed = kc.seed;
   a.vseed = vc.seed;
-  a.kdir = k_cache->dir;
-  a.knrm = k_cache->nrm;
+  a.k_idx = k_cache->idx;
   a.kqjl = k_cache->qjl;
   a.kgamma = k_cache->gamma;
   a.kgamma_r = k_cache->gamma_r;
-  a.vdir = v_cache->dir;
-  a.vnrm = v_cache->nrm;
+  a.v_idx = v_cache->idx;
   a.vgamma = v_cache->gamma;
   a.capacity = k_cache->capacity;
   a.n_split = p.n_split;

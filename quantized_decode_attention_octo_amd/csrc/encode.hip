@@ -15,8 +15,9 @@
 //                 rho = ||t||;
 //   Sec. 3.6      with QJL: r = u - u^, sigma = sign(H diag(s') r) and
 //                 gamma_r = fp16(||r||);
-//   Sec. 3        the packed index streams I_dir, I_nrm, assembled in
-//                 registers at constant bit offsets.
+//   Sec. 3        the indices of I_dir and I_nrm, packed in registers at
+//                 constant bit offsets as one field per triplet
+//                 (xi | eta << b_dir | rho << 2 b_dir, B_tri bits).
 // A workgroup of 256 lanes takes 256 consecutive tokens of one (batch, head)
 // plane; in the tile-64 layout word w of 64 consecutive tokens is 256
 // contiguous bytes, so every word store of a wavefront is one coalesced
@@ -45,8 +46,7 @@ struct EncodeArgs {
   Codebook cb;                    // C_xi, C_rho values
   uint64_t seed;
   int qjl, rounding;
-  uint32_t* dir;
-  uint32_t* nrm;
+  uint32_t* idx;                  // index stream, one B_tri-bit field per triplet
   float* gamma;
   uint32_t* qjl_bits;
   uint16_t* gamma_r;
@@ -141,7 +141,8 @@ template <int BD, int BN>
 __global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
   constexpr int K = 1 << BD, R = 1 << BN;
   constexpr int FWD = 2 * BD;                         // xi | eta << BD
-  constexpr int WD = (kNTri * FWD + 31) / 32, WN = (kNTri * BN + 31) / 32;
+  constexpr int BT = FWD + BN;                        // + rho << 2 BD: one field per triplet
+  constexpr int WI = (kNTri * BT + 31) / 32;
 
   constexpr int KP = K + 2;                           // padded side of the direction table
   // Direction table, padded by one cell on every side: entry (i, j), i, j in
@@ -264,11 +265,9 @@ __global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
   }
 
   // ---- triplets: octahedral map, seeds, joint rounding, packing
-  uint32_t dw[WD + 1], nw[WN + 1];
+  uint32_t iw[WI + 1];
 #pragma unroll
-  for (int w = 0; w <= WD; ++w) dw[w] = 0u;
-#pragma unroll
-  for (int w = 0; w <= WN; ++w) nw[w] = 0u;
+  for (int w = 0; w <= WI; ++w) iw[w] = 0u;
   const bool scalar = a.rounding == OCTO_ROUND_SCALAR;     // kernel argument: uniform
   StaticFor<0, kNTri>::run([&](auto ic) {
     constexpr int i = decltype(ic)::value;
@@ -320,16 +319,12 @@ __global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
         }
       ir = rho_index<R>(mr, best);
     }
-    // pack at constant bit offsets (LSB-first streams)
+    // pack the triplet's field at its constant bit offset (LSB-first stream)
     {
-      constexpr int pos = i * FWD, w = pos >> 5, sh = pos & 31;
-      dw[w] |= code << sh;
-      if (sh + FWD > 32) dw[w + 1] |= code >> ((32 - sh) & 31);
-    }
-    {
-      constexpr int pos = i * BN, w = pos >> 5, sh = pos & 31;
-      nw[w] |= (uint32_t)ir << sh;
-      if (sh + BN > 32) nw[w + 1] |= (uint32_t)ir >> ((32 - sh) & 31);
+      constexpr int pos = i * BT, w = pos >> 5, sh = pos & 31;
+      const uint32_t f = code | ((uint32_t)ir << FWD);
+      iw[w] |= f << sh;
+      if (sh + BT > 32) iw[w + 1] |= f >> ((32 - sh) & 31);
     }
     if (a.qjl) {
       // rotated-frame residual r = u - u^ (Sec. 3.6), over the real coordinates
@@ -349,9 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
   const int tc = a.token_offset + t;
   if (valid) {
 #pragma unroll
-    for (int w = 0; w < WD; ++w) a.dir[tile_word(plane, a.capacity, tc, w, WD)] = dw[w];
-#pragma unroll
-    for (int w = 0; w < WN; ++w) a.nrm[tile_word(plane, a.capacity, tc, w, WN)] = nw[w];
+    for (int w = 0; w < WI; ++w) a.idx[tile_word(plane, a.capacity, tc, w, WI)] = iw[w];
     a.gamma[plane * a.capacity + tc] = gamma;
   }
 
@@ -430,8 +423,7 @@ extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, 
   a.seed = c.seed;
   a.qjl = c.qjl;
   a.rounding = c.rounding;
-  a.dir = dst->dir;
-  a.nrm = dst->nrm;
+  a.idx = dst->idx;
   a.gamma = dst->gamma;
   a.qjl_bits = dst->qjl;
   a.gamma_r = dst->gamma_r;

@@ -38,7 +38,7 @@ struct Codec {
   int b_dir, b_nrm;     // bits per octahedral coordinate / per triplet norm
   int K;                // 2^b_dir entries of C_xi
   int R;                // 2^b_nrm entries of C_rho
-  int w_dir, w_nrm, w_qjl;  // 32-bit words per token of each stream
+  int w_idx, w_qjl;     // 32-bit words per token of each stream
   int qjl;
   int rounding;
   uint64_t seed;
@@ -123,6 +123,15 @@ __device__ inline float wave_max(float v) {
 
 // bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits.
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS
+// operations but leaves its global loads in flight (a full __syncthreads
+// also waits for every outstanding global load).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Field of WIDTH bits at bit offset POS of a little-endian LSB-first stream
 // held in registers (POS and WIDTH become constants after unrolling).

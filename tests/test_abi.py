@@ -56,26 +56,25 @@ def desc(bits=3, b_dir=0, b_nrm=0, qjl=0, head_dim=128, version=ob.ABI_VERSION, 
     return ob.CodecDesc(version, head_dim, bits, b_dir, b_nrm, rounding, qjl, 0, 0, p, p)
 
 
-# bytes per token of each stream with words padded to 4 B (dir, nrm) and the
-# QJL sketch of d = 128 bits
-@pytest.mark.parametrize("bits,bd,bn,dir_w,nrm_w", [
-    (4, 5, 3, 14, 5), (3, 4, 2, 11, 3), (2, 3, 1, 9, 2),
-    (4, 4, 4, 11, 6), (3, 3, 3, 9, 5), (2, 2, 2, 6, 3)])
-def test_record_sizes(L, bits, bd, bn, dir_w, nrm_w):
+# words per token of the index stream (43 fields of 2 b_dir + b_nrm bits,
+# padded to whole words) and of the QJL sketch of d = 128 bits
+@pytest.mark.parametrize("bits,bd,bn,idx_w", [
+    (4, 5, 3, 18), (3, 4, 2, 14), (2, 3, 1, 10),
+    (4, 4, 4, 17), (3, 3, 3, 13), (2, 2, 2, 9)])
+def test_record_sizes(L, bits, bd, bn, idx_w):
     explicit = (bd, bn) != (bits + 1, bits - 1)
     d = desc(bits, bd if explicit else 0, bn if explicit else 0, qjl=1, tables=False)
     s = ob.octo_record_sizes(d)
     assert (s.b_dir, s.b_nrm, s.n_triplets) == (bd, bn, 43)
-    assert s.dir_words == dir_w == -(-(2 * 43 * bd) // 32)
-    assert s.nrm_words == nrm_w == -(-(43 * bn) // 32)
+    assert s.idx_words == idx_w == -(-(43 * (2 * bd + bn)) // 32)
     assert s.qjl_words == 4
 
 
 def test_record_bytes_of_default_splits(L):
-    # K record = dir + nrm + gamma: 80 / 60 / 48 bytes at b = 4 / 3 / 2
-    for bits, nbytes in ((4, 80), (3, 60), (2, 48)):
+    # K record = index stream + gamma: 76 / 60 / 44 bytes at b = 4 / 3 / 2
+    for bits, nbytes in ((4, 76), (3, 60), (2, 44)):
         s = ob.octo_record_sizes(desc(bits, tables=False))
-        assert 4 * (s.dir_words + s.nrm_words + 1) == nbytes
+        assert 4 * (s.idx_words + 1) == nbytes
 
 
 def test_codec_errors(L):
@@ -95,7 +94,7 @@ def test_codec_errors(L):
 
 def view(B=1, H=1, cap=128, ptr=4096, layout=0, qjl=False):
     q = ptr if qjl else None
-    return ob.CacheView(ptr, ptr, ptr, q, q, B, H, cap, layout)
+    return ob.CacheView(ptr, ptr, q, q, B, H, cap, layout)
 
 
 def enc(L, d, x, B, H, T, v, off, strides=(128 * 256, 128 * 256, 128, 1), dt=1):

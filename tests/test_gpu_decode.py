@@ -65,7 +65,7 @@ def _plane(h, b, g):
     n = h["B"] * h["H"]
     p = b * h["H"] + g
     out = {"B": 1, "H": 1, "capacity": h["capacity"],
-           "dir": h["dir"].reshape(n, -1)[p], "nrm": h["nrm"].reshape(n, -1)[p],
+           "idx": h["idx"].reshape(n, -1)[p],
            "gamma": h["gamma"][b:b + 1, g:g + 1]}
     if "qjl" in h:
         out["qjl"] = h["qjl"].reshape(n, -1)[p]

@@ -117,5 +117,5 @@ def test_encode_deterministic():
     gc, _ = codecs(4)
     a = encode_gpu(inp["K"], gc).to_host()
     b = encode_gpu(inp["K"], gc).to_host()
-    for k in ("dir", "nrm", "gamma"):
+    for k in ("idx", "gamma"):
         assert np.array_equal(a[k], b[k])

@@ -3,7 +3,9 @@
   * pack/unpack are inverse for every field width used (1..6 bits);
   * explicit bit positions of hand-made fields (LSB-first, little-endian);
   * padding bits are zero; words per token match the record-size table
-    (I_dir 86 fields, I_nrm 43 fields, QJL 128 one-bit fields at d = 128);
+    (43 triplet fields of 2 b_dir + b_nrm bits, QJL 128 one-bit fields at
+    d = 128); a triplet field splits back into (xi, eta, rho) and holds the
+    same bits as the I_dir pair followed by the I_nrm entry;
   * the tile-64 word index formula, scatter/gather round trip, and an
     encode -> cache -> read round trip of the indices.
 """
@@ -39,13 +41,39 @@ def test_explicit_bits_and_padding():
 
 
 def test_record_sizes():
-    table = {4: (14, 5), 3: (11, 3), 2: (9, 2)}
-    for b, (wd, wn) in table.items():
-        s = C.stream_sizes(codec(b))
-        assert (s["dir"], s["nrm"]) == (wd, wn)
+    # words per token: ceil(43 * (2 b_dir + b_nrm) / 32) for the splits 4 -> (5,3), 3 -> (4,2), 2 -> (3,1)
+    table = {4: 18, 3: 14, 2: 10}
+    for b, w in table.items():
+        assert C.stream_sizes(codec(b))["idx"] == w
+        bd, bn = codec(b)["b_dir"], codec(b)["b_nrm"]
+        assert w == -(-43 * (2 * bd + bn) // 32)
     assert C.stream_sizes(codec(2, qjl=True))["qjl"] == 4
     # bytes per token: K and V records incl. fp32 gamma
-    assert 4 * (14 + 5 + 1) == 80 and 4 * (11 + 3 + 1) == 60 and 4 * (9 + 2 + 1) == 48
+    assert 4 * (18 + 1) == 76 and 4 * (14 + 1) == 60 and 4 * (10 + 1) == 44
+
+
+def test_triplet_fields():
+    rng = np.random.default_rng(3)
+    for bd, bn in [(5, 3), (4, 2), (3, 1), (4, 4), (2, 2), (6, 0)]:
+        xi = rng.integers(0, 2 ** bd, size=(5, 43))
+        eta = rng.integers(0, 2 ** bd, size=(5, 43))
+        rho = rng.integers(0, 2 ** bn, size=(5, 43)) if bn else np.zeros((5, 43), dtype=np.int64)
+        f = P.triplet_fields(xi, eta, rho, bd)
+        assert f.max() < 2 ** (2 * bd + bn)
+        a, b, c = P.split_triplet_fields(f, bd, bn)
+        assert np.array_equal(a, xi) and np.array_equal(b, eta) and np.array_equal(c, rho)
+        # the packed field stream carries, triplet by triplet, the xi, eta (b_dir bits each)
+        # and rho (b_nrm bits) fields in that order: bit p of the stream is the same bit
+        # of the interleaved b_dir/b_dir/b_nrm sequence
+        words = P.pack_fields(f, 2 * bd + bn)
+        bits = []
+        for i in range(43):
+            for v, w in ((xi[0, i], bd), (eta[0, i], bd), (rho[0, i], bn)):
+                bits += [(int(v) >> k) & 1 for k in range(w)]
+        stream = [(int(words[0, p // 32]) >> (p % 32)) & 1 for p in range(len(bits))]
+        assert stream == bits
+    # explicit: xi = 1, eta = 2, rho = 3 at (b_dir, b_nrm) = (3, 2) -> 1 | 2 << 3 | 3 << 6
+    assert int(P.triplet_fields([[1]], [[2]], [[3]], 3)[0, 0]) == 1 | (2 << 3) | (3 << 6)
 
 
 def test_tile_index_and_scatter_gather():
