@@ -67,6 +67,26 @@ def encode_into(cache, codec, x, token_offset=0):
             for k, v in enc.items()}
 
 
+def encode_at(cache, codec, x, b, h, token_offset):
+    """Encode x[T, d] into tokens [token_offset, token_offset+T) of plane (b, h)
+    alone (the other planes are untouched).  Returns the encoder outputs."""
+    x = np.asarray(x, dtype=np.float64)
+    T, d = x.shape
+    enc = encode(x, codec["c_xi"], codec["c_rho"], codec["seed"],
+                 rounding=codec.get("rounding", "local3x3"), qjl=codec.get("qjl", False))
+    w = stream_sizes(codec)
+    H, cap = cache["H"], cache["capacity"]
+    idxw = pack.pack_fields(pack.triplet_fields(enc["i_xi"], enc["i_eta"], enc["i_rho"], codec["b_dir"]),
+                            2 * codec["b_dir"] + codec["b_nrm"])
+    pack.scatter_tokens(cache["idx"], idxw.reshape(T, w["idx"]), b, h, token_offset, H, cap)
+    cache["gamma"][b, h, token_offset:token_offset + T] = enc["gamma_f32"]
+    if codec.get("qjl"):
+        sigw = pack.pack_fields(enc["sigma_neg"].astype(np.int64), 1)
+        pack.scatter_tokens(cache["qjl"], sigw, b, h, token_offset, H, cap)
+        cache["gamma_r"][b, h, token_offset:token_offset + T] = enc["gamma_r_f16"].view(np.uint16)
+    return enc
+
+
 def read_tokens(cache, codec, b, h, t0, T):
     """Indices and side data of tokens [t0, t0+T) of plane (b, h)."""
     nt = n_triplets(codec["d"])
