@@ -289,6 +289,83 @@ def run_decode(w, steps, warmup):
     return res, (inp, kc, vc, kcache, vcache)
 
 
+def run_step(w, steps, warmup):
+    """Decode steps with a residual window: the packed prefix holds tokens
+    [0, T - W + 1), the rings the last W - 1 tokens, and every step appends a
+    token from the pool, attends over T + 1 + s tokens and encodes the token
+    leaving the window."""
+    if warmup + steps > 1024:
+        raise SystemExit("the decode-step workload keeps room for 1024 steps")
+    inp = make_inputs(w)
+    kc = octo.Codec(bits=w.bits, qjl=w.qjl)
+    vc = octo.Codec(bits=w.bits)
+    W, T = w.window, w.T
+    P0 = T - W + 1
+    K, V = inp["K"].cuda(), inp["V"].cuda()
+    cap = w.capacity
+    kcache = octo.PackedCache(kc, w.B, w.Hkv, cap)
+    vcache = octo.PackedCache(vc, w.B, w.Hkv, cap)
+    octo.octo_encode(kc, K[:, :, :P0].contiguous(), kcache)
+    octo.octo_encode(vc, V[:, :, :P0].contiguous(), vcache)
+    kr = torch.zeros(w.B, w.Hkv, W, w.d, dtype=torch.bfloat16, device="cuda")
+    vr = torch.zeros_like(kr)
+    for j in range(P0, T):
+        kr[:, :, j % W] = K[:, :, j]
+        vr[:, :, j % W] = V[:, :, j]
+    plens = torch.full((w.B,), P0, dtype=torch.int32, device="cuda")
+    wlens = torch.full((w.B,), W - 1, dtype=torch.int32, device="cuda")
+    q = inp["q"].cuda()
+    kn, vn = inp["K_new"].cuda(), inp["V_new"].cuda()
+    new = [(kn[:, :, i].contiguous(), vn[:, :, i].contiguous()) for i in range(kn.shape[2])]
+    ws = octo.workspace(octo.octo_decode_step_workspace_bytes(kc, w.B, w.Hq, w.Hkv, cap), "cuda")
+    out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    t_att = Timer()
+    count = [0]
+
+    def step(timed):
+        k1, v1 = new[count[0] % len(new)]
+        e0 = t_att.start() if timed else None
+        octo.octo_decode_step(kc, vc, kcache, vcache, q, k1, v1, kr, vr, plens, wlens, cap,
+                              out=out, ws=ws)
+        if timed:
+            t_att.stop(e0)
+        count[0] += 1
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    att_ms = t_att.mean_ms()
+    # tokens attended per step: P + W = T + 1 + s at step s (every step evicts)
+    tokens = w.B * (T + 1 + warmup + (steps - 1) / 2.0)
+    packed = w.B * w.Hkv * (tokens / w.B - W) * (packed_bytes_per_token(kc) + packed_bytes_per_token(vc))
+    native = w.B * w.Hkv * (W * 2 * w.d * 2 + 2 * w.d * 2)      # window rows read, new rows written
+    enc = w.B * w.Hkv * (2 * w.d * 2 + packed_bytes_per_token(kc) + packed_bytes_per_token(vc))
+    step_bytes = packed + native + enc
+    achieved = step_bytes / (att_ms * 1e-3) / 1e9
+    res = {
+        "value": tokens / (att_ms * 1e-3),
+        "unit": "cached KV-tokens/s",
+        "ms_per_step": wall / steps * 1e3,
+        "dtype": "f32",
+        "attention_us": att_ms * 1e3,
+        "attention_us_percentiles": t_att.percentiles_us(),
+        "encode_us": None,
+        "encode_tokens_per_s": None,
+        "token_kv_heads_per_s": tokens * w.Hkv / (att_ms * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.key),
+                     "kernel": "octo_decode_step (split-K scan with the window workgroup + merge)",
+                     "algorithmic_bytes_per_launch": step_bytes},
+    }
+    state = (inp, kc, vc, kcache, vcache, kr, vr, plens, wlens, new)
+    return res, state
+
+
 def run_chunk(w, steps, warmup):
     inp = make_inputs(w)
     kc = octo.Codec(bits=w.bits)
@@ -368,7 +445,7 @@ def cpu_baseline(w, state):
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import attention as oatt
     from oracle_codecs import codec as oracle_codec
-    inp, kc, vc, kcache, vcache = state
+    inp, kc, vc, kcache, vcache = state[:5]
     hk = oracle_codec(bits=w.bits, qjl=w.qjl)
     hv = oracle_codec(bits=w.bits)
     hkc, hvc = kcache.to_host(), vcache.to_host()
@@ -377,7 +454,34 @@ def cpu_baseline(w, state):
     with threadpool_limits(limits=1):
         torch.set_num_threads(1)
         done, dt, units = 0.0, 0.0, 0
-        if not w.chunk_q:
+        if w.window:
+            # one oracle decode step per (batch, KV head) plane, in order and
+            # repeated, from the state the GPU steps left; a plane-step counts
+            # (P + n + 1) / Hkv of a step's cached KV-tokens
+            from oracle import step as ostep
+            _, _, _, _, _, kr, vr, plens, wlens, new = state
+            kr_h, vr_h = kr.double().cpu().numpy(), vr.double().cpu().numpy()
+            P, n = plens.cpu().numpy(), wlens.cpu().numpy()
+            planes = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+            while dt < CPU_SECONDS:
+                b, g = planes[units % len(planes)]
+                st = {"k": _host_plane(hkc, b, g), "v": _host_plane(hvc, b, g),
+                      "k_ring": kr_h[b:b + 1, g:g + 1].copy(), "v_ring": vr_h[b:b + 1, g:g + 1].copy(),
+                      "P": P[b:b + 1].astype(np.int64), "n": n[b:b + 1].astype(np.int64),
+                      "W": w.window}
+                k1, v1 = new[units % len(new)]
+                qn = inp["q"][b:b + 1, g * G:(g + 1) * G].double().numpy()
+                t0 = time.perf_counter()
+                ostep.decode_step(st, qn, k1[b:b + 1, g:g + 1].double().cpu().numpy(),
+                                  v1[b:b + 1, g:g + 1].double().cpu().numpy(), hk, hv)
+                dt += time.perf_counter() - t0
+                done += (int(P[b]) + int(n[b]) + 1) / w.Hkv
+                units += 1
+            value = done / dt
+            sample = (f"{units} oracle decode steps, one (batch, KV head) plane each ({len(planes)} "
+                      f"in all, in order and repeated), {G} query heads over the packed prefix and "
+                      f"the window; each counts (P + n + 1) / {w.Hkv} cached KV-tokens")
+        elif not w.chunk_q:
             # (batch, KV head) planes in order, repeated if the workload is
             # smaller than the budget; a plane of sequence b is len_b / Hkv of
             # the step's cached KV-tokens
@@ -454,9 +558,12 @@ def main():
     log(f"bench {a.workload}: {w.name}; warmup {a.warmup}, steps {a.steps}")
     if w.chunk_q:
         res, state = run_chunk(w, a.steps, a.warmup)
+    elif w.window:
+        res, state = run_step(w, a.steps, a.warmup)
     else:
         res, state = run_decode(w, a.steps, a.warmup)
-    log(f"attention {res['attention_us']:.1f} us, encode {res['encode_us']:.1f} us")
+    enc = "" if res["encode_us"] is None else f", encode {res['encode_us']:.1f} us"
+    log(f"attention {res['attention_us']:.1f} us{enc}")
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(w, state)
@@ -468,7 +575,7 @@ def main():
         "dtype": res["dtype"], "data": "synthetic (seeded Gaussian, see workloads.py)",
         "config": {"workload": f"{a.workload}: {w.name}", "batch": w.B, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.d, "context": w.T, "bits": w.bits,
-                   "qjl": w.qjl, "chunk_queries": w.chunk_q},
+                   "qjl": w.qjl, "chunk_queries": w.chunk_q, "window": w.window},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "attention_us": res["attention_us"], "encode_us": res["encode_us"],

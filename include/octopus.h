@@ -174,6 +174,53 @@ octo_status octo_attend_decode(const octo_codec_desc* k_codec, const octo_codec_
                                float softmax_scale, float* out,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes needed by octo_decode_step for these shapes.              */
+octo_status octo_decode_step_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
+                                             int32_t num_q_heads, int32_t kv_heads,
+                                             int32_t max_packed_len, size_t* bytes);
+
+/* octo_decode_step -- one decode step with a residual window of native-
+ * precision tokens beside the packed cache (the OCTOPUS paper's experiments
+ * keep the most recent tokens at native precision, Sec. 4 "default recipe";
+ * Sec. 4.2 uses 32).  The paper gives no mechanism; this call's:
+ *   State of sequence b: the packed caches hold tokens [0, P_b), the rings
+ *   hold tokens [P_b, P_b + n_b), n_b < window, token j in ring slot
+ *   j mod window.  P_b = packed_lens[b], n_b = window_lens[b].
+ *   1. k_new[b], v_new[b] become token t = P_b + n_b, written to ring slot
+ *      t mod window;
+ *   2. out[b, h] = softmax attention of q[b, h] over the packed tokens
+ *      [0, P_b) (as octo_attend_decode, QJL term included) and the native
+ *      rows of tokens P_b .. t, in one softmax (fp32 over the native rows);
+ *   3. if n_b + 1 == window, token P_b is encoded from its ring row into
+ *      packed slot P_b of k_cache and v_cache (as octo_encode would) and
+ *      P_b += 1; otherwise n_b += 1.  packed_lens and window_lens are
+ *      updated on the device by the call's second kernel.
+ * So the attention always sees the last min(window, t + 1) tokens at native
+ * precision, and a token is compressed when it leaves the window.
+ *   q           device [B, num_q_heads, d], fp32 or bf16.
+ *   k_new, v_new  device bf16 [B, kv_heads, d].
+ *   k_window, v_window  device bf16 rings [B, kv_heads, window, d], owned
+ *               by the caller, read and written.
+ *   window      1 .. 64.
+ *   packed_lens, window_lens  device int32 [B], read and updated in place.
+ *   max_packed_len  host bound: every P_b <= max_packed_len <= capacity
+ *               (the split plan is sized by it; larger P_b are clamped).
+ *   workspace   device, >= octo_decode_step_workspace_bytes(...), 256-byte
+ *               aligned.
+ * Device-resident preconditions (not checked on the host): 0 <= n_b < window;
+ * P_b < capacity when the ring is full (else nothing is encoded and the
+ * lengths keep their values).  Two kernels: the scan, with one more
+ * workgroup per (batch, KV head) for steps 1 and 3 and the native rows, then
+ * the merge with the length update.                                         */
+octo_status octo_decode_step(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
+                             const octo_cache_view* k_cache, const octo_cache_view* v_cache,
+                             const void* q, octo_dtype q_dtype, int32_t num_q_heads,
+                             const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_window,
+                             uint16_t* v_window, int32_t window, int32_t* packed_lens,
+                             int32_t* window_lens, int32_t max_packed_len, float softmax_scale,
+                             float* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* Workspace bytes needed by octo_attend_chunk for these shapes.             */
 octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
                                        int32_t num_q_heads, int32_t kv_heads, int32_t Tq,

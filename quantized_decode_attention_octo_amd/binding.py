@@ -89,8 +89,15 @@ def lib():
                                         ctypes.POINTER(CacheView), ctypes.POINTER(CacheView), _I,
                                         _P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P,
                                         ctypes.c_size_t, _P]
+        L.octo_decode_step_workspace_bytes.argtypes = [ctypes.POINTER(CodecDesc), _I, _I, _I, _I,
+                                                       ctypes.POINTER(ctypes.c_size_t)]
+        L.octo_decode_step.argtypes = [ctypes.POINTER(CodecDesc), ctypes.POINTER(CodecDesc),
+                                       ctypes.POINTER(CacheView), ctypes.POINTER(CacheView),
+                                       _P, ctypes.c_int, _I, _P, _P, _P, _P, _I, _P, _P, _I,
+                                       ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
         for f in ("octo_record_sizes", "octo_encode", "octo_decode_workspace_bytes",
-                  "octo_attend_decode", "octo_chunk_workspace_bytes", "octo_attend_chunk"):
+                  "octo_attend_decode", "octo_chunk_workspace_bytes", "octo_attend_chunk",
+                  "octo_decode_step_workspace_bytes", "octo_decode_step"):
             getattr(L, f).restype = ctypes.c_int
         if L.octo_abi_version() != ABI_VERSION:
             raise RuntimeError("liboctopus.so ABI version mismatch")
@@ -231,6 +238,48 @@ def octo_attend_decode(k_codec, v_codec, k_cache, v_cache, q, seq_lens, max_seq_
                                     float(softmax_scale), _ptr(out),
                                     ctypes.c_void_p(_aligned_ptr(ws)), ws.numel() - 256,
                                     _stream(q.device)))
+    return out
+
+
+def octo_decode_step_workspace_bytes(k_codec, B, num_q_heads, kv_heads, max_packed_len):
+    n = ctypes.c_size_t()
+    _check(lib().octo_decode_step_workspace_bytes(ctypes.byref(k_codec.desc), B, num_q_heads,
+                                                  kv_heads, max_packed_len, ctypes.byref(n)))
+    return n.value
+
+
+def octo_decode_step(k_codec, v_codec, k_cache, v_cache, q, k_new, v_new, k_window, v_window,
+                     packed_lens, window_lens, max_packed_len=None, softmax_scale=0.0,
+                     out=None, ws=None):
+    """One decode step with a residual window (see include/octopus.h).
+    q[B, H_q, d] (fp32 or bf16), k_new/v_new[B, H_kv, d] bf16, rings
+    k_window/v_window[B, H_kv, W, d] bf16, packed_lens/window_lens int32 [B]
+    (all on the device; the rings and the lengths are updated in place).
+    Returns out[B, H_q, d] fp32."""
+    if q.dtype not in (torch.float32, torch.bfloat16) or not q.is_contiguous():
+        raise TypeError("q must be a contiguous float32 or bfloat16 tensor")
+    for t in (k_new, v_new, k_window, v_window):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError("new rows and rings must be contiguous bfloat16 tensors")
+    for t in (packed_lens, window_lens):
+        if t.dtype != torch.int32:
+            raise TypeError("packed_lens and window_lens must be int32")
+    B, Hq, d = q.shape
+    W = k_window.shape[2]
+    max_packed_len = k_cache.capacity if max_packed_len is None else int(max_packed_len)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    need = octo_decode_step_workspace_bytes(k_codec, B, Hq, k_cache.H, max_packed_len)
+    if ws is None or ws.numel() < need + 256:
+        ws = workspace(need, q.device)
+    dt = DTYPE_F32 if q.dtype == torch.float32 else DTYPE_BF16
+    _check(lib().octo_decode_step(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
+                                  ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
+                                  _ptr(q), dt, Hq, _ptr(k_new), _ptr(v_new), _ptr(k_window),
+                                  _ptr(v_window), W, _ptr(packed_lens), _ptr(window_lens),
+                                  max_packed_len, float(softmax_scale), _ptr(out),
+                                  ctypes.c_void_p(_aligned_ptr(ws)), ws.numel() - 256,
+                                  _stream(q.device)))
     return out
 
 

@@ -99,8 +99,18 @@ struct DecodeArgs {
   const uint16_t* kgamma_r;
   int capacity;
   int n_split, split_len;
-  float2* ws_ml;       // [B][Hq][n_split] (running max, normalizer)
-  float* ws_acc;       // [B][Hq][n_split][128] rotated-frame value sums (x64)
+  int n_part;          // partials per (batch, query head): n_split (+1 in a step)
+  float2* ws_ml;       // [B][Hq][n_part] (running max, normalizer)
+  float* ws_acc;       // [B][Hq][n_part][128] rotated-frame value sums (x64)
+  // octo_decode_step only (step = 1): the residual window, as split n_split
+  int step, window;
+  const int* win_lens;                 // n_b, tokens in the ring before the step
+  const uint16_t *k_new, *v_new;       // [B][Hkv][128] bf16
+  uint16_t *k_win, *v_win;             // rings [B][Hkv][window][128] bf16
+  uint32_t *k_idx_w, *k_qjl_w, *v_idx_w;   // the caches, written at slot P_b
+  float *k_gamma_w, *v_gamma_w;
+  uint16_t* k_gamma_r_w;
+  int k_rounding, v_rounding;
 };
 
 __device__ inline void wave_sync() {
@@ -262,6 +272,245 @@ __device__ inline void load_gv(BlockWords<BD, BN, QJL>& r, const DecodeArgs& a, 
     r.gv[kt] = *reinterpret_cast<const float4*>(a.vgamma + gbase + 16 * kt);
 }
 
+// ---------------------------------------------------------------- decode step
+// The residual window of a decode step (octo_decode_step; the paper keeps the
+// most recent tokens at native precision, OCTOPUS Sec. 4): one extra
+// workgroup per (batch, KV head) writes the new token to the ring, attends
+// over the window's native rows, leaves its partial (m, l, acc) beside the
+// scan's, and, when the ring is full, encodes the token leaving it into the
+// packed caches.
+constexpr int kMaxWindow = 64;
+
+// One wavefront encodes one bf16 vector x[128] into slot t of a plane: the
+// encoder of encode_kernel with the same decisions in the same arithmetic
+// (Sec. 3.1-3.6), the 43 triplets spread over lanes 0..42 instead of one lane
+// per vector.  u and fld are this wavefront's LDS scratch (129 floats, 43
+// words).
+template <int BD, int BN>
+__device__ void encode_one(const uint16_t* x, const float* cx, const float* cr, uint64_t seed,
+                           int rounding, bool qjl, uint32_t* idx, float* gamma,
+                           uint32_t* qjl_bits, uint16_t* gamma_r, size_t plane, int cap, int t,
+                           float* u, uint32_t* fld) {
+  constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD, BT = FWD + BN;
+  constexpr int WI = (kNTri * BT + 31) / 32;
+  const int L = threadIdx.x & 63;
+  // gamma, sign flip, rotation (Sec. 3.1)
+  float a0 = bf16_to_f32(x[L]), a1 = bf16_to_f32(x[L + 64]);
+  const float gam = sqrtf(wave_sum(fmaf(a0, a0, a1 * a1)));
+  a0 *= splitmix_sign(seed, L);
+  a1 *= splitmix_sign(seed, L + 64);
+  wht128(a0, a1);
+  const float scale = kInvSqrtD / fmaxf(gam, 1e-20f);
+  u[L] = a0 * scale;
+  u[L + 64] = a1 * scale;
+  if (L == 0) u[128] = 0.0f;                          // the zero pad (Sec. 3.2)
+  wave_sync();
+  if (L < kNTri) {
+    const float tx = u[3 * L], ty = u[3 * L + 1], tz = u[3 * L + 2];
+    // Eq. 5 on the L1-normalized direction, sign(0) = +1
+    const float inv_l1 = __builtin_amdgcn_rcpf(fmaxf(fabsf(tx) + fabsf(ty) + fabsf(tz), 1e-20f));
+    const float px = tx * inv_l1, py = ty * inv_l1, pz = tz * inv_l1;
+    float xi = px, eta = py;
+    if (pz < 0.0f) {
+      xi = (px >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(py));
+      eta = (py >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(px));
+    }
+    // Lloyd seeds: the number of C_xi cell boundaries below
+    int sx = 0, sy = 0;
+    for (int k = 0; k < K - 1; ++k) {
+      const float m = 0.5f * (cx[k] + cx[k + 1]);
+      sx += xi > m ? 1 : 0;
+      sy += eta > m ? 1 : 0;
+    }
+    // decoded unit direction of a code pair (Eq. 6, App. C.7, normalized)
+    auto dir = [&](int ci, int cj, float& nx, float& ny, float& nz) {
+      const float a = cx[ci], c = cx[cj];
+      const float z = 1.0f - fabsf(a) - fabsf(c);
+      float x0 = a, y0 = c;
+      if (z < 0.0f) {
+        x0 = (a >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(c));
+        y0 = (c >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(a));
+      }
+      const float nn = fmaxf(sqrtf(x0 * x0 + y0 * y0 + z * z), 1e-20f);
+      nx = x0 / nn;
+      ny = y0 / nn;
+      nz = z / nn;
+    };
+    int ci = sx, cj = sy;
+    float nx, ny, nz;
+    dir(ci, cj, nx, ny, nz);
+    float sel = 0.0f;                   // rho for the scalar rounding, best s otherwise
+    if (rounding == OCTO_ROUND_SCALAR) {
+      sel = sqrtf(tx * tx + ty * ty + tz * tz);
+    } else {
+      // seed first, then the other eight neighbours row-major (dx outer);
+      // only a strictly larger s replaces the incumbent (Sec. 3.5)
+      float best = tx * nx + ty * ny + tz * nz;
+      for (int dx = 0; dx < 3; ++dx)
+        for (int dy = 0; dy < 3; ++dy) {
+          if (dx == 1 && dy == 1) continue;
+          const int ai = min(max(sx + dx - 1, 0), K - 1), aj = min(max(sy + dy - 1, 0), K - 1);
+          float mx, my, mz;
+          dir(ai, aj, mx, my, mz);
+          const float sv = tx * mx + ty * my + tz * mz;
+          if (sv > best) {
+            best = sv;
+            ci = ai;
+            cj = aj;
+            nx = mx;
+            ny = my;
+            nz = mz;
+          }
+        }
+      sel = best;
+    }
+    int ir = 0;
+    for (int k = 0; k < R - 1; ++k) ir += sel > 0.5f * (cr[k] + cr[k + 1]) ? 1 : 0;
+    fld[L] = (uint32_t)(ci | (cj << BD)) | ((uint32_t)ir << FWD);
+    if (qjl) {
+      // rotated-frame residual r = u - u^ over the real coordinates (Sec. 3.6)
+      const float rho = cr[ir];
+      u[3 * L] = tx - rho * nx;
+      u[3 * L + 1] = ty - rho * ny;
+      if (3 * L + 2 < kHeadDim) u[3 * L + 2] = tz - rho * nz;
+    }
+  }
+  wave_sync();
+  // pack: word w gathers the fields that overlap its 32 bits
+  if (L < WI) {
+    uint32_t word = 0u;
+    const int i0 = 32 * L / BT, i1 = min(kNTri - 1, (32 * L + 31) / BT);
+    for (int i = i0; i <= i1; ++i) {
+      const int pos = i * BT - 32 * L;
+      word |= pos >= 0 ? fld[i] << pos : fld[i] >> -pos;
+    }
+    idx[tile_word(plane, cap, t, L, WI)] = word;
+  }
+  if (L == 0) gamma[plane * cap + t] = gam;
+  if (qjl) {
+    // sigma = sign(H diag(s') r), gamma_r = fp16(||r||)
+    float r0 = u[L], r1 = u[L + 64];
+    const float rn = sqrtf(wave_sum(fmaf(r0, r0, r1 * r1)));
+    r0 *= splitmix_sign(seed, kHeadDim + L);
+    r1 *= splitmix_sign(seed, kHeadDim + L + 64);
+    wht128(r0, r1);
+    const uint64_t b0 = __ballot(r0 < 0.0f), b1 = __ballot(r1 < 0.0f);
+    if (L < 4) {
+      const uint64_t bb = L < 2 ? b0 : b1;
+      qjl_bits[tile_word(plane, cap, t, L, 4)] = (uint32_t)(bb >> (32 * (L & 1)));
+    }
+    if (L == 0) gamma_r[plane * cap + t] = __builtin_bit_cast(uint16_t, (_Float16)rn);
+  }
+}
+
+// The window workgroup of (b, g).  State: packed tokens [0, P), ring tokens
+// [P, P + n), n < W, token j in ring slot j mod W.  The new token t = P + n
+// goes to slot t mod W; the partial covers tokens P .. t (the new one read
+// from k_new / v_new); if n + 1 == W token P is encoded into packed slot P.
+template <int BD, int BN, bool QJL, int NW>
+__device__ void window_step(const DecodeArgs& a, char* smem, char* qbuf, const float* cxk,
+                            const float* crk, const float* cxv, const float* crv, int b, int g) {
+  constexpr int kThreads = 64 * NW;
+  const int tid = threadIdx.x, L = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = a.window, G = a.G;
+  const int P = max(0, min(a.seq_lens[b], min(a.max_len, a.capacity)));
+  const int n = max(0, min(a.win_lens[b], W - 1));
+  const int t = P + n;
+  const size_t plane = (size_t)b * a.Hkv + g;
+  const uint16_t* kn = a.k_new + plane * kHeadDim;
+  const uint16_t* vn = a.v_new + plane * kHeadDim;
+  uint16_t* kr = a.k_win + plane * (size_t)W * kHeadDim;
+  uint16_t* vr = a.v_win + plane * (size_t)W * kHeadDim;
+  // the new token to its ring slot
+  if (tid < kHeadDim)
+    kr[(t % W) * kHeadDim + tid] = kn[tid];
+  else if (tid < 2 * kHeadDim)
+    vr[(t % W) * kHeadDim + tid - kHeadDim] = vn[tid - kHeadDim];
+  // stage K^T [128][64] and V [64][128] (bf16) and q (fp32)
+  uint16_t* kT = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* vs = kT + kHeadDim * kMaxWindow;
+  float* qs = reinterpret_cast<float*>(qbuf);
+  for (int e = tid; e < (n + 1) * kHeadDim; e += kThreads) {
+    const int j = e >> 7, c = e & 127;
+    const size_t row = (size_t)((P + j) % W) * kHeadDim;
+    kT[c * kMaxWindow + j] = j == n ? kn[c] : kr[row + c];
+    vs[j * kHeadDim + c] = j == n ? vn[c] : vr[row + c];
+  }
+  for (int e = tid; e < G * kHeadDim; e += kThreads) {
+    const size_t qo = ((size_t)b * a.Hq + (size_t)g * G) * kHeadDim + e;
+    qs[e] = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[qo])
+                     : static_cast<const float*>(a.q)[qo];
+  }
+  lds_barrier();
+  // scores of (head, token) pairs, scaled (natural-log units, as the scan's)
+  constexpr int kPer = (kMaxG * kMaxWindow + kThreads - 1) / kThreads;
+  float sv[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = tid + r * kThreads, h = e >> 6, j = e & 63;
+    float s = -INFINITY;
+    if (h < G && j <= n) {
+      float acc = 0.0f;
+      for (int c = 0; c < kHeadDim; ++c)
+        acc = fmaf(qs[h * kHeadDim + c], bf16_to_f32(kT[c * kMaxWindow + j]), acc);
+      s = acc * a.scale;
+    }
+    sv[r] = s;
+  }
+  lds_barrier();                                    // K^T and q are read
+  float* sc = reinterpret_cast<float*>(smem);       // [16][64] over K^T
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = tid + r * kThreads;
+    if (e < kMaxG * kMaxWindow) sc[e] = sv[r];
+  }
+  lds_barrier();
+  for (int h = wave; h < G; h += NW) {
+    const float s = sc[h * kMaxWindow + L];
+    const float m = wave_max(s);                     // token n is always there
+    const float p = __expf(s - m);                   // 0 past the window
+    const float l = wave_sum(p);
+    sc[h * kMaxWindow + L] = p;
+    if (L == 0) {
+      const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_part + a.n_split;
+      a.ws_ml[row] = make_float2(m, l);
+    }
+  }
+  lds_barrier();
+  float* acc_o = qs;                                // [16][128] over q
+  for (int e = tid; e < G * kHeadDim; e += kThreads) {
+    const int h = e >> 7, c = e & 127;
+    float acc = 0.0f;
+    for (int j = 0; j <= n; ++j) acc = fmaf(sc[h * kMaxWindow + j], bf16_to_f32(vs[j * kHeadDim + c]), acc);
+    acc_o[e] = acc;
+  }
+  lds_barrier();
+  // into the value frame, x64 like the scan's partials: R_v v = H diag(s_v) v / sqrt(d)
+  const float s_lo = splitmix_sign(a.vseed, L), s_hi = splitmix_sign(a.vseed, L + 64);
+  for (int h = wave; h < G; h += NW) {
+    float x0 = acc_o[h * kHeadDim + L] * s_lo, x1 = acc_o[h * kHeadDim + L + 64] * s_hi;
+    wht128(x0, x1);
+    const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_part + a.n_split;
+    a.ws_acc[row * kHeadDim + L] = x0 * (kInvSqrtD * kUScale);
+    a.ws_acc[row * kHeadDim + L + 64] = x1 * (kInvSqrtD * kUScale);
+  }
+  // eviction of token P (its row is the new one when W = 1)
+  if (n + 1 == W && P < a.capacity) {
+    float* scratch = reinterpret_cast<float*>(smem) + wave * 192;   // sc is dead
+    const uint16_t* ksrc = n == 0 ? kn : kr + (size_t)(P % W) * kHeadDim;
+    const uint16_t* vsrc = n == 0 ? vn : vr + (size_t)(P % W) * kHeadDim;
+    if (wave == 0)
+      encode_one<BD, BN>(ksrc, cxk, crk, a.kseed, a.k_rounding, QJL, a.k_idx_w, a.k_gamma_w,
+                         a.k_qjl_w, a.k_gamma_r_w, plane, a.capacity, P, scratch,
+                         reinterpret_cast<uint32_t*>(scratch + 132));
+    else if (wave == 1)
+      encode_one<BD, BN>(vsrc, cxv, crv, a.vseed, a.v_rounding, false, a.v_idx_w, a.v_gamma_w,
+                         nullptr, nullptr, plane, a.capacity, P, scratch,
+                         reinterpret_cast<uint32_t*>(scratch + 132));
+  }
+}
+
 template <int BD, int BN, bool QJL, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * NW, kWaves = NW;
@@ -353,6 +602,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     crv[tid] = cr_v;
   }
   lds_barrier();
+  if (a.step && split == a.n_split) {            // the residual window of a step
+    window_step<BD, BN, QJL, NW>(a, smem, qbuf, cxk, crk, cxv, crv, b, g);
+    return;
+  }
   const int n_tables = PRE || !a.shared_tables ? 2 : 1;
   // pre-split tables are rho-major, entry rho_index K^2 + code pair, so that
   // consecutive lanes write consecutive entries
@@ -705,11 +958,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
       Lsum += f * red_ml[(w * kMaxG + h) * 2 + 1];
       A += f * red_o[(w * kMaxG + h) * kHeadDim + c];
     }
-    const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_split + split;
+    const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_part + split;
     a.ws_acc[row * kHeadDim + c] = A;
     if (c == 0) a.ws_ml[row] = make_float2(M, Lsum);
   }
 }
+
+// The lengths a decode step updates (packed_lens = NULL: no step).
+struct StepState {
+  int* packed_lens;
+  int* win_lens;
+  int window, max_len, capacity;
+};
 
 // Merges the splits of one (batch, query head) by their log-sum-exp and
 // applies R_v^T = diag(s_v) H / sqrt(d).  Eight wavefronts take 16
@@ -721,19 +981,34 @@ constexpr int kMergeWaves = 8;
 constexpr int kMergeU = 16;
 __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float2* __restrict__ ws_ml,
                                                                  const float* __restrict__ ws_acc,
-                                                                 int n_split, int Hq,
+                                                                 int n_part, int Hq,
                                                                  uint64_t vseed,
-                                                                 float* __restrict__ out) {
+                                                                 float* __restrict__ out,
+                                                                 StepState st) {
   __shared__ float part[kMergeWaves][2 * 64 + 2];
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
-  const size_t row0 = ((size_t)blockIdx.y * Hq + blockIdx.x) * n_split;
+  if (st.packed_lens && blockIdx.x == 0 && tid == 0) {
+    // a step's state update, after every read of it (the scan launch): the
+    // token P left the ring into the packed caches, or the ring grew
+    const int b = blockIdx.y;
+    const int P = max(0, min(st.packed_lens[b], min(st.max_len, st.capacity)));
+    const int n = max(0, min(st.win_lens[b], st.window - 1));
+    if (n + 1 < st.window) {
+      st.packed_lens[b] = P;
+      st.win_lens[b] = n + 1;
+    } else {
+      st.packed_lens[b] = P < st.capacity ? P + 1 : P;
+      st.win_lens[b] = n;
+    }
+  }
+  const size_t row0 = ((size_t)blockIdx.y * Hq + blockIdx.x) * n_part;
   float M = -INFINITY, Lsum = 0.0f, a0 = 0.0f, a1 = 0.0f;
-  for (int s0 = wave * kMergeU; s0 < n_split; s0 += kMergeWaves * kMergeU) {
+  for (int s0 = wave * kMergeU; s0 < n_part; s0 += kMergeWaves * kMergeU) {
     float2 ml[kMergeU];
     float x0[kMergeU], x1[kMergeU];
 #pragma unroll
     for (int u = 0; u < kMergeU; ++u) {
-      const size_t r = row0 + min(s0 + u, n_split - 1);
+      const size_t r = row0 + min(s0 + u, n_part - 1);
       ml[u] = ws_ml[r];
       x0[u] = ws_acc[r * kHeadDim + L];
       x1[u] = ws_acc[r * kHeadDim + L + 64];
@@ -741,7 +1016,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float2* _
     float m_new = M;
 #pragma unroll
     for (int u = 0; u < kMergeU; ++u)
-      if (s0 + u < n_split) m_new = fmaxf(m_new, ml[u].x);
+      if (s0 + u < n_part) m_new = fmaxf(m_new, ml[u].x);
     if (m_new != -INFINITY) {            // the same in every lane
       const float f0 = M == -INFINITY ? 0.0f : __expf(M - m_new);
       Lsum *= f0;
@@ -749,7 +1024,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float2* _
       a1 *= f0;
 #pragma unroll
       for (int u = 0; u < kMergeU; ++u) {
-        const bool in = s0 + u < n_split && ml[u].x != -INFINITY;
+        const bool in = s0 + u < n_part && ml[u].x != -INFINITY;
         const float f = in ? __expf(ml[u].x - m_new) : 0.0f;
         Lsum = fmaf(f, ml[u].y, Lsum);
         a0 = fmaf(f, x0[u], a0);
@@ -795,8 +1070,9 @@ struct Plan {
 };
 
 // Splits of `nw`-wave workgroups: about eight waves per CU in all, each
-// split a multiple of nw 32-token blocks.
-Plan make_plan(int B, int Hq, int Hkv, int max_len, int nw) {
+// split a multiple of nw 32-token blocks; `extra` more partials per row (the
+// residual window of a step).
+Plan make_plan(int B, int Hq, int Hkv, int max_len, int nw, int extra) {
   Plan p;
   const int units = B * Hkv;
   const int target_blocks = 256 * (8 / nw);
@@ -806,7 +1082,7 @@ Plan make_plan(int B, int Hq, int Hkv, int max_len, int nw) {
   sl = (sl + quantum - 1) / quantum * quantum;
   p.split_len = max(sl, quantum);
   p.n_split = max(1, (max_len + p.split_len - 1) / p.split_len);
-  const size_t rows = (size_t)B * Hq * p.n_split;
+  const size_t rows = (size_t)B * Hq * (p.n_split + extra);
   p.ml_bytes = (rows * sizeof(float2) + 255) / 256 * 256;
   p.acc_bytes = rows * kHeadDim * sizeof(float);
   p.total = p.ml_bytes + p.acc_bytes;
@@ -822,7 +1098,7 @@ int waves_for(int b_dir, int b_nrm, bool shared) {
 
 template <int BD, int BN, bool QJL>
 void launch_q(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.n_split, a.Hkv, a.B);
+  dim3 grid(a.n_split + a.step, a.Hkv, a.B);
   constexpr bool big = (1 << (2 * BD + BN)) > kMaxSmallPre;
   if constexpr (!big) {
     hipLaunchKernelGGL((decode_kernel<BD, BN, QJL, kPre, kWavesSmall>), grid, dim3(64 * kWavesSmall), 0, st, a);
@@ -864,19 +1140,111 @@ static octo_status check_kv(const octo_codec_desc* k_codec, const octo_codec_des
   return OCTO_OK;
 }
 
+// Checks shared by octo_attend_decode and octo_decode_step and the
+// arguments of the scan (no step fields).  `extra`: partials per row beyond
+// the splits.
+static octo_status prepare(const char* what, const octo_codec_desc* k_codec,
+                           const octo_codec_desc* v_codec, const octo_cache_view* k_cache,
+                           const octo_cache_view* v_cache, const void* q, octo_dtype q_dtype,
+                           int32_t num_q_heads, const int32_t* seq_lens, int32_t max_seq_len,
+                           float softmax_scale, float* out, void* workspace,
+                           size_t workspace_bytes, int extra, DecodeArgs* a, Codec* kc, Codec* vc) {
+  octo_status s = check_kv(k_codec, v_codec, k_cache, v_cache, what, kc, vc);
+  if (s != OCTO_OK) return s;
+  if (q_dtype != OCTO_DTYPE_F32 && q_dtype != OCTO_DTYPE_BF16)
+    return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: q_dtype %d unknown", what, (int)q_dtype);
+  if (!q || !seq_lens || !out)
+    return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: q, the lengths and out must be set", what);
+  if ((uintptr_t)q % (q_dtype == OCTO_DTYPE_F32 ? 4 : 2) || ((uintptr_t)seq_lens & 3) ||
+      ((uintptr_t)out & 3))
+    return fail(OCTO_ERR_ALIGNMENT, "%s: q, the lengths or out misaligned", what);
+  const int B = k_cache->batch, Hkv = k_cache->kv_heads;
+  if (num_q_heads < 1 || num_q_heads % Hkv)
+    return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: %d query heads on %d KV heads", what,
+                num_q_heads, Hkv);
+  const int G = num_q_heads / Hkv;
+  if (G > kMaxG)
+    return fail(OCTO_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most %d)", what, G,
+                kMaxG);
+  if (max_seq_len < 0 || max_seq_len > k_cache->capacity)
+    return fail(OCTO_ERR_CAPACITY, "%s: max length %d outside [0, capacity %d]", what,
+                max_seq_len, k_cache->capacity);
+  if (B > 65535 || Hkv > 65535 || num_q_heads > 65535)
+    return fail(OCTO_ERR_UNSUPPORTED, "%s: batch and heads must be <= 65535", what);
+  const bool shared = std::memcmp(&kc->cb, &vc->cb, sizeof(Codebook)) == 0;
+  const Plan p =
+      make_plan(B, num_q_heads, Hkv, max_seq_len, waves_for(kc->b_dir, kc->b_nrm, shared), extra);
+  if (!workspace || workspace_bytes < p.total)
+    return fail(OCTO_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", what,
+                workspace_bytes, p.total);
+  if ((uintptr_t)workspace & 255)
+    return fail(OCTO_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", what);
+
+  std::memset(a, 0, sizeof(*a));
+  a->q = q;
+  a->q_bf16 = q_dtype == OCTO_DTYPE_BF16;
+  a->B = B;
+  a->Hq = num_q_heads;
+  a->Hkv = Hkv;
+  a->G = G;
+  a->seq_lens = seq_lens;
+  a->max_len = max_seq_len;
+  a->scale = softmax_scale > 0.0f ? softmax_scale : kInvSqrtD;
+  a->kcb = kc->cb;
+  a->vcb = vc->cb;
+  a->shared_tables = shared;
+  a->kseed = kc->seed;
+  a->vseed = vc->seed;
+  a->k_idx = k_cache->idx;
+  a->kqjl = k_cache->qjl;
+  a->kgamma = k_cache->gamma;
+  a->kgamma_r = k_cache->gamma_r;
+  a->v_idx = v_cache->idx;
+  a->vgamma = v_cache->gamma;
+  a->capacity = k_cache->capacity;
+  a->n_split = p.n_split;
+  a->split_len = p.split_len;
+  a->n_part = p.n_split + extra;
+  char* ws = static_cast<char*>(workspace);
+  a->ws_ml = reinterpret_cast<float2*>(ws);
+  a->ws_acc = reinterpret_cast<float*>(ws + p.ml_bytes);
+  return OCTO_OK;
+}
+
+static octo_status launch_scan(const DecodeArgs& a, const Codec& kc, const char* what,
+                               hipStream_t stream) {
+  switch (kc.b_dir * 10 + kc.b_nrm) {
+    case 31: launch<3, 1>(a, kc.qjl, stream); break;
+    case 42: launch<4, 2>(a, kc.qjl, stream); break;
+    case 53: launch<5, 3>(a, kc.qjl, stream); break;
+    case 22: launch<2, 2>(a, kc.qjl, stream); break;
+    case 33: launch<3, 3>(a, kc.qjl, stream); break;
+    case 44: launch<4, 4>(a, kc.qjl, stream); break;
+    default: return fail(OCTO_ERR_UNSUPPORTED, "%s: configuration not compiled", what);
+  }
+  return check_launch(what);
+}
+
+static octo_status workspace_bytes_for(const char* what, const octo_codec_desc* k_codec,
+                                       int32_t B, int32_t num_q_heads, int32_t kv_heads,
+                                       int32_t max_len, int extra, size_t* bytes) {
+  Codec kc;
+  octo_status s = resolve_codec(k_codec, what, &kc, false);
+  if (s != OCTO_OK) return s;
+  if (!bytes) return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", what);
+  if (B < 1 || num_q_heads < 1 || kv_heads < 1 || max_len < 0)
+    return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: bad sizes", what);
+  // the small-workgroup plan has the most splits: enough for either
+  *bytes = make_plan(B, num_q_heads, kv_heads, max_len, kWavesSmall, extra).total;
+  return OCTO_OK;
+}
+
 extern "C" octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
                                                    int32_t num_q_heads, int32_t kv_heads,
                                                    int32_t max_seq_len, size_t* bytes) {
   clear_error();
-  Codec kc;
-  octo_status s = resolve_codec(k_codec, "octo_decode_workspace_bytes", &kc, false);
-  if (s != OCTO_OK) return s;
-  if (!bytes) return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_decode_workspace_bytes: bytes is NULL");
-  if (B < 1 || num_q_heads < 1 || kv_heads < 1 || max_seq_len < 0)
-    return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_decode_workspace_bytes: bad sizes");
-  // the small-workgroup plan has the most splits: enough for either
-  *bytes = make_plan(B, num_q_heads, kv_heads, max_seq_len, kWavesSmall).total;
-  return OCTO_OK;
+  return workspace_bytes_for("octo_decode_workspace_bytes", k_codec, B, num_q_heads, kv_heads,
+                             max_seq_len, 0, bytes);
 }
 
 extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
@@ -889,76 +1257,72 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
                                           size_t workspace_bytes, hipStream_t stream) {
   clear_error();
   const char* what = "octo_attend_decode";
-  Codec kc, vc;
-  octo_status s = check_kv(k_codec, v_codec, k_cache, v_cache, what, &kc, &vc);
-  if (s != OCTO_OK) return s;
-  if (q_dtype != OCTO_DTYPE_F32 && q_dtype != OCTO_DTYPE_BF16)
-    return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: q_dtype %d unknown", what, (int)q_dtype);
-  if (!q || !seq_lens || !out)
-    return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: q, seq_lens and out must be set", what);
-  if ((uintptr_t)q % (q_dtype == OCTO_DTYPE_F32 ? 4 : 2) || ((uintptr_t)seq_lens & 3) ||
-      ((uintptr_t)out & 3))
-    return fail(OCTO_ERR_ALIGNMENT, "%s: q, seq_lens or out misaligned", what);
-  const int B = k_cache->batch, Hkv = k_cache->kv_heads;
-  if (num_q_heads < 1 || num_q_heads % Hkv)
-    return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: %d query heads on %d KV heads", what,
-                num_q_heads, Hkv);
-  const int G = num_q_heads / Hkv;
-  if (G > kMaxG)
-    return fail(OCTO_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most %d)", what, G,
-                kMaxG);
-  if (max_seq_len < 0 || max_seq_len > k_cache->capacity)
-    return fail(OCTO_ERR_CAPACITY, "%s: max_seq_len %d outside [0, capacity %d]", what,
-                max_seq_len, k_cache->capacity);
-  if (B > 65535 || Hkv > 65535 || num_q_heads > 65535)
-    return fail(OCTO_ERR_UNSUPPORTED, "%s: batch and heads must be <= 65535", what);
-  const bool shared = std::memcmp(&kc.cb, &vc.cb, sizeof(Codebook)) == 0;
-  const Plan p = make_plan(B, num_q_heads, Hkv, max_seq_len, waves_for(kc.b_dir, kc.b_nrm, shared));
-  if (!workspace || workspace_bytes < p.total)
-    return fail(OCTO_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", what,
-                workspace_bytes, p.total);
-  if ((uintptr_t)workspace & 255)
-    return fail(OCTO_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", what);
-
   DecodeArgs a;
-  a.q = q;
-  a.q_bf16 = q_dtype == OCTO_DTYPE_BF16;
-  a.B = B;
-  a.Hq = num_q_heads;
-  a.Hkv = Hkv;
-  a.G = G;
-  a.seq_lens = seq_lens;
-  a.max_len = max_seq_len;
-  a.scale = softmax_scale > 0.0f ? softmax_scale : kInvSqrtD;
-  a.kcb = kc.cb;
-  a.vcb = vc.cb;
-  a.shared_tables = shared;
-  a.kseed = kc.seed;
-  a.vseed = vc.seed;
-  a.k_idx = k_cache->idx;
-  a.kqjl = k_cache->qjl;
-  a.kgamma = k_cache->gamma;
-  a.kgamma_r = k_cache->gamma_r;
-  a.v_idx = v_cache->idx;
-  a.vgamma = v_cache->gamma;
-  a.capacity = k_cache->capacity;
-  a.n_split = p.n_split;
-  a.split_len = p.split_len;
-  char* ws = static_cast<char*>(workspace);
-  a.ws_ml = reinterpret_cast<float2*>(ws);
-  a.ws_acc = reinterpret_cast<float*>(ws + p.ml_bytes);
+  Codec kc, vc;
+  octo_status s = prepare(what, k_codec, v_codec, k_cache, v_cache, q, q_dtype, num_q_heads,
+                          seq_lens, max_seq_len, softmax_scale, out, workspace, workspace_bytes,
+                          0, &a, &kc, &vc);
+  if (s != OCTO_OK) return s;
+  if ((s = launch_scan(a, kc, what, stream)) != OCTO_OK) return s;
+  hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, a.B), dim3(kMergeWaves * 64), 0, stream,
+                     a.ws_ml, a.ws_acc, a.n_part, num_q_heads, vc.seed, out,
+                     StepState{nullptr, nullptr, 0, 0, 0});
+  return check_launch(what);
+}
 
-  switch (kc.b_dir * 10 + kc.b_nrm) {
-    case 31: launch<3, 1>(a, kc.qjl, stream); break;
-    case 42: launch<4, 2>(a, kc.qjl, stream); break;
-    case 53: launch<5, 3>(a, kc.qjl, stream); break;
-    case 22: launch<2, 2>(a, kc.qjl, stream); break;
-    case 33: launch<3, 3>(a, kc.qjl, stream); break;
-    case 44: launch<4, 4>(a, kc.qjl, stream); break;
-    default: return fail(OCTO_ERR_UNSUPPORTED, "%s: configuration not compiled", what);
-  }
-  if ((s = check_launch(what)) != OCTO_OK) return s;
-  hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, B), dim3(kMergeWaves * 64), 0, stream, a.ws_ml, a.ws_acc,
-                     a.n_split, num_q_heads, vc.seed, out);
+extern "C" octo_status octo_decode_step_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
+                                                        int32_t num_q_heads, int32_t kv_heads,
+                                                        int32_t max_packed_len, size_t* bytes) {
+  clear_error();
+  return workspace_bytes_for("octo_decode_step_workspace_bytes", k_codec, B, num_q_heads,
+                             kv_heads, max_packed_len, 1, bytes);
+}
+
+extern "C" octo_status octo_decode_step(const octo_codec_desc* k_codec,
+                                        const octo_codec_desc* v_codec,
+                                        const octo_cache_view* k_cache,
+                                        const octo_cache_view* v_cache, const void* q,
+                                        octo_dtype q_dtype, int32_t num_q_heads,
+                                        const uint16_t* k_new, const uint16_t* v_new,
+                                        uint16_t* k_window, uint16_t* v_window, int32_t window,
+                                        int32_t* packed_lens, int32_t* window_lens,
+                                        int32_t max_packed_len, float softmax_scale, float* out,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  clear_error();
+  const char* what = "octo_decode_step";
+  DecodeArgs a;
+  Codec kc, vc;
+  octo_status s = prepare(what, k_codec, v_codec, k_cache, v_cache, q, q_dtype, num_q_heads,
+                          packed_lens, max_packed_len, softmax_scale, out, workspace,
+                          workspace_bytes, 1, &a, &kc, &vc);
+  if (s != OCTO_OK) return s;
+  if (window < 1 || window > kMaxWindow)
+    return fail(OCTO_ERR_UNSUPPORTED, "%s: window %d outside [1, %d]", what, window, kMaxWindow);
+  if (!k_new || !v_new || !k_window || !v_window || !window_lens)
+    return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: new rows, rings and window_lens must be set", what);
+  if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_window | (uintptr_t)v_window) & 1 ||
+      ((uintptr_t)window_lens & 3))
+    return fail(OCTO_ERR_ALIGNMENT, "%s: rows or window_lens misaligned", what);
+  a.step = 1;
+  a.window = window;
+  a.win_lens = window_lens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_win = k_window;
+  a.v_win = v_window;
+  a.k_idx_w = k_cache->idx;
+  a.k_qjl_w = k_cache->qjl;
+  a.k_gamma_w = k_cache->gamma;
+  a.k_gamma_r_w = k_cache->gamma_r;
+  a.v_idx_w = v_cache->idx;
+  a.v_gamma_w = v_cache->gamma;
+  a.k_rounding = kc.rounding;
+  a.v_rounding = vc.rounding;
+  if ((s = launch_scan(a, kc, what, stream)) != OCTO_OK) return s;
+  hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, a.B), dim3(kMergeWaves * 64), 0, stream,
+                     a.ws_ml, a.ws_acc, a.n_part, num_q_heads, vc.seed, out,
+                     StepState{packed_lens, window_lens, window, max_packed_len,
+                               k_cache->capacity});
   return check_launch(what);
 }

@@ -14,6 +14,8 @@ Draw order per workload (one torch.Generator("cpu").manual_seed(seed)):
   K, V and in every query head of that KV head's group, then the sequence
   lengths (uniform integers in [len_lo, len_hi]) when they vary.
   Chunk workloads draw K, V of the cached window, q, then K_cur, V_cur.
+  Decode-step workloads (window > 0) then draw a pool of new-token rows
+  K_new, V_new [B, H_kv, 64, d], with the same outlier channels scaled.
 bf16 workloads are cast from fp32 with round-to-nearest-even.
 """
 import dataclasses
@@ -37,11 +39,13 @@ class Workload:
     len_lo: int = 0        # > 0: per-sequence lengths ~ U[len_lo, len_hi]
     len_hi: int = 0
     chunk_q: int = 0       # > 0: chunk workload with this many queries / current tokens
+    window: int = 0        # > 0: decode-step workload with a residual window of this size
     seed: int = 0
 
     @property
     def capacity(self):
-        total = self.T + self.chunk_q
+        # a decode-step workload keeps room for 1024 tokens leaving the window
+        total = self.T + self.chunk_q + (1024 if self.window else 0)
         return -(-total // 64) * 64
 
 
@@ -55,6 +59,9 @@ WORKLOADS = {
                         len_lo=4096, len_hi=8192),
     "long128k": Workload("long128k", "GQA 28/4, batch 4, context 131072, bf16, b=2 + QJL keys",
                          B=4, Hq=28, Hkv=4, d=128, T=131072, bits=2, dtype="bf16", qjl=True),
+    "step32k": Workload("step32k", "decode step, GQA 28/4, batch 1, context 32768 (last 32 tokens native), bf16 + outliers, b=4",
+                        B=1, Hq=28, Hkv=4, d=128, T=32768, bits=4, dtype="bf16", outliers=True,
+                        window=32),
     "chunk": Workload("chunk", "MHA 40 heads, d=128, 1560 queries over 9360 cached + 1560 current tokens, bf16, b=2",
                       B=1, Hq=40, Hkv=40, d=128, T=9360, bits=2, dtype="bf16", chunk_q=1560),
 }
@@ -82,10 +89,12 @@ def make_inputs(w: Workload, scale_T=None):
         V_cur = torch.randn(w.B, w.Hkv, w.chunk_q, w.d, generator=g)
     else:
         q = torch.randn(w.B, w.Hq, w.d, generator=g)
+    chans = []
     if w.outliers:
         G = w.Hq // w.Hkv
         for h in range(w.Hkv):
             ch = torch.randperm(w.d, generator=g)[:4]
+            chans.append(ch)
             K[:, h, :, ch] *= 10.0
             V[:, h, :, ch] *= 10.0
             q[:, h * G:(h + 1) * G, ..., ch] *= 10.0
@@ -99,4 +108,12 @@ def make_inputs(w: Workload, scale_T=None):
     if w.chunk_q:
         out["K_cur"] = _cast(K_cur, w.dtype)
         out["V_cur"] = _cast(V_cur, w.dtype)
+    if w.window:
+        K_new = torch.randn(w.B, w.Hkv, 64, w.d, generator=g)
+        V_new = torch.randn(w.B, w.Hkv, 64, w.d, generator=g)
+        for h, ch in enumerate(chans):
+            K_new[:, h, :, ch] *= 10.0
+            V_new[:, h, :, ch] *= 10.0
+        out["K_new"] = _cast(K_new, w.dtype)
+        out["V_new"] = _cast(V_new, w.dtype)
     return out

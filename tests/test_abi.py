@@ -165,6 +165,38 @@ def test_decode_errors(L):
     assert L.octo_decode_workspace_bytes(ctypes.byref(kd), 0, 28, 4, 32768, ctypes.byref(n)) == 1
 
 
+def test_step_errors(L):
+    """Host-side checks of octo_decode_step; no call here reaches a launch."""
+    kd, vd = desc(), desc()
+    kv, vv = view(H=2), view(H=2)
+    n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.octo_decode_workspace_bytes(ctypes.byref(kd), 2, 4, 2, 128, ctypes.byref(n0)) == 0
+    assert L.octo_decode_step_workspace_bytes(ctypes.byref(kd), 2, 4, 2, 128, ctypes.byref(n1)) == 0
+    # one more partial per (batch, query head): 2 x 4 rows of one split and the
+    # window each, (m, l) pairs padded to 256 bytes, then 128 sums per partial
+    assert n0.value == 256 + 2 * 4 * 1 * 128 * 4
+    assert n1.value == 256 + 2 * 4 * 2 * 128 * 4
+    # the views below have batch 1: their workspace
+    assert L.octo_decode_step_workspace_bytes(ctypes.byref(kd), 1, 4, 2, 128, ctypes.byref(n1)) == 0
+    assert n1.value == 256 + 4 * 2 * 128 * 4
+    p = ctypes.c_void_p(4096)
+
+    def st(window=32, k_new=p, ring=p, lens=p, wlens=p, ws_bytes=n1.value, max_len=128):
+        return L.octo_decode_step(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(kv),
+                                  ctypes.byref(vv), p, 0, 4, k_new, p, ring, p, window, lens,
+                                  wlens, max_len, 0.0, p, p, ws_bytes, None)
+    assert st(window=0) == 2
+    assert st(window=65) == 2
+    assert st(k_new=None) == 1
+    assert st(wlens=None) == 1
+    assert st(lens=None) == 1
+    assert st(ring=ctypes.c_void_p(4097)) == 3
+    assert st(wlens=ctypes.c_void_p(4098)) == 3
+    assert st(ws_bytes=n1.value - 1) == 5
+    assert st(max_len=129) == 4
+    assert b"octo_decode_step" in L.octo_last_error()
+
+
 def test_chunk_errors(L):
     kd, vd = desc(bits=2), desc(bits=2)
     kv, vv = view(H=2, cap=256), view(H=2, cap=256)
