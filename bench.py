@@ -290,17 +290,20 @@ def run_decode(w, steps, warmup):
 
 
 def run_step(w, steps, warmup):
-    """Decode steps with a residual window: the packed prefix holds tokens
-    [0, T - W + 1), the rings the last W - 1 tokens, and every step appends a
-    token from the pool, attends over T + 1 + s tokens and encodes the token
-    leaving the window."""
-    if warmup + steps > 1024:
-        raise SystemExit("the decode-step workload keeps room for 1024 steps")
+    """Decode steps with a residual window of W tokens over a context of up to
+    T tokens: the packed prefix starts with P0 = T - W - 63 tokens and the
+    rings with the next W - 1, and step s appends a token from the pool,
+    attends over P0 + W + s tokens (at most T over 64 steps) and encodes the
+    token leaving the window.  The split plan is sized by the last step's
+    packed length, T - W."""
+    if warmup + steps > 64:
+        raise SystemExit("the decode-step workload runs at most 64 steps (warmup included)")
     inp = make_inputs(w)
     kc = octo.Codec(bits=w.bits, qjl=w.qjl)
     vc = octo.Codec(bits=w.bits)
     W, T = w.window, w.T
-    P0 = T - W + 1
+    P0 = T - W - 63
+    max_packed = T - W
     K, V = inp["K"].cuda(), inp["V"].cuda()
     cap = w.capacity
     kcache = octo.PackedCache(kc, w.B, w.Hkv, cap)
@@ -309,7 +312,7 @@ def run_step(w, steps, warmup):
     octo.octo_encode(vc, V[:, :, :P0].contiguous(), vcache)
     kr = torch.zeros(w.B, w.Hkv, W, w.d, dtype=torch.bfloat16, device="cuda")
     vr = torch.zeros_like(kr)
-    for j in range(P0, T):
+    for j in range(P0, P0 + W - 1):
         kr[:, :, j % W] = K[:, :, j]
         vr[:, :, j % W] = V[:, :, j]
     plens = torch.full((w.B,), P0, dtype=torch.int32, device="cuda")
@@ -317,7 +320,7 @@ def run_step(w, steps, warmup):
     q = inp["q"].cuda()
     kn, vn = inp["K_new"].cuda(), inp["V_new"].cuda()
     new = [(kn[:, :, i].contiguous(), vn[:, :, i].contiguous()) for i in range(kn.shape[2])]
-    ws = octo.workspace(octo.octo_decode_step_workspace_bytes(kc, w.B, w.Hq, w.Hkv, cap), "cuda")
+    ws = octo.workspace(octo.octo_decode_step_workspace_bytes(kc, w.B, w.Hq, w.Hkv, max_packed), "cuda")
     out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
     t_att = Timer()
     count = [0]
@@ -325,8 +328,8 @@ def run_step(w, steps, warmup):
     def step(timed):
         k1, v1 = new[count[0] % len(new)]
         e0 = t_att.start() if timed else None
-        octo.octo_decode_step(kc, vc, kcache, vcache, q, k1, v1, kr, vr, plens, wlens, cap,
-                              out=out, ws=ws)
+        octo.octo_decode_step(kc, vc, kcache, vcache, q, k1, v1, kr, vr, plens, wlens,
+                              max_packed, out=out, ws=ws)
         if timed:
             t_att.stop(e0)
         count[0] += 1
@@ -340,8 +343,8 @@ def run_step(w, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     att_ms = t_att.mean_ms()
-    # tokens attended per step: P + W = T + 1 + s at step s (every step evicts)
-    tokens = w.B * (T + 1 + warmup + (steps - 1) / 2.0)
+    # tokens attended per step: P + W = P0 + W + s at step s (every step evicts)
+    tokens = w.B * (P0 + W + warmup + (steps - 1) / 2.0)
     packed = w.B * w.Hkv * (tokens / w.B - W) * (packed_bytes_per_token(kc) + packed_bytes_per_token(vc))
     native = w.B * w.Hkv * (W * 2 * w.d * 2 + 2 * w.d * 2)      # window rows read, new rows written
     enc = w.B * w.Hkv * (2 * w.d * 2 + packed_bytes_per_token(kc) + packed_bytes_per_token(vc))

@@ -198,10 +198,10 @@ octo_status octo_decode_step_workspace_bytes(const octo_codec_desc* k_codec, int
  * So the attention always sees the last min(window, t + 1) tokens at native
  * precision, and a token is compressed when it leaves the window.
  *   q           device [B, num_q_heads, d], fp32 or bf16.
- *   k_new, v_new  device bf16 [B, kv_heads, d].
- *   k_window, v_window  device bf16 rings [B, kv_heads, window, d], owned
- *               by the caller, read and written.
- *   window      1 .. 64.
+ *   k_new, v_new  device bf16 [B, kv_heads, d], 16-byte aligned.
+ *   k_window, v_window  device bf16 rings [B, kv_heads, window, d], 16-byte
+ *               aligned, owned by the caller, read and written.
+ *   window      1 .. 256.
  *   packed_lens, window_lens  device int32 [B], read and updated in place.
  *   max_packed_len  host bound: every P_b <= max_packed_len <= capacity
  *               (the split plan is sized by it; larger P_b are clamped).
@@ -209,9 +209,10 @@ octo_status octo_decode_step_workspace_bytes(const octo_codec_desc* k_codec, int
  *               aligned.
  * Device-resident preconditions (not checked on the host): 0 <= n_b < window;
  * P_b < capacity when the ring is full (else nothing is encoded and the
- * lengths keep their values).  Two kernels: the scan, with one more
- * workgroup per (batch, KV head) for steps 1 and 3 and the native rows, then
- * the merge with the length update.                                         */
+ * lengths keep their values).  Two kernels: the scan of octo_attend_decode
+ * over the packed tokens, then the merge, which folds in the native rows and
+ * in which one more workgroup per sequence does steps 1 and 3 and updates
+ * the lengths.                                                              */
 octo_status octo_decode_step(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
                              const octo_cache_view* k_cache, const octo_cache_view* v_cache,
                              const void* q, octo_dtype q_dtype, int32_t num_q_heads,

@@ -99,18 +99,13 @@ struct DecodeArgs {
   const uint16_t* kgamma_r;
   int capacity;
   int n_split, split_len;
-  int n_part;          // partials per (batch, query head): n_split (+1 in a step)
+  int n_part;          // partials per (batch, query head): n_split
   float2* ws_ml;       // [B][Hq][n_part] (running max, normalizer)
   float* ws_acc;       // [B][Hq][n_part][128] rotated-frame value sums (x64)
-  // octo_decode_step only (step = 1): the residual window, as split n_split
+  // octo_decode_step only (step = 1): (P_b, n_b) as the scan read them
   int step, window;
   const int* win_lens;                 // n_b, tokens in the ring before the step
-  const uint16_t *k_new, *v_new;       // [B][Hkv][128] bf16
-  uint16_t *k_win, *v_win;             // rings [B][Hkv][window][128] bf16
-  uint32_t *k_idx_w, *k_qjl_w, *v_idx_w;   // the caches, written at slot P_b
-  float *k_gamma_w, *v_gamma_w;
-  uint16_t* k_gamma_r_w;
-  int k_rounding, v_rounding;
+  int2* snap;                          // [B] in the workspace
 };
 
 __device__ inline void wave_sync() {
@@ -274,24 +269,53 @@ __device__ inline void load_gv(BlockWords<BD, BN, QJL>& r, const DecodeArgs& a, 
 
 // ---------------------------------------------------------------- decode step
 // The residual window of a decode step (octo_decode_step; the paper keeps the
-// most recent tokens at native precision, OCTOPUS Sec. 4): one extra
-// workgroup per (batch, KV head) writes the new token to the ring, attends
-// over the window's native rows, leaves its partial (m, l, acc) beside the
-// scan's, and, when the ring is full, encodes the token leaving it into the
-// packed caches.
-constexpr int kMaxWindow = 64;
+// most recent tokens at native precision, OCTOPUS Sec. 4).  The scan is the
+// one of octo_attend_decode over the packed prefix, and it copies each
+// sequence's (P, n) to the workspace.  The merge launch then folds the
+// window's native rows into each head's merge, and one more workgroup per
+// sequence writes the new token to the ring, encodes the token leaving a
+// full ring into its packed slot and updates the lengths (which nothing else
+// in that launch reads: the other workgroups use the copy).
+constexpr int kMaxWindow = 256;
+
+// The encoder's tables for one codebook, in LDS: the decoded unit direction
+// of every code pair with the pair's code (Eq. 6, App. C.7, normalized),
+// padded by one clamped cell per side, so that the 3x3 neighbourhood of seed
+// (sx, sy) is lut[(sx + dx) + KP (sy + dy)], dx, dy in 0..2; the C_xi cell
+// boundaries padded with -inf and +inf; the C_rho boundaries.  The same
+// arithmetic as encode_kernel's tables.  All threads of the workgroup build.
+template <int BD, int BN>
+__device__ void encoder_tables(const float* cx, const float* cr, floatx4* lut, float* midp,
+                               float* mid_rho, int tid, int nthreads) {
+  constexpr int K = 1 << BD, R = 1 << BN, KP = K + 2;
+  for (int e = tid; e < KP * KP; e += nthreads) {
+    const int ci = min(max(e % KP - 1, 0), K - 1), cj = min(max(e / KP - 1, 0), K - 1);
+    const float xi = cx[ci], eta = cx[cj];
+    const float z = 1.0f - fabsf(xi) - fabsf(eta);
+    float x = xi, y = eta;
+    if (z < 0.0f) {
+      x = (xi >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(eta));
+      y = (eta >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(xi));
+    }
+    const float n = fmaxf(sqrtf(x * x + y * y + z * z), 1e-20f);
+    lut[e] = floatx4{x / n, y / n, z / n, __uint_as_float((uint32_t)(ci | (cj << BD)))};
+  }
+  if (tid <= K) midp[tid] = tid == 0 ? -INFINITY : tid == K ? INFINITY : 0.5f * (cx[tid - 1] + cx[tid]);
+  if (tid < R - 1) mid_rho[tid] = 0.5f * (cr[tid] + cr[tid + 1]);
+}
 
 // One wavefront encodes one bf16 vector x[128] into slot t of a plane: the
 // encoder of encode_kernel with the same decisions in the same arithmetic
 // (Sec. 3.1-3.6), the 43 triplets spread over lanes 0..42 instead of one lane
-// per vector.  u and fld are this wavefront's LDS scratch (129 floats, 43
-// words).
+// per vector, with the tables of encoder_tables.  u and fld are this
+// wavefront's LDS scratch (129 floats, 43 words).
 template <int BD, int BN>
-__device__ void encode_one(const uint16_t* x, const float* cx, const float* cr, uint64_t seed,
-                           int rounding, bool qjl, uint32_t* idx, float* gamma,
-                           uint32_t* qjl_bits, uint16_t* gamma_r, size_t plane, int cap, int t,
-                           float* u, uint32_t* fld) {
-  constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD, BT = FWD + BN;
+__device__ void encode_one(const uint16_t* x, const floatx4* lut, const float* midp,
+                           const float* mid_rho, const float* cr, uint64_t seed, int rounding,
+                           bool qjl, uint32_t* idx, float* gamma, uint32_t* qjl_bits,
+                           uint16_t* gamma_r, size_t plane, int cap, int t, float* u,
+                           uint32_t* fld) {
+  constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD, BT = FWD + BN, KP = K + 2;
   constexpr int WI = (kNTri * BT + 31) / 32;
   const int L = threadIdx.x & 63;
   // gamma, sign flip, rotation (Sec. 3.1)
@@ -315,64 +339,46 @@ __device__ void encode_one(const uint16_t* x, const float* cx, const float* cr, 
       xi = (px >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(py));
       eta = (py >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(px));
     }
-    // Lloyd seeds: the number of C_xi cell boundaries below
+    // Lloyd seeds: the number of C_xi cell boundaries below (binary search)
     int sx = 0, sy = 0;
-    for (int k = 0; k < K - 1; ++k) {
-      const float m = 0.5f * (cx[k] + cx[k + 1]);
-      sx += xi > m ? 1 : 0;
-      sy += eta > m ? 1 : 0;
+#pragma unroll
+    for (int step = K >> 1; step > 0; step >>= 1) {
+      if (xi > midp[sx + step]) sx += step;
+      if (eta > midp[sy + step]) sy += step;
     }
-    // decoded unit direction of a code pair (Eq. 6, App. C.7, normalized)
-    auto dir = [&](int ci, int cj, float& nx, float& ny, float& nz) {
-      const float a = cx[ci], c = cx[cj];
-      const float z = 1.0f - fabsf(a) - fabsf(c);
-      float x0 = a, y0 = c;
-      if (z < 0.0f) {
-        x0 = (a >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(c));
-        y0 = (c >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(a));
-      }
-      const float nn = fmaxf(sqrtf(x0 * x0 + y0 * y0 + z * z), 1e-20f);
-      nx = x0 / nn;
-      ny = y0 / nn;
-      nz = z / nn;
-    };
-    int ci = sx, cj = sy;
-    float nx, ny, nz;
-    dir(ci, cj, nx, ny, nz);
-    float sel = 0.0f;                   // rho for the scalar rounding, best s otherwise
+    const floatx4* nbh = lut + sx + KP * sy;
+    floatx4 nb = nbh[1 + KP];                          // the seed
+    float sel;
     if (rounding == OCTO_ROUND_SCALAR) {
       sel = sqrtf(tx * tx + ty * ty + tz * tz);
     } else {
       // seed first, then the other eight neighbours row-major (dx outer);
       // only a strictly larger s replaces the incumbent (Sec. 3.5)
-      float best = tx * nx + ty * ny + tz * nz;
+      float best = tx * nb.x + ty * nb.y + tz * nb.z;
+#pragma unroll
       for (int dx = 0; dx < 3; ++dx)
+#pragma unroll
         for (int dy = 0; dy < 3; ++dy) {
           if (dx == 1 && dy == 1) continue;
-          const int ai = min(max(sx + dx - 1, 0), K - 1), aj = min(max(sy + dy - 1, 0), K - 1);
-          float mx, my, mz;
-          dir(ai, aj, mx, my, mz);
-          const float sv = tx * mx + ty * my + tz * mz;
+          const floatx4 n = nbh[dx + KP * dy];
+          const float sv = tx * n.x + ty * n.y + tz * n.z;
           if (sv > best) {
             best = sv;
-            ci = ai;
-            cj = aj;
-            nx = mx;
-            ny = my;
-            nz = mz;
+            nb = n;
           }
         }
       sel = best;
     }
     int ir = 0;
-    for (int k = 0; k < R - 1; ++k) ir += sel > 0.5f * (cr[k] + cr[k + 1]) ? 1 : 0;
-    fld[L] = (uint32_t)(ci | (cj << BD)) | ((uint32_t)ir << FWD);
+#pragma unroll
+    for (int k = 0; k < R - 1; ++k) ir += sel > mid_rho[k] ? 1 : 0;
+    fld[L] = __float_as_uint(nb.w) | ((uint32_t)ir << FWD);
     if (qjl) {
       // rotated-frame residual r = u - u^ over the real coordinates (Sec. 3.6)
       const float rho = cr[ir];
-      u[3 * L] = tx - rho * nx;
-      u[3 * L + 1] = ty - rho * ny;
-      if (3 * L + 2 < kHeadDim) u[3 * L + 2] = tz - rho * nz;
+      u[3 * L] = tx - rho * nb.x;
+      u[3 * L + 1] = ty - rho * nb.y;
+      if (3 * L + 2 < kHeadDim) u[3 * L + 2] = tz - rho * nb.z;
     }
   }
   wave_sync();
@@ -400,114 +406,6 @@ __device__ void encode_one(const uint16_t* x, const float* cx, const float* cr, 
       qjl_bits[tile_word(plane, cap, t, L, 4)] = (uint32_t)(bb >> (32 * (L & 1)));
     }
     if (L == 0) gamma_r[plane * cap + t] = __builtin_bit_cast(uint16_t, (_Float16)rn);
-  }
-}
-
-// The window workgroup of (b, g).  State: packed tokens [0, P), ring tokens
-// [P, P + n), n < W, token j in ring slot j mod W.  The new token t = P + n
-// goes to slot t mod W; the partial covers tokens P .. t (the new one read
-// from k_new / v_new); if n + 1 == W token P is encoded into packed slot P.
-template <int BD, int BN, bool QJL, int NW>
-__device__ void window_step(const DecodeArgs& a, char* smem, char* qbuf, const float* cxk,
-                            const float* crk, const float* cxv, const float* crv, int b, int g) {
-  constexpr int kThreads = 64 * NW;
-  const int tid = threadIdx.x, L = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int W = a.window, G = a.G;
-  const int P = max(0, min(a.seq_lens[b], min(a.max_len, a.capacity)));
-  const int n = max(0, min(a.win_lens[b], W - 1));
-  const int t = P + n;
-  const size_t plane = (size_t)b * a.Hkv + g;
-  const uint16_t* kn = a.k_new + plane * kHeadDim;
-  const uint16_t* vn = a.v_new + plane * kHeadDim;
-  uint16_t* kr = a.k_win + plane * (size_t)W * kHeadDim;
-  uint16_t* vr = a.v_win + plane * (size_t)W * kHeadDim;
-  // the new token to its ring slot
-  if (tid < kHeadDim)
-    kr[(t % W) * kHeadDim + tid] = kn[tid];
-  else if (tid < 2 * kHeadDim)
-    vr[(t % W) * kHeadDim + tid - kHeadDim] = vn[tid - kHeadDim];
-  // stage K^T [128][64] and V [64][128] (bf16) and q (fp32)
-  uint16_t* kT = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* vs = kT + kHeadDim * kMaxWindow;
-  float* qs = reinterpret_cast<float*>(qbuf);
-  for (int e = tid; e < (n + 1) * kHeadDim; e += kThreads) {
-    const int j = e >> 7, c = e & 127;
-    const size_t row = (size_t)((P + j) % W) * kHeadDim;
-    kT[c * kMaxWindow + j] = j == n ? kn[c] : kr[row + c];
-    vs[j * kHeadDim + c] = j == n ? vn[c] : vr[row + c];
-  }
-  for (int e = tid; e < G * kHeadDim; e += kThreads) {
-    const size_t qo = ((size_t)b * a.Hq + (size_t)g * G) * kHeadDim + e;
-    qs[e] = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[qo])
-                     : static_cast<const float*>(a.q)[qo];
-  }
-  lds_barrier();
-  // scores of (head, token) pairs, scaled (natural-log units, as the scan's)
-  constexpr int kPer = (kMaxG * kMaxWindow + kThreads - 1) / kThreads;
-  float sv[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int e = tid + r * kThreads, h = e >> 6, j = e & 63;
-    float s = -INFINITY;
-    if (h < G && j <= n) {
-      float acc = 0.0f;
-      for (int c = 0; c < kHeadDim; ++c)
-        acc = fmaf(qs[h * kHeadDim + c], bf16_to_f32(kT[c * kMaxWindow + j]), acc);
-      s = acc * a.scale;
-    }
-    sv[r] = s;
-  }
-  lds_barrier();                                    // K^T and q are read
-  float* sc = reinterpret_cast<float*>(smem);       // [16][64] over K^T
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int e = tid + r * kThreads;
-    if (e < kMaxG * kMaxWindow) sc[e] = sv[r];
-  }
-  lds_barrier();
-  for (int h = wave; h < G; h += NW) {
-    const float s = sc[h * kMaxWindow + L];
-    const float m = wave_max(s);                     // token n is always there
-    const float p = __expf(s - m);                   // 0 past the window
-    const float l = wave_sum(p);
-    sc[h * kMaxWindow + L] = p;
-    if (L == 0) {
-      const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_part + a.n_split;
-      a.ws_ml[row] = make_float2(m, l);
-    }
-  }
-  lds_barrier();
-  float* acc_o = qs;                                // [16][128] over q
-  for (int e = tid; e < G * kHeadDim; e += kThreads) {
-    const int h = e >> 7, c = e & 127;
-    float acc = 0.0f;
-    for (int j = 0; j <= n; ++j) acc = fmaf(sc[h * kMaxWindow + j], bf16_to_f32(vs[j * kHeadDim + c]), acc);
-    acc_o[e] = acc;
-  }
-  lds_barrier();
-  // into the value frame, x64 like the scan's partials: R_v v = H diag(s_v) v / sqrt(d)
-  const float s_lo = splitmix_sign(a.vseed, L), s_hi = splitmix_sign(a.vseed, L + 64);
-  for (int h = wave; h < G; h += NW) {
-    float x0 = acc_o[h * kHeadDim + L] * s_lo, x1 = acc_o[h * kHeadDim + L + 64] * s_hi;
-    wht128(x0, x1);
-    const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_part + a.n_split;
-    a.ws_acc[row * kHeadDim + L] = x0 * (kInvSqrtD * kUScale);
-    a.ws_acc[row * kHeadDim + L + 64] = x1 * (kInvSqrtD * kUScale);
-  }
-  // eviction of token P (its row is the new one when W = 1)
-  if (n + 1 == W && P < a.capacity) {
-    float* scratch = reinterpret_cast<float*>(smem) + wave * 192;   // sc is dead
-    const uint16_t* ksrc = n == 0 ? kn : kr + (size_t)(P % W) * kHeadDim;
-    const uint16_t* vsrc = n == 0 ? vn : vr + (size_t)(P % W) * kHeadDim;
-    if (wave == 0)
-      encode_one<BD, BN>(ksrc, cxk, crk, a.kseed, a.k_rounding, QJL, a.k_idx_w, a.k_gamma_w,
-                         a.k_qjl_w, a.k_gamma_r_w, plane, a.capacity, P, scratch,
-                         reinterpret_cast<uint32_t*>(scratch + 132));
-    else if (wave == 1)
-      encode_one<BD, BN>(vsrc, cxv, crv, a.vseed, a.v_rounding, false, a.v_idx_w, a.v_gamma_w,
-                         nullptr, nullptr, plane, a.capacity, P, scratch,
-                         reinterpret_cast<uint32_t*>(scratch + 132));
   }
 }
 
@@ -591,6 +489,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   len = max(0, min(len, min(a.max_len, a.capacity)));
   // uniform: the loop and its prefetch test become scalar branches
   const int t_end = __builtin_amdgcn_readfirstlane(min(len, t_begin + a.split_len));
+  if (a.step && split == 0 && g == 0 && tid == 0)   // the step's (P, n) for the merge launch
+    a.snap[b] = make_int2(len, max(0, min(a.win_lens[b], a.window - 1)));
 
   // ---- tables: codebooks to LDS first, then the table entries
   if (tid < K) {
@@ -602,10 +502,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     crv[tid] = cr_v;
   }
   lds_barrier();
-  if (a.step && split == a.n_split) {            // the residual window of a step
-    window_step<BD, BN, QJL, NW>(a, smem, qbuf, cxk, crk, cxv, crv, b, g);
-    return;
-  }
   const int n_tables = PRE || !a.shared_tables ? 2 : 1;
   // pre-split tables are rho-major, entry rho_index K^2 + code pair, so that
   // consecutive lanes write consecutive entries
@@ -964,44 +860,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// The lengths a decode step updates (packed_lens = NULL: no step).
-struct StepState {
-  int* packed_lens;
-  int* win_lens;
-  int window, max_len, capacity;
-};
-
-// Merges the splits of one (batch, query head) by their log-sum-exp and
+// Merges the partials of one (batch, query head) by their log-sum-exp and
 // applies R_v^T = diag(s_v) H / sqrt(d).  Eight wavefronts take 16
-// consecutive splits each per round, every load of the round in flight at
+// consecutive partials each per round, every load of the round in flight at
 // once, with a running maximum (an online rescale) so that no pass over the
-// maxima has to come first; the wavefronts meet in LDS in a fixed order, so
-// the result does not depend on scheduling.
+// maxima has to come first; `fold` may then add more to a wavefront's
+// running (M, l, acc) (rotated frame, x64); the wavefronts meet in LDS in a
+// fixed order, so the result does not depend on scheduling.
 constexpr int kMergeWaves = 8;
 constexpr int kMergeU = 16;
-__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float2* __restrict__ ws_ml,
-                                                                 const float* __restrict__ ws_acc,
-                                                                 int n_part, int Hq,
-                                                                 uint64_t vseed,
-                                                                 float* __restrict__ out,
-                                                                 StepState st) {
+
+template <class Fold>
+__device__ inline void merge_head(const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+                                  int n_part, int Hq, uint64_t vseed, float* __restrict__ out,
+                                  int head, int b, Fold fold) {
   __shared__ float part[kMergeWaves][2 * 64 + 2];
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
-  if (st.packed_lens && blockIdx.x == 0 && tid == 0) {
-    // a step's state update, after every read of it (the scan launch): the
-    // token P left the ring into the packed caches, or the ring grew
-    const int b = blockIdx.y;
-    const int P = max(0, min(st.packed_lens[b], min(st.max_len, st.capacity)));
-    const int n = max(0, min(st.win_lens[b], st.window - 1));
-    if (n + 1 < st.window) {
-      st.packed_lens[b] = P;
-      st.win_lens[b] = n + 1;
-    } else {
-      st.packed_lens[b] = P < st.capacity ? P + 1 : P;
-      st.win_lens[b] = n;
-    }
-  }
-  const size_t row0 = ((size_t)blockIdx.y * Hq + blockIdx.x) * n_part;
+  const size_t row0 = ((size_t)b * Hq + head) * n_part;
   float M = -INFINITY, Lsum = 0.0f, a0 = 0.0f, a1 = 0.0f;
   for (int s0 = wave * kMergeU; s0 < n_part; s0 += kMergeWaves * kMergeU) {
     float2 ml[kMergeU];
@@ -1033,6 +908,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float2* _
       M = m_new;
     }
   }
+  fold(wave, L, M, Lsum, a0, a1);
   part[wave][L] = a0;
   part[wave][64 + L] = a1;
   if (L == 0) {
@@ -1059,20 +935,195 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float2* _
   t0 *= inv;
   t1 *= inv;
   wht128(t0, t1);
-  const size_t o = ((size_t)blockIdx.y * Hq + blockIdx.x) * kHeadDim;
+  const size_t o = ((size_t)b * Hq + head) * kHeadDim;
   out[o + L] = t0 * kInvSqrtD * splitmix_sign(vseed, L);
   out[o + L + 64] = t1 * kInvSqrtD * splitmix_sign(vseed, L + 64);
 }
 
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float2* __restrict__ ws_ml,
+                                                                 const float* __restrict__ ws_acc,
+                                                                 int n_part, int Hq,
+                                                                 uint64_t vseed,
+                                                                 float* __restrict__ out) {
+  merge_head(ws_ml, ws_acc, n_part, Hq, vseed, out, blockIdx.x, blockIdx.y,
+             [](int, int, float&, float&, float&, float&) {});
+}
+
+// The arguments of a step's merge launch.
+struct StepArgs {
+  const int2* snap;                    // (P_b, n_b) as the scan read them
+  int* packed_lens;
+  int* win_lens;
+  int window, capacity, Hkv, G;
+  const void* q;
+  int q_bf16;
+  float scale;
+  const uint16_t *k_new, *v_new;       // [B][Hkv][128] bf16
+  uint16_t *k_win, *v_win;             // rings [B][Hkv][window][128] bf16
+  Codebook kcb, vcb;
+  int shared;                          // K and V codebook values agree
+  uint64_t kseed, vseed;
+  int k_rounding, v_rounding, k_qjl;
+  uint32_t *k_idx, *k_qjl_bits, *v_idx;   // the caches, written at slot P_b
+  float *k_gamma, *v_gamma;
+  uint16_t* k_gamma_r;
+};
+
+// The append workgroup of sequence b: the new tokens to their ring slots,
+// the tokens leaving full rings encoded into packed slot P (one wavefront per
+// vector; the ring row, or the new row when the window is one token), and
+// the lengths.
+template <int BD, int BN>
+__device__ void append_block(const StepArgs& a, int b) {
+  constexpr int K = 1 << BD, R = 1 << BN, KP = K + 2;
+  __shared__ float cx_k[K], cx_v[K], cr_k[R], cr_v[R];
+  __shared__ floatx4 lut[2][KP * KP];
+  __shared__ float midp[2][K + 1], mid_rho[2][R > 1 ? R - 1 : 1];
+  __shared__ float scratch[kMergeWaves][192];
+  constexpr int kThreads = kMergeWaves * 64;
+  const int tid = threadIdx.x, L = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = a.window;
+  const int P = a.snap[b].x, n = a.snap[b].y, t = P + n;
+  for (int e = tid; e < a.Hkv * 2 * kHeadDim; e += kThreads) {
+    const int gq = e / (2 * kHeadDim), r = e % (2 * kHeadDim), c = r & (kHeadDim - 1);
+    const size_t plane = (size_t)b * a.Hkv + gq;
+    uint16_t* ring = r < kHeadDim ? a.k_win : a.v_win;
+    const uint16_t* src = r < kHeadDim ? a.k_new : a.v_new;
+    ring[(plane * W + t % W) * kHeadDim + c] = src[plane * kHeadDim + c];
+  }
+  const bool evict = n + 1 == W && P < a.capacity;
+  if (evict) {
+    // the codebooks at constant indices (scalar loads of the kernel arguments)
+    float xk = 0.0f, xv = 0.0f, rk = 0.0f, rv = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      xk = L == i ? a.kcb.xi[i] : xk;
+      xv = L == i ? a.vcb.xi[i] : xv;
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      rk = L == i ? a.kcb.rho[i] : rk;
+      rv = L == i ? a.vcb.rho[i] : rv;
+    }
+    if (tid < K) {
+      cx_k[tid] = xk;
+      cx_v[tid] = xv;
+    }
+    if (tid < R) {
+      cr_k[tid] = rk;
+      cr_v[tid] = rv;
+    }
+    __syncthreads();
+    encoder_tables<BD, BN>(cx_k, cr_k, lut[0], midp[0], mid_rho[0], tid, kThreads);
+    const int vt = a.shared ? 0 : 1;
+    if (!a.shared) encoder_tables<BD, BN>(cx_v, cr_v, lut[1], midp[1], mid_rho[1], tid, kThreads);
+    __syncthreads();
+    for (int item = wave; item < 2 * a.Hkv; item += kMergeWaves) {
+      const int gq = item >> 1;
+      const bool v = item & 1;
+      const size_t plane = (size_t)b * a.Hkv + gq;
+      const uint16_t* src = n == 0 ? (v ? a.v_new : a.k_new) + plane * kHeadDim
+                                   : (v ? a.v_win : a.k_win) + (plane * W + P % W) * kHeadDim;
+      float* u = scratch[wave];
+      uint32_t* fld = reinterpret_cast<uint32_t*>(u + 132);
+      if (v)
+        encode_one<BD, BN>(src, lut[vt], midp[vt], mid_rho[vt], cr_v, a.vseed, a.v_rounding,
+                           false, a.v_idx, a.v_gamma, nullptr, nullptr, plane, a.capacity, P,
+                           u, fld);
+      else
+        encode_one<BD, BN>(src, lut[0], midp[0], mid_rho[0], cr_k, a.kseed, a.k_rounding,
+                           a.k_qjl != 0, a.k_idx, a.k_gamma, a.k_qjl_bits, a.k_gamma_r, plane,
+                           a.capacity, P, u, fld);
+      wave_sync();                       // the scratch is reused by the next item
+    }
+  }
+  if (tid == 0) {
+    a.packed_lens[b] = evict ? P + 1 : P;
+    a.win_lens[b] = n + 1 < W ? n + 1 : n;
+  }
+}
+
+// A step's merge: blocks (head, b) merge the scan's partials and fold in the
+// native rows of tokens P .. P + n (the last one the new token), wavefront w
+// taking tokens j = w, w + 8, ... with its own online softmax, four tokens'
+// loads in flight at a time; its sum goes into the value frame (x64) as the
+// scan's are.  Block (Hq, b) is the append workgroup.
+constexpr int kFoldChunk = 4;
+template <int BD, int BN>
+__global__ __launch_bounds__(kMergeWaves * 64) void step_merge_kernel(
+    const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc, int n_part, int Hq,
+    float* __restrict__ out, StepArgs a) {
+  const int b = blockIdx.y;
+  if ((int)blockIdx.x == Hq) {
+    append_block<BD, BN>(a, b);
+    return;
+  }
+  const int head = blockIdx.x, g = head / a.G;
+  const int W = a.window, P = a.snap[b].x, n = a.snap[b].y;
+  const size_t plane = (size_t)b * a.Hkv + g;
+  merge_head(ws_ml, ws_acc, n_part, Hq, a.vseed, out, head, b,
+             [&](int wave, int L, float& M, float& Lsum, float& a0, float& a1) {
+    const size_t qo = ((size_t)b * Hq + head) * kHeadDim;
+    float q0, q1;
+    if (a.q_bf16) {
+      q0 = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qo + L]);
+      q1 = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qo + L + 64]);
+    } else {
+      q0 = static_cast<const float*>(a.q)[qo + L];
+      q1 = static_cast<const float*>(a.q)[qo + L + 64];
+    }
+    float wm = -INFINITY, wl = 0.0f, w0 = 0.0f, w1 = 0.0f;
+    for (int j0 = wave; j0 <= n; j0 += kFoldChunk * kMergeWaves) {
+      uint16_t k0[kFoldChunk], k1[kFoldChunk], v0[kFoldChunk], v1[kFoldChunk];
+#pragma unroll
+      for (int c = 0; c < kFoldChunk; ++c) {
+        // tokens past the window read the new token's row (never used)
+        const int j = min(j0 + c * kMergeWaves, n);
+        const size_t row = (plane * W + (P + j) % W) * kHeadDim;
+        const uint16_t* kr = j == n ? a.k_new + plane * kHeadDim : a.k_win + row;
+        const uint16_t* vr = j == n ? a.v_new + plane * kHeadDim : a.v_win + row;
+        k0[c] = kr[L];
+        k1[c] = kr[L + 64];
+        v0[c] = vr[L];
+        v1[c] = vr[L + 64];
+      }
+#pragma unroll
+      for (int c = 0; c < kFoldChunk; ++c) {
+        if (j0 + c * kMergeWaves > n) break;
+        const float s =
+            a.scale * wave_sum(fmaf(q0, bf16_to_f32(k0[c]), q1 * bf16_to_f32(k1[c])));
+        const float mn = fmaxf(wm, s);
+        const float f = __expf(wm - mn), p = __expf(s - mn);
+        wl = fmaf(wl, f, p);
+        w0 = fmaf(w0, f, p * bf16_to_f32(v0[c]));
+        w1 = fmaf(w1, f, p * bf16_to_f32(v1[c]));
+        wm = mn;
+      }
+    }
+    if (wm != -INFINITY) {              // the same in every lane
+      // R_v v = H diag(s_v) v / sqrt(d), x64 like the scan's sums
+      float x0 = w0 * splitmix_sign(a.vseed, L), x1 = w1 * splitmix_sign(a.vseed, L + 64);
+      wht128(x0, x1);
+      const float mn = fmaxf(M, wm);
+      const float fa = M == -INFINITY ? 0.0f : __expf(M - mn), fb = __expf(wm - mn);
+      Lsum = fmaf(Lsum, fa, wl * fb);
+      a0 = fmaf(a0, fa, x0 * (kInvSqrtD * kUScale) * fb);
+      a1 = fmaf(a1, fa, x1 * (kInvSqrtD * kUScale) * fb);
+      M = mn;
+    }
+  });
+}
+
 struct Plan {
   int n_split, split_len;
-  size_t ml_bytes, acc_bytes, total;
+  size_t ml_bytes, acc_bytes, snap_bytes, total;
 };
 
 // Splits of `nw`-wave workgroups: about eight waves per CU in all, each
-// split a multiple of nw 32-token blocks; `extra` more partials per row (the
-// residual window of a step).
-Plan make_plan(int B, int Hq, int Hkv, int max_len, int nw, int extra) {
+// split a multiple of nw 32-token blocks; a step also keeps each sequence's
+// (P, n) after the partials.
+Plan make_plan(int B, int Hq, int Hkv, int max_len, int nw, bool step) {
   Plan p;
   const int units = B * Hkv;
   const int target_blocks = 256 * (8 / nw);
@@ -1082,10 +1133,11 @@ Plan make_plan(int B, int Hq, int Hkv, int max_len, int nw, int extra) {
   sl = (sl + quantum - 1) / quantum * quantum;
   p.split_len = max(sl, quantum);
   p.n_split = max(1, (max_len + p.split_len - 1) / p.split_len);
-  const size_t rows = (size_t)B * Hq * (p.n_split + extra);
+  const size_t rows = (size_t)B * Hq * p.n_split;
   p.ml_bytes = (rows * sizeof(float2) + 255) / 256 * 256;
   p.acc_bytes = rows * kHeadDim * sizeof(float);
-  p.total = p.ml_bytes + p.acc_bytes;
+  p.snap_bytes = step ? ((size_t)B * sizeof(int2) + 255) / 256 * 256 : 0;
+  p.total = p.ml_bytes + p.acc_bytes + p.snap_bytes;
   return p;
 }
 
@@ -1098,7 +1150,7 @@ int waves_for(int b_dir, int b_nrm, bool shared) {
 
 template <int BD, int BN, bool QJL>
 void launch_q(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.n_split + a.step, a.Hkv, a.B);
+  dim3 grid(a.n_split, a.Hkv, a.B);
   constexpr bool big = (1 << (2 * BD + BN)) > kMaxSmallPre;
   if constexpr (!big) {
     hipLaunchKernelGGL((decode_kernel<BD, BN, QJL, kPre, kWavesSmall>), grid, dim3(64 * kWavesSmall), 0, st, a);
@@ -1141,14 +1193,13 @@ static octo_status check_kv(const octo_codec_desc* k_codec, const octo_codec_des
 }
 
 // Checks shared by octo_attend_decode and octo_decode_step and the
-// arguments of the scan (no step fields).  `extra`: partials per row beyond
-// the splits.
+// arguments of the scan (no step fields but the snapshot's place).
 static octo_status prepare(const char* what, const octo_codec_desc* k_codec,
                            const octo_codec_desc* v_codec, const octo_cache_view* k_cache,
                            const octo_cache_view* v_cache, const void* q, octo_dtype q_dtype,
                            int32_t num_q_heads, const int32_t* seq_lens, int32_t max_seq_len,
                            float softmax_scale, float* out, void* workspace,
-                           size_t workspace_bytes, int extra, DecodeArgs* a, Codec* kc, Codec* vc) {
+                           size_t workspace_bytes, bool step, DecodeArgs* a, Codec* kc, Codec* vc) {
   octo_status s = check_kv(k_codec, v_codec, k_cache, v_cache, what, kc, vc);
   if (s != OCTO_OK) return s;
   if (q_dtype != OCTO_DTYPE_F32 && q_dtype != OCTO_DTYPE_BF16)
@@ -1173,7 +1224,7 @@ static octo_status prepare(const char* what, const octo_codec_desc* k_codec,
     return fail(OCTO_ERR_UNSUPPORTED, "%s: batch and heads must be <= 65535", what);
   const bool shared = std::memcmp(&kc->cb, &vc->cb, sizeof(Codebook)) == 0;
   const Plan p =
-      make_plan(B, num_q_heads, Hkv, max_seq_len, waves_for(kc->b_dir, kc->b_nrm, shared), extra);
+      make_plan(B, num_q_heads, Hkv, max_seq_len, waves_for(kc->b_dir, kc->b_nrm, shared), step);
   if (!workspace || workspace_bytes < p.total)
     return fail(OCTO_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", what,
                 workspace_bytes, p.total);
@@ -1204,10 +1255,11 @@ static octo_status prepare(const char* what, const octo_codec_desc* k_codec,
   a->capacity = k_cache->capacity;
   a->n_split = p.n_split;
   a->split_len = p.split_len;
-  a->n_part = p.n_split + extra;
+  a->n_part = p.n_split;
   char* ws = static_cast<char*>(workspace);
   a->ws_ml = reinterpret_cast<float2*>(ws);
   a->ws_acc = reinterpret_cast<float*>(ws + p.ml_bytes);
+  a->snap = step ? reinterpret_cast<int2*>(ws + p.ml_bytes + p.acc_bytes) : nullptr;
   return OCTO_OK;
 }
 
@@ -1227,7 +1279,7 @@ static octo_status launch_scan(const DecodeArgs& a, const Codec& kc, const char*
 
 static octo_status workspace_bytes_for(const char* what, const octo_codec_desc* k_codec,
                                        int32_t B, int32_t num_q_heads, int32_t kv_heads,
-                                       int32_t max_len, int extra, size_t* bytes) {
+                                       int32_t max_len, bool step, size_t* bytes) {
   Codec kc;
   octo_status s = resolve_codec(k_codec, what, &kc, false);
   if (s != OCTO_OK) return s;
@@ -1235,7 +1287,7 @@ static octo_status workspace_bytes_for(const char* what, const octo_codec_desc* 
   if (B < 1 || num_q_heads < 1 || kv_heads < 1 || max_len < 0)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: bad sizes", what);
   // the small-workgroup plan has the most splits: enough for either
-  *bytes = make_plan(B, num_q_heads, kv_heads, max_len, kWavesSmall, extra).total;
+  *bytes = make_plan(B, num_q_heads, kv_heads, max_len, kWavesSmall, step).total;
   return OCTO_OK;
 }
 
@@ -1244,7 +1296,7 @@ extern "C" octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_code
                                                    int32_t max_seq_len, size_t* bytes) {
   clear_error();
   return workspace_bytes_for("octo_decode_workspace_bytes", k_codec, B, num_q_heads, kv_heads,
-                             max_seq_len, 0, bytes);
+                             max_seq_len, false, bytes);
 }
 
 extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
@@ -1261,12 +1313,11 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
   Codec kc, vc;
   octo_status s = prepare(what, k_codec, v_codec, k_cache, v_cache, q, q_dtype, num_q_heads,
                           seq_lens, max_seq_len, softmax_scale, out, workspace, workspace_bytes,
-                          0, &a, &kc, &vc);
+                          false, &a, &kc, &vc);
   if (s != OCTO_OK) return s;
   if ((s = launch_scan(a, kc, what, stream)) != OCTO_OK) return s;
   hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, a.B), dim3(kMergeWaves * 64), 0, stream,
-                     a.ws_ml, a.ws_acc, a.n_part, num_q_heads, vc.seed, out,
-                     StepState{nullptr, nullptr, 0, 0, 0});
+                     a.ws_ml, a.ws_acc, a.n_part, num_q_heads, vc.seed, out);
   return check_launch(what);
 }
 
@@ -1275,7 +1326,7 @@ extern "C" octo_status octo_decode_step_workspace_bytes(const octo_codec_desc* k
                                                         int32_t max_packed_len, size_t* bytes) {
   clear_error();
   return workspace_bytes_for("octo_decode_step_workspace_bytes", k_codec, B, num_q_heads,
-                             kv_heads, max_packed_len, 1, bytes);
+                             kv_heads, max_packed_len, true, bytes);
 }
 
 extern "C" octo_status octo_decode_step(const octo_codec_desc* k_codec,
@@ -1295,34 +1346,62 @@ extern "C" octo_status octo_decode_step(const octo_codec_desc* k_codec,
   Codec kc, vc;
   octo_status s = prepare(what, k_codec, v_codec, k_cache, v_cache, q, q_dtype, num_q_heads,
                           packed_lens, max_packed_len, softmax_scale, out, workspace,
-                          workspace_bytes, 1, &a, &kc, &vc);
+                          workspace_bytes, true, &a, &kc, &vc);
   if (s != OCTO_OK) return s;
   if (window < 1 || window > kMaxWindow)
     return fail(OCTO_ERR_UNSUPPORTED, "%s: window %d outside [1, %d]", what, window, kMaxWindow);
   if (!k_new || !v_new || !k_window || !v_window || !window_lens)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: new rows, rings and window_lens must be set", what);
-  if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_window | (uintptr_t)v_window) & 1 ||
+  if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_window | (uintptr_t)v_window) & 15 ||
       ((uintptr_t)window_lens & 3))
     return fail(OCTO_ERR_ALIGNMENT, "%s: rows or window_lens misaligned", what);
   a.step = 1;
   a.window = window;
   a.win_lens = window_lens;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.k_win = k_window;
-  a.v_win = v_window;
-  a.k_idx_w = k_cache->idx;
-  a.k_qjl_w = k_cache->qjl;
-  a.k_gamma_w = k_cache->gamma;
-  a.k_gamma_r_w = k_cache->gamma_r;
-  a.v_idx_w = v_cache->idx;
-  a.v_gamma_w = v_cache->gamma;
-  a.k_rounding = kc.rounding;
-  a.v_rounding = vc.rounding;
   if ((s = launch_scan(a, kc, what, stream)) != OCTO_OK) return s;
-  hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, a.B), dim3(kMergeWaves * 64), 0, stream,
-                     a.ws_ml, a.ws_acc, a.n_part, num_q_heads, vc.seed, out,
-                     StepState{packed_lens, window_lens, window, max_packed_len,
-                               k_cache->capacity});
+  StepArgs st;
+  std::memset(&st, 0, sizeof(st));
+  st.snap = a.snap;
+  st.packed_lens = packed_lens;
+  st.win_lens = window_lens;
+  st.window = window;
+  st.capacity = k_cache->capacity;
+  st.Hkv = a.Hkv;
+  st.G = a.G;
+  st.q = q;
+  st.q_bf16 = a.q_bf16;
+  st.scale = a.scale;
+  st.k_new = k_new;
+  st.v_new = v_new;
+  st.k_win = k_window;
+  st.v_win = v_window;
+  st.kcb = kc.cb;
+  st.vcb = vc.cb;
+  st.shared = a.shared_tables;
+  st.kseed = kc.seed;
+  st.vseed = vc.seed;
+  st.k_rounding = kc.rounding;
+  st.v_rounding = vc.rounding;
+  st.k_qjl = kc.qjl;
+  st.k_idx = k_cache->idx;
+  st.k_qjl_bits = k_cache->qjl;
+  st.k_gamma = k_cache->gamma;
+  st.k_gamma_r = k_cache->gamma_r;
+  st.v_idx = v_cache->idx;
+  st.v_gamma = v_cache->gamma;
+  const dim3 grid(num_q_heads + 1, a.B), block(kMergeWaves * 64);
+#define OCTO_STEP_MERGE(BD, BN)                                                                   \
+  hipLaunchKernelGGL((step_merge_kernel<BD, BN>), grid, block, 0, stream, a.ws_ml, a.ws_acc, \
+                     a.n_part, num_q_heads, out, st)
+  switch (kc.b_dir * 10 + kc.b_nrm) {
+    case 31: OCTO_STEP_MERGE(3, 1); break;
+    case 42: OCTO_STEP_MERGE(4, 2); break;
+    case 53: OCTO_STEP_MERGE(5, 3); break;
+    case 22: OCTO_STEP_MERGE(2, 2); break;
+    case 33: OCTO_STEP_MERGE(3, 3); break;
+    case 44: OCTO_STEP_MERGE(4, 4); break;
+    default: return fail(OCTO_ERR_UNSUPPORTED, "%s: configuration not compiled", what);
+  }
+#undef OCTO_STEP_MERGE
   return check_launch(what);
 }

@@ -44,8 +44,7 @@ class Workload:
 
     @property
     def capacity(self):
-        # a decode-step workload keeps room for 1024 tokens leaving the window
-        total = self.T + self.chunk_q + (1024 if self.window else 0)
+        total = self.T + self.chunk_q
         return -(-total // 64) * 64
 
 
@@ -59,7 +58,7 @@ WORKLOADS = {
                         len_lo=4096, len_hi=8192),
     "long128k": Workload("long128k", "GQA 28/4, batch 4, context 131072, bf16, b=2 + QJL keys",
                          B=4, Hq=28, Hkv=4, d=128, T=131072, bits=2, dtype="bf16", qjl=True),
-    "step32k": Workload("step32k", "decode step, GQA 28/4, batch 1, context 32768 (last 32 tokens native), bf16 + outliers, b=4",
+    "step32k": Workload("step32k", "decode step, GQA 28/4, batch 1, context up to 32768 (last 32 tokens native), bf16 + outliers, b=4",
                         B=1, Hq=28, Hkv=4, d=128, T=32768, bits=4, dtype="bf16", outliers=True,
                         window=32),
     "chunk": Workload("chunk", "MHA 40 heads, d=128, 1560 queries over 9360 cached + 1560 current tokens, bf16, b=2",

@@ -172,13 +172,13 @@ def test_step_errors(L):
     n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
     assert L.octo_decode_workspace_bytes(ctypes.byref(kd), 2, 4, 2, 128, ctypes.byref(n0)) == 0
     assert L.octo_decode_step_workspace_bytes(ctypes.byref(kd), 2, 4, 2, 128, ctypes.byref(n1)) == 0
-    # one more partial per (batch, query head): 2 x 4 rows of one split and the
-    # window each, (m, l) pairs padded to 256 bytes, then 128 sums per partial
+    # 2 x 4 rows of one split: (m, l) pairs padded to 256 bytes, 128 sums per
+    # partial; a step adds each sequence's (P, n), padded to 256 bytes
     assert n0.value == 256 + 2 * 4 * 1 * 128 * 4
-    assert n1.value == 256 + 2 * 4 * 2 * 128 * 4
+    assert n1.value == n0.value + 256
     # the views below have batch 1: their workspace
     assert L.octo_decode_step_workspace_bytes(ctypes.byref(kd), 1, 4, 2, 128, ctypes.byref(n1)) == 0
-    assert n1.value == 256 + 4 * 2 * 128 * 4
+    assert n1.value == 256 + 4 * 128 * 4 + 256
     p = ctypes.c_void_p(4096)
 
     def st(window=32, k_new=p, ring=p, lens=p, wlens=p, ws_bytes=n1.value, max_len=128):
@@ -186,11 +186,13 @@ def test_step_errors(L):
                                   ctypes.byref(vv), p, 0, 4, k_new, p, ring, p, window, lens,
                                   wlens, max_len, 0.0, p, p, ws_bytes, None)
     assert st(window=0) == 2
-    assert st(window=65) == 2
+    assert st(window=257) == 2
     assert st(k_new=None) == 1
     assert st(wlens=None) == 1
     assert st(lens=None) == 1
     assert st(ring=ctypes.c_void_p(4097)) == 3
+    assert st(ring=ctypes.c_void_p(4104)) == 3               # rows are read 16 bytes at a time
+    assert st(k_new=ctypes.c_void_p(4104)) == 3
     assert st(wlens=ctypes.c_void_p(4098)) == 3
     assert st(ws_bytes=n1.value - 1) == 5
     assert st(max_len=129) == 4
