@@ -142,6 +142,18 @@ octo_status octo_encode(const octo_codec_desc* codec, const void* x, octo_dtype 
                         const octo_cache_view* dst, int32_t token_offset,
                         hipStream_t stream);
 
+/* octo_decode_tokens -- the explicit reconstruction of packed tokens:
+ * out[b, h, t - t0, :] = gamma R^T u^[:d] for t in [t0, t0 + T) of every
+ * plane (paper Sec. 3.6 Eq. 13 and App. C.14: the factorized score is
+ * q . x^).  For quality measurement and for callers that need dense vectors;
+ * the attention entry points never materialize K^.  With a QJL codec this is
+ * the MSE reconstruction alone (the sign sketch estimates inner products and
+ * reconstructs nothing).
+ *   out   device fp32 [B, H, T, d], contiguous.
+ * Tokens beyond capacity return OCTO_ERR_CAPACITY; T = 0 does nothing.      */
+octo_status octo_decode_tokens(const octo_codec_desc* codec, const octo_cache_view* cache,
+                               int32_t t0, int32_t T, float* out, hipStream_t stream);
+
 /* Workspace bytes needed by octo_attend_decode for these shapes.            */
 octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
                                         int32_t num_q_heads, int32_t kv_heads,

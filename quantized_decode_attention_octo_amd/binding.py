@@ -95,9 +95,11 @@ def lib():
                                        ctypes.POINTER(CacheView), ctypes.POINTER(CacheView),
                                        _P, ctypes.c_int, _I, _P, _P, _P, _P, _I, _P, _P, _I,
                                        ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+        L.octo_decode_tokens.argtypes = [ctypes.POINTER(CodecDesc), ctypes.POINTER(CacheView),
+                                         _I, _I, _P, _P]
         for f in ("octo_record_sizes", "octo_encode", "octo_decode_workspace_bytes",
                   "octo_attend_decode", "octo_chunk_workspace_bytes", "octo_attend_chunk",
-                  "octo_decode_step_workspace_bytes", "octo_decode_step"):
+                  "octo_decode_step_workspace_bytes", "octo_decode_step", "octo_decode_tokens"):
             getattr(L, f).restype = ctypes.c_int
         if L.octo_abi_version() != ABI_VERSION:
             raise RuntimeError("liboctopus.so ABI version mismatch")
@@ -197,6 +199,15 @@ def octo_encode(codec, x, cache, token_offset=0):
     dt = DTYPE_F32 if x.dtype == torch.float32 else DTYPE_BF16
     _check(lib().octo_encode(ctypes.byref(codec.desc), _ptr(x), dt, B, H, T, strides,
                              ctypes.byref(cache.view), token_offset, _stream(x.device)))
+
+
+def octo_decode_tokens(codec, cache, t0, T, out=None):
+    """Reconstructed tokens [t0, t0 + T) of every plane: out[B, H, T, d] fp32."""
+    if out is None:
+        out = torch.empty(cache.B, cache.H, T, 128, dtype=torch.float32, device=cache.gamma.device)
+    _check(lib().octo_decode_tokens(ctypes.byref(codec.desc), ctypes.byref(cache.view), t0, T,
+                                    _ptr(out), _stream(out.device)))
+    return out
 
 
 def octo_decode_workspace_bytes(k_codec, B, num_q_heads, kv_heads, max_seq_len):

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liboctopus.so")
-SOURCES = ["api.cpp", "encode.hip", "decode.hip", "chunk.hip"]
+SOURCES = ["api.cpp", "encode.hip", "decode.hip", "chunk.hip", "reconstruct.hip"]
 ARCH = "gfx950"
 
 

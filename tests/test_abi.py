@@ -199,6 +199,20 @@ def test_step_errors(L):
     assert b"octo_decode_step" in L.octo_last_error()
 
 
+def test_decode_tokens_errors(L):
+    """Host-side checks of octo_decode_tokens; no call here reaches a launch."""
+    kd = desc()
+    kv = view(H=2)
+    p = ctypes.c_void_p(4096)
+    assert L.octo_decode_tokens(ctypes.byref(kd), ctypes.byref(kv), 0, 0, p, None) == 0   # nothing to do
+    assert L.octo_decode_tokens(ctypes.byref(kd), ctypes.byref(kv), -1, 4, p, None) == 1
+    assert L.octo_decode_tokens(ctypes.byref(kd), ctypes.byref(kv), 100, 29, p, None) == 4  # past 128
+    assert L.octo_decode_tokens(ctypes.byref(kd), ctypes.byref(kv), 0, 4, None, None) == 1
+    assert L.octo_decode_tokens(ctypes.byref(kd), ctypes.byref(kv), 0, 4, ctypes.c_void_p(4098), None) == 3
+    assert L.octo_decode_tokens(ctypes.byref(desc(tables=False)), ctypes.byref(kv), 0, 4, p, None) == 1
+    assert L.octo_decode_tokens(ctypes.byref(kd), None, 0, 4, p, None) == 1
+
+
 def test_chunk_errors(L):
     kd, vd = desc(bits=2), desc(bits=2)
     kv, vv = view(H=2, cap=256), view(H=2, cap=256)
