@@ -25,14 +25,18 @@ and by exact attention as the bit width grows (tests/test_oracle_attention.py).
 """
 import numpy as np
 
-from .cache import read_tokens, u_hat_from_indices
+from . import group as grp
+from .cache import is_group, read_tokens, u_hat_from_indices
 from .rotation import qjl_rotation_matrix, rotation_matrix
 
 
 def reconstruct(cache, codec, b, h, t0, T):
-    """Explicit float64 vectors gamma R^T u^[:d] for tokens [t0, t0+T)."""
+    """Explicit float64 vectors gamma R^T u^[:d] (OCTOPUS) or R^T u^ (group
+    codec) for tokens [t0, t0+T)."""
     d = codec["d"]
     rec = read_tokens(cache, codec, b, h, t0, T)
+    if is_group(codec):
+        return grp.reconstruct(rec["codes"], rec["scale8"], rec["zero16"], codec["group"], codec["seed"]), rec
     u_hat = u_hat_from_indices(codec, rec["i_xi"], rec["i_eta"], rec["i_rho"])
     x_hat = rec["gamma"][:, None] * (u_hat[:, :d] @ rotation_matrix(d, codec["seed"]))
     return x_hat, rec

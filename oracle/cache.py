@@ -8,16 +8,26 @@ flat host arrays in the layout documented in oracle.pack:
   "gamma_r" uint16, [B, H, capacity] fp16 bit patterns  (only with QJL)
 
 The codec is described by a plain dict:
-  d, b_dir, b_nrm, seed, qjl (bool), c_xi, c_rho (float32 arrays), rounding.
+  d, b_dir, b_nrm, seed, qjl (bool), c_xi, c_rho (float32 arrays), rounding;
+or, for the group-wise value codec of oracle.group, kind="group", d, bits,
+group, seed.  A group cache has only the "idx" stream (codes, scales and
+zero-points in one record) and no "gamma".
 """
 import numpy as np
 
+from . import group as grp
 from . import pack
 from .encode import encode, n_triplets
 from .octahedral import oct_decode
 
 
+def is_group(codec):
+    return codec.get("kind") == "group"
+
+
 def stream_sizes(codec):
+    if is_group(codec):
+        return {"idx": grp.record_words(codec["d"], codec["bits"], codec["group"]), "qjl": 0}
     nt = n_triplets(codec["d"])
     return {
         "idx": pack.stream_words(nt, 2 * codec["b_dir"] + codec["b_nrm"]),
@@ -31,9 +41,10 @@ def empty_cache(codec, B, H, capacity):
     w = stream_sizes(codec)
     c = {
         "idx": np.zeros(B * H * capacity * w["idx"], dtype=np.uint32),
-        "gamma": np.zeros((B, H, capacity), dtype=np.float32),
         "B": B, "H": H, "capacity": capacity,
     }
+    if not is_group(codec):
+        c["gamma"] = np.zeros((B, H, capacity), dtype=np.float32)
     if codec.get("qjl"):
         c["qjl"] = np.zeros(B * H * capacity * w["qjl"], dtype=np.uint32)
         c["gamma_r"] = np.zeros((B, H, capacity), dtype=np.uint16)
@@ -47,6 +58,14 @@ def encode_into(cache, codec, x, token_offset=0):
     [B, H, T, ...] so that tests can compare decisions and margins."""
     B, H, T, d = x.shape
     flat = np.asarray(x, dtype=np.float64).reshape(B * H * T, d)
+    if is_group(codec):
+        enc = grp.encode(flat, codec["bits"], codec["group"], codec["seed"])
+        words = grp.pack_record(enc["codes"], enc["scale8"], enc["zero16"], codec["bits"])
+        for b in range(B):
+            for h in range(H):
+                sl = slice((b * H + h) * T, (b * H + h + 1) * T)
+                pack.scatter_tokens(cache["idx"], words[sl], b, h, token_offset, H, cache["capacity"])
+        return {k: v.reshape((B, H, T) + v.shape[1:]) for k, v in enc.items()}
     enc = encode(flat, codec["c_xi"], codec["c_rho"], codec["seed"],
                  rounding=codec.get("rounding", "local3x3"), qjl=codec.get("qjl", False))
     w = stream_sizes(codec)
@@ -72,6 +91,11 @@ def encode_at(cache, codec, x, b, h, token_offset):
     alone (the other planes are untouched).  Returns the encoder outputs."""
     x = np.asarray(x, dtype=np.float64)
     T, d = x.shape
+    if is_group(codec):
+        enc = grp.encode(x, codec["bits"], codec["group"], codec["seed"])
+        words = grp.pack_record(enc["codes"], enc["scale8"], enc["zero16"], codec["bits"])
+        pack.scatter_tokens(cache["idx"], words, b, h, token_offset, cache["H"], cache["capacity"])
+        return enc
     enc = encode(x, codec["c_xi"], codec["c_rho"], codec["seed"],
                  rounding=codec.get("rounding", "local3x3"), qjl=codec.get("qjl", False))
     w = stream_sizes(codec)
@@ -89,10 +113,13 @@ def encode_at(cache, codec, x, b, h, token_offset):
 
 def read_tokens(cache, codec, b, h, t0, T):
     """Indices and side data of tokens [t0, t0+T) of plane (b, h)."""
-    nt = n_triplets(codec["d"])
     w = stream_sizes(codec)
     H, cap = cache["H"], cache["capacity"]
     idxw = pack.gather_tokens(cache["idx"], b, h, t0, T, H, cap, w["idx"])
+    if is_group(codec):
+        codes, s8, z16 = grp.unpack_record(idxw, codec["d"], codec["bits"], codec["group"])
+        return {"codes": codes, "scale8": s8, "zero16": z16, "idx_words": idxw}
+    nt = n_triplets(codec["d"])
     f = pack.unpack_fields(idxw, nt, 2 * codec["b_dir"] + codec["b_nrm"])
     i_xi, i_eta, i_rho = pack.split_triplet_fields(f, codec["b_dir"], codec["b_nrm"])
     out = {

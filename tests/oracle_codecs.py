@@ -31,3 +31,8 @@ def codec(bits=3, seed=0, qjl=False, b_dir=None, b_nrm=None, rounding="local3x3"
         "c_xi": np.array(a["c_xi"][str(bd)], dtype=np.float32),
         "c_rho": np.array(a["c_rho"][str(bn)], dtype=np.float32),
     }
+
+
+def group_codec(bits=2, group=32, seed=0, d=128):
+    """Oracle dict of the group-wise value codec (oracle.group)."""
+    return {"kind": "group", "d": d, "bits": bits, "group": group, "seed": seed}
