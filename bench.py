@@ -193,6 +193,8 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
 
 def packed_bytes_per_token(codec):
     s = codec.sizes()
+    if codec.group:
+        return 4 * s.idx_words                        # codes, scales and zero-points
     b = 4 * s.idx_words + 4                           # index stream + gamma
     if codec.qjl:
         b += 4 * s.qjl_words + 2                      # sigma + fp16 gamma_r
@@ -226,10 +228,15 @@ class Timer:
         return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
 
 
+def value_codec(w):
+    """The workload's value codec: OCTOPUS, or the group-wise codec."""
+    return octo.Codec(bits=w.bits, group=w.v_group) if w.v_group else octo.Codec(bits=w.bits)
+
+
 def run_decode(w, steps, warmup):
     inp = make_inputs(w)
     kc = octo.Codec(bits=w.bits, qjl=w.qjl)
-    vc = octo.Codec(bits=w.bits)
+    vc = value_codec(w)
     K, V = inp["K"].cuda(), inp["V"].cuda()
     q, seq = inp["q"].cuda(), inp["seq_lens"].cuda()
     cap = w.capacity
@@ -431,9 +438,9 @@ def _host_plane(h, b, g):
     """Host cache of plane (b, g) alone, in the same layout with B = H = 1."""
     n = h["B"] * h["H"]
     p = b * h["H"] + g
-    out = {"B": 1, "H": 1, "capacity": h["capacity"],
-           "idx": h["idx"].reshape(n, -1)[p],
-           "gamma": h["gamma"][b:b + 1, g:g + 1]}
+    out = {"B": 1, "H": 1, "capacity": h["capacity"], "idx": h["idx"].reshape(n, -1)[p]}
+    if "gamma" in h:
+        out["gamma"] = h["gamma"][b:b + 1, g:g + 1]
     if "qjl" in h:
         out["qjl"] = h["qjl"].reshape(n, -1)[p]
         out["gamma_r"] = h["gamma_r"][b:b + 1, g:g + 1]
@@ -448,9 +455,10 @@ def cpu_baseline(w, state):
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import attention as oatt
     from oracle_codecs import codec as oracle_codec
+    from oracle_codecs import group_codec as oracle_group_codec
     inp, kc, vc, kcache, vcache = state[:5]
     hk = oracle_codec(bits=w.bits, qjl=w.qjl)
-    hv = oracle_codec(bits=w.bits)
+    hv = oracle_group_codec(bits=w.bits, group=w.v_group) if w.v_group else oracle_codec(bits=w.bits)
     hkc, hvc = kcache.to_host(), vcache.to_host()
     G = w.Hq // w.Hkv
     lens = inp["seq_lens"].numpy()
@@ -578,7 +586,8 @@ def main():
         "dtype": res["dtype"], "data": "synthetic (seeded Gaussian, see workloads.py)",
         "config": {"workload": f"{a.workload}: {w.name}", "batch": w.B, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.d, "context": w.T, "bits": w.bits,
-                   "qjl": w.qjl, "chunk_queries": w.chunk_q, "window": w.window},
+                   "qjl": w.qjl, "chunk_queries": w.chunk_q, "window": w.window,
+                   "value_group": w.v_group},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "attention_us": res["attention_us"], "encode_us": res["encode_us"],

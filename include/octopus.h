@@ -42,6 +42,24 @@
  * i.e. each 64-token tile keeps its W words as W rows of 64 consecutive words,
  * so that one wavefront reading word w of 64 tokens reads 256 contiguous bytes.
  * gamma (fp32) and gamma_r (fp16 bit pattern) are plain [B][H][capacity].
+ *
+ * Group-wise value codec (codec.group = 16 or 32).  The OCTOPUS paper's
+ * experiments share one value codec with a value-side group size of 16 or
+ * 32 (Sec. 4, default recipe; Sec. 4.2) without defining it; it is read from
+ * "Quantized Keys Steal Attention" (Sec. 3, quantization granularity and the
+ * Hadamard rotation; Sec. 4.3, FP8 E4M3 scales and BF16 zero-points,
+ * B_eff = b + 24/g; Sec. 5, asymmetric round-to-nearest):
+ *     u = R v (the same R = H diag(s) as above, /sqrt(d)), and per group j
+ *     of g consecutive coordinates: Delta = (max - min) / (2^b - 1) in fp32,
+ *     stored as E4M3 (round to nearest even, saturating at 448); z = min
+ *     stored as BF16 (round to nearest even); code c = clamp(rint((u_c - z) /
+ *     Delta), 0, 2^b - 1) in fp32 (0 where Delta rounds to 0);
+ *     v^ = R^T (Delta code + z).
+ * Its record is one index-stream record of W = (128 b + 24 * 128/g) / 32
+ * words: 128 fields of b bits (the codes, coordinate order), then 128/g
+ * fields of 8 bits (E4M3 scales), then 128/g fields of 16 bits (BF16
+ * zero-points), in the same tile-64 layout.  It has no gamma, QJL or
+ * codebooks.
  */
 #ifndef OCTOPUS_H
 #define OCTOPUS_H
@@ -54,7 +72,7 @@
 extern "C" {
 #endif
 
-#define OCTO_ABI_VERSION 3u
+#define OCTO_ABI_VERSION 4u
 
 typedef enum {
   OCTO_OK = 0,
@@ -89,7 +107,9 @@ typedef struct {
   int32_t b_nrm;          /* explicit bits per triplet norm, or 0              */
   int32_t rounding;       /* octo_rounding                                     */
   int32_t qjl;            /* 1: keys carry the QJL sign sketch (Sec. 3.6)      */
-  int32_t reserved;
+  int32_t group;          /* 0: OCTOPUS codec; 16 or 32: the group-wise value
+                             codec described above (bits in 2..4, b_dir =
+                             b_nrm = 0, no QJL, rounding and codebooks ignored)*/
   uint64_t seed;          /* rotation seed                                     */
   const float* c_xi;      /* host, 2^b_dir fp32 centroids, ascending           */
   const float* c_rho;     /* host, 2^b_nrm fp32 centroids, ascending           */
@@ -98,7 +118,7 @@ typedef struct {
 /* A packed cache for one tensor (K or V), layout OCTO_LAYOUT_TILE64.        */
 typedef struct {
   uint32_t* idx;          /* B*H*capacity*W_idx words                          */
-  float* gamma;           /* B*H*capacity                                      */
+  float* gamma;           /* B*H*capacity; unused (may be NULL) for a group codec */
   uint32_t* qjl;          /* B*H*capacity*W_qjl words, NULL unless codec.qjl   */
   uint16_t* gamma_r;      /* B*H*capacity fp16 bits, NULL unless codec.qjl     */
   int32_t batch;          /* B                                                 */
@@ -109,10 +129,11 @@ typedef struct {
 
 /* 32-bit words per token of each stream for a codec.                        */
 typedef struct {
-  int32_t idx_words;      /* ceil(n_triplets * (2*b_dir + b_nrm) / 32)         */
+  int32_t idx_words;      /* ceil(n_triplets * (2*b_dir + b_nrm) / 32); for a
+                             group codec the record's (128 b + 24*128/g) / 32   */
   int32_t qjl_words;
-  int32_t n_triplets;     /* ceil(d / 3)                                       */
-  int32_t b_dir;          /* the resolved split                                */
+  int32_t n_triplets;     /* ceil(d / 3); 0 for a group codec                  */
+  int32_t b_dir;          /* the resolved split (0, 0 for a group codec)       */
   int32_t b_nrm;
 } octo_stream_sizes;
 
@@ -129,7 +150,8 @@ octo_status octo_record_sizes(const octo_codec_desc* codec, octo_stream_sizes* o
  * token_offset + t of plane (b, h) of `dst`: gamma = ||x||_2, u = R x/gamma,
  * zero-pad to 3*ceil(d/3), triplets, octahedral map (Eq. 5), Lloyd seeds,
  * 3x3 joint rounding (or scalar rounding), packing; with codec.qjl also the
- * QJL signs of R'(u - u^) and gamma_r = fp16(||u - u^||).
+ * QJL signs of R'(u - u^) and gamma_r = fp16(||u - u^||).  With a group
+ * codec it writes the group record of R x instead (no gamma).
  *   x          device, element (b,h,t,e) at x + b*s0 + h*s1 + t*s2 + e*s3,
  *              x_strides = {s0,s1,s2,s3} in elements, s3 must be 1, the
  *              others >= 0; x aligned to its element size.
@@ -148,7 +170,7 @@ octo_status octo_encode(const octo_codec_desc* codec, const void* x, octo_dtype 
  * q . x^).  For quality measurement and for callers that need dense vectors;
  * the attention entry points never materialize K^.  With a QJL codec this is
  * the MSE reconstruction alone (the sign sketch estimates inner products and
- * reconstructs nothing).
+ * reconstructs nothing).  A group codec gives R^T (Delta code + z).
  *   out   device fp32 [B, H, T, d], contiguous.
  * Tokens beyond capacity return OCTO_ERR_CAPACITY; T = 0 does nothing.      */
 octo_status octo_decode_tokens(const octo_codec_desc* codec, const octo_cache_view* cache,
@@ -178,7 +200,11 @@ octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_codec, int32_t 
  * Both contractions run on MFMA with fp16 hi/lo operand pairs and fp32
  * accumulation (about 2^-20 relative per product); softmax and the merge of
  * the splits are fp32.  K and V caches must share B, kv_heads, capacity and
- * (b_dir, b_nrm); V must not carry QJL.                                      */
+ * (b_dir, b_nrm); V must not carry QJL.  V may instead use the group codec
+ * (group 16 or 32) when K uses the (b+1, b-1) split and V has the same b
+ * (the symmetric K = V bit width of the paper's comparisons); its products
+ * take Delta * code, exact in fp16, against the hi/lo weights, and the
+ * zero-point term sum_j p_j z_j in fp32.  K must use the OCTOPUS codec.      */
 octo_status octo_attend_decode(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
                                const octo_cache_view* k_cache, const octo_cache_view* v_cache,
                                const void* q, octo_dtype q_dtype, int32_t num_q_heads,
@@ -224,7 +250,7 @@ octo_status octo_decode_step_workspace_bytes(const octo_codec_desc* k_codec, int
  * lengths keep their values).  Two kernels: the scan of octo_attend_decode
  * over the packed tokens, then the merge, which folds in the native rows and
  * in which one more workgroup per sequence does steps 1 and 3 and updates
- * the lengths.                                                              */
+ * the lengths.  Codec combinations as for octo_attend_decode.                */
 octo_status octo_decode_step(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
                              const octo_cache_view* k_cache, const octo_cache_view* v_cache,
                              const void* q, octo_dtype q_dtype, int32_t num_q_heads,
@@ -255,7 +281,8 @@ octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B
  *              Tc == 0).
  *   out        device fp32 [B, num_q_heads, Tq, d].
  *   workspace  device, >= octo_chunk_workspace_bytes(...), 256-byte aligned.
- * Keys must not carry QJL in this path.  Operand range and precision: the
+ * Keys must not carry QJL in this path; values may use the group codec (as
+ * for octo_attend_decode).  Operand range and precision: the
  * fp16 staging requires |rotated entries| < 65504 and rounds each operand to
  * 11 significant bits, so this path is meant for inputs without large
  * outlier channels (the decode path computes in fp32).  Tq == 0 is a no-op;

@@ -25,7 +25,7 @@ with the rest):
     per group j of g consecutive coordinates of u:
       Delta  = (max_j - min_j) / (2^b - 1)                     (fp32)
       Delta^ = E4M3(Delta), round to nearest even, saturating at 448
-      z^     = BF16(min_j), round to nearest even
+      z^     = BF16(min_j), round to nearest even (a zero minimum as +0)
       q_c    = clamp(rint((u_c - z^) / Delta^), 0, 2^b - 1)    (fp32), 0 if Delta^ = 0
       u^_c   = Delta^ q_c + z^
     v^ = R^T u^.
@@ -128,7 +128,7 @@ def quantize_rotated(u32, bits, g):
     G = n_groups(d, g)
     levels = (1 << bits) - 1
     ug = u32.reshape(N, G, g)
-    mn = ug.min(axis=-1)
+    mn = ug.min(axis=-1) + np.float32(0.0)                # a zero minimum is +0 (reading)
     mx = ug.max(axis=-1)
     delta = (mx - mn) / np.float32(levels)                # fp32 subtract, fp32 divide
     s8, s_margin = to_e4m3(delta)

@@ -22,7 +22,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liboctopus.so")
 CODEBOOKS = os.path.join(PKG, "codebooks", "octopus_d{d}.json")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 STATUS = ["OCTO_OK", "OCTO_ERR_INVALID_ARGUMENT", "OCTO_ERR_UNSUPPORTED", "OCTO_ERR_ALIGNMENT",
           "OCTO_ERR_CAPACITY", "OCTO_ERR_WORKSPACE_TOO_SMALL", "OCTO_ERR_VERSION", "OCTO_ERR_HIP"]
 DTYPE_F32, DTYPE_BF16 = 0, 1
@@ -40,7 +40,7 @@ class CodecDesc(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_uint32), ("head_dim", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("b_dir", ctypes.c_int32), ("b_nrm", ctypes.c_int32),
                 ("rounding", ctypes.c_int32), ("qjl", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("group", ctypes.c_int32), ("seed", ctypes.c_uint64),
                 ("c_xi", ctypes.c_void_p), ("c_rho", ctypes.c_void_p)]
 
 
@@ -130,10 +130,20 @@ class Codec:
 
     bits: b; the split defaults to the paper's (b+1, b-1) (b_dir, b_nrm).
     The codebook values come from the shipped artifact (Lloyd-Max tables,
-    Sec. 3.4 of the OCTOPUS paper)."""
+    Sec. 3.4 of the OCTOPUS paper).  group = 16 or 32 selects the group-wise
+    value codec instead (b-bit codes, E4M3 scales, BF16 zero-points; no
+    codebooks)."""
 
     def __init__(self, bits=3, seed=0, qjl=False, b_dir=None, b_nrm=None,
-                 rounding=ROUND_LOCAL3X3, device="cuda", d=128, tables=None):
+                 rounding=ROUND_LOCAL3X3, device="cuda", d=128, tables=None, group=0):
+        self.group = int(group)
+        if self.group:
+            self.c_xi = self.c_rho = None
+            self.desc = CodecDesc(ABI_VERSION, d, bits, 0, 0, rounding, int(bool(qjl)), self.group,
+                                  seed, None, None)
+            self.bits, self.b_dir, self.b_nrm, self.seed, self.qjl = bits, 0, 0, seed, bool(qjl)
+            self.rounding, self.d, self.device = rounding, d, device
+            return
         if b_dir is None:
             b_dir, b_nrm = bits + 1, bits - 1
         art = tables or load_codebooks(d)
@@ -158,11 +168,14 @@ class PackedCache:
         n = B * H * capacity
         i32 = dict(dtype=torch.int32, device=device)
         self.idx = torch.zeros(n * s.idx_words, **i32)
-        self.gamma = torch.zeros(B, H, capacity, dtype=torch.float32, device=device)
+        # the group codec keeps its scales and zero-points in the record
+        self.gamma = (None if codec.group else
+                      torch.zeros(B, H, capacity, dtype=torch.float32, device=device))
         self.qjl = torch.zeros(n * s.qjl_words, **i32) if codec.qjl else None
         self.gamma_r = torch.zeros(B, H, capacity, dtype=torch.int16, device=device) if codec.qjl else None
         self.B, self.H, self.capacity, self.sizes = B, H, capacity, s
-        self.view = CacheView(self.idx.data_ptr(), self.gamma.data_ptr(),
+        self.device = self.idx.device
+        self.view = CacheView(self.idx.data_ptr(), self.gamma.data_ptr() if self.gamma is not None else None,
                               self.qjl.data_ptr() if self.qjl is not None else None,
                               self.gamma_r.data_ptr() if self.gamma_r is not None else None,
                               B, H, capacity, LAYOUT_TILE64)
@@ -174,8 +187,9 @@ class PackedCache:
     def to_host(self):
         """Host copies of the streams (numpy) in the layout the oracle reads."""
         out = {"idx": self.idx.cpu().numpy().view("<u4"),
-               "gamma": self.gamma.cpu().numpy(),
                "B": self.B, "H": self.H, "capacity": self.capacity}
+        if self.gamma is not None:
+            out["gamma"] = self.gamma.cpu().numpy()
         if self.qjl is not None:
             out["qjl"] = self.qjl.cpu().numpy().view("<u4")
             out["gamma_r"] = self.gamma_r.cpu().numpy().view("<u2")
@@ -204,7 +218,7 @@ def octo_encode(codec, x, cache, token_offset=0):
 def octo_decode_tokens(codec, cache, t0, T, out=None):
     """Reconstructed tokens [t0, t0 + T) of every plane: out[B, H, T, d] fp32."""
     if out is None:
-        out = torch.empty(cache.B, cache.H, T, 128, dtype=torch.float32, device=cache.gamma.device)
+        out = torch.empty(cache.B, cache.H, T, 128, dtype=torch.float32, device=cache.device)
     _check(lib().octo_decode_tokens(ctypes.byref(codec.desc), ctypes.byref(cache.view), t0, T,
                                     _ptr(out), _stream(out.device)))
     return out

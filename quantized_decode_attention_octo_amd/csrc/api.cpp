@@ -45,6 +45,29 @@ octo_status resolve_codec(const octo_codec_desc* d, const char* what, Codec* out
                 d->head_dim);
   if (d->head_dim != kHeadDim)
     return fail(OCTO_ERR_UNSUPPORTED, "%s: head_dim %d (only 128 is compiled)", what, d->head_dim);
+  if (d->group != 0) {
+    // the group-wise value codec: codes, E4M3 scales and BF16 zero-points
+    if (d->group < 0) return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: group %d is negative", what, d->group);
+    if (d->group != 16 && d->group != 32)
+      return fail(OCTO_ERR_UNSUPPORTED, "%s: group size %d (16 and 32 are compiled)", what, d->group);
+    if (d->bits < 1 || d->bits > 8)
+      return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: bits %d out of range", what, d->bits);
+    if (d->bits < 2 || d->bits > 4)
+      return fail(OCTO_ERR_UNSUPPORTED, "%s: group codec bits %d (2, 3 and 4 are compiled)", what,
+                  d->bits);
+    if (d->b_dir != 0 || d->b_nrm != 0)
+      return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: b_dir and b_nrm must be 0 with a group codec", what);
+    if (d->qjl != 0)
+      return fail(OCTO_ERR_UNSUPPORTED, "%s: the group codec carries no QJL sketch", what);
+    Codec g;
+    std::memset(&g, 0, sizeof(g));
+    g.group = d->group;
+    g.bits = d->bits;
+    g.w_idx = group_record_words(d->bits, d->group);
+    g.seed = d->seed;
+    *out = g;
+    return OCTO_OK;
+  }
   int bd = d->b_dir, bn = d->b_nrm;
   if (bd == 0 && bn == 0) {
     if (d->bits < 1 || d->bits > 8)
@@ -76,6 +99,8 @@ octo_status resolve_codec(const octo_codec_desc* d, const char* what, Codec* out
       if (!std::isfinite(cb.rho[i]) || (i > 0 && !(cb.rho[i] > cb.rho[i - 1])))
         return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: c_rho is not finite and ascending", what);
   }
+  out->group = 0;
+  out->bits = bd == bn ? bd : bd - 1;
   out->b_dir = bd;
   out->b_nrm = bn;
   out->K = 1 << bd;
@@ -99,11 +124,11 @@ octo_status check_cache(const octo_cache_view* v, const Codec& c, const char* wh
   if (v->capacity % 64)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: capacity %d is not a multiple of 64", what,
                 v->capacity);
-  if (!v->idx || !v->gamma)
+  if (!v->idx || (!c.group && !v->gamma))
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: stream pointer is NULL", what);
   if (c.qjl && (!v->qjl || !v->gamma_r))
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: QJL codec needs qjl and gamma_r streams", what);
-  uintptr_t a = (uintptr_t)v->idx | (uintptr_t)v->gamma;
+  uintptr_t a = (uintptr_t)v->idx | (c.group ? 0 : (uintptr_t)v->gamma);
   if (c.qjl) a |= (uintptr_t)v->qjl;
   if (a & 15) return fail(OCTO_ERR_ALIGNMENT, "%s: streams must be 16-byte aligned", what);
   if (c.qjl && ((uintptr_t)v->gamma_r & 1))
@@ -147,7 +172,7 @@ octo_status octo_record_sizes(const octo_codec_desc* codec, octo_stream_sizes* o
   if (s != OCTO_OK) return s;
   out->idx_words = c.w_idx;
   out->qjl_words = c.w_qjl;
-  out->n_triplets = octo::kNTri;
+  out->n_triplets = c.group ? 0 : octo::kNTri;
   out->b_dir = c.b_dir;
   out->b_nrm = c.b_nrm;
   return OCTO_OK;

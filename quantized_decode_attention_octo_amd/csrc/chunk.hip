@@ -16,7 +16,8 @@
 //   1. rotate_rows (x3): q, k_cur -> fp16 rotated rows; v_cur -> fp16 rotated
 //      columns of the transposed value matrix
 //   2. decode_rows (x2): cached keys -> fp16 gamma u^ rows; cached values ->
-//      columns of the transposed value matrix
+//      columns of the transposed value matrix (with the group-wise value
+//      codec, Delta code + z, already the rotated value)
 //   3. chunk_attn: fp16 MFMA flash attention (fp32 accumulation, online
 //      softmax), epilogue 1/l and R_v^T; XCD-aware workgroup order.
 // The window is decoded once per call and shared by every query tile.
@@ -404,6 +405,57 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
   }
 }
 
+// The group-wise value codec: one workgroup per 64 cached tokens of a plane
+// stages their records (word w of the 64 tokens is 256 contiguous bytes) in
+// LDS, then lanes take (token, coordinate) items token-fastest and write
+// fp16(Delta code + z), the rotated value, into the tile stored as above.
+template <int VB, int GS, bool TRANSPOSED>
+__global__ __launch_bounds__(256) void group_decode_rows_kernel(const uint32_t* __restrict__ idx,
+                                                                int capacity, int cached,
+                                                                _Float16* __restrict__ out,
+                                                                int out_rows) {
+  constexpr int G = kHeadDim / GS, WC = VB * kHeadDim / 32, W = group_record_words(VB, GS);
+  constexpr int kRow = 136;
+  __shared__ uint32_t rec[W * 64];
+  __shared__ __attribute__((aligned(16))) _Float16 tile[64 * kRow];
+  const int tid = threadIdx.x;
+  const size_t plane = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  const int nt = min(64, cached - t0);
+  for (int e = tid; e < W * 64; e += 256) {
+    const int w = e >> 6, k = e & 63;
+    rec[e] = k < nt ? idx[tile_word(plane, capacity, t0 + k, w, W)] : 0u;
+  }
+  __syncthreads();
+  for (int e = tid; e < 64 * kHeadDim; e += 256) {
+    const int k = e & 63, c = e >> 6;
+    const int pos = c * VB, w = pos >> 5, sh = pos & 31;
+    const uint32_t lo = rec[w * 64 + k];
+    const uint32_t hi = sh + VB > 32 ? rec[(w + 1) * 64 + k] : 0u;
+    const uint32_t q = (uint32_t)((((uint64_t)hi << 32) | lo) >> sh) & ((1u << VB) - 1u);
+    const int j = c / GS;
+    const uint32_t sw = rec[(WC + j / 4) * 64 + k], zw = rec[(WC + G / 4 + j / 2) * 64 + k];
+    const float dh = e4m3_value((sw >> (8 * (j % 4))) & 0xffu);
+    const float zh = __uint_as_float(((zw >> (16 * (j % 2))) & 0xffffu) << 16);
+    tile[k * kRow + c] = (_Float16)fmaf(dh, (float)q, zh);
+  }
+  __syncthreads();
+  if (TRANSPOSED) {
+    for (int e = tid; e < 64 * kHeadDim; e += 256) {
+      const int c = e >> 6, k = e & 63;
+      if (k < nt) out[(plane * kHeadDim + c) * out_rows + key_column(t0 + k)] = tile[k * kRow + c];
+    }
+  } else {
+    typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+    for (int e = tid; e < 64 * 16; e += 256) {
+      const int k = e >> 4, c8 = (e & 15) * 8;
+      if (k < nt)
+        *reinterpret_cast<half8v*>(out + (plane * out_rows + t0 + k) * kHeadDim + c8) =
+            *reinterpret_cast<const half8v*>(&tile[k * kRow + c8]);
+    }
+  }
+}
+
 struct ChunkPlan {
   int Tk, Tk_pad;
   size_t q_off, k_off, v_off, total;
@@ -434,8 +486,31 @@ void launch_decode_rows(const octo_cache_view* c, const Codec& cd, int cached, _
                        c->gamma, cd.cb, c->capacity, cached, out, out_rows);
 }
 
+template <int VB, int GS>
+void launch_group_rows(const octo_cache_view* c, int cached, _Float16* out, int out_rows,
+                       bool transposed, hipStream_t st) {
+  dim3 grid((cached + 63) / 64, c->batch * c->kv_heads);
+  if (transposed)
+    hipLaunchKernelGGL((group_decode_rows_kernel<VB, GS, true>), grid, dim3(256), 0, st, c->idx,
+                       c->capacity, cached, out, out_rows);
+  else
+    hipLaunchKernelGGL((group_decode_rows_kernel<VB, GS, false>), grid, dim3(256), 0, st, c->idx,
+                       c->capacity, cached, out, out_rows);
+}
+
 bool decode_rows(const octo_cache_view* c, const Codec& cd, int cached, _Float16* out,
                  int out_rows, bool transposed, hipStream_t st) {
+  if (cd.group) {
+    switch (cd.bits * 100 + cd.group) {
+      case 216: launch_group_rows<2, 16>(c, cached, out, out_rows, transposed, st); return true;
+      case 232: launch_group_rows<2, 32>(c, cached, out, out_rows, transposed, st); return true;
+      case 316: launch_group_rows<3, 16>(c, cached, out, out_rows, transposed, st); return true;
+      case 332: launch_group_rows<3, 32>(c, cached, out, out_rows, transposed, st); return true;
+      case 416: launch_group_rows<4, 16>(c, cached, out, out_rows, transposed, st); return true;
+      case 432: launch_group_rows<4, 32>(c, cached, out, out_rows, transposed, st); return true;
+    }
+    return false;
+  }
   switch (cd.b_dir * 10 + cd.b_nrm) {
     case 31: launch_decode_rows<3, 1>(c, cd, cached, out, out_rows, transposed, st); return true;
     case 42: launch_decode_rows<4, 2>(c, cd, cached, out, out_rows, transposed, st); return true;
@@ -460,6 +535,8 @@ extern "C" octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec
   Codec kc;
   octo_status s = resolve_codec(k_codec, "octo_chunk_workspace_bytes", &kc, false);
   if (s != OCTO_OK) return s;
+  if (kc.group)
+    return fail(OCTO_ERR_UNSUPPORTED, "octo_chunk_workspace_bytes: keys need the OCTOPUS codec");
   if (!bytes) return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_chunk_workspace_bytes: bytes is NULL");
   if (B < 1 || num_q_heads < 1 || kv_heads < 1 || Tq < 0 || cached_tokens < 0 || Tc < 0)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_chunk_workspace_bytes: bad sizes");
@@ -484,6 +561,7 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   if ((s = check_cache(k_cache, kc, what)) != OCTO_OK) return s;
   if ((s = check_cache(v_cache, vc, what)) != OCTO_OK) return s;
   if (kc.qjl || vc.qjl) return fail(OCTO_ERR_UNSUPPORTED, "%s: QJL is not supported here", what);
+  if (kc.group) return fail(OCTO_ERR_UNSUPPORTED, "%s: keys need the OCTOPUS codec", what);
   if (k_cache->batch != v_cache->batch || k_cache->kv_heads != v_cache->kv_heads ||
       k_cache->capacity != v_cache->capacity)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: K and V caches differ in shape", what);

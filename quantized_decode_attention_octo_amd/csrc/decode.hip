@@ -93,6 +93,7 @@ struct DecodeArgs {
   float scale;
   Codebook kcb, vcb;   // C_xi, C_rho of K and of V
   int shared_tables;   // K and V use the same codebook values
+  int v_group;         // 0, or the group size of the group-wise value codec
   uint64_t kseed, vseed;
   const uint32_t *k_idx, *kqjl, *v_idx;   // index streams, K sign stream
   const float *kgamma, *vgamma;
@@ -212,11 +213,22 @@ constexpr int kIdxRows = 44;          // 43 triplets + the spare
 // cover the triplets of lane group grp4 (and word grp4 of its sign record);
 // value side: lane L holds the record words of token L % 32 that cover
 // triplets 22 (L / 32) .. + 21.
-template <int BD, int BN, bool QJL>
+// With the group-wise value codec (VG = its group size) lane L instead holds
+// words 2 k + L / 32 of token L % 32's value record (VW words).
+template <int VB, int VG>
+struct GroupRecord {
+  static constexpr int G = kHeadDim / VG;             // groups per token
+  static constexpr int WC = VB * kHeadDim / 32;       // code words
+  static constexpr int W = group_record_words(VB, VG);
+  static constexpr int kRows = WC + G;                // LDS rows: codes, fp16 scales, zeros
+};
+
+template <int BD, int BN, bool QJL, int VG = 0>
 struct BlockWords {
   static constexpr int BT = 2 * BD + BN;            // bits of one triplet field
   static constexpr int WI = (kNTri * BT + 31) / 32;
-  static constexpr int KWI = group_words(BT), KVI = value_words(BT);
+  static constexpr int VW = VG ? group_record_words(BD - 1, VG) : 0;
+  static constexpr int KWI = group_words(BT), KVI = VG ? (VW + 1) / 2 : value_words(BT);
   uint32_t iw[2][KWI], sw[2];
   uint32_t vi[KVI];
   float4 gk[2], gv[2];
@@ -229,10 +241,10 @@ struct BlockWords {
 // apart: one base address per stream and immediate offsets; a group's window
 // is clamped to the record (the words past its end only ever feed bits above
 // the last field).
-template <int BD, int BN, bool QJL>
-__device__ inline void load_block(BlockWords<BD, BN, QJL>& r, const DecodeArgs& a, size_t plane,
+template <int BD, int BN, bool QJL, int VG>
+__device__ inline void load_block(BlockWords<BD, BN, QJL, VG>& r, const DecodeArgs& a, size_t plane,
                                   int t0, int L) {
-  using BW = BlockWords<BD, BN, QJL>;
+  using BW = BlockWords<BD, BN, QJL, VG>;
   constexpr int BT = BW::BT, WI = BW::WI;
   const int col = L & 15, grp4 = L >> 4, w0 = L >> 5, tk = L & 31;
   const int iwo = (kTriPerGroup * BT * grp4) >> 5;
@@ -248,19 +260,28 @@ __device__ inline void load_block(BlockWords<BD, BN, QJL>& r, const DecodeArgs& 
     r.gk[kt] = *reinterpret_cast<const float4*>(a.kgamma + gbase + 16 * kt);
     if (QJL) r.gr[kt] = *reinterpret_cast<const uint2*>(a.kgamma_r + gbase + 16 * kt);
   }
-  const int vwo = (kValTri * BT * w0) >> 5;
-  const uint32_t* pvi = a.v_idx + tile * (WI * 64) + tin + tk;
+  if constexpr (VG != 0) {
+    // value records: word 2 k + w0 of token tk (the spare slot of an odd
+    // record re-reads its last word)
+    const uint32_t* pvi = a.v_idx + tile * (BW::VW * 64) + tin + tk;
 #pragma unroll
-  for (int w = 0; w < BW::KVI; ++w) r.vi[w] = pvi[64 * min(vwo + w, WI - 1)];
+    for (int k = 0; k < BW::KVI; ++k) r.vi[k] = pvi[64 * min(2 * k + w0, BW::VW - 1)];
+  } else {
+    const int vwo = (kValTri * BT * w0) >> 5;
+    const uint32_t* pvi = a.v_idx + tile * (WI * 64) + tin + tk;
+#pragma unroll
+    for (int w = 0; w < BW::KVI; ++w) r.vi[w] = pvi[64 * min(vwo + w, WI - 1)];
+  }
 }
 
 // The value norms of the block at t0, loaded apart from the rest: the
 // softmax still reads the current block's norms when the next block's
 // words are requested, and a separate load keeps the two sets from being
 // live at once (which costs register copies at the end of every iteration).
-template <int BD, int BN, bool QJL>
-__device__ inline void load_gv(BlockWords<BD, BN, QJL>& r, const DecodeArgs& a, size_t plane,
+template <int BD, int BN, bool QJL, int VG>
+__device__ inline void load_gv(BlockWords<BD, BN, QJL, VG>& r, const DecodeArgs& a, size_t plane,
                                int t0, int L) {
+  if constexpr (VG != 0) return;           // the group codec has no value norms
   const size_t gbase = plane * (size_t)a.capacity + (size_t)t0 + 4 * (L >> 4);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
@@ -409,14 +430,16 @@ __device__ void encode_one(const uint16_t* x, const floatx4* lut, const float* m
   }
 }
 
-template <int BD, int BN, bool QJL, int MODE, int NW>
+template <int BD, int BN, bool QJL, int MODE, int NW, int VG = 0>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * NW, kWaves = NW;
   constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD, BT = FWD + BN;
   constexpr bool PRE = MODE == kPre;                // pre-split (code, rho) table
   constexpr bool BIG = K * K * R > kMaxSmallPre;    // one shared table, one WG per CU
   constexpr int kTab = PRE ? K * K * R : K * K;     // entries per table (16 B each)
-  constexpr int kTabBytes = (PRE && BIG ? 1 : 2) * kTab * 16;
+  constexpr int kTabBytes = (VG || (PRE && BIG) ? 1 : 2) * kTab * 16;   // VG: the K table alone
+  using GR = GroupRecord<(VG ? BD - 1 : 2), (VG ? VG : 32)>;            // the value record (VG)
+  static_assert(GR::kRows * 32 * 4 <= kIdxRows * kIdxRow * 2, "value records fit a wave's rows");
   constexpr int kRedBytes = kWaves * kMaxG * kHeadDim * 4;
   constexpr int kUnion = kTabBytes > kRedBytes ? kTabBytes : kRedBytes;
 
@@ -429,6 +452,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char qbuf[kQsBytes > kIdxBytes ? kQsBytes : kIdxBytes];
   float* qs = reinterpret_cast<float*>(qbuf);
   __shared__ float red_ml[kWaves * kMaxG * 2];
+  // group codec: per-wave zero-point sums of each (head, group)
+  __shared__ float red_z[VG ? kWaves * kMaxG * GR::G : 1];
 
   const int tid = threadIdx.x, L = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -480,7 +505,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   }
   const int t_begin = split * a.split_len;
   int t0 = t_begin + wave * kBlock;
-  BlockWords<BD, BN, QJL> blk;
+  BlockWords<BD, BN, QJL, VG> blk;
   if (!QJL && t0 < min(a.max_len, a.capacity)) {
     load_block(blk, a, plane, t0, L);
     load_gv(blk, a, plane, t0, L);
@@ -502,7 +527,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     crv[tid] = cr_v;
   }
   lds_barrier();
-  const int n_tables = PRE || !a.shared_tables ? 2 : 1;
+  const int n_tables = VG ? 1 : (PRE || !a.shared_tables ? 2 : 1);
   // pre-split tables are rho-major, entry rho_index K^2 + code pair, so that
   // consecutive lanes write consecutive entries
   constexpr int KK = K * K;
@@ -612,6 +637,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   for (int i = 0; i < 3; ++i)
 #pragma unroll
     for (int c = 0; c < 3; ++c) o[i][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  // group codec: tile c holds columns 16 c .. 16 c + 15 (one group), and
+  // zacc[j] the running sum of 64 p z of group j over this lane's tokens
+  floatx4 og[8];
+  float zacc[GR::G];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) og[c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < GR::G; ++j) zacc[j] = 0.0f;
+  uint32_t* vrec = reinterpret_cast<uint32_t*>(qbuf) + wave * (kIdxRows * kIdxRow / 2);
   float m_run = -INFINITY, l_run = 0.0f;            // of head `col`
   const float qjl_c = 1.2533141373155003f * kInvSqrtD;   // sqrt(pi / 2) / sqrt(d)
   uint16_t* vidx = reinterpret_cast<uint16_t*>(qbuf) + wave * (kIdxRows * kIdxRow);
@@ -630,8 +664,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     // -- value-side triplet fields, code | rho index << 2 b_dir (the entry of
     //    a pre-split table), into this wavefront's rows (the previous block's
     //    reads of them ended at the wave_sync closing its iteration)
-    {
-      using BW = BlockWords<BD, BN, QJL>;
+    if constexpr (!VG) {
+      using BW = BlockWords<BD, BN, QJL, VG>;
       const int h = L >> 5, tk = L & 31;
       const uint32_t ish = (kValTri * BT * h) & 31;
       uint32_t ri[BW::KVI];
@@ -642,12 +676,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < kValTri; ++j) row[j * kIdxRow] = (uint16_t)field<BT>(ri, j * BT);
     }
+    else {
+      // the group records of the block's 32 tokens as rows of 32 words:
+      // code words as they are, each scale word as two rows of fp16 scales
+      // (exact: every E4M3 value is an fp16 value), zero-point words as they
+      // are.  Row r, token tk at vrec[32 r + tk].
+      using BW = BlockWords<BD, BN, QJL, VG>;
+      const int h = L >> 5, tk = L & 31;
+#pragma unroll
+      for (int k = 0; k < BW::KVI; ++k) {
+        const int w = 2 * k + h;
+        const uint32_t x = blk.vi[k];
+        if (w >= GR::W) continue;
+        if (w >= GR::WC && w < GR::WC + GR::G / 4) {
+          const int r = GR::WC + 2 * (w - GR::WC);
+          const fp16x2 lo = {(__fp16)e4m3_value(x & 0xffu), (__fp16)e4m3_value((x >> 8) & 0xffu)};
+          const fp16x2 hi = {(__fp16)e4m3_value((x >> 16) & 0xffu), (__fp16)e4m3_value(x >> 24)};
+          vrec[32 * r + tk] = pk(lo);
+          vrec[32 * (r + 1) + tk] = pk(hi);
+        } else {
+          vrec[32 * (w < GR::WC ? w : w + GR::G / 4) + tk] = x;
+        }
+      }
+    }
     // -- scores, two 16-token tiles
     floatx4 sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       // shift the group's window so that its triplet j starts at bit j B_tri
-      using BW = BlockWords<BD, BN, QJL>;
+      using BW = BlockWords<BD, BN, QJL, VG>;
       const uint32_t ish = (kTriPerGroup * BT * grp4) & 31;
       uint32_t iw[BW::KWI];
 #pragma unroll
@@ -749,7 +806,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     float pw[8], psum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const float gva[4] = {blk.gv[kt].x, blk.gv[kt].y, blk.gv[kt].z, blk.gv[kt].w};
+      // group codec: the weights carry the exact factor 64 of the frame
+      const float gva[4] = {VG ? kUScale : blk.gv[kt].x, VG ? kUScale : blk.gv[kt].y,
+                            VG ? kUScale : blk.gv[kt].z, VG ? kUScale : blk.gv[kt].w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = sc[kt][r] == -INFINITY ? 0.0f : __expf(sc[kt][r] - m_new);
@@ -775,46 +834,121 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
       float al[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp4 + r, 64);
+      if constexpr (VG != 0) {
 #pragma unroll
-      for (int i = 0; i < 3; ++i)
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int c = 0; c < 3; ++c)
+          for (int r = 0; r < 4; ++r) og[c][r] *= al[r];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[i][c][r] *= al[r];
+        for (int j = 0; j < GR::G; ++j) zacc[j] *= alpha;      // this lane's head: col
+      } else {
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+          for (int c = 0; c < 3; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[i][c][r] *= al[r];
+      }
     }
     // -- values: triplet 16 grp + col for this lane group's 8 tokens
     wave_sync();
+    if constexpr (VG != 0) {
+      // group codec.  Slot e of this lane group is token
+      // tok(e) = 16 (e / 4) + 4 grp4 + e % 4 of the block (the score layout).
+      // Tile c: B[e][col] = Delta code of column 16 c + col, exact in fp16
+      // (an E4M3 scale times an integer below 16 has at most 7 significant
+      // bits), so the products against the hi/lo weights are exact in the
+      // fp32 accumulation; the zero-point adds sum_e 64 p_e z_e per group.
+      constexpr int VB = BD - 1, kMask = (1 << VB) - 1;
+      constexpr int kTilesPerGroup = VG / 16;
+      const uint32_t* rq0 = vrec + 4 * grp4;                 // tokens 4 grp4 + (0..3)
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      // with QJL the registers are short: one value tile at a time
-      if (QJL) __builtin_amdgcn_sched_barrier(0);
-      // indices of tokens 4 grp4 + (0..3) and 16 + 4 grp4 + (0..3): slots e
-      const uint2 p0 = *reinterpret_cast<const uint2*>(vidx + vrow[i]);
-      const uint2 p1 = *reinterpret_cast<const uint2*>(vidx + vrow[i] + 16);
-      const uint32_t pw2[4] = {p0.x, p0.y, p1.x, p1.y};
-      half8 bh[3], bl[3];
-      if (PRE) {
-        uint4 E[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) E[e] = tabv[(pw2[e >> 1] >> (16 * (e & 1))) & 0xffffu];
-        operands_pre(E, bh, bl);
-      } else {
-        float vx[8], vy[8], vz[8];
+      for (int j = 0; j < GR::G; ++j) {
+        // fp16 scales (row WC + j / 2, half j % 2) and zero-points
+        // (row WC + G / 2 + j / 2, half j % 2) of the 8 slots
+        const uint4 d0 = *reinterpret_cast<const uint4*>(rq0 + 32 * (GR::WC + j / 2));
+        const uint4 d1 = *reinterpret_cast<const uint4*>(rq0 + 32 * (GR::WC + j / 2) + 16);
+        const uint4 z0 = *reinterpret_cast<const uint4*>(rq0 + 32 * (GR::WC + GR::G / 2 + j / 2));
+        const uint4 z1 = *reinterpret_cast<const uint4*>(rq0 + 32 * (GR::WC + GR::G / 2 + j / 2) + 16);
+        const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        const uint32_t zw[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+        float zs = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t idx = (pw2[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          const uint4 n = tabv[idx & (KK - 1)];
-          const float rho = crv[idx >> FWD];
-          vx[e] = rho * __uint_as_float(n.x);
-          vy[e] = rho * __uint_as_float(n.y);
-          vz[e] = rho * __uint_as_float(n.z);
+          const float z = __uint_as_float(j & 1 ? (zw[e] & 0xffff0000u) : (zw[e] << 16));
+          zs = fmaf(pw[e], z, zs);
         }
-        split8(vx, bh[0], bl[0]);
-        split8(vy, bh[1], bl[1]);
-        split8(vz, bh[2], bl[2]);
-      }
+        zacc[j] += zs;
+        fp16x2 dp[4];
 #pragma unroll
-      for (int c = 0; c < 3; ++c) o[i][c] = mfma3(pah, pal, bh[c], bl[c], o[i][c]);
+        for (int m = 0; m < 4; ++m)
+          dp[m] = __builtin_bit_cast(fp16x2, j & 1 ? pair_hi(dw[2 * m], dw[2 * m + 1])
+                                                   : pair_lo(dw[2 * m], dw[2 * m + 1]));
+#pragma unroll
+        for (int cc = 0; cc < kTilesPerGroup; ++cc) {
+          const int c = j * kTilesPerGroup + cc;
+          // the code of column 16 c + col starts at bit pos of the record
+          const int pos = (16 * c + col) * VB, wr = pos >> 5, sh = pos & 31;
+          const uint4 a0 = *reinterpret_cast<const uint4*>(rq0 + 32 * wr);
+          const uint4 a1 = *reinterpret_cast<const uint4*>(rq0 + 32 * wr + 16);
+          uint32_t cw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          if constexpr ((16 * VB) % 32 != 0) {
+            // 3-bit codes cross word boundaries: funnel in the next row
+            const uint4 b0 = *reinterpret_cast<const uint4*>(rq0 + 32 * (wr + 1));
+            const uint4 b1 = *reinterpret_cast<const uint4*>(rq0 + 32 * (wr + 1) + 16);
+            const uint32_t nw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cw[e] = __builtin_amdgcn_alignbit(nw[e], cw[e], sh);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cw[e] >>= sh;
+          }
+          u32x4 bq;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            // 1024 + code as fp16 (0x6400 | code), less 1024, times Delta: exact
+            const uint32_t x = (cw[2 * m] & kMask) | ((cw[2 * m + 1] & kMask) << 16) | 0x64006400u;
+            const fp16x2 q = __builtin_bit_cast(fp16x2, x) - fp16x2{(__fp16)1024.0f, (__fp16)1024.0f};
+            bq[m] = pk(q * dp[m]);
+          }
+          const half8 B = __builtin_bit_cast(half8, bq);
+          og[c] = mfma(pal, B, og[c]);
+          og[c] = mfma(pah, B, og[c]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        // with QJL the registers are short: one value tile at a time
+        if (QJL) __builtin_amdgcn_sched_barrier(0);
+        // indices of tokens 4 grp4 + (0..3) and 16 + 4 grp4 + (0..3): slots e
+        const uint2 p0 = *reinterpret_cast<const uint2*>(vidx + vrow[i]);
+        const uint2 p1 = *reinterpret_cast<const uint2*>(vidx + vrow[i] + 16);
+        const uint32_t pw2[4] = {p0.x, p0.y, p1.x, p1.y};
+        half8 bh[3], bl[3];
+        if (PRE) {
+          uint4 E[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) E[e] = tabv[(pw2[e >> 1] >> (16 * (e & 1))) & 0xffffu];
+          operands_pre(E, bh, bl);
+        } else {
+          float vx[8], vy[8], vz[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t idx = (pw2[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const uint4 n = tabv[idx & (KK - 1)];
+            const float rho = crv[idx >> FWD];
+            vx[e] = rho * __uint_as_float(n.x);
+            vy[e] = rho * __uint_as_float(n.y);
+            vz[e] = rho * __uint_as_float(n.z);
+          }
+          split8(vx, bh[0], bl[0]);
+          split8(vy, bh[1], bl[1]);
+          split8(vz, bh[2], bl[2]);
+        }
+#pragma unroll
+        for (int c = 0; c < 3; ++c) o[i][c] = mfma3(pah, pal, bh[c], bl[c], o[i][c]);
+      }
     }
     if (QJL) {
       load_block(blk, a, plane, t_next, L);
@@ -830,16 +964,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     red_ml[(wave * kMaxG + col) * 2] = m_run;
     red_ml[(wave * kMaxG + col) * 2 + 1] = l_run;
   }
+  if constexpr (VG != 0) {
 #pragma unroll
-  for (int i = 0; i < 3; ++i)
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
-      const int coord = 3 * (16 * i + col) + c;
-      if (coord < kHeadDim) {
+      for (int r = 0; r < 4; ++r)
+        red_o[(wave * kMaxG + 4 * grp4 + r) * kHeadDim + 16 * c + col] = og[c][r];
+    // the zero-point sums of head col: its four lane groups' tokens
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red_o[(wave * kMaxG + 4 * grp4 + r) * kHeadDim + coord] = o[i][c][r];
-      }
+    for (int j = 0; j < GR::G; ++j) {
+      const float z = rows_sum(zacc[j]);
+      if (grp4 == 0 && col < G) red_z[(wave * kMaxG + col) * GR::G + j] = z;
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        const int coord = 3 * (16 * i + col) + c;
+        if (coord < kHeadDim) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            red_o[(wave * kMaxG + 4 * grp4 + r) * kHeadDim + coord] = o[i][c][r];
+        }
+      }
+  }
   lds_barrier();
   for (int e = tid; e < G * kHeadDim; e += kThreads) {
     const int h = e >> 7, c = e & 127;
@@ -852,7 +1001,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
       const float mw = red_ml[(w * kMaxG + h) * 2];
       const float f = mw == -INFINITY ? 0.0f : __expf(mw - M);
       Lsum += f * red_ml[(w * kMaxG + h) * 2 + 1];
-      A += f * red_o[(w * kMaxG + h) * kHeadDim + c];
+      const float zt = VG ? red_z[(w * kMaxG + h) * GR::G + c / (VG ? VG : 1)] : 0.0f;
+      A += f * (red_o[(w * kMaxG + h) * kHeadDim + c] + zt);
     }
     const size_t row = ((size_t)b * a.Hq + (size_t)g * G + h) * a.n_part + split;
     a.ws_acc[row * kHeadDim + c] = A;
@@ -1149,9 +1299,21 @@ int waves_for(int b_dir, int b_nrm, bool shared) {
 }
 
 template <int BD, int BN, bool QJL>
-void launch_q(const DecodeArgs& a, hipStream_t st) {
+void launch_q(const DecodeArgs& a, int vg, hipStream_t st) {
   dim3 grid(a.n_split, a.Hkv, a.B);
   constexpr bool big = (1 << (2 * BD + BN)) > kMaxSmallPre;
+  constexpr int NW = big ? kWavesBig : kWavesSmall;
+  if constexpr (BD == BN + 2) {
+    // the group-wise value codec with b = b_dir - 1 bits: one (K) table
+    if (vg == 16) {
+      hipLaunchKernelGGL((decode_kernel<BD, BN, QJL, kPre, NW, 16>), grid, dim3(64 * NW), 0, st, a);
+      return;
+    }
+    if (vg == 32) {
+      hipLaunchKernelGGL((decode_kernel<BD, BN, QJL, kPre, NW, 32>), grid, dim3(64 * NW), 0, st, a);
+      return;
+    }
+  }
   if constexpr (!big) {
     hipLaunchKernelGGL((decode_kernel<BD, BN, QJL, kPre, kWavesSmall>), grid, dim3(64 * kWavesSmall), 0, st, a);
   } else {
@@ -1163,11 +1325,11 @@ void launch_q(const DecodeArgs& a, hipStream_t st) {
 }
 
 template <int BD, int BN>
-void launch(const DecodeArgs& a, bool qjl, hipStream_t st) {
+void launch(const DecodeArgs& a, bool qjl, int vg, hipStream_t st) {
   if (qjl)
-    launch_q<BD, BN, true>(a, st);
+    launch_q<BD, BN, true>(a, vg, st);
   else
-    launch_q<BD, BN, false>(a, st);
+    launch_q<BD, BN, false>(a, vg, st);
 }
 
 }  // namespace
@@ -1183,9 +1345,15 @@ static octo_status check_kv(const octo_codec_desc* k_codec, const octo_codec_des
   if ((s = resolve_codec(v_codec, what, vc)) != OCTO_OK) return s;
   if ((s = check_cache(k_cache, *kc, what)) != OCTO_OK) return s;
   if ((s = check_cache(v_cache, *vc, what)) != OCTO_OK) return s;
+  if (kc->group) return fail(OCTO_ERR_UNSUPPORTED, "%s: keys need the OCTOPUS codec", what);
   if (vc->qjl) return fail(OCTO_ERR_UNSUPPORTED, "%s: the value codec cannot carry QJL", what);
-  if (kc->b_dir != vc->b_dir || kc->b_nrm != vc->b_nrm)
+  if (vc->group) {
+    if (kc->b_dir != kc->b_nrm + 2 || vc->bits != kc->bits)
+      return fail(OCTO_ERR_UNSUPPORTED,
+                  "%s: a group value codec needs keys in the (b+1, b-1) split with the same b", what);
+  } else if (kc->b_dir != vc->b_dir || kc->b_nrm != vc->b_nrm) {
     return fail(OCTO_ERR_UNSUPPORTED, "%s: K and V must share (b_dir, b_nrm)", what);
+  }
   if (k_cache->batch != v_cache->batch || k_cache->kv_heads != v_cache->kv_heads ||
       k_cache->capacity != v_cache->capacity)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: K and V caches differ in shape", what);
@@ -1222,7 +1390,8 @@ static octo_status prepare(const char* what, const octo_codec_desc* k_codec,
                 max_seq_len, k_cache->capacity);
   if (B > 65535 || Hkv > 65535 || num_q_heads > 65535)
     return fail(OCTO_ERR_UNSUPPORTED, "%s: batch and heads must be <= 65535", what);
-  const bool shared = std::memcmp(&kc->cb, &vc->cb, sizeof(Codebook)) == 0;
+  // a group value codec needs no table of its own: the big K table is alone
+  const bool shared = vc->group || std::memcmp(&kc->cb, &vc->cb, sizeof(Codebook)) == 0;
   const Plan p =
       make_plan(B, num_q_heads, Hkv, max_seq_len, waves_for(kc->b_dir, kc->b_nrm, shared), step);
   if (!workspace || workspace_bytes < p.total)
@@ -1244,6 +1413,7 @@ static octo_status prepare(const char* what, const octo_codec_desc* k_codec,
   a->kcb = kc->cb;
   a->vcb = vc->cb;
   a->shared_tables = shared;
+  a->v_group = vc->group;
   a->kseed = kc->seed;
   a->vseed = vc->seed;
   a->k_idx = k_cache->idx;
@@ -1251,7 +1421,7 @@ static octo_status prepare(const char* what, const octo_codec_desc* k_codec,
   a->kgamma = k_cache->gamma;
   a->kgamma_r = k_cache->gamma_r;
   a->v_idx = v_cache->idx;
-  a->vgamma = v_cache->gamma;
+  a->vgamma = v_cache->gamma;          // NULL with a group value codec (unread)
   a->capacity = k_cache->capacity;
   a->n_split = p.n_split;
   a->split_len = p.split_len;
@@ -1265,13 +1435,14 @@ static octo_status prepare(const char* what, const octo_codec_desc* k_codec,
 
 static octo_status launch_scan(const DecodeArgs& a, const Codec& kc, const char* what,
                                hipStream_t stream) {
+  const int vg = a.v_group;
   switch (kc.b_dir * 10 + kc.b_nrm) {
-    case 31: launch<3, 1>(a, kc.qjl, stream); break;
-    case 42: launch<4, 2>(a, kc.qjl, stream); break;
-    case 53: launch<5, 3>(a, kc.qjl, stream); break;
-    case 22: launch<2, 2>(a, kc.qjl, stream); break;
-    case 33: launch<3, 3>(a, kc.qjl, stream); break;
-    case 44: launch<4, 4>(a, kc.qjl, stream); break;
+    case 31: launch<3, 1>(a, kc.qjl, vg, stream); break;
+    case 42: launch<4, 2>(a, kc.qjl, vg, stream); break;
+    case 53: launch<5, 3>(a, kc.qjl, vg, stream); break;
+    case 22: launch<2, 2>(a, kc.qjl, vg, stream); break;
+    case 33: launch<3, 3>(a, kc.qjl, vg, stream); break;
+    case 44: launch<4, 4>(a, kc.qjl, vg, stream); break;
     default: return fail(OCTO_ERR_UNSUPPORTED, "%s: configuration not compiled", what);
   }
   return check_launch(what);
@@ -1283,6 +1454,7 @@ static octo_status workspace_bytes_for(const char* what, const octo_codec_desc* 
   Codec kc;
   octo_status s = resolve_codec(k_codec, what, &kc, false);
   if (s != OCTO_OK) return s;
+  if (kc.group) return fail(OCTO_ERR_UNSUPPORTED, "%s: keys need the OCTOPUS codec", what);
   if (!bytes) return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", what);
   if (B < 1 || num_q_heads < 1 || kv_heads < 1 || max_len < 0)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: bad sizes", what);
@@ -1355,6 +1527,8 @@ extern "C" octo_status octo_decode_step(const octo_codec_desc* k_codec,
   if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_window | (uintptr_t)v_window) & 15 ||
       ((uintptr_t)window_lens & 3))
     return fail(OCTO_ERR_ALIGNMENT, "%s: rows or window_lens misaligned", what);
+  if (vc.group)
+    return fail(OCTO_ERR_UNSUPPORTED, "%s: the group value codec is not compiled for the step", what);
   a.step = 1;
   a.window = window;
   a.win_lens = window_lens;

@@ -18,6 +18,7 @@
 //   Sec. 3        the indices of I_dir and I_nrm, packed in registers at
 //                 constant bit offsets as one field per triplet
 //                 (xi | eta << b_dir | rho << 2 b_dir, B_tri bits).
+// group_encode_kernel encodes the group-wise value codec the same way.
 // A workgroup of 256 lanes takes 256 consecutive tokens of one (batch, head)
 // plane; in the tile-64 layout word w of 64 consecutive tokens is 256
 // contiguous bytes, so every word store of a wavefront is one coalesced
@@ -137,6 +138,49 @@ __device__ inline void flip_signs(float (&v)[128], uint64_t m0, uint64_t m1) {
   }
 }
 
+// Loads row (b, h, t) of x as fp32 (zeros for a lane past the last token).
+__device__ inline void load_row(const EncodeArgs& a, int b, int h, int t, bool valid,
+                                float (&v)[128]) {
+  const int64_t off = (int64_t)b * a.s0 + (int64_t)h * a.s1 + (int64_t)(valid ? t : 0) * a.s2;
+  if (a.is_bf16) {
+    const uint16_t* row = static_cast<const uint16_t*>(a.x) + off;
+    if (a.vec16) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint4 w = reinterpret_cast<const uint4*>(row)[k];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          v[8 * k + 2 * m] = __uint_as_float(ws[m] << 16);
+          v[8 * k + 2 * m + 1] = __uint_as_float(ws[m] & 0xffff0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 128; ++j) v[j] = bf16_to_f32(row[j]);
+    }
+  } else {
+    const float* row = static_cast<const float*>(a.x) + off;
+    if (a.vec16) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const float4 w = reinterpret_cast<const float4*>(row)[k];
+        v[4 * k] = w.x;
+        v[4 * k + 1] = w.y;
+        v[4 * k + 2] = w.z;
+        v[4 * k + 3] = w.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 128; ++j) v[j] = row[j];
+    }
+  }
+  if (!valid) {
+#pragma unroll
+    for (int j = 0; j < 128; ++j) v[j] = 0.0f;
+  }
+}
+
 template <int BD, int BN>
 __global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
   constexpr int K = 1 << BD, R = 1 << BN;
@@ -169,46 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
 
   // ---- the row of this token, issued before the tables are built
   float v[128];
-  {
-    const int64_t off = (int64_t)b * a.s0 + (int64_t)h * a.s1 + (int64_t)(valid ? t : 0) * a.s2;
-    if (a.is_bf16) {
-      const uint16_t* row = static_cast<const uint16_t*>(a.x) + off;
-      if (a.vec16) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const uint4 w = reinterpret_cast<const uint4*>(row)[k];
-          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            v[8 * k + 2 * m] = __uint_as_float(ws[m] << 16);
-            v[8 * k + 2 * m + 1] = __uint_as_float(ws[m] & 0xffff0000u);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 128; ++j) v[j] = bf16_to_f32(row[j]);
-      }
-    } else {
-      const float* row = static_cast<const float*>(a.x) + off;
-      if (a.vec16) {
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-          const float4 w = reinterpret_cast<const float4*>(row)[k];
-          v[4 * k] = w.x;
-          v[4 * k + 1] = w.y;
-          v[4 * k + 2] = w.z;
-          v[4 * k + 3] = w.w;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 128; ++j) v[j] = row[j];
-      }
-    }
-    if (!valid) {
-#pragma unroll
-      for (int j = 0; j < 128; ++j) v[j] = 0.0f;
-    }
-  }
+  load_row(a, b, h, t, valid, v);
 
   // ---- tables: codebooks, cell boundaries, decoded directions
   if (tid < K) cxi[tid] = a.cb.xi[tid];
@@ -368,10 +373,77 @@ __global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
   }
 }
 
+// The group-wise value codec (group = 16 or 32): one lane per token, u = R x
+// in registers as above, then per group of GS coordinates the range, the
+// E4M3 step size, the BF16 zero-point and the codes (the quantizer of
+// "Quantized Keys Steal Attention", Sec. 3 and Sec. 4.3, as the value codec
+// of the OCTOPUS experiments, Sec. 4).  Every decision is an fp32 operation:
+// the division is the correctly rounded one, rint rounds half to even.
+template <int VB, int GS>
+__global__ __launch_bounds__(kThreads, 2) void group_encode_kernel(EncodeArgs a) {
+  constexpr int G = kHeadDim / GS, WC = VB * kHeadDim / 32, W = group_record_words(VB, GS);
+  constexpr float kLevels = (float)((1 << VB) - 1);
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int t = blockIdx.x * kThreads + tid;
+  const bool valid = t < a.T;
+  const size_t plane = (size_t)b * a.H + h;
+  const int ln = tid & 63;
+  const uint64_t sm0 = __ballot(splitmix_sign(a.seed, ln) < 0.0f);
+  const uint64_t sm1 = __ballot(splitmix_sign(a.seed, ln + 64) < 0.0f);
+  float v[128];
+  load_row(a, b, h, t, valid, v);
+  flip_signs(v, sm0, sm1);
+  wht128_regs(v);
+#pragma unroll
+  for (int j = 0; j < 128; ++j) v[j] *= kInvSqrtD;
+
+  uint32_t rec[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) rec[w] = 0u;
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    __builtin_amdgcn_sched_barrier(0);   // one group at a time (no interleaving spills)
+    float mn = v[gi * GS], mx = mn;
+#pragma unroll
+    for (int j = 1; j < GS; ++j) {
+      mn = fminf(mn, v[gi * GS + j]);
+      mx = fmaxf(mx, v[gi * GS + j]);
+    }
+    mn += 0.0f;                          // a zero minimum is stored as +0
+    const uint32_t s8 = e4m3_rne((mx - mn) / kLevels);
+    const float dh = e4m3_value(s8);
+    const uint32_t z16 = bf16_rne(mn);
+    const float zh = __uint_as_float(z16 << 16);
+#pragma unroll
+    for (int j = 0; j < GS; ++j) {
+      const int c = gi * GS + j;
+      const float qf = fminf(fmaxf(rintf((v[c] - zh) / dh), 0.0f), kLevels);
+      const uint32_t q = dh > 0.0f ? (uint32_t)qf : 0u;
+      const int pos = c * VB, w = pos >> 5, sh = pos & 31;
+      rec[w] |= q << sh;
+      if (sh + VB > 32) rec[w + 1] |= q >> (32 - sh);
+    }
+    rec[WC + gi / 4] |= s8 << (8 * (gi % 4));
+    rec[WC + G / 4 + gi / 2] |= z16 << (16 * (gi % 2));
+  }
+  if (valid) {
+    const int tc = a.token_offset + t;
+#pragma unroll
+    for (int w = 0; w < W; ++w) a.idx[tile_word(plane, a.capacity, tc, w, W)] = rec[w];
+  }
+}
+
 template <int BD, int BN>
 void launch(const EncodeArgs& a, hipStream_t st) {
   dim3 grid((a.T + kThreads - 1) / kThreads, a.H, a.B);
   hipLaunchKernelGGL((encode_kernel<BD, BN>), grid, dim3(kThreads), 0, st, a);
+}
+
+template <int VB, int GS>
+void launch_group(const EncodeArgs& a, hipStream_t st) {
+  dim3 grid((a.T + kThreads - 1) / kThreads, a.H, a.B);
+  hipLaunchKernelGGL((group_encode_kernel<VB, GS>), grid, dim3(kThreads), 0, st, a);
 }
 
 }  // namespace
@@ -429,6 +501,18 @@ extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, 
   a.gamma_r = dst->gamma_r;
   a.capacity = dst->capacity;
   a.token_offset = token_offset;
+  if (c.group) {
+    switch (c.bits * 100 + c.group) {
+      case 216: launch_group<2, 16>(a, stream); break;
+      case 232: launch_group<2, 32>(a, stream); break;
+      case 316: launch_group<3, 16>(a, stream); break;
+      case 332: launch_group<3, 32>(a, stream); break;
+      case 416: launch_group<4, 16>(a, stream); break;
+      case 432: launch_group<4, 32>(a, stream); break;
+      default: return fail(OCTO_ERR_UNSUPPORTED, "octo_encode: group codec not compiled");
+    }
+    return check_launch("octo_encode");
+  }
   switch (c.b_dir * 10 + c.b_nrm) {
     case 31: launch<3, 1>(a, stream); break;
     case 42: launch<4, 2>(a, stream); break;

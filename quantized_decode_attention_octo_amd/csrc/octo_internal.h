@@ -33,8 +33,12 @@ struct Codebook {
   float rho[kMaxRho];
 };
 
-// A codec with its bit split resolved (Sec. 3.3: B_tri = 2 b_dir + b_nrm).
+// A codec with its bit split resolved (Sec. 3.3: B_tri = 2 b_dir + b_nrm),
+// or the group-wise value codec (group = 16 or 32; b_dir = b_nrm = 0).
 struct Codec {
+  int group;            // 0: OCTOPUS; else the group size g of the value codec
+  int bits;             // b of the group codec (the OCTOPUS codec: b_dir - 1
+                        // for the (b+1, b-1) split, b_dir for the uniform one)
   int b_dir, b_nrm;     // bits per octahedral coordinate / per triplet norm
   int K;                // 2^b_dir entries of C_xi
   int R;                // 2^b_nrm entries of C_rho
@@ -60,6 +64,10 @@ octo_status check_cache(const octo_cache_view* v, const Codec& c, const char* wh
 octo_status check_launch(const char* what);
 
 inline int words_for_bits(int bits) { return (bits + 31) / 32; }
+
+// Words of one group-codec record: 128 b-bit codes, 128/g E4M3 scales and
+// 128/g BF16 zero-points.
+constexpr int group_record_words(int bits, int g) { return (kHeadDim * bits + 24 * (kHeadDim / g)) / 32; }
 
 // ---------------------------------------------------------------- device side
 // SplitMix64 output j of the generator started at `seed` (Steele, Lea and
@@ -123,6 +131,28 @@ __device__ inline float wave_max(float v) {
 
 // bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits.
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// E4M3 (4 exponent bits, bias 7, 3 mantissa bits, no infinities, largest
+// finite value 448) code of a non-negative finite fp32 value: round to
+// nearest, ties to the even code, saturating at 448.  Codes 0..8 are the
+// multiples of 2^-9 up to 2^-6 (the subnormals and the smallest normal);
+// above, the fp32 exponent and top mantissa bits are the code once the
+// bias is moved from 127 to 7.
+__device__ inline uint32_t e4m3_rne(float x) {
+  if (!(x < 448.0f)) return 0x7Eu;
+  if (x < 0.015625f) return (uint32_t)rintf(x * 512.0f);
+  const uint32_t u = __float_as_uint(x);
+  return ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+}
+// Exact fp32 value of an E4M3 code 0..0x7E.
+__device__ inline float e4m3_value(uint32_t c) {
+  return c >= 8u ? __uint_as_float((c + (120u << 3)) << 20) : (float)c * 0.001953125f;
+}
+// BF16 bit pattern of a finite fp32 value, round to nearest even.
+__device__ inline uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 
 // Workgroup barrier that orders LDS only: it waits for this wave's LDS
 // operations but leaves its global loads in flight (a full __syncthreads

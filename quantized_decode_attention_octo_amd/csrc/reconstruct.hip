@@ -11,6 +11,10 @@
 // lane-pair Walsh-Hadamard transform and scales by gamma.  With a QJL codec
 // the result is the MSE reconstruction alone: the sign sketch estimates inner
 // products (Sec. 3.6), it does not reconstruct the residual.
+//
+// The group-wise value codec decodes the same way: lane l reads the codes of
+// coordinates l and l + 64 and their groups' E4M3 scale and BF16 zero-point,
+// u^ = Delta code + z, then R^T as above.
 #include <math.h>
 
 #include "octo_internal.h"
@@ -80,6 +84,40 @@ __global__ __launch_bounds__(64 * kWaves) void reconstruct_kernel(ReconArgs a) {
   o[L + 64] = a1 * splitmix_sign(a.seed, L + 64) * g;
 }
 
+template <int VB, int GS>
+__global__ __launch_bounds__(64 * kWaves) void group_reconstruct_kernel(ReconArgs a) {
+  constexpr int G = kHeadDim / GS, WC = VB * kHeadDim / 32, W = group_record_words(VB, GS);
+  const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x * kWaves + wave;
+  if (t >= a.T) return;                               // whole wavefronts
+  const size_t plane = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const int tc = a.t0 + t;
+  float u[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = L + 64 * k, pos = c * VB, w = pos >> 5, sh = pos & 31;
+    const uint32_t lo = a.idx[tile_word(plane, a.capacity, tc, w, W)];
+    const uint32_t hi = sh + VB > 32 ? a.idx[tile_word(plane, a.capacity, tc, w + 1, W)] : 0u;
+    const uint32_t q = (uint32_t)((((uint64_t)hi << 32) | lo) >> sh) & ((1u << VB) - 1u);
+    const int gi = c / GS;
+    const uint32_t sw = a.idx[tile_word(plane, a.capacity, tc, WC + gi / 4, W)];
+    const uint32_t zw = a.idx[tile_word(plane, a.capacity, tc, WC + G / 4 + gi / 2, W)];
+    const float dh = e4m3_value((sw >> (8 * (gi % 4))) & 0xffu);
+    const float zh = __uint_as_float(((zw >> (16 * (gi % 2))) & 0xffffu) << 16);
+    u[k] = fmaf(dh, (float)q, zh);
+  }
+  wht128(u[0], u[1]);
+  float* o = a.out + (plane * a.T + t) * kHeadDim;
+  o[L] = u[0] * splitmix_sign(a.seed, L) * kInvSqrtD;
+  o[L + 64] = u[1] * splitmix_sign(a.seed, L + 64) * kInvSqrtD;
+}
+
+template <int VB, int GS>
+void launch_group(const ReconArgs& a, hipStream_t st) {
+  dim3 grid((a.T + kWaves - 1) / kWaves, a.H, a.B);
+  hipLaunchKernelGGL((group_reconstruct_kernel<VB, GS>), grid, dim3(64 * kWaves), 0, st, a);
+}
+
 template <int BD, int BN>
 void launch(const ReconArgs& a, hipStream_t st) {
   dim3 grid((a.T + kWaves - 1) / kWaves, a.H, a.B);
@@ -120,6 +158,18 @@ extern "C" octo_status octo_decode_tokens(const octo_codec_desc* codec,
   a.t0 = t0;
   a.T = T;
   a.out = out;
+  if (c.group) {
+    switch (c.bits * 100 + c.group) {
+      case 216: launch_group<2, 16>(a, stream); break;
+      case 232: launch_group<2, 32>(a, stream); break;
+      case 316: launch_group<3, 16>(a, stream); break;
+      case 332: launch_group<3, 32>(a, stream); break;
+      case 416: launch_group<4, 16>(a, stream); break;
+      case 432: launch_group<4, 32>(a, stream); break;
+      default: return fail(OCTO_ERR_UNSUPPORTED, "%s: group codec not compiled", what);
+    }
+    return check_launch(what);
+  }
   switch (c.b_dir * 10 + c.b_nrm) {
     case 31: launch<3, 1>(a, stream); break;
     case 42: launch<4, 2>(a, stream); break;

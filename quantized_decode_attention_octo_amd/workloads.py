@@ -40,6 +40,7 @@ class Workload:
     len_hi: int = 0
     chunk_q: int = 0       # > 0: chunk workload with this many queries / current tokens
     window: int = 0        # > 0: decode-step workload with a residual window of this size
+    v_group: int = 0       # > 0: values in the group-wise codec with this group size
     seed: int = 0
 
     @property
@@ -53,6 +54,10 @@ WORKLOADS = {
                      B=1, Hq=1, Hkv=1, d=128, T=256, bits=3, dtype="fp32"),
     "gqa32k": Workload("gqa32k", "GQA 28/4 heads, d=128, batch 1, context 32768, bf16 + outliers, b=4",
                        B=1, Hq=28, Hkv=4, d=128, T=32768, bits=4, dtype="bf16", outliers=True),
+    "gqa32k_g32": Workload("gqa32k_g32", "GQA 28/4 heads, d=128, batch 1, context 32768, bf16 + outliers, "
+                           "b=4 keys, values in the group-32 codec at b=4",
+                           B=1, Hq=28, Hkv=4, d=128, T=32768, bits=4, dtype="bf16", outliers=True,
+                           v_group=32),
     "batch16": Workload("batch16", "GQA 28/4, batch 16, context U[4096, 8192] (capacity 8192), bf16 + outliers, b=3",
                         B=16, Hq=28, Hkv=4, d=128, T=8192, bits=3, dtype="bf16", outliers=True,
                         len_lo=4096, len_hi=8192),

@@ -9,7 +9,11 @@ Parity rules (the oracle is float64, the kernels fp32):
     already carry an allowed index mismatch (their residual differs);
   * gamma within 4 fp32 ulps; gamma_r within 1 fp16 ulp;
   * attention outputs within max-abs 2e-3 of the oracle evaluated on the
-    GPU-written cache.
+    GPU-written cache;
+  * group-wise value codec: E4M3 scales, BF16 zero-points and codes bit-exact;
+    a field may differ only where the oracle's decision margin is below 1e-6
+    of the token's largest |u| (the codes of a group whose scale or
+    zero-point differs that way are then not compared).
 """
 import dataclasses
 import os
@@ -28,7 +32,9 @@ import quantized_decode_attention_octo_amd as octo  # noqa: E402
 from oracle import attention as oatt  # noqa: E402
 from oracle import cache as ocache  # noqa: E402
 from oracle import encode as oenc  # noqa: E402
+from oracle import group as ogroup  # noqa: E402
 from oracle_codecs import codec as oracle_codec  # noqa: E402
+from oracle_codecs import group_codec as oracle_group_codec  # noqa: E402
 from quantized_decode_attention_octo_amd.workloads import WORKLOADS, make_inputs  # noqa: E402
 
 MARGIN = 1e-6
@@ -49,6 +55,62 @@ def codecs(bits, qjl=False, seed=0, b_dir=None, b_nrm=None, rounding="local3x3")
     g = octo.Codec(bits=bits, seed=seed, qjl=qjl, b_dir=b_dir, b_nrm=b_nrm, rounding=r)
     h = oracle_codec(bits=bits, seed=seed, qjl=qjl, b_dir=b_dir, b_nrm=b_nrm, rounding=rounding)
     return g, h
+
+
+def group_codecs(bits, group, seed=0):
+    """(GPU codec, oracle codec dict) of the group-wise value codec."""
+    return octo.Codec(bits=bits, seed=seed, group=group), oracle_group_codec(bits, group, seed)
+
+
+def plane_of(h, b, g):
+    """The host cache of plane (b, g) alone (same layout with B = H = 1)."""
+    n = h["B"] * h["H"]
+    p = b * h["H"] + g
+    out = {"B": 1, "H": 1, "capacity": h["capacity"], "idx": h["idx"].reshape(n, -1)[p]}
+    if "gamma" in h:
+        out["gamma"] = h["gamma"][b:b + 1, g:g + 1]
+    if "qjl" in h:
+        out["qjl"] = h["qjl"].reshape(n, -1)[p]
+        out["gamma_r"] = h["gamma_r"][b:b + 1, g:g + 1]
+    return out
+
+
+def compare_group_encode(host_cache, hcodec, x, token_offset=0, planes=None, tokens=None):
+    """Compares GPU-written group records with the oracle's encoding of x."""
+    B, H, T, d = x.shape
+    planes = planes or [(b, h) for b in range(B) for h in range(H)]
+    st = dict(codes=0, mismatch=0, bad=0, groups=0, meta_mismatch=0, meta_bad=0)
+    g = hcodec["group"]
+    for b, h in planes:
+        ts = np.arange(T) if tokens is None else np.asarray(tokens)
+        e = ogroup.encode(x[b, h].double().numpy()[ts], hcodec["bits"], g, hcodec["seed"])
+        rec = ocache.read_tokens(host_cache, hcodec, b, h, token_offset, T)
+        codes, s8, z16 = rec["codes"][ts], rec["scale8"][ts], rec["zero16"][ts]
+        tol = MARGIN * np.abs(e["u"]).max(axis=1, keepdims=True)           # per token
+        sm, zm = s8 != e["scale8"], z16 != e["zero16"]
+        meta_bad = (sm & (e["scale_margin"] >= tol)) | (zm & (e["zero_margin"] >= tol))
+        st["groups"] += sm.size
+        st["meta_mismatch"] += int((sm | zm).sum())
+        st["meta_bad"] += int(meta_bad.sum())
+        skip = np.repeat(sm | zm, g, axis=1)                  # codes of a moved grid
+        cm = (codes != e["codes"]) & ~skip
+        bad = cm & (e["code_margin"] >= tol)
+        st["codes"] += cm.size
+        st["mismatch"] += int(cm.sum())
+        st["bad"] += int(bad.sum())
+        if bad.any() or meta_bad.any():
+            i = np.argwhere(bad)[0] if bad.any() else np.argwhere(meta_bad)[0]
+            say("first bad mismatch", (b, h, int(ts[i[0]]), int(i[1])), "gpu codes",
+                codes[i[0]].tolist()[:16], "oracle", e["codes"][i[0]].tolist()[:16],
+                "scales", s8[i[0]].tolist(), e["scale8"][i[0]].tolist(),
+                "zeros", z16[i[0]].tolist(), e["zero16"][i[0]].tolist())
+    return st
+
+
+def assert_group_encode_ok(st, what):
+    say(f"[{what}] codes {st['codes']} mismatches {st['mismatch']} (bad {st['bad']}); groups"
+        f" {st['groups']} scale/zero mismatches {st['meta_mismatch']} (bad {st['meta_bad']})")
+    assert st["bad"] == 0 and st["meta_bad"] == 0
 
 
 def encode_gpu(x, gcodec, capacity=None, token_offset=0, cache=None):

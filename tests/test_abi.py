@@ -234,3 +234,51 @@ def test_chunk_errors(L):
     assert ch(Tq=-1) == 1
     assert ch(kd=desc(bits=2, qjl=1), kv=view(H=2, cap=256, qjl=True)) == 2
     assert ch(Tq=0) == 0                                     # nothing to do
+
+
+def gdesc(bits=2, group=32, b_dir=0, b_nrm=0, qjl=0):
+    """Descriptor of the group-wise value codec (no codebooks)."""
+    return ob.CodecDesc(ob.ABI_VERSION, 128, bits, b_dir, b_nrm, 0, qjl, group, 0, None, None)
+
+
+@pytest.mark.parametrize("bits,group,words", [(2, 32, 11), (2, 16, 14), (3, 32, 15), (3, 16, 18),
+                                              (4, 32, 19), (4, 16, 22)])
+def test_group_record_sizes(L, bits, group, words):
+    # 128 codes of b bits, 128/g E4M3 scales and 128/g BF16 zero-points:
+    # b + 24/g bits per coordinate ("Quantized Keys Steal Attention", Sec. 4.3)
+    out = ob.StreamSizes()
+    assert L.octo_record_sizes(ctypes.byref(gdesc(bits, group)), ctypes.byref(out)) == 0
+    assert out.idx_words == words == (128 * bits + 24 * 128 // group) // 32
+    assert (out.qjl_words, out.n_triplets, out.b_dir, out.b_nrm) == (0, 0, 0, 0)
+
+
+def test_group_codec_errors(L):
+    out = ob.StreamSizes()
+
+    def rs(d):
+        return L.octo_record_sizes(ctypes.byref(d), ctypes.byref(out))
+    assert rs(gdesc(group=24)) == 2
+    assert rs(gdesc(group=-16)) == 1
+    assert rs(gdesc(bits=5)) == 2
+    assert rs(gdesc(bits=9)) == 1
+    assert rs(gdesc(b_dir=3, b_nrm=1)) == 1
+    assert rs(gdesc(qjl=1)) == 2
+    # a group cache needs no gamma stream
+    gv = view(H=2)
+    gv.gamma = None
+    p = ctypes.c_void_p(4096)
+    kd = desc(bits=2)
+    # keys need the OCTOPUS codec; values need the same b with a (b+1, b-1) key split
+    assert dec(L, gdesc(), gdesc(), gv, gv) == 2
+    assert dec(L, kd, gdesc(bits=3), view(H=2), gv) == 2
+    assert dec(L, desc(bits=2, b_dir=2, b_nrm=2), gdesc(bits=2), view(H=2), gv) == 2
+    assert dec(L, kd, gdesc(bits=2), view(H=2), gv, ws_bytes=0) == 5        # accepted up to here
+    n = ctypes.c_size_t()
+    assert L.octo_decode_workspace_bytes(ctypes.byref(gdesc()), 1, 4, 2, 128, ctypes.byref(n)) == 2
+    assert L.octo_chunk_workspace_bytes(ctypes.byref(gdesc()), 1, 2, 2, 64, 128, 64,
+                                        ctypes.byref(n)) == 2
+    assert L.octo_attend_chunk(ctypes.byref(gdesc()), ctypes.byref(gdesc()), ctypes.byref(gv),
+                               ctypes.byref(gv), 64, p, p, p, 2, 64, 64, 0.0, p, p, 1 << 20,
+                               None) == 2
+    assert L.octo_decode_tokens(ctypes.byref(gdesc()), ctypes.byref(gv), 100, 29, p, None) == 4
+    assert L.octo_decode_tokens(ctypes.byref(gdesc()), ctypes.byref(gv), 0, 4, None, None) == 1
