@@ -1114,10 +1114,70 @@ struct StepArgs {
   int shared;                          // K and V codebook values agree
   uint64_t kseed, vseed;
   int k_rounding, v_rounding, k_qjl;
+  int v_group;                         // 0, or the group size of the group value codec
   uint32_t *k_idx, *k_qjl_bits, *v_idx;   // the caches, written at slot P_b
   float *k_gamma, *v_gamma;
   uint16_t* k_gamma_r;
 };
+
+// One wavefront encodes the bf16 vector x[128] with the group-wise value
+// codec into token t of `plane` (the arithmetic of the lane-per-token
+// encoder, octo_encode): u = H diag(s) x / sqrt(d) with lane l holding
+// coordinates l and l + 64; a group of GS coordinates is GS consecutive
+// lanes, so its range is an xor-shuffle reduction (exact in any order); the
+// record's words are then assembled from the codes in `scr` (at least
+// 128 + 2 * 128 / GS words) by lanes w < W.
+template <int VB, int GS>
+__device__ void encode_group_one(const uint16_t* x, uint64_t seed, uint32_t* idx, size_t plane,
+                                 int capacity, int t, uint32_t* scr) {
+  constexpr int G = kHeadDim / GS, WC = VB * kHeadDim / 32, W = group_record_words(VB, GS);
+  constexpr float kLevels = (float)((1 << VB) - 1);
+  const int L = threadIdx.x & 63;
+  float u[2] = {bf16_to_f32(x[L]) * splitmix_sign(seed, L),
+                bf16_to_f32(x[L + 64]) * splitmix_sign(seed, L + 64)};
+  wht128(u[0], u[1]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float v = u[k] * kInvSqrtD;
+    float mn = v, mx = v;
+#pragma unroll
+    for (int m = 1; m < GS; m <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, m, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    }
+    mn += 0.0f;                          // a zero minimum is stored as +0
+    const uint32_t s8 = e4m3_rne((mx - mn) / kLevels);
+    const float dh = e4m3_value(s8);
+    const uint32_t z16 = bf16_rne(mn);
+    const float zh = __uint_as_float(z16 << 16);
+    const float qf = fminf(fmaxf(rintf((v - zh) / dh), 0.0f), kLevels);
+    const int c = L + 64 * k;
+    scr[c] = dh > 0.0f ? (uint32_t)qf : 0u;
+    if (c % GS == 0) {
+      scr[kHeadDim + c / GS] = s8;
+      scr[kHeadDim + G + c / GS] = z16;
+    }
+  }
+  wave_sync();
+  if (L < W) {
+    uint32_t word = 0u;
+    if (L < WC) {
+      // codes whose bits meet [32 L, 32 L + 32)
+      for (int c = (32 * L) / VB; c < kHeadDim && c * VB < 32 * L + 32; ++c) {
+        const int sh = c * VB - 32 * L;
+        word |= sh >= 0 ? scr[c] << sh : scr[c] >> -sh;
+      }
+    } else if (L < WC + G / 4) {
+      const int j = 4 * (L - WC);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) word |= scr[kHeadDim + j + k] << (8 * k);
+    } else {
+      const int j = 2 * (L - WC - G / 4);
+      word = scr[kHeadDim + G + j] | (scr[kHeadDim + G + j + 1] << 16);
+    }
+    idx[tile_word(plane, capacity, t, L, W)] = word;
+  }
+}
 
 // The append workgroup of sequence b: the new tokens to their ring slots,
 // the tokens leaving full rings encoded into packed slot P (one wavefront per
@@ -1177,7 +1237,15 @@ __device__ void append_block(const StepArgs& a, int b) {
                                    : (v ? a.v_win : a.k_win) + (plane * W + P % W) * kHeadDim;
       float* u = scratch[wave];
       uint32_t* fld = reinterpret_cast<uint32_t*>(u + 132);
-      if (v)
+      if (v && a.v_group) {
+        if constexpr (BD == BN + 2) {       // the group codec has b = b_dir - 1 bits here
+          uint32_t* scr = reinterpret_cast<uint32_t*>(u);
+          if (a.v_group == 16)
+            encode_group_one<BD - 1, 16>(src, a.vseed, a.v_idx, plane, a.capacity, P, scr);
+          else
+            encode_group_one<BD - 1, 32>(src, a.vseed, a.v_idx, plane, a.capacity, P, scr);
+        }
+      } else if (v)
         encode_one<BD, BN>(src, lut[vt], midp[vt], mid_rho[vt], cr_v, a.vseed, a.v_rounding,
                            false, a.v_idx, a.v_gamma, nullptr, nullptr, plane, a.capacity, P,
                            u, fld);
@@ -1527,8 +1595,6 @@ extern "C" octo_status octo_decode_step(const octo_codec_desc* k_codec,
   if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_window | (uintptr_t)v_window) & 15 ||
       ((uintptr_t)window_lens & 3))
     return fail(OCTO_ERR_ALIGNMENT, "%s: rows or window_lens misaligned", what);
-  if (vc.group)
-    return fail(OCTO_ERR_UNSUPPORTED, "%s: the group value codec is not compiled for the step", what);
   a.step = 1;
   a.window = window;
   a.win_lens = window_lens;
@@ -1557,6 +1623,7 @@ extern "C" octo_status octo_decode_step(const octo_codec_desc* k_codec,
   st.k_rounding = kc.rounding;
   st.v_rounding = vc.rounding;
   st.k_qjl = kc.qjl;
+  st.v_group = vc.group;
   st.k_idx = k_cache->idx;
   st.k_qjl_bits = k_cache->qjl;
   st.k_gamma = k_cache->gamma;

@@ -12,14 +12,16 @@ Each step compares:
 After each step the oracle continues from the GPU-written cache, so every
 step is judged on identical inputs.  Small cases span several splits, W = 1
 (every token compressed after its step), W = 5 and 8, QJL keys, sequences of
-different packed lengths and partly filled rings; the full-size case is the
-32k-context GQA shape with a 32-token window.
+different packed lengths and partly filled rings, and values in the
+group-wise codec (its evicted records compared as octo_encode's are); the
+full-size cases are the 32k-context GQA shape with a 32-token window.
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_parity import ATOL, assert_encode_ok, codecs, compare_encode, encode_gpu, octo, say
+from gpu_parity import (ATOL, assert_encode_ok, assert_group_encode_ok, codecs, compare_encode,
+                        compare_group_encode, encode_gpu, group_codecs, octo, say)
 from oracle import step as ostep
 
 pytestmark = pytest.mark.gpu
@@ -35,11 +37,12 @@ def bf16(g, *shape, scale=1.0):
     return (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16)
 
 
-def run_steps(bits, qjl, W, G, Hkv, P0, n0, steps, cap, seed=0, q_f32=False, check_every=1):
+def run_steps(bits, qjl, W, G, Hkv, P0, n0, steps, cap, seed=0, q_f32=False, check_every=1,
+              v_group=0):
     B = len(P0)
     Hq = G * Hkv
     kc, hk = codecs(bits, qjl=qjl, seed=seed)
-    vc, hv = codecs(bits, seed=seed)
+    vc, hv = group_codecs(bits, v_group, seed=seed) if v_group else codecs(bits, seed=seed)
     g = torch.Generator().manual_seed(100 + seed)
     Tpre = max(p + n for p, n in zip(P0, n0))
     K0, V0 = bf16(g, B, Hkv, Tpre, 128), bf16(g, B, Hkv, Tpre, 128)
@@ -93,7 +96,11 @@ def run_steps(bits, qjl, W, G, Hkv, P0, n0, steps, cap, seed=0, q_f32=False, che
             xv[b, :, 0] = torch.tensor(st["v_ring"][b, :, P % W]) if W > 1 else vn[b].double()
             planes = [(b, h) for h in range(Hkv)]
             assert_encode_ok(compare_encode(hk_now, hk, xk, P, planes=planes), f"step {s} K b={b}")
-            assert_encode_ok(compare_encode(hv_now, hv, xv, P, planes=planes), f"step {s} V b={b}")
+            if v_group:
+                assert_group_encode_ok(compare_group_encode(hv_now, hv, xv, P, planes=planes),
+                                       f"step {s} V b={b}")
+            else:
+                assert_encode_ok(compare_encode(hv_now, hv, xv, P, planes=planes), f"step {s} V b={b}")
         # continue from the GPU-written cache
         st["k"], st["v"] = hk_now, hv_now
     say(f"[step bits={bits} qjl={qjl} W={W} G={G}] {steps} steps, max-abs err {worst:.2e}")
@@ -123,3 +130,17 @@ def test_step_full_size_gqa32k():
     # the 32k-context GQA shape (28/4 heads, b = 4) with a full 32-token window
     run_steps(4, False, 32, 7, Hkv=4, P0=[32768 - 64], n0=[31], steps=3, cap=32768,
               check_every=3)
+
+
+@pytest.mark.parametrize("bits,qjl,W,G,P0,n0,group", [
+    (3, False, 8, 4, [300, 61], [0, 5], 32),
+    (2, True, 5, 7, [130, 1], [4, 2], 16),
+    (4, False, 1, 2, [64, 200], [0, 0], 16),
+])
+def test_step_group_values(bits, qjl, W, G, P0, n0, group):
+    run_steps(bits, qjl, W, G, Hkv=2, P0=P0, n0=n0, steps=2 * W + 3, cap=512, v_group=group)
+
+
+def test_step_full_size_gqa32k_group_values():
+    run_steps(4, False, 32, 7, Hkv=4, P0=[32768 - 64], n0=[31], steps=3, cap=32768,
+              check_every=3, v_group=32)
