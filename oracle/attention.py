@@ -82,11 +82,15 @@ def decode_attention(q, k_cache, v_cache, k_codec, v_codec, seq_lens, scale=None
 
 
 def chunk_attention(q, k_cache, v_cache, k_codec, v_codec, cached_tokens,
-                    k_cur, v_cur, scale=None, q_rows=None):
+                    k_cur, v_cur, scale=None, q_rows=None, correction=False):
     """q[B, H_q, Tq, d], k_cur/v_cur[B, H_kv, Tc, d] -> out[B, H_q, Tq, d].
 
     q_rows: optional index array of query rows to evaluate (others are left 0),
-    so that large chunks can be checked on a sample."""
+    so that large chunks can be checked on a sample.
+    correction: subtract the Jensen bias of oracle.group.jensen_bias (the
+    Taylor form of "Quantized Keys Steal Attention", Eq. 15) from the logits
+    of the cached tokens; the keys must use the group-wise codec, whose
+    round-to-nearest noise the correction models."""
     q = np.asarray(q, dtype=np.float64)
     B, Hq, Tq, d = q.shape
     Hkv = k_cache["H"]
@@ -113,5 +117,12 @@ def chunk_attention(q, k_cache, v_cache, k_codec, v_codec, cached_tokens,
                 score = qh @ keys.T
                 if k_codec.get("qjl") and cached_tokens:
                     score[:, :cached_tokens] += qjl_correction(qh, krec, k_codec)
-                out[b, h][rows] = softmax_rows(scale * score) @ vals
+                logit = scale * score
+                if correction and cached_tokens:
+                    if not is_group(k_codec):
+                        raise ValueError("the correction models round-to-nearest keys (group codec)")
+                    q_rot = qh @ rotation_matrix(d, k_codec["seed"]).T
+                    logit[:, :cached_tokens] -= grp.jensen_bias(q_rot, krec["scale8"],
+                                                                k_codec["group"], scale)
+                out[b, h][rows] = softmax_rows(logit) @ vals
     return out

@@ -38,6 +38,17 @@ fields of 8 bits (the E4M3 scale codes), then G fields of 16 bits (the BF16
 zero-points), in 32-bit words: W = (b d + 24 G) / 32 words per token, which
 is exactly B_eff = b + 24/g bits per coordinate.
 
+Jensen-bias correction ("Quantized Keys Steal Attention", Sec. 4.1-4.2 and
+the appendix "Taylor approximation"): round-to-nearest noise on a cached key,
+uniform on [-Delta/2, Delta/2] per coordinate, raises the expected
+exponentiated score by the factor prod_c sinh(a_c)/a_c, a_c = tau q_c Delta_c
+/ 2 (tau the softmax scale, 1/sqrt(d) on the page), so log(sinh(a)/a) summed
+over the coordinates is subtracted from the cached token's logit; its Taylor
+form a^2/6 gives Eq. 15, b_i = tau^2/24 sum_j Delta_ij^2 ||q_j||^2 over the
+groups j.  Under the rotation (that appendix, "Taylor approximation under
+rotation") the noise lives in the rotated frame, so q_j are the groups of
+R q.  jensen_bias is that Taylor form, jensen_bias_exact the log-sinh one.
+
 Parity: pinned in tests/test_oracle_group.py by the E4M3 format table, torch's
 float8_e4m3fn and bfloat16 conversions (library routines), brute-force
 nearest-grid-point search in exact rational arithmetic, the half-step error
@@ -194,3 +205,29 @@ def unpack_record(words, d, bits, g):
     s8 = pack.unpack_fields(words[:, wc:wc + ws], G, 8).astype(np.uint8)
     z16 = pack.unpack_fields(words[:, wc + ws:], G, 16).astype(np.uint16)
     return codes, s8, z16
+
+
+def jensen_bias(q_rot, scale8, g, tau):
+    """Eq. 15 of the QKSA page, generalized to softmax scale tau:
+    b[q, i] = tau^2 / 24 * sum_j Delta^_ij^2 ||q_rot_j||^2 for query rows
+    q_rot[Q, d] (rotated) and tokens' E4M3 scale codes scale8[T, G]."""
+    q_rot = np.asarray(q_rot, dtype=np.float64)
+    Q, d = q_rot.shape
+    G = n_groups(d, g)
+    qn2 = (q_rot.reshape(Q, G, g) ** 2).sum(axis=-1)                  # [Q, G]
+    d2 = from_e4m3(scale8).reshape(-1, G) ** 2                        # [T, G]
+    return tau * tau / 24.0 * (qn2 @ d2.T)
+
+
+def jensen_bias_exact(q_rot, scale8, g, tau):
+    """sum_c log(sinh(a_c) / a_c), a_c = tau q_c Delta^_ic / 2 (the exact
+    log of the expected noise factor under uniform noise)."""
+    q_rot = np.asarray(q_rot, dtype=np.float64)
+    Q, d = q_rot.shape
+    G = n_groups(d, g)
+    dh = np.repeat(from_e4m3(scale8).reshape(-1, G), g, axis=1)       # [T, d]
+    a = np.abs(tau * q_rot[:, None, :] * dh[None, :, :] / 2.0)       # [Q, T, d]
+    small = a < 1e-4
+    with np.errstate(divide="ignore", invalid="ignore"):
+        f = np.where(small, a * a / 6.0, np.log(np.sinh(np.where(small, 1.0, a)) / np.where(small, 1.0, a)))
+    return f.sum(axis=-1)
