@@ -378,15 +378,17 @@ def run_step(w, steps, warmup):
 
 def run_chunk(w, steps, warmup):
     inp = make_inputs(w)
-    kc = octo.Codec(bits=w.bits)
-    vc = octo.Codec(bits=w.bits)
+    kc = octo.Codec(bits=w.bits, group=w.k_group) if w.k_group else octo.Codec(bits=w.bits)
+    vc = value_codec(w)
     cached, Tq = w.T, w.chunk_q
     kcache = octo.PackedCache(kc, w.B, w.Hkv, w.capacity)
     vcache = octo.PackedCache(vc, w.B, w.Hkv, w.capacity)
     octo.octo_encode(kc, inp["K"].cuda(), kcache)
     octo.octo_encode(vc, inp["V"].cuda(), vcache)
     q, kcur, vcur = inp["q"].cuda(), inp["K_cur"].cuda(), inp["V_cur"].cuda()
-    ws = octo.workspace(octo.octo_chunk_workspace_bytes(kc, w.B, w.Hq, w.Hkv, Tq, cached, Tq), "cuda")
+    flags = octo.binding.CHUNK_JENSEN_CORRECTION if w.jensen else 0
+    ws = octo.workspace(octo.octo_chunk_workspace_bytes(kc, w.B, w.Hq, w.Hkv, Tq, cached, Tq, flags),
+                        "cuda")
     out = torch.empty(w.B, w.Hq, Tq, 128, dtype=torch.float32, device="cuda")
     t_enc, t_att = Timer(), Timer()
 
@@ -397,7 +399,8 @@ def run_chunk(w, steps, warmup):
         if timed:
             t_enc.stop(e0)
             e0 = t_att.start()
-        octo.octo_attend_chunk(kc, vc, kcache, vcache, cached, q, kcur, vcur, out=out, ws=ws)
+        octo.octo_attend_chunk(kc, vc, kcache, vcache, cached, q, kcur, vcur, out=out, ws=ws,
+                               correction=w.jensen)
         if timed:
             t_att.stop(e0)
 
@@ -457,7 +460,8 @@ def cpu_baseline(w, state):
     from oracle_codecs import codec as oracle_codec
     from oracle_codecs import group_codec as oracle_group_codec
     inp, kc, vc, kcache, vcache = state[:5]
-    hk = oracle_codec(bits=w.bits, qjl=w.qjl)
+    hk = (oracle_group_codec(bits=w.bits, group=w.k_group) if w.k_group
+          else oracle_codec(bits=w.bits, qjl=w.qjl))
     hv = oracle_group_codec(bits=w.bits, group=w.v_group) if w.v_group else oracle_codec(bits=w.bits)
     hkc, hvc = kcache.to_host(), vcache.to_host()
     G = w.Hq // w.Hkv
@@ -520,7 +524,8 @@ def cpu_baseline(w, state):
                 t0 = time.perf_counter()
                 oatt.chunk_attention(inp["q"][:, :1].double().numpy(), pk, pv, hk, hv, w.T,
                                      inp["K_cur"][:, :1].double().numpy(),
-                                     inp["V_cur"][:, :1].double().numpy(), q_rows=rows)
+                                     inp["V_cur"][:, :1].double().numpy(), q_rows=rows,
+                                     correction=w.jensen)
                 dt += time.perf_counter() - t0
                 done += len(rows)
                 units += 1
@@ -587,7 +592,8 @@ def main():
         "config": {"workload": f"{a.workload}: {w.name}", "batch": w.B, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.d, "context": w.T, "bits": w.bits,
                    "qjl": w.qjl, "chunk_queries": w.chunk_q, "window": w.window,
-                   "value_group": w.v_group},
+                   "value_group": w.v_group, "key_group": w.k_group,
+                   "jensen_correction": w.jensen},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "attention_us": res["attention_us"], "encode_us": res["encode_us"],

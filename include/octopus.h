@@ -204,7 +204,8 @@ octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_codec, int32_t 
  * (group 16 or 32) when K uses the (b+1, b-1) split and V has the same b
  * (the symmetric K = V bit width of the paper's comparisons); its products
  * take Delta * code, exact in fp16, against the hi/lo weights, and the
- * zero-point term sum_j p_j z_j in fp32.  K must use the OCTOPUS codec.      */
+ * zero-point term sum_j p_j z_j in fp32.  K must use the OCTOPUS codec here
+ * (the group codec for keys is taken by octo_attend_chunk only).            */
 octo_status octo_attend_decode(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
                                const octo_cache_view* k_cache, const octo_cache_view* v_cache,
                                const void* q, octo_dtype q_dtype, int32_t num_q_heads,
@@ -260,10 +261,19 @@ octo_status octo_decode_step(const octo_codec_desc* k_codec, const octo_codec_de
                              float* out, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
-/* Workspace bytes needed by octo_attend_chunk for these shapes.             */
+/* Flags of octo_attend_chunk.
+ * OCTO_CHUNK_JENSEN_CORRECTION: subtract from every cached token's logit the
+ * Jensen bias of "Quantized Keys Steal Attention" (Sec. 4.2, Eq. 15; its
+ * appendix on the rotation): b = tau^2 / 24 * sum_j Delta_j^2 ||(R q)_j||^2
+ * over the key's groups j, tau the softmax scale (Eq. 15 has tau = 1/sqrt(d)).
+ * It models round-to-nearest noise, so the keys must use the group codec.  */
+#define OCTO_CHUNK_JENSEN_CORRECTION 1u
+
+/* Workspace bytes needed by octo_attend_chunk for these shapes and flags.   */
 octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
                                        int32_t num_q_heads, int32_t kv_heads, int32_t Tq,
-                                       int32_t cached_tokens, int32_t Tc, size_t* bytes);
+                                       int32_t cached_tokens, int32_t Tc, uint32_t flags,
+                                       size_t* bytes);
 
 /* octo_attend_chunk -- chunk-wise attention ("Quantized Keys Steal Attention",
  * Sec. 3, Token Structure and Attention Decomposition; OCTOPUS paper Sec. 4.3
@@ -281,8 +291,11 @@ octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B
  *              Tc == 0).
  *   out        device fp32 [B, num_q_heads, Tq, d].
  *   workspace  device, >= octo_chunk_workspace_bytes(...), 256-byte aligned.
- * Keys must not carry QJL in this path; values may use the group codec (as
- * for octo_attend_decode).  Operand range and precision: the
+ * Keys must not carry QJL in this path; keys and values may use the group
+ * codec, any b and g.  flags: 0 or OCTO_CHUNK_JENSEN_CORRECTION (above; the
+ * bias is one more MFMA k-slice per 16 keys, the product of fp16 query
+ * features -16 log2(e) tau^2/24 ||(R q)_j||^2 and key features Delta_j^2/16,
+ * so it shares the fp16 range limits below).  Operand range and precision: the
  * fp16 staging requires |rotated entries| < 65504 and rounds each operand to
  * 11 significant bits, so this path is meant for inputs without large
  * outlier channels (the decode path computes in fp32).  Tq == 0 is a no-op;
@@ -291,7 +304,7 @@ octo_status octo_attend_chunk(const octo_codec_desc* k_codec, const octo_codec_d
                               const octo_cache_view* k_cache, const octo_cache_view* v_cache,
                               int32_t cached_tokens, const void* q, const void* k_cur,
                               const void* v_cur, int32_t num_q_heads, int32_t Tq, int32_t Tc,
-                              float softmax_scale, float* out, void* workspace,
+                              float softmax_scale, uint32_t flags, float* out, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus

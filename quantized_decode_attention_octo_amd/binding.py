@@ -26,6 +26,7 @@ ABI_VERSION = 4
 STATUS = ["OCTO_OK", "OCTO_ERR_INVALID_ARGUMENT", "OCTO_ERR_UNSUPPORTED", "OCTO_ERR_ALIGNMENT",
           "OCTO_ERR_CAPACITY", "OCTO_ERR_WORKSPACE_TOO_SMALL", "OCTO_ERR_VERSION", "OCTO_ERR_HIP"]
 DTYPE_F32, DTYPE_BF16 = 0, 1
+CHUNK_JENSEN_CORRECTION = 1
 ROUND_LOCAL3X3, ROUND_SCALAR = 0, 1
 LAYOUT_TILE64 = 0
 
@@ -84,11 +85,11 @@ def lib():
                                          _P, ctypes.c_int, _I, _P, _I, ctypes.c_float, _P, _P,
                                          ctypes.c_size_t, _P]
         L.octo_chunk_workspace_bytes.argtypes = [ctypes.POINTER(CodecDesc), _I, _I, _I, _I, _I, _I,
-                                                 ctypes.POINTER(ctypes.c_size_t)]
+                                                 ctypes.c_uint32, ctypes.POINTER(ctypes.c_size_t)]
         L.octo_attend_chunk.argtypes = [ctypes.POINTER(CodecDesc), ctypes.POINTER(CodecDesc),
                                         ctypes.POINTER(CacheView), ctypes.POINTER(CacheView), _I,
-                                        _P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P,
-                                        ctypes.c_size_t, _P]
+                                        _P, _P, _P, _I, _I, _I, ctypes.c_float, ctypes.c_uint32,
+                                        _P, _P, ctypes.c_size_t, _P]
         L.octo_decode_step_workspace_bytes.argtypes = [ctypes.POINTER(CodecDesc), _I, _I, _I, _I,
                                                        ctypes.POINTER(ctypes.c_size_t)]
         L.octo_decode_step.argtypes = [ctypes.POINTER(CodecDesc), ctypes.POINTER(CodecDesc),
@@ -308,17 +309,21 @@ def octo_decode_step(k_codec, v_codec, k_cache, v_cache, q, k_new, v_new, k_wind
     return out
 
 
-def octo_chunk_workspace_bytes(k_codec, B, num_q_heads, kv_heads, Tq, cached_tokens, Tc):
+def octo_chunk_workspace_bytes(k_codec, B, num_q_heads, kv_heads, Tq, cached_tokens, Tc, flags=0):
     n = ctypes.c_size_t()
     _check(lib().octo_chunk_workspace_bytes(ctypes.byref(k_codec.desc), B, num_q_heads,
-                                            kv_heads, Tq, cached_tokens, Tc, ctypes.byref(n)))
+                                            kv_heads, Tq, cached_tokens, Tc,
+                                            ctypes.c_uint32(flags), ctypes.byref(n)))
     return n.value
 
 
 def octo_attend_chunk(k_codec, v_codec, k_cache, v_cache, cached_tokens, q, k_cur, v_cur,
-                      softmax_scale=0.0, out=None, ws=None):
+                      softmax_scale=0.0, out=None, ws=None, correction=False):
     """q[B, H_q, Tq, d], k_cur/v_cur[B, H_kv, Tc, d] (bf16, contiguous).
+    correction: the Jensen-bias correction of the cached keys' logits
+    (OCTO_CHUNK_JENSEN_CORRECTION; keys in the group codec).
     Returns out[B, H_q, Tq, d] fp32."""
+    flags = CHUNK_JENSEN_CORRECTION if correction else 0
     for t in (q, k_cur, v_cur):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise TypeError("q, k_cur and v_cur must be contiguous bfloat16 tensors")
@@ -326,13 +331,13 @@ def octo_attend_chunk(k_codec, v_codec, k_cache, v_cache, cached_tokens, q, k_cu
     Tc = k_cur.shape[2]
     if out is None:
         out = torch.empty(B, Hq, Tq, d, dtype=torch.float32, device=q.device)
-    need = octo_chunk_workspace_bytes(k_codec, B, Hq, k_cache.H, Tq, cached_tokens, Tc)
+    need = octo_chunk_workspace_bytes(k_codec, B, Hq, k_cache.H, Tq, cached_tokens, Tc, flags)
     if ws is None or ws.numel() < need + 256:
         ws = workspace(need, q.device)
     _check(lib().octo_attend_chunk(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
                                    ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
                                    cached_tokens, _ptr(q), _ptr(k_cur), _ptr(v_cur), Hq, Tq, Tc,
-                                   float(softmax_scale), _ptr(out),
+                                   ctypes.c_float(softmax_scale), ctypes.c_uint32(flags), _ptr(out),
                                    ctypes.c_void_p(_aligned_ptr(ws)), ws.numel() - 256,
                                    _stream(q.device)))
     return out

@@ -55,12 +55,19 @@ __device__ inline int key_column(int k) {
 // One workgroup takes 64 rows, one wavefront per row for the transform; the
 // transposed store goes through LDS so that 64 consecutive columns are
 // written together.
+//
+// With `feat` set (queries of the Jensen-bias correction), row t also gets
+// kFeat fp16 features: slot j < 128 / feat_gs holds feat_c ||(R x_t)_j||^2
+// over group j of the rotated coordinates, the other slots 0.
+constexpr int kFeat = 8;           // feature slots per row: groups of g >= 16
 template <bool TRANSPOSED>
 __global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __restrict__ in,
                                                           int T, int T_out, uint64_t seed,
                                                           float post,
                                                           _Float16* __restrict__ out,
-                                                          int out_rows, int out_off) {
+                                                          int out_rows, int out_off,
+                                                          _Float16* __restrict__ feat = nullptr,
+                                                          int feat_gs = 32, float feat_c = 0.0f) {
   __shared__ _Float16 tile[TRANSPOSED ? 64 * 130 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int plane = blockIdx.y;
@@ -91,6 +98,21 @@ __global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __rest
         _Float16* dst = out + ((size_t)plane * out_rows + out_off + t) * kHeadDim;
         dst[lane] = (_Float16)(a * post);
         dst[lane + 64] = (_Float16)(b * post);
+      }
+      if (!TRANSPOSED && feat != nullptr) {        // uniform branch
+        // group sums of the squared rotated coordinates (a: coordinates
+        // 0..63, b: 64..127), reduced within the groups' lanes
+        float sa = a * a * (kInvSqrtD * kInvSqrtD), sb = b * b * (kInvSqrtD * kInvSqrtD);
+        for (int m = 1; m < feat_gs; m <<= 1) {
+          sa += __shfl_xor(sa, m, 64);
+          sb += __shfl_xor(sb, m, 64);
+        }
+        const int ga = 64 / feat_gs;                  // groups held in a
+        const int j = lane & (kFeat - 1);
+        const float fa = __shfl(sa, min(j, ga - 1) * feat_gs, 64);
+        const float fb = __shfl(sb, max(min(j - ga, ga - 1), 0) * feat_gs, 64);
+        const float f = j < ga ? fa : (j < 2 * ga ? fb : 0.0f);
+        if (t < T && lane < kFeat) feat[((size_t)plane * T + t) * kFeat + lane] = (_Float16)(feat_c * f);
       }
     }
   }
@@ -194,6 +216,10 @@ struct ChunkArgs {
   int Hq, Hkv, Tq, Tk, Tk_pad;
   int q_tiles;         // query tiles per (batch, head)
   uint64_t vseed;
+  // Jensen-bias correction: fp16 feature rows whose product is minus the
+  // bias in log2 units ([B][Hq][Tq][kFeat] queries, [B][Hkv][Tk_pad][kFeat] keys)
+  const _Float16* qfeat;
+  const _Float16* kfeat;
 };
 
 // Lane layout of v_mfma_f32_16x16x32_f16 (wave of 64, L = lane):
@@ -212,9 +238,19 @@ struct ChunkArgs {
 // XCDs in turn, so the linear id is mapped such that all query tiles of one
 // (batch, head) run on the same XCD and stream its keys and values through
 // that XCD's L2 together.
+//
+// CORR: the Jensen-bias correction ("Quantized Keys Steal Attention",
+// Eq. 15).  Its bias is a rank-(128 / g) product of query and key features,
+// so it is one more k-slice of the score MFMA per 16 keys, whose slots 0..7
+// (lane group 0) hold the features and the rest zeros: the key features ride
+// in the 8 padding halves of each key row of the tile, the workgroup's query
+// features sit in LDS (1 KB), so four workgroups still share a CU.
+template <bool CORR>
 __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
+  static_assert(kKStride >= kHeadDim + kFeat, "key features fit the row padding");
   __shared__ _Float16 ks[kBN * kKStride];
   __shared__ _Float16 vs[kHeadDim * kVStride];
+  __shared__ _Float16 qfs[CORR ? kBM * kFeat : 1];
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
   const int col = L & 15, grp = L >> 4;
   const int n_units = gridDim.x;
@@ -230,6 +266,14 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
   const int hq = bh % a.Hq, b = bh / a.Hq;
   const int hk = hq / (a.Hq / a.Hkv);
   const int q0 = tile * kBM + wave * 16 * kRG;
+  if constexpr (CORR) {
+    // the workgroup's 64 query feature rows (rows past Tq repeat the last)
+    for (int r = tid; r < kBM; r += kCThreads) {
+      const int qrow = min(tile * kBM + r, a.Tq - 1);
+      *reinterpret_cast<half8*>(&qfs[r * kFeat]) = *reinterpret_cast<const half8*>(
+          a.qfeat + (((size_t)b * a.Hq + hq) * a.Tq + qrow) * kFeat);
+    }
+  }
 
   // Q^T fragments (B operand): query q0 + 16 rg + col, dims 32 s + 8 grp + e.
   half8 qf[kRG][4];
@@ -264,6 +308,12 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
   _Float16* const vs_dst = &vs[(tid >> 3) * kVStride + (tid & 7) * 8];
   constexpr int kChunks = 1024 / kCThreads;
   auto copy_tile = [&](int kt0) {
+    if constexpr (CORR) {
+      const _Float16* kf = a.kfeat + (((size_t)b * a.Hkv + hk) * a.Tk_pad + kt0) * kFeat;
+      for (int r = tid; r < kBN; r += kCThreads)
+        *reinterpret_cast<half8*>(&ks[r * kKStride + kHeadDim]) =
+            *reinterpret_cast<const half8*>(kf + (size_t)r * kFeat);
+    }
     const char* kb = reinterpret_cast<const char*>(a.k + kbase + (size_t)kt0 * kHeadDim);
     const char* vb = reinterpret_cast<const char*>(a.vt + vbase + kt0);
 #pragma unroll 4
@@ -280,6 +330,15 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     constexpr bool MASKED = decltype(masked_c)::value;
     // scores of the 64 keys (log2 units): st[kt][rg][r] = key kt0 + 16 kt + 4 grp + r
     floatx4 st[4][kRG];
+    half8 qf5[CORR ? kRG : 1];
+    const half8 zero8 = {};
+    if constexpr (CORR) {
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg) {
+        qf5[rg] = *reinterpret_cast<const half8*>(&qfs[(wave * 16 * kRG + 16 * rg + col) * kFeat]);
+        qf5[rg] = grp == 0 ? qf5[rg] : zero8;          // slots 8..31 are zero
+      }
+    }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
@@ -291,6 +350,14 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg)
           st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[rg][s], st[kt][rg], 0, 0, 0);
+      }
+      if constexpr (CORR) {
+        // minus the Jensen bias of keys 16 kt + (0..15), in log2 units
+        half8 kf5 = *reinterpret_cast<const half8*>(&ks[(16 * kt + col) * kKStride + kHeadDim]);
+        kf5 = grp == 0 ? kf5 : zero8;
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg)
+          st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf5, qf5[rg], st[kt][rg], 0, 0, 0);
       }
     }
     half8 pf[kRG][2];
@@ -456,21 +523,53 @@ __global__ __launch_bounds__(256) void group_decode_rows_kernel(const uint32_t* 
   }
 }
 
+// Key features of the Jensen-bias correction: row t < Tk_pad of a plane gets
+// Delta^_tj^2 / 16 in slot j < 128 / GS for the cached tokens (t < cached),
+// 0 elsewhere (current tokens, tile padding, unused slots).  The factor 1/16
+// keeps Delta^2 <= 448^2 in the fp16 range; the query features carry 16.
+template <int VB, int GS>
+__global__ __launch_bounds__(256) void key_features_kernel(const uint32_t* __restrict__ idx,
+                                                           int capacity, int cached, int Tk_pad,
+                                                           _Float16* __restrict__ feat) {
+  constexpr int G = kHeadDim / GS, WC = VB * kHeadDim / 32, W = group_record_words(VB, GS);
+  const size_t plane = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  for (int e = threadIdx.x; e < 64 * kFeat; e += 256) {
+    const int t = t0 + e / kFeat, j = e % kFeat;
+    float f = 0.0f;
+    if (t < cached && j < G) {
+      const uint32_t sw = idx[tile_word(plane, capacity, t, WC + j / 4, W)];
+      const float dh = e4m3_value((sw >> (8 * (j % 4))) & 0xffu);
+      f = dh * dh * 0.0625f;
+    }
+    feat[(plane * Tk_pad + t) * kFeat + j] = (_Float16)f;
+  }
+}
+
 struct ChunkPlan {
   int Tk, Tk_pad;
-  size_t q_off, k_off, v_off, total;
+  size_t q_off, k_off, v_off, qf_off, kf_off, total;
 };
 
-ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Tq, int cached, int Tc) {
+// corr: room for the correction's query and key feature rows after the rows
+ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Tq, int cached, int Tc, bool corr) {
   ChunkPlan p;
   p.Tk = cached + Tc;
   p.Tk_pad = (p.Tk + kBN - 1) / kBN * kBN;
   const size_t row = kHeadDim * sizeof(_Float16);
+  auto up = [](size_t n) { return (n + 255) / 256 * 256; };
   p.q_off = 0;
-  p.k_off = ((size_t)B * Hq * Tq * row + 255) / 256 * 256;
+  p.k_off = up((size_t)B * Hq * Tq * row);
   const size_t kv = (size_t)B * Hkv * p.Tk_pad * row;
-  p.v_off = p.k_off + (kv + 255) / 256 * 256;
+  p.v_off = p.k_off + up(kv);
   p.total = p.v_off + kv;
+  p.qf_off = p.kf_off = 0;
+  if (corr) {
+    const size_t frow = kFeat * sizeof(_Float16);
+    p.qf_off = up(p.total);
+    p.kf_off = p.qf_off + up((size_t)B * Hq * Tq * frow);
+    p.total = p.kf_off + (size_t)B * Hkv * p.Tk_pad * frow;
+  }
   return p;
 }
 
@@ -530,17 +629,18 @@ using namespace octo;
 extern "C" octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
                                                   int32_t num_q_heads, int32_t kv_heads,
                                                   int32_t Tq, int32_t cached_tokens, int32_t Tc,
-                                                  size_t* bytes) {
+                                                  uint32_t flags, size_t* bytes) {
   clear_error();
   Codec kc;
   octo_status s = resolve_codec(k_codec, "octo_chunk_workspace_bytes", &kc, false);
   if (s != OCTO_OK) return s;
-  if (kc.group)
-    return fail(OCTO_ERR_UNSUPPORTED, "octo_chunk_workspace_bytes: keys need the OCTOPUS codec");
+  if (flags & ~OCTO_CHUNK_JENSEN_CORRECTION)
+    return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_chunk_workspace_bytes: unknown flags 0x%x", flags);
   if (!bytes) return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_chunk_workspace_bytes: bytes is NULL");
   if (B < 1 || num_q_heads < 1 || kv_heads < 1 || Tq < 0 || cached_tokens < 0 || Tc < 0)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_chunk_workspace_bytes: bad sizes");
-  *bytes = chunk_plan(B, num_q_heads, kv_heads, Tq, cached_tokens, Tc).total;
+  *bytes = chunk_plan(B, num_q_heads, kv_heads, Tq, cached_tokens, Tc,
+                      (flags & OCTO_CHUNK_JENSEN_CORRECTION) != 0).total;
   return OCTO_OK;
 }
 
@@ -550,8 +650,9 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
                                          const octo_cache_view* v_cache, int32_t cached_tokens,
                                          const void* q, const void* k_cur, const void* v_cur,
                                          int32_t num_q_heads, int32_t Tq, int32_t Tc,
-                                         float softmax_scale, float* out, void* workspace,
-                                         size_t workspace_bytes, hipStream_t stream) {
+                                         float softmax_scale, uint32_t flags, float* out,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
   clear_error();
   const char* what = "octo_attend_chunk";
   Codec kc, vc;
@@ -561,7 +662,12 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   if ((s = check_cache(k_cache, kc, what)) != OCTO_OK) return s;
   if ((s = check_cache(v_cache, vc, what)) != OCTO_OK) return s;
   if (kc.qjl || vc.qjl) return fail(OCTO_ERR_UNSUPPORTED, "%s: QJL is not supported here", what);
-  if (kc.group) return fail(OCTO_ERR_UNSUPPORTED, "%s: keys need the OCTOPUS codec", what);
+  if (flags & ~OCTO_CHUNK_JENSEN_CORRECTION)
+    return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: unknown flags 0x%x", what, flags);
+  const bool corr = (flags & OCTO_CHUNK_JENSEN_CORRECTION) != 0;
+  if (corr && !kc.group)
+    return fail(OCTO_ERR_UNSUPPORTED,
+                "%s: the Jensen-bias correction models round-to-nearest keys (group codec)", what);
   if (k_cache->batch != v_cache->batch || k_cache->kv_heads != v_cache->kv_heads ||
       k_cache->capacity != v_cache->capacity)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: K and V caches differ in shape", what);
@@ -581,7 +687,7 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: q, out, k_cur, v_cur must be set", what);
   if (((uintptr_t)q | (uintptr_t)k_cur | (uintptr_t)v_cur) & 1 || ((uintptr_t)out & 3))
     return fail(OCTO_ERR_ALIGNMENT, "%s: q, k_cur, v_cur or out misaligned", what);
-  const ChunkPlan p = chunk_plan(B, num_q_heads, Hkv, Tq, cached_tokens, Tc);
+  const ChunkPlan p = chunk_plan(B, num_q_heads, Hkv, Tq, cached_tokens, Tc, corr);
   if (!workspace || workspace_bytes < p.total)
     return fail(OCTO_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", what,
                 workspace_bytes, p.total);
@@ -594,10 +700,16 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   _Float16* vr = reinterpret_cast<_Float16*>(ws + p.v_off);
   const int planes_q = B * num_q_heads, planes_kv = B * Hkv;
 
-  const float scale2 = (softmax_scale > 0.0f ? softmax_scale : kInvSqrtD) * kLog2e;
+  const float tau = softmax_scale > 0.0f ? softmax_scale : kInvSqrtD;
+  const float scale2 = tau * kLog2e;
+  _Float16* qf = corr ? reinterpret_cast<_Float16*>(ws + p.qf_off) : nullptr;
+  _Float16* kf = corr ? reinterpret_cast<_Float16*>(ws + p.kf_off) : nullptr;
+  // query features: minus 16 log2(e) tau^2 / 24 ||(R q)_j||^2 (the key
+  // features carry Delta^2 / 16), so that their product is -b in log2 units
+  const float feat_c = -16.0f * kLog2e * tau * tau / 24.0f;
   hipLaunchKernelGGL(rotate_rows_kernel<false>, dim3((Tq + 63) / 64, planes_q), dim3(256), 0,
                      stream, static_cast<const uint16_t*>(q), Tq, Tq, kc.seed, kInvSqrtD * scale2,
-                     qr, Tq, 0);
+                     qr, Tq, 0, qf, corr ? kc.group : 32, feat_c);
   const int cur_out = p.Tk_pad - cached_tokens;  // current rows plus the zero tile padding
   if (cur_out > 0) {
     hipLaunchKernelGGL(rotate_rows_kernel<false>, dim3((cur_out + 63) / 64, planes_kv), dim3(256),
@@ -612,6 +724,22 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
         !decode_rows(v_cache, vc, cached_tokens, vr, p.Tk_pad, true, stream))
       return fail(OCTO_ERR_UNSUPPORTED, "%s: split not compiled", what);
   }
+  if (corr && p.Tk_pad > 0) {
+    const dim3 fgrid(p.Tk_pad / 64, planes_kv);
+    switch (kc.bits * 100 + kc.group) {
+#define OCTO_KEY_FEATURES(VB, GS)                                                            \
+  hipLaunchKernelGGL((key_features_kernel<VB, GS>), fgrid, dim3(256), 0, stream, k_cache->idx, \
+                     k_cache->capacity, cached_tokens, p.Tk_pad, kf)
+      case 216: OCTO_KEY_FEATURES(2, 16); break;
+      case 232: OCTO_KEY_FEATURES(2, 32); break;
+      case 316: OCTO_KEY_FEATURES(3, 16); break;
+      case 332: OCTO_KEY_FEATURES(3, 32); break;
+      case 416: OCTO_KEY_FEATURES(4, 16); break;
+      case 432: OCTO_KEY_FEATURES(4, 32); break;
+#undef OCTO_KEY_FEATURES
+      default: return fail(OCTO_ERR_UNSUPPORTED, "%s: group codec not compiled", what);
+    }
+  }
   if ((s = check_launch(what)) != OCTO_OK) return s;
   ChunkArgs a;
   a.q = qr;
@@ -625,9 +753,14 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   a.Tk_pad = p.Tk_pad;
   a.q_tiles = (Tq + kBM - 1) / kBM;
   a.vseed = vc.seed;
+  a.qfeat = qf;
+  a.kfeat = kf;
   const long long units = (long long)a.q_tiles * num_q_heads * B;
   if (units > 0x7fffffffLL)
     return fail(OCTO_ERR_UNSUPPORTED, "%s: too many query tiles", what);
-  hipLaunchKernelGGL(chunk_attn_kernel, dim3((unsigned)units), dim3(kCThreads), 0, stream, a);
+  if (corr)
+    hipLaunchKernelGGL(chunk_attn_kernel<true>, dim3((unsigned)units), dim3(kCThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(chunk_attn_kernel<false>, dim3((unsigned)units), dim3(kCThreads), 0, stream, a);
   return check_launch(what);
 }

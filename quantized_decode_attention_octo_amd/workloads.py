@@ -41,6 +41,8 @@ class Workload:
     chunk_q: int = 0       # > 0: chunk workload with this many queries / current tokens
     window: int = 0        # > 0: decode-step workload with a residual window of this size
     v_group: int = 0       # > 0: values in the group-wise codec with this group size
+    k_group: int = 0       # > 0: keys in the group-wise codec (chunk workloads)
+    jensen: bool = False   # chunk workloads: the Jensen-bias correction of cached logits
     seed: int = 0
 
     @property
@@ -66,6 +68,10 @@ WORKLOADS = {
     "step32k": Workload("step32k", "decode step, GQA 28/4, batch 1, context up to 32768 (last 32 tokens native), bf16 + outliers, b=4",
                         B=1, Hq=28, Hkv=4, d=128, T=32768, bits=4, dtype="bf16", outliers=True,
                         window=32),
+    "chunk_qksa": Workload("chunk_qksa", "MHA 40 heads, d=128, 1560 queries over 9360 cached + 1560 current "
+                           "tokens, bf16, group-32 INT2 keys and values, Jensen-bias correction",
+                           B=1, Hq=40, Hkv=40, d=128, T=9360, bits=2, dtype="bf16", chunk_q=1560,
+                           k_group=32, v_group=32, jensen=True),
     "chunk": Workload("chunk", "MHA 40 heads, d=128, 1560 queries over 9360 cached + 1560 current tokens, bf16, b=2",
                       B=1, Hq=40, Hkv=40, d=128, T=9360, bits=2, dtype="bf16", chunk_q=1560),
 }

@@ -217,15 +217,20 @@ def test_chunk_errors(L):
     kd, vd = desc(bits=2), desc(bits=2)
     kv, vv = view(H=2, cap=256), view(H=2, cap=256)
     n = ctypes.c_size_t()
-    assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, ctypes.byref(n)) == 0
+    assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 0, ctypes.byref(n)) == 0
     need = n.value
     # fp16 rotated queries [1, 2, 64, 128] and key / value rows [1, 2, 192, 128]
     assert need == (64 * 2 + 2 * 2 * 192) * 256
+    # the correction adds 8 fp16 features per query row and per key row
+    assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 1, ctypes.byref(n)) == 0
+    assert n.value == need + 64 * 2 * 16 + 2 * 192 * 16
+    assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 2, ctypes.byref(n)) == 1
 
-    def ch(kd=kd, vd=vd, kv=kv, vv=vv, cached=128, Hq=2, Tq=64, Tc=64, ws=4096, ws_bytes=need):
+    def ch(kd=kd, vd=vd, kv=kv, vv=vv, cached=128, Hq=2, Tq=64, Tc=64, ws=4096, ws_bytes=need,
+           flags=0):
         p = ctypes.c_void_p(4096)
         return L.octo_attend_chunk(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(kv),
-                                   ctypes.byref(vv), cached, p, p, p, Hq, Tq, Tc, 0.0, p, ws,
+                                   ctypes.byref(vv), cached, p, p, p, Hq, Tq, Tc, 0.0, flags, p, ws,
                                    ws_bytes, None)
     assert ch(ws_bytes=need - 1) == 5
     assert ch(ws=4352 + 1) == 3
@@ -234,6 +239,8 @@ def test_chunk_errors(L):
     assert ch(Tq=-1) == 1
     assert ch(kd=desc(bits=2, qjl=1), kv=view(H=2, cap=256, qjl=True)) == 2
     assert ch(Tq=0) == 0                                     # nothing to do
+    assert ch(flags=4) == 1                                  # unknown flag
+    assert ch(flags=1) == 2                                  # correction with OCTOPUS keys
 
 
 def gdesc(bits=2, group=32, b_dir=0, b_nrm=0, qjl=0):
@@ -275,10 +282,11 @@ def test_group_codec_errors(L):
     assert dec(L, kd, gdesc(bits=2), view(H=2), gv, ws_bytes=0) == 5        # accepted up to here
     n = ctypes.c_size_t()
     assert L.octo_decode_workspace_bytes(ctypes.byref(gdesc()), 1, 4, 2, 128, ctypes.byref(n)) == 2
-    assert L.octo_chunk_workspace_bytes(ctypes.byref(gdesc()), 1, 2, 2, 64, 128, 64,
-                                        ctypes.byref(n)) == 2
+    # the chunk path takes group keys (and the correction needs them)
+    assert L.octo_chunk_workspace_bytes(ctypes.byref(gdesc()), 1, 2, 2, 64, 128, 64, 1,
+                                        ctypes.byref(n)) == 0
     assert L.octo_attend_chunk(ctypes.byref(gdesc()), ctypes.byref(gdesc()), ctypes.byref(gv),
-                               ctypes.byref(gv), 64, p, p, p, 2, 64, 64, 0.0, p, p, 1 << 20,
-                               None) == 2
+                               ctypes.byref(gv), 64, p, p, p, 2, 64, 64, 0.0, 1, p, p, 16,
+                               None) == 5
     assert L.octo_decode_tokens(ctypes.byref(gdesc()), ctypes.byref(gv), 100, 29, p, None) == 4
     assert L.octo_decode_tokens(ctypes.byref(gdesc()), ctypes.byref(gv), 0, 4, None, None) == 1

@@ -11,7 +11,10 @@ round-to-nearest codes.  Checked against the oracle (oracle/group.py):
   * octo_attend_decode and octo_attend_chunk with OCTOPUS keys and group
     values: max-abs 2e-3 against the oracle's float64 attention on the
     GPU-written caches, at small ragged sizes, the full 32k-context size,
-    empty and clipped lengths and several GQA group sizes.
+    empty and clipped lengths and several GQA group sizes;
+  * octo_attend_chunk with group keys, with and without the Jensen-bias
+    correction of cached logits (QKSA Sec. 4.2, Eq. 15), the same bar, and
+    the correction's own effect well above the error.
 """
 import numpy as np
 import pytest
@@ -199,3 +202,49 @@ def test_group_chunk(group, cached, tc):
         err = max(err, np.abs(out[0, h] - ref[0, 0]).max())
     say(f"group chunk g={group} cached={cached} tc={tc} err {err:.3e}")
     assert err <= ATOL
+
+
+@pytest.mark.parametrize("kbits,kgroup,vbits,vgroup,correction,cached,tc", [
+    (2, 32, 2, 32, False, None, None),
+    (2, 32, 2, 32, True, None, None),
+    (3, 16, 3, 16, True, 57, None),
+    (4, 32, 2, 16, True, None, 0),
+    (2, 16, 2, 32, True, 0, None),
+])
+def test_group_keys_chunk_and_jensen_correction(kbits, kgroup, vbits, vgroup, correction, cached, tc):
+    """Group-codec keys in the chunk path ("Quantized Keys Steal Attention"
+    setting: group-wise round-to-nearest keys and values), with and without
+    the Jensen-bias correction of cached logits (Eq. 15, its appendix on the
+    rotation), against the oracle on the GPU-written caches."""
+    w = workload("chunk", Hq=4, Hkv=2, T=300, chunk_q=150)
+    inp = make_inputs(w)
+    kc, hk = group_codecs(kbits, kgroup, seed=3)
+    vc, hv = group_codecs(vbits, vgroup, seed=4)
+    K, V = inp["K"], inp["V"]
+    cached = K.shape[2] if cached is None else cached
+    cap = -(-K.shape[2] // 64) * 64
+    kcache = encode_gpu(K, kc, capacity=cap)
+    vcache = encode_gpu(V, vc, capacity=cap)
+    q, kcur, vcur = inp["q"], inp["K_cur"], inp["V_cur"]
+    if tc is not None:
+        kcur, vcur = kcur[:, :, :tc].contiguous(), vcur[:, :, :tc].contiguous()
+    out = octo.octo_attend_chunk(kc, vc, kcache, vcache, cached, q.cuda(), kcur.cuda(), vcur.cuda(),
+                                 correction=correction)
+    torch.cuda.synchronize()
+    out = out.cpu().double().numpy()
+    hkc, hvc = kcache.to_host(), vcache.to_host()
+    G = w.Hq // w.Hkv
+    err = moved = 0.0
+    for h in range(w.Hq):
+        g = h // G
+        args = (q[:, h:h + 1].double().numpy(), plane_of(hkc, 0, g), plane_of(hvc, 0, g), hk, hv,
+                cached, kcur[:, g:g + 1].double().numpy(), vcur[:, g:g + 1].double().numpy())
+        ref = oatt.chunk_attention(*args, correction=correction)
+        err = max(err, np.abs(out[0, h] - ref[0, 0]).max())
+        if correction and cached and kcur.shape[2]:
+            moved = max(moved, np.abs(ref - oatt.chunk_attention(*args)).max())
+    say(f"group-key chunk K b{kbits} g{kgroup} V b{vbits} g{vgroup} corr={correction} "
+        f"cached={cached} tc={tc}: err {err:.3e} (correction moves the output by {moved:.3e})")
+    assert err <= ATOL
+    if correction and cached and kcur.shape[2]:
+        assert moved > 10 * err                     # the test sees the correction itself
