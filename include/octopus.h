@@ -24,8 +24,9 @@
  *   - Supported now: head_dim = 128; (b_dir, b_nrm) in {(3,1), (4,2), (5,3)}
  *     (the paper's (b+1, b-1) split for b = 2, 3, 4; Sec. 3.3) and the uniform
  *     splits {(2,2), (3,3), (4,4)}; for decode, 1 to 16 query heads per KV
- *     head; QJL on keys only, in the decode path only.  Anything else returns
- *     OCTO_ERR_UNSUPPORTED.
+ *     head; QJL on keys only, in the decode path only; the group-wise codec
+ *     (group 16 or 32, b = 2, 3, 4; described below) for values, and for
+ *     keys in the chunk path.  Anything else returns OCTO_ERR_UNSUPPORTED.
  *
  * Cache layout (OCTO_LAYOUT_TILE64).  The paper fixes no bit layout; this one
  * is this library's.  A stream is a little-endian LSB-first bit string: field
