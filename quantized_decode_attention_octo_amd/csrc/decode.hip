@@ -430,6 +430,12 @@ __device__ void encode_one(const uint16_t* x, const floatx4* lut, const float* m
   }
 }
 
+// A zero block standing in for the first block's speculative loads when the
+// cache holds no tokens: 64 tokens of the widest record (words past the
+// record's end are clamped to its last word).
+constexpr int kZeroBlockWords = 64 * 40;
+__device__ uint32_t g_zero_block[kZeroBlockWords];
+
 template <int BD, int BN, bool QJL, int MODE, int NW, int VG = 0>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * NW, kWaves = NW;
@@ -439,6 +445,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   constexpr int kTab = PRE ? K * K * R : K * K;     // entries per table (16 B each)
   constexpr int kTabBytes = (VG || (PRE && BIG) ? 1 : 2) * kTab * 16;   // VG: the K table alone
   using GR = GroupRecord<(VG ? BD - 1 : 2), (VG ? VG : 32)>;            // the value record (VG)
+  static_assert(BlockWords<BD, BN, QJL, VG>::WI <= kZeroBlockWords / 64 &&
+                    BlockWords<BD, BN, QJL, VG>::VW <= kZeroBlockWords / 64,
+                "the zero block covers a 64-token tile of every stream");
   static_assert(GR::kRows * 32 * 4 <= kIdxRows * kIdxRow * 2, "value records fit a wave's rows");
   constexpr int kRedBytes = kWaves * kMaxG * kHeadDim * 4;
   constexpr int kUnion = kTabBytes > kRedBytes ? kTabBytes : kRedBytes;
@@ -470,61 +479,62 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   float* red_o = reinterpret_cast<float*>(smem);          // [wave][head][128]
 
   // ---- every global load of the prologue goes out first, none waiting for
-  // another: codebooks, q, the first block (speculatively: any t0 below the
-  // capacity is in bounds, whatever seq_lens holds) and seq_lens.
-  // The codebooks are read at constant indices (scalar loads of the kernel
-  // arguments), so that their LDS stores wait on no vector load; q is kept
-  // as raw bits until the tables are built.
-  float cx_k = 0.0f, cx_v = 0.0f, cr_k = 0.0f, cr_v = 0.0f;
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-    cx_k = L == i ? a.kcb.xi[i] : cx_k;
-    cx_v = L == i ? a.vcb.xi[i] : cx_v;
-  }
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    cr_k = L == i ? a.kcb.rho[i] : cr_k;
-    cr_v = L == i ? a.vcb.rho[i] : cr_v;
-  }
+  // another: codebooks, q, the first block and seq_lens.  The kernel
+  // arguments their addresses need come in one batch of scalar loads (a
+  // first use further down would wait for its own round trip).  The
+  // codebooks are vector loads of the argument block, one value per lane;
+  // the first block is loaded unconditionally (a block of the plane below
+  // min(max_len, capacity), or a zero block when that is empty), so that the
+  // compiler's counts of outstanding loads are exact and the table build
+  // waits for the codebooks alone.
+  const int cbl = min(L, kMaxXi + kMaxRho - 1);
+  const float cb_k = reinterpret_cast<const float*>(&a.kcb)[cbl];
+  const float cb_v = reinterpret_cast<const float*>(&a.vcb)[cbl];
+  asm volatile("" ::"s"(a.q), "s"(a.k_idx), "s"(a.v_idx), "s"(a.kgamma), "s"(a.vgamma),
+               "s"(a.seq_lens), "s"(a.max_len), "s"(a.capacity), "s"(a.split_len), "s"(a.Hq),
+               "s"(a.G), "s"(a.Hkv), "s"(a.q_bf16));
   constexpr int kHeadsPerWave = kMaxG / kWaves;
   uint32_t qraw[kHeadsPerWave][2];                 // bf16 or fp32 bits
 #pragma unroll
   for (int k = 0; k < kHeadsPerWave; ++k) {
-    const int hh = wave + kWaves * k;
-    qraw[k][0] = qraw[k][1] = 0u;
-    if (hh < G) {
-      const size_t qo = ((size_t)b * a.Hq + (size_t)g * G + hh) * kHeadDim;
-      if (a.q_bf16) {
-        qraw[k][0] = static_cast<const uint16_t*>(a.q)[qo + L];
-        qraw[k][1] = static_cast<const uint16_t*>(a.q)[qo + L + 64];
-      } else {
-        qraw[k][0] = static_cast<const uint32_t*>(a.q)[qo + L];
-        qraw[k][1] = static_cast<const uint32_t*>(a.q)[qo + L + 64];
-      }
-    }
+    // heads past G read head G - 1 (unused): unconditional loads
+    const int hh = min(wave + kWaves * k, G - 1);
+    const size_t qo = ((size_t)b * a.Hq + (size_t)g * G + hh) * kHeadDim;
+    const uint32_t* q32 = static_cast<const uint32_t*>(a.q);
+    const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
+    qraw[k][0] = a.q_bf16 ? (uint32_t)q16[qo + L] : q32[qo + L];
+    qraw[k][1] = a.q_bf16 ? (uint32_t)q16[qo + L + 64] : q32[qo + L + 64];
   }
   const int t_begin = split * a.split_len;
   int t0 = t_begin + wave * kBlock;
   BlockWords<BD, BN, QJL, VG> blk;
-  if (!QJL && t0 < min(a.max_len, a.capacity)) {
-    load_block(blk, a, plane, t0, L);
-    load_gv(blk, a, plane, t0, L);
+  if (!QJL) {
+    const int lim = min(a.max_len, a.capacity);
+    DecodeArgs f = a;
+    size_t fplane = plane;
+    int ft0 = min(t0, (lim - 1) & ~(kBlock - 1));
+    if (lim <= 0) {                       // uniform: scalar selects, no branch
+      f.k_idx = f.v_idx = g_zero_block;
+      f.kgamma = f.vgamma = reinterpret_cast<const float*>(g_zero_block);
+      f.capacity = 64;
+      fplane = 0;
+      ft0 = 0;
+    }
+    load_block(blk, f, fplane, ft0, L);
+    load_gv(blk, f, fplane, ft0, L);
   }
-  int len = a.seq_lens[b];
-  len = max(0, min(len, min(a.max_len, a.capacity)));
-  // uniform: the loop and its prefetch test become scalar branches
-  const int t_end = __builtin_amdgcn_readfirstlane(min(len, t_begin + a.split_len));
-  if (a.step && split == 0 && g == 0 && tid == 0)   // the step's (P, n) for the merge launch
-    a.snap[b] = make_int2(len, max(0, min(a.win_lens[b], a.window - 1)));
+  const int len_raw = __hip_atomic_load(a.seq_lens + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int win_raw = a.step ? __hip_atomic_load(a.win_lens + b, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) : 0;
 
   // ---- tables: codebooks to LDS first, then the table entries
   if (tid < K) {
-    cxk[tid] = cx_k;
-    cxv[tid] = cx_v;
+    cxk[tid] = cb_k;
+    cxv[tid] = cb_v;
   }
-  if (tid < R) {
-    crk[tid] = cr_k;
-    crv[tid] = cr_v;
+  if (tid >= kMaxXi && tid < kMaxXi + R) {
+    crk[tid - kMaxXi] = cb_k;
+    crv[tid - kMaxXi] = cb_v;
   }
   lds_barrier();
   const int n_tables = VG ? 1 : (PRE || !a.shared_tables ? 2 : 1);
@@ -569,7 +579,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     const int qsh = a.q_bf16 ? 16 : 0;
     float q0 = __uint_as_float(qraw[k][0] << qsh) * s_lo;
     float q1 = __uint_as_float(qraw[k][1] << qsh) * s_hi;
-    if (wave + kWaves * k < G) wht128(q0, q1);
+    if (wave + kWaves * k < G)
+      wht128(q0, q1);
+    else
+      q0 = q1 = 0.0f;                   // rows past G are zero
     qs[hh * 132 + L] = q0 * kInvSqrtD;
     qs[hh * 132 + L + 64] = q1 * kInvSqrtD;
   }
@@ -655,6 +668,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < 3; ++i) vrow[i] = min(16 * i + col, kNTri - 1) * kIdxRow + 4 * grp4;
   lds_barrier();                 // every wave is done with qs before it holds indices
+
+  const int len = max(0, min(len_raw, min(a.max_len, a.capacity)));
+  // uniform: the loop and its prefetch test become scalar branches
+  const int t_end = __builtin_amdgcn_readfirstlane(min(len, t_begin + a.split_len));
+  if (a.step && split == 0 && g == 0 && tid == 0)   // the step's (P, n) for the merge launch
+    a.snap[b] = make_int2(len, max(0, min(win_raw, a.window - 1)));
 
   if (QJL && t0 < t_end) {                                   // (registers are short)
     load_block(blk, a, plane, t0, L);
