@@ -205,8 +205,16 @@ constexpr int kCThreads = 64 * kCWaves;
 constexpr int kBM = 16 * kRG * kCWaves;   // 64 queries per workgroup
 constexpr int kXcds = 8;        // workgroups are dealt round-robin to the XCDs
 constexpr int kBN = 64;         // keys per LDS tile
-constexpr int kKStride = 136;   // halves per key row in LDS (128 + 8 pad)
-constexpr int kVStride = 72;    // halves per transposed value row in LDS (64 + 8 pad)
+// LDS tiles are unpadded, written by direct global-to-LDS loads (16 bytes a
+// lane, 1 KB contiguous per wavefront instruction).  16-byte chunk c of a row
+// is stored at chunk c ^ swizzle(row): for key rows (256 B, 16 chunks)
+// swizzle = row mod 16, for transposed value rows (128 B, 8 chunks)
+// swizzle = (row / 2) mod 8, so that the 16 rows one fragment read touches
+// fall in 16 different bank quads.
+constexpr int kKChunks = kHeadDim / 8;   // 16-byte chunks per key row
+// Fourth word of a raw buffer descriptor: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kVChunks = kBN / 8;        // 16-byte chunks per transposed value row
 
 struct ChunkArgs {
   const _Float16* q;   // [B][Hq][Tq][128] rotated, times scale log2(e)
@@ -242,16 +250,16 @@ struct ChunkArgs {
 // CORR: the Jensen-bias correction ("Quantized Keys Steal Attention",
 // Eq. 15).  Its bias is a rank-(128 / g) product of query and key features,
 // so it is one more k-slice of the score MFMA per 16 keys, whose slots 0..7
-// (lane group 0) hold the features and the rest zeros: the key features ride
-// in the 8 padding halves of each key row of the tile, the workgroup's query
+// (lane group 0) hold the features and the rest zeros: the key features of
+// the tile sit beside it in LDS (1 KB), the workgroup's query
 // features sit in LDS (1 KB), so four workgroups still share a CU.
 template <bool CORR>
 __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
-  static_assert(kKStride >= kHeadDim + kFeat, "key features fit the row padding");
-  __shared__ _Float16 ks[kBN * kKStride];
-  __shared__ _Float16 vs[kHeadDim * kVStride];
+  __shared__ __attribute__((aligned(1024))) _Float16 ks[kBN * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) _Float16 vs[kHeadDim * kBN];
+  __shared__ __attribute__((aligned(1024))) _Float16 kfs[CORR ? kBN * kFeat : 8];
   __shared__ _Float16 qfs[CORR ? kBM * kFeat : 1];
-  const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, L = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = L & 15, grp = L >> 4;
   const int n_units = gridDim.x;
   const int id = blockIdx.x;
@@ -299,30 +307,52 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
   const size_t kbase = ((size_t)b * a.Hkv + hk) * a.Tk_pad * kHeadDim;
   const size_t vbase = ((size_t)b * a.Hkv + hk) * kHeadDim * a.Tk_pad;
   // The 64-key tiles of K (64 rows x 128 dims, contiguous) and V^T (128 rows x
-  // 64 keys) travel in 16-byte chunks, chunk tid + 128 j of each: a uniform
-  // base per tile plus a lane offset.  (Holding the next tile in registers
-  // during the current one does not fit beside two row groups' state.)
-  const uint32_t koff = 16u * tid;
-  const uint32_t voff = (uint32_t)(((size_t)(tid >> 3) * a.Tk_pad + 8 * (tid & 7)) * 2);
-  _Float16* const ks_dst = &ks[(tid >> 4) * kKStride + (tid & 15) * 8];
-  _Float16* const vs_dst = &vs[(tid >> 3) * kVStride + (tid & 7) * 8];
-  constexpr int kChunks = 1024 / kCThreads;
+  // 64 keys) go straight from global memory to LDS, 16 KB each: wavefront w
+  // issues instructions j = 0..7 of each, lane L of instruction j filling
+  // stored chunk p = 64 (8 w + j) + L, i.e. row p / 16 (K) or p / 8 (V^T), whose
+  // logical chunk is the stored one xor the row's swizzle.  Every load of the
+  // tile is in flight at once and holds no registers.
+  static_assert(kCWaves * 8 * 64 == kBN * kKChunks && kCWaves * 8 * 64 == kHeadDim * kVChunks,
+                "two wavefronts of eight instructions fill each tile");
+  // Instructions j and j + 4 (K) or j and j + 2 (V^T) share the swizzle: a
+  // lane keeps four and two source offsets, the rest are uniform steps.
+  uint32_t ksrc[4], vsrc[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = 64 * (8 * wave + j) + L;
+    const int kr = p / kKChunks, kc = (p % kKChunks) ^ (kr % kKChunks);
+    ksrc[j] = (uint32_t)((kr * kHeadDim + kc * 8) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = 64 * (8 * wave + j) + L;
+    const int vr = p / kVChunks, vc = (p % kVChunks) ^ ((vr >> 1) % kVChunks);
+    vsrc[j] = (uint32_t)((size_t)vr * a.Tk_pad * 2 + vc * 16);
+  }
+  // Buffer descriptors of this plane's K and V^T (raw, byte-addressed): the
+  // lane offsets above, a uniform offset per tile and instruction.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<_Float16*>(a.k + kbase), (short)0, a.Tk_pad * kHeadDim * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<_Float16*>(a.vt + vbase), (short)0, a.Tk_pad * kHeadDim * 2, kBufferWord3);
+  const int vstep = 16 * a.Tk_pad * 2;     // 16 value rows, in bytes
   auto copy_tile = [&](int kt0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, ks + 512 * (8 * wave + j), 16, ksrc[j & 3],
+                                               kt0 * kHeadDim * 2 + (j >> 2) * 4096, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vs + 512 * (8 * wave + j), 16, vsrc[j & 1],
+                                               kt0 * 2 + (j >> 1) * vstep, 0, 0);
+    }
     if constexpr (CORR) {
-      const _Float16* kf = a.kfeat + (((size_t)b * a.Hkv + hk) * a.Tk_pad + kt0) * kFeat;
-      for (int r = tid; r < kBN; r += kCThreads)
-        *reinterpret_cast<half8*>(&ks[r * kKStride + kHeadDim]) =
-            *reinterpret_cast<const half8*>(kf + (size_t)r * kFeat);
+      // the tile's 64 key feature rows, one 16-byte row a lane of wavefront 0
+      if (wave == 0) {
+        const _Float16* kf = a.kfeat + (((size_t)b * a.Hkv + hk) * a.Tk_pad + kt0) * kFeat;
+        *reinterpret_cast<half8*>(&kfs[L * kFeat]) =
+            *reinterpret_cast<const half8*>(kf + (size_t)L * kFeat);
+      }
     }
-    const char* kb = reinterpret_cast<const char*>(a.k + kbase + (size_t)kt0 * kHeadDim);
-    const char* vb = reinterpret_cast<const char*>(a.vt + vbase + kt0);
-#pragma unroll 4
-    for (int j = 0; j < kChunks; ++j) {
-      *reinterpret_cast<half8*>(ks_dst + j * (kCThreads / 16) * kKStride) =
-          *reinterpret_cast<const half8*>(kb + (size_t)j * (kCThreads * 16) + koff);
-      *reinterpret_cast<half8*>(vs_dst + j * (kCThreads / 8) * kVStride) =
-          *reinterpret_cast<const half8*>(vb + (size_t)j * (kCThreads / 8) * a.Tk_pad * 2 + voff);
-    }
+    __builtin_amdgcn_s_waitcnt(0);      // the tile has landed in LDS
   };
 
   // One 64-key tile from LDS; only the last, ragged tile masks keys past Tk.
@@ -343,17 +373,18 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      const _Float16* kr = &ks[(16 * kt + col) * kKStride + 8 * grp];
+      // key 16 kt + col (row swizzle col), logical chunk 4 s + grp
+      const _Float16* kr = &ks[(16 * kt + col) * kHeadDim];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const half8 kf = *reinterpret_cast<const half8*>(kr + 32 * s);
+        const half8 kf = *reinterpret_cast<const half8*>(kr + 8 * ((4 * s + grp) ^ col));
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg)
           st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[rg][s], st[kt][rg], 0, 0, 0);
       }
       if constexpr (CORR) {
         // minus the Jensen bias of keys 16 kt + (0..15), in log2 units
-        half8 kf5 = *reinterpret_cast<const half8*>(&ks[(16 * kt + col) * kKStride + kHeadDim]);
+        half8 kf5 = *reinterpret_cast<const half8*>(&kfs[(16 * kt + col) * kFeat]);
         kf5 = grp == 0 ? kf5 : zero8;
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg)
@@ -403,7 +434,9 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const half8 vf = *reinterpret_cast<const half8*>(&vs[(16 * c + col) * kVStride + 32 * sb + 8 * grp]);
+        // value row 16 c + col (row swizzle (col / 2) mod 8), logical chunk 4 sb + grp
+        const half8 vf = *reinterpret_cast<const half8*>(
+            &vs[(16 * c + col) * kBN + 8 * ((4 * sb + grp) ^ ((col >> 1) & 7))]);
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg)
           o[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg][sb], vf, o[rg][c], 0, 0, 0);
