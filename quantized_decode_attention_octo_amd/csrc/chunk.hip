@@ -204,17 +204,32 @@ constexpr int kCWaves = 2;
 constexpr int kCThreads = 64 * kCWaves;
 constexpr int kBM = 16 * kRG * kCWaves;   // 64 queries per workgroup
 constexpr int kXcds = 8;        // workgroups are dealt round-robin to the XCDs
-constexpr int kBN = 64;         // keys per LDS tile
-// LDS tiles are unpadded, written by direct global-to-LDS loads (16 bytes a
+constexpr int kPadKeys = 64;    // the staged key rows are padded to a multiple of this
+// Key tiles: BN keys per LDS tile, NBUF buffers.  Without the correction,
+// 32-key tiles in two buffers: the next tile streams in while the current one
+// is used, in 32 KB of LDS (four workgroups per CU).  The correction's extra
+// registers do not leave room for that pipeline; it keeps 64-key tiles in one
+// buffer.
+template <bool CORR>
+struct TileShape {
+  static constexpr int BN = CORR ? 64 : 32;
+  static constexpr int NBUF = CORR ? 1 : 2;
+  static constexpr int VC = BN / 8;                  // 16-byte chunks per V^T row
+  static constexpr int INSTS = BN * (kHeadDim / 8) / 64 / kCWaves;   // per wavefront, K and V^T each
+  static_assert(kPadKeys % BN == 0, "tiles never straddle the padded end");
+};
+// LDS tiles are unpadded, written by direct buffer-to-LDS loads (16 bytes a
 // lane, 1 KB contiguous per wavefront instruction).  16-byte chunk c of a row
 // is stored at chunk c ^ swizzle(row): for key rows (256 B, 16 chunks)
-// swizzle = row mod 16, for transposed value rows (128 B, 8 chunks)
-// swizzle = (row / 2) mod 8, so that the 16 rows one fragment read touches
-// fall in 16 different bank quads.
+// swizzle = row mod 16, for transposed value rows of VC chunks
+// swizzle = (row / (16 / VC)) mod VC, so that the 16 rows one fragment read
+// touches fall in 16 different bank quads.
 constexpr int kKChunks = kHeadDim / 8;   // 16-byte chunks per key row
 // Fourth word of a raw buffer descriptor: 32-bit data format, no swizzle.
 constexpr int kBufferWord3 = 0x00020000;
-constexpr int kVChunks = kBN / 8;        // 16-byte chunks per transposed value row
+// s_waitcnt immediate waiting until no vector-memory operation of the
+// wavefront is outstanding (vmcnt 0; expcnt and lgkmcnt not waited for).
+constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
 struct ChunkArgs {
   const _Float16* q;   // [B][Hq][Tq][128] rotated, times scale log2(e)
@@ -255,9 +270,13 @@ struct ChunkArgs {
 // features sit in LDS (1 KB), so four workgroups still share a CU.
 template <bool CORR>
 __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
-  __shared__ __attribute__((aligned(1024))) _Float16 ks[kBN * kHeadDim];
-  __shared__ __attribute__((aligned(1024))) _Float16 vs[kHeadDim * kBN];
-  __shared__ __attribute__((aligned(1024))) _Float16 kfs[CORR ? kBN * kFeat : 8];
+  using TS = TileShape<CORR>;
+  constexpr int kBN = TS::BN, kVChunks = TS::VC, kTileInsts = TS::INSTS;
+  __shared__ __attribute__((aligned(1024))) _Float16 ks0[kBN * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) _Float16 vs0[kHeadDim * kBN];
+  __shared__ __attribute__((aligned(1024))) _Float16 kfs0[CORR ? kBN * kFeat : 8];
+  __shared__ __attribute__((aligned(1024))) _Float16 ks1[TS::NBUF > 1 ? kBN * kHeadDim : 8];
+  __shared__ __attribute__((aligned(1024))) _Float16 vs1[TS::NBUF > 1 ? kHeadDim * kBN : 8];
   __shared__ _Float16 qfs[CORR ? kBM * kFeat : 1];
   const int tid = threadIdx.x, L = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = L & 15, grp = L >> 4;
@@ -306,60 +325,61 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
 
   const size_t kbase = ((size_t)b * a.Hkv + hk) * a.Tk_pad * kHeadDim;
   const size_t vbase = ((size_t)b * a.Hkv + hk) * kHeadDim * a.Tk_pad;
-  // The 64-key tiles of K (64 rows x 128 dims, contiguous) and V^T (128 rows x
-  // 64 keys) go straight from global memory to LDS, 16 KB each: wavefront w
-  // issues instructions j = 0..7 of each, lane L of instruction j filling
-  // stored chunk p = 64 (8 w + j) + L, i.e. row p / 16 (K) or p / 8 (V^T), whose
-  // logical chunk is the stored one xor the row's swizzle.  Every load of the
-  // tile is in flight at once and holds no registers.
-  static_assert(kCWaves * 8 * 64 == kBN * kKChunks && kCWaves * 8 * 64 == kHeadDim * kVChunks,
-                "two wavefronts of eight instructions fill each tile");
-  // Instructions j and j + 4 (K) or j and j + 2 (V^T) share the swizzle: a
-  // lane keeps four and two source offsets, the rest are uniform steps.
+  // The tiles of K (kBN rows x 128 dims, contiguous) and V^T (128 rows x kBN
+  // keys) go straight from global memory to LDS: wavefront w issues
+  // instructions j < kTileInsts of each, lane L of instruction j filling
+  // stored chunk p = 64 (kTileInsts w + j) + L, i.e. row p / 16 (K) or
+  // p / kVChunks (V^T), whose logical chunk is the stored one xor the row's
+  // swizzle.  Every load of a tile is in flight at once and holds no registers.
+  static_assert(kCWaves * kTileInsts * 64 == kBN * kKChunks &&
+                    kCWaves * kTileInsts * 64 == kHeadDim * kVChunks,
+                "the wavefronts' instructions fill each tile");
+  // The swizzle of instruction j depends on j mod 4 (K) and j mod 2 (V^T):
+  // a lane keeps four and two source offsets, the rest are uniform steps.
   uint32_t ksrc[4], vsrc[2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int p = 64 * (8 * wave + j) + L;
+    const int p = 64 * (kTileInsts * wave + j) + L;
     const int kr = p / kKChunks, kc = (p % kKChunks) ^ (kr % kKChunks);
     ksrc[j] = (uint32_t)((kr * kHeadDim + kc * 8) * 2);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int p = 64 * (8 * wave + j) + L;
-    const int vr = p / kVChunks, vc = (p % kVChunks) ^ ((vr >> 1) % kVChunks);
-    vsrc[j] = (uint32_t)((size_t)vr * a.Tk_pad * 2 + vc * 16);
+    const int p = 64 * (kTileInsts * wave + j) + L;
+    const int vr = p / kVChunks, vc = (p % kVChunks) ^ ((vr / (16 / kVChunks)) % kVChunks);
+    vsrc[j] = (uint32_t)(vr * a.Tk_pad * 2 + vc * 16);
   }
-  // Buffer descriptors of this plane's K and V^T (raw, byte-addressed): the
-  // lane offsets above, a uniform offset per tile and instruction.
+  const int vstep = (128 / kVChunks) * a.Tk_pad * 2;   // two instructions' rows, in bytes
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<_Float16*>(a.k + kbase), (short)0, a.Tk_pad * kHeadDim * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<_Float16*>(a.vt + vbase), (short)0, a.Tk_pad * kHeadDim * 2, kBufferWord3);
-  const int vstep = 16 * a.Tk_pad * 2;     // 16 value rows, in bytes
-  auto copy_tile = [&](int kt0) {
+  const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<_Float16*>(CORR ? a.kfeat + ((size_t)b * a.Hkv + hk) * a.Tk_pad * kFeat : a.k),
+      (short)0, a.Tk_pad * kFeat * 2, kBufferWord3);
+  // Issues the loads of the tile at kt0 into (ks, vs, kfs); none is waited for here.
+  auto copy_tile = [&](int kt0, _Float16* ks, _Float16* vs, _Float16* kfs) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, ks + 512 * (8 * wave + j), 16, ksrc[j & 3],
+    for (int j = 0; j < kTileInsts; ++j) {
+      const int inst = kTileInsts * wave + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, ks + 512 * inst, 16, ksrc[j & 3],
                                                kt0 * kHeadDim * 2 + (j >> 2) * 4096, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vs + 512 * (8 * wave + j), 16, vsrc[j & 1],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vs + 512 * inst, 16, vsrc[j & 1],
                                                kt0 * 2 + (j >> 1) * vstep, 0, 0);
     }
     if constexpr (CORR) {
-      // the tile's 64 key feature rows, one 16-byte row a lane of wavefront 0
-      if (wave == 0) {
-        const _Float16* kf = a.kfeat + (((size_t)b * a.Hkv + hk) * a.Tk_pad + kt0) * kFeat;
-        *reinterpret_cast<half8*>(&kfs[L * kFeat]) =
-            *reinterpret_cast<const half8*>(kf + (size_t)L * kFeat);
-      }
+      // the tile's key feature rows, a 16-byte row a lane of wavefront 0
+      if (wave == 0 && L < kBN)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(frs, kfs, 16, L * kFeat * 2, kt0 * kFeat * 2, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0);      // the tile has landed in LDS
   };
 
-  // One 64-key tile from LDS; only the last, ragged tile masks keys past Tk.
-  auto tile_step = [&](int kt0, auto masked_c) {
+  // One tile from LDS; only the last, ragged tile masks keys past Tk.
+  auto tile_step = [&](int kt0, auto masked_c, const _Float16* ks, const _Float16* vs,
+                       const _Float16* kfs) {
     constexpr bool MASKED = decltype(masked_c)::value;
-    // scores of the 64 keys (log2 units): st[kt][rg][r] = key kt0 + 16 kt + 4 grp + r
-    floatx4 st[4][kRG];
+    // scores of the tile's keys (log2 units): st[kt][rg][r] = key kt0 + 16 kt + 4 grp + r
+    floatx4 st[kBN / 16][kRG];
     half8 qf5[CORR ? kRG : 1];
     const half8 zero8 = {};
     if constexpr (CORR) {
@@ -370,7 +390,7 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
       }
     }
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < kBN / 16; ++kt) {
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
       // key 16 kt + col (row swizzle col), logical chunk 4 s + grp
@@ -391,13 +411,13 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
           st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf5, qf5[rg], st[kt][rg], 0, 0, 0);
       }
     }
-    half8 pf[kRG][2];
+    half8 pf[kRG][kBN / 32];
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
-      float x[16];
+      float x[kBN / 4];
       float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < kBN / 4; ++e) {
         const int kt = e >> 2, r = e & 3;
         x[e] = st[kt][rg][r];
         if (MASKED && kt0 + 16 * kt + 4 * grp + r >= a.Tk) x[e] = -INFINITY;
@@ -408,7 +428,7 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
       const float alpha = m_run[rg] == m_new ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
       float ps = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < kBN / 4; ++e) {
         // probabilities are at most 1: the raw exp2 (flushing results below
         // the normal range to zero) is exact enough
         const float p = __builtin_amdgcn_exp2f(x[e] - m_new);
@@ -431,26 +451,51 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     }
     // O += P V: slot e of sub-block sb is key kt0 + 32 sb + 16 (e / 4) + 4 grp + e % 4
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < kBN / 32; ++sb)
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        // value row 16 c + col (row swizzle (col / 2) mod 8), logical chunk 4 sb + grp
+        // value row 16 c + col, logical chunk 4 sb + grp
+        const int sw = (col / (16 / kVChunks)) % kVChunks;
         const half8 vf = *reinterpret_cast<const half8*>(
-            &vs[(16 * c + col) * kBN + 8 * ((4 * sb + grp) ^ ((col >> 1) & 7))]);
+            &vs[(16 * c + col) * kBN + 8 * ((4 * sb + grp) ^ sw)]);
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg)
           o[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg][sb], vf, o[rg][c], 0, 0, 0);
       }
   };
   const int tk_full = a.Tk / kBN * kBN;
-  for (int kt0 = 0; kt0 < a.Tk; kt0 += kBN) {
-    __syncthreads();               // the previous tile's LDS reads are done
-    copy_tile(kt0);
-    __syncthreads();
-    if (kt0 < tk_full)
-      tile_step(kt0, std::false_type{});
+  const int n_tiles = (a.Tk + kBN - 1) / kBN;
+  auto compute = [&](int t, const _Float16* ks, const _Float16* vs, const _Float16* kfs) {
+    if (t * kBN < tk_full)
+      tile_step(t * kBN, std::false_type{}, ks, vs, kfs);
     else
-      tile_step(kt0, std::true_type{});
+      tile_step(t * kBN, std::true_type{}, ks, vs, kfs);
+  };
+  if constexpr (TS::NBUF == 2) {
+    // Tile t sits in buffer t % 2.  Tile t + 1 is requested before tile t's
+    // arithmetic and waited for after it, at the barrier (whose fence also
+    // waits for this wave's loads into LDS), which also frees buffer t % 2.
+    auto step = [&](int t, const _Float16* ks, const _Float16* vs, _Float16* nks, _Float16* nvs) {
+      if (t + 1 < n_tiles) copy_tile((t + 1) * kBN, nks, nvs, kfs0);
+      compute(t, ks, vs, kfs0);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      lds_barrier();
+    };
+    if (n_tiles > 0) copy_tile(0, ks0, vs0, kfs0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    lds_barrier();
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(t, ks0, vs0, ks1, vs1);
+      if (t + 1 < n_tiles) step(t + 1, ks1, vs1, ks0, vs0);
+    }
+  } else {
+    for (int t = 0; t < n_tiles; ++t) {
+      copy_tile(t * kBN, ks0, vs0, kfs0);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      lds_barrier();                   // the tile has landed
+      compute(t, ks0, vs0, kfs0);
+      lds_barrier();                   // its reads are done before the next copy
+    }
   }
 
   // ---- epilogue: 1/l, then R_v^T = diag(s_v) H / sqrt(d) on every query row.
@@ -588,7 +633,7 @@ struct ChunkPlan {
 ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Tq, int cached, int Tc, bool corr) {
   ChunkPlan p;
   p.Tk = cached + Tc;
-  p.Tk_pad = (p.Tk + kBN - 1) / kBN * kBN;
+  p.Tk_pad = (p.Tk + kPadKeys - 1) / kPadKeys * kPadKeys;
   const size_t row = kHeadDim * sizeof(_Float16);
   auto up = [](size_t n) { return (n + 255) / 256 * 256; };
   p.q_off = 0;
