@@ -205,6 +205,7 @@ constexpr int kCThreads = 64 * kCWaves;
 constexpr int kBM = 16 * kRG * kCWaves;   // 64 queries per workgroup
 constexpr int kXcds = 8;        // workgroups are dealt round-robin to the XCDs
 constexpr int kPadKeys = 64;    // the staged key rows are padded to a multiple of this
+constexpr float kLazyLog2 = 8.0f;   // slack of the lazy running maximum (log2 units)
 // Key tiles: BN keys per LDS tile, NBUF buffers.  Without the correction,
 // 32-key tiles in two buffers: the next tile streams in while the current one
 // is used, in 32 KB of LDS (four workgroups per CU).  The correction's extra
@@ -316,7 +317,9 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
   for (int rg = 0; rg < kRG; ++rg)
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[rg][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run[kRG], l_run[kRG];   // of query q0 + 16 rg + col, log2 units
+  // of query q0 + 16 rg + col: running maximum (log2 units), and this
+  // lane's part of the normalizer
+  float m_run[kRG], l_run[kRG];
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg) {
     m_run[rg] = -INFINITY;
@@ -424,22 +427,17 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
         mx = fmaxf(mx, x[e]);
       }
       mx = rows_max(mx);
-      const float m_new = fmaxf(m_run[rg], mx);
-      const float alpha = m_run[rg] == m_new ? 1.0f : __builtin_amdgcn_exp2f(m_run[rg] - m_new);
-      float ps = 0.0f;
-#pragma unroll
-      for (int e = 0; e < kBN / 4; ++e) {
-        // probabilities are at most 1: the raw exp2 (flushing results below
-        // the normal range to zero) is exact enough
-        const float p = __builtin_amdgcn_exp2f(x[e] - m_new);
-        ps += p;
-        pf[rg][e >> 3][e & 7] = (_Float16)p;
-      }
-      ps = rows_sum(ps);
-      l_run[rg] = l_run[rg] * alpha + ps;
-      m_run[rg] = m_new;
-      // rescale O rows (queries q0 + 16 rg + 4 grp + r) unless no row moved
-      if (__ballot(alpha != 1.0f)) {
+      // Lazy running maximum: a row moves its maximum (and rescales its sums)
+      // only when a score exceeds it by more than kLazyLog2, so that nearly
+      // every tile skips the rescale; probabilities then stay below
+      // 2^kLazyLog2, well inside fp16, and the final 1/l cancels the shift.
+      const bool up = mx > m_run[rg] + kLazyLog2;
+      if (__ballot(up)) {
+        const float m_new = up ? mx : m_run[rg];
+        const float alpha = up ? __builtin_amdgcn_exp2f(m_run[rg] - m_new) : 1.0f;
+        l_run[rg] *= alpha;
+        m_run[rg] = m_new;
+        // rescale O rows (queries q0 + 16 rg + 4 grp + r)
         float al[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
@@ -448,6 +446,16 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[rg][c][r] *= al[r];
       }
+      float ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kBN / 4; ++e) {
+        // the raw exp2 (flushing results below the normal range to zero) is
+        // exact enough next to the row's largest terms (at least 1)
+        const float p = __builtin_amdgcn_exp2f(x[e] - m_run[rg]);
+        ps += p;
+        pf[rg][e >> 3][e & 7] = (_Float16)p;
+      }
+      l_run[rg] += ps;                 // this lane's keys; rows are summed at the end
     }
     // O += P V: slot e of sub-block sb is key kt0 + 32 sb + 16 (e / 4) + 4 grp + e % 4
 #pragma unroll
@@ -507,10 +515,11 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
   for (int c = 0; c < 8; ++c) sv[c] = kInvSqrtD * splitmix_sign(a.vseed, 16 * c + col);
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg) {
+    const float l_tot = rows_sum(l_run[rg]);   // the row's four lane groups
     float li[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float l = __shfl(l_run[rg], 4 * grp + r, 64);
+      const float l = __shfl(l_tot, 4 * grp + r, 64);
       li[r] = l > 0.0f ? 1.0f / l : 0.0f;
     }
     float v[8][4];
