@@ -73,23 +73,24 @@ __global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __rest
   const int plane = blockIdx.y;
   const int t0 = blockIdx.x * 64;
   const float s0 = splitmix_sign(seed, lane), s1 = splitmix_sign(seed, lane + 64);
-#pragma unroll 1
-  for (int j0 = 0; j0 < 16; j0 += 4) {
-    float xa[4], xb[4];
+  // the wavefront's 16 rows: every load in flight at once (rows past T read
+  // row T - 1 and are zeroed; with T = 0 there is nothing to read)
+  uint16_t ra[16] = {}, rb[16] = {};
+  if (T > 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = t0 + wave + 4 * (j0 + j);
-      xa[j] = xb[j] = 0.0f;
-      if (t < T) {
-        const uint16_t* src = in + ((size_t)plane * T + t) * kHeadDim;
-        xa[j] = bf16_to_f32(src[lane]);
-        xb[j] = bf16_to_f32(src[lane + 64]);
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int t = min(t0 + wave + 4 * j, T - 1);
+      const uint16_t* src = in + ((size_t)plane * T + t) * kHeadDim;
+      ra[j] = src[lane];
+      rb[j] = src[lane + 64];
     }
+  }
+  {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = wave + 4 * (j0 + j), t = t0 + k;
-      float a = xa[j] * s0, b = xb[j] * s1;
+    for (int j = 0; j < 16; ++j) {
+      const int k = wave + 4 * j, t = t0 + k;
+      const float xaj = t < T ? bf16_to_f32(ra[j]) : 0.0f, xbj = t < T ? bf16_to_f32(rb[j]) : 0.0f;
+      float a = xaj * s0, b = xbj * s1;
       wht128(a, b);
       if (TRANSPOSED) {
         tile[k * 130 + lane] = (_Float16)(a * post);
@@ -152,29 +153,42 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
   constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD, BT = FWD + BN;
   constexpr int WI = (kNTri * BT + 31) / 32;
   constexpr int kRow = 136;                        // halves per token row in LDS
+  constexpr int kTriG = 11;                        // triplets per thread: 4 x 11 >= 43
+  constexpr int GW = (31 + kTriG * BT + 31) / 32;  // record words covering them from any shift
   __shared__ float4 lut[K * K];
   __shared__ float crho[R], cxi[K];
   __shared__ __attribute__((aligned(16))) _Float16 tile[64 * kRow];
   const int tid = threadIdx.x;
+  const size_t plane = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  const int nt = min(64, cached - t0);
+  // Thread (k, w): token t0 + k, triplets 11 w .. 11 w + 10.  Its record
+  // words and gamma are all requested first (a token past the cached ones
+  // reads token t0, whose values are not stored).
+  const int k = tid & 63, w = tid >> 6;
+  const int t = t0 + (k < nt ? k : 0);
+  const int iwo = (kTriG * BT * w) >> 5, ish = (kTriG * BT * w) & 31;
+  uint32_t wd[GW];
+#pragma unroll
+  for (int j = 0; j < GW; ++j) wd[j] = idx[tile_word(plane, capacity, t, min(iwo + j, WI - 1), WI)];
+  const float gam = gamma[plane * capacity + t];
   if (tid < K) cxi[tid] = cb.xi[tid];
   if (tid < R) crho[tid] = cb.rho[tid];
   __syncthreads();
   for (int e = tid; e < K * K; e += 256) lut[e] = oct_dir(cxi[e % K], cxi[e / K]);
   __syncthreads();
-  const size_t plane = blockIdx.y;
-  const int t0 = blockIdx.x * 64;
-  const int nt = min(64, cached - t0);
-  for (int e = tid; e < 64 * kNTri; e += 256) {
-    const int k = e & 63, i = e >> 6;
-    const int t = t0 + k;
-    if (k >= nt) continue;
+  // shift the words so that triplet 11 w + m starts at bit m B_tri
+  uint32_t sw[GW];
+#pragma unroll
+  for (int j = 0; j < GW; ++j) sw[j] = __builtin_amdgcn_alignbit(j + 1 < GW ? wd[j + 1] : 0u, wd[j], ish);
+#pragma unroll
+  for (int m = 0; m < kTriG; ++m) {
+    const int i = kTriG * w + m;
+    if (i >= kNTri) break;
     // triplet field i: code pair | rho index << 2 b_dir
-    const int p = i * BT;
-    const uint32_t lo = idx[tile_word(plane, capacity, t, p >> 5, WI)];
-    const uint32_t hi = ((p & 31) + BT > 32) ? idx[tile_word(plane, capacity, t, (p >> 5) + 1, WI)] : 0u;
-    const uint32_t f = (uint32_t)((((uint64_t)hi << 32) | lo) >> (p & 31)) & ((1u << BT) - 1u);
+    const uint32_t f = field<BT>(sw, m * BT);
     const uint32_t code = f & ((1u << FWD) - 1u), ir = f >> FWD;
-    const float s = crho[ir] * gamma[plane * capacity + t];
+    const float s = crho[ir] * gam;
     const float4 n = lut[code];
     _Float16* dst = &tile[k * kRow + 3 * i];
     dst[0] = (_Float16)(s * n.x);
@@ -182,18 +196,34 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
     if (i < kNTri - 1) dst[2] = (_Float16)(s * n.z);   // coordinate 128 is the pad
   }
   __syncthreads();
+  typedef _Float16 half8v __attribute__((ext_vector_type(8)));
   if (TRANSPOSED) {
-    for (int e = tid; e < 64 * kHeadDim; e += 256) {
-      const int c = e >> 6, k = e & 63;
-      if (k < nt) out[(plane * kHeadDim + c) * out_rows + key_column(t0 + k)] = tile[k * kRow + c];
+    if (nt == 64) {
+      // 16-byte stores: columns 8 q .. 8 q + 7 of coordinate c hold keys
+      // 32 (q / 4) + {4 j + r, 16 + 4 j + r}, j = q mod 4, r < 4 (key_column)
+      for (int e = tid; e < kHeadDim * 8; e += 256) {
+        const int c = e >> 3, q = e & 7;
+        const int kb = 32 * (q >> 2) + 4 * (q & 3);
+        half8v v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = tile[(kb + r) * kRow + c];
+          v[4 + r] = tile[(kb + 16 + r) * kRow + c];
+        }
+        *reinterpret_cast<half8v*>(out + (plane * kHeadDim + c) * out_rows + t0 + 8 * q) = v;
+      }
+    } else {
+      for (int e = tid; e < 64 * kHeadDim; e += 256) {
+        const int c = e >> 6, kk = e & 63;
+        if (kk < nt) out[(plane * kHeadDim + c) * out_rows + key_column(t0 + kk)] = tile[kk * kRow + c];
+      }
     }
   } else {
-    typedef _Float16 half8v __attribute__((ext_vector_type(8)));
     for (int e = tid; e < 64 * 16; e += 256) {
-      const int k = e >> 4, c8 = (e & 15) * 8;
-      if (k < nt)
-        *reinterpret_cast<half8v*>(out + (plane * out_rows + t0 + k) * kHeadDim + c8) =
-            *reinterpret_cast<const half8v*>(&tile[k * kRow + c8]);
+      const int kk = e >> 4, c8 = (e & 15) * 8;
+      if (kk < nt)
+        *reinterpret_cast<half8v*>(out + (plane * out_rows + t0 + kk) * kHeadDim + c8) =
+            *reinterpret_cast<const half8v*>(&tile[kk * kRow + c8]);
     }
   }
 }
