@@ -236,25 +236,18 @@ constexpr int kBM = 16 * kRG * kCWaves;   // 64 queries per workgroup
 constexpr int kXcds = 8;        // workgroups are dealt round-robin to the XCDs
 constexpr int kPadKeys = 64;    // the staged key rows are padded to a multiple of this
 constexpr float kLazyLog2 = 8.0f;   // slack of the lazy running maximum (log2 units)
-// Key tiles: BN keys per LDS tile, NBUF buffers.  Without the correction,
-// 32-key tiles in two buffers: the next tile streams in while the current one
-// is used, in 32 KB of LDS (four workgroups per CU).  The correction's extra
-// registers do not leave room for that pipeline; it keeps 64-key tiles in one
-// buffer.
-template <bool CORR>
-struct TileShape {
-  static constexpr int BN = CORR ? 64 : 32;
-  static constexpr int NBUF = CORR ? 1 : 2;
-  static constexpr int VC = BN / 8;                  // 16-byte chunks per V^T row
-  static constexpr int INSTS = BN * (kHeadDim / 8) / 64 / kCWaves;   // per wavefront, K and V^T each
-  static_assert(kPadKeys % BN == 0, "tiles never straddle the padded end");
-};
+// Key tiles: 32 keys per LDS tile, in two buffers: the next tile streams in
+// while the current one is used, in 32 KB of LDS (four workgroups per CU).
+constexpr int kBN = 32;
+constexpr int kVChunks = kBN / 8;                                 // 16-byte chunks per V^T row
+constexpr int kTileInsts = kBN * (kHeadDim / 8) / 64 / kCWaves;   // per wavefront, K and V^T each
+static_assert(kPadKeys % kBN == 0, "tiles never straddle the padded end");
 // LDS tiles are unpadded, written by direct buffer-to-LDS loads (16 bytes a
 // lane, 1 KB contiguous per wavefront instruction).  16-byte chunk c of a row
 // is stored at chunk c ^ swizzle(row): for key rows (256 B, 16 chunks)
-// swizzle = row mod 16, for transposed value rows of VC chunks
-// swizzle = (row / (16 / VC)) mod VC, so that the 16 rows one fragment read
-// touches fall in 16 different bank quads.
+// swizzle = row mod 16, for transposed value rows (64 B, 4 chunks)
+// swizzle = (row / 4) mod 4, so that the 16 rows one fragment read touches
+// fall in 16 different bank quads.
 constexpr int kKChunks = kHeadDim / 8;   // 16-byte chunks per key row
 // Fourth word of a raw buffer descriptor: 32-bit data format, no swizzle.
 constexpr int kBufferWord3 = 0x00020000;
@@ -296,18 +289,16 @@ struct ChunkArgs {
 // CORR: the Jensen-bias correction ("Quantized Keys Steal Attention",
 // Eq. 15).  Its bias is a rank-(128 / g) product of query and key features,
 // so it is one more k-slice of the score MFMA per 16 keys, whose slots 0..7
-// (lane group 0) hold the features and the rest zeros: the key features of
-// the tile sit beside it in LDS (1 KB), the workgroup's query
-// features sit in LDS (1 KB), so four workgroups still share a CU.
+// (lane group 0) hold the features and the rest zeros: lane group 0 reads
+// the tile's key features (beside the tile, 512 B a buffer) and the
+// workgroup's query features (1 KB of LDS) where they are used, the other
+// lanes hold zeros, so four workgroups still share a CU.
 template <bool CORR>
 __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
-  using TS = TileShape<CORR>;
-  constexpr int kBN = TS::BN, kVChunks = TS::VC, kTileInsts = TS::INSTS;
-  __shared__ __attribute__((aligned(1024))) _Float16 ks0[kBN * kHeadDim];
-  __shared__ __attribute__((aligned(1024))) _Float16 vs0[kHeadDim * kBN];
-  __shared__ __attribute__((aligned(1024))) _Float16 kfs0[CORR ? kBN * kFeat : 8];
-  __shared__ __attribute__((aligned(1024))) _Float16 ks1[TS::NBUF > 1 ? kBN * kHeadDim : 8];
-  __shared__ __attribute__((aligned(1024))) _Float16 vs1[TS::NBUF > 1 ? kHeadDim * kBN : 8];
+  __shared__ __attribute__((aligned(1024))) _Float16 ks0[kBN * kHeadDim], ks1[kBN * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) _Float16 vs0[kHeadDim * kBN], vs1[kHeadDim * kBN];
+  __shared__ __attribute__((aligned(1024))) _Float16 kfs0[CORR ? kBN * kFeat : 8],
+      kfs1[CORR ? kBN * kFeat : 8];
   __shared__ _Float16 qfs[CORR ? kBM * kFeat : 1];
   const int tid = threadIdx.x, L = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = L & 15, grp = L >> 4;
@@ -413,15 +404,7 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     constexpr bool MASKED = decltype(masked_c)::value;
     // scores of the tile's keys (log2 units): st[kt][rg][r] = key kt0 + 16 kt + 4 grp + r
     floatx4 st[kBN / 16][kRG];
-    half8 qf5[CORR ? kRG : 1];
     const half8 zero8 = {};
-    if constexpr (CORR) {
-#pragma unroll
-      for (int rg = 0; rg < kRG; ++rg) {
-        qf5[rg] = *reinterpret_cast<const half8*>(&qfs[(wave * 16 * kRG + 16 * rg + col) * kFeat]);
-        qf5[rg] = grp == 0 ? qf5[rg] : zero8;          // slots 8..31 are zero
-      }
-    }
 #pragma unroll
     for (int kt = 0; kt < kBN / 16; ++kt) {
 #pragma unroll
@@ -437,11 +420,16 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
       }
       if constexpr (CORR) {
         // minus the Jensen bias of keys 16 kt + (0..15), in log2 units
-        half8 kf5 = *reinterpret_cast<const half8*>(&kfs[(16 * kt + col) * kFeat]);
-        kf5 = grp == 0 ? kf5 : zero8;
+        // (slots 8..31 of both operands are zero: lane groups 1..3 read nothing)
+        half8 kf5 = zero8;
+        if (grp == 0) kf5 = *reinterpret_cast<const half8*>(&kfs[(16 * kt + col) * kFeat]);
 #pragma unroll
-        for (int rg = 0; rg < kRG; ++rg)
-          st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf5, qf5[rg], st[kt][rg], 0, 0, 0);
+        for (int rg = 0; rg < kRG; ++rg) {
+          half8 qf5 = zero8;
+          if (grp == 0)
+            qf5 = *reinterpret_cast<const half8*>(&qfs[(wave * 16 * kRG + 16 * rg + col) * kFeat]);
+          st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf5, qf5, st[kt][rg], 0, 0, 0);
+        }
       }
     }
     half8 pf[kRG][kBN / 32];
@@ -509,31 +497,22 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     else
       tile_step(t * kBN, std::true_type{}, ks, vs, kfs);
   };
-  if constexpr (TS::NBUF == 2) {
-    // Tile t sits in buffer t % 2.  Tile t + 1 is requested before tile t's
-    // arithmetic and waited for after it, at the barrier (whose fence also
-    // waits for this wave's loads into LDS), which also frees buffer t % 2.
-    auto step = [&](int t, const _Float16* ks, const _Float16* vs, _Float16* nks, _Float16* nvs) {
-      if (t + 1 < n_tiles) copy_tile((t + 1) * kBN, nks, nvs, kfs0);
-      compute(t, ks, vs, kfs0);
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      lds_barrier();
-    };
-    if (n_tiles > 0) copy_tile(0, ks0, vs0, kfs0);
+  // Tile t sits in buffer t % 2.  Tile t + 1 is requested before tile t's
+  // arithmetic and waited for after it, at the barrier (whose fence also
+  // waits for this wave's loads into LDS), which also frees buffer t % 2.
+  auto step = [&](int t, const _Float16* ks, const _Float16* vs, const _Float16* kfs,
+                  _Float16* nks, _Float16* nvs, _Float16* nkfs) {
+    if (t + 1 < n_tiles) copy_tile((t + 1) * kBN, nks, nvs, nkfs);
+    compute(t, ks, vs, kfs);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     lds_barrier();
-    for (int t = 0; t < n_tiles; t += 2) {
-      step(t, ks0, vs0, ks1, vs1);
-      if (t + 1 < n_tiles) step(t + 1, ks1, vs1, ks0, vs0);
-    }
-  } else {
-    for (int t = 0; t < n_tiles; ++t) {
-      copy_tile(t * kBN, ks0, vs0, kfs0);
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      lds_barrier();                   // the tile has landed
-      compute(t, ks0, vs0, kfs0);
-      lds_barrier();                   // its reads are done before the next copy
-    }
+  };
+  if (n_tiles > 0) copy_tile(0, ks0, vs0, kfs0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  lds_barrier();
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, ks0, vs0, kfs0, ks1, vs1, kfs1);
+    if (t + 1 < n_tiles) step(t + 1, ks1, vs1, kfs1, ks0, vs0, kfs0);
   }
 
   // ---- epilogue: 1/l, then R_v^T = diag(s_v) H / sqrt(d) on every query row.
