@@ -138,6 +138,45 @@ __device__ inline float4 oct_dir(float xi, float eta) {
   return make_float4(x / n, y / n, z / n, 0.0f);
 }
 
+// Stores the LDS tile of tokens t0 .. t0 + nt - 1 (rows of kRow halves) as
+// rows of a [out_rows][128] plane (16-byte chunks) or as columns of a
+// [128][out_rows] plane at key_column.  A full transposed tile goes out in
+// 16-byte chunks: columns 8 q .. 8 q + 7 of coordinate c hold keys
+// 32 (q / 4) + {4 j + r, 16 + 4 j + r}, j = q mod 4, r < 4.
+template <bool TRANSPOSED>
+__device__ inline void store_rows(const _Float16* tile, int kRow, _Float16* __restrict__ out,
+                                  int out_rows, size_t plane, int t0, int nt) {
+  typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+  const int tid = threadIdx.x;
+  if (TRANSPOSED) {
+    if (nt == 64) {
+      for (int e = tid; e < kHeadDim * 8; e += 256) {
+        const int c = e >> 3, q = e & 7;
+        const int kb = 32 * (q >> 2) + 4 * (q & 3);
+        half8v v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = tile[(kb + r) * kRow + c];
+          v[4 + r] = tile[(kb + 16 + r) * kRow + c];
+        }
+        *reinterpret_cast<half8v*>(out + (plane * kHeadDim + c) * out_rows + t0 + 8 * q) = v;
+      }
+    } else {
+      for (int e = tid; e < 64 * kHeadDim; e += 256) {
+        const int c = e >> 6, kk = e & 63;
+        if (kk < nt) out[(plane * kHeadDim + c) * out_rows + key_column(t0 + kk)] = tile[kk * kRow + c];
+      }
+    }
+  } else {
+    for (int e = tid; e < 64 * 16; e += 256) {
+      const int kk = e >> 4, c8 = (e & 15) * 8;
+      if (kk < nt)
+        *reinterpret_cast<half8v*>(out + (plane * out_rows + t0 + kk) * kHeadDim + c8) =
+            *reinterpret_cast<const half8v*>(&tile[kk * kRow + c8]);
+    }
+  }
+}
+
 // One workgroup per 64 cached tokens of a plane: lanes take (token, triplet)
 // items token-fastest (coalesced reads of the tile-64 words) and write
 // fp16(gamma_t u^_t[0:128]) into an LDS tile, which is then stored as rows t
@@ -196,36 +235,7 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
     if (i < kNTri - 1) dst[2] = (_Float16)(s * n.z);   // coordinate 128 is the pad
   }
   __syncthreads();
-  typedef _Float16 half8v __attribute__((ext_vector_type(8)));
-  if (TRANSPOSED) {
-    if (nt == 64) {
-      // 16-byte stores: columns 8 q .. 8 q + 7 of coordinate c hold keys
-      // 32 (q / 4) + {4 j + r, 16 + 4 j + r}, j = q mod 4, r < 4 (key_column)
-      for (int e = tid; e < kHeadDim * 8; e += 256) {
-        const int c = e >> 3, q = e & 7;
-        const int kb = 32 * (q >> 2) + 4 * (q & 3);
-        half8v v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = tile[(kb + r) * kRow + c];
-          v[4 + r] = tile[(kb + 16 + r) * kRow + c];
-        }
-        *reinterpret_cast<half8v*>(out + (plane * kHeadDim + c) * out_rows + t0 + 8 * q) = v;
-      }
-    } else {
-      for (int e = tid; e < 64 * kHeadDim; e += 256) {
-        const int c = e >> 6, kk = e & 63;
-        if (kk < nt) out[(plane * kHeadDim + c) * out_rows + key_column(t0 + kk)] = tile[kk * kRow + c];
-      }
-    }
-  } else {
-    for (int e = tid; e < 64 * 16; e += 256) {
-      const int kk = e >> 4, c8 = (e & 15) * 8;
-      if (kk < nt)
-        *reinterpret_cast<half8v*>(out + (plane * out_rows + t0 + kk) * kHeadDim + c8) =
-            *reinterpret_cast<const half8v*>(&tile[kk * kRow + c8]);
-    }
-  }
+  store_rows<TRANSPOSED>(tile, kRow, out, out_rows, plane, t0, nt);
 }
 
 // ---------------------------------------------------------------- attention
@@ -585,9 +595,18 @@ __global__ __launch_bounds__(256) void group_decode_rows_kernel(const uint32_t* 
   const size_t plane = blockIdx.y;
   const int t0 = blockIdx.x * 64;
   const int nt = min(64, cached - t0);
-  for (int e = tid; e < W * 64; e += 256) {
-    const int w = e >> 6, k = e & 63;
-    rec[e] = k < nt ? idx[tile_word(plane, capacity, t0 + k, w, W)] : 0u;
+  // every load of the staging goes out before the first LDS store
+  constexpr int kLoads = (W * 64 + 255) / 256;
+  uint32_t rv[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int e = tid + 256 * j, w = e >> 6, k = e & 63;
+    rv[j] = e < W * 64 && k < nt ? idx[tile_word(plane, capacity, t0 + k, w, W)] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int e = tid + 256 * j;
+    if (e < W * 64) rec[e] = rv[j];
   }
   __syncthreads();
   for (int e = tid; e < 64 * kHeadDim; e += 256) {
@@ -603,20 +622,7 @@ __global__ __launch_bounds__(256) void group_decode_rows_kernel(const uint32_t* 
     tile[k * kRow + c] = (_Float16)fmaf(dh, (float)q, zh);
   }
   __syncthreads();
-  if (TRANSPOSED) {
-    for (int e = tid; e < 64 * kHeadDim; e += 256) {
-      const int c = e >> 6, k = e & 63;
-      if (k < nt) out[(plane * kHeadDim + c) * out_rows + key_column(t0 + k)] = tile[k * kRow + c];
-    }
-  } else {
-    typedef _Float16 half8v __attribute__((ext_vector_type(8)));
-    for (int e = tid; e < 64 * 16; e += 256) {
-      const int k = e >> 4, c8 = (e & 15) * 8;
-      if (k < nt)
-        *reinterpret_cast<half8v*>(out + (plane * out_rows + t0 + k) * kHeadDim + c8) =
-            *reinterpret_cast<const half8v*>(&tile[k * kRow + c8]);
-    }
-  }
+  store_rows<TRANSPOSED>(tile, kRow, out, out_rows, plane, t0, nt);
 }
 
 // Key features of the Jensen-bias correction: row t < Tk_pad of a plane gets
