@@ -557,18 +557,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = tid / KK; r < R; r += kSlices) tabk[r * KK + c] = presplit_entry(n, crk[r]);
     }
+  } else if (PRE) {
+    // small pre-split tables: one direction per (table, code pair), written
+    // for every norm index
+    for (int e = tid; e < n_tables * KK; e += kThreads) {
+      const bool v = e >= KK;
+      const int code = v ? e - KK : e;
+      const float* cx = v ? cxv : cxk;
+      const float* cr = v ? crv : crk;
+      const float4 n = decode_dir(cx[code % K], cx[code / K]);
+      uint4* t = tabk + (v ? kTab : 0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) t[r * KK + code] = presplit_entry(n, cr[r]);
+    }
   } else {
     for (int e = tid; e < n_tables * kTab; e += kThreads) {
       const bool v = e >= kTab;
       const int i = v ? e - kTab : e;
       const float* cx = v ? cxv : cxk;
-      if (PRE) {
-        const int code = i % KK, r = i / KK;
-        tabk[e] = presplit_entry(decode_dir(cx[code % K], cx[code / K]), (v ? crv : crk)[r]);
-      } else {
-        const float4 n = decode_dir(cx[i % K], cx[i / K]);
-        tabk[e] = make_uint4(__float_as_uint(n.x), __float_as_uint(n.y), __float_as_uint(n.z), 0u);
-      }
+      const float4 n = decode_dir(cx[i % K], cx[i / K]);
+      tabk[e] = make_uint4(__float_as_uint(n.x), __float_as_uint(n.y), __float_as_uint(n.z), 0u);
     }
   }
   // ---- q_rot = H diag(s) q / sqrt(d) for the G heads (rows >= G are zero)
