@@ -97,3 +97,15 @@ def test_chunk_full_size_sampled():
     err, _ = run_chunk(w, rows=rows, heads=[0, 17, 39])
     say(f"chunk full err {err:.3e}")
     assert err <= ATOL
+
+
+@pytest.mark.parametrize("cached,tc", [(0, 1), (5, 20), (20, 12), (31, 1), (32, 32), (40, 40), (64, 32),
+                                       (40, 57)])
+def test_chunk_tile_counts(cached, tc):
+    """Windows of one, two and three 32-key tiles, full and ragged, so that
+    both buffers of the tile pipeline serve as the last one and a single
+    partial tile is the whole key range."""
+    w = workload("chunk", Hq=2, Hkv=2, T=64, chunk_q=max(tc, 1))
+    err, _ = run_chunk(w, cached=cached, tc=tc)
+    say(f"chunk cached {cached} current {tc} err {err:.3e}")
+    assert err <= ATOL

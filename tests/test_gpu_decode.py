@@ -178,3 +178,12 @@ def test_decode_reuses_workspace():
         ref = oatt.decode_attention(inp["q"].double().numpy(), kcache.to_host(),
                                     vcache.to_host(), hk, hv, inp["seq_lens"].numpy())
         assert np.abs(out.cpu().double().numpy() - ref).max() <= ATOL
+
+
+def test_decode_max_len_zero():
+    """max_seq_len = 0: every row is zero (the scan's speculative first-block
+    loads read a zeroed device block instead of the cache)."""
+    w = workload("gqa32k", B=2)
+    err, out, lens = run_case(w, T=128, seq_override=[5, 128], max_len=0)
+    assert err <= ATOL
+    assert np.all(out == 0.0)
