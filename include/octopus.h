@@ -300,7 +300,9 @@ octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B
  * fp16 staging requires |rotated entries| < 65504 and rounds each operand to
  * 11 significant bits, so this path is meant for inputs without large
  * outlier channels (the decode path computes in fp32).  Tq == 0 is a no-op;
- * an empty window gives zero output rows.                                  */
+ * an empty window gives zero output rows.  A window whose staged rows exceed
+ * 2 GiB a plane (cached_tokens + Tc, rounded up to 64, times 256 bytes)
+ * returns OCTO_ERR_UNSUPPORTED.                                            */
 octo_status octo_attend_chunk(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
                               const octo_cache_view* k_cache, const octo_cache_view* v_cache,
                               int32_t cached_tokens, const void* q, const void* k_cur,

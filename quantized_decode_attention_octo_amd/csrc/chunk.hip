@@ -790,6 +790,11 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   if (((uintptr_t)q | (uintptr_t)k_cur | (uintptr_t)v_cur) & 1 || ((uintptr_t)out & 3))
     return fail(OCTO_ERR_ALIGNMENT, "%s: q, k_cur, v_cur or out misaligned", what);
   const ChunkPlan p = chunk_plan(B, num_q_heads, Hkv, Tq, cached_tokens, Tc, corr);
+  // the attention kernel addresses a plane's staged keys and values through
+  // buffer descriptors with 32-bit byte ranges
+  if ((int64_t)p.Tk_pad * kHeadDim * 2 > INT32_MAX)
+    return fail(OCTO_ERR_UNSUPPORTED, "%s: %d keys a plane exceed 2 GiB of staged rows", what,
+                p.Tk_pad);
   if (!workspace || workspace_bytes < p.total)
     return fail(OCTO_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", what,
                 workspace_bytes, p.total);

@@ -241,6 +241,9 @@ def test_chunk_errors(L):
     assert ch(Tq=0) == 0                                     # nothing to do
     assert ch(flags=4) == 1                                  # unknown flag
     assert ch(flags=1) == 2                                  # correction with OCTOPUS keys
+    # staged rows of a plane beyond 2 GiB (2^23 keys x 256 B): unsupported
+    big = view(H=2, cap=1 << 23)
+    assert ch(kv=big, vv=big, cached=(1 << 23) - 64, Tc=64, ws_bytes=1 << 62) == 2
 
 
 def gdesc(bits=2, group=32, b_dir=0, b_nrm=0, qjl=0):
