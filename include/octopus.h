@@ -287,9 +287,9 @@ octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B
  * R_v v_cur and gamma u^ of the cached tokens (Eq. 13); the epilogue applies
  * R_v^T.  The workspace receives the fp16 rotated queries and the fp16
  * rotated key and value rows of the whole window (cached then current).
- *   q          device bf16 [B, num_q_heads, Tq, d] contiguous.
- *   k_cur,v_cur device bf16 [B, kv_heads, Tc, d] contiguous (may be NULL if
- *              Tc == 0).
+ *   q          device bf16 [B, num_q_heads, Tq, d] contiguous, 16-byte aligned.
+ *   k_cur,v_cur device bf16 [B, kv_heads, Tc, d] contiguous, 16-byte aligned
+ *              (may be NULL if Tc == 0).
  *   out        device fp32 [B, num_q_heads, Tq, d].
  *   workspace  device, >= octo_chunk_workspace_bytes(...), 256-byte aligned.
  * Keys must not carry QJL in this path; keys and values may use the group

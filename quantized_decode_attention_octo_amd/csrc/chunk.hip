@@ -52,7 +52,7 @@ __device__ inline int key_column(int k) {
 // queries, so that scores come out of the MFMA in log2 units.  Row-major
 // output: row out_off + t of a [out_rows][128] plane.  Transposed output:
 // column key_column(out_off + t) of a [128][out_rows] plane.
-// One workgroup takes 64 rows, one wavefront per row for the transform; the
+// One workgroup takes 64 rows, sixteen lanes a row for the transform; the
 // transposed store goes through LDS so that 64 consecutive columns are
 // written together.
 //
@@ -68,53 +68,78 @@ __global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __rest
                                                           int out_rows, int out_off,
                                                           _Float16* __restrict__ feat = nullptr,
                                                           int feat_gs = 32, float feat_c = 0.0f) {
-  __shared__ _Float16 tile[TRANSPOSED ? 64 * 130 : 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+  __shared__ _Float16 tile[TRANSPOSED ? 64 * 130 : 2];
+  // Sixteen lanes take a row, lane cl holding coordinates 8 cl .. 8 cl + 7
+  // (one 16-byte load and store); a wavefront instruction covers 4 rows.
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane >> 4, cl = lane & 15;
   const int plane = blockIdx.y;
   const int t0 = blockIdx.x * 64;
-  const float s0 = splitmix_sign(seed, lane), s1 = splitmix_sign(seed, lane + 64);
+  float sg[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sg[e] = splitmix_sign(seed, 8 * cl + e);
   // the wavefront's 16 rows: every load in flight at once (rows past T read
   // row T - 1 and are zeroed; with T = 0 there is nothing to read)
-  uint16_t ra[16] = {}, rb[16] = {};
+  uint4 raw[4] = {};
   if (T > 0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int t = min(t0 + wave + 4 * j, T - 1);
-      const uint16_t* src = in + ((size_t)plane * T + t) * kHeadDim;
-      ra[j] = src[lane];
-      rb[j] = src[lane + 64];
+    for (int j = 0; j < 4; ++j) {
+      const int t = min(t0 + 16 * wave + 4 * j + sub, T - 1);
+      raw[j] = *reinterpret_cast<const uint4*>(in + ((size_t)plane * T + t) * kHeadDim + 8 * cl);
     }
   }
-  {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int k = wave + 4 * j, t = t0 + k;
-      const float xaj = t < T ? bf16_to_f32(ra[j]) : 0.0f, xbj = t < T ? bf16_to_f32(rb[j]) : 0.0f;
-      float a = xaj * s0, b = xbj * s1;
-      wht128(a, b);
-      if (TRANSPOSED) {
-        tile[k * 130 + lane] = (_Float16)(a * post);
-        tile[k * 130 + lane + 64] = (_Float16)(b * post);
-      } else if (t < T_out) {
-        _Float16* dst = out + ((size_t)plane * out_rows + out_off + t) * kHeadDim;
-        dst[lane] = (_Float16)(a * post);
-        dst[lane + 64] = (_Float16)(b * post);
-      }
-      if (!TRANSPOSED && feat != nullptr) {        // uniform branch
-        // group sums of the squared rotated coordinates (a: coordinates
-        // 0..63, b: 64..127), reduced within the groups' lanes
-        float sa = a * a * (kInvSqrtD * kInvSqrtD), sb = b * b * (kInvSqrtD * kInvSqrtD);
-        for (int m = 1; m < feat_gs; m <<= 1) {
-          sa += __shfl_xor(sa, m, 64);
-          sb += __shfl_xor(sb, m, 64);
+  for (int j = 0; j < 4; ++j) {
+    const int k = 16 * wave + 4 * j + sub, t = t0 + k;
+    const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t h = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);   // bf16 -> fp32
+      v[e] = t < T ? __uint_as_float(h) * sg[e] : 0.0f;
+    }
+    // H (Sylvester order, unnormalized) on the row: coordinate bits 0..2
+    // within the lane, bits 3..6 across the row's 16 lanes
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!(e & m)) {
+          const float x = v[e], y = v[e | m];
+          v[e] = x + y;
+          v[e | m] = x - y;
         }
-        const int ga = 64 / feat_gs;                  // groups held in a
-        const int j = lane & (kFeat - 1);
-        const float fa = __shfl(sa, min(j, ga - 1) * feat_gs, 64);
-        const float fb = __shfl(sb, max(min(j - ga, ga - 1), 0) * feat_gs, 64);
-        const float f = j < ga ? fa : (j < 2 * ga ? fb : 0.0f);
-        if (t < T && lane < kFeat) feat[((size_t)plane * T + t) * kFeat + lane] = (_Float16)(feat_c * f);
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __shfl_xor(v[e], m, 64);
+        v[e] = (cl & m) ? (p - v[e]) : (v[e] + p);
       }
+    half8v o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (_Float16)(v[e] * post);
+    if (TRANSPOSED) {
+      typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        *reinterpret_cast<half2v*>(&tile[k * 130 + 8 * cl + e]) = half2v{o[e], o[e + 1]};
+    } else if (t < T_out) {
+      *reinterpret_cast<half8v*>(out + ((size_t)plane * out_rows + out_off + t) * kHeadDim + 8 * cl) = o;
+    }
+    if (!TRANSPOSED && feat != nullptr) {          // uniform branch
+      // group sums of the squared rotated coordinates: a group of feat_gs
+      // coordinates is feat_gs / 8 consecutive lanes of the row
+      float sq = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq = fmaf(v[e] * kInvSqrtD, v[e] * kInvSqrtD, sq);
+      const int lpg = feat_gs / 8;
+      for (int m = 1; m < lpg; m <<= 1) sq += __shfl_xor(sq, m, 64);
+      // slot cl < kFeat of the row's feature vector: group cl, or 0 past the groups
+      const int ng = kHeadDim / feat_gs;
+      const float f = __shfl(sq, 16 * sub + min(cl, ng - 1) * lpg, 64);
+      if (t < T && cl < kFeat) feat[((size_t)plane * T + t) * kFeat + cl] = (_Float16)(cl < ng ? feat_c * f : 0.0f);
     }
   }
   if (TRANSPOSED) {
@@ -787,8 +812,9 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   if (Tq == 0) return OCTO_OK;
   if (!q || !out || (Tc > 0 && (!k_cur || !v_cur)))
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: q, out, k_cur, v_cur must be set", what);
-  if (((uintptr_t)q | (uintptr_t)k_cur | (uintptr_t)v_cur) & 1 || ((uintptr_t)out & 3))
-    return fail(OCTO_ERR_ALIGNMENT, "%s: q, k_cur, v_cur or out misaligned", what);
+  // the rows are read 16 bytes a lane
+  if (((uintptr_t)q | (uintptr_t)k_cur | (uintptr_t)v_cur) & 15 || ((uintptr_t)out & 3))
+    return fail(OCTO_ERR_ALIGNMENT, "%s: q, k_cur, v_cur (16 bytes) or out (4) misaligned", what);
   const ChunkPlan p = chunk_plan(B, num_q_heads, Hkv, Tq, cached_tokens, Tc, corr);
   // the attention kernel addresses a plane's staged keys and values through
   // buffer descriptors with 32-bit byte ranges

@@ -227,13 +227,14 @@ def test_chunk_errors(L):
     assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 2, ctypes.byref(n)) == 1
 
     def ch(kd=kd, vd=vd, kv=kv, vv=vv, cached=128, Hq=2, Tq=64, Tc=64, ws=4096, ws_bytes=need,
-           flags=0):
+           flags=0, qp=4096):
         p = ctypes.c_void_p(4096)
         return L.octo_attend_chunk(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(kv),
-                                   ctypes.byref(vv), cached, p, p, p, Hq, Tq, Tc, 0.0, flags, p, ws,
-                                   ws_bytes, None)
+                                   ctypes.byref(vv), cached, ctypes.c_void_p(qp), p, p, Hq, Tq, Tc,
+                                   0.0, flags, p, ws, ws_bytes, None)
     assert ch(ws_bytes=need - 1) == 5
     assert ch(ws=4352 + 1) == 3
+    assert ch(qp=4096 + 8) == 3                              # rows are read 16 bytes a lane
     assert ch(cached=300) == 4
     assert ch(Hq=3) == 1
     assert ch(Tq=-1) == 1
