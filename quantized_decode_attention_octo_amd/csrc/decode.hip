@@ -77,6 +77,7 @@ constexpr int kBlock = 32;            // tokens per wavefront iteration
 constexpr int kMaxG = 16;             // query heads per KV head (MFMA columns)
 constexpr float kUScale = 64.0f;      // exact scale of u^ in the operands
 constexpr float kInvSqrtD = 0.08838834764831845f;
+constexpr float kLazy = 5.545177444479562f;   // 8 ln 2: slack of the lazy running maximum
 constexpr int kMaxSmallPre = 1024;    // largest pre-split table beside a second
                                       // workgroup on the CU (entries)
 
@@ -828,8 +829,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kt][r]);
     mx = rows_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_run == m_new ? 1.0f : __expf(m_run - m_new);
+    // Lazy running maximum: a head moves its maximum (and rescales its sums)
+    // only when a score exceeds it by more than kLazy, so that most blocks
+    // skip the rescale; the weights stay below e^kLazy = 256 (times the value
+    // norm, or 64), inside fp16, and the merges cancel the shift exactly.
+    const bool up = mx > m_run + kLazy;
+    const float m_new = up ? mx : m_run;
+    const float alpha = up ? __expf(m_run - m_new) : 1.0f;
     float pw[8], psum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
