@@ -163,41 +163,54 @@ __device__ inline float4 oct_dir(float xi, float eta) {
   return make_float4(x / n, y / n, z / n, 0.0f);
 }
 
-// Stores the LDS tile of tokens t0 .. t0 + nt - 1 (rows of kRow halves) as
-// rows of a [out_rows][128] plane (16-byte chunks) or as columns of a
-// [128][out_rows] plane at key_column.  A full transposed tile goes out in
-// 16-byte chunks: columns 8 q .. 8 q + 7 of coordinate c hold keys
-// 32 (q / 4) + {4 j + r, 16 + 4 j + r}, j = q mod 4, r < 4.
+// LDS staging tile of 64 tokens x 128 coordinates, laid out for its store.
+// Row-major output: token rows of 130 halves (65 words), so that the 64
+// lanes of a wavefront writing one coordinate of 64 tokens meet 64 different
+// banks.  Transposed output: coordinate rows of 72 halves holding the tokens
+// at key_column order, so that a coordinate's 64 keys leave in 16-byte
+// chunks exactly as they lie in the output, and the writes of one coordinate
+// fill 32 consecutive words.
 template <bool TRANSPOSED>
-__device__ inline void store_rows(const _Float16* tile, int kRow, _Float16* __restrict__ out,
+struct StageTile {
+  static constexpr int kRowHalves = TRANSPOSED ? 72 : 130;
+  static constexpr int kElems = TRANSPOSED ? kHeadDim * 72 : 64 * 130;
+  __device__ static int at(int k, int c) {
+    return TRANSPOSED ? c * 72 + key_column(k) : k * 130 + c;
+  }
+};
+
+// Stores the staging tile of tokens t0 .. t0 + nt - 1 (t0 a multiple of 64)
+// as rows of a [out_rows][128] plane (16-byte chunks) or as columns of a
+// [128][out_rows] plane at key_column.
+template <bool TRANSPOSED>
+__device__ inline void store_rows(const _Float16* tile, _Float16* __restrict__ out,
                                   int out_rows, size_t plane, int t0, int nt) {
-  typedef _Float16 half8v __attribute__((ext_vector_type(8)));
   const int tid = threadIdx.x;
   if (TRANSPOSED) {
     if (nt == 64) {
       for (int e = tid; e < kHeadDim * 8; e += 256) {
         const int c = e >> 3, q = e & 7;
-        const int kb = 32 * (q >> 2) + 4 * (q & 3);
-        half8v v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = tile[(kb + r) * kRow + c];
-          v[4 + r] = tile[(kb + 16 + r) * kRow + c];
-        }
-        *reinterpret_cast<half8v*>(out + (plane * kHeadDim + c) * out_rows + t0 + 8 * q) = v;
+        *reinterpret_cast<uint4*>(out + (plane * kHeadDim + c) * out_rows + t0 + 8 * q) =
+            *reinterpret_cast<const uint4*>(&tile[c * 72 + 8 * q]);
       }
     } else {
       for (int e = tid; e < 64 * kHeadDim; e += 256) {
         const int c = e >> 6, kk = e & 63;
-        if (kk < nt) out[(plane * kHeadDim + c) * out_rows + key_column(t0 + kk)] = tile[kk * kRow + c];
+        if (kk < nt)
+          out[(plane * kHeadDim + c) * out_rows + key_column(t0 + kk)] =
+              tile[StageTile<true>::at(kk, c)];
       }
     }
   } else {
+    // four word reads a chunk: token rows are 4-byte but not 16-byte aligned
+    const uint32_t* tw = reinterpret_cast<const uint32_t*>(tile);
     for (int e = tid; e < 64 * 16; e += 256) {
       const int kk = e >> 4, c8 = (e & 15) * 8;
-      if (kk < nt)
-        *reinterpret_cast<half8v*>(out + (plane * out_rows + t0 + kk) * kHeadDim + c8) =
-            *reinterpret_cast<const half8v*>(&tile[kk * kRow + c8]);
+      if (kk < nt) {
+        const int w0 = kk * 65 + c8 / 2;
+        *reinterpret_cast<uint4*>(out + (plane * out_rows + t0 + kk) * kHeadDim + c8) =
+            make_uint4(tw[w0], tw[w0 + 1], tw[w0 + 2], tw[w0 + 3]);
+      }
     }
   }
 }
@@ -216,12 +229,12 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
                                                           int out_rows) {
   constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD, BT = FWD + BN;
   constexpr int WI = (kNTri * BT + 31) / 32;
-  constexpr int kRow = 136;                        // halves per token row in LDS
+  using ST = StageTile<TRANSPOSED>;
   constexpr int kTriG = 11;                        // triplets per thread: 4 x 11 >= 43
   constexpr int GW = (31 + kTriG * BT + 31) / 32;  // record words covering them from any shift
   __shared__ float4 lut[K * K];
   __shared__ float crho[R], cxi[K];
-  __shared__ __attribute__((aligned(16))) _Float16 tile[64 * kRow];
+  __shared__ __attribute__((aligned(16))) _Float16 tile[ST::kElems];
   const int tid = threadIdx.x;
   const size_t plane = blockIdx.y;
   const int t0 = blockIdx.x * 64;
@@ -254,13 +267,12 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
     const uint32_t code = f & ((1u << FWD) - 1u), ir = f >> FWD;
     const float s = crho[ir] * gam;
     const float4 n = lut[code];
-    _Float16* dst = &tile[k * kRow + 3 * i];
-    dst[0] = (_Float16)(s * n.x);
-    dst[1] = (_Float16)(s * n.y);
-    if (i < kNTri - 1) dst[2] = (_Float16)(s * n.z);   // coordinate 128 is the pad
+    tile[ST::at(k, 3 * i)] = (_Float16)(s * n.x);
+    tile[ST::at(k, 3 * i + 1)] = (_Float16)(s * n.y);
+    if (i < kNTri - 1) tile[ST::at(k, 3 * i + 2)] = (_Float16)(s * n.z);   // coordinate 128 is the pad
   }
   __syncthreads();
-  store_rows<TRANSPOSED>(tile, kRow, out, out_rows, plane, t0, nt);
+  store_rows<TRANSPOSED>(tile, out, out_rows, plane, t0, nt);
 }
 
 // ---------------------------------------------------------------- attention
@@ -605,17 +617,17 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
 
 // The group-wise value codec: one workgroup per 64 cached tokens of a plane
 // stages their records (word w of the 64 tokens is 256 contiguous bytes) in
-// LDS, then lanes take (token, coordinate) items token-fastest and write
-// fp16(Delta code + z), the rotated value, into the tile stored as above.
+// LDS, then thread (token, quarter) writes fp16(Delta code + z), the rotated
+// value, of its 32 coordinates into the tile stored as above.
 template <int VB, int GS, bool TRANSPOSED>
 __global__ __launch_bounds__(256) void group_decode_rows_kernel(const uint32_t* __restrict__ idx,
                                                                 int capacity, int cached,
                                                                 _Float16* __restrict__ out,
                                                                 int out_rows) {
   constexpr int G = kHeadDim / GS, WC = VB * kHeadDim / 32, W = group_record_words(VB, GS);
-  constexpr int kRow = 136;
+  using ST = StageTile<TRANSPOSED>;
   __shared__ uint32_t rec[W * 64];
-  __shared__ __attribute__((aligned(16))) _Float16 tile[64 * kRow];
+  __shared__ __attribute__((aligned(16))) _Float16 tile[ST::kElems];
   const int tid = threadIdx.x;
   const size_t plane = blockIdx.y;
   const int t0 = blockIdx.x * 64;
@@ -634,20 +646,29 @@ __global__ __launch_bounds__(256) void group_decode_rows_kernel(const uint32_t* 
     if (e < W * 64) rec[e] = rv[j];
   }
   __syncthreads();
-  for (int e = tid; e < 64 * kHeadDim; e += 256) {
-    const int k = e & 63, c = e >> 6;
-    const int pos = c * VB, w = pos >> 5, sh = pos & 31;
-    const uint32_t lo = rec[w * 64 + k];
-    const uint32_t hi = sh + VB > 32 ? rec[(w + 1) * 64 + k] : 0u;
-    const uint32_t q = (uint32_t)((((uint64_t)hi << 32) | lo) >> sh) & ((1u << VB) - 1u);
-    const int j = c / GS;
+  // Thread (k, w): token k, coordinates 32 w .. 32 w + 31, whose codes fill
+  // words VB w .. VB w + VB - 1 of the record and whose groups' steps and
+  // zero points are decoded once.
+  static_assert(GS == 16 || GS == 32, "a thread's 32 coordinates span whole groups");
+  const int k = tid & 63, w = tid >> 6;
+  uint32_t cw[VB];
+#pragma unroll
+  for (int i = 0; i < VB; ++i) cw[i] = rec[(VB * w + i) * 64 + k];
+#pragma unroll
+  for (int gi = 0; gi < 32 / GS; ++gi) {
+    const int j = (32 / GS) * w + gi;
     const uint32_t sw = rec[(WC + j / 4) * 64 + k], zw = rec[(WC + G / 4 + j / 2) * 64 + k];
     const float dh = e4m3_value((sw >> (8 * (j % 4))) & 0xffu);
     const float zh = __uint_as_float(((zw >> (16 * (j % 2))) & 0xffffu) << 16);
-    tile[k * kRow + c] = (_Float16)fmaf(dh, (float)q, zh);
+#pragma unroll
+    for (int m = 0; m < GS; ++m) {
+      const int cl = GS * gi + m;
+      const uint32_t q = field<VB>(cw, cl * VB);
+      tile[ST::at(k, 32 * w + cl)] = (_Float16)fmaf(dh, (float)q, zh);
+    }
   }
   __syncthreads();
-  store_rows<TRANSPOSED>(tile, kRow, out, out_rows, plane, t0, nt);
+  store_rows<TRANSPOSED>(tile, out, out_rows, plane, t0, nt);
 }
 
 // Key features of the Jensen-bias correction: row t < Tk_pad of a plane gets
