@@ -60,22 +60,35 @@ __device__ inline int key_column(int k) {
 // kFeat fp16 features: slot j < 128 / feat_gs holds feat_c ||(R x_t)_j||^2
 // over group j of the rotated coordinates, the other slots 0.
 constexpr int kFeat = 8;           // feature slots per row: groups of g >= 16
+struct RotJob {
+  const uint16_t* in;            // [planes][T][128] bf16
+  int T, T_out;
+  uint64_t seed;
+  float post;
+  _Float16* out;
+  int out_rows, out_off;
+  _Float16* feat;                // query features, or null
+  int feat_gs;
+  float feat_c;
+  int tiles, planes;             // 64-row tiles per plane; planes (0: no job)
+};
+
 template <bool TRANSPOSED>
-__global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __restrict__ in,
-                                                          int T, int T_out, uint64_t seed,
-                                                          float post,
-                                                          _Float16* __restrict__ out,
-                                                          int out_rows, int out_off,
-                                                          _Float16* __restrict__ feat = nullptr,
-                                                          int feat_gs = 32, float feat_c = 0.0f) {
+__device__ inline void rotate_rows(const RotJob& jb, int tile_x, int plane, _Float16* tile) {
   typedef _Float16 half8v __attribute__((ext_vector_type(8)));
-  __shared__ _Float16 tile[TRANSPOSED ? 64 * 130 : 2];
+  const uint16_t* __restrict__ in = jb.in;
+  _Float16* __restrict__ out = jb.out;
+  const int T = jb.T, T_out = jb.T_out, out_rows = jb.out_rows, out_off = jb.out_off;
+  const uint64_t seed = jb.seed;
+  const float post = jb.post;
+  _Float16* __restrict__ feat = jb.feat;
+  const int feat_gs = jb.feat_gs;
+  const float feat_c = jb.feat_c;
   // Sixteen lanes take a row, lane cl holding coordinates 8 cl .. 8 cl + 7
   // (one 16-byte load and store); a wavefront instruction covers 4 rows.
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane >> 4, cl = lane & 15;
-  const int plane = blockIdx.y;
-  const int t0 = blockIdx.x * 64;
+  const int t0 = tile_x * 64;
   float sg[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sg[e] = splitmix_sign(seed, 8 * cl + e);
@@ -149,6 +162,24 @@ __global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __rest
       if (t < T_out)
         out[((size_t)plane * kHeadDim + c) * out_rows + key_column(out_off + t)] = tile[k * 130 + c];
     }
+  }
+}
+
+// The three row transforms of a chunk call (queries; current keys; current
+// values, transposed) in one launch, so that the loads of one overlap the
+// stores of another: workgroups [0, n0) take job 0, the next n1 job 1, the
+// rest job 2, where n_i = tiles_i planes_i.
+__global__ __launch_bounds__(256) void rotate_rows_kernel(RotJob q, RotJob k, RotJob v) {
+  __shared__ _Float16 tile[64 * 130];
+  const int n0 = q.tiles * q.planes, n1 = k.tiles * k.planes;
+  int id = blockIdx.x;
+  if (id < n0) {
+    rotate_rows<false>(q, id % q.tiles, id / q.tiles, tile);
+  } else if ((id -= n0) < n1) {
+    rotate_rows<false>(k, id % k.tiles, id / k.tiles, tile);
+  } else {
+    id -= n1;
+    rotate_rows<true>(v, id % v.tiles, id / v.tiles, tile);
   }
 }
 
@@ -861,18 +892,17 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   // query features: minus 16 log2(e) tau^2 / 24 ||(R q)_j||^2 (the key
   // features carry Delta^2 / 16), so that their product is -b in log2 units
   const float feat_c = -16.0f * kLog2e * tau * tau / 24.0f;
-  hipLaunchKernelGGL(rotate_rows_kernel<false>, dim3((Tq + 63) / 64, planes_q), dim3(256), 0,
-                     stream, static_cast<const uint16_t*>(q), Tq, Tq, kc.seed, kInvSqrtD * scale2,
-                     qr, Tq, 0, qf, corr ? kc.group : 32, feat_c);
+  RotJob jq{static_cast<const uint16_t*>(q), Tq, Tq, kc.seed, kInvSqrtD * scale2, qr, Tq, 0,
+            qf, corr ? kc.group : 32, feat_c, (Tq + 63) / 64, planes_q};
   const int cur_out = p.Tk_pad - cached_tokens;  // current rows plus the zero tile padding
-  if (cur_out > 0) {
-    hipLaunchKernelGGL(rotate_rows_kernel<false>, dim3((cur_out + 63) / 64, planes_kv), dim3(256),
-                       0, stream, static_cast<const uint16_t*>(k_cur), Tc, cur_out, kc.seed,
-                       kInvSqrtD, kr, p.Tk_pad, cached_tokens);
-    hipLaunchKernelGGL(rotate_rows_kernel<true>, dim3((cur_out + 63) / 64, planes_kv), dim3(256),
-                       0, stream, static_cast<const uint16_t*>(v_cur), Tc, cur_out, vc.seed,
-                       kInvSqrtD, vr, p.Tk_pad, cached_tokens);
-  }
+  const int cur_tiles = cur_out > 0 ? (cur_out + 63) / 64 : 0;
+  RotJob jk{static_cast<const uint16_t*>(k_cur), Tc, cur_out, kc.seed, kInvSqrtD, kr, p.Tk_pad,
+            cached_tokens, nullptr, 32, 0.0f, cur_tiles, planes_kv};
+  RotJob jv{static_cast<const uint16_t*>(v_cur), Tc, cur_out, vc.seed, kInvSqrtD, vr, p.Tk_pad,
+            cached_tokens, nullptr, 32, 0.0f, cur_tiles, planes_kv};
+  const long rot_blocks = (long)jq.tiles * jq.planes + 2L * cur_tiles * planes_kv;
+  if (rot_blocks > 0)
+    hipLaunchKernelGGL(rotate_rows_kernel, dim3((unsigned)rot_blocks), dim3(256), 0, stream, jq, jk, jv);
   if (cached_tokens > 0) {
     if (!decode_rows(k_cache, kc, cached_tokens, kr, p.Tk_pad, false, stream) ||
         !decode_rows(v_cache, vc, cached_tokens, vr, p.Tk_pad, true, stream))
