@@ -6,7 +6,7 @@ matched to the empirical xi marginal; both are trained offline with the
 standard alternating assignment / update Lloyd-Max iteration "to distortion
 1e-10", serialized, and depend only on (d, b_dir, b_nrm).
 
-Readings (the paper leaves these open; all are listed in the design doc):
+Readings (the paper leaves these open):
   * samples are drawn by seeded Monte Carlo through the implementation itself:
     Gaussian keys in R^d -> unit norm -> R = H D_s -> triplets -> Eq. 5.  Only
     the full triplets (the first floor(d/3)) are pooled, since the zero-padded

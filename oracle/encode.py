@@ -17,7 +17,7 @@ Follows the OCTOPUS paper in its own order:
   Sec. 3.6 / App. C.15  optional QJL residual: r = u - u^, sigma = sign(R' r),
                         gamma_r = ||r|| stored as fp16
 
-Readings where the paper is silent (all listed in the design doc):
+Readings where the paper is silent:
   * eps = 1e-20; gamma is stored as fp32 (round to nearest even).
   * nearest centroid = brute-force argmin |x - c_k|, ties -> lowest index.
   * 3x3 tie rule: start from the seed (0, 0), visit the other eight in

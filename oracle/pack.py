@@ -4,8 +4,8 @@ The OCTOPUS paper (Sec. 3) stores S(k) = (gamma, I_dir, I_nrm): the norm, a
 packed stream of octahedral-coordinate indices and a packed stream of
 triplet-norm indices; with QJL also sigma in {+-1}^d and gamma_r in fp16
 (Sec. 3.6).  The paper fixes no bit layout.  The layout below is this
-project's (stated in the design doc) and is written here independently of the HIP
-code from its description:
+project's own and is written here independently of the HIP code from its
+description:
 
   * A stream is a little-endian, LSB-first bit string: field j of width w
     occupies bits [j*w, (j+1)*w), bit p is bit (p % 8) of byte p // 8.
@@ -25,7 +25,7 @@ code from its description:
     So one 64-token tile stores its W words as W rows of 64 consecutive words.
 
 Parity: pinned by pack/unpack round trips, explicit bit positions for
-hand-made fields, zero padding and the record sizes of the table in the design doc
+hand-made fields, zero padding and the record sizes per (b_dir, b_nrm, QJL)
 (tests/test_oracle_pack.py).
 """
 import numpy as np

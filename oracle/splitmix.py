@@ -4,7 +4,7 @@ The OCTOPUS paper (Sec. 1 and the abstract) calls the codec "deterministic
 given a seed" and builds R = H diag(s) with a random sign vector s (Sec. 3.1,
 App. C.2) and, for the QJL residual, a second rotation R' = H diag(s') "with
 independent seed" (Sec. 3.6).  It never names the generator.  Reading used
-here (stated in the design doc): the j-th sign is drawn from the j-th output of a
+here: the j-th sign is drawn from the j-th output of a
 SplitMix64 generator started at `seed`, i.e. the counter form
 
     z_j = mix64(seed + (j + 1) * 0x9E3779B97F4A7C15 mod 2^64)
