@@ -200,7 +200,10 @@ octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_codec, int32_t 
  *              Calls that share a workspace must not overlap in time.
  * Both contractions run on MFMA with fp16 hi/lo operand pairs and fp32
  * accumulation (about 2^-20 relative per product); softmax and the merge of
- * the splits are fp32.  K and V caches must share B, kv_heads, capacity and
+ * the splits are fp32.  Any finite value norm is supported: a token whose
+ * norm is 128 or more enters the running maximum with its score raised by
+ * its norm's binary exponent, so that every weight p gamma_v stays below
+ * 2^15, inside the fp16 operands.  K and V caches must share B, kv_heads, capacity and
  * (b_dir, b_nrm); V must not carry QJL.  V may instead use the group codec
  * (group 16 or 32) when K uses the (b+1, b-1) split and V has the same b
  * (the symmetric K = V bit width of the paper's comparisons); its products
@@ -244,7 +247,10 @@ octo_status octo_decode_step_workspace_bytes(const octo_codec_desc* k_codec, int
  *   window      1 .. 256.
  *   packed_lens, window_lens  device int32 [B], read and updated in place.
  *   max_packed_len  host bound: every P_b <= max_packed_len <= capacity
- *               (the split plan is sized by it; larger P_b are clamped).
+ *               (the split plan is sized by it).  A larger P_b breaks this
+ *               precondition: its packed tokens past max_packed_len are then
+ *               left out of the attention, while the ring slots, the
+ *               eviction and the length updates still follow P_b itself.
  *   workspace   device, >= octo_decode_step_workspace_bytes(...), 256-byte
  *               aligned.
  * Device-resident preconditions (not checked on the host): 0 <= n_b < window;

@@ -121,6 +121,45 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _expect(t, name, shape, dtypes, contiguous=True):
+    """Raises ValueError unless tensor t has exactly `shape` (None entries
+    match any size) and one of `dtypes` and, if asked, is contiguous.  The library sees only pointers, so these checks
+    are the only guard against reads and writes past a buffer."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {list(dtypes)}")
+    if t.dim() != len(shape) or any(e is not None and e != n for e, n in zip(shape, t.shape)):
+        want = tuple("*" if e is None else e for e in shape)
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_device(device, **tensors):
+    """Raises ValueError unless every tensor lives on `device`, a CUDA device
+    (checked after the shapes, so that a shape error is named first)."""
+    for name, t in tensors.items():
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} is on {t.device}; the kernels need device memory")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the cache on {device}")
+
+
+def _same_caches(k_cache, v_cache, k_codec, v_codec):
+    if k_cache.device != v_cache.device:
+        raise ValueError("the K and V caches live on different devices")
+    if (k_cache.B, k_cache.H, k_cache.capacity) != (v_cache.B, v_cache.H, v_cache.capacity):
+        raise ValueError("the K and V caches differ in batch, heads or capacity")
+    for c, cd, nm in ((k_cache, k_codec, "k_cache"), (v_cache, v_codec, "v_cache")):
+        if c.codec_key != cd.key():
+            raise ValueError(f"{nm} was allocated for another codec")
+
+
+F32_BF16 = (torch.float32, torch.bfloat16)
+BF16 = (torch.bfloat16,)
+
+
 def load_codebooks(d=128):
     with open(CODEBOOKS.format(d=d)) as f:
         return json.load(f)
@@ -160,6 +199,10 @@ class Codec:
     def sizes(self):
         return octo_record_sizes(self.desc)
 
+    def key(self):
+        """What fixes the record layout of a cache: (group, bits, split, QJL)."""
+        return (self.group, self.bits if self.group else 0, self.b_dir, self.b_nrm, self.qjl)
+
 
 class PackedCache:
     """The packed streams of one tensor (K or V) in the tile-64 layout."""
@@ -175,6 +218,7 @@ class PackedCache:
         self.qjl = torch.zeros(n * s.qjl_words, **i32) if codec.qjl else None
         self.gamma_r = torch.zeros(B, H, capacity, dtype=torch.int16, device=device) if codec.qjl else None
         self.B, self.H, self.capacity, self.sizes = B, H, capacity, s
+        self.codec_key = codec.key()
         self.device = self.idx.device
         self.view = CacheView(self.idx.data_ptr(), self.gamma.data_ptr() if self.gamma is not None else None,
                               self.qjl.data_ptr() if self.qjl is not None else None,
@@ -207,8 +251,12 @@ def octo_record_sizes(desc):
 def octo_encode(codec, x, cache, token_offset=0):
     """Encodes x[B, H, T, d] (fp32 or bf16, any strides with unit last stride)
     into tokens [token_offset, token_offset + T) of `cache`."""
-    if x.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("x must be float32 or bfloat16")
+    _expect(x, "x", (cache.B, cache.H, None, codec.d), F32_BF16, contiguous=False)
+    if cache.codec_key != codec.key():
+        raise ValueError("the cache was allocated for another codec")
+    if x.stride(3) != 1 or min(x.stride()) < 0:
+        raise ValueError("x needs a unit last stride and non-negative strides")
+    _on_device(cache.device, x=x, cache=cache.idx)
     B, H, T, d = x.shape
     strides = (ctypes.c_int64 * 4)(*x.stride())
     dt = DTYPE_F32 if x.dtype == torch.float32 else DTYPE_BF16
@@ -218,8 +266,12 @@ def octo_encode(codec, x, cache, token_offset=0):
 
 def octo_decode_tokens(codec, cache, t0, T, out=None):
     """Reconstructed tokens [t0, t0 + T) of every plane: out[B, H, T, d] fp32."""
+    if cache.codec_key != codec.key():
+        raise ValueError("the cache was allocated for another codec")
     if out is None:
-        out = torch.empty(cache.B, cache.H, T, 128, dtype=torch.float32, device=cache.device)
+        out = torch.empty(cache.B, cache.H, T, codec.d, dtype=torch.float32, device=cache.device)
+    _expect(out, "out", (cache.B, cache.H, T, codec.d), (torch.float32,))
+    _on_device(cache.device, out=out, cache=cache.idx)
     _check(lib().octo_decode_tokens(ctypes.byref(codec.desc), ctypes.byref(cache.view), t0, T,
                                     _ptr(out), _stream(out.device)))
     return out
@@ -246,17 +298,23 @@ def octo_attend_decode(k_codec, v_codec, k_cache, v_cache, q, seq_lens, max_seq_
                        softmax_scale=0.0, out=None, ws=None):
     """q[B, H_q, d] (fp32 or bf16, contiguous), seq_lens int32 [B] on the device.
     Returns out[B, H_q, d] fp32."""
-    if q.dtype not in (torch.float32, torch.bfloat16) or not q.is_contiguous():
-        raise TypeError("q must be a contiguous float32 or bfloat16 tensor")
-    if seq_lens.dtype != torch.int32:
-        raise TypeError("seq_lens must be int32")
-    B, Hq, d = q.shape
+    _same_caches(k_cache, v_cache, k_codec, v_codec)
+    dev, B = k_cache.device, k_cache.B
+    _expect(q, "q", (B, None, k_codec.d), F32_BF16)
+    Hq, d = q.shape[1], q.shape[2]
+    if Hq % k_cache.H:
+        raise ValueError(f"q has {Hq} heads, not a multiple of the {k_cache.H} KV heads")
+    _expect(seq_lens, "seq_lens", (B,), (torch.int32,))
     max_seq_len = k_cache.capacity if max_seq_len is None else int(max_seq_len)
     if out is None:
-        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    _expect(out, "out", (B, Hq, d), (torch.float32,))
+    _on_device(dev, q=q, seq_lens=seq_lens, out=out, k_cache=k_cache.idx, v_cache=v_cache.idx)
     need = octo_decode_workspace_bytes(k_codec, B, Hq, k_cache.H, max_seq_len)
     if ws is None or ws.numel() < need + 256:
-        ws = workspace(need, q.device)
+        ws = workspace(need, dev)
+    _expect(ws, "ws", (None,), (torch.uint8,))
+    _on_device(dev, ws=ws)
     dt = DTYPE_F32 if q.dtype == torch.float32 else DTYPE_BF16
     _check(lib().octo_attend_decode(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
                                     ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
@@ -282,22 +340,31 @@ def octo_decode_step(k_codec, v_codec, k_cache, v_cache, q, k_new, v_new, k_wind
     k_window/v_window[B, H_kv, W, d] bf16, packed_lens/window_lens int32 [B]
     (all on the device; the rings and the lengths are updated in place).
     Returns out[B, H_q, d] fp32."""
-    if q.dtype not in (torch.float32, torch.bfloat16) or not q.is_contiguous():
-        raise TypeError("q must be a contiguous float32 or bfloat16 tensor")
-    for t in (k_new, v_new, k_window, v_window):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise TypeError("new rows and rings must be contiguous bfloat16 tensors")
-    for t in (packed_lens, window_lens):
-        if t.dtype != torch.int32:
-            raise TypeError("packed_lens and window_lens must be int32")
-    B, Hq, d = q.shape
+    _same_caches(k_cache, v_cache, k_codec, v_codec)
+    dev, B, Hkv, D = k_cache.device, k_cache.B, k_cache.H, k_codec.d
+    _expect(q, "q", (B, None, D), F32_BF16)
+    Hq, d = q.shape[1], q.shape[2]
+    if Hq % Hkv:
+        raise ValueError(f"q has {Hq} heads, not a multiple of the {Hkv} KV heads")
+    _expect(k_new, "k_new", (B, Hkv, D), BF16)
+    _expect(v_new, "v_new", (B, Hkv, D), BF16)
+    _expect(k_window, "k_window", (B, Hkv, None, D), BF16)
     W = k_window.shape[2]
+    _expect(v_window, "v_window", (B, Hkv, W, D), BF16)
+    _expect(packed_lens, "packed_lens", (B,), (torch.int32,))
+    _expect(window_lens, "window_lens", (B,), (torch.int32,))
     max_packed_len = k_cache.capacity if max_packed_len is None else int(max_packed_len)
     if out is None:
-        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    _expect(out, "out", (B, Hq, d), (torch.float32,))
+    _on_device(dev, q=q, k_new=k_new, v_new=v_new, k_window=k_window, v_window=v_window,
+               packed_lens=packed_lens, window_lens=window_lens, out=out,
+               k_cache=k_cache.idx, v_cache=v_cache.idx)
     need = octo_decode_step_workspace_bytes(k_codec, B, Hq, k_cache.H, max_packed_len)
     if ws is None or ws.numel() < need + 256:
-        ws = workspace(need, q.device)
+        ws = workspace(need, dev)
+    _expect(ws, "ws", (None,), (torch.uint8,))
+    _on_device(dev, ws=ws)
     dt = DTYPE_F32 if q.dtype == torch.float32 else DTYPE_BF16
     _check(lib().octo_decode_step(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
                                   ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
@@ -324,16 +391,25 @@ def octo_attend_chunk(k_codec, v_codec, k_cache, v_cache, cached_tokens, q, k_cu
     (OCTO_CHUNK_JENSEN_CORRECTION; keys in the group codec).
     Returns out[B, H_q, Tq, d] fp32."""
     flags = CHUNK_JENSEN_CORRECTION if correction else 0
-    for t in (q, k_cur, v_cur):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise TypeError("q, k_cur and v_cur must be contiguous bfloat16 tensors")
-    B, Hq, Tq, d = q.shape
+    _same_caches(k_cache, v_cache, k_codec, v_codec)
+    dev, B, Hkv, D = k_cache.device, k_cache.B, k_cache.H, k_codec.d
+    _expect(q, "q", (B, None, None, D), BF16)
+    Hq, Tq, d = q.shape[1], q.shape[2], q.shape[3]
+    if Hq % Hkv:
+        raise ValueError(f"q has {Hq} heads, not a multiple of the {Hkv} KV heads")
+    _expect(k_cur, "k_cur", (B, Hkv, None, D), BF16)
     Tc = k_cur.shape[2]
+    _expect(v_cur, "v_cur", (B, Hkv, Tc, D), BF16)
     if out is None:
-        out = torch.empty(B, Hq, Tq, d, dtype=torch.float32, device=q.device)
+        out = torch.empty(B, Hq, Tq, d, dtype=torch.float32, device=dev)
+    _expect(out, "out", (B, Hq, Tq, d), (torch.float32,))
+    _on_device(dev, q=q, k_cur=k_cur, v_cur=v_cur, out=out, k_cache=k_cache.idx,
+               v_cache=v_cache.idx)
     need = octo_chunk_workspace_bytes(k_codec, B, Hq, k_cache.H, Tq, cached_tokens, Tc, flags)
     if ws is None or ws.numel() < need + 256:
-        ws = workspace(need, q.device)
+        ws = workspace(need, dev)
+    _expect(ws, "ws", (None,), (torch.uint8,))
+    _on_device(dev, ws=ws)
     _check(lib().octo_attend_chunk(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
                                    ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
                                    cached_tokens, _ptr(q), _ptr(k_cur), _ptr(v_cur), Hq, Tq, Tc,

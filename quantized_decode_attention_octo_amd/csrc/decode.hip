@@ -78,6 +78,8 @@ constexpr int kMaxG = 16;             // query heads per KV head (MFMA columns)
 constexpr float kUScale = 64.0f;      // exact scale of u^ in the operands
 constexpr float kInvSqrtD = 0.08838834764831845f;
 constexpr float kLazy = 5.545177444479562f;   // 8 ln 2: slack of the lazy running maximum
+constexpr float kTwoLn2 = 1.3862943611198906f; // 2 ln 2: one step of an fp32 exponent byte
+constexpr float kNormByte = 66.0f;            // exponent byte of value norms below 128
 constexpr int kMaxSmallPre = 1024;    // largest pre-split table beside a second
                                       // workgroup on the CU (entries)
 
@@ -681,8 +683,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   const int len = max(0, min(len_raw, min(a.max_len, a.capacity)));
   // uniform: the loop and its prefetch test become scalar branches
   const int t_end = __builtin_amdgcn_readfirstlane(min(len, t_begin + a.split_len));
-  if (a.step && split == 0 && g == 0 && tid == 0)   // the step's (P, n) for the merge launch
-    a.snap[b] = make_int2(len, max(0, min(win_raw, a.window - 1)));
+  // The step's (P, n) for the merge launch: P as stored (within the
+  // capacity), so that the ring slots and the eviction follow the sequence's
+  // state even where P exceeds max_len and the scan stops short of it.
+  if (a.step && split == 0 && g == 0 && tid == 0)
+    a.snap[b] = make_int2(max(0, min(len_raw, a.capacity)), max(0, min(win_raw, a.window - 1)));
 
   if (QJL && t0 < t_end) {                                   // (registers are short)
     load_block(blk, a, plane, t0, L);
@@ -823,16 +828,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     const int t_next = t0 + kWaves * kBlock < t_end ? t0 + kWaves * kBlock : t0;
     if (!QJL) load_block(blk, a, plane, t_next, L);
     // -- online softmax over the 32 tokens, head col (Sec. 3.6 / App. A)
+    // The value-side weight p gamma_v enters the MFMA as an fp16 hi/lo pair,
+    // so it must stay below 2^16.  A token whose value norm has fp32
+    // exponent byte b3 = bits >> 24 above kNormByte (gamma_v >= 128) takes
+    // part in the running maximum with its score raised by
+    // 2 ln 2 (b3 - kNormByte), which caps p gamma_v below 2^15 for any
+    // finite norm; smaller norms (b3 <= kNormByte, gamma_v < 128) leave the
+    // score as it is.  The merges only need every partial's sums to share
+    // the units exp(-m) of its maximum, which holds for any such shift.
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      const float gvn[4] = {blk.gv[kt].x, blk.gv[kt].y, blk.gv[kt].z, blk.gv[kt].w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kt][r]);
+      for (int r = 0; r < 4; ++r) {
+        float t = sc[kt][r];
+        if constexpr (VG == 0) {
+          const float b3 = (float)(__float_as_uint(gvn[r]) >> 24);
+          t = fmaf(fmaxf(b3, kNormByte), kTwoLn2, t);
+        }
+        mx = fmaxf(mx, t);
+      }
+    }
     mx = rows_max(mx);
+    if constexpr (VG == 0) mx -= kNormByte * kTwoLn2;
     // Lazy running maximum: a head moves its maximum (and rescales its sums)
-    // only when a score exceeds it by more than kLazy, so that most blocks
-    // skip the rescale; the weights stay below e^kLazy = 256 (times the value
-    // norm, or 64), inside fp16, and the merges cancel the shift exactly.
+    // only when a (raised) score exceeds it by more than kLazy, so that most
+    // blocks skip the rescale; p stays below e^kLazy = 256, p gamma_v below
+    // 2^15 (or 64 p below 2^14 with group values), inside fp16, and the
+    // merges cancel the shift exactly.
     const bool up = mx > m_run + kLazy;
     const float m_new = up ? mx : m_run;
     const float alpha = up ? __expf(m_run - m_new) : 1.0f;
@@ -1290,7 +1314,7 @@ __device__ void append_block(const StepArgs& a, int b) {
     }
   }
   if (tid == 0) {
-    a.packed_lens[b] = evict ? P + 1 : P;
+    if (evict) a.packed_lens[b] = P + 1;
     a.win_lens[b] = n + 1 < W ? n + 1 : n;
   }
 }

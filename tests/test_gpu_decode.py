@@ -187,3 +187,31 @@ def test_decode_max_len_zero():
     err, out, lens = run_case(w, T=128, seq_override=[5, 128], max_len=0)
     assert err <= ATOL
     assert np.all(out == 0.0)
+
+
+@pytest.mark.parametrize("vscale", [300.0, 3000.0])
+def test_decode_large_value_norms(vscale):
+    """Value norms of about 1e3 to 1e5 (values scaled by vscale on alternate
+    runs of 37 tokens, so that one scan mixes norms near 20 with large ones)
+    behind peaked scores (outlier channels): the value-side weight p gamma_v
+    must stay inside the fp16 range of the MFMA operands.  Outputs scale with
+    the values, so the 2e-3 bar is applied at unit value scale."""
+    w = workload("gqa32k")
+    inp = make_inputs(w, scale_T=1500)
+    T = inp["V"].shape[2]
+    s = torch.where((torch.arange(T) // 37) % 2 == 0, vscale, 1.0).view(1, 1, T, 1)
+    V = (inp["V"].float() * s).to(torch.bfloat16)
+    kc, hk = codecs(w.bits)
+    vc, hv = codecs(w.bits)
+    kcache = encode_gpu(inp["K"], kc)
+    vcache = encode_gpu(V, vc)
+    out = octo.octo_attend_decode(kc, vc, kcache, vcache, inp["q"].cuda(), inp["seq_lens"].cuda())
+    torch.cuda.synchronize()
+    hv_cache = vcache.to_host()
+    say(f"  value norms up to {float(hv_cache['gamma'].max()):.3e}")
+    ref = oatt.decode_attention(inp["q"].double().numpy(), kcache.to_host(), hv_cache, hk, hv,
+                                inp["seq_lens"].numpy())
+    err = np.abs(out.cpu().double().numpy() - ref).max()
+    say(f"  vscale {vscale} max-abs err {err:.3e} (bar {ATOL * vscale:.3e})")
+    assert np.isfinite(out.cpu().numpy()).all()
+    assert err <= ATOL * vscale
