@@ -26,12 +26,24 @@ Readings where the paper is silent:
   * full-grid tie rule: lowest (i_xi, i_eta) in row-major order.
   * sign(0) = +1 for sigma; the zero pad coordinate is not part of r.
 
-Every decision also yields a margin: the distance (in the units of the quantity
-decided on) to the nearest point where the decision would change.  Per triplet
-the margin is the minimum over: |p_z| (hemisphere), |p_x| and |p_y| on the
-lower hemisphere (fold signs), the seed distances to their cell boundaries, the
-gap between the best and the best different candidate s, and the distance of
-s* (or rho) to the C_rho cell boundaries.  For sigma_j it is |(R' r)_j|.
+Every decision also yields a margin: how far the quantity it is taken on
+(its input) can move, in the max-norm, before the decision can change.  The
+parity rule of the GPU tests forgives a disagreement only where the smallest
+margin of a triplet is below 1e-6, i.e. where the input lies within 1e-6 of a
+decision threshold.  The decisions of one triplet and their margins:
+  hemisphere      input p_z, threshold 0                  |p_z|
+  fold signs      inputs p_x, p_y (lower hemisphere only) min(|p_x|, |p_y|)
+  Lloyd seeds     inputs xi, eta; thresholds the C_xi cell edges (midpoints
+                  of adjacent centroids)                  distance to the
+                  nearer edge of the chosen centroid's cell
+  joint argmax    input the vector of candidate scores s; a different code
+                  wins once the best s and a rival's meet: half the gap
+                  between the best s and the best s of another code
+  norm index      input s* (scalar mode: rho); thresholds the C_rho cell edges
+and the triplet's margin is the smallest of these.  For sigma_j the input is
+(R' r)_j, threshold 0, margin |(R' r)_j|.  encode_triplets and qjl_signs take
+optional additive nudges of these inputs, so that tests can move each input
+right up to, and just past, its margin.
 
 Parity: pinned by tests/test_oracle_encode.py (tiny-d exhaustive joint search,
 l_full <= l_3x3 <= l_scalar, equality of argmax-s/nearest-rho with the literal
@@ -40,29 +52,38 @@ rounding ablation, QJL unbiasedness).
 """
 import numpy as np
 
-from .octahedral import oct_decode, oct_encode, sign0
+from .octahedral import oct_decode, sign0
 from .rotation import qjl_rotation_matrix, rotation_matrix
 
 EPS = 1e-20
 ROUND_LOCAL3X3 = "local3x3"
 ROUND_SCALAR = "scalar"
 ROUND_FULL = "full"
+# the 3x3 neighbourhood, seed first, then row-major (dx outer, dy inner)
+ORDER = [(0, 0)] + [(a, b) for a in (-1, 0, 1) for b in (-1, 0, 1) if (a, b) != (0, 0)]
 
 
 def n_triplets(d):
     return -(-d // 3)
 
 
+def cell_margin(x, c, idx):
+    """Distance of x to the nearer edge of the cell of centroid idx of the
+    ascending codebook c (its edges are the midpoints with the adjacent
+    centroids; the outer cells are unbounded)."""
+    c = np.asarray(c, dtype=np.float64)
+    K = c.size
+    lo = np.where(idx > 0, 0.5 * (c[np.maximum(idx - 1, 0)] + c[idx]), -np.inf)
+    hi = np.where(idx < K - 1, 0.5 * (c[idx] + c[np.minimum(idx + 1, K - 1)]), np.inf)
+    return np.minimum(x - lo, hi - x)
+
+
 def nearest_centroid(x, c):
     """Brute-force nearest centroid (ties -> lowest index) and its margin."""
-    dist = np.abs(x[..., None] - c)
+    c = np.asarray(c, dtype=np.float64)
+    dist = np.abs(np.asarray(x, dtype=np.float64)[..., None] - c)
     idx = np.argmin(dist, axis=-1)
-    if c.size == 1:
-        return idx, np.full(x.shape, np.inf)
-    best = np.take_along_axis(dist, idx[..., None], axis=-1)
-    other = np.where(np.arange(c.size) == idx[..., None], np.inf, dist)
-    margin = 0.5 * (other.min(axis=-1) - best[..., 0])
-    return idx, margin
+    return idx, cell_margin(x, c, idx)
 
 
 def magnitude_split(x):
@@ -84,6 +105,92 @@ def candidate_directions(c_xi):
     return oct_decode(xi, eta)
 
 
+def encode_triplets(t, c_xi, c_rho, rounding=ROUND_LOCAL3X3, nudge=None):
+    """The decisions of Sec. 3.2 (Eq. 5) and Sec. 3.5 on triplets t[..., 3].
+
+    nudge: optional additive perturbations of the decision inputs, each
+    broadcastable to the triplet shape: "pz" (hemisphere test), "px", "py"
+    (fold signs), "xi", "eta" (seed searches), "s" (candidate scores, a last
+    axis of 9 in local3x3 mode or K^2 in full mode), "s_star" (the norm
+    search's input on top of the chosen score; scalar mode: the input rho).
+    The margins describe the inputs as nudged; tests read them from an
+    unnudged call.
+
+    Returns the indices (i_xi, i_eta, i_rho), the intermediate decisions
+    (upper, neg_x, neg_y, seed_xi, seed_eta, code), the margins (m_hemi,
+    m_fold, m_seed, m_gap, m_rho) and their minimum `margin`, and u_hat, the
+    rotated-frame reconstruction rho^ n^ [..., 3]."""
+    nudge = nudge or {}
+    g = lambda k: nudge.get(k, 0.0)                         # noqa: E731
+    t = np.asarray(t, dtype=np.float64)
+    c_xi = np.asarray(c_xi, dtype=np.float64)
+    c_rho = np.asarray(c_rho, dtype=np.float64)
+    K = c_xi.size
+    rho = np.sqrt((t * t).sum(axis=-1))
+    # Eq. 5 on the L1-normalized direction, sign(0) = +1
+    l1 = np.abs(t).sum(axis=-1)
+    p = t / np.maximum(l1, EPS)[..., None]
+    px, py, pz = p[..., 0], p[..., 1], p[..., 2]
+    upper = pz + g("pz") >= 0
+    sx, sy = sign0(px + g("px")), sign0(py + g("py"))
+    xi = np.where(upper, px, sx * (1.0 - np.abs(py)))
+    eta = np.where(upper, py, sy * (1.0 - np.abs(px)))
+    m_hemi = np.abs(pz)
+    m_fold = np.where(upper, np.inf, np.minimum(np.abs(px), np.abs(py)))
+
+    seed_xi, m_xi = nearest_centroid(xi + g("xi"), c_xi)
+    seed_eta, m_eta = nearest_centroid(eta + g("eta"), c_xi)
+    m_seed = np.minimum(m_xi, m_eta)
+    dirs = candidate_directions(c_xi)                       # [K, K, 3]
+    inf = np.full(rho.shape, np.inf)
+    if rounding == ROUND_SCALAR:
+        i_xi, i_eta = seed_xi, seed_eta
+        m_gap = inf
+        i_rho, m_rho = nearest_centroid(rho + g("s_star"), c_rho)
+    elif rounding in (ROUND_LOCAL3X3, ROUND_FULL):
+        if rounding == ROUND_LOCAL3X3:
+            cx = np.stack([np.clip(seed_xi + a, 0, K - 1) for a, _ in ORDER], axis=-1)
+            cy = np.stack([np.clip(seed_eta + b, 0, K - 1) for _, b in ORDER], axis=-1)
+        else:
+            m_seed = inf                                    # the full grid uses no seed
+            cx = np.broadcast_to(np.repeat(np.arange(K), K), rho.shape + (K * K,))
+            cy = np.broadcast_to(np.tile(np.arange(K), K), rho.shape + (K * K,))
+        s = (t[..., None, :] * dirs[cx, cy]).sum(axis=-1) + g("s")
+        # the first candidate in order, replaced only on a strictly larger s
+        best = np.zeros(rho.shape, dtype=np.int64)
+        best_s = s[..., 0].copy()
+        for k in range(1, s.shape[-1]):
+            take = s[..., k] > best_s
+            best = np.where(take, k, best)
+            best_s = np.where(take, s[..., k], best_s)
+        i_xi = np.take_along_axis(cx, best[..., None], axis=-1)[..., 0]
+        i_eta = np.take_along_axis(cy, best[..., None], axis=-1)[..., 0]
+        code = cx * K + cy
+        rival = np.where(code == (i_xi * K + i_eta)[..., None], -np.inf, s).max(axis=-1)
+        m_gap = 0.5 * (best_s - rival)
+        i_rho, m_rho = nearest_centroid(best_s + g("s_star"), c_rho)
+    else:
+        raise ValueError(rounding)
+    margin = np.minimum.reduce([m_hemi, m_fold, m_seed, m_gap, m_rho])
+    u_hat = c_rho[i_rho][..., None] * dirs[i_xi, i_eta]
+    return {
+        "i_xi": i_xi.astype(np.int64), "i_eta": i_eta.astype(np.int64),
+        "i_rho": i_rho.astype(np.int64), "upper": upper, "neg_x": sx < 0, "neg_y": sy < 0,
+        "seed_xi": seed_xi, "seed_eta": seed_eta, "code": i_xi * K + i_eta,
+        "m_hemi": m_hemi, "m_fold": m_fold, "m_seed": m_seed, "m_gap": m_gap, "m_rho": m_rho,
+        "margin": margin, "u_hat": u_hat,
+    }
+
+
+def qjl_signs(r, seed, nudge=None):
+    """sigma = sign(R' r) with sign(0) = +1 (Sec. 3.6) for residuals r[N, d]:
+    True where sigma = -1, and the margin |(R' r)_j|.  nudge: an additive
+    perturbation of (R' r)."""
+    r = np.asarray(r, dtype=np.float64)
+    proj = r @ qjl_rotation_matrix(r.shape[-1], seed).T
+    return sign0(proj + (0.0 if nudge is None else nudge)) < 0, np.abs(proj)
+
+
 def encode(x, c_xi, c_rho, seed, rounding=ROUND_LOCAL3X3, qjl=False):
     """Encode vectors x[N, d] (float64 copies of fp32/bf16 data).
 
@@ -95,83 +202,28 @@ def encode(x, c_xi, c_rho, seed, rounding=ROUND_LOCAL3X3, qjl=False):
       gamma_r_f16 [N] (float16), r_norm [N].
     """
     x = np.asarray(x, dtype=np.float64)
-    c_xi = np.asarray(c_xi, dtype=np.float64)
-    c_rho = np.asarray(c_rho, dtype=np.float64)
     n, d = x.shape
-    K = c_xi.size
-
     gamma, u_tilde = magnitude_split(x)
     u = u_tilde @ rotation_matrix(d, seed).T
     t = split_triplets(u)                                   # [N, nt, 3]
-    rho = np.sqrt((t * t).sum(axis=-1))
-    xi, eta, p = oct_encode(t)
-
-    lower = p[..., 2] < 0
-    margin = np.abs(p[..., 2])
-    margin = np.minimum(margin, np.where(lower, np.abs(p[..., 0]), np.inf))
-    margin = np.minimum(margin, np.where(lower, np.abs(p[..., 1]), np.inf))
-
-    seed_xi, m_xi = nearest_centroid(xi, c_xi)
-    seed_eta, m_eta = nearest_centroid(eta, c_xi)
-    dirs = candidate_directions(c_xi)                       # [K, K, 3]
-
-    if rounding == ROUND_SCALAR:
-        i_xi, i_eta = seed_xi, seed_eta
-        margin = np.minimum(margin, np.minimum(m_xi, m_eta))
-        i_rho, m_rho = nearest_centroid(rho, c_rho)
-        margin = np.minimum(margin, m_rho)
-        n_hat = dirs[i_xi, i_eta]
-    elif rounding == ROUND_LOCAL3X3:
-        margin = np.minimum(margin, np.minimum(m_xi, m_eta))
-        order = [(0, 0)] + [(a, b) for a in (-1, 0, 1) for b in (-1, 0, 1) if (a, b) != (0, 0)]
-        cx = np.stack([np.clip(seed_xi + a, 0, K - 1) for a, _ in order], axis=-1)
-        cy = np.stack([np.clip(seed_eta + b, 0, K - 1) for _, b in order], axis=-1)
-        s = (t[..., None, :] * dirs[cx, cy]).sum(axis=-1)   # [N, nt, 9]
-        best = np.zeros(s.shape[:-1], dtype=np.int64)
-        best_s = s[..., 0].copy()
-        for k in range(1, 9):
-            take = s[..., k] > best_s
-            best = np.where(take, k, best)
-            best_s = np.where(take, s[..., k], best_s)
-        i_xi = np.take_along_axis(cx, best[..., None], axis=-1)[..., 0]
-        i_eta = np.take_along_axis(cy, best[..., None], axis=-1)[..., 0]
-        code = cx * K + cy
-        best_code = i_xi * K + i_eta
-        rival = np.where(code == best_code[..., None], -np.inf, s).max(axis=-1)
-        margin = np.minimum(margin, best_s - rival)
-        i_rho, m_rho = nearest_centroid(best_s, c_rho)
-        margin = np.minimum(margin, m_rho)
-        n_hat = dirs[i_xi, i_eta]
-    elif rounding == ROUND_FULL:
-        s = np.einsum("ntc,abc->ntab", t, dirs).reshape(n, -1, K * K)
-        flat = np.argmax(s, axis=-1)                        # first max = lowest code
-        best_s = np.take_along_axis(s, flat[..., None], axis=-1)[..., 0]
-        rival = np.where(np.arange(K * K) == flat[..., None], -np.inf, s).max(axis=-1)
-        margin = np.minimum(margin, best_s - rival)
-        i_xi, i_eta = flat // K, flat % K
-        i_rho, m_rho = nearest_centroid(best_s, c_rho)
-        margin = np.minimum(margin, m_rho)
-        n_hat = dirs[i_xi, i_eta]
-    else:
-        raise ValueError(rounding)
-
-    u_hat = (c_rho[i_rho][..., None] * n_hat).reshape(n, -1)
+    e = encode_triplets(t, c_xi, c_rho, rounding)
+    u_hat = e["u_hat"].reshape(n, -1)
     out = {
         "gamma": gamma,
         "gamma_f32": gamma.astype(np.float32),
-        "i_xi": i_xi.astype(np.int64),
-        "i_eta": i_eta.astype(np.int64),
-        "i_rho": i_rho.astype(np.int64),
-        "margin": margin,
+        "i_xi": e["i_xi"],
+        "i_eta": e["i_eta"],
+        "i_rho": e["i_rho"],
+        "margin": e["margin"],
         "u": u,
         "u_hat": u_hat,
     }
     if qjl:
         r = u - u_hat[:, :d]
-        proj = r @ qjl_rotation_matrix(d, seed).T
+        sigma_neg, sigma_margin = qjl_signs(r, seed)
         r_norm = np.sqrt((r * r).sum(axis=-1))
-        out["sigma_neg"] = sign0(proj) < 0
-        out["sigma_margin"] = np.abs(proj)
+        out["sigma_neg"] = sigma_neg
+        out["sigma_margin"] = sigma_margin
         out["r_norm"] = r_norm
         out["gamma_r_f16"] = r_norm.astype(np.float16)
     return out

@@ -82,7 +82,9 @@ _E4M3 = e4m3_values()
 def to_e4m3(x):
     """Non-negative fp32 values -> E4M3 codes (uint8): nearest value, ties to
     the even code, values beyond the largest finite value saturate to 448.
-    Also returns the decision margin |x - nearest rounding boundary|."""
+    Also returns the decision margin: the distance of x to the nearer edge of
+    the chosen code's rounding cell (the midpoints with the adjacent codes;
+    the cell of 448 has no upper edge)."""
     x = np.asarray(x, dtype=np.float32).astype(np.float64)
     if np.any(x < 0) or np.any(~np.isfinite(x)):
         raise ValueError("scales are finite and non-negative")
@@ -91,7 +93,10 @@ def to_e4m3(x):
     dl, dh = x - _E4M3[lo], _E4M3[hi] - x
     code = np.where((dh < dl) | ((dh == dl) & (hi % 2 == 0)), hi, lo)
     code = np.where(x >= _E4M3[-1], E4M3_MAX_CODE, code)
-    margin = np.where(x >= _E4M3[-1], np.inf, np.abs(x - 0.5 * (_E4M3[lo] + _E4M3[hi])))
+    below = np.where(code > 0, 0.5 * (_E4M3[np.maximum(code - 1, 0)] + _E4M3[code]), -np.inf)
+    above = np.where(code < E4M3_MAX_CODE,
+                     0.5 * (_E4M3[code] + _E4M3[np.minimum(code + 1, E4M3_MAX_CODE)]), np.inf)
+    margin = np.minimum(x - below, above - x)
     return code.astype(np.uint8), margin
 
 
@@ -101,7 +106,9 @@ def from_e4m3(code):
 
 def to_bf16(x):
     """fp32 values -> BF16 bit patterns (uint16), round to nearest even.
-    Also returns the margin |x - the midpoint between the two candidates|."""
+    Also returns the decision margin: the distance of x to the nearer edge of
+    the chosen value's rounding cell (the midpoints with the adjacent BF16
+    values of the same sign; a zero's cell reaches down to zero)."""
     x32 = np.asarray(x, dtype=np.float32)
     bits = x32.view(np.uint32).astype(np.int64)
     low = bits & ~0xFFFF                       # truncation toward zero
@@ -112,7 +119,16 @@ def to_bf16(x):
     dl, dh = np.abs(xv - vlow), np.abs(vhigh - xv)
     pick_high = (dh < dl) | ((dh == dl) & (((low >> 16) & 1) == 1))
     out = np.where(pick_high, high, low) >> 16
-    return out.astype(np.uint16), np.abs(xv - 0.5 * (vlow + vhigh))
+    # magnitudes of the chosen value and of its neighbours toward and away
+    # from zero
+    mag = out & 0x7FFF
+    val = lambda m: np.abs(((m << 16).astype(np.uint32)).view(np.float32).astype(np.float64))  # noqa: E731
+    v = val(mag)
+    toward = np.where(mag > 0, 0.5 * (v + val(np.maximum(mag - 1, 0))), 0.0)
+    away = 0.5 * (v + val(mag + 1))
+    ax = np.abs(xv)
+    margin = np.minimum(ax - toward, away - ax)
+    return out.astype(np.uint16), margin
 
 
 def from_bf16(h):
@@ -146,20 +162,36 @@ def quantize_rotated(u32, bits, g):
     z16, z_margin = to_bf16(mn)
     dh = from_e4m3(s8).astype(np.float32)[..., None]
     zh = from_bf16(z16).astype(np.float32)[..., None]
+    q, q_margin = group_codes(ug, dh, zh, bits)
+    return {
+        "codes": q.reshape(N, d), "scale8": s8, "zero16": z16,
+        "scale_margin": s_margin, "zero_margin": z_margin, "code_margin": q_margin.reshape(N, d),
+        "u32": u32,
+    }
+
+
+def group_codes(u32, dh, zh, bits, nudge=None):
+    """Codes q = clamp(rint((u - z^) / Delta^), 0, 2^b - 1) in fp32 (0 where
+    Delta^ = 0) of fp32 coordinates u32 against fp32 steps dh and zero-points
+    zh (broadcast), and their margins in u units: the distance of u to the
+    nearer edge of its code's cell (the code changes where (u - z^) / Delta^
+    crosses k + 1/2).  nudge: an additive perturbation of u (float64, taken
+    to fp32 with u)."""
+    levels = (1 << bits) - 1
+    u32 = np.asarray(u32, dtype=np.float32)
+    if nudge is not None:
+        u32 = (u32.astype(np.float64) + nudge).astype(np.float32)
+    dh = np.asarray(dh, dtype=np.float32)
+    zh = np.asarray(zh, dtype=np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
-        qf = (ug - zh) / dh                               # fp32
+        qf = (u32 - zh) / dh                              # fp32
     qf = np.where(dh > 0, qf, np.float32(0))
     q = np.clip(np.rint(qf), 0, levels).astype(np.int64)
     q = np.where(dh > 0, q, 0)
     # code decisions turn at k + 1/2, k = 0 .. levels - 1
     bnd = np.arange(levels, dtype=np.float64) + 0.5
     dist = np.abs(qf.astype(np.float64)[..., None] - bnd).min(axis=-1) * dh.astype(np.float64)
-    q_margin = np.where(dh > 0, dist, np.inf)
-    return {
-        "codes": q.reshape(N, d), "scale8": s8, "zero16": z16,
-        "scale_margin": s_margin, "zero_margin": z_margin, "code_margin": q_margin.reshape(N, d),
-        "u32": u32,
-    }
+    return q, np.where(dh > 0, dist, np.inf)
 
 
 def dequantize_rotated(codes, scale8, zero16, g):
