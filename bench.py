@@ -1,6 +1,7 @@
 """Benchmark of the OCTOPUS hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa32k]
+                    [--extras batch16,long128k,chunk,step32k | none]
 
 A step is one pass of the whole hot path over one batch of synthetic input
 with everything already resident in HBM:
@@ -8,10 +9,14 @@ with everything already resident in HBM:
                     then single-query decode attention over it;
   chunk workload    encode the current chunk (K and V) into the cache slots
                     after the cached window, then chunk attention of its
-                    queries over the window and the chunk.
+                    queries over the window and the chunk;
+  step workload     one decode step with a residual window (append, attend,
+                    evict).
 The timed region brackets exactly K steps with torch.cuda.synchronize();
 HIP events recorded on the stream the kernels run on give the per-call
-durations.  One JSON line is printed.
+durations.  One JSON line is printed: the headline workload (--workload) at
+the top level and every workload of --extras under "configs", each with the
+same keys.
 
 value      cached KV-tokens/s of the attention call: tokens attended per
            step (sum of the sequence lengths; for the chunk workload the
@@ -20,9 +25,16 @@ roofline   for the attention call: algorithmic bytes (packed cache of the
            attended tokens, K and V) per launch over the mean duration,
            against 8 TB/s (decode), or algorithmic MFMA flops against the
            fp16 dense peak (chunk).
-cpu_baseline  the float64 oracle on a bounded sample (one KV-head plane of
-           the decode workload; a few query rows for the chunk workload),
-           on one host thread, scaled to the same unit.
+cpu_baseline  the float64 oracle on bounded samples in the same units:
+           attention (one KV-head plane at a time of the decode workloads; a
+           few query rows of the chunk workload) and the encoder (token
+           positions/s), each with every available core and with one thread
+           (single_core, encode_single_core).
+parity     by-product of the oracle legs: the encoder's indices on the
+           sampled tokens against the GPU-written records (triplets,
+           mismatches, forgiven near-threshold ones, bad ones) and the
+           largest difference between the oracle's and the GPU's attention
+           outputs on the sampled rows.
 cold       (decode) the same call over cache replicas spanning 600 MB, taken in
            turn, so each call reads from HBM rather than the 256 MB
            Infinity Cache; achieved GB/s and fraction of 8 TB/s beside it.
@@ -57,6 +69,9 @@ METRIC = "decode-attn cached KV-tokens/s + % of HBM peak on packed cache; encode
 HBM_PEAK_GBS = 8000.0
 COPY_MIB = 512                     # size of the counter calibration copy
 MFMA_FP16_PEAK_TFLOPS = 2500.0
+# decode: both contractions on MFMA with fp16 operands split into hi + lo
+# pairs (about 2^-20 relative per product), fp32 accumulation and softmax
+DECODE_DTYPE = "f16-hi/lo-mfma/f32-acc"
 
 
 def log(*a):
@@ -278,7 +293,7 @@ def run_decode(w, steps, warmup):
         "value": tokens / (att_ms * 1e-3),
         "unit": "cached KV-tokens/s",
         "ms_per_step": wall / steps * 1e3,
-        "dtype": "f32",
+        "dtype": DECODE_DTYPE,
         "attention_us": att_ms * 1e3,
         "attention_us_percentiles": t_att.percentiles_us(),
         "cold": {"attention_us": cold_us, "percentiles_us": cold_pct, "replicas": n_rep,
@@ -287,6 +302,7 @@ def run_decode(w, steps, warmup):
         "encode_us": enc_ms * 1e3,
         "encode_tokens_per_s": enc_tokens / (enc_ms * 1e-3),
         "token_kv_heads_per_s": tokens * w.Hkv / (att_ms * 1e-3),
+        "_out": out,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.key),
                      "kernel": "octo_attend_decode (split-K scan + merge)",
@@ -361,12 +377,13 @@ def run_step(w, steps, warmup):
         "value": tokens / (att_ms * 1e-3),
         "unit": "cached KV-tokens/s",
         "ms_per_step": wall / steps * 1e3,
-        "dtype": "f32",
+        "dtype": DECODE_DTYPE,
         "attention_us": att_ms * 1e3,
         "attention_us_percentiles": t_att.percentiles_us(),
         "encode_us": None,
         "encode_tokens_per_s": None,
         "token_kv_heads_per_s": tokens * w.Hkv / (att_ms * 1e-3),
+        "_out": out,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.key),
                      "kernel": "octo_decode_step (split-K scan with the window workgroup + merge)",
@@ -425,6 +442,7 @@ def run_chunk(w, steps, warmup):
         "attention_us_percentiles": t_att.percentiles_us(),
         "encode_us": enc_ms * 1e3,
         "encode_tokens_per_s": w.B * Tq / (enc_ms * 1e-3),
+        "_out": out,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_FP16_PEAK_TFLOPS,
                      "traffic": recorded_traffic(w.key),
@@ -434,7 +452,8 @@ def run_chunk(w, steps, warmup):
     return res, (inp, kc, vc, kcache, vcache)
 
 
-CPU_SECONDS = 10.0                 # oracle work per baseline (bounded sample)
+CPU_SECONDS = 8.0                  # oracle attention work per leg (bounded sample)
+ENC_SECONDS = 4.0                  # oracle encoder work per leg
 
 
 def _host_plane(h, b, g):
@@ -450,13 +469,139 @@ def _host_plane(h, b, g):
     return out
 
 
-def cpu_baseline(w, state):
-    """The oracle on one host thread over a bounded sample (about CPU_SECONDS
-    of work), in the same unit as the GPU value."""
+def _attention_leg(w, state, out_gpu, hk, hv, hkc, hvc, seconds):
+    """The oracle's attention on a bounded sample of the workload, timed,
+    and the largest difference to the GPU outputs of the same rows."""
     import numpy as np
+    from oracle import attention as oatt
+    inp = state[0]
+    G = w.Hq // w.Hkv
+    lens = inp["seq_lens"].numpy()
+    done, dt, units, err = 0.0, 0.0, 0, 0.0
+    if w.window:
+        # one oracle decode step per (batch, KV head) plane, in order and
+        # repeated, from the state the GPU steps left; a plane-step counts
+        # (P + n + 1) / Hkv of a step's cached KV-tokens
+        from oracle import step as ostep
+        _, _, _, _, _, kr, vr, plens, wlens, new = state
+        kr_h, vr_h = kr.double().cpu().numpy(), vr.double().cpu().numpy()
+        P, n = plens.cpu().numpy(), wlens.cpu().numpy()
+        planes = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+        while dt < seconds:
+            b, g = planes[units % len(planes)]
+            st = {"k": _host_plane(hkc, b, g), "v": _host_plane(hvc, b, g),
+                  "k_ring": kr_h[b:b + 1, g:g + 1].copy(), "v_ring": vr_h[b:b + 1, g:g + 1].copy(),
+                  "P": P[b:b + 1].astype(np.int64), "n": n[b:b + 1].astype(np.int64),
+                  "W": w.window}
+            k1, v1 = new[units % len(new)]
+            qn = inp["q"][b:b + 1, g * G:(g + 1) * G].double().numpy()
+            t0 = time.perf_counter()
+            ostep.decode_step(st, qn, k1[b:b + 1, g:g + 1].double().cpu().numpy(),
+                              v1[b:b + 1, g:g + 1].double().cpu().numpy(), hk, hv)
+            dt += time.perf_counter() - t0
+            done += (int(P[b]) + int(n[b]) + 1) / w.Hkv
+            units += 1
+        sample = (f"{units} oracle decode steps, one (batch, KV head) plane each ({len(planes)} "
+                  f"in all, in order and repeated), {G} query heads over the packed prefix and "
+                  f"the window; each counts (P + n + 1) / {w.Hkv} cached KV-tokens")
+        return done / dt, dt, sample, None
+    if not w.chunk_q:
+        # (batch, KV head) planes in order, repeated if the workload is
+        # smaller than the budget; a plane of sequence b is len_b / Hkv of
+        # the step's cached KV-tokens
+        planes = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+        ref_o = out_gpu.double().cpu().numpy()
+        while dt < seconds:
+            b, g = planes[units % len(planes)]
+            qn = inp["q"][b:b + 1, g * G:(g + 1) * G].double().numpy()
+            t0 = time.perf_counter()
+            o = oatt.decode_attention(qn, _host_plane(hkc, b, g), _host_plane(hvc, b, g), hk, hv,
+                                      lens[b:b + 1])
+            dt += time.perf_counter() - t0
+            err = max(err, float(np.abs(o[0] - ref_o[b, g * G:(g + 1) * G]).max()))
+            done += lens[b] / w.Hkv
+            units += 1
+        sample = (f"oracle decode attention over {units} (batch, KV head) planes of the workload "
+                  f"({len(planes)} in all, taken in order and repeated), "
+                  f"{G} query heads each; each plane counts len_b / {w.Hkv} cached KV-tokens")
+        return done / dt, dt, sample, err
+    # 8-row groups of head 0's queries; one row attends the whole window and
+    # chunk, 1 / (Hq Tq) of the step
+    pk, pv = _host_plane(hkc, 0, 0), _host_plane(hvc, 0, 0)
+    keys = w.T + w.chunk_q
+    ref_o = out_gpu[0, 0].double().cpu().numpy()
+    while dt < seconds and units * 8 < w.chunk_q:
+        rows = np.arange(units * 8, min(units * 8 + 8, w.chunk_q))
+        t0 = time.perf_counter()
+        o = oatt.chunk_attention(inp["q"][:, :1].double().numpy(), pk, pv, hk, hv, w.T,
+                                 inp["K_cur"][:, :1].double().numpy(),
+                                 inp["V_cur"][:, :1].double().numpy(), q_rows=rows,
+                                 correction=w.jensen)
+        dt += time.perf_counter() - t0
+        err = max(err, float(np.abs(o[0, 0][rows] - ref_o[rows]).max()))
+        done += len(rows)
+        units += 1
+    sample = (f"oracle chunk attention of head 0, {int(done)} query rows over {keys} keys, "
+              f"scaled to {w.Hq} heads x {w.chunk_q} rows")
+    return keys * done / (dt * w.Hq * w.chunk_q), dt, sample, err
+
+
+def _encode_leg(w, state, hk, hv, hkc, hvc, seconds):
+    """The oracle encoder on a bounded sample (K and V vectors of plane (0, 0),
+    64 tokens at a time, from the first token of the step's encode), timed,
+    and its indices compared with the GPU-written records of the same tokens:
+    (token positions / s, seconds, sample, counts)."""
+    import numpy as np
+    from oracle import cache as ocache
+    from oracle import encode as oenc
+    from oracle import group as ogroup
+    inp = state[0]
+    off = w.T if w.chunk_q else 0
+    src = {"K": inp["K_cur"] if w.chunk_q else inp["K"], "V": inp["V_cur"] if w.chunk_q else inp["V"]}
+    T = src["K"].shape[2]
+    st = dict(vectors=0, triplets=0, mismatch=0, forgiven=0, bad=0, codes=0)
+    dt, t = 0.0, 0
+    while dt < seconds and t < T:
+        ts = np.arange(t, min(t + 64, T))
+        for name, hc, host in (("K", hk, hkc), ("V", hv, hvc)):
+            xv = src[name][0, 0].double().numpy()[ts]
+            t0 = time.perf_counter()
+            if hc.get("group"):
+                e = ogroup.encode(xv, hc["bits"], hc["group"], hc["seed"])
+            else:
+                e = oenc.encode(xv, hc["c_xi"], hc["c_rho"], hc["seed"], rounding=hc["rounding"],
+                                qjl=hc["qjl"])
+            dt += time.perf_counter() - t0
+            rec = ocache.read_tokens(host, hc, 0, 0, off + ts[0], len(ts))
+            st["vectors"] += len(ts)
+            if hc.get("group"):
+                cm = rec["codes"] != e["codes"]
+                st["codes"] += cm.size
+                st["mismatch"] += int(cm.sum())
+            else:
+                mism = ((rec["i_xi"] != e["i_xi"]) | (rec["i_eta"] != e["i_eta"]) |
+                        (rec["i_rho"] != e["i_rho"]))
+                bad = mism & (e["margin"] >= 1e-6)
+                st["triplets"] += mism.size
+                st["mismatch"] += int(mism.sum())
+                st["bad"] += int(bad.sum())
+                st["forgiven"] += int((mism & ~bad).sum())
+        t += len(ts)
+    # a token position of the step encodes 2 Hkv B vectors
+    rate = st["vectors"] / 2 / dt / (w.Hkv * w.B)
+    sample = (f"oracle encode of tokens 0..{t - 1} of plane (0, 0), K and V, scaled to "
+              f"{w.B} x {w.Hkv} planes")
+    return rate, dt, sample, st
+
+
+def cpu_baseline(w, state, out_gpu, seconds=CPU_SECONDS, enc_seconds=ENC_SECONDS):
+    """The oracle on the host over bounded samples, in the units of the GPU
+    figures: attention (cached KV-tokens/s) and encode (token positions/s),
+    each with BLAS and torch limited to one thread and with every available
+    core.  Its by-products are the parity record of the sample: the index
+    comparison of the encoded tokens and the largest output difference."""
     from threadpoolctl import threadpool_limits
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from oracle import attention as oatt
     from oracle_codecs import codec as oracle_codec
     from oracle_codecs import group_codec as oracle_group_codec
     inp, kc, vc, kcache, vcache = state[:5]
@@ -464,77 +609,33 @@ def cpu_baseline(w, state):
           else oracle_codec(bits=w.bits, qjl=w.qjl))
     hv = oracle_group_codec(bits=w.bits, group=w.v_group) if w.v_group else oracle_codec(bits=w.bits)
     hkc, hvc = kcache.to_host(), vcache.to_host()
-    G = w.Hq // w.Hkv
-    lens = inp["seq_lens"].numpy()
-    with threadpool_limits(limits=1):
-        torch.set_num_threads(1)
-        done, dt, units = 0.0, 0.0, 0
-        if w.window:
-            # one oracle decode step per (batch, KV head) plane, in order and
-            # repeated, from the state the GPU steps left; a plane-step counts
-            # (P + n + 1) / Hkv of a step's cached KV-tokens
-            from oracle import step as ostep
-            _, _, _, _, _, kr, vr, plens, wlens, new = state
-            kr_h, vr_h = kr.double().cpu().numpy(), vr.double().cpu().numpy()
-            P, n = plens.cpu().numpy(), wlens.cpu().numpy()
-            planes = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
-            while dt < CPU_SECONDS:
-                b, g = planes[units % len(planes)]
-                st = {"k": _host_plane(hkc, b, g), "v": _host_plane(hvc, b, g),
-                      "k_ring": kr_h[b:b + 1, g:g + 1].copy(), "v_ring": vr_h[b:b + 1, g:g + 1].copy(),
-                      "P": P[b:b + 1].astype(np.int64), "n": n[b:b + 1].astype(np.int64),
-                      "W": w.window}
-                k1, v1 = new[units % len(new)]
-                qn = inp["q"][b:b + 1, g * G:(g + 1) * G].double().numpy()
-                t0 = time.perf_counter()
-                ostep.decode_step(st, qn, k1[b:b + 1, g:g + 1].double().cpu().numpy(),
-                                  v1[b:b + 1, g:g + 1].double().cpu().numpy(), hk, hv)
-                dt += time.perf_counter() - t0
-                done += (int(P[b]) + int(n[b]) + 1) / w.Hkv
-                units += 1
-            value = done / dt
-            sample = (f"{units} oracle decode steps, one (batch, KV head) plane each ({len(planes)} "
-                      f"in all, in order and repeated), {G} query heads over the packed prefix and "
-                      f"the window; each counts (P + n + 1) / {w.Hkv} cached KV-tokens")
-        elif not w.chunk_q:
-            # (batch, KV head) planes in order, repeated if the workload is
-            # smaller than the budget; a plane of sequence b is len_b / Hkv of
-            # the step's cached KV-tokens
-            planes = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
-            while dt < CPU_SECONDS:
-                b, g = planes[units % len(planes)]
-                qn = inp["q"][b:b + 1, g * G:(g + 1) * G].double().numpy()
-                t0 = time.perf_counter()
-                oatt.decode_attention(qn, _host_plane(hkc, b, g), _host_plane(hvc, b, g), hk, hv,
-                                      lens[b:b + 1])
-                dt += time.perf_counter() - t0
-                done += lens[b] / w.Hkv
-                units += 1
-            value = done / dt
-            sample = (f"oracle decode attention over {units} (batch, KV head) planes of the workload "
-                      f"({len(planes)} in all, taken in order and repeated), "
-                      f"{G} query heads each; each plane counts len_b / {w.Hkv} cached KV-tokens")
-        else:
-            # 8-row groups of head 0's queries; one row attends the whole window
-            # and chunk, 1 / (Hq Tq) of the step
-            pk, pv = _host_plane(hkc, 0, 0), _host_plane(hvc, 0, 0)
-            keys = w.T + w.chunk_q
-            while dt < CPU_SECONDS and units * 8 < w.chunk_q:
-                rows = np.arange(units * 8, min(units * 8 + 8, w.chunk_q))
-                t0 = time.perf_counter()
-                oatt.chunk_attention(inp["q"][:, :1].double().numpy(), pk, pv, hk, hv, w.T,
-                                     inp["K_cur"][:, :1].double().numpy(),
-                                     inp["V_cur"][:, :1].double().numpy(), q_rows=rows,
-                                     correction=w.jensen)
-                dt += time.perf_counter() - t0
-                done += len(rows)
-                units += 1
-            value = keys * done / (dt * w.Hq * w.chunk_q)
-            sample = (f"oracle chunk attention of head 0, {int(done)} query rows over {keys} keys, "
-                      f"scaled to {w.Hq} heads x {w.chunk_q} rows")
-    return {"value": value, "unit": "cached KV-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": sample, "seconds": dt, "cpu_model": _cpu_model(),
-            "host_cores_available": len(os.sched_getaffinity(0)), "blas_threads": 1}
+    cores = len(os.sched_getaffinity(0))
+    legs, parity = {}, {}
+    default_threads = torch.get_num_threads()
+    for label, n in (("single_core", 1), ("all_cores", cores)):
+        with threadpool_limits(limits=n):
+            torch.set_num_threads(n)
+            v, dt, sample, err = _attention_leg(w, state, out_gpu, hk, hv, hkc, hvc, seconds)
+            legs[label] = {"value": v, "unit": "cached KV-tokens/s", "cores": n, "kind": "oracle",
+                           "sample": sample, "seconds": dt}
+            if err is not None:
+                parity["attention_max_abs_err"] = max(err, parity.get("attention_max_abs_err", 0.0))
+            if not w.window:
+                ev, edt, esample, est = _encode_leg(w, state, hk, hv, hkc, hvc, enc_seconds)
+                legs["encode_" + label] = {"value": ev, "unit": "token positions/s", "cores": n,
+                                           "kind": "oracle", "sample": esample, "seconds": edt}
+                parity["encode"] = est
+    torch.set_num_threads(default_threads)
+    main = dict(legs["all_cores"])
+    main.update({"single_core": legs["single_core"], "encode": legs.get("encode_all_cores"),
+                 "encode_single_core": legs.get("encode_single_core"),
+                 "cpu_model": _cpu_model(), "host_cores_available": cores})
+    if parity:
+        parity["rule"] = ("indices bit-exact except where the oracle's decision margin is below "
+                          "1e-6 (forgiven); attention max-abs 2e-3 against the float64 oracle on "
+                          "the GPU-written cache")
+        parity["attention_atol"] = 2e-3
+    return main, (parity or None)
 
 
 def _cpu_model():
@@ -548,12 +649,63 @@ def _cpu_model():
     return None
 
 
+EXTRAS = ("batch16", "long128k", "chunk", "step32k")
+
+
+def _config(key, w):
+    return {"workload": f"{key}: {w.name}", "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+            "head_dim": w.d, "context": w.T, "bits": w.bits, "qjl": w.qjl,
+            "chunk_queries": w.chunk_q, "window": w.window, "value_group": w.v_group,
+            "key_group": w.k_group, "jensen_correction": w.jensen}
+
+
+def run_one(key, steps, warmup, cpu, cpu_seconds, enc_seconds):
+    """Times one workload and runs its oracle legs; returns the JSON entry."""
+    w = WORKLOADS[key]
+    if w.window:
+        # the decode-step workload runs at most 64 steps, warmup included
+        warmup = min(warmup, 16)
+        steps = min(steps, 64 - warmup)
+    log(f"bench {key}: {w.name}; warmup {warmup}, steps {steps}")
+    if w.chunk_q:
+        res, state = run_chunk(w, steps, warmup)
+    elif w.window:
+        res, state = run_step(w, steps, warmup)
+    else:
+        res, state = run_decode(w, steps, warmup)
+    out_gpu = res.pop("_out")
+    enc = "" if res["encode_us"] is None else f", encode {res['encode_us']:.1f} us"
+    log(f"  attention {res['attention_us']:.1f} us{enc}, roofline frac {res['roofline']['frac']:.3f}")
+    base, parity = None, None
+    if cpu:
+        base, parity = cpu_baseline(w, state, out_gpu, cpu_seconds, enc_seconds)
+        log(f"  cpu baseline {base['value']:.3g} {base['unit']} ({base['cores']} cores), "
+            f"parity {json.dumps(parity)}")
+    entry = {"value": res["value"], "unit": res["unit"], "steps": steps, "warmup": warmup,
+             "ms_per_step": res["ms_per_step"], "dtype": res["dtype"],
+             "config": _config(key, w), "roofline": res["roofline"], "cpu_baseline": base,
+             "parity": parity, "attention_us": res["attention_us"],
+             "attention_us_percentiles": res.get("attention_us_percentiles"),
+             "encode_us": res["encode_us"], "encode_tokens_per_s": res["encode_tokens_per_s"]}
+    for k in ("token_kv_heads_per_s", "cold"):
+        if k in res:
+            entry[k] = res[k]
+    del state, out_gpu
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return entry
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gqa32k", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="gqa32k", choices=sorted(WORKLOADS),
+                    help="the headline workload (value, roofline, cpu_baseline)")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="comma-separated workloads reported beside it under 'configs' "
+                         "('none' for the headline alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", nargs=5,
@@ -569,41 +721,30 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               "(the workloads fit one MI355X and no multi-GPU path is built)", file=sys.stderr)
         sys.exit(2)
+    extras = [] if a.extras in ("", "none") else [e for e in a.extras.split(",") if e != a.workload]
+    for e in extras:
+        if e not in WORKLOADS:
+            raise SystemExit(f"unknown workload {e}")
     octo.lib()
-    w = WORKLOADS[a.workload]
-    log(f"bench {a.workload}: {w.name}; warmup {a.warmup}, steps {a.steps}")
-    if w.chunk_q:
-        res, state = run_chunk(w, a.steps, a.warmup)
-    elif w.window:
-        res, state = run_step(w, a.steps, a.warmup)
-    else:
-        res, state = run_decode(w, a.steps, a.warmup)
-    enc = "" if res["encode_us"] is None else f", encode {res['encode_us']:.1f} us"
-    log(f"attention {res['attention_us']:.1f} us{enc}")
-    cpu = None
-    if not a.no_cpu_baseline:
-        cpu = cpu_baseline(w, state)
-        log(f"cpu baseline {cpu['value']:.3g} {cpu['unit']} in {cpu['seconds']:.1f} s")
+    cpu = not a.no_cpu_baseline
+    head = run_one(a.workload, a.steps, a.warmup, cpu, CPU_SECONDS, ENC_SECONDS)
     line = {
-        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": res["ms_per_step"],
+        "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": res["dtype"], "data": "synthetic (seeded Gaussian, see workloads.py)",
-        "config": {"workload": f"{a.workload}: {w.name}", "batch": w.B, "q_heads": w.Hq,
-                   "kv_heads": w.Hkv, "head_dim": w.d, "context": w.T, "bits": w.bits,
-                   "qjl": w.qjl, "chunk_queries": w.chunk_q, "window": w.window,
-                   "value_group": w.v_group, "key_group": w.k_group,
-                   "jensen_correction": w.jensen},
-        "roofline": res["roofline"],
-        "cpu_baseline": cpu,
-        "attention_us": res["attention_us"], "encode_us": res["encode_us"],
-        "attention_us_percentiles": res.get("attention_us_percentiles"),
-        "encode_tokens_per_s": res["encode_tokens_per_s"],
+        "dtype": head["dtype"], "data": "synthetic (seeded Gaussian, see workloads.py)",
+        "config": head["config"], "roofline": head["roofline"], "cpu_baseline": head["cpu_baseline"],
+        "parity": head["parity"], "attention_us": head["attention_us"],
+        "encode_us": head["encode_us"], "attention_us_percentiles": head["attention_us_percentiles"],
+        "encode_tokens_per_s": head["encode_tokens_per_s"],
     }
-    if "token_kv_heads_per_s" in res:
-        line["token_kv_heads_per_s"] = res["token_kv_heads_per_s"]
-    if "cold" in res:
-        line["cold"] = res["cold"]
+    for k in ("token_kv_heads_per_s", "cold"):
+        if k in head:
+            line[k] = head[k]
+    # the other configurations, each with its own roofline, oracle legs and
+    # parity record (shorter oracle legs)
+    line["configs"] = {e: run_one(e, a.steps, a.warmup, cpu, CPU_SECONDS / 2, ENC_SECONDS / 2)
+                       for e in extras}
     print(json.dumps(line), flush=True)
 
 

@@ -39,6 +39,33 @@ from quantized_decode_attention_octo_amd.workloads import WORKLOADS, make_inputs
 
 MARGIN = 1e-6
 ATOL = 2e-3
+# Every index comparison adds its counts here (case name -> counts): the
+# GPU run's record of the mismatches the near-threshold rule forgave.
+COUNTS_PATH = os.environ.get("OCTO_PARITY_COUNTS",
+                             os.path.join(ROOT, "gpurun_out", "parity_counts.json"))
+
+
+def record_counts(what, st):
+    """Adds the counts of one comparison to the run's record (best effort:
+    a read-only tree skips it)."""
+    import json
+    try:
+        os.makedirs(os.path.dirname(COUNTS_PATH), exist_ok=True)
+        try:
+            with open(COUNTS_PATH) as f:
+                rec = json.load(f)
+        except (OSError, ValueError):
+            rec = {"rule": "an index may differ from the oracle only where the oracle's smallest "
+                           "decision margin is below 1e-6 (forgiven); bad = other mismatches",
+                   "cases": {}}
+        # a case name seen again in the run (a loop over steps) adds up
+        old = rec["cases"].get(what, {})
+        rec["cases"][what] = {k: (max(float(v), old.get(k, 0.0)) if isinstance(v, float)
+                                  else int(v) + old.get(k, 0)) for k, v in st.items()}
+        with open(COUNTS_PATH, "w") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+    except OSError:
+        pass
 
 
 def say(*a):
@@ -108,8 +135,11 @@ def compare_group_encode(host_cache, hcodec, x, token_offset=0, planes=None, tok
 
 
 def assert_group_encode_ok(st, what):
+    st = dict(st, forgiven=st["mismatch"] - st["bad"],
+              meta_forgiven=st["meta_mismatch"] - st["meta_bad"])
     say(f"[{what}] codes {st['codes']} mismatches {st['mismatch']} (bad {st['bad']}); groups"
         f" {st['groups']} scale/zero mismatches {st['meta_mismatch']} (bad {st['meta_bad']})")
+    record_counts("group " + what, st)
     assert st["bad"] == 0 and st["meta_bad"] == 0
 
 
@@ -165,6 +195,8 @@ def compare_encode(host_cache, hcodec, x, token_offset=0, planes=None, tokens=No
 
 
 def assert_encode_ok(st, what):
+    st = dict(st, forgiven=st["mismatch"] - st["bad"], sig_forgiven=st["sig_mismatch"] - st["sig_bad"])
+    record_counts(what, st)
     say(f"[{what}] triplets {st['triplets']} mismatches {st['mismatch']} (all with margin < 1e-6"
         f" unless bad={st['bad']}); gamma rel err {st['gamma_err']:.2e}; sigma mismatches"
         f" {st['sig_mismatch']} bad {st['sig_bad']}; gamma_r bad {st['gr_bad']}")

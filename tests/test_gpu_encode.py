@@ -41,16 +41,18 @@ def test_encode_full_size_sampled(key):
     w = workload(key)
     say(f"encode full {key}")
     inp = make_inputs(w)
-    gc, hc = codecs(w.bits, qjl=w.qjl)
-    x = inp["K"]
-    cache = encode_gpu(x, gc, capacity=w.capacity)
-    B, H, T, _ = x.shape
-    rng = np.random.default_rng(1)
-    tokens = np.sort(rng.choice(T, size=min(T, 384), replace=False))
-    tokens[-1] = T - 1
-    planes = [(0, 0), (B - 1, H - 1)]
-    assert_encode_ok(compare_encode(cache.to_host(), hc, x, planes=planes, tokens=tokens),
-                     f"{key} full")
+    for name, qjl in (("K", w.qjl), ("V", False)):
+        gc, hc = codecs(w.bits, qjl=qjl)
+        x = inp[name]
+        cache = encode_gpu(x, gc, capacity=w.capacity)
+        B, H, T, _ = x.shape
+        rng = np.random.default_rng(1)
+        tokens = np.sort(rng.choice(T, size=min(T, 384), replace=False))
+        tokens[-1] = T - 1
+        planes = [(0, 0), (B - 1, H - 1)]
+        assert_encode_ok(compare_encode(cache.to_host(), hc, x, planes=planes, tokens=tokens),
+                         f"{key} full {name}")
+        del cache
 
 
 def test_encode_append_unaligned_offsets():

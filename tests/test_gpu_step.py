@@ -95,12 +95,12 @@ def run_steps(bits, qjl, W, G, Hkv, P0, n0, steps, cap, seed=0, q_f32=False, che
             xk[b, :, 0] = torch.tensor(st["k_ring"][b, :, P % W]) if W > 1 else kn[b].double()
             xv[b, :, 0] = torch.tensor(st["v_ring"][b, :, P % W]) if W > 1 else vn[b].double()
             planes = [(b, h) for h in range(Hkv)]
-            assert_encode_ok(compare_encode(hk_now, hk, xk, P, planes=planes), f"step {s} K b={b}")
+            assert_encode_ok(compare_encode(hk_now, hk, xk, P, planes=planes), f"step K b={b}")
             if v_group:
                 assert_group_encode_ok(compare_group_encode(hv_now, hv, xv, P, planes=planes),
-                                       f"step {s} V b={b}")
+                                       f"step V b={b}")
             else:
-                assert_encode_ok(compare_encode(hv_now, hv, xv, P, planes=planes), f"step {s} V b={b}")
+                assert_encode_ok(compare_encode(hv_now, hv, xv, P, planes=planes), f"step V b={b}")
         # continue from the GPU-written cache
         st["k"], st["v"] = hk_now, hv_now
     say(f"[step bits={bits} qjl={qjl} W={W} G={G}] {steps} steps, max-abs err {worst:.2e}")
