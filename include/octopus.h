@@ -217,6 +217,28 @@ octo_status octo_attend_decode(const octo_codec_desc* k_codec, const octo_codec_
                                float softmax_scale, float* out,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* octo_attend_decode_noalloc -- octo_attend_decode without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * kernels and results as octo_attend_decode, bit for bit; the per-split
+ * partials live in a static device array of OCTO_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that the library keeps on each device it runs on until the
+ * process ends.  The call allocates and frees nothing.  Shapes whose
+ * partials need more (octo_decode_workspace_bytes > 16 MiB) return
+ * OCTO_ERR_CAPACITY before any launch.  Every call on one device uses that
+ * device's one array, which keeps the last call's partials: calls that
+ * overlap in time on one device (different streams, or a capture replayed
+ * beside another call) race and must be ordered by the caller.  Nothing in
+ * the array has to start at any particular value.                         */
+#define OCTO_NOALLOC_SCRATCH_BYTES (16u << 20)
+octo_status octo_attend_decode_noalloc(const octo_codec_desc* k_codec,
+                                       const octo_codec_desc* v_codec,
+                                       const octo_cache_view* k_cache,
+                                       const octo_cache_view* v_cache, const void* q,
+                                       octo_dtype q_dtype, int32_t num_q_heads,
+                                       const int32_t* seq_lens, int32_t max_seq_len,
+                                       float softmax_scale, float* out, hipStream_t stream);
+
 /* Workspace bytes needed by octo_decode_step for these shapes.              */
 octo_status octo_decode_step_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,
                                              int32_t num_q_heads, int32_t kv_heads,

@@ -98,9 +98,13 @@ def lib():
                                        ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
         L.octo_decode_tokens.argtypes = [ctypes.POINTER(CodecDesc), ctypes.POINTER(CacheView),
                                          _I, _I, _P, _P]
+        L.octo_attend_decode_noalloc.argtypes = [ctypes.POINTER(CodecDesc), ctypes.POINTER(CodecDesc),
+                                                 ctypes.POINTER(CacheView), ctypes.POINTER(CacheView),
+                                                 _P, ctypes.c_int, _I, _P, _I, ctypes.c_float, _P, _P]
         for f in ("octo_record_sizes", "octo_encode", "octo_decode_workspace_bytes",
                   "octo_attend_decode", "octo_chunk_workspace_bytes", "octo_attend_chunk",
-                  "octo_decode_step_workspace_bytes", "octo_decode_step", "octo_decode_tokens"):
+                  "octo_decode_step_workspace_bytes", "octo_decode_step", "octo_decode_tokens",
+                  "octo_attend_decode_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         if L.octo_abi_version() != ABI_VERSION:
             raise RuntimeError("liboctopus.so ABI version mismatch")
@@ -322,6 +326,31 @@ def octo_attend_decode(k_codec, v_codec, k_cache, v_cache, q, seq_lens, max_seq_
                                     float(softmax_scale), _ptr(out),
                                     ctypes.c_void_p(_aligned_ptr(ws)), ws.numel() - 256,
                                     _stream(q.device)))
+    return out
+
+
+def octo_attend_decode_noalloc(k_codec, v_codec, k_cache, v_cache, q, seq_lens, max_seq_len=None,
+                               softmax_scale=0.0, out=None):
+    """octo_attend_decode without a workspace: the library keeps the partials
+    in its static per-device scratch (see include/octopus.h; calls on one
+    device must not overlap).  Returns out[B, H_q, d] fp32."""
+    _same_caches(k_cache, v_cache, k_codec, v_codec)
+    dev, B = k_cache.device, k_cache.B
+    _expect(q, "q", (B, None, k_codec.d), F32_BF16)
+    Hq, d = q.shape[1], q.shape[2]
+    if Hq % k_cache.H:
+        raise ValueError(f"q has {Hq} heads, not a multiple of the {k_cache.H} KV heads")
+    _expect(seq_lens, "seq_lens", (B,), (torch.int32,))
+    max_seq_len = k_cache.capacity if max_seq_len is None else int(max_seq_len)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    _expect(out, "out", (B, Hq, d), (torch.float32,))
+    _on_device(dev, q=q, seq_lens=seq_lens, out=out, k_cache=k_cache.idx, v_cache=v_cache.idx)
+    dt = DTYPE_F32 if q.dtype == torch.float32 else DTYPE_BF16
+    _check(lib().octo_attend_decode_noalloc(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
+                                            ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
+                                            _ptr(q), dt, Hq, _ptr(seq_lens), max_seq_len,
+                                            float(softmax_scale), _ptr(out), _stream(dev)))
     return out
 
 

@@ -60,6 +60,7 @@
 #include <math.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "octo_internal.h"
 
@@ -1596,16 +1597,13 @@ extern "C" octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_code
                              max_seq_len, false, bytes);
 }
 
-extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
-                                          const octo_codec_desc* v_codec,
-                                          const octo_cache_view* k_cache,
-                                          const octo_cache_view* v_cache, const void* q,
-                                          octo_dtype q_dtype, int32_t num_q_heads,
-                                          const int32_t* seq_lens, int32_t max_seq_len,
-                                          float softmax_scale, float* out, void* workspace,
-                                          size_t workspace_bytes, hipStream_t stream) {
-  clear_error();
-  const char* what = "octo_attend_decode";
+static octo_status attend_decode(const char* what, const octo_codec_desc* k_codec,
+                                 const octo_codec_desc* v_codec, const octo_cache_view* k_cache,
+                                 const octo_cache_view* v_cache, const void* q,
+                                 octo_dtype q_dtype, int32_t num_q_heads,
+                                 const int32_t* seq_lens, int32_t max_seq_len,
+                                 float softmax_scale, float* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
   DecodeArgs a;
   Codec kc, vc;
   octo_status s = prepare(what, k_codec, v_codec, k_cache, v_cache, q, q_dtype, num_q_heads,
@@ -1616,6 +1614,81 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
   hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, a.B), dim3(kMergeWaves * 64), 0, stream,
                      a.ws_ml, a.ws_acc, a.n_part, num_q_heads, vc.seed, out);
   return check_launch(what);
+}
+
+extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
+                                          const octo_codec_desc* v_codec,
+                                          const octo_cache_view* k_cache,
+                                          const octo_cache_view* v_cache, const void* q,
+                                          octo_dtype q_dtype, int32_t num_q_heads,
+                                          const int32_t* seq_lens, int32_t max_seq_len,
+                                          float softmax_scale, float* out, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  return attend_decode("octo_attend_decode", k_codec, v_codec, k_cache, v_cache, q, q_dtype,
+                       num_q_heads, seq_lens, max_seq_len, softmax_scale, out, workspace,
+                       workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- no-alloc variant
+// octo_attend_decode_noalloc keeps the per-split partials of a call in this
+// device array instead of a caller's workspace.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code the array's name
+// is not a device address: every host use goes through the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, resolved on the first call on
+// that device.
+static octo_status scratch_address(const char* what, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(OCTO_ERR_HIP, "%s: no current HIP device", what);
+  if (dev >= kMaxDevices)
+    return fail(OCTO_ERR_UNSUPPORTED, "%s: device %d (at most %d devices)", what, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(OCTO_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s",
+                  what, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return OCTO_OK;
+}
+
+extern "C" octo_status octo_attend_decode_noalloc(const octo_codec_desc* k_codec,
+                                                  const octo_codec_desc* v_codec,
+                                                  const octo_cache_view* k_cache,
+                                                  const octo_cache_view* v_cache, const void* q,
+                                                  octo_dtype q_dtype, int32_t num_q_heads,
+                                                  const int32_t* seq_lens, int32_t max_seq_len,
+                                                  float softmax_scale, float* out,
+                                                  hipStream_t stream) {
+  clear_error();
+  const char* what = "octo_attend_decode_noalloc";
+  // the same split plan as octo_attend_decode: its partials must fit the array
+  if (!k_cache) return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: k_cache is NULL", what);
+  size_t need = 0;
+  octo_status s = workspace_bytes_for(what, k_codec, k_cache->batch, num_q_heads,
+                                      k_cache->kv_heads, max_seq_len, false, &need);
+  if (s != OCTO_OK) return s;
+  if (need > kScratchBytes)
+    return fail(OCTO_ERR_CAPACITY,
+                "%s: these shapes need %zu bytes of partials, more than the %zu-byte static "
+                "scratch; use octo_attend_decode with a workspace", what, need, kScratchBytes);
+  void* ptr = nullptr;
+  if ((s = scratch_address(what, &ptr)) != OCTO_OK) return s;
+  return attend_decode(what, k_codec, v_codec, k_cache, v_cache, q, q_dtype, num_q_heads,
+                       seq_lens, max_seq_len, softmax_scale, out, ptr, kScratchBytes, stream);
 }
 
 extern "C" octo_status octo_decode_step_workspace_bytes(const octo_codec_desc* k_codec, int32_t B,

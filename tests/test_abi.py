@@ -294,3 +294,15 @@ def test_group_codec_errors(L):
                                None) == 5
     assert L.octo_decode_tokens(ctypes.byref(gdesc()), ctypes.byref(gv), 100, 29, p, None) == 4
     assert L.octo_decode_tokens(ctypes.byref(gdesc()), ctypes.byref(gv), 0, 4, None, None) == 1
+
+
+def test_noalloc_refuses_oversized_shapes_on_the_host(L):
+    """octo_attend_decode_noalloc checks that the call's partials fit its
+    static scratch before touching any device."""
+    d = desc(bits=3)
+    cache = ob.CacheView(None, None, None, None, 2500, 4, 64, 0)
+    st = L.octo_attend_decode_noalloc(ctypes.byref(d), ctypes.byref(d), ctypes.byref(cache),
+                                      ctypes.byref(cache), None, 1, 16, None, 64,
+                                      ctypes.c_float(0.0), None, None)
+    assert ob.STATUS[st] == "OCTO_ERR_CAPACITY"
+    assert b"static" in L.octo_last_error()
