@@ -78,8 +78,9 @@ constexpr int kBlock = 32;            // tokens per wavefront iteration
 constexpr int kMaxG = 16;             // query heads per KV head (MFMA columns)
 constexpr float kUScale = 64.0f;      // exact scale of u^ in the operands
 constexpr float kInvSqrtD = 0.08838834764831845f;
-constexpr float kLazy = 5.545177444479562f;   // 8 ln 2: slack of the lazy running maximum
-constexpr float kTwoLn2 = 1.3862943611198906f; // 2 ln 2: one step of an fp32 exponent byte
+constexpr float kQjlC = 1.2533141373155003f;  // sqrt(pi / 2)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;                 // slack of the lazy running maximum (log2 units)
 constexpr float kNormByte = 66.0f;            // exponent byte of value norms below 128
 constexpr int kMaxSmallPre = 1024;    // largest pre-split table beside a second
                                       // workgroup on the CU (entries)
@@ -120,6 +121,20 @@ __device__ inline void wave_sync() {
 }
 
 __device__ inline uint32_t pk(fp16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+
+// (x & m) | c in one instruction, m and c held in vector registers (the
+// compiler splits the expression when its constants need literal operands).
+__device__ inline uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
+  return r;
+}
+// A constant materialized in a vector register.
+__device__ inline uint32_t vreg(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
 
 // x = hi + lo for 8 slots: hi rounded toward zero to fp16, lo the residual.
 __device__ inline void split8(const float* x, half8& hi, half8& lo) {
@@ -583,7 +598,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
       tabk[e] = make_uint4(__float_as_uint(n.x), __float_as_uint(n.y), __float_as_uint(n.z), 0u);
     }
   }
-  // ---- q_rot = H diag(s) q / sqrt(d) for the G heads (rows >= G are zero)
+  // ---- q_rot = H diag(s) q / sqrt(d) for the G heads (rows >= G are zero),
+  // times the softmax scale and log2(e): scores leave the MFMA in log2 units
+  const float qscale = kInvSqrtD * a.scale * kLog2e;
   const float s_lo = splitmix_sign(a.kseed, L), s_hi = splitmix_sign(a.kseed, L + 64);
 #pragma unroll
   for (int k = 0; k < kHeadsPerWave; ++k) {
@@ -595,8 +612,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
       wht128(q0, q1);
     else
       q0 = q1 = 0.0f;                   // rows past G are zero
-    qs[hh * 132 + L] = q0 * kInvSqrtD;
-    qs[hh * 132 + L + 64] = q1 * kInvSqrtD;
+    qs[hh * 132 + L] = q0 * qscale;
+    qs[hh * 132 + L + 64] = q1 * qscale;
   }
   lds_barrier();
 
@@ -643,15 +660,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
       float p1 = qs[hh * 132 + L + 64] * splitmix_sign(a.kseed, kHeadDim + L + 64);
       wht128(p0, p1);
       wave_sync();
-      qs[hh * 132 + L] = p0 * kInvSqrtD;
-      qs[hh * 132 + L + 64] = p1 * kInvSqrtD;
+      // H / sqrt(d), times sqrt(pi / 2) / sqrt(d), the estimator's factor (Sec. 3.6)
+      qs[hh * 132 + L] = p0 * (kInvSqrtD * kInvSqrtD * kQjlC);
+      qs[hh * 132 + L + 64] = p1 * (kInvSqrtD * kInvSqrtD * kQjlC);
     }
     lds_barrier();
+    // Slot map: dword m of call k (slots 2 m, 2 m + 1) stands for sign bits
+    // 15 - s and 31 - s of the lane group's sign word, s = 4 k + m, so that
+    // (word << s) holds them at bits 15 and 31, the fp16 sign bits.
 #pragma unroll
     for (int k = 0; k < (QJL ? 4 : 1); ++k) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = qs[col * 132 + 32 * grp4 + 8 * k + e];
+      for (int e = 0; e < 8; ++e)
+        x[e] = qs[col * 132 + 32 * grp4 + ((e & 1) ? 31 : 15) - (4 * k + (e >> 1))];
       split8(x, ph[k], pl[k]);
     }
   }
@@ -672,7 +694,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   for (int j = 0; j < GR::G; ++j) zacc[j] = 0.0f;
   uint32_t* vrec = reinterpret_cast<uint32_t*>(qbuf) + wave * (kIdxRows * kIdxRow / 2);
   float m_run = -INFINITY, l_run = 0.0f;            // of head `col`
-  const float qjl_c = 1.2533141373155003f * kInvSqrtD;   // sqrt(pi / 2) / sqrt(d)
   uint16_t* vidx = reinterpret_cast<uint16_t*>(qbuf) + wave * (kIdxRows * kIdxRow);
   // value-side rows of this lane's triplets 16 i + col (lanes past the last
   // triplet read a copy of it: finite values in columns never written out)
@@ -690,6 +711,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   if (a.step && split == 0 && g == 0 && tid == 0)
     a.snap[b] = make_int2(max(0, min(len_raw, a.capacity)), max(0, min(win_raw, a.window - 1)));
 
+  // fp16 sign bits and the fp16 pair (1, 1), in registers for and_or
+  const uint32_t sgn_mask = QJL ? vreg(0x80008000u) : 0u, one_pair = QJL ? vreg(0x3C003C00u) : 0u;
   if (QJL && t0 < t_end) {                                   // (registers are short)
     load_block(blk, a, plane, t0, L);
     load_gv(blk, a, plane, t0, L);
@@ -782,8 +805,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
           for (int c = 0; c < 3; ++c) acc = mfma3(ah[c], al[c], qh[3 * gi + c], ql[3 * gi + c], acc);
         }
       }
-      // this lane's 4 tokens: t0 + 16 kt + 4 grp4 + r, head col
-      const int tb = t0 + 16 * kt + 4 * grp4;
+      // this lane's 4 tokens: t0 + 16 kt + 4 grp4 + r, head col; scores in
+      // log2 units (the queries carry the softmax scale and log2 e)
       const float gka[4] = {blk.gk[kt].x, blk.gk[kt].y, blk.gk[kt].z, blk.gk[kt].w};
       float s4[4];
 #pragma unroll
@@ -793,14 +816,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
         floatx4 qa = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          // sigma_j = -1 where the bit is set: fp16 +-1 = 0x3C00 | bit << 15
-          const uint32_t byte = (sw >> (8 * k)) & 0xffu;
+          // sigma = -1 where the bit is set: fp16 +-1 = 0x3C00 | bit << 15,
+          // the two bits of dword m at 15 and 31 after the shift (slot map)
           u32x4 sg;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint32_t bits = byte >> (2 * m);
-            sg[m] = 0x3C003C00u | ((bits & 1u) << 15) | ((bits & 2u) << 30);
-          }
+          for (int m = 0; m < 4; ++m) sg[m] = and_or(sw << (4 * k + m), sgn_mask, one_pair);
           const half8 sgh = __builtin_bit_cast(half8, sg);
           qa = mfma(sgh, pl[k], qa);
           qa = mfma(sgh, ph[k], qa);
@@ -809,13 +829,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const uint16_t h = (uint16_t)(gr2[r >> 1] >> (16 * (r & 1)));
-          s4[r] += qjl_c * (float)__builtin_bit_cast(_Float16, h) * qa[r];
+          s4[r] = fmaf((float)__builtin_bit_cast(_Float16, h), qa[r], s4[r]);
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool valid = tb + r < t_end;
-        sc[kt][r] = valid ? s4[r] * gka[r] * a.scale : -INFINITY;
+      for (int r = 0; r < 4; ++r) sc[kt][r] = s4[r] * gka[r];
+      if (t0 + kBlock > t_end) {          // the split's ragged last block (uniform)
+        const int tb = t0 + 16 * kt + 4 * grp4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[kt][r] = tb + r < t_end ? sc[kt][r] : -INFINITY;
       }
     }
     // -- the key words are consumed: the next block's loads go out now and
@@ -832,8 +854,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
     // The value-side weight p gamma_v enters the MFMA as an fp16 hi/lo pair,
     // so it must stay below 2^16.  A token whose value norm has fp32
     // exponent byte b3 = bits >> 24 above kNormByte (gamma_v >= 128) takes
-    // part in the running maximum with its score raised by
-    // 2 ln 2 (b3 - kNormByte), which caps p gamma_v below 2^15 for any
+    // part in the running maximum with its (log2) score raised by
+    // 2 (b3 - kNormByte), which caps p gamma_v below 2^15 for any
     // finite norm; smaller norms (b3 <= kNormByte, gamma_v < 128) leave the
     // score as it is.  The merges only need every partial's sums to share
     // the units exp(-m) of its maximum, which holds for any such shift.
@@ -846,21 +868,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
         float t = sc[kt][r];
         if constexpr (VG == 0) {
           const float b3 = (float)(__float_as_uint(gvn[r]) >> 24);
-          t = fmaf(fmaxf(b3, kNormByte), kTwoLn2, t);
+          t = fmaf(fmaxf(b3, kNormByte), 2.0f, t);
         }
         mx = fmaxf(mx, t);
       }
     }
     mx = rows_max(mx);
-    if constexpr (VG == 0) mx -= kNormByte * kTwoLn2;
+    if constexpr (VG == 0) mx -= 2.0f * kNormByte;
     // Lazy running maximum: a head moves its maximum (and rescales its sums)
     // only when a (raised) score exceeds it by more than kLazy, so that most
-    // blocks skip the rescale; p stays below e^kLazy = 256, p gamma_v below
+    // blocks skip the rescale; p stays below 2^kLazy = 256, p gamma_v below
     // 2^15 (or 64 p below 2^14 with group values), inside fp16, and the
     // merges cancel the shift exactly.
     const bool up = mx > m_run + kLazy;
     const float m_new = up ? mx : m_run;
-    const float alpha = up ? __expf(m_run - m_new) : 1.0f;
+    const float alpha = up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     float pw[8], psum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -869,7 +891,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
                             VG ? kUScale : blk.gv[kt].z, VG ? kUScale : blk.gv[kt].w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = sc[kt][r] == -INFINITY ? 0.0f : __expf(sc[kt][r] - m_new);
+        // m_new is finite here (every block holds a valid token): a masked
+        // score gives exp2(-inf) = 0
+        const float p = __builtin_amdgcn_exp2f(sc[kt][r] - m_new);
         psum += p;
         pw[4 * kt + r] = p * gva[r];
       }
@@ -1057,7 +1081,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = red_ml[(w * kMaxG + h) * 2];
-      const float f = mw == -INFINITY ? 0.0f : __expf(mw - M);
+      const float f = mw == -INFINITY ? 0.0f : exp2f(mw - M);
       Lsum += f * red_ml[(w * kMaxG + h) * 2 + 1];
       const float zt = VG ? red_z[(w * kMaxG + h) * GR::G + c / (VG ? VG : 1)] : 0.0f;
       A += f * (red_o[(w * kMaxG + h) * kHeadDim + c] + zt);
@@ -1101,14 +1125,14 @@ __device__ inline void merge_head(const float2* __restrict__ ws_ml, const float*
     for (int u = 0; u < kMergeU; ++u)
       if (s0 + u < n_part) m_new = fmaxf(m_new, ml[u].x);
     if (m_new != -INFINITY) {            // the same in every lane
-      const float f0 = M == -INFINITY ? 0.0f : __expf(M - m_new);
+      const float f0 = M == -INFINITY ? 0.0f : exp2f(M - m_new);
       Lsum *= f0;
       a0 *= f0;
       a1 *= f0;
 #pragma unroll
       for (int u = 0; u < kMergeU; ++u) {
         const bool in = s0 + u < n_part && ml[u].x != -INFINITY;
-        const float f = in ? __expf(ml[u].x - m_new) : 0.0f;
+        const float f = in ? exp2f(ml[u].x - m_new) : 0.0f;
         Lsum = fmaf(f, ml[u].y, Lsum);
         a0 = fmaf(f, x0[u], a0);
         a1 = fmaf(f, x1[u], a1);
@@ -1133,7 +1157,7 @@ __device__ inline void merge_head(const float2* __restrict__ ws_ml, const float*
 #pragma unroll
     for (int w = 0; w < kMergeWaves; ++w) {
       const float mw = part[w][128];
-      const float f = mw == -INFINITY ? 0.0f : __expf(mw - Mt);
+      const float f = mw == -INFINITY ? 0.0f : exp2f(mw - Mt);
       t0 = fmaf(f, part[w][L], t0);
       t1 = fmaf(f, part[w][64 + L], t1);
       tl = fmaf(f, part[w][129], tl);
@@ -1370,7 +1394,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void step_merge_kernel(
         const float s =
             a.scale * wave_sum(fmaf(q0, bf16_to_f32(k0[c]), q1 * bf16_to_f32(k1[c])));
         const float mn = fmaxf(wm, s);
-        const float f = __expf(wm - mn), p = __expf(s - mn);
+        const float f = exp2f(wm - mn), p = exp2f(s - mn);
         wl = fmaf(wl, f, p);
         w0 = fmaf(w0, f, p * bf16_to_f32(v0[c]));
         w1 = fmaf(w1, f, p * bf16_to_f32(v1[c]));
@@ -1382,7 +1406,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void step_merge_kernel(
       float x0 = w0 * splitmix_sign(a.vseed, L), x1 = w1 * splitmix_sign(a.vseed, L + 64);
       wht128(x0, x1);
       const float mn = fmaxf(M, wm);
-      const float fa = M == -INFINITY ? 0.0f : __expf(M - mn), fb = __expf(wm - mn);
+      const float fa = M == -INFINITY ? 0.0f : exp2f(M - mn), fb = exp2f(wm - mn);
       Lsum = fmaf(Lsum, fa, wl * fb);
       a0 = fmaf(a0, fa, x0 * (kInvSqrtD * kUScale) * fb);
       a1 = fmaf(a1, fa, x1 * (kInvSqrtD * kUScale) * fb);
@@ -1740,7 +1764,7 @@ extern "C" octo_status octo_decode_step(const octo_codec_desc* k_codec,
   st.G = a.G;
   st.q = q;
   st.q_bf16 = a.q_bf16;
-  st.scale = a.scale;
+  st.scale = a.scale * kLog2e;          // the fold's scores in log2 units, as the scan's
   st.k_new = k_new;
   st.v_new = v_new;
   st.k_win = k_window;
