@@ -23,6 +23,8 @@
 // The window is decoded once per call and shared by every query tile.
 #include <math.h>
 
+#include <algorithm>
+#include <cstring>
 #include <type_traits>
 
 #include "octo_internal.h"
@@ -37,24 +39,31 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr float kInvSqrtD = 0.08838834764831845f;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Column of key k in the transposed value matrix.  Within each 32-key block
-// the keys are stored in the order in which the score MFMA leaves them in a
-// lane's P slots (slot e of lane group g is key 16 (e / 4) + 4 g + e % 4), so
-// that a lane's eight value slots are eight consecutive halves: one 16-byte
-// LDS read.
-__device__ inline int key_column(int k) {
-  return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+// Order of the head coordinates in the attention tiles when a tensor uses
+// the OCTOPUS codec.  A 128-coordinate row is four parts of 32 halves; part
+// p holds coordinates 30 p .. 30 p + 29 (its ten whole triplets 10 p .. 10 p
+// + 9, Sec. 3.2) and then coordinates 120 + 2 p and 121 + 2 p (two of the
+// last eight, which belong to triplets 40..42).  One thread decodes one
+// part of a row and stores it as four 16-byte chunks.  Scores and the
+// weighted sum of values are sums over coordinates, so the queries and
+// current keys (values) stored in the same order give the same results;
+// the output is put back into coordinate order at the end.
+__host__ __device__ inline int part_pos(int c) {
+  return c < 120 ? 32 * (c / 30) + c % 30 : 32 * ((c - 120) >> 1) + 30 + ((c - 120) & 1);
+}
+__host__ __device__ inline int part_coord(int pos) {
+  const int p = pos >> 5, o = pos & 31;
+  return o < 30 ? 30 * p + o : 120 + 2 * p + (o - 30);
 }
 
 // ---------------------------------------------------------------- pre-passes
 // Rows t < T_out of a plane: fp16(post H diag(s) x_t), zero for t >= T (tile
 // padding); post = 1 / sqrt(d), times the softmax scale and log2(e) for the
-// queries, so that scores come out of the MFMA in log2 units.  Row-major
-// output: row out_off + t of a [out_rows][128] plane.  Transposed output:
-// column key_column(out_off + t) of a [128][out_rows] plane.
+// queries, so that scores come out of the MFMA in log2 units.  Row out_off +
+// t of an [out_rows][stride] plane (stride >= 128 halves; the halves past 128
+// are not written), coordinates in part order (part_pos) when `perm` is set.
 // One workgroup takes 64 rows, sixteen lanes a row for the transform; the
-// transposed store goes through LDS so that 64 consecutive columns are
-// written together.
+// part order is applied through LDS so that each lane still stores 16 bytes.
 //
 // With `feat` set (queries of the Jensen-bias correction), row t also gets
 // kFeat fp16 features: slot j < 128 / feat_gs holds feat_c ||(R x_t)_j||^2
@@ -66,14 +75,16 @@ struct RotJob {
   uint64_t seed;
   float post;
   _Float16* out;
-  int out_rows, out_off;
+  int out_rows, out_off, stride;
   _Float16* feat;                // query features, or null
   int feat_gs;
   float feat_c;
   int tiles, planes;             // 64-row tiles per plane; planes (0: no job)
+  int perm;                      // coordinates in part order
 };
 
-template <bool TRANSPOSED>
+constexpr int kRotRow = kHeadDim + 8;   // halves per row of the LDS staging tile
+
 __device__ inline void rotate_rows(const RotJob& jb, int tile_x, int plane, _Float16* tile) {
   typedef _Float16 half8v __attribute__((ext_vector_type(8)));
   const uint16_t* __restrict__ in = jb.in;
@@ -133,15 +144,18 @@ __device__ inline void rotate_rows(const RotJob& jb, int tile_x, int plane, _Flo
     half8v o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (_Float16)(v[e] * post);
-    if (TRANSPOSED) {
-      typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+    if (jb.perm) {                                  // uniform branch
+      // through the wavefront's own rows of the LDS tile
 #pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        *reinterpret_cast<half2v*>(&tile[k * 130 + 8 * cl + e]) = half2v{o[e], o[e + 1]};
-    } else if (t < T_out) {
-      *reinterpret_cast<half8v*>(out + ((size_t)plane * out_rows + out_off + t) * kHeadDim + 8 * cl) = o;
+      for (int e = 0; e < 8; ++e) tile[k * kRotRow + part_pos(8 * cl + e)] = o[e];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      o = *reinterpret_cast<const half8v*>(&tile[k * kRotRow + 8 * cl]);
     }
-    if (!TRANSPOSED && feat != nullptr) {          // uniform branch
+    if (t < T_out)
+      *reinterpret_cast<half8v*>(out + ((size_t)plane * out_rows + out_off + t) * jb.stride + 8 * cl) = o;
+    if (feat != nullptr) {                          // uniform branch
       // group sums of the squared rotated coordinates: a group of feat_gs
       // coordinates is feat_gs / 8 consecutive lanes of the row
       float sq = 0.0f;
@@ -155,31 +169,23 @@ __device__ inline void rotate_rows(const RotJob& jb, int tile_x, int plane, _Flo
       if (t < T && cl < kFeat) feat[((size_t)plane * T + t) * kFeat + cl] = (_Float16)(cl < ng ? feat_c * f : 0.0f);
     }
   }
-  if (TRANSPOSED) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * kHeadDim; e += 256) {
-      const int c = e >> 6, k = e & 63, t = t0 + k;
-      if (t < T_out)
-        out[((size_t)plane * kHeadDim + c) * out_rows + key_column(out_off + t)] = tile[k * 130 + c];
-    }
-  }
 }
 
 // The three row transforms of a chunk call (queries; current keys; current
-// values, transposed) in one launch, so that the loads of one overlap the
-// stores of another: workgroups [0, n0) take job 0, the next n1 job 1, the
-// rest job 2, where n_i = tiles_i planes_i.
+// values) in one launch, so that the loads of one overlap the stores of
+// another: workgroups [0, n0) take job 0, the next n1 job 1, the rest job 2,
+// where n_i = tiles_i planes_i.
 __global__ __launch_bounds__(256) void rotate_rows_kernel(RotJob q, RotJob k, RotJob v) {
-  __shared__ _Float16 tile[64 * 130];
+  __shared__ __attribute__((aligned(16))) _Float16 tile[64 * kRotRow];
   const int n0 = q.tiles * q.planes, n1 = k.tiles * k.planes;
   int id = blockIdx.x;
   if (id < n0) {
-    rotate_rows<false>(q, id % q.tiles, id / q.tiles, tile);
+    rotate_rows(q, id % q.tiles, id / q.tiles, tile);
   } else if ((id -= n0) < n1) {
-    rotate_rows<false>(k, id % k.tiles, id / k.tiles, tile);
+    rotate_rows(k, id % k.tiles, id / k.tiles, tile);
   } else {
     id -= n1;
-    rotate_rows<true>(v, id % v.tiles, id / v.tiles, tile);
+    rotate_rows(v, id % v.tiles, id / v.tiles, tile);
   }
 }
 
@@ -194,158 +200,349 @@ __device__ inline float4 oct_dir(float xi, float eta) {
   return make_float4(x / n, y / n, z / n, 0.0f);
 }
 
-// LDS staging tile of 64 tokens x 128 coordinates, laid out for its store.
-// Row-major output: token rows of 130 halves (65 words), so that the 64
-// lanes of a wavefront writing one coordinate of 64 tokens meet 64 different
-// banks.  Transposed output: coordinate rows of 72 halves holding the tokens
-// at key_column order, so that a coordinate's 64 keys leave in 16-byte
-// chunks exactly as they lie in the output, and the writes of one coordinate
-// fill 32 consecutive words.
-template <bool TRANSPOSED>
-struct StageTile {
-  static constexpr int kRowHalves = TRANSPOSED ? 72 : 130;
-  static constexpr int kElems = TRANSPOSED ? kHeadDim * 72 : 64 * 130;
-  __device__ static int at(int k, int c) {
-    return TRANSPOSED ? c * 72 + key_column(k) : k * 130 + c;
-  }
-};
-
-// Stores the staging tile of tokens t0 .. t0 + nt - 1 (t0 a multiple of 64)
-// as rows of a [out_rows][128] plane (16-byte chunks) or as columns of a
-// [128][out_rows] plane at key_column.
-template <bool TRANSPOSED>
-__device__ inline void store_rows(const _Float16* tile, _Float16* __restrict__ out,
-                                  int out_rows, size_t plane, int t0, int nt) {
-  const int tid = threadIdx.x;
-  if (TRANSPOSED) {
-    if (nt == 64) {
-      for (int e = tid; e < kHeadDim * 8; e += 256) {
-        const int c = e >> 3, q = e & 7;
-        *reinterpret_cast<uint4*>(out + (plane * kHeadDim + c) * out_rows + t0 + 8 * q) =
-            *reinterpret_cast<const uint4*>(&tile[c * 72 + 8 * q]);
-      }
-    } else {
-      for (int e = tid; e < 64 * kHeadDim; e += 256) {
-        const int c = e >> 6, kk = e & 63;
-        if (kk < nt)
-          out[(plane * kHeadDim + c) * out_rows + key_column(t0 + kk)] =
-              tile[StageTile<true>::at(kk, c)];
-      }
-    }
-  } else {
-    // four word reads a chunk: token rows are 4-byte but not 16-byte aligned
-    const uint32_t* tw = reinterpret_cast<const uint32_t*>(tile);
-    for (int e = tid; e < 64 * 16; e += 256) {
-      const int kk = e >> 4, c8 = (e & 15) * 8;
-      if (kk < nt) {
-        const int w0 = kk * 65 + c8 / 2;
-        *reinterpret_cast<uint4*>(out + (plane * out_rows + t0 + kk) * kHeadDim + c8) =
-            make_uint4(tw[w0], tw[w0 + 1], tw[w0 + 2], tw[w0 + 3]);
-      }
-    }
-  }
-}
-
-// One workgroup per 64 cached tokens of a plane: lanes take (token, triplet)
-// items token-fastest (coalesced reads of the tile-64 words) and write
-// fp16(gamma_t u^_t[0:128]) into an LDS tile, which is then stored as rows t
-// of a [out_rows][128] plane (16-byte chunks) or as columns t of a
-// [128][out_rows] plane (64 consecutive keys per row, at key_column).
-template <int BD, int BN, bool TRANSPOSED>
-__global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __restrict__ idx,
-                                                          const float* __restrict__ gamma,
-                                                          const Codebook cb,
-                                                          int capacity, int cached,
-                                                          _Float16* __restrict__ out,
-                                                          int out_rows) {
-  constexpr int K = 1 << BD, R = 1 << BN, FWD = 2 * BD, BT = FWD + BN;
-  constexpr int WI = (kNTri * BT + 31) / 32;
-  using ST = StageTile<TRANSPOSED>;
-  constexpr int kTriG = 11;                        // triplets per thread: 4 x 11 >= 43
-  constexpr int GW = (31 + kTriG * BT + 31) / 32;  // record words covering them from any shift
-  __shared__ float4 lut[K * K];
-  __shared__ float crho[R], cxi[K];
-  __shared__ __attribute__((aligned(16))) _Float16 tile[ST::kElems];
-  const int tid = threadIdx.x;
-  const size_t plane = blockIdx.y;
-  const int t0 = blockIdx.x * 64;
-  const int nt = min(64, cached - t0);
-  // Thread (k, w): token t0 + k, triplets 11 w .. 11 w + 10.  Its record
-  // words and gamma are all requested first (a token past the cached ones
-  // reads token t0, whose values are not stored).
-  const int k = tid & 63, w = tid >> 6;
-  const int t = t0 + (k < nt ? k : 0);
-  const int iwo = (kTriG * BT * w) >> 5, ish = (kTriG * BT * w) & 31;
-  uint32_t wd[GW];
-#pragma unroll
-  for (int j = 0; j < GW; ++j) wd[j] = idx[tile_word(plane, capacity, t, min(iwo + j, WI - 1), WI)];
-  const float gam = gamma[plane * capacity + t];
-  if (tid < K) cxi[tid] = cb.xi[tid];
-  if (tid < R) crho[tid] = cb.rho[tid];
-  __syncthreads();
-  for (int e = tid; e < K * K; e += 256) lut[e] = oct_dir(cxi[e % K], cxi[e / K]);
-  __syncthreads();
-  // shift the words so that triplet 11 w + m starts at bit m B_tri
-  uint32_t sw[GW];
-#pragma unroll
-  for (int j = 0; j < GW; ++j) sw[j] = __builtin_amdgcn_alignbit(j + 1 < GW ? wd[j + 1] : 0u, wd[j], ish);
-#pragma unroll
-  for (int m = 0; m < kTriG; ++m) {
-    const int i = kTriG * w + m;
-    if (i >= kNTri) break;
-    // triplet field i: code pair | rho index << 2 b_dir
-    const uint32_t f = field<BT>(sw, m * BT);
-    const uint32_t code = f & ((1u << FWD) - 1u), ir = f >> FWD;
-    const float s = crho[ir] * gam;
-    const float4 n = lut[code];
-    tile[ST::at(k, 3 * i)] = (_Float16)(s * n.x);
-    tile[ST::at(k, 3 * i + 1)] = (_Float16)(s * n.y);
-    if (i < kNTri - 1) tile[ST::at(k, 3 * i + 2)] = (_Float16)(s * n.z);   // coordinate 128 is the pad
-  }
-  __syncthreads();
-  store_rows<TRANSPOSED>(tile, out, out_rows, plane, t0, nt);
-}
-
 // ---------------------------------------------------------------- attention
+// The cached window is reconstructed inside the attention kernel, one 32-key
+// tile at a time, into the LDS tiles the matrix cores read (OCTOPUS paper,
+// Sec. 3.6: the factorized score needs u^ and gamma, never K^ in memory).
+// Each thread loads the packed words of one part of one cached row (keys and
+// values alike) straight into registers and writes that part as four
+// 16-byte chunks:
+//   - key rows: fp16 rho^ n^ (OCTOPUS keys, part order; gamma multiplies the
+//     fp32 scores) or Delta^ code + z^ (group keys, coordinate order);
+//   - value rows: fp16 gamma rho^ n^ (OCTOPUS values, part order) or Delta^
+//     code + z^ (group values, coordinate order).
+// The current chunk's rows come from the pre-pass (rotate_rows) by direct
+// loads into the same tiles.  The value fragments of O = P V (eight keys of
+// one coordinate a lane) are read from the row-major value tile with the
+// transposing LDS read.
 constexpr int kRG = 2;          // 16-query row groups per wavefront
 constexpr int kCWaves = 2;
 constexpr int kCThreads = 64 * kCWaves;
 constexpr int kBM = 16 * kRG * kCWaves;   // 64 queries per workgroup
 constexpr int kXcds = 8;        // workgroups are dealt round-robin to the XCDs
-constexpr int kPadKeys = 64;    // the staged key rows are padded to a multiple of this
 constexpr float kLazyLog2 = 8.0f;   // slack of the lazy running maximum (log2 units)
-// Key tiles: 32 keys per LDS tile, in two buffers: the next tile streams in
-// while the current one is used, in 32 KB of LDS (four workgroups per CU).
-constexpr int kBN = 32;
-constexpr int kVChunks = kBN / 8;                                 // 16-byte chunks per V^T row
-constexpr int kTileInsts = kBN * (kHeadDim / 8) / 64 / kCWaves;   // per wavefront, K and V^T each
-static_assert(kPadKeys % kBN == 0, "tiles never straddle the padded end");
-// LDS tiles are unpadded, written by direct buffer-to-LDS loads (16 bytes a
-// lane, 1 KB contiguous per wavefront instruction).  16-byte chunk c of a row
-// is stored at chunk c ^ swizzle(row): for key rows (256 B, 16 chunks)
-// swizzle = row mod 16, for transposed value rows (64 B, 4 chunks)
-// swizzle = (row / 4) mod 4, so that the 16 rows one fragment read touches
-// fall in 16 different bank quads.
-constexpr int kKChunks = kHeadDim / 8;   // 16-byte chunks per key row
+constexpr int kBN = 32;         // keys per tile
+constexpr int kCurPad = kBN;    // the current rows are padded to whole tiles
+// Key tile: 32 rows of 256 bytes, unpadded; 16-byte chunk c of row r is
+// stored at chunk c ^ (r mod 16), so that the 8 rows one fragment read (or
+// one chunk store) serves at a time fall in 8 different bank quads.
+constexpr int kKChunks = kHeadDim / 8;
+constexpr int kKTileBytes = kBN * kHeadDim * 2;
+constexpr int kKTileInsts = kBN * kKChunks / 64 / kCWaves;    // direct loads a wavefront
+// Value tile: 32 rows of 288 bytes (256 of values, 32 of pad), so that the
+// four rows one transposing read serves at a time start 8 banks apart.
+// The current values come in rows of the same length.
+constexpr int kVRowBytes = 288;
+constexpr int kVRowHalves = kVRowBytes / 2;
+constexpr int kVTileBytes = kBN * kVRowBytes;
+constexpr int kVTileChunks = kVTileBytes / 16;
+constexpr int kVTileInsts = (kVTileChunks + 64 * kCWaves - 1) / (64 * kCWaves);   // a wavefront
+constexpr int kTilesBytes = 2 * kKTileBytes + 2 * kVTileBytes;
+// Output blocks of 16 value coordinates.
+constexpr int kOB = kHeadDim / 16;
 // Fourth word of a raw buffer descriptor: 32-bit data format, no swizzle.
 constexpr int kBufferWord3 = 0x00020000;
 // s_waitcnt immediate waiting until no vector-memory operation of the
 // wavefront is outstanding (vmcnt 0; expcnt and lgkmcnt not waited for).
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
+// Byte offset past any buffer: a load there returns zero.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+typedef _Float16 fp16x2 __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint32_t pk2(fp16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ inline fp16x2 upk2(uint32_t u) { return __builtin_bit_cast(fp16x2, u); }
+// (fp16(a), fp16(b)) rounded to nearest even, as one word
+__device__ inline uint32_t pack_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, fp16x2{(_Float16)a, (_Float16)b});
+}
+// low halves of e0, e1 as (e0.lo, e1.lo)
+__device__ inline uint32_t pair_lo(uint32_t e0, uint32_t e1) {
+  return __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+}
+// (e.hi of the first word, e.lo of the second): (y | z) of an entry (x|y), (z|0)
+__device__ inline uint32_t hi_lo(uint32_t e_xy, uint32_t e_z) {
+  return __builtin_amdgcn_perm(e_z, e_xy, 0x05040302u);
+}
+__device__ inline uint32_t mul2(uint32_t a, uint32_t b) { return pk2(upk2(a) * upk2(b)); }
+// A value the compiler must treat as unknown: keeps a table index in its own
+// register, so that its address is one shift-add from it.
+__device__ inline uint32_t opaque(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// One packed tensor as the attention kernel reads it.  The OCTOPUS table is
+// "pre-split" (fp16 rho^ n^ at rho index K^2 + code pair, the triplet's field
+// as stored) when it has at most kMaxPre entries, else it holds fp16 n^ per
+// code pair with the (rho^, rho^) pairs beside it.
+constexpr int kMaxPre = 512;
+struct ChunkCodec {
+  int sel;          // OCTOPUS: 10 b_dir + b_nrm; group: 1000 + 100 b + g
+  int W;            // record words
+  int tab;          // byte offset of its table in the dynamic LDS (OCTOPUS)
+  int rho;          // byte offset of its rho pairs
+};
 
 struct ChunkArgs {
-  const _Float16* q;   // [B][Hq][Tq][128] rotated, times scale log2(e)
-  const _Float16* k;   // [B][Hkv][Tk_pad][128] rotated
-  const _Float16* vt;  // [B][Hkv][128][Tk_pad] rotated, transposed
-  float* out;          // [B][Hq][Tq][128]
-  int Hq, Hkv, Tq, Tk, Tk_pad;
-  int q_tiles;         // query tiles per (batch, head)
+  const _Float16* q;     // [B][Hq][Tq][128] rotated, times scale log2(e) / sqrt(d)
+  const _Float16* kc;    // current keys [B][Hkv][Tc_pad][128] rotated
+  const _Float16* vc;    // current values [B][Hkv][Tc_pad][kVRowHalves] rotated
+  float* out;            // [B][Hq][Tq][128]
+  int Hq, Hkv, Tq, q_tiles;
+  int cached, Tc, Tc_pad, capacity;
   uint64_t vseed;
-  // Jensen-bias correction: fp16 feature rows whose product is minus the
-  // bias in log2 units ([B][Hq][Tq][kFeat] queries, [B][Hkv][Tk_pad][kFeat] keys)
-  const _Float16* qfeat;
-  const _Float16* kfeat;
+  const _Float16* qfeat; // Jensen-bias correction: query features [B][Hq][Tq][kFeat]
+  const uint32_t *k_idx, *v_idx;
+  const float *k_gamma, *v_gamma;
+  ChunkCodec kcod, vcod;
+  int vperm;             // value rows in part order (OCTOPUS values)
+  int share_tab;         // K and V use one table (same split, same codebooks)
+  Codebook kcb, vcb;
 };
+
+// ---- tables
+template <int BD, int BN>
+__device__ __forceinline__ void build_octo_table(const float* cx, const float* cr, char* dyn,
+                                                 const ChunkCodec& c, int tid) {
+  constexpr int K = 1 << BD, KK = K * K, R = 1 << BN;
+  constexpr bool PRE = KK * R <= kMaxPre;
+  uint2* tab = reinterpret_cast<uint2*>(dyn + c.tab);
+  for (int e = tid; e < KK; e += kCThreads) {
+    const float4 n = oct_dir(cx[e % K], cx[e / K]);          // field: xi | eta << b_dir
+    if (PRE) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        tab[r * KK + e] = make_uint2(pack_rne(cr[r] * n.x, cr[r] * n.y), pack_rne(cr[r] * n.z, 0.0f));
+    } else {
+      tab[e] = make_uint2(pack_rne(n.x, n.y), pack_rne(n.z, 0.0f));
+    }
+  }
+  if (!PRE && tid < R) reinterpret_cast<uint32_t*>(dyn + c.rho)[tid] = pack_rne(cr[tid], cr[tid]);
+}
+
+// ---- the packed words a thread decodes
+// Thread (k = L mod 32, part pg = 2 (L / 32) + wavefront) decodes part pg of
+// row k of the tile, of the keys and then of the values: OCTOPUS rows, the
+// triplets 10 pg .. 10 pg + 9 and the coordinates 120 + 2 pg, 121 + 2 pg of
+// triplets 40..42 (part_pos); group rows, coordinates 32 pg .. 32 pg + 31.
+// A word row (word w of the 64 tokens of a tile-64 block) is 256 bytes; the
+// tile's 32 tokens start at byte 4 (t0 mod 64) of it.
+// Words holding the fields of triplets 10 p .. 10 p + 9 of any part p.
+constexpr int main_words(int bt) {
+  int m = 0;
+  for (int p = 0; p < 4; ++p) {
+    const int n = ((10 * bt * p) % 32 + 10 * bt + 31) / 32;
+    m = n > m ? n : m;
+  }
+  return m;
+}
+// Words holding the fields of triplets 40..42.
+constexpr int tail_words(int bt) { return ((43 * bt - 1) >> 5) - ((40 * bt) >> 5) + 1; }
+// Codec selectors (as in ChunkCodec::sel) and the registers of one row
+// part's words; selector 0 stands for "any codec, chosen at run time".
+constexpr int kOctoSel[6] = {31, 42, 53, 22, 33, 44};
+constexpr int kGroupSel[6] = {1216, 1232, 1316, 1332, 1416, 1432};
+constexpr int row_words(int sel) {
+  if (sel == 0) {
+    int m = 0;
+    for (int i = 0; i < 6; ++i) {
+      const int a = row_words(kOctoSel[i]), b = row_words(kGroupSel[i]);
+      m = a > m ? a : m;
+      m = b > m ? b : m;
+    }
+    return m;
+  }
+  if (sel < 1000) {
+    const int bt = 2 * (sel / 10) + sel % 10;
+    return main_words(bt) + tail_words(bt) + 1;
+  }
+  return (sel - 1000) / 100 + 2;
+}
+// Calls f(std::integral_constant<int, s>) for the codec with selector s:
+// SEL itself when it is not 0, else the run-time `sel`.
+template <int SEL, class F>
+__device__ __forceinline__ void with_codec(int sel, F&& f) {
+  if constexpr (SEL != 0) {
+    f(std::integral_constant<int, SEL>{});
+  } else {
+    switch (sel) {
+      case 31: f(std::integral_constant<int, 31>{}); break;
+      case 42: f(std::integral_constant<int, 42>{}); break;
+      case 53: f(std::integral_constant<int, 53>{}); break;
+      case 22: f(std::integral_constant<int, 22>{}); break;
+      case 33: f(std::integral_constant<int, 33>{}); break;
+      case 44: f(std::integral_constant<int, 44>{}); break;
+      case 1216: f(std::integral_constant<int, 1216>{}); break;
+      case 1232: f(std::integral_constant<int, 1232>{}); break;
+      case 1316: f(std::integral_constant<int, 1316>{}); break;
+      case 1332: f(std::integral_constant<int, 1332>{}); break;
+      case 1416: f(std::integral_constant<int, 1416>{}); break;
+      case 1432: f(std::integral_constant<int, 1432>{}); break;
+    }
+  }
+}
+
+// OCTOPUS rows: the words of bits [10 pg B_tri, ...), the words of triplets
+// 40..42, then gamma (zero for a key past the window, `valid` false, so that
+// a masked value stays finite)
+template <int BD, int BN, int N>
+__device__ __forceinline__ void load_octo_row(uint32_t (&w)[N], __amdgpu_buffer_rsrc_t is,
+                                              __amdgpu_buffer_rsrc_t gs, int sbase, int t0, int kk,
+                                              int pg, bool valid) {
+  constexpr int BT = 2 * BD + BN, NWm = main_words(BT), NWe = tail_words(BT);
+  static_assert(NWm + NWe + 1 <= N, "row part words");
+  const int v0 = kk * 4;
+  const int vm = v0 + ((10 * BT * pg) >> 5) * 256;
+#pragma unroll
+  for (int i = 0; i < NWm; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(is, vm + 256 * i, sbase, 0);
+#pragma unroll
+  for (int i = 0; i < NWe; ++i)
+    w[NWm + i] = __builtin_amdgcn_raw_buffer_load_b32(is, v0 + 256 * (((40 * BT) >> 5) + i), sbase, 0);
+  w[NWm + NWe] = __builtin_amdgcn_raw_buffer_load_b32(gs, valid ? v0 : kOutOfRange, t0 * 4, 0);
+}
+
+// Group rows: the part's code words, its scale word and zero-point word (the
+// zero-point zero for a key past the window)
+template <int VB, int GS, int N>
+__device__ __forceinline__ void load_group_row(uint32_t (&w)[N], __amdgpu_buffer_rsrc_t is,
+                                               int sbase, int kk, int pg, bool valid) {
+  static_assert(VB + 2 <= N, "row part words");
+  constexpr int G = kHeadDim / GS, NG = 32 / GS, WC = VB * kHeadDim / 32;
+  const int v0 = kk * 4;
+#pragma unroll
+  for (int i = 0; i < VB; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(is, v0 + 256 * (VB * pg + i), sbase, 0);
+  w[VB] = __builtin_amdgcn_raw_buffer_load_b32(is, v0 + 256 * (WC + (NG * pg) / 4), sbase, 0);
+  w[VB + 1] = __builtin_amdgcn_raw_buffer_load_b32(
+      is, valid ? v0 + 256 * (WC + G / 4 + (NG * pg) / 2) : kOutOfRange, sbase, 0);
+}
+
+// ---- row decoders (words in registers)
+
+// Stores a row part: 16 dwords as four 16-byte chunks at the given offsets.
+__device__ inline void store_part(char* tile, const int (&cw)[4], const uint32_t (&d)[16]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    *reinterpret_cast<u32x4*>(tile + cw[c]) = u32x4{d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]};
+}
+
+// OCTOPUS row part (PAR: the wavefront, so pg = 2 hi + PAR): the ten
+// triplets as five pairs of three dwords, (x|y) of the first, (z of the
+// first | x of the second), (y|z) of the second; then the extra dword:
+// part 0 (x|y) of triplet 40, part 1 (z of 40 | x of 41), part 2 (y|z) of
+// 41, part 3 (x|y) of 42.  Keys (VAL false): the scores take gamma in fp32,
+// the threads of part 0 copy it to gk.  Values: every word times gamma.
+template <int BD, int BN, int PAR, bool VAL, int N>
+__device__ __forceinline__ void dec_octo_row(const uint32_t (&w)[N], const char* dyn,
+                                             const ChunkCodec& c, char* tile, const int (&cw)[4],
+                                             float* gk, int kk, int hi) {
+  constexpr int BT = 2 * BD + BN, NWm = main_words(BT), NWe = tail_words(BT);
+  constexpr int KK = 1 << (2 * BD);
+  constexpr bool PRE = KK * (1 << BN) <= kMaxPre;
+  const int pg = 2 * hi + PAR;
+  const int sh = (10 * BT * pg) & 31;
+  uint32_t x[NWm], xe[NWe + 1];
+#pragma unroll
+  for (int i = 0; i < NWm; ++i) x[i] = __builtin_amdgcn_alignbit(i + 1 < NWm ? w[i + 1] : 0u, w[i], sh);
+#pragma unroll
+  for (int i = 0; i < NWe; ++i) xe[i] = w[NWm + i];
+  xe[NWe] = 0u;
+  const uint32_t gam = w[NWm + NWe];
+  if (!VAL && pg == 0) gk[kk] = __uint_as_float(gam);
+  const uint2* tab = reinterpret_cast<const uint2*>(dyn + c.tab);
+  const uint32_t* rhop = reinterpret_cast<const uint32_t*>(dyn + c.rho);
+  auto entry = [&](uint32_t f) __attribute__((always_inline)) -> uint2 {
+    if constexpr (PRE) {
+      return tab[opaque(f)];
+    } else {
+      const uint2 e = tab[opaque(f & (KK - 1))];
+      const uint32_t p = rhop[opaque(f >> (2 * BD))];
+      return make_uint2(mul2(e.x, p), mul2(e.y, p));
+    }
+  };
+  uint32_t d[16];
+#pragma unroll
+  for (int m = 0; m < 5; ++m) {
+    const uint2 e0 = entry(field<BT>(x, 2 * m * BT)), e1 = entry(field<BT>(x, (2 * m + 1) * BT));
+    d[3 * m] = e0.x;
+    d[3 * m + 1] = pair_lo(e0.y, e1.x);
+    d[3 * m + 2] = hi_lo(e1.x, e1.y);
+  }
+  // triplets 40..42 at bit offsets from the first tail word
+  constexpr int eb = ((40 * BT) >> 5) * 32;
+  auto tail = [&](int t) __attribute__((always_inline)) { return field<BT>(xe, t * BT - eb); };
+  if constexpr (PAR == 0) {          // parts 0 and 2
+    const uint2 ea = entry(hi ? tail(41) : tail(40));
+    d[15] = hi ? hi_lo(ea.x, ea.y) : ea.x;
+  } else {                           // parts 1 and 3
+    const uint2 ea = entry(hi ? tail(42) : tail(40)), eb2 = entry(tail(41));
+    d[15] = hi ? ea.x : pair_lo(ea.y, eb2.x);
+  }
+  if constexpr (VAL) {
+    const uint32_t G = pack_rne(__uint_as_float(gam), __uint_as_float(gam));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d[i] = mul2(d[i], G);
+  }
+  store_part(tile, cw, d);
+}
+
+// Group-codec scale of group j from its scale word (byte j mod 4) and
+// zero-point from its zero word (half j mod 2) (an E4M3 step is exact in
+// fp16; the BF16 zero-point is rounded).
+__device__ inline float group_scale(uint32_t sw, int j) { return e4m3_value((sw >> (8 * (j & 3))) & 0xffu); }
+__device__ inline float group_zero(uint32_t zw, int j) { return __uint_as_float(((zw >> (16 * (j & 1))) & 0xffffu) << 16); }
+
+// (code 2d | code 2d + 1) of a VB-bit stream as fp16 integers: the two fields
+// spread to the halves by one multiply, over 1024 + value as fp16 bits, less
+// 1024 (k1024 holds the fp16 pair (1024, 1024)).
+template <int VB>
+__device__ inline uint32_t code_pair(uint32_t x2, uint32_t k1024) {
+  constexpr uint32_t M = (1u << VB) - 1u;
+  const uint32_t y = x2 * (1u + (1u << (16 - VB)));
+  return pk2(upk2((y & (M | (M << 16))) | 0x64006400u) - upk2(k1024));
+}
+
+// Group row part: the 16 words (Delta^ code + z^) of coordinates 32 pg .. 32
+// pg + 31.  Keys: gamma 1 for the scores, and with CORR the key features
+// Delta^2 / 16 of the part's groups (zero in the unused slots).
+template <int VB, int GS, bool CORR, bool VAL, int N>
+__device__ __forceinline__ void dec_group_row(const uint32_t (&w)[N], char* tile,
+                                              const int (&cw)[4], float* gk, _Float16* kf, int kk,
+                                              int pg, uint32_t k1024) {
+  constexpr int G = kHeadDim / GS, NG = 32 / GS > 0 ? 32 / GS : 1;
+  if (!VAL && pg == 0) gk[kk] = 1.0f;
+  uint32_t sc[NG], zz[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int j = NG * pg + gi;
+    const float dh = group_scale(w[VB], j), zf = group_zero(w[VB + 1], j);
+    sc[gi] = pack_rne(dh, dh);
+    zz[gi] = pack_rne(zf, zf);
+    if (!VAL && CORR) kf[kk * kFeat + j] = (_Float16)(dh * dh * 0.0625f);
+  }
+  if (!VAL && CORR && G == 4) kf[kk * kFeat + 4 + pg] = (_Float16)0.0f;
+  uint32_t cwd[VB + 1];
+#pragma unroll
+  for (int i = 0; i < VB; ++i) cwd[i] = w[i];
+  cwd[VB] = 0u;
+  uint32_t d[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t x2 = field<2 * VB>(cwd, 2 * i * VB);
+    const int gi = (2 * i) / GS;
+    d[i] = pk2(__builtin_elementwise_fma(upk2(code_pair<VB>(x2, k1024)), upk2(sc[gi]), upk2(zz[gi])));
+  }
+  store_part(tile, cw, d);
+}
+
+// Workgroup barrier for the tile pipeline: this wave's LDS operations are
+// complete, its global loads stay in flight (the pipeline waits for its
+// direct-to-LDS loads itself, before the barrier that publishes them).  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ inline void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Lane layout of v_mfma_f32_16x16x32_f16 (wave of 64, L = lane):
 //   A[i][k]: i = L % 16, k = 8 (L / 16) + e  (e = element 0..7)
@@ -353,11 +550,25 @@ struct ChunkArgs {
 //   D[i][j]: i = 4 (L / 16) + r, j = L % 16  (r = register 0..3)
 // Scores are computed transposed, S^T = K Q^T (keys are rows), so that each
 // lane ends up with 4 keys of one query, which is exactly the A operand
-// layout P needs for O = P V with keys as the contraction index.  Each
-// wavefront owns two 16-query row groups, so every key / value fragment read
-// from LDS feeds two MFMAs.  The softmax state is updated once per 64-key
-// tile.  Small workgroups (64 queries) keep four resident per CU, which
-// hides the tile loads and leaves no lone final round of workgroups.
+// layout P needs for O = P V with keys as the contraction index: slot e of
+// lane group g is key 16 (e / 4) + 4 g + e % 4.  Each wavefront owns two
+// 16-query row groups, so every key / value fragment read from LDS feeds two
+// MFMAs.  The softmax state is updated once per tile.
+//
+// Value fragments: the transposing read (ds_read_b64_tr_b16) gives lane i of
+// a 16-lane group, element j, element i % 4 of the four halves that lane
+// 4 j + i / 4 of the group addressed.  Lane s = 4 j + q of group g
+// addresses row 4 g + j (then 16 + 4 g + j) of the value tile at
+// coordinates 16 c + 4 q .. 16 c + 4 q + 3, so lane i receives coordinate
+// 16 c + i of keys 4 g + j (then 16 + 4 g + j): its B fragment.
+//
+// Tiles: the cached window's ceil(cached / 32) tiles first, then the current
+// chunk's; tile u lives in buffer u % 2.  Iteration t: the words of cached
+// tile t + 2 are requested (registers of stage t % 2), or the rows of
+// current tile t + 1 (direct loads into buffer (t + 1) % 2); tile t is
+// computed; the threads decode cached tile t + 1 (words of stage (t + 1) %
+// 2) into buffer (t + 1) % 2; one barrier.  The loop is unrolled by two so
+// that buffer offsets and word stages are constants.
 //
 // XCD-aware order: the hardware deals consecutive workgroup ids to the 8
 // XCDs in turn, so the linear id is mapped such that all query tiles of one
@@ -366,18 +577,17 @@ struct ChunkArgs {
 //
 // CORR: the Jensen-bias correction ("Quantized Keys Steal Attention",
 // Eq. 15).  Its bias is a rank-(128 / g) product of query and key features,
-// so it is one more k-slice of the score MFMA per 16 keys, whose slots 0..7
-// (lane group 0) hold the features and the rest zeros: lane group 0 reads
-// the tile's key features (beside the tile, 512 B a buffer) and the
-// workgroup's query features (1 KB of LDS) where they are used, the other
-// lanes hold zeros, so four workgroups still share a CU.
-template <bool CORR>
+// so it is one more k-slice of the score MFMA per 16 cached keys, whose slots
+// 0..7 (lane group 0) hold the features and the rest zeros.
+template <bool CORR, int KSEL, int VSEL>
 __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
-  __shared__ __attribute__((aligned(1024))) _Float16 ks0[kBN * kHeadDim], ks1[kBN * kHeadDim];
-  __shared__ __attribute__((aligned(1024))) _Float16 vs0[kHeadDim * kBN], vs1[kHeadDim * kBN];
-  __shared__ __attribute__((aligned(1024))) _Float16 kfs0[CORR ? kBN * kFeat : 8],
-      kfs1[CORR ? kBN * kFeat : 8];
-  __shared__ _Float16 qfs[CORR ? kBM * kFeat : 1];
+  constexpr int KW = row_words(KSEL), VW = row_words(VSEL);
+  __shared__ __attribute__((aligned(1024))) char tiles[kTilesBytes];
+  __shared__ __attribute__((aligned(16))) float gks[2][kBN];
+  __shared__ __attribute__((aligned(16))) _Float16 kfs[2][CORR ? kBN * kFeat : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 qfs[CORR ? kBM * kFeat : 8];
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
+
   const int tid = threadIdx.x, L = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = L & 15, grp = L >> 4;
   const int n_units = gridDim.x;
@@ -392,13 +602,63 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
   const int tile = unit % a.q_tiles, bh = unit / a.q_tiles;
   const int hq = bh % a.Hq, b = bh / a.Hq;
   const int hk = hq / (a.Hq / a.Hkv);
+  const size_t plane = (size_t)b * a.Hkv + hk;
   const int q0 = tile * kBM + wave * 16 * kRG;
+  const bool kgroup = a.kcod.sel >= 1000;
+
+  // ---- codebooks to LDS (in the tile area, free until the first tile),
+  // one value a lane from the argument block; then the tables
+  constexpr int kCb = kMaxXi + kMaxRho;
+  float* cbs = reinterpret_cast<float*>(tiles);
+  {
+    // constant indices into the argument block (a run-time index would put
+    // a copy of it in private memory)
+    float ck = 0.0f, cv = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kCb; ++i) {
+      ck = tid == i ? (i < kMaxXi ? a.kcb.xi[i] : a.kcb.rho[i - kMaxXi]) : ck;
+      cv = tid == i ? (i < kMaxXi ? a.vcb.xi[i] : a.vcb.rho[i - kMaxXi]) : cv;
+    }
+    if (tid < kCb) {
+      cbs[tid] = ck;
+      cbs[kCb + tid] = cv;
+    }
+  }
   if constexpr (CORR) {
     // the workgroup's 64 query feature rows (rows past Tq repeat the last)
     for (int r = tid; r < kBM; r += kCThreads) {
       const int qrow = min(tile * kBM + r, a.Tq - 1);
       *reinterpret_cast<half8*>(&qfs[r * kFeat]) = *reinterpret_cast<const half8*>(
           a.qfeat + (((size_t)b * a.Hq + hq) * a.Tq + qrow) * kFeat);
+    }
+  }
+  __syncthreads();
+  {
+    const float *cxk = cbs, *crk = cbs + kMaxXi, *cxv = cbs + kCb, *crv = cbs + kCb + kMaxXi;
+    with_codec<KSEL>(a.kcod.sel, [&](auto cs) __attribute__((always_inline)) {
+      constexpr int C = decltype(cs)::value;
+      if constexpr (C < 1000) build_octo_table<C / 10, C % 10>(cxk, crk, dyn, a.kcod, tid);
+    });
+    if (!a.share_tab) {
+      with_codec<VSEL>(a.vcod.sel, [&](auto cs) __attribute__((always_inline)) {
+        constexpr int C = decltype(cs)::value;
+        if constexpr (C < 1000) build_octo_table<C / 10, C % 10>(cxv, crv, dyn, a.vcod, tid);
+      });
+    }
+  }
+  // fp16 pair (1024, 1024) in a register (for the group codec's integers)
+  uint32_t k1024;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k1024));
+
+  // ---- per-thread constants of the decoders: the byte offsets (buffer 0)
+  // of the four chunks of the thread's row part in the key and value tiles
+  int kw[4], vw[4];
+  {
+    const int kk = L & 31, pg = 2 * (L >> 5) + wave;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      kw[d] = kk * 256 + (((4 * pg + d) ^ (kk & 15)) << 4);
+      vw[d] = 2 * kKTileBytes + kk * kVRowBytes + 64 * pg + 16 * d;
     }
   }
 
@@ -411,195 +671,315 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[rg][s] = *reinterpret_cast<const half8*>(src + 32 * s + 8 * grp);
   }
-  floatx4 o[kRG][8];
+  floatx4 o[kRG][kOB];
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) o[rg][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  // of query q0 + 16 rg + col: running maximum (log2 units), and this
-  // lane's part of the normalizer
+    for (int c = 0; c < kOB; ++c) o[rg][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  // of query q0 + 16 rg + col: running maximum (log2 units; 0 until the
+  // first tile sets it), and this lane's part of the normalizer
   float m_run[kRG], l_run[kRG];
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg) {
-    m_run[rg] = -INFINITY;
+    m_run[rg] = 0.0f;
     l_run[rg] = 0.0f;
   }
 
-  const size_t kbase = ((size_t)b * a.Hkv + hk) * a.Tk_pad * kHeadDim;
-  const size_t vbase = ((size_t)b * a.Hkv + hk) * kHeadDim * a.Tk_pad;
-  // The tiles of K (kBN rows x 128 dims, contiguous) and V^T (128 rows x kBN
-  // keys) go straight from global memory to LDS: wavefront w issues
-  // instructions j < kTileInsts of each, lane L of instruction j filling
-  // stored chunk p = 64 (kTileInsts w + j) + L, i.e. row p / 16 (K) or
-  // p / kVChunks (V^T), whose logical chunk is the stored one xor the row's
-  // swizzle.  Every load of a tile is in flight at once and holds no registers.
-  static_assert(kCWaves * kTileInsts * 64 == kBN * kKChunks &&
-                    kCWaves * kTileInsts * 64 == kHeadDim * kVChunks,
-                "the wavefronts' instructions fill each tile");
-  // The swizzle of instruction j depends on j mod 4 (K) and j mod 2 (V^T):
-  // a lane keeps four and two source offsets, the rest are uniform steps.
-  uint32_t ksrc[4], vsrc[2];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = 64 * (kTileInsts * wave + j) + L;
-    const int kr = p / kKChunks, kc = (p % kKChunks) ^ (kr % kKChunks);
-    ksrc[j] = (uint32_t)((kr * kHeadDim + kc * 8) * 2);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int p = 64 * (kTileInsts * wave + j) + L;
-    const int vr = p / kVChunks, vc = (p % kVChunks) ^ ((vr / (16 / kVChunks)) % kVChunks);
-    vsrc[j] = (uint32_t)(vr * a.Tk_pad * 2 + vc * 16);
-  }
-  const int vstep = (128 / kVChunks) * a.Tk_pad * 2;   // two instructions' rows, in bytes
+  // the current chunk's rows and the packed cache of this plane (loads past
+  // a plane's range return zero)
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<_Float16*>(a.k + kbase), (short)0, a.Tk_pad * kHeadDim * 2, kBufferWord3);
+      const_cast<_Float16*>(a.kc + plane * a.Tc_pad * kHeadDim), (short)0,
+      a.Tc_pad * kHeadDim * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<_Float16*>(a.vt + vbase), (short)0, a.Tk_pad * kHeadDim * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<_Float16*>(CORR ? a.kfeat + ((size_t)b * a.Hkv + hk) * a.Tk_pad * kFeat : a.k),
-      (short)0, a.Tk_pad * kFeat * 2, kBufferWord3);
-  // Issues the loads of the tile at kt0 into (ks, vs, kfs); none is waited for here.
-  auto copy_tile = [&](int kt0, _Float16* ks, _Float16* vs, _Float16* kfs) {
+      const_cast<_Float16*>(a.vc + plane * a.Tc_pad * kVRowHalves), (short)0,
+      a.Tc_pad * kVRowBytes, kBufferWord3);
+  const int tiles64 = a.capacity >> 6;
+  const __amdgpu_buffer_rsrc_t kis = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(a.k_idx + plane * tiles64 * a.kcod.W * 64), (short)0,
+      a.capacity * a.kcod.W * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vis = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(a.v_idx + plane * tiles64 * a.vcod.W * 64), (short)0,
+      a.capacity * a.vcod.W * 4, kBufferWord3);
+  const bool vgroup = a.vcod.sel >= 1000;
+  const __amdgpu_buffer_rsrc_t kgs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(kgroup ? nullptr : a.k_gamma + plane * a.capacity), (short)0,
+      kgroup ? 0 : a.capacity * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vgs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(vgroup ? nullptr : a.v_gamma + plane * a.capacity), (short)0,
+      vgroup ? 0 : a.capacity * 4, kBufferWord3);
+
+  const int n_ct = (a.cached + kBN - 1) / kBN, n_rt = (a.Tc + kBN - 1) / kBN;
+  const int n_tiles = n_ct + n_rt;
+
+  // Words of cached tile u into registers (key part, value part).
+  auto load_words = [&](int u, uint32_t (&wk)[KW], uint32_t (&wv)[VW]) __attribute__((always_inline)) {
+    const int t0 = u * kBN;
+    // the codec's per-thread offsets are formed here from an opaque copy of
+    // the thread index, tile by tile, rather than kept live for every codec
+    int lt = tid;
+    asm volatile("" : "+v"(lt));
+    const int kk = lt & 31, pg = 2 * ((lt & 63) >> 5) + wave;
+    const bool valid = kk < a.cached - t0;
+    // byte offset of the tile's first token in word row 0 of a W-word plane
+    const int sk = (t0 >> 6) * a.kcod.W * 256 + (t0 & 63) * 4;
+    const int sv = (t0 >> 6) * a.vcod.W * 256 + (t0 & 63) * 4;
+    with_codec<KSEL>(a.kcod.sel, [&](auto cs) __attribute__((always_inline)) {
+      constexpr int C = decltype(cs)::value;
+      if constexpr (C < 1000) load_octo_row<C / 10, C % 10>(wk, kis, kgs, sk, t0, kk, pg, valid);
+      else load_group_row<(C - 1000) / 100, C % 100>(wk, kis, sk, kk, pg, valid);
+    });
+    with_codec<VSEL>(a.vcod.sel, [&](auto cs) __attribute__((always_inline)) {
+      constexpr int C = decltype(cs)::value;
+      if constexpr (C < 1000) load_octo_row<C / 10, C % 10>(wv, vis, vgs, sv, t0, kk, pg, valid);
+      else load_group_row<(C - 1000) / 100, C % 100>(wv, vis, sv, kk, pg, valid);
+    });
+  };
+  // Decodes cached tile u from its words into buffer S (= u % 2).  Keys past
+  // the window (in its ragged last tile) decode from whatever words follow
+  // it: their scores are masked, and their values are finite (their gammas
+  // or zero-points load as zero).
+  auto decode = [&](int u, auto stage, const uint32_t (&wk)[KW], const uint32_t (&wv)[VW]) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    int lt = tid;
+    asm volatile("" : "+v"(lt));
+    const int kk = lt & 31, hi = (lt & 63) >> 5, pg = 2 * hi + wave;
+    char* kt = tiles + S * kKTileBytes;
+    char* vt = tiles + S * kVTileBytes;          // vw holds the value tiles' offset
+    with_codec<KSEL>(a.kcod.sel, [&](auto cs) __attribute__((always_inline)) {
+      constexpr int C = decltype(cs)::value;
+      if constexpr (C < 1000) {
+        if (wave) dec_octo_row<C / 10, C % 10, 1, false>(wk, dyn, a.kcod, kt, kw, gks[S], kk, hi);
+        else dec_octo_row<C / 10, C % 10, 0, false>(wk, dyn, a.kcod, kt, kw, gks[S], kk, hi);
+      } else {
+        dec_group_row<(C - 1000) / 100, C % 100, CORR, false>(wk, kt, kw, gks[S], kfs[S], kk, pg, k1024);
+      }
+    });
+    with_codec<VSEL>(a.vcod.sel, [&](auto cs) __attribute__((always_inline)) {
+      constexpr int C = decltype(cs)::value;
+      if constexpr (C < 1000) {
+        if (wave) dec_octo_row<C / 10, C % 10, 1, true>(wv, dyn, a.vcod, vt, vw, nullptr, kk, hi);
+        else dec_octo_row<C / 10, C % 10, 0, true>(wv, dyn, a.vcod, vt, vw, nullptr, kk, hi);
+      } else {
+        dec_group_row<(C - 1000) / 100, C % 100, false, true>(wv, vt, vw, nullptr, nullptr, kk, pg, k1024);
+      }
+    });
+  };
+  // Requests the rows of current tile u into buffer S (= u % 2); nothing is
+  // waited for here.
+  auto request_rows = [&](int u, auto stage) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    const int kt0 = (u - n_ct) * kBN;
+    char* ks = tiles + S * kKTileBytes;
+    char* vs = tiles + 2 * kKTileBytes + S * kVTileBytes;
+    // source offsets, formed here (current tiles are few) rather than kept
+    // in registers across the loop
+    uint32_t lx = L;
+    asm volatile("" : "+v"(lx));
+    if (wave == 0 && lx < kBN) gks[S][lx] = 1.0f;     // the scores take no gamma
+    // key tile: lane L of instruction j fills stored chunk p = 64 (4 w + j) +
+    // L, row p / 16, logical chunk (p % 16) ^ (row % 16)
 #pragma unroll
-    for (int j = 0; j < kTileInsts; ++j) {
-      const int inst = kTileInsts * wave + j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, ks + 512 * inst, 16, ksrc[j & 3],
-                                               kt0 * kHeadDim * 2 + (j >> 2) * 4096, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vs + 512 * inst, 16, vsrc[j & 1],
-                                               kt0 * 2 + (j >> 1) * vstep, 0, 0);
+    for (int j = 0; j < kKTileInsts; ++j) {
+      const uint32_t p = 64 * (kKTileInsts * wave + j) + lx;
+      const uint32_t kr = p / kKChunks, kc = (p % kKChunks) ^ (kr % kKChunks);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, ks + 1024 * (kKTileInsts * wave + j), 16,
+                                               (kr * kHeadDim + kc * 8) * 2, kt0 * kHeadDim * 2, 0, 0);
     }
-    if constexpr (CORR) {
-      // the tile's key feature rows, a 16-byte row a lane of wavefront 0
-      if (wave == 0 && L < kBN)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(frs, kfs, 16, L * kFeat * 2, kt0 * kFeat * 2, 0, 0);
+    // value tile: the padded rows as they are, chunk p = 64 (5 w + j) + L
+#pragma unroll
+    for (int j = 0; j < kVTileInsts; ++j) {
+      const uint32_t p = 64 * (kVTileInsts * wave + j) + lx;
+      if (p < kVTileChunks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vs + 1024 * (kVTileInsts * wave + j), 16, p * 16,
+                                                 kt0 * kVRowBytes, 0, 0);
     }
   };
 
-  // One tile from LDS; only the last, ragged tile masks keys past Tk.
-  auto tile_step = [&](int kt0, auto masked_c, const _Float16* ks, const _Float16* vs,
-                       const _Float16* kfs) {
-    constexpr bool MASKED = decltype(masked_c)::value;
-    // scores of the tile's keys (log2 units): st[kt][rg][r] = key kt0 + 16 kt + 4 grp + r
+  // per-lane offsets of the key fragments of slice s (row col, logical chunk
+  // 4 s + grp, stored at chunk (4 s + grp) ^ col; row 16 kt + col adds 4096
+  // kt) and of the transposing value reads (row 4 grp + col / 4, coordinates
+  // 4 (col % 4) ..; the other four keys 16 rows on, block c 32 c bytes on)
+  int kfr[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) kfr[s] = col * 256 + (((4 * s + grp) ^ col) << 4);
+  const int vtr = (4 * grp + (col >> 2)) * kVRowBytes + 8 * (col & 3);
+  // One tile from buffer S.  The first tile sets the running maxima; only
+  // the ragged last tile of each segment masks keys.  (Both are uniform
+  // branches on the scores alone, so that one copy of the MFMA chains
+  // serves every tile.)
+  auto compute = [&](int u, auto stage) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    const bool cachedt = u < n_ct, first = u == 0;
+    const int nvalid = cachedt ? a.cached - u * kBN : a.Tc - (u - n_ct) * kBN;
+    const char* ks = tiles + S * kKTileBytes;
+    const char* vs = tiles + 2 * kKTileBytes + S * kVTileBytes;
+    // scores of the tile's keys (log2 units): st[kt][rg][r] = key 16 kt + 4 grp + r
     floatx4 st[kBN / 16][kRG];
     const half8 zero8 = {};
 #pragma unroll
     for (int kt = 0; kt < kBN / 16; ++kt) {
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      // key 16 kt + col (row swizzle col), logical chunk 4 s + grp
-      const _Float16* kr = &ks[(16 * kt + col) * kHeadDim];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const half8 kf = *reinterpret_cast<const half8*>(kr + 8 * ((4 * s + grp) ^ col));
+        const half8 kf = *reinterpret_cast<const half8*>(ks + 16 * kt * 256 + kfr[s]);
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg)
           st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[rg][s], st[kt][rg], 0, 0, 0);
       }
       if constexpr (CORR) {
-        // minus the Jensen bias of keys 16 kt + (0..15), in log2 units
-        // (slots 8..31 of both operands are zero: lane groups 1..3 read nothing)
-        half8 kf5 = zero8;
-        if (grp == 0) kf5 = *reinterpret_cast<const half8*>(&kfs[(16 * kt + col) * kFeat]);
+        if (cachedt) {
+          // minus the Jensen bias of keys 16 kt + (0..15), in log2 units
+          // (slots 8..31 of both operands are zero: lane groups 1..3 read nothing)
+          half8 kf5 = zero8;
+          if (grp == 0) kf5 = *reinterpret_cast<const half8*>(&kfs[S][(16 * kt + col) * kFeat]);
 #pragma unroll
-        for (int rg = 0; rg < kRG; ++rg) {
-          half8 qf5 = zero8;
-          if (grp == 0)
-            qf5 = *reinterpret_cast<const half8*>(&qfs[(wave * 16 * kRG + 16 * rg + col) * kFeat]);
-          st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf5, qf5, st[kt][rg], 0, 0, 0);
+          for (int rg = 0; rg < kRG; ++rg) {
+            half8 qf5 = zero8;
+            if (grp == 0)
+              qf5 = *reinterpret_cast<const half8*>(&qfs[(wave * 16 * kRG + 16 * rg + col) * kFeat]);
+            st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf5, qf5, st[kt][rg], 0, 0, 0);
+          }
         }
       }
     }
-    half8 pf[kRG][kBN / 32];
+    // x = gamma s - m in log2 units relative to the running maximum (0
+    // before the first tile): gamma in fp32 from gks for OCTOPUS keys of the
+    // window (the tile holds rho^ n^), 1 for every other tile
+    float x[kRG][kBN / 4];
+    float4 g4[kBN / 16];
+#pragma unroll
+    for (int kt = 0; kt < kBN / 16; ++kt) g4[kt] = *reinterpret_cast<const float4*>(&gks[S][16 * kt + 4 * grp]);
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
-      float x[kBN / 4];
-      float mx = -INFINITY;
+      const float mneg = -m_run[rg];
 #pragma unroll
       for (int e = 0; e < kBN / 4; ++e) {
         const int kt = e >> 2, r = e & 3;
-        x[e] = st[kt][rg][r];
-        if (MASKED && kt0 + 16 * kt + 4 * grp + r >= a.Tk) x[e] = -INFINITY;
-        mx = fmaxf(mx, x[e]);
+        const float g = r == 0 ? g4[kt].x : r == 1 ? g4[kt].y : r == 2 ? g4[kt].z : g4[kt].w;
+        x[rg][e] = fmaf(st[kt][rg][r], g, mneg);
       }
+    }
+    if (nvalid < kBN) {
+      // keys 16 kt + 4 grp + r past the segment (an opaque lane offset, so
+      // that no per-slot key index is kept in registers)
+      int k4 = 4 * grp;
+      asm volatile("" : "+v"(k4));
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg)
+#pragma unroll
+        for (int e = 0; e < kBN / 4; ++e)
+          if (16 * (e >> 2) + k4 + (e & 3) >= nvalid) x[rg][e] = -INFINITY;
+    }
+    // Lazy running maximum: a row moves its maximum (and rescales its sums)
+    // only when a score exceeds it by more than kLazyLog2 -- or on the first
+    // tile, which sets it -- so that nearly every tile skips the rescale;
+    // probabilities then stay below 2^kLazyLog2, well inside fp16, and the
+    // final 1/l cancels the shift.
+    float sh[kRG];
+    bool any = false;
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) {
+      float mx = x[rg][0];
+#pragma unroll
+      for (int e = 1; e < kBN / 4; ++e) mx = fmaxf(mx, x[rg][e]);
       mx = rows_max(mx);
-      // Lazy running maximum: a row moves its maximum (and rescales its sums)
-      // only when a score exceeds it by more than kLazyLog2, so that nearly
-      // every tile skips the rescale; probabilities then stay below
-      // 2^kLazyLog2, well inside fp16, and the final 1/l cancels the shift.
-      const bool up = mx > m_run[rg] + kLazyLog2;
-      if (__ballot(up)) {
-        const float m_new = up ? mx : m_run[rg];
-        const float alpha = up ? __builtin_amdgcn_exp2f(m_run[rg] - m_new) : 1.0f;
+      const bool up = first || mx > kLazyLog2;
+      sh[rg] = up ? mx : 0.0f;
+      any = any || __ballot(up) != 0;
+    }
+    // P (and its sums), then O += P V (value fragments by the transposing
+    // read).  Written out on both sides of the (uniform) rescale branch, so
+    // that the accumulators stay in place on either side.
+    auto pv = [&](auto shifted) __attribute__((always_inline)) {
+      constexpr bool SH = decltype(shifted)::value;
+      half8 pf[kRG];
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg) {
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kBN / 4; ++e) {
+          // the raw exp2 (flushing results below the normal range to zero) is
+          // exact enough next to the row's largest terms (at least 1)
+          const float p = __builtin_amdgcn_exp2f(SH ? x[rg][e] - sh[rg] : x[rg][e]);
+          ps += p;
+          pf[rg][e] = (_Float16)p;
+        }
+        l_run[rg] += ps;               // this lane's keys; rows are summed at the end
+      }
+#pragma unroll
+      for (int c = 0; c < kOB; ++c) {
+        typedef __attribute__((address_space(3))) short4v lds_short4;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vs + vtr + 32 * c));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4*)(vs + vtr + 16 * kVRowBytes + 32 * c));
+        const half8 vf = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg)
+          o[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg], vf, o[rg][c], 0, 0, 0);
+      }
+    };
+    if (any) {
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg) {
+        m_run[rg] += sh[rg];
+        // O rows (queries q0 + 16 rg + 4 grp + r) and the sums scale by
+        // 2^-shift; on the first tile (both 0, shift of either sign) by at
+        // most 1
+        const float alpha = __builtin_amdgcn_exp2f(-fmaxf(sh[rg], 0.0f));
         l_run[rg] *= alpha;
-        m_run[rg] = m_new;
-        // rescale O rows (queries q0 + 16 rg + 4 grp + r)
         float al[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
+        for (int c = 0; c < kOB; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[rg][c][r] *= al[r];
       }
-      float ps = 0.0f;
-#pragma unroll
-      for (int e = 0; e < kBN / 4; ++e) {
-        // the raw exp2 (flushing results below the normal range to zero) is
-        // exact enough next to the row's largest terms (at least 1)
-        const float p = __builtin_amdgcn_exp2f(x[e] - m_run[rg]);
-        ps += p;
-        pf[rg][e >> 3][e & 7] = (_Float16)p;
-      }
-      l_run[rg] += ps;                 // this lane's keys; rows are summed at the end
+      pv(std::true_type{});
+    } else {
+      pv(std::false_type{});
     }
-    // O += P V: slot e of sub-block sb is key kt0 + 32 sb + 16 (e / 4) + 4 grp + e % 4
-#pragma unroll
-    for (int sb = 0; sb < kBN / 32; ++sb)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        // value row 16 c + col, logical chunk 4 sb + grp
-        const int sw = (col / (16 / kVChunks)) % kVChunks;
-        const half8 vf = *reinterpret_cast<const half8*>(
-            &vs[(16 * c + col) * kBN + 8 * ((4 * sb + grp) ^ sw)]);
-#pragma unroll
-        for (int rg = 0; rg < kRG; ++rg)
-          o[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg][sb], vf, o[rg][c], 0, 0, 0);
-      }
   };
-  const int tk_full = a.Tk / kBN * kBN;
-  const int n_tiles = (a.Tk + kBN - 1) / kBN;
-  auto compute = [&](int t, const _Float16* ks, const _Float16* vs, const _Float16* kfs) {
-    if (t * kBN < tk_full)
-      tile_step(t * kBN, std::false_type{}, ks, vs, kfs);
-    else
-      tile_step(t * kBN, std::true_type{}, ks, vs, kfs);
-  };
-  // Tile t sits in buffer t % 2.  Tile t + 1 is requested before tile t's
-  // arithmetic and waited for after it, at the barrier (whose fence also
-  // waits for this wave's loads into LDS), which also frees buffer t % 2.
-  auto step = [&](int t, const _Float16* ks, const _Float16* vs, const _Float16* kfs,
-                  _Float16* nks, _Float16* nvs, _Float16* nkfs) {
-    if (t + 1 < n_tiles) copy_tile((t + 1) * kBN, nks, nvs, nkfs);
-    compute(t, ks, vs, kfs);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    lds_barrier();
-  };
-  if (n_tiles > 0) copy_tile(0, ks0, vs0, kfs0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  // ---- the tile pipeline: the words of cached tile u in registers of
+  // stage u % 2, requested two tiles ahead
+  uint32_t wk0[KW] = {}, wv0[VW] = {}, wk1[KW] = {}, wv1[VW] = {};
+  if (n_ct > 0) load_words(0, wk0, wv0);
+  if (n_ct > 1) load_words(1, wk1, wv1);
+  if (n_ct == 0 && n_tiles > 0) request_rows(0, std::integral_constant<int, 0>{});
+  lds_barrier();                       // tables built
+  if (n_ct > 0) decode(0, std::integral_constant<int, 0>{}, wk0, wv0);
+  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
   lds_barrier();
+  // iteration t, buffer and word stage S = t % 2
+  auto iter = [&](int t, auto stage, uint32_t (&wkS)[KW], uint32_t (&wvS)[VW],
+                  uint32_t (&wkN)[KW], uint32_t (&wvN)[VW]) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    using Next = std::integral_constant<int, 1 - S>;
+    if (t + 2 < n_ct) load_words(t + 2, wkS, wvS);
+    const bool next_cur = t + 1 >= n_ct && t + 1 < n_tiles;
+    if (next_cur) request_rows(t + 1, Next{});
+    compute(t, stage);
+    if (t + 1 < n_ct) decode(t + 1, Next{}, wkN, wvN);
+    else if (next_cur) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    tile_barrier();                    // tile t read by all; tile t + 1 in place
+  };
   for (int t = 0; t < n_tiles; t += 2) {
-    step(t, ks0, vs0, kfs0, ks1, vs1, kfs1);
-    if (t + 1 < n_tiles) step(t + 1, ks1, vs1, kfs1, ks0, vs0, kfs0);
+    iter(t, std::integral_constant<int, 0>{}, wk0, wv0, wk1, wv1);
+    if (t + 1 < n_tiles) iter(t + 1, std::integral_constant<int, 1>{}, wk1, wv1, wk0, wv0);
   }
 
-  // ---- epilogue: 1/l, then R_v^T = diag(s_v) H / sqrt(d) on every query row.
-  // Lane holds coordinate 16 c + col of queries q0 + 16 rg + 4 grp + r: the
-  // Hadamard butterflies on coordinate bits 4..6 are register-local, bits
-  // 0..3 cross lanes within each 16-lane group.
+  // ---- epilogue: 1/l; value columns back to coordinate order (OCTOPUS
+  // values, through LDS); then R_v^T = diag(s_v) H / sqrt(d) on every query
+  // row.  Lane holds coordinate 16 c + col of queries q0 + 16 rg + 4 grp +
+  // r: the Hadamard butterflies on coordinate bits 4..6 are register-local,
+  // bits 0..3 cross lanes within each 16-lane group.
   float sv[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) sv[c] = kInvSqrtD * splitmix_sign(a.vseed, 16 * c + col);
+  constexpr int kORow = kHeadDim + 4;                  // floats per query row in LDS
+  float* ob = reinterpret_cast<float*>(tiles) + wave * (16 * kRG * kORow);
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg) {
     const float l_tot = rows_sum(l_run[rg]);   // the row's four lane groups
@@ -609,11 +989,38 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
       const float l = __shfl(l_tot, 4 * grp + r, 64);
       li[r] = l > 0.0f ? 1.0f / l : 0.0f;
     }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[rg][c][r] *= li[r];
+  }
+  if (a.vperm) {
+    // column 16 c + col holds coordinate part_coord(16 c + col)
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int crd = part_coord(16 * c + col);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ob[(16 * rg + 4 * grp + r) * kORow + crd] = o[rg][c][r];
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[rg][c][r] = ob[(16 * rg + 4 * grp + r) * kORow + 16 * c + col];
+  }
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
     float v[8][4];
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[c][r] = o[rg][c][r] * li[r];
+      for (int r = 0; r < 4; ++r) v[c][r] = o[rg][c][r];
 #pragma unroll
     for (int m = 4; m >= 1; m >>= 1)
 #pragma unroll
@@ -646,158 +1053,70 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
   }
 }
 
-// The group-wise value codec: one workgroup per 64 cached tokens of a plane
-// stages their records (word w of the 64 tokens is 256 contiguous bytes) in
-// LDS, then thread (token, quarter) writes fp16(Delta code + z), the rotated
-// value, of its 32 coordinates into the tile stored as above.
-template <int VB, int GS, bool TRANSPOSED>
-__global__ __launch_bounds__(256) void group_decode_rows_kernel(const uint32_t* __restrict__ idx,
-                                                                int capacity, int cached,
-                                                                _Float16* __restrict__ out,
-                                                                int out_rows) {
-  constexpr int G = kHeadDim / GS, WC = VB * kHeadDim / 32, W = group_record_words(VB, GS);
-  using ST = StageTile<TRANSPOSED>;
-  __shared__ uint32_t rec[W * 64];
-  __shared__ __attribute__((aligned(16))) _Float16 tile[ST::kElems];
-  const int tid = threadIdx.x;
-  const size_t plane = blockIdx.y;
-  const int t0 = blockIdx.x * 64;
-  const int nt = min(64, cached - t0);
-  // every load of the staging goes out before the first LDS store
-  constexpr int kLoads = (W * 64 + 255) / 256;
-  uint32_t rv[kLoads];
-#pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
-    const int e = tid + 256 * j, w = e >> 6, k = e & 63;
-    rv[j] = e < W * 64 && k < nt ? idx[tile_word(plane, capacity, t0 + k, w, W)] : 0u;
-  }
-#pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
-    const int e = tid + 256 * j;
-    if (e < W * 64) rec[e] = rv[j];
-  }
-  __syncthreads();
-  // Thread (k, w): token k, coordinates 32 w .. 32 w + 31, whose codes fill
-  // words VB w .. VB w + VB - 1 of the record and whose groups' steps and
-  // zero points are decoded once.
-  static_assert(GS == 16 || GS == 32, "a thread's 32 coordinates span whole groups");
-  const int k = tid & 63, w = tid >> 6;
-  uint32_t cw[VB];
-#pragma unroll
-  for (int i = 0; i < VB; ++i) cw[i] = rec[(VB * w + i) * 64 + k];
-#pragma unroll
-  for (int gi = 0; gi < 32 / GS; ++gi) {
-    const int j = (32 / GS) * w + gi;
-    const uint32_t sw = rec[(WC + j / 4) * 64 + k], zw = rec[(WC + G / 4 + j / 2) * 64 + k];
-    const float dh = e4m3_value((sw >> (8 * (j % 4))) & 0xffu);
-    const float zh = __uint_as_float(((zw >> (16 * (j % 2))) & 0xffffu) << 16);
-#pragma unroll
-    for (int m = 0; m < GS; ++m) {
-      const int cl = GS * gi + m;
-      const uint32_t q = field<VB>(cw, cl * VB);
-      tile[ST::at(k, 32 * w + cl)] = (_Float16)fmaf(dh, (float)q, zh);
-    }
-  }
-  __syncthreads();
-  store_rows<TRANSPOSED>(tile, out, out_rows, plane, t0, nt);
-}
-
-// Key features of the Jensen-bias correction: row t < Tk_pad of a plane gets
-// Delta^_tj^2 / 16 in slot j < 128 / GS for the cached tokens (t < cached),
-// 0 elsewhere (current tokens, tile padding, unused slots).  The factor 1/16
-// keeps Delta^2 <= 448^2 in the fp16 range; the query features carry 16.
-template <int VB, int GS>
-__global__ __launch_bounds__(256) void key_features_kernel(const uint32_t* __restrict__ idx,
-                                                           int capacity, int cached, int Tk_pad,
-                                                           _Float16* __restrict__ feat) {
-  constexpr int G = kHeadDim / GS, WC = VB * kHeadDim / 32, W = group_record_words(VB, GS);
-  const size_t plane = blockIdx.y;
-  const int t0 = blockIdx.x * 64;
-  for (int e = threadIdx.x; e < 64 * kFeat; e += 256) {
-    const int t = t0 + e / kFeat, j = e % kFeat;
-    float f = 0.0f;
-    if (t < cached && j < G) {
-      const uint32_t sw = idx[tile_word(plane, capacity, t, WC + j / 4, W)];
-      const float dh = e4m3_value((sw >> (8 * (j % 4))) & 0xffu);
-      f = dh * dh * 0.0625f;
-    }
-    feat[(plane * Tk_pad + t) * kFeat + j] = (_Float16)f;
-  }
-}
-
 struct ChunkPlan {
-  int Tk, Tk_pad;
-  size_t q_off, k_off, v_off, qf_off, kf_off, total;
+  int Tc_pad;
+  size_t q_off, k_off, v_off, qf_off, total;
 };
 
-// corr: room for the correction's query and key feature rows after the rows
-ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Tq, int cached, int Tc, bool corr) {
+// Workspace: fp16 rotated queries, the current chunk's rotated key rows and
+// value rows (padded to whole tiles; value rows of kVRowHalves), and with the
+// correction the query features.  Nothing of the cached window is staged.
+ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Tq, int Tc, bool corr) {
   ChunkPlan p;
-  p.Tk = cached + Tc;
-  p.Tk_pad = (p.Tk + kPadKeys - 1) / kPadKeys * kPadKeys;
+  p.Tc_pad = (Tc + kCurPad - 1) / kCurPad * kCurPad;
   const size_t row = kHeadDim * sizeof(_Float16);
   auto up = [](size_t n) { return (n + 255) / 256 * 256; };
   p.q_off = 0;
   p.k_off = up((size_t)B * Hq * Tq * row);
-  const size_t kv = (size_t)B * Hkv * p.Tk_pad * row;
+  const size_t kv = (size_t)B * Hkv * p.Tc_pad * row;
   p.v_off = p.k_off + up(kv);
-  p.total = p.v_off + kv;
-  p.qf_off = p.kf_off = 0;
+  p.total = p.v_off + up((size_t)B * Hkv * p.Tc_pad * kVRowBytes);
+  p.qf_off = 0;
   if (corr) {
-    const size_t frow = kFeat * sizeof(_Float16);
-    p.qf_off = up(p.total);
-    p.kf_off = p.qf_off + up((size_t)B * Hq * Tq * frow);
-    p.total = p.kf_off + (size_t)B * Hkv * p.Tk_pad * frow;
+    p.qf_off = p.total;
+    p.total += (size_t)B * Hq * Tq * kFeat * sizeof(_Float16);
   }
   return p;
 }
 
-template <int BD, int BN>
-void launch_decode_rows(const octo_cache_view* c, const Codec& cd, int cached, _Float16* out,
-                        int out_rows, bool transposed, hipStream_t st) {
-  dim3 grid((cached + 63) / 64, c->batch * c->kv_heads);
-  if (transposed)
-    hipLaunchKernelGGL((decode_rows_kernel<BD, BN, true>), grid, dim3(256), 0, st, c->idx,
-                       c->gamma, cd.cb, c->capacity, cached, out, out_rows);
-  else
-    hipLaunchKernelGGL((decode_rows_kernel<BD, BN, false>), grid, dim3(256), 0, st, c->idx,
-                       c->gamma, cd.cb, c->capacity, cached, out, out_rows);
+// The kernel's view of a codec; its table space is assigned by the caller.
+ChunkCodec chunk_codec(const Codec& c) {
+  ChunkCodec k;
+  std::memset(&k, 0, sizeof(k));
+  k.sel = c.group ? 1000 + 100 * c.bits + c.group : 10 * c.b_dir + c.b_nrm;
+  k.W = c.w_idx;
+  return k;
 }
 
-template <int VB, int GS>
-void launch_group_rows(const octo_cache_view* c, int cached, _Float16* out, int out_rows,
-                       bool transposed, hipStream_t st) {
-  dim3 grid((cached + 63) / 64, c->batch * c->kv_heads);
-  if (transposed)
-    hipLaunchKernelGGL((group_decode_rows_kernel<VB, GS, true>), grid, dim3(256), 0, st, c->idx,
-                       c->capacity, cached, out, out_rows);
-  else
-    hipLaunchKernelGGL((group_decode_rows_kernel<VB, GS, false>), grid, dim3(256), 0, st, c->idx,
-                       c->capacity, cached, out, out_rows);
-}
-
-bool decode_rows(const octo_cache_view* c, const Codec& cd, int cached, _Float16* out,
-                 int out_rows, bool transposed, hipStream_t st) {
-  if (cd.group) {
-    switch (cd.bits * 100 + cd.group) {
-      case 216: launch_group_rows<2, 16>(c, cached, out, out_rows, transposed, st); return true;
-      case 232: launch_group_rows<2, 32>(c, cached, out, out_rows, transposed, st); return true;
-      case 316: launch_group_rows<3, 16>(c, cached, out, out_rows, transposed, st); return true;
-      case 332: launch_group_rows<3, 32>(c, cached, out, out_rows, transposed, st); return true;
-      case 416: launch_group_rows<4, 16>(c, cached, out, out_rows, transposed, st); return true;
-      case 432: launch_group_rows<4, 32>(c, cached, out, out_rows, transposed, st); return true;
+// The attention kernel for a codec pair: compiled for the pair when keys and
+// values use the same codec (the common case: the word registers and the
+// decoders are then fixed), else the one that chooses the codecs at run time.
+const void* chunk_kernel(bool corr, int ksel, int vsel) {
+  if (ksel == vsel) {
+#define K_(C, S) case S: return reinterpret_cast<const void*>(&chunk_attn_kernel<C, S, S>);
+    if (corr) {
+      switch (ksel) { K_(true, 1216) K_(true, 1232) K_(true, 1316) K_(true, 1332) K_(true, 1416) K_(true, 1432) }
+    } else {
+      switch (ksel) {
+        K_(false, 31) K_(false, 42) K_(false, 53) K_(false, 22) K_(false, 33) K_(false, 44)
+        K_(false, 1216) K_(false, 1232) K_(false, 1316) K_(false, 1332) K_(false, 1416) K_(false, 1432)
+      }
     }
-    return false;
+#undef K_
   }
-  switch (cd.b_dir * 10 + cd.b_nrm) {
-    case 31: launch_decode_rows<3, 1>(c, cd, cached, out, out_rows, transposed, st); return true;
-    case 42: launch_decode_rows<4, 2>(c, cd, cached, out, out_rows, transposed, st); return true;
-    case 53: launch_decode_rows<5, 3>(c, cd, cached, out, out_rows, transposed, st); return true;
-    case 22: launch_decode_rows<2, 2>(c, cd, cached, out, out_rows, transposed, st); return true;
-    case 33: launch_decode_rows<3, 3>(c, cd, cached, out, out_rows, transposed, st); return true;
-    case 44: launch_decode_rows<4, 4>(c, cd, cached, out, out_rows, transposed, st); return true;
+  return corr ? reinterpret_cast<const void*>(&chunk_attn_kernel<true, 0, 0>)
+              : reinterpret_cast<const void*>(&chunk_attn_kernel<false, 0, 0>);
+}
+
+// LDS bytes of an OCTOPUS codec's table (and rho pairs).
+int table_bytes(const Codec& c, int* rho_off) {
+  const int KK = c.K * c.K;
+  if (KK * c.R <= kMaxPre) {
+    *rho_off = KK * c.R * 8;
+    return KK * c.R * 8;
   }
-  return false;
+  *rho_off = KK * 8;
+  return KK * 8 + c.R * 4;
 }
 
 }  // namespace
@@ -818,8 +1137,7 @@ extern "C" octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec
   if (!bytes) return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_chunk_workspace_bytes: bytes is NULL");
   if (B < 1 || num_q_heads < 1 || kv_heads < 1 || Tq < 0 || cached_tokens < 0 || Tc < 0)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "octo_chunk_workspace_bytes: bad sizes");
-  *bytes = chunk_plan(B, num_q_heads, kv_heads, Tq, cached_tokens, Tc,
-                      (flags & OCTO_CHUNK_JENSEN_CORRECTION) != 0).total;
+  *bytes = chunk_plan(B, num_q_heads, kv_heads, Tq, Tc, (flags & OCTO_CHUNK_JENSEN_CORRECTION) != 0).total;
   return OCTO_OK;
 }
 
@@ -867,12 +1185,12 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   // the rows are read 16 bytes a lane
   if (((uintptr_t)q | (uintptr_t)k_cur | (uintptr_t)v_cur) & 15 || ((uintptr_t)out & 3))
     return fail(OCTO_ERR_ALIGNMENT, "%s: q, k_cur, v_cur (16 bytes) or out (4) misaligned", what);
-  const ChunkPlan p = chunk_plan(B, num_q_heads, Hkv, Tq, cached_tokens, Tc, corr);
-  // the attention kernel addresses a plane's staged keys and values through
-  // buffer descriptors with 32-bit byte ranges
-  if ((int64_t)p.Tk_pad * kHeadDim * 2 > INT32_MAX)
-    return fail(OCTO_ERR_UNSUPPORTED, "%s: %d keys a plane exceed 2 GiB of staged rows", what,
-                p.Tk_pad);
+  const ChunkPlan p = chunk_plan(B, num_q_heads, Hkv, Tq, Tc, corr);
+  // buffer descriptors address a plane's current rows and packed streams
+  // with 32-bit byte ranges
+  if ((int64_t)p.Tc_pad * kVRowBytes > INT32_MAX ||
+      (int64_t)k_cache->capacity * std::max(kc.w_idx, vc.w_idx) * 4 > INT32_MAX)
+    return fail(OCTO_ERR_UNSUPPORTED, "%s: a plane's rows or packed streams exceed 2 GiB", what);
   if (!workspace || workspace_bytes < p.total)
     return fail(OCTO_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", what,
                 workspace_bytes, p.total);
@@ -884,67 +1202,81 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   _Float16* kr = reinterpret_cast<_Float16*>(ws + p.k_off);
   _Float16* vr = reinterpret_cast<_Float16*>(ws + p.v_off);
   const int planes_q = B * num_q_heads, planes_kv = B * Hkv;
+  // coordinates in part order for tensors in the OCTOPUS codec (queries and
+  // current keys follow the keys' codec)
+  const int kperm = kc.group ? 0 : 1, vperm = vc.group ? 0 : 1;
 
   const float tau = softmax_scale > 0.0f ? softmax_scale : kInvSqrtD;
   const float scale2 = tau * kLog2e;
   _Float16* qf = corr ? reinterpret_cast<_Float16*>(ws + p.qf_off) : nullptr;
-  _Float16* kf = corr ? reinterpret_cast<_Float16*>(ws + p.kf_off) : nullptr;
   // query features: minus 16 log2(e) tau^2 / 24 ||(R q)_j||^2 (the key
   // features carry Delta^2 / 16), so that their product is -b in log2 units
   const float feat_c = -16.0f * kLog2e * tau * tau / 24.0f;
   RotJob jq{static_cast<const uint16_t*>(q), Tq, Tq, kc.seed, kInvSqrtD * scale2, qr, Tq, 0,
-            qf, corr ? kc.group : 32, feat_c, (Tq + 63) / 64, planes_q};
-  const int cur_out = p.Tk_pad - cached_tokens;  // current rows plus the zero tile padding
-  const int cur_tiles = cur_out > 0 ? (cur_out + 63) / 64 : 0;
-  RotJob jk{static_cast<const uint16_t*>(k_cur), Tc, cur_out, kc.seed, kInvSqrtD, kr, p.Tk_pad,
-            cached_tokens, nullptr, 32, 0.0f, cur_tiles, planes_kv};
-  RotJob jv{static_cast<const uint16_t*>(v_cur), Tc, cur_out, vc.seed, kInvSqrtD, vr, p.Tk_pad,
-            cached_tokens, nullptr, 32, 0.0f, cur_tiles, planes_kv};
-  const long rot_blocks = (long)jq.tiles * jq.planes + 2L * cur_tiles * planes_kv;
+            kHeadDim, qf, corr ? kc.group : 32, feat_c, (Tq + 63) / 64, planes_q, kperm};
+  const int cur_tiles = (p.Tc_pad + 63) / 64;
+  RotJob jk{static_cast<const uint16_t*>(k_cur), Tc, p.Tc_pad, kc.seed, kInvSqrtD, kr, p.Tc_pad,
+            0, kHeadDim, nullptr, 32, 0.0f, Tc > 0 ? cur_tiles : 0, planes_kv, kperm};
+  RotJob jv{static_cast<const uint16_t*>(v_cur), Tc, p.Tc_pad, vc.seed, kInvSqrtD, vr, p.Tc_pad,
+            0, kVRowHalves, nullptr, 32, 0.0f, Tc > 0 ? cur_tiles : 0, planes_kv, vperm};
+  const long rot_blocks = (long)jq.tiles * jq.planes + (long)jk.tiles * planes_kv * 2;
   if (rot_blocks > 0)
     hipLaunchKernelGGL(rotate_rows_kernel, dim3((unsigned)rot_blocks), dim3(256), 0, stream, jq, jk, jv);
-  if (cached_tokens > 0) {
-    if (!decode_rows(k_cache, kc, cached_tokens, kr, p.Tk_pad, false, stream) ||
-        !decode_rows(v_cache, vc, cached_tokens, vr, p.Tk_pad, true, stream))
-      return fail(OCTO_ERR_UNSUPPORTED, "%s: split not compiled", what);
-  }
-  if (corr && p.Tk_pad > 0) {
-    const dim3 fgrid(p.Tk_pad / 64, planes_kv);
-    switch (kc.bits * 100 + kc.group) {
-#define OCTO_KEY_FEATURES(VB, GS)                                                            \
-  hipLaunchKernelGGL((key_features_kernel<VB, GS>), fgrid, dim3(256), 0, stream, k_cache->idx, \
-                     k_cache->capacity, cached_tokens, p.Tk_pad, kf)
-      case 216: OCTO_KEY_FEATURES(2, 16); break;
-      case 232: OCTO_KEY_FEATURES(2, 32); break;
-      case 316: OCTO_KEY_FEATURES(3, 16); break;
-      case 332: OCTO_KEY_FEATURES(3, 32); break;
-      case 416: OCTO_KEY_FEATURES(4, 16); break;
-      case 432: OCTO_KEY_FEATURES(4, 32); break;
-#undef OCTO_KEY_FEATURES
-      default: return fail(OCTO_ERR_UNSUPPORTED, "%s: group codec not compiled", what);
-    }
-  }
   if ((s = check_launch(what)) != OCTO_OK) return s;
+
   ChunkArgs a;
+  std::memset(&a, 0, sizeof(a));
   a.q = qr;
-  a.k = kr;
-  a.vt = vr;
+  a.kc = kr;
+  a.vc = vr;
   a.out = out;
   a.Hq = num_q_heads;
   a.Hkv = Hkv;
   a.Tq = Tq;
-  a.Tk = p.Tk;
-  a.Tk_pad = p.Tk_pad;
   a.q_tiles = (Tq + kBM - 1) / kBM;
+  a.cached = cached_tokens;
+  a.Tc = Tc;
+  a.Tc_pad = p.Tc_pad;
+  a.capacity = k_cache->capacity;
   a.vseed = vc.seed;
   a.qfeat = qf;
-  a.kfeat = kf;
+  a.k_idx = k_cache->idx;
+  a.v_idx = v_cache->idx;
+  a.k_gamma = k_cache->gamma;
+  a.v_gamma = v_cache->gamma;
+  a.kcod = chunk_codec(kc);
+  a.vcod = chunk_codec(vc);
+  a.vperm = vperm;
+  a.kcb = kc.cb;
+  a.vcb = vc.cb;
+  // dynamic LDS: the tables (OCTOPUS codecs)
+  int off = 0;
+  a.share_tab = !kc.group && !vc.group && kc.b_dir == vc.b_dir && kc.b_nrm == vc.b_nrm &&
+                std::memcmp(&kc.cb, &vc.cb, sizeof(Codebook)) == 0;
+  if (!kc.group) {
+    int rho;
+    a.kcod.tab = off;
+    off += table_bytes(kc, &rho);
+    a.kcod.rho = a.kcod.tab + rho;
+  }
+  if (!vc.group) {
+    if (a.share_tab) {
+      a.vcod.tab = a.kcod.tab;
+      a.vcod.rho = a.kcod.rho;
+    } else {
+      int rho;
+      a.vcod.tab = (off + 7) / 8 * 8;
+      off = a.vcod.tab + table_bytes(vc, &rho);
+      a.vcod.rho = a.vcod.tab + rho;
+    }
+  }
+  const size_t dyn_bytes = (size_t)(off + 15) / 16 * 16;
   const long long units = (long long)a.q_tiles * num_q_heads * B;
   if (units > 0x7fffffffLL)
     return fail(OCTO_ERR_UNSUPPORTED, "%s: too many query tiles", what);
-  if (corr)
-    hipLaunchKernelGGL(chunk_attn_kernel<true>, dim3((unsigned)units), dim3(kCThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(chunk_attn_kernel<false>, dim3((unsigned)units), dim3(kCThreads), 0, stream, a);
+  void* kargs[] = {&a};
+  const hipError_t e = hipLaunchKernel(chunk_kernel(corr, a.kcod.sel, a.vcod.sel), dim3((unsigned)units),
+                                       dim3(kCThreads), kargs, dyn_bytes, stream);
+  if (e != hipSuccess) return fail(OCTO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return check_launch(what);
 }

@@ -219,11 +219,17 @@ def test_chunk_errors(L):
     n = ctypes.c_size_t()
     assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 0, ctypes.byref(n)) == 0
     need = n.value
-    # fp16 rotated queries [1, 2, 64, 128] and key / value rows [1, 2, 192, 128]
-    assert need == (64 * 2 + 2 * 2 * 192) * 256
-    # the correction adds 8 fp16 features per query row and per key row
+    # fp16 rotated queries [1, 2, 64, 128], the current chunk's key rows
+    # [1, 2, 64, 128] and value rows [1, 2, 64, 144] (padded rows); the
+    # cached window is decoded inside the kernel
+    assert need == (64 * 2 + 2 * 64) * 256 + 2 * 64 * 288
+    # the same with 128 cached tokens more: nothing of the window is staged
+    assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 256, 64, 0, ctypes.byref(n)) == 0
+    assert n.value == need
+    # the correction adds 8 fp16 features per query row (the key features are
+    # formed in the kernel)
     assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 1, ctypes.byref(n)) == 0
-    assert n.value == need + 64 * 2 * 16 + 2 * 192 * 16
+    assert n.value == need + 64 * 2 * 16
     assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 2, ctypes.byref(n)) == 1
 
     def ch(kd=kd, vd=vd, kv=kv, vv=vv, cached=128, Hq=2, Tq=64, Tc=64, ws=4096, ws_bytes=need,
@@ -242,9 +248,11 @@ def test_chunk_errors(L):
     assert ch(Tq=0) == 0                                     # nothing to do
     assert ch(flags=4) == 1                                  # unknown flag
     assert ch(flags=1) == 2                                  # correction with OCTOPUS keys
-    # staged rows of a plane beyond 2 GiB (2^23 keys x 256 B): unsupported
-    big = view(H=2, cap=1 << 23)
-    assert ch(kv=big, vv=big, cached=(1 << 23) - 64, Tc=64, ws_bytes=1 << 62) == 2
+    # a plane's current value rows beyond 2 GiB (2^23 keys x 288 B): unsupported
+    assert ch(Tc=1 << 23, ws_bytes=1 << 62) == 2
+    # a plane's packed stream beyond 2 GiB (2^26 tokens x 9 words x 4 B): unsupported
+    big = view(H=2, cap=1 << 26)
+    assert ch(kv=big, vv=big, cached=1 << 20, Tc=64, ws_bytes=1 << 62) == 2
 
 
 def gdesc(bits=2, group=32, b_dir=0, b_nrm=0, qjl=0):
