@@ -313,8 +313,10 @@ octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B
  * h / (num_q_heads / kv_heads).  QK^T and PV run on MFMA with fp16 operands
  * and fp32 accumulation, everything in the rotated frames: R_k q, R_k k_cur,
  * R_v v_cur and gamma u^ of the cached tokens (Eq. 13); the epilogue applies
- * R_v^T.  The workspace receives the fp16 rotated queries and the fp16
- * rotated key and value rows of the whole window (cached then current).
+ * R_v^T.  The cached window is decoded inside the attention kernel, tile by
+ * tile, into on-chip memory: it is read once per query tile as packed words
+ * and never written out.  The workspace receives only the fp16 rotated
+ * queries and the fp16 rotated key and value rows of the current chunk.
  *   q          device bf16 [B, num_q_heads, Tq, d] contiguous, 16-byte aligned.
  *   k_cur,v_cur device bf16 [B, kv_heads, Tc, d] contiguous, 16-byte aligned
  *              (may be NULL if Tc == 0).
@@ -324,12 +326,13 @@ octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B
  * codec, any b and g.  flags: 0 or OCTO_CHUNK_JENSEN_CORRECTION (above; the
  * bias is one more MFMA k-slice per 16 keys, the product of fp16 query
  * features -16 log2(e) tau^2/24 ||(R q)_j||^2 and key features Delta_j^2/16,
- * so it shares the fp16 range limits below).  Operand range and precision: the
- * fp16 staging requires |rotated entries| < 65504 and rounds each operand to
- * 11 significant bits, so this path is meant for inputs without large
- * outlier channels (the decode path computes in fp32).  Tq == 0 is a no-op;
- * an empty window gives zero output rows.  A window whose staged rows exceed
- * 2 GiB a plane (cached_tokens + Tc, rounded up to 64, times 256 bytes)
+ * so it shares the fp16 range limits below).  Operand range and precision:
+ * the fp16 operands require |rotated entries| < 65504 (for cached values,
+ * gamma rho^ < 65504) and round each operand to 11 significant bits, so this
+ * path is meant for inputs without large outlier channels (the decode path
+ * computes in fp32).  Tq == 0 is a no-op; an empty window gives zero output
+ * rows.  A plane whose current value rows (Tc rounded up to 32, times 288
+ * bytes) or packed records (capacity times record bytes) exceed 2 GiB
  * returns OCTO_ERR_UNSUPPORTED.                                            */
 octo_status octo_attend_chunk(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
                               const octo_cache_view* k_cache, const octo_cache_view* v_cache,

@@ -13,14 +13,14 @@
 // R_v^T applied to the softmax-weighted rotated values.
 //
 // Launches on one stream:
-//   1. rotate_rows (x3): q, k_cur -> fp16 rotated rows; v_cur -> fp16 rotated
-//      columns of the transposed value matrix
-//   2. decode_rows (x2): cached keys -> fp16 gamma u^ rows; cached values ->
-//      columns of the transposed value matrix (with the group-wise value
-//      codec, Delta code + z, already the rotated value)
-//   3. chunk_attn: fp16 MFMA flash attention (fp32 accumulation, online
-//      softmax), epilogue 1/l and R_v^T; XCD-aware workgroup order.
-// The window is decoded once per call and shared by every query tile.
+//   1. rotate_rows (x3): q, k_cur, v_cur -> fp16 rotated rows (coordinates in
+//      part order for tensors in the OCTOPUS codec, see part_pos)
+//   2. chunk_attn: fp16 MFMA flash attention (fp32 accumulation, online
+//      softmax) whose threads decode the cached window tile by tile from
+//      the packed records into LDS; epilogue 1/l and R_v^T; XCD-aware
+//      workgroup order.
+// The cached window is never written out: each query tile reads its packed
+// records (a few bytes a coordinate) and decodes them on chip.
 #include <math.h>
 
 #include <algorithm>
