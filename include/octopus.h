@@ -26,7 +26,11 @@
  *     splits {(2,2), (3,3), (4,4)}; for decode, 1 to 16 query heads per KV
  *     head; QJL on keys only, in the decode path only; the group-wise codec
  *     (group 16 or 32, b = 2, 3, 4; described below) for values, and for
- *     keys in the chunk path.  Anything else returns OCTO_ERR_UNSUPPORTED.
+ *     keys in the chunk path.  octo_encode, octo_decode_tokens and
+ *     octo_record_sizes also take the other splits of the (b + delta,
+ *     b - delta) sweep of Sec. 3.3 (b = 2, 3, 4; delta = -2 .. 2, so b_dir and
+ *     b_nrm from 0 to 6), for quality measurement; the attention entry points
+ *     do not.  Anything else returns OCTO_ERR_UNSUPPORTED.
  *
  * Cache layout (OCTO_LAYOUT_TILE64).  The paper fixes no bit layout; this one
  * is this library's.  A stream is a little-endian LSB-first bit string: field

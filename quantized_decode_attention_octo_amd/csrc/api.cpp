@@ -24,7 +24,7 @@ octo_status fail(octo_status s, const char* fmt, ...) {
 
 void clear_error() { g_msg[0] = 0; }
 
-// The splits the kernels are compiled for: the paper's (b+1, b-1) default for
+// The splits every kernel is compiled for: the paper's (b+1, b-1) default for
 // b = 2, 3, 4 (Sec. 3.3, 3.4: at most 32 + 8 centroids) and the uniform (b, b)
 // reference for the same b.
 static bool split_supported(int bd, int bn) {
@@ -34,8 +34,16 @@ static bool split_supported(int bd, int bn) {
   return false;
 }
 
+// The rest of the (b + delta, b - delta) sweep of Sec. 3.3 (Empirical
+// verification: b = 2, 3, 4, delta = -2 .. 2), for the encoder and the
+// explicit reconstruction only.
+static bool sweep_split(int bd, int bn) {
+  const int b = (bd + bn) / 2, delta = bd - b;
+  return (bd + bn) % 2 == 0 && b >= 2 && b <= 4 && delta >= -2 && delta <= 2;
+}
+
 octo_status resolve_codec(const octo_codec_desc* d, const char* what, Codec* out,
-                          bool need_tables) {
+                          bool need_tables, bool any_split) {
   if (!d) return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: codec descriptor is NULL", what);
   if (d->abi_version != OCTO_ABI_VERSION)
     return fail(OCTO_ERR_VERSION, "%s: descriptor abi_version %u, library %u", what,
@@ -77,30 +85,36 @@ octo_status resolve_codec(const octo_codec_desc* d, const char* what, Codec* out
   }
   if (bd < 0 || bn < 0 || bd > 8 || bn > 8)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: split (%d, %d) out of range", what, bd, bn);
-  if (!split_supported(bd, bn))
+  if (!split_supported(bd, bn) && !(any_split && sweep_split(bd, bn)))
     return fail(OCTO_ERR_UNSUPPORTED, "%s: split (b_dir %d, b_nrm %d) not compiled", what, bd, bn);
   if (d->rounding != OCTO_ROUND_LOCAL3X3 && d->rounding != OCTO_ROUND_SCALAR)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: rounding %d unknown", what, d->rounding);
   if (d->qjl != 0 && d->qjl != 1)
     return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: qjl must be 0 or 1", what);
   Codebook cb;
+  WideCodebook wcb;
   std::memset(&cb, 0, sizeof(cb));
+  std::memset(&wcb, 0, sizeof(wcb));
   if (need_tables) {
     if (!d->c_xi || !d->c_rho)
       return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: codebook pointer is NULL", what);
     if (((uintptr_t)d->c_xi | (uintptr_t)d->c_rho) & 3)
       return fail(OCTO_ERR_ALIGNMENT, "%s: codebooks must be 4-byte aligned", what);
-    std::memcpy(cb.xi, d->c_xi, sizeof(float) << bd);
-    std::memcpy(cb.rho, d->c_rho, sizeof(float) << bn);
+    std::memcpy(wcb.xi, d->c_xi, sizeof(float) << bd);
+    std::memcpy(wcb.rho, d->c_rho, sizeof(float) << bn);
     for (int i = 0; i < (1 << bd); ++i)
-      if (!std::isfinite(cb.xi[i]) || (i > 0 && !(cb.xi[i] > cb.xi[i - 1])))
+      if (!std::isfinite(wcb.xi[i]) || (i > 0 && !(wcb.xi[i] > wcb.xi[i - 1])))
         return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: c_xi is not finite and ascending", what);
     for (int i = 0; i < (1 << bn); ++i)
-      if (!std::isfinite(cb.rho[i]) || (i > 0 && !(cb.rho[i] > cb.rho[i - 1])))
+      if (!std::isfinite(wcb.rho[i]) || (i > 0 && !(wcb.rho[i] > wcb.rho[i - 1])))
         return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: c_rho is not finite and ascending", what);
+    if (bd <= 5 && bn <= 4) {
+      std::memcpy(cb.xi, wcb.xi, sizeof(float) << bd);
+      std::memcpy(cb.rho, wcb.rho, sizeof(float) << bn);
+    }
   }
   out->group = 0;
-  out->bits = bd == bn ? bd : bd - 1;
+  out->bits = (bd + bn) / 2;
   out->b_dir = bd;
   out->b_nrm = bn;
   out->K = 1 << bd;
@@ -111,6 +125,7 @@ octo_status resolve_codec(const octo_codec_desc* d, const char* what, Codec* out
   out->rounding = d->rounding;
   out->seed = d->seed;
   out->cb = cb;
+  out->wcb = wcb;
   return OCTO_OK;
 }
 
@@ -168,7 +183,7 @@ octo_status octo_record_sizes(const octo_codec_desc* codec, octo_stream_sizes* o
   octo::clear_error();
   if (!out) return octo::fail(OCTO_ERR_INVALID_ARGUMENT, "octo_record_sizes: out is NULL");
   octo::Codec c;
-  octo_status s = octo::resolve_codec(codec, "octo_record_sizes", &c, false);
+  octo_status s = octo::resolve_codec(codec, "octo_record_sizes", &c, false, true);
   if (s != OCTO_OK) return s;
   out->idx_words = c.w_idx;
   out->qjl_words = c.w_qjl;

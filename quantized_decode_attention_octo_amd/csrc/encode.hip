@@ -44,7 +44,7 @@ struct EncodeArgs {
   int64_t s0, s1, s2;             // element strides of b, h, t
   int is_bf16, vec16;             // vec16: every row starts 16-byte aligned
   int B, H, T;
-  Codebook cb;                    // C_xi, C_rho values
+  WideCodebook cb;                // C_xi, C_rho values
   uint64_t seed;
   int qjl, rounding;
   uint32_t* idx;                  // index stream, one B_tri-bit field per triplet
@@ -456,7 +456,7 @@ extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, 
   using namespace octo;
   clear_error();
   Codec c;
-  octo_status s = resolve_codec(codec, "octo_encode", &c);
+  octo_status s = resolve_codec(codec, "octo_encode", &c, true, true);
   if (s != OCTO_OK) return s;
   if ((s = check_cache(dst, c, "octo_encode dst")) != OCTO_OK) return s;
   if (x_dtype != OCTO_DTYPE_F32 && x_dtype != OCTO_DTYPE_BF16)
@@ -491,7 +491,7 @@ extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, 
   a.B = B;
   a.H = H;
   a.T = T;
-  a.cb = c.cb;
+  a.cb = c.wcb;
   a.seed = c.seed;
   a.qjl = c.qjl;
   a.rounding = c.rounding;
@@ -520,6 +520,16 @@ extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, 
     case 22: launch<2, 2>(a, stream); break;
     case 33: launch<3, 3>(a, stream); break;
     case 44: launch<4, 4>(a, stream); break;
+    // the rest of the (b + delta, b - delta) sweep (Sec. 3.3)
+    case 4: launch<0, 4>(a, stream); break;
+    case 15: launch<1, 5>(a, stream); break;
+    case 26: launch<2, 6>(a, stream); break;
+    case 13: launch<1, 3>(a, stream); break;
+    case 24: launch<2, 4>(a, stream); break;
+    case 35: launch<3, 5>(a, stream); break;
+    case 40: launch<4, 0>(a, stream); break;
+    case 51: launch<5, 1>(a, stream); break;
+    case 62: launch<6, 2>(a, stream); break;
     default: return fail(OCTO_ERR_UNSUPPORTED, "octo_encode: split not compiled");
   }
   return check_launch("octo_encode");

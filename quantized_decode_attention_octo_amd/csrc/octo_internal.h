@@ -32,13 +32,21 @@ struct Codebook {
   float xi[kMaxXi];
   float rho[kMaxRho];
 };
+// The same for the encoder and the explicit reconstruction, which also take
+// the splits of the (b + delta, b - delta) sweep (Sec. 3.3), up to 2^6
+// centroids on either side.
+constexpr int kMaxWide = 64;
+struct WideCodebook {
+  float xi[kMaxWide];
+  float rho[kMaxWide];
+};
 
 // A codec with its bit split resolved (Sec. 3.3: B_tri = 2 b_dir + b_nrm),
 // or the group-wise value codec (group = 16 or 32; b_dir = b_nrm = 0).
 struct Codec {
   int group;            // 0: OCTOPUS; else the group size g of the value codec
-  int bits;             // b of the group codec (the OCTOPUS codec: b_dir - 1
-                        // for the (b+1, b-1) split, b_dir for the uniform one)
+  int bits;             // b of the group codec (the OCTOPUS codec: the mean
+                        // (b_dir + b_nrm) / 2, b of a (b + delta, b - delta) split)
   int b_dir, b_nrm;     // bits per octahedral coordinate / per triplet norm
   int K;                // 2^b_dir entries of C_xi
   int R;                // 2^b_nrm entries of C_rho
@@ -47,6 +55,8 @@ struct Codec {
   int rounding;
   uint64_t seed;
   Codebook cb;          // the C_xi, C_rho values read from the descriptor
+                        // (splits the attention kernels take)
+  WideCodebook wcb;     // the same, for any split the encoder takes
 };
 
 // ---------------------------------------------------------------- host side
@@ -56,8 +66,10 @@ void clear_error();
 // Validates a descriptor and resolves its split; nothing on the device is read.
 // need_tables: the codebook pointers must be set and are read (every compute
 // entry point): finite, ascending values.
+// any_split: also the splits of the (b + delta, b - delta) sweep that only the
+// encoder and the explicit reconstruction are compiled for.
 octo_status resolve_codec(const octo_codec_desc* desc, const char* what, Codec* out,
-                          bool need_tables = true);
+                          bool need_tables = true, bool any_split = false);
 // Validates a cache view against a codec (pointers, sizes, alignment).
 octo_status check_cache(const octo_cache_view* v, const Codec& c, const char* what);
 // Maps the last HIP launch error to OCTO_ERR_HIP.

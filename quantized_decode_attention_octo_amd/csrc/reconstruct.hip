@@ -28,7 +28,7 @@ constexpr float kInvSqrtD = 0.08838834764831845f;
 struct ReconArgs {
   const uint32_t* idx;
   const float* gamma;
-  Codebook cb;
+  WideCodebook cb;
   uint64_t seed;
   int B, H, capacity, t0, T;
   float* out;                          // [B][H][T][128]
@@ -135,7 +135,7 @@ extern "C" octo_status octo_decode_tokens(const octo_codec_desc* codec,
   clear_error();
   const char* what = "octo_decode_tokens";
   Codec c;
-  octo_status s = resolve_codec(codec, what, &c);
+  octo_status s = resolve_codec(codec, what, &c, true, true);
   if (s != OCTO_OK) return s;
   if ((s = check_cache(cache, c, what)) != OCTO_OK) return s;
   if (t0 < 0 || T < 0) return fail(OCTO_ERR_INVALID_ARGUMENT, "%s: t0 %d, T %d", what, t0, T);
@@ -150,7 +150,7 @@ extern "C" octo_status octo_decode_tokens(const octo_codec_desc* codec,
   ReconArgs a;
   a.idx = cache->idx;
   a.gamma = cache->gamma;
-  a.cb = c.cb;
+  a.cb = c.wcb;
   a.seed = c.seed;
   a.B = cache->batch;
   a.H = cache->kv_heads;
@@ -177,6 +177,16 @@ extern "C" octo_status octo_decode_tokens(const octo_codec_desc* codec,
     case 22: launch<2, 2>(a, stream); break;
     case 33: launch<3, 3>(a, stream); break;
     case 44: launch<4, 4>(a, stream); break;
+    // the rest of the (b + delta, b - delta) sweep (Sec. 3.3)
+    case 4: launch<0, 4>(a, stream); break;
+    case 15: launch<1, 5>(a, stream); break;
+    case 26: launch<2, 6>(a, stream); break;
+    case 13: launch<1, 3>(a, stream); break;
+    case 24: launch<2, 4>(a, stream); break;
+    case 35: launch<3, 5>(a, stream); break;
+    case 40: launch<4, 0>(a, stream); break;
+    case 51: launch<5, 1>(a, stream); break;
+    case 62: launch<6, 2>(a, stream); break;
     default: return fail(OCTO_ERR_UNSUPPORTED, "%s: configuration not compiled", what);
   }
   return check_launch(what);

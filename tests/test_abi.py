@@ -85,7 +85,10 @@ def test_codec_errors(L):
     assert L.octo_record_sizes(ctypes.byref(desc(head_dim=96)), ctypes.byref(out)) == 1
     assert L.octo_record_sizes(ctypes.byref(desc(head_dim=64)), ctypes.byref(out)) == 2
     assert L.octo_record_sizes(ctypes.byref(desc(bits=6)), ctypes.byref(out)) == 2
-    assert L.octo_record_sizes(ctypes.byref(desc(b_dir=5, b_nrm=1)), ctypes.byref(out)) == 2
+    # (1, 1) is no split of any kernel; (5, 1), a split of the (b + delta,
+    # b - delta) sweep, only has its layout and the encoder
+    assert L.octo_record_sizes(ctypes.byref(desc(b_dir=1, b_nrm=1)), ctypes.byref(out)) == 2
+    assert L.octo_record_sizes(ctypes.byref(desc(b_dir=5, b_nrm=1)), ctypes.byref(out)) == 0
     assert L.octo_record_sizes(ctypes.byref(desc(rounding=5)), ctypes.byref(out)) == 1
     assert L.octo_record_sizes(ctypes.byref(desc(qjl=2)), ctypes.byref(out)) == 1
     assert L.octo_record_sizes(ctypes.byref(desc()), ctypes.byref(out)) == 0
@@ -143,6 +146,14 @@ def dec(L, kd, vd, kv, vv, Hq=4, lens=4096, max_len=128, out=4096, ws=4096, ws_b
     return L.octo_attend_decode(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(kv),
                                 ctypes.byref(vv), q, qdt, Hq, lens, max_len, 0.0, out, ws,
                                 ws_bytes, None)
+
+
+def test_sweep_splits_only_for_the_encoder(L):
+    """A split of the (b + delta, b - delta) sweep beyond delta = 0, +1 has a
+    record layout and the encoder, but no attention kernel."""
+    sw = desc(bits=3, b_dir=5, b_nrm=1)
+    assert dec(L, sw, sw, view(H=1), view(H=1), Hq=1) == 2
+    assert b"not compiled" in L.octo_last_error()
 
 
 def test_decode_errors(L):

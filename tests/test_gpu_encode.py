@@ -94,8 +94,13 @@ def test_encode_zero_and_degenerate_vectors():
         assert_encode_ok(compare_encode(h, hc, x), f"degenerate b={bits}")
 
 
+# the (b + delta, b - delta) sweep splits of Sec. 3.3 besides delta = 0, +1
+SWEEP = [(b, b + dl, b - dl) for b in (2, 3, 4) for dl in (-2, -1, 2)]
+
+
 @pytest.mark.parametrize("bits,b_dir,b_nrm,rounding", [
-    (3, None, None, "scalar"), (2, 2, 2, "local3x3"), (3, 3, 3, "local3x3"), (4, 4, 4, "scalar")])
+    (3, None, None, "scalar"), (2, 2, 2, "local3x3"), (3, 3, 3, "local3x3"), (4, 4, 4, "scalar")]
+    + [(b, bd, bn, "local3x3") for b, bd, bn in SWEEP])
 def test_encode_modes(bits, b_dir, b_nrm, rounding):
     w = workload("tiny")
     inp = make_inputs(w)

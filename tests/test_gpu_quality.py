@@ -5,9 +5,9 @@ quality.py) and parity of octo_decode_tokens.
     gamma R^T u^ of the GPU-written cache (every split, QJL codecs, a token
     offset, ragged lengths): relative error <= 1e-5 per vector;
   * the paper's synthetic claims measured on the GPU codec (stored with
-    their citations in tests/golden/paper_claims.json): the (b+1, b-1)
-    split against (b, b) (Sec. 3.3), 3x3 against scalar rounding (Sec. 3.5,
-    App. E), and the needle's softmax mass (Sec. 4.1).
+    their citations in tests/golden/paper_claims.json): the (b + delta,
+    b - delta) split sweep, delta = -2 .. 2 (Sec. 3.3), 3x3 against scalar
+    rounding (Sec. 3.5, App. E), and the needle's softmax mass (Sec. 4.1).
 """
 import json
 import os
@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_parity import ROOT, codecs, encode_gpu, oatt, octo, say
+from gpu_parity import ROOT, codecs, encode_gpu, oatt, octo, record_counts, say
 from quantized_decode_attention_octo_amd import quality
 
 pytestmark = pytest.mark.gpu
@@ -32,7 +32,7 @@ def _need_gpu():
 @pytest.mark.parametrize("bits,qjl,split", [
     (3, False, (None, None)), (4, False, (None, None)), (2, True, (None, None)),
     (2, False, (2, 2)), (3, False, (3, 3)), (4, True, (4, 4)),
-])
+] + [(b, False, (b + dl, b - dl)) for b in (2, 3, 4) for dl in (-2, -1, 2)])
 def test_decode_tokens_matches_oracle(bits, qjl, split):
     gc, hc = codecs(bits, qjl=qjl, b_dir=split[0], b_nrm=split[1], seed=3)
     g = torch.Generator().manual_seed(bits)
@@ -51,13 +51,28 @@ def test_decode_tokens_matches_oracle(bits, qjl, split):
 
 
 def test_split_sweep_on_gpu():
-    lo, hi = CLAIMS["bit_split_sweep"]["delta_plus1_mse_reduction_pct"]
+    """The (b + delta, b - delta) sweep of Sec. 3.3 on the GPU encoder and
+    reconstruction, delta = -2 .. 2, with the oracle's checks: the minimum
+    at delta = +1, the +1 and +2 bands, and the delta = -2 factor (the golden
+    one for b = 3, 4; 5 at b = 2, where the split (0, 4) saturates)."""
+    cl = CLAIMS["bit_split_sweep"]
+    lo, hi = cl["delta_plus1_mse_reduction_pct"]
+    lo2, hi2 = cl["delta_plus2_mse_increase_pct"]
     for b in (2, 3, 4):
-        d = quality.reconstruction(b, n=4096, seeds=1)["mse_per_coord"]
-        u = quality.reconstruction(b, b_dir=b, b_nrm=b, n=4096, seeds=1)["mse_per_coord"]
-        red = 100 * (1 - d / u)
-        say(f"[split sweep b={b}] MSE (b+1,b-1) {d:.3e}, (b,b) {u:.3e}: {red:.1f}% lower")
+        mse = {dl: quality.reconstruction(b, b_dir=b + dl, b_nrm=b - dl, n=4096, seeds=1)["mse_per_coord"]
+               for dl in (-2, -1, 0, 1, 2)}
+        red = 100 * (1 - mse[1] / mse[0])
+        say(f"[split sweep b={b}] MSE / MSE(delta=0): "
+            + ", ".join(f"{dl:+d}: {mse[dl] / mse[0]:.3f}" for dl in sorted(mse)) + f"; +1 is {red:.1f}% lower")
+        record_counts(f"split sweep b={b}", {f"mse_ratio_delta{dl:+d}": float(mse[dl] / mse[0]) for dl in mse})
+        assert min(mse, key=mse.get) == cl["argmin_delta"], (b, mse)
         assert lo - 3 <= red <= hi + 3, (b, red)
+        assert mse[2] > mse[1] and mse[2] > mse[0]
+        if b > 2:
+            inc = 100 * (mse[2] / mse[0] - 1)
+            assert lo2 - 5 <= inc <= hi2 + 5, (b, inc)
+        fac = cl["delta_minus2_factor_at_least"] if b > 2 else 5.0
+        assert mse[-2] / mse[0] >= fac, (b, mse[-2] / mse[0])
 
 
 def test_rounding_gain_on_gpu():

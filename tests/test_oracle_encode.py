@@ -145,7 +145,13 @@ def test_bit_split_sweep_reproduces_paper():
             inc = 100 * (mse[2] / mse[0] - 1)
             lo2, hi2 = cl["delta_plus2_mse_increase_pct"]
             assert lo2 - 5 <= inc <= hi2 + 5, (b, inc)
-        assert mse[-2] / mse[0] >= 5.0, (b, mse[-2] / mse[0])
+        # Sec. 3.3: delta = -2 raises the MSE "by an order of magnitude or
+        # more" (the golden factor).  Reading: at b = 2 that split is (0, 4),
+        # one direction centroid per axis, whose error saturates near the
+        # triplet's own energy; the factor stays below ten there (6.8 on these
+        # keys), so b = 2 keeps the weaker bound 5 and b = 3, 4 the golden one.
+        fac = cl["delta_minus2_factor_at_least"] if b > 2 else 5.0
+        assert mse[-2] / mse[0] >= fac, (b, mse[-2] / mse[0])
 
 
 def test_rounding_ablation_reproduces_paper():
