@@ -90,6 +90,9 @@ typedef enum {
   OCTO_ERR_HIP = 7                 /* a HIP launch reported an error          */
 } octo_status;
 
+/* The enums below name the values of plain int32_t arguments and fields:
+   a caller may pass any int, and a value outside the enum is rejected
+   with OCTO_ERR_INVALID_ARGUMENT rather than read as an enum.            */
 typedef enum { OCTO_DTYPE_F32 = 0, OCTO_DTYPE_BF16 = 1 } octo_dtype;
 
 /* Encoder rounding (OCTOPUS paper Sec. 3.5; App. A/E summaries).
@@ -143,7 +146,9 @@ typedef struct {
 } octo_stream_sizes;
 
 uint32_t octo_abi_version(void);
-const char* octo_status_string(octo_status s);
+/* Name of a status code; "OCTO_ERR_UNKNOWN" for any other value.  The code
+   is taken as a plain int, so a value outside the enum is well defined.     */
+const char* octo_status_string(int32_t s);
 /* Message of the last failing call on this thread ("" if none).             */
 const char* octo_last_error(void);
 
@@ -164,7 +169,7 @@ octo_status octo_record_sizes(const octo_codec_desc* codec, octo_stream_sizes* o
  *   dst        cache with batch == B, kv_heads == H and
  *              token_offset + T <= capacity (else OCTO_ERR_CAPACITY).
  * Zero vectors encode as gamma = 0 with the placeholder direction (0, 0).   */
-octo_status octo_encode(const octo_codec_desc* codec, const void* x, octo_dtype x_dtype,
+octo_status octo_encode(const octo_codec_desc* codec, const void* x, int32_t x_dtype,
                         int32_t B, int32_t H, int32_t T, const int64_t x_strides[4],
                         const octo_cache_view* dst, int32_t token_offset,
                         hipStream_t stream);
@@ -216,7 +221,7 @@ octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_codec, int32_t 
  * (the group codec for keys is taken by octo_attend_chunk only).            */
 octo_status octo_attend_decode(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
                                const octo_cache_view* k_cache, const octo_cache_view* v_cache,
-                               const void* q, octo_dtype q_dtype, int32_t num_q_heads,
+                               const void* q, int32_t q_dtype, int32_t num_q_heads,
                                const int32_t* seq_lens, int32_t max_seq_len,
                                float softmax_scale, float* out,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -239,7 +244,7 @@ octo_status octo_attend_decode_noalloc(const octo_codec_desc* k_codec,
                                        const octo_codec_desc* v_codec,
                                        const octo_cache_view* k_cache,
                                        const octo_cache_view* v_cache, const void* q,
-                                       octo_dtype q_dtype, int32_t num_q_heads,
+                                       int32_t q_dtype, int32_t num_q_heads,
                                        const int32_t* seq_lens, int32_t max_seq_len,
                                        float softmax_scale, float* out, hipStream_t stream);
 
@@ -287,7 +292,7 @@ octo_status octo_decode_step_workspace_bytes(const octo_codec_desc* k_codec, int
  * the lengths.  Codec combinations as for octo_attend_decode.                */
 octo_status octo_decode_step(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,
                              const octo_cache_view* k_cache, const octo_cache_view* v_cache,
-                             const void* q, octo_dtype q_dtype, int32_t num_q_heads,
+                             const void* q, int32_t q_dtype, int32_t num_q_heads,
                              const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_window,
                              uint16_t* v_window, int32_t window, int32_t* packed_lens,
                              int32_t* window_lens, int32_t max_packed_len, float softmax_scale,

@@ -19,7 +19,9 @@ import numpy as np
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "liboctopus.so")
+# OCTO_LIB names another build of the same library (the host-sanitized one of
+# build.py --sanitize, for the ABI checks under ASan and UBSan).
+LIB_PATH = os.environ.get("OCTO_LIB") or os.path.join(PKG, "liboctopus.so")
 CODEBOOKS = os.path.join(PKG, "codebooks", "octopus_d{d}.json")
 
 ABI_VERSION = 4

@@ -5,6 +5,14 @@
 Every source under csrc/ is compiled with hipcc for gfx950 into _build/ and
 linked into quantized_decode_attention_octo_amd/liboctopus.so.  The device
 code is compiled without packed-FP32 instructions.
+
+    python -m quantized_decode_attention_octo_amd.build --sanitize
+
+builds liboctopus_san.so (objects in _build_san/) whose host code carries
+AddressSanitizer and UndefinedBehaviorSanitizer checks (the device code is
+built as usual).  It is loaded with the sanitizer runtime preloaded
+(sanitizer_runtime()) and OCTO_LIB naming it, which is how
+tests/test_sanitized_abi.py runs the ABI checks.
 """
 import os
 import shutil
@@ -18,6 +26,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liboctopus.so")
+BUILD_SAN = os.path.join(ROOT, "_build_san")
+LIB_SAN = os.path.join(PKG, "liboctopus_san.so")
 SOURCES = ["api.cpp", "encode.hip", "decode.hip", "chunk.hip", "reconstruct.hip"]
 ARCH = "gfx950"
 
@@ -44,12 +54,34 @@ def device_flags():
 FILE_FLAGS = {"chunk.hip": ["-fno-honor-nans"]}
 
 
-def compile_one(src, verbose=False):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def sanitizer_flags():
+    # host compilation only (each flag behind -Xarch_host)
+    flags = []
+    for f in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+              "-fno-omit-frame-pointer"):
+        flags += ["-Xarch_host", f]
+    return flags
+
+
+def sanitizer_runtime():
+    """The ASan runtime (with UBSan's handlers) of the hipcc toolchain, to be
+    preloaded into a process that loads the sanitized library."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+        return path
+    raise RuntimeError("the ASan runtime of the hipcc toolchain was not found")
+
+
+def compile_one(src, verbose=False, sanitize=False):
+    obj = os.path.join(BUILD_SAN if sanitize else BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd += device_flags()
     cmd += FILE_FLAGS.get(src, [])
+    if sanitize:
+        cmd += sanitizer_flags()
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,22 +90,23 @@ def compile_one(src, verbose=False):
     return obj
 
 
-def build(verbose=False, jobs=None):
+def build(verbose=False, jobs=None, sanitize=False):
     """Compiles every source and links the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(BUILD_SAN if sanitize else BUILD, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 8)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: compile_one(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: compile_one(s, verbose, sanitize), SOURCES))
+    lib = LIB_SAN if sanitize else LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

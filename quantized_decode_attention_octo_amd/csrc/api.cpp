@@ -163,7 +163,7 @@ extern "C" {
 
 uint32_t octo_abi_version(void) { return OCTO_ABI_VERSION; }
 
-const char* octo_status_string(octo_status s) {
+const char* octo_status_string(int32_t s) {
   switch (s) {
     case OCTO_OK: return "OCTO_OK";
     case OCTO_ERR_INVALID_ARGUMENT: return "OCTO_ERR_INVALID_ARGUMENT";

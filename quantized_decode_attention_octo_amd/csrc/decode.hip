@@ -1514,7 +1514,7 @@ static octo_status check_kv(const octo_codec_desc* k_codec, const octo_codec_des
 // arguments of the scan (no step fields but the snapshot's place).
 static octo_status prepare(const char* what, const octo_codec_desc* k_codec,
                            const octo_codec_desc* v_codec, const octo_cache_view* k_cache,
-                           const octo_cache_view* v_cache, const void* q, octo_dtype q_dtype,
+                           const octo_cache_view* v_cache, const void* q, int32_t q_dtype,
                            int32_t num_q_heads, const int32_t* seq_lens, int32_t max_seq_len,
                            float softmax_scale, float* out, void* workspace,
                            size_t workspace_bytes, bool step, DecodeArgs* a, Codec* kc, Codec* vc) {
@@ -1624,7 +1624,7 @@ extern "C" octo_status octo_decode_workspace_bytes(const octo_codec_desc* k_code
 static octo_status attend_decode(const char* what, const octo_codec_desc* k_codec,
                                  const octo_codec_desc* v_codec, const octo_cache_view* k_cache,
                                  const octo_cache_view* v_cache, const void* q,
-                                 octo_dtype q_dtype, int32_t num_q_heads,
+                                 int32_t q_dtype, int32_t num_q_heads,
                                  const int32_t* seq_lens, int32_t max_seq_len,
                                  float softmax_scale, float* out, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
@@ -1644,7 +1644,7 @@ extern "C" octo_status octo_attend_decode(const octo_codec_desc* k_codec,
                                           const octo_codec_desc* v_codec,
                                           const octo_cache_view* k_cache,
                                           const octo_cache_view* v_cache, const void* q,
-                                          octo_dtype q_dtype, int32_t num_q_heads,
+                                          int32_t q_dtype, int32_t num_q_heads,
                                           const int32_t* seq_lens, int32_t max_seq_len,
                                           float softmax_scale, float* out, void* workspace,
                                           size_t workspace_bytes, hipStream_t stream) {
@@ -1693,7 +1693,7 @@ extern "C" octo_status octo_attend_decode_noalloc(const octo_codec_desc* k_codec
                                                   const octo_codec_desc* v_codec,
                                                   const octo_cache_view* k_cache,
                                                   const octo_cache_view* v_cache, const void* q,
-                                                  octo_dtype q_dtype, int32_t num_q_heads,
+                                                  int32_t q_dtype, int32_t num_q_heads,
                                                   const int32_t* seq_lens, int32_t max_seq_len,
                                                   float softmax_scale, float* out,
                                                   hipStream_t stream) {
@@ -1727,7 +1727,7 @@ extern "C" octo_status octo_decode_step(const octo_codec_desc* k_codec,
                                         const octo_codec_desc* v_codec,
                                         const octo_cache_view* k_cache,
                                         const octo_cache_view* v_cache, const void* q,
-                                        octo_dtype q_dtype, int32_t num_q_heads,
+                                        int32_t q_dtype, int32_t num_q_heads,
                                         const uint16_t* k_new, const uint16_t* v_new,
                                         uint16_t* k_window, uint16_t* v_window, int32_t window,
                                         int32_t* packed_lens, int32_t* window_lens,

@@ -449,7 +449,7 @@ void launch_group(const EncodeArgs& a, hipStream_t st) {
 }  // namespace
 }  // namespace octo
 
-extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, octo_dtype x_dtype,
+extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, int32_t x_dtype,
                                    int32_t B, int32_t H, int32_t T, const int64_t x_strides[4],
                                    const octo_cache_view* dst, int32_t token_offset,
                                    hipStream_t stream) {
