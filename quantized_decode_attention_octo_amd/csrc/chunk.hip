@@ -216,9 +216,10 @@ __device__ inline float4 oct_dir(float xi, float eta) {
 // one coordinate a lane) are read from the row-major value tile with the
 // transposing LDS read.
 constexpr int kRG = 2;          // 16-query row groups per wavefront
-constexpr int kCWaves = 2;
+constexpr int kQB = 16 * kRG;   // queries of a wavefront (one query block)
+constexpr int kCWaves = 8;      // one workgroup a compute unit, two wavefronts a SIMD
 constexpr int kCThreads = 64 * kCWaves;
-constexpr int kBM = 16 * kRG * kCWaves;   // 64 queries per workgroup
+constexpr int kSlots = 2;       // (batch, KV head) planes a workgroup may span
 constexpr int kXcds = 8;        // workgroups are dealt round-robin to the XCDs
 constexpr float kLazyLog2 = 8.0f;   // slack of the lazy running maximum (log2 units)
 constexpr int kBN = 32;         // keys per tile
@@ -228,7 +229,7 @@ constexpr int kCurPad = kBN;    // the current rows are padded to whole tiles
 // one chunk store) serves at a time fall in 8 different bank quads.
 constexpr int kKChunks = kHeadDim / 8;
 constexpr int kKTileBytes = kBN * kHeadDim * 2;
-constexpr int kKTileInsts = kBN * kKChunks / 64 / kCWaves;    // direct loads a wavefront
+constexpr int kKTileInsts = kBN * kKChunks / 64;    // 64-lane direct loads of a key tile
 // Value tile: 32 rows of 288 bytes (256 of values, 32 of pad), so that the
 // four rows one transposing read serves at a time start 8 banks apart.
 // The current values come in rows of the same length.
@@ -236,8 +237,11 @@ constexpr int kVRowBytes = 288;
 constexpr int kVRowHalves = kVRowBytes / 2;
 constexpr int kVTileBytes = kBN * kVRowBytes;
 constexpr int kVTileChunks = kVTileBytes / 16;
-constexpr int kVTileInsts = (kVTileChunks + 64 * kCWaves - 1) / (64 * kCWaves);   // a wavefront
-constexpr int kTilesBytes = 2 * kKTileBytes + 2 * kVTileBytes;
+constexpr int kVTileInsts = kVTileChunks / 64;      // 64-lane direct loads of a value tile
+static_assert(kVTileChunks % 64 == 0, "value tile in whole direct loads");
+// A slot's two key tiles, then its two value tiles (tile u in buffer u % 2).
+constexpr int kSlotBytes = 2 * kKTileBytes + 2 * kVTileBytes;
+constexpr int kTilesBytes = kSlots * kSlotBytes;
 // Output blocks of 16 value coordinates.
 constexpr int kOB = kHeadDim / 16;
 // Fourth word of a raw buffer descriptor: 32-bit data format, no swizzle.
@@ -290,7 +294,12 @@ struct ChunkArgs {
   const _Float16* kc;    // current keys [B][Hkv][Tc_pad][128] rotated
   const _Float16* vc;    // current values [B][Hkv][Tc_pad][kVRowHalves] rotated
   float* out;            // [B][Hq][Tq][128]
-  int Hq, Hkv, Tq, q_tiles;
+  int Hq, Hkv, Tq;
+  // 32-query blocks: qb a (batch, query head), n_blocks in all, in (batch,
+  // head, block) order.  packed: workgroup w takes blocks 8 w .. 8 w + 7
+  // (at most two KV planes, as a plane has bpp >= 8 blocks); else it takes
+  // the bpp < 8 blocks of plane w.
+  int qb, n_blocks, bpp, packed;
   int cached, Tc, Tc_pad, capacity;
   uint64_t vseed;
   const _Float16* qfeat; // Jensen-bias correction: query features [B][Hq][Tq][kFeat]
@@ -303,20 +312,34 @@ struct ChunkArgs {
 };
 
 // ---- tables
+// Each table is stored in C = tab_copies(b_dir, b_nrm) interleaved copies,
+// entry e of copy c at 8-byte slot C e + c, and lane L reads copy L mod C.
+// With 32 copies the two banks a lane's 8-byte read touches depend on the
+// lane alone, so the gathers of a wavefront (random entries) never
+// conflict; tables too large for 32 copies in 32 KB get fewer.
+__host__ __device__ constexpr int pre_entries(int bd, int bn) {
+  return (1 << (2 * bd)) * (1 << bn) <= kMaxPre ? (1 << (2 * bd)) * (1 << bn) : (1 << (2 * bd));
+}
+__host__ __device__ constexpr int tab_copies(int bd, int bn) {
+  return 32768 / (8 * pre_entries(bd, bn)) >= 32 ? 32 : 32768 / (8 * pre_entries(bd, bn));
+}
 template <int BD, int BN>
 __device__ __forceinline__ void build_octo_table(const float* cx, const float* cr, char* dyn,
                                                  const ChunkCodec& c, int tid) {
   constexpr int K = 1 << BD, KK = K * K, R = 1 << BN;
   constexpr bool PRE = KK * R <= kMaxPre;
+  constexpr int C = tab_copies(BD, BN);
   uint2* tab = reinterpret_cast<uint2*>(dyn + c.tab);
-  for (int e = tid; e < KK; e += kCThreads) {
+  for (int i = tid; i < KK * C; i += kCThreads) {
+    const int e = i / C;
     const float4 n = oct_dir(cx[e % K], cx[e / K]);          // field: xi | eta << b_dir
     if (PRE) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        tab[r * KK + e] = make_uint2(pack_rne(cr[r] * n.x, cr[r] * n.y), pack_rne(cr[r] * n.z, 0.0f));
+        tab[(r * KK + e) * C + i % C] =
+            make_uint2(pack_rne(cr[r] * n.x, cr[r] * n.y), pack_rne(cr[r] * n.z, 0.0f));
     } else {
-      tab[e] = make_uint2(pack_rne(n.x, n.y), pack_rne(n.z, 0.0f));
+      tab[i] = make_uint2(pack_rne(n.x, n.y), pack_rne(n.z, 0.0f));
     }
   }
   if (!PRE && tid < R) reinterpret_cast<uint32_t*>(dyn + c.rho)[tid] = pack_rne(cr[tid], cr[tid]);
@@ -427,19 +450,21 @@ __device__ inline void store_part(char* tile, const int (&cw)[4], const uint32_t
     *reinterpret_cast<u32x4*>(tile + cw[c]) = u32x4{d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]};
 }
 
-// OCTOPUS row part (PAR: the wavefront, so pg = 2 hi + PAR): the ten
-// triplets as five pairs of three dwords, (x|y) of the first, (z of the
-// first | x of the second), (y|z) of the second; then the extra dword:
-// part 0 (x|y) of triplet 40, part 1 (z of 40 | x of 41), part 2 (y|z) of
-// 41, part 3 (x|y) of 42.  Keys (VAL false): the scores take gamma in fp32,
-// the threads of part 0 copy it to gk.  Values: every word times gamma.
+// OCTOPUS row part (PAR: pg = 2 hi + PAR): the ten triplets as five pairs
+// of three dwords, (x|y) of the first, (z of the first | x of the second),
+// (y|z) of the second; then the extra dword: part 0 (x|y) of triplet 40,
+// part 1 (z of 40 | x of 41), part 2 (y|z) of 41, part 3 (x|y) of 42.
+// Keys (VAL false): the scores take gamma in fp32, the threads of part 0
+// copy it to gk.  Values: every word times gamma.  `tab` is the lane's copy
+// of the table (entry e at tab + 8 C e).
 template <int BD, int BN, int PAR, bool VAL, int N>
-__device__ __forceinline__ void dec_octo_row(const uint32_t (&w)[N], const char* dyn,
-                                             const ChunkCodec& c, char* tile, const int (&cw)[4],
+__device__ __forceinline__ void dec_octo_row(const uint32_t (&w)[N], const char* tab,
+                                             const char* rhotab, char* tile, const int (&cw)[4],
                                              float* gk, int kk, int hi) {
   constexpr int BT = 2 * BD + BN, NWm = main_words(BT), NWe = tail_words(BT);
   constexpr int KK = 1 << (2 * BD);
   constexpr bool PRE = KK * (1 << BN) <= kMaxPre;
+  constexpr int CS = 3 + __builtin_ctz(tab_copies(BD, BN));   // log2 of 8 C
   const int pg = 2 * hi + PAR;
   const int sh = (10 * BT * pg) & 31;
   uint32_t x[NWm], xe[NWe + 1];
@@ -450,13 +475,12 @@ __device__ __forceinline__ void dec_octo_row(const uint32_t (&w)[N], const char*
   xe[NWe] = 0u;
   const uint32_t gam = w[NWm + NWe];
   if (!VAL && pg == 0) gk[kk] = __uint_as_float(gam);
-  const uint2* tab = reinterpret_cast<const uint2*>(dyn + c.tab);
-  const uint32_t* rhop = reinterpret_cast<const uint32_t*>(dyn + c.rho);
+  const uint32_t* rhop = reinterpret_cast<const uint32_t*>(rhotab);
   auto entry = [&](uint32_t f) __attribute__((always_inline)) -> uint2 {
     if constexpr (PRE) {
-      return tab[opaque(f)];
+      return *reinterpret_cast<const uint2*>(tab + (opaque(f) << CS));
     } else {
-      const uint2 e = tab[opaque(f & (KK - 1))];
+      const uint2 e = *reinterpret_cast<const uint2*>(tab + (opaque(f & (KK - 1)) << CS));
       const uint32_t p = rhop[opaque(f >> (2 * BD))];
       return make_uint2(mul2(e.x, p), mul2(e.y, p));
     }
@@ -562,54 +586,81 @@ __device__ inline void tile_barrier() {
 // coordinates 16 c + 4 q .. 16 c + 4 q + 3, so lane i receives coordinate
 // 16 c + i of keys 4 g + j (then 16 + 4 g + j): its B fragment.
 //
+// Workgroups: a wavefront takes one block of 32 queries of one (batch,
+// query head) and every key of its plane; a workgroup takes eight
+// consecutive blocks, which may end one plane and begin the next (two
+// "slots", each with its own tiles).  The threads decode each cached tile
+// once for every wavefront of its plane: wavefront w decodes slot w / 4,
+// keys (w / 2 even) or values, part 2 (L / 32) + w % 2 of row L % 32 -- one
+// row part a thread a tile.  With a workgroup a compute unit the LDS holds
+// the tables in 32 lane-private copies (see tab_copies).
+//
 // Tiles: the cached window's ceil(cached / 32) tiles first, then the current
-// chunk's; tile u lives in buffer u % 2.  Iteration t: the words of cached
-// tile t + 2 are requested (registers of stage t % 2), or the rows of
-// current tile t + 1 (direct loads into buffer (t + 1) % 2); tile t is
+// chunk's; tile u lives in buffer u % 2 of its slot.  Iteration t: the words
+// of cached tile t + 2 are requested (registers of stage t % 2), or the rows
+// of current tile t + 1 (direct loads into buffer (t + 1) % 2); tile t is
 // computed; the threads decode cached tile t + 1 (words of stage (t + 1) %
 // 2) into buffer (t + 1) % 2; one barrier.  The loop is unrolled by two so
 // that buffer offsets and word stages are constants.
 //
 // XCD-aware order: the hardware deals consecutive workgroup ids to the 8
-// XCDs in turn, so the linear id is mapped such that all query tiles of one
-// (batch, head) run on the same XCD and stream its keys and values through
-// that XCD's L2 together.
+// XCDs in turn, so the linear id is mapped such that consecutive workgroups
+// (the query blocks of one plane) run on the same XCD and stream its keys
+// and values through that XCD's L2 together.
 //
 // CORR: the Jensen-bias correction ("Quantized Keys Steal Attention",
 // Eq. 15).  Its bias is a rank-(128 / g) product of query and key features,
 // so it is one more k-slice of the score MFMA per 16 cached keys, whose slots
 // 0..7 (lane group 0) hold the features and the rest zeros.
 template <bool CORR, int KSEL, int VSEL>
-__global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
-  constexpr int KW = row_words(KSEL), VW = row_words(VSEL);
+__global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
+  static_assert(KSEL == VSEL, "one codec for both tensors, or chosen at run time");
+  constexpr int NW = row_words(KSEL);
   __shared__ __attribute__((aligned(1024))) char tiles[kTilesBytes];
-  __shared__ __attribute__((aligned(16))) float gks[2][kBN];
-  __shared__ __attribute__((aligned(16))) _Float16 kfs[2][CORR ? kBN * kFeat : 8];
-  __shared__ __attribute__((aligned(16))) _Float16 qfs[CORR ? kBM * kFeat : 8];
+  __shared__ __attribute__((aligned(16))) float gks[kSlots][2][kBN];
+  __shared__ __attribute__((aligned(16))) _Float16 kfs[kSlots][2][CORR ? kBN * kFeat : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 qfs[CORR ? kCWaves * kQB * kFeat : 8];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
 
   const int tid = threadIdx.x, L = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = L & 15, grp = L >> 4;
   const int n_units = gridDim.x;
   const int id = blockIdx.x;
-  // id -> (xcd, local); units (head-major, tile-minor) are split into 8
-  // contiguous ranges, range x running on XCD x.
+  // id -> (xcd, local); units are split into 8 contiguous ranges, range x
+  // running on XCD x.
   const int per_xcd = (n_units + kXcds - 1) / kXcds;
   const int xcd = id % kXcds, local = id / kXcds;
   const int full_xcds = n_units - (per_xcd - 1) * kXcds;   // XCDs with per_xcd units
   const int unit = xcd < full_xcds ? xcd * per_xcd + local
                                    : full_xcds * per_xcd + (xcd - full_xcds) * (per_xcd - 1) + local;
-  const int tile = unit % a.q_tiles, bh = unit / a.q_tiles;
-  const int hq = bh % a.Hq, b = bh / a.Hq;
-  const int hk = hq / (a.Hq / a.Hkv);
-  const size_t plane = (size_t)b * a.Hkv + hk;
-  const int q0 = tile * kBM + wave * 16 * kRG;
-  const bool kgroup = a.kcod.sel >= 1000;
+  // the workgroup's query blocks [start, start + count) and their planes
+  const int start = a.packed ? unit * kCWaves : unit * a.bpp;
+  const int count = a.packed ? min(kCWaves, a.n_blocks - start) : a.bpp;
+  const int gq = a.Hq / a.Hkv;
+  auto plane_of = [&](int g) {
+    const int bhq = g / a.qb;
+    return (bhq / a.Hq) * a.Hkv + (bhq % a.Hq) / gq;
+  };
+  const int plane0 = plane_of(start), plane1 = plane_of(start + count - 1);
+  const bool two = plane1 != plane0;
+  // this wavefront's block (batch b, query head hq, queries q0 ..) and slot
+  const bool active = wave < count;
+  const int gb = start + min(wave, count - 1);
+  const int bh = gb / a.qb, q0 = (gb % a.qb) * kQB;
+  const int cslot = plane_of(gb) != plane0;
+  // its decode task: slot, tensor (0 keys, 1 values), part parity
+  const int dslot = wave >> 2, dten = (wave >> 1) & 1, dpar = wave & 1;
+  const bool dact = dslot == 0 || two;
+  const size_t dplane = dslot ? plane1 : plane0;
+  const int dsel = dten ? a.vcod.sel : a.kcod.sel;
+  const int dW = dten ? a.vcod.W : a.kcod.W;
+  const int dtab = dten ? a.vcod.tab : a.kcod.tab, drho = dten ? a.vcod.rho : a.kcod.rho;
 
-  // ---- codebooks to LDS (in the tile area, free until the first tile),
-  // one value a lane from the argument block; then the tables
+  // ---- codebooks to LDS (at the end of the tile area: buffer 1 of slot 1,
+  // first written after the barriers of tile 0), one value a lane from the
+  // argument block; then the tables
   constexpr int kCb = kMaxXi + kMaxRho;
-  float* cbs = reinterpret_cast<float*>(tiles);
+  float* cbs = reinterpret_cast<float*>(tiles + kTilesBytes) - 2 * kCb;
   {
     // constant indices into the argument block (a run-time index would put
     // a copy of it in private memory)
@@ -625,11 +676,11 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     }
   }
   if constexpr (CORR) {
-    // the workgroup's 64 query feature rows (rows past Tq repeat the last)
-    for (int r = tid; r < kBM; r += kCThreads) {
-      const int qrow = min(tile * kBM + r, a.Tq - 1);
-      *reinterpret_cast<half8*>(&qfs[r * kFeat]) = *reinterpret_cast<const half8*>(
-          a.qfeat + (((size_t)b * a.Hq + hq) * a.Tq + qrow) * kFeat);
+    // each wavefront's 32 query feature rows (rows past Tq repeat the last)
+    if (L < kQB) {
+      const int qrow = min(q0 + L, a.Tq - 1);
+      *reinterpret_cast<half8*>(&qfs[(wave * kQB + L) * kFeat]) =
+          *reinterpret_cast<const half8*>(a.qfeat + ((size_t)bh * a.Tq + qrow) * kFeat);
     }
   }
   __syncthreads();
@@ -650,24 +701,24 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
   uint32_t k1024;
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k1024));
 
-  // ---- per-thread constants of the decoders: the byte offsets (buffer 0)
-  // of the four chunks of the thread's row part in the key and value tiles
-  int kw[4], vw[4];
+  // ---- per-thread constants of the decoder: the byte offsets (buffer 0 of
+  // the task's slot) of the four chunks of the thread's row part
+  int tw[4];
   {
-    const int kk = L & 31, pg = 2 * (L >> 5) + wave;
+    const int kk = L & 31, pg = 2 * (L >> 5) + dpar, base = dslot * kSlotBytes;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      kw[d] = kk * 256 + (((4 * pg + d) ^ (kk & 15)) << 4);
-      vw[d] = 2 * kKTileBytes + kk * kVRowBytes + 64 * pg + 16 * d;
-    }
+    for (int d = 0; d < 4; ++d)
+      tw[d] = base + (dten ? 2 * kKTileBytes + kk * kVRowBytes + 64 * pg + 16 * d
+                           : kk * 256 + (((4 * pg + d) ^ (kk & 15)) << 4));
   }
+  const int tstage = dten ? kVTileBytes : kKTileBytes;   // buffer 1 less buffer 0
 
   // Q^T fragments (B operand): query q0 + 16 rg + col, dims 32 s + 8 grp + e.
   half8 qf[kRG][4];
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg) {
     const int qrow = min(q0 + 16 * rg + col, a.Tq - 1);
-    const _Float16* src = a.q + (((size_t)b * a.Hq + hq) * a.Tq + qrow) * kHeadDim;
+    const _Float16* src = a.q + ((size_t)bh * a.Tq + qrow) * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[rg][s] = *reinterpret_cast<const half8*>(src + 32 * s + 8 * grp);
   }
@@ -685,116 +736,106 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     l_run[rg] = 0.0f;
   }
 
-  // the current chunk's rows and the packed cache of this plane (loads past
-  // a plane's range return zero)
+  // the task's packed stream and gammas, and the current chunk's rows of the
+  // task's plane (loads past a plane's range return zero)
+  const int tiles64 = a.capacity >> 6;
+  const bool dgroup = dsel >= 1000;
+  const __amdgpu_buffer_rsrc_t dis = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>((dten ? a.v_idx : a.k_idx) + dplane * tiles64 * dW * 64), (short)0,
+      a.capacity * dW * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t dgs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(dgroup ? nullptr : (dten ? a.v_gamma : a.k_gamma) + dplane * a.capacity),
+      (short)0, dgroup ? 0 : a.capacity * 4, kBufferWord3);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<_Float16*>(a.kc + plane * a.Tc_pad * kHeadDim), (short)0,
+      const_cast<_Float16*>(a.kc + dplane * a.Tc_pad * kHeadDim), (short)0,
       a.Tc_pad * kHeadDim * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<_Float16*>(a.vc + plane * a.Tc_pad * kVRowHalves), (short)0,
+      const_cast<_Float16*>(a.vc + dplane * a.Tc_pad * kVRowHalves), (short)0,
       a.Tc_pad * kVRowBytes, kBufferWord3);
-  const int tiles64 = a.capacity >> 6;
-  const __amdgpu_buffer_rsrc_t kis = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(a.k_idx + plane * tiles64 * a.kcod.W * 64), (short)0,
-      a.capacity * a.kcod.W * 4, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vis = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(a.v_idx + plane * tiles64 * a.vcod.W * 64), (short)0,
-      a.capacity * a.vcod.W * 4, kBufferWord3);
-  const bool vgroup = a.vcod.sel >= 1000;
-  const __amdgpu_buffer_rsrc_t kgs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(kgroup ? nullptr : a.k_gamma + plane * a.capacity), (short)0,
-      kgroup ? 0 : a.capacity * 4, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vgs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(vgroup ? nullptr : a.v_gamma + plane * a.capacity), (short)0,
-      vgroup ? 0 : a.capacity * 4, kBufferWord3);
 
   const int n_ct = (a.cached + kBN - 1) / kBN, n_rt = (a.Tc + kBN - 1) / kBN;
   const int n_tiles = n_ct + n_rt;
 
-  // Words of cached tile u into registers (key part, value part).
-  auto load_words = [&](int u, uint32_t (&wk)[KW], uint32_t (&wv)[VW]) __attribute__((always_inline)) {
+  // Words of the thread's row part of cached tile u into registers.
+  auto load_words = [&](int u, uint32_t (&w)[NW]) __attribute__((always_inline)) {
     const int t0 = u * kBN;
-    // the codec's per-thread offsets are formed here from an opaque copy of
-    // the thread index, tile by tile, rather than kept live for every codec
+    // the per-thread offsets are formed here from an opaque copy of the
+    // thread index, tile by tile, rather than kept live across the loop
     int lt = tid;
     asm volatile("" : "+v"(lt));
-    const int kk = lt & 31, pg = 2 * ((lt & 63) >> 5) + wave;
+    const int kk = lt & 31, pg = 2 * ((lt & 63) >> 5) + dpar;
     const bool valid = kk < a.cached - t0;
     // byte offset of the tile's first token in word row 0 of a W-word plane
-    const int sk = (t0 >> 6) * a.kcod.W * 256 + (t0 & 63) * 4;
-    const int sv = (t0 >> 6) * a.vcod.W * 256 + (t0 & 63) * 4;
-    with_codec<KSEL>(a.kcod.sel, [&](auto cs) __attribute__((always_inline)) {
+    const int sb = (t0 >> 6) * dW * 256 + (t0 & 63) * 4;
+    with_codec<KSEL>(dsel, [&](auto cs) __attribute__((always_inline)) {
       constexpr int C = decltype(cs)::value;
-      if constexpr (C < 1000) load_octo_row<C / 10, C % 10>(wk, kis, kgs, sk, t0, kk, pg, valid);
-      else load_group_row<(C - 1000) / 100, C % 100>(wk, kis, sk, kk, pg, valid);
-    });
-    with_codec<VSEL>(a.vcod.sel, [&](auto cs) __attribute__((always_inline)) {
-      constexpr int C = decltype(cs)::value;
-      if constexpr (C < 1000) load_octo_row<C / 10, C % 10>(wv, vis, vgs, sv, t0, kk, pg, valid);
-      else load_group_row<(C - 1000) / 100, C % 100>(wv, vis, sv, kk, pg, valid);
+      if constexpr (C < 1000) load_octo_row<C / 10, C % 10>(w, dis, dgs, sb, t0, kk, pg, valid);
+      else load_group_row<(C - 1000) / 100, C % 100>(w, dis, sb, kk, pg, valid);
     });
   };
-  // Decodes cached tile u from its words into buffer S (= u % 2).  Keys past
-  // the window (in its ragged last tile) decode from whatever words follow
-  // it: their scores are masked, and their values are finite (their gammas
-  // or zero-points load as zero).
-  auto decode = [&](int u, auto stage, const uint32_t (&wk)[KW], const uint32_t (&wv)[VW]) __attribute__((always_inline)) {
+  // Decodes the thread's row part of cached tile u from its words into
+  // buffer S (= u % 2) of its slot.  Keys past the window (in its ragged last
+  // tile) decode from whatever words follow it: their scores are masked, and
+  // their values are finite (their gammas or zero-points load as zero).
+  auto decode = [&](int u, auto stage, const uint32_t (&w)[NW]) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
     int lt = tid;
     asm volatile("" : "+v"(lt));
-    const int kk = lt & 31, hi = (lt & 63) >> 5, pg = 2 * hi + wave;
-    char* kt = tiles + S * kKTileBytes;
-    char* vt = tiles + S * kVTileBytes;          // vw holds the value tiles' offset
-    with_codec<KSEL>(a.kcod.sel, [&](auto cs) __attribute__((always_inline)) {
+    const int kk = lt & 31, hi = (lt & 63) >> 5, pg = 2 * hi + dpar;
+    char* tb = tiles + S * tstage;               // tw holds the slot's offsets
+    float* gk = gks[dslot][S];
+    with_codec<KSEL>(dsel, [&](auto cs) __attribute__((always_inline)) {
       constexpr int C = decltype(cs)::value;
       if constexpr (C < 1000) {
-        if (wave) dec_octo_row<C / 10, C % 10, 1, false>(wk, dyn, a.kcod, kt, kw, gks[S], kk, hi);
-        else dec_octo_row<C / 10, C % 10, 0, false>(wk, dyn, a.kcod, kt, kw, gks[S], kk, hi);
+        constexpr int BD = C / 10, BN = C % 10, NC = tab_copies(BD, BN);
+        const char* tab = dyn + dtab + ((lt & (NC - 1)) << 3);
+        const char* rt = dyn + drho;
+        if (dten) {
+          if (dpar) dec_octo_row<BD, BN, 1, true>(w, tab, rt, tb, tw, nullptr, kk, hi);
+          else dec_octo_row<BD, BN, 0, true>(w, tab, rt, tb, tw, nullptr, kk, hi);
+        } else {
+          if (dpar) dec_octo_row<BD, BN, 1, false>(w, tab, rt, tb, tw, gk, kk, hi);
+          else dec_octo_row<BD, BN, 0, false>(w, tab, rt, tb, tw, gk, kk, hi);
+        }
       } else {
-        dec_group_row<(C - 1000) / 100, C % 100, CORR, false>(wk, kt, kw, gks[S], kfs[S], kk, pg, k1024);
-      }
-    });
-    with_codec<VSEL>(a.vcod.sel, [&](auto cs) __attribute__((always_inline)) {
-      constexpr int C = decltype(cs)::value;
-      if constexpr (C < 1000) {
-        if (wave) dec_octo_row<C / 10, C % 10, 1, true>(wv, dyn, a.vcod, vt, vw, nullptr, kk, hi);
-        else dec_octo_row<C / 10, C % 10, 0, true>(wv, dyn, a.vcod, vt, vw, nullptr, kk, hi);
-      } else {
-        dec_group_row<(C - 1000) / 100, C % 100, false, true>(wv, vt, vw, nullptr, nullptr, kk, pg, k1024);
+        constexpr int VB = (C - 1000) / 100, GS = C % 100;
+        if (dten) dec_group_row<VB, GS, false, true>(w, tb, tw, nullptr, nullptr, kk, pg, k1024);
+        else dec_group_row<VB, GS, CORR, false>(w, tb, tw, gk, kfs[dslot][S], kk, pg, k1024);
       }
     });
   };
-  // Requests the rows of current tile u into buffer S (= u % 2); nothing is
-  // waited for here.
+  // Requests the rows of current tile u into buffer S (= u % 2) of the
+  // thread's slot, by the slot's four wavefronts; nothing is waited for here.
   auto request_rows = [&](int u, auto stage) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
     const int kt0 = (u - n_ct) * kBN;
-    char* ks = tiles + S * kKTileBytes;
-    char* vs = tiles + 2 * kKTileBytes + S * kVTileBytes;
+    char* ks = tiles + dslot * kSlotBytes + S * kKTileBytes;
+    char* vs = tiles + dslot * kSlotBytes + 2 * kKTileBytes + S * kVTileBytes;
     // source offsets, formed here (current tiles are few) rather than kept
     // in registers across the loop
     uint32_t lx = L;
     asm volatile("" : "+v"(lx));
-    if (wave == 0 && lx < kBN) gks[S][lx] = 1.0f;     // the scores take no gamma
-    // key tile: lane L of instruction j fills stored chunk p = 64 (4 w + j) +
-    // L, row p / 16, logical chunk (p % 16) ^ (row % 16)
+    const int lw = wave & 3;
+    if (lw == 0 && lx < kBN) gks[dslot][S][lx] = 1.0f;     // the scores take no gamma
+    // key tile: lane L of load j fills stored chunk p = 64 j + L, row p / 16,
+    // logical chunk (p % 16) ^ (row % 16)
 #pragma unroll
-    for (int j = 0; j < kKTileInsts; ++j) {
-      const uint32_t p = 64 * (kKTileInsts * wave + j) + lx;
+    for (int i = 0; i < kKTileInsts / 4; ++i) {
+      const int j = 4 * i + lw;
+      const uint32_t p = 64 * j + lx;
       const uint32_t kr = p / kKChunks, kc = (p % kKChunks) ^ (kr % kKChunks);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, ks + 1024 * (kKTileInsts * wave + j), 16,
-                                               (kr * kHeadDim + kc * 8) * 2, kt0 * kHeadDim * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, ks + 1024 * j, 16, (kr * kHeadDim + kc * 8) * 2,
+                                               kt0 * kHeadDim * 2, 0, 0);
     }
-    // value tile: the padded rows as they are, chunk p = 64 (5 w + j) + L
+    // value tile: the padded rows as they are, chunk p = 64 j + L
 #pragma unroll
-    for (int j = 0; j < kVTileInsts; ++j) {
-      const uint32_t p = 64 * (kVTileInsts * wave + j) + lx;
-      if (p < kVTileChunks)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vs + 1024 * (kVTileInsts * wave + j), 16, p * 16,
+    for (int i = 0; i < (kVTileInsts + 3) / 4; ++i) {
+      const int j = 4 * i + lw;
+      if (j < kVTileInsts)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vs + 1024 * j, 16, (64 * j + lx) * 16,
                                                  kt0 * kVRowBytes, 0, 0);
     }
   };
-
   // per-lane offsets of the key fragments of slice s (row col, logical chunk
   // 4 s + grp, stored at chunk (4 s + grp) ^ col; row 16 kt + col adds 4096
   // kt) and of the transposing value reads (row 4 grp + col / 4, coordinates
@@ -811,8 +852,8 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     constexpr int S = decltype(stage)::value;
     const bool cachedt = u < n_ct, first = u == 0;
     const int nvalid = cachedt ? a.cached - u * kBN : a.Tc - (u - n_ct) * kBN;
-    const char* ks = tiles + S * kKTileBytes;
-    const char* vs = tiles + 2 * kKTileBytes + S * kVTileBytes;
+    const char* ks = tiles + cslot * kSlotBytes + S * kKTileBytes;
+    const char* vs = tiles + cslot * kSlotBytes + 2 * kKTileBytes + S * kVTileBytes;
     // scores of the tile's keys (log2 units): st[kt][rg][r] = key 16 kt + 4 grp + r
     floatx4 st[kBN / 16][kRG];
     const half8 zero8 = {};
@@ -832,12 +873,12 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
           // minus the Jensen bias of keys 16 kt + (0..15), in log2 units
           // (slots 8..31 of both operands are zero: lane groups 1..3 read nothing)
           half8 kf5 = zero8;
-          if (grp == 0) kf5 = *reinterpret_cast<const half8*>(&kfs[S][(16 * kt + col) * kFeat]);
+          if (grp == 0) kf5 = *reinterpret_cast<const half8*>(&kfs[cslot][S][(16 * kt + col) * kFeat]);
 #pragma unroll
           for (int rg = 0; rg < kRG; ++rg) {
             half8 qf5 = zero8;
             if (grp == 0)
-              qf5 = *reinterpret_cast<const half8*>(&qfs[(wave * 16 * kRG + 16 * rg + col) * kFeat]);
+              qf5 = *reinterpret_cast<const half8*>(&qfs[(wave * kQB + 16 * rg + col) * kFeat]);
             st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf5, qf5, st[kt][rg], 0, 0, 0);
           }
         }
@@ -849,7 +890,7 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     float x[kRG][kBN / 4];
     float4 g4[kBN / 16];
 #pragma unroll
-    for (int kt = 0; kt < kBN / 16; ++kt) g4[kt] = *reinterpret_cast<const float4*>(&gks[S][16 * kt + 4 * grp]);
+    for (int kt = 0; kt < kBN / 16; ++kt) g4[kt] = *reinterpret_cast<const float4*>(&gks[cslot][S][16 * kt + 4 * grp]);
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
       const float mneg = -m_run[rg];
@@ -944,83 +985,81 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
 
   // ---- the tile pipeline: the words of cached tile u in registers of
   // stage u % 2, requested two tiles ahead
-  uint32_t wk0[KW] = {}, wv0[VW] = {}, wk1[KW] = {}, wv1[VW] = {};
-  if (n_ct > 0) load_words(0, wk0, wv0);
-  if (n_ct > 1) load_words(1, wk1, wv1);
-  if (n_ct == 0 && n_tiles > 0) request_rows(0, std::integral_constant<int, 0>{});
+  uint32_t w0[NW] = {}, w1[NW] = {};
+  if (dact && n_ct > 0) load_words(0, w0);
+  if (dact && n_ct > 1) load_words(1, w1);
+  if (dact && n_ct == 0 && n_tiles > 0) request_rows(0, std::integral_constant<int, 0>{});
   lds_barrier();                       // tables built
-  if (n_ct > 0) decode(0, std::integral_constant<int, 0>{}, wk0, wv0);
-  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  if (n_ct > 0) {
+    if (dact) decode(0, std::integral_constant<int, 0>{}, w0);
+  } else {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  }
   lds_barrier();
   // iteration t, buffer and word stage S = t % 2
-  auto iter = [&](int t, auto stage, uint32_t (&wkS)[KW], uint32_t (&wvS)[VW],
-                  uint32_t (&wkN)[KW], uint32_t (&wvN)[VW]) __attribute__((always_inline)) {
+  auto iter = [&](int t, auto stage, uint32_t (&wS)[NW], uint32_t (&wN)[NW]) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
     using Next = std::integral_constant<int, 1 - S>;
-    if (t + 2 < n_ct) load_words(t + 2, wkS, wvS);
+    if (dact && t + 2 < n_ct) load_words(t + 2, wS);
     const bool next_cur = t + 1 >= n_ct && t + 1 < n_tiles;
-    if (next_cur) request_rows(t + 1, Next{});
-    compute(t, stage);
-    if (t + 1 < n_ct) decode(t + 1, Next{}, wkN, wvN);
-    else if (next_cur) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (dact && next_cur) request_rows(t + 1, Next{});
+    if (active) compute(t, stage);
+    if (t + 1 < n_ct) {
+      if (dact) decode(t + 1, Next{}, wN);
+    } else if (next_cur) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
     tile_barrier();                    // tile t read by all; tile t + 1 in place
   };
   for (int t = 0; t < n_tiles; t += 2) {
-    iter(t, std::integral_constant<int, 0>{}, wk0, wv0, wk1, wv1);
-    if (t + 1 < n_tiles) iter(t + 1, std::integral_constant<int, 1>{}, wk1, wv1, wk0, wv0);
+    iter(t, std::integral_constant<int, 0>{}, w0, w1);
+    if (t + 1 < n_tiles) iter(t + 1, std::integral_constant<int, 1>{}, w1, w0);
   }
 
-  // ---- epilogue: 1/l; value columns back to coordinate order (OCTOPUS
-  // values, through LDS); then R_v^T = diag(s_v) H / sqrt(d) on every query
-  // row.  Lane holds coordinate 16 c + col of queries q0 + 16 rg + 4 grp +
-  // r: the Hadamard butterflies on coordinate bits 4..6 are register-local,
-  // bits 0..3 cross lanes within each 16-lane group.
+  // ---- epilogue, one 16-query row group at a time: 1/l; value columns back
+  // to coordinate order (OCTOPUS values, through the wavefront's own rows of
+  // LDS); then R_v^T = diag(s_v) H / sqrt(d) on every query row.  Lane holds
+  // coordinate 16 c + col of queries q0 + 16 rg + 4 grp + r: the Hadamard
+  // butterflies on coordinate bits 4..6 are register-local, bits 0..3 cross
+  // lanes within each 16-lane group.
+  if (!active) return;
   float sv[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) sv[c] = kInvSqrtD * splitmix_sign(a.vseed, 16 * c + col);
   constexpr int kORow = kHeadDim + 4;                  // floats per query row in LDS
-  float* ob = reinterpret_cast<float*>(tiles) + wave * (16 * kRG * kORow);
+  static_assert(kCWaves * 16 * kORow * 4 <= kTilesBytes, "epilogue rows fit the tiles");
+  float* ob = reinterpret_cast<float*>(tiles) + wave * (16 * kORow);
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg) {
     const float l_tot = rows_sum(l_run[rg]);   // the row's four lane groups
-    float li[4];
+    float v[8][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float l = __shfl(l_tot, 4 * grp + r, 64);
-      li[r] = l > 0.0f ? 1.0f / l : 0.0f;
+      const float li = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c][r] = o[rg][c][r] * li;
     }
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[rg][c][r] *= li[r];
-  }
-  if (a.vperm) {
-    // column 16 c + col holds coordinate part_coord(16 c + col)
-#pragma unroll
-    for (int rg = 0; rg < kRG; ++rg)
+    if (a.vperm) {
+      // column 16 c + col holds coordinate part_coord(16 c + col)
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int crd = part_coord(16 * c + col);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ob[(16 * rg + 4 * grp + r) * kORow + crd] = o[rg][c][r];
+        for (int r = 0; r < 4; ++r) ob[(4 * grp + r) * kORow + crd] = v[c][r];
       }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int rg = 0; rg < kRG; ++rg)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[rg][c][r] = ob[(16 * rg + 4 * grp + r) * kORow + 16 * c + col];
-  }
-#pragma unroll
-  for (int rg = 0; rg < kRG; ++rg) {
-    float v[8][4];
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[c][r] = o[rg][c][r];
+        for (int r = 0; r < 4; ++r) v[c][r] = ob[(4 * grp + r) * kORow + 16 * c + col];
+      // the rows are read before the next row group writes them
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 #pragma unroll
     for (int m = 4; m >= 1; m >>= 1)
 #pragma unroll
@@ -1046,7 +1085,7 @@ __global__ __launch_bounds__(kCThreads, 2) void chunk_attn_kernel(ChunkArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int q = q0 + 16 * rg + 4 * grp + r;
       if (q >= a.Tq) continue;
-      float* dst = a.out + (((size_t)b * a.Hq + hq) * a.Tq + q) * kHeadDim;
+      float* dst = a.out + ((size_t)bh * a.Tq + q) * kHeadDim;
 #pragma unroll
       for (int c = 0; c < 8; ++c) dst[16 * c + col] = v[c][r] * sv[c];
     }
@@ -1108,15 +1147,12 @@ const void* chunk_kernel(bool corr, int ksel, int vsel) {
               : reinterpret_cast<const void*>(&chunk_attn_kernel<false, 0, 0>);
 }
 
-// LDS bytes of an OCTOPUS codec's table (and rho pairs).
+// LDS bytes of an OCTOPUS codec's table in its copies (and rho pairs).
 int table_bytes(const Codec& c, int* rho_off) {
-  const int KK = c.K * c.K;
-  if (KK * c.R <= kMaxPre) {
-    *rho_off = KK * c.R * 8;
-    return KK * c.R * 8;
-  }
-  *rho_off = KK * 8;
-  return KK * 8 + c.R * 4;
+  const int entries = pre_entries(c.b_dir, c.b_nrm);
+  const int tab = entries * 8 * tab_copies(c.b_dir, c.b_nrm);
+  *rho_off = tab;
+  return entries == c.K * c.K * c.R ? tab : tab + c.R * 4;
 }
 
 }  // namespace
@@ -1233,7 +1269,12 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   a.Hq = num_q_heads;
   a.Hkv = Hkv;
   a.Tq = Tq;
-  a.q_tiles = (Tq + kBM - 1) / kBM;
+  a.qb = (Tq + kQB - 1) / kQB;
+  const long long n_blocks = (long long)B * num_q_heads * a.qb;
+  if (n_blocks > 0x7fffffffLL) return fail(OCTO_ERR_UNSUPPORTED, "%s: too many query blocks", what);
+  a.n_blocks = (int)n_blocks;
+  a.bpp = (num_q_heads / Hkv) * a.qb;
+  a.packed = a.bpp >= kCWaves;
   a.cached = cached_tokens;
   a.Tc = Tc;
   a.Tc_pad = p.Tc_pad;
@@ -1271,12 +1312,14 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
     }
   }
   const size_t dyn_bytes = (size_t)(off + 15) / 16 * 16;
-  const long long units = (long long)a.q_tiles * num_q_heads * B;
-  if (units > 0x7fffffffLL)
-    return fail(OCTO_ERR_UNSUPPORTED, "%s: too many query tiles", what);
+  const long long units = a.packed ? (n_blocks + kCWaves - 1) / kCWaves : (long long)B * Hkv;
+  const void* fn = chunk_kernel(corr, a.kcod.sel, a.vcod.sel);
+  if (dyn_bytes > 65536) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_bytes);
+    if (e != hipSuccess) return fail(OCTO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  }
   void* kargs[] = {&a};
-  const hipError_t e = hipLaunchKernel(chunk_kernel(corr, a.kcod.sel, a.vcod.sel), dim3((unsigned)units),
-                                       dim3(kCThreads), kargs, dyn_bytes, stream);
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)units), dim3(kCThreads), kargs, dyn_bytes, stream);
   if (e != hipSuccess) return fail(OCTO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return check_launch(what);
 }
