@@ -462,7 +462,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   constexpr bool PRE = MODE == kPre;                // pre-split (code, rho) table
   constexpr bool BIG = K * K * R > kMaxSmallPre;    // one shared table, one WG per CU
   constexpr int kTab = PRE ? K * K * R : K * K;     // entries per table (16 B each)
-  constexpr int kTabBytes = (VG || (PRE && BIG) ? 1 : 2) * kTab * 16;   // VG: the K table alone
+  // Small pre-split tables are stored in kCopies interleaved copies (entry
+  // e of copy c at kCopies e + c; lane L reads copy L mod kCopies), at most
+  // 32 KB a table: the 16 lanes that one LDS pass of a 16-byte gather serves
+  // then read 16 different bank quads whatever their entries.
+  constexpr int kCopies = !PRE || BIG ? 1 : (kTab * 16 * 16 <= 32768 ? 16 : 32768 / (kTab * 16));
+  constexpr int kTabBytes = (VG || (PRE && BIG) ? 1 : 2) * kTab * 16 * kCopies;   // VG: the K table alone
   using GR = GroupRecord<(VG ? BD - 1 : 2), (VG ? VG : 32)>;            // the value record (VG)
   static_assert(BlockWords<BD, BN, QJL, VG>::WI <= kZeroBlockWords / 64 &&
                     BlockWords<BD, BN, QJL, VG>::VW <= kZeroBlockWords / 64,
@@ -494,8 +499,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
   // table sits at a constant offset that the LDS reads take as an
   // immediate.  fp32 tables are shared when the codebooks agree.
   uint4* tabk = reinterpret_cast<uint4*>(smem);
-  uint4* tabv = PRE ? (BIG ? tabk : tabk + kTab) : (a.shared_tables ? tabk : tabk + kTab);
+  uint4* tabv = PRE ? (BIG ? tabk : tabk + kTab * kCopies) : (a.shared_tables ? tabk : tabk + kTab);
   float* red_o = reinterpret_cast<float*>(smem);          // [wave][head][128]
+  // this lane's copy of each table
+  const uint4* tabk_l = tabk + (L & (kCopies - 1));
+  const uint4* tabv_l = tabv + (L & (kCopies - 1));
 
   // ---- every global load of the prologue goes out first, none waiting for
   // another: codebooks, q, the first block and seq_lens.  The kernel
@@ -585,9 +593,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
       const float* cx = v ? cxv : cxk;
       const float* cr = v ? crv : crk;
       const float4 n = decode_dir(cx[code % K], cx[code / K]);
-      uint4* t = tabk + (v ? kTab : 0);
+      uint4* t = tabk + (v ? kTab * kCopies : 0);
 #pragma unroll
-      for (int r = 0; r < R; ++r) t[r * KK + code] = presplit_entry(n, cr[r]);
+      for (int r = 0; r < R; ++r) {
+        const uint4 en = presplit_entry(n, cr[r]);
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) t[(r * KK + code) * kCopies + c] = en;
+      }
     }
   } else {
     for (int e = tid; e < n_tables * kTab; e += kThreads) {
@@ -775,7 +787,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
           // rho K^2 + code pair, and the entry {hx|hy, hz|0, lx|ly, lz|0},
           // one 16-byte read (random gathers conflict least in wide reads),
           // is the A operand as it stands
-          const half8 A = __builtin_bit_cast(half8, tabk[field<BT>(iw, m * BT)]);
+          const half8 A = __builtin_bit_cast(half8, tabk_l[field<BT>(iw, m * BT) * kCopies]);
           acc = mfma(A, ql[m], acc);
           acc = mfma(A, qh[m], acc);
         }
@@ -1011,7 +1023,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_kernel(DecodeArgs a) {
         if (PRE) {
           uint4 E[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) E[e] = tabv[(pw2[e >> 1] >> (16 * (e & 1))) & 0xffffu];
+          for (int e = 0; e < 8; ++e) E[e] = tabv_l[((pw2[e >> 1] >> (16 * (e & 1))) & 0xffffu) * kCopies];
           operands_pre(E, bh, bl);
         } else {
           float vx[8], vy[8], vz[8];
