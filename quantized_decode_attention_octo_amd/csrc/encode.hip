@@ -1,11 +1,8 @@
 // octo_encode: the OCTOPUS encoder on gfx950.
 //
-// One lane encodes one token, entirely in registers, following the OCTOPUS
-// paper (arXiv 2605.21226):
-//   Sec. 3.1      gamma = ||x||_2 and u = R x / gamma with R = H diag(s): the
-//                 sign flip is an xor with a 128-bit mask (wave ballots of
-//                 the SplitMix64 signs), the Walsh-Hadamard transform is the
-//                 7-stage butterfly on the lane's 128 registers;
+// Each token follows the OCTOPUS paper (arXiv 2605.21226):
+//   Sec. 3.1      gamma = ||x||_2 and u = R x / gamma with R = H diag(s)
+//                 (the SplitMix64 signs as 128-bit wave-ballot masks);
 //   Sec. 3.2      u zero-padded to 129 coordinates, 43 triplets t_i, the
 //                 octahedral coordinates (xi, eta) of Eq. 5;
 //   Sec. 3.5      scalar Lloyd seeds, then the local 3x3 joint rounding: the
@@ -15,20 +12,25 @@
 //                 rho = ||t||;
 //   Sec. 3.6      with QJL: r = u - u^, sigma = sign(H diag(s') r) and
 //                 gamma_r = fp16(||r||);
-//   Sec. 3        the indices of I_dir and I_nrm, packed in registers at
-//                 constant bit offsets as one field per triplet
+//   Sec. 3        the indices of I_dir and I_nrm as one field per triplet
 //                 (xi | eta << b_dir | rho << 2 b_dir, B_tri bits).
-// group_encode_kernel encodes the group-wise value codec the same way.
-// A workgroup of 256 lanes takes 256 consecutive tokens of one (batch, head)
-// plane; in the tile-64 layout word w of 64 consecutive tokens is 256
-// contiguous bytes, so every word store of a wavefront is one coalesced
-// 256-byte write.  LDS holds the codebooks, their cell boundaries and, for
-// every code pair, the decoded unit direction n(xi^, eta^) with the pair's
-// code, in a table padded by one clamped cell per side so that the 3x3
-// search is nine reads at constant offsets and two selects per candidate.
-// The kernel is bound for two wavefronts per SIMD (at most 256 VGPRs).
+// Two kernels compute the same records (the choice is in launch()):
+//   encode_row_kernel   one lane a token, the row in 128 registers, the
+//                       Walsh-Hadamard transform the 7-stage butterfly in
+//                       registers, the fields packed at constant offsets;
+//                       a workgroup of 256 lanes takes 256 tokens;
+//   encode_part_kernel  four lanes a token, the rotation on the matrix cores
+//                       (see its section), a workgroup of 64 tokens.
+// group_encode_kernel encodes the group-wise value codec (one lane a token).
+// In the tile-64 layout word w of 64 consecutive tokens is 256 contiguous
+// bytes, so the word stores are coalesced.  LDS holds the codebooks, their
+// cell boundaries and, for every code pair, the decoded unit direction
+// n(xi^, eta^) with the pair's code, in a table padded by one clamped cell
+// per side so that the 3x3 search is nine reads at constant offsets and two
+// selects per candidate.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "octo_internal.h"
@@ -181,8 +183,10 @@ __device__ inline void load_row(const EncodeArgs& a, int b, int h, int t, bool v
   }
 }
 
+// One lane per token, the whole row in 128 registers: the rotation is the
+// 7-stage butterfly in registers.  Two wavefronts a SIMD.
 template <int BD, int BN>
-__global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void encode_row_kernel(EncodeArgs a) {
   constexpr int K = 1 << BD, R = 1 << BN;
   constexpr int FWD = 2 * BD;                         // xi | eta << BD
   constexpr int BT = FWD + BN;                        // + rho << 2 BD: one field per triplet
@@ -373,6 +377,440 @@ __global__ __launch_bounds__(kThreads, 2) void encode_kernel(EncodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- encoder, four lanes a token
+// Four lanes per token.  A wavefront takes 16 tokens at a time (column col =
+// L % 16 of the matrix products) and lane group g = L / 16 of a token holds
+// its coordinates 32 g .. 32 g + 31.
+//
+// Rotation: with k = 8 k_hi + k_lo (Sylvester order) H_128 = H_16 (x) H_8,
+// so R x = H diag(s) x is, for each k_lo, the 16 x 16 product
+//   V_klo[r_hi][token] = sum_khi H_16[r_hi][k_hi] s_(8 k_hi + k_lo) x_(8 k_hi + k_lo)
+// -- one v_mfma_f32_16x16x16_bf16 whose operands are exact (+-1 and the bf16
+// input; an fp32 input is split into three bf16 terms, each product exact in
+// the fp32 accumulation) -- followed by the 8-point transform over k_lo in
+// registers: y_(8 r_hi + r_lo) = sum_klo H_8[r_lo][k_lo] V_klo[r_hi].  The
+// product's lane layout leaves rows r_hi = 4 g .. 4 g + 3 in lane group g,
+// that is, coordinates 32 g .. 32 g + 31 again.
+//
+// Triplets: through the wavefront's rows of LDS, lane group g takes the
+// coordinates of triplets 10 g .. 10 g + 9 and of triplet 40 + g (g < 3), so
+// that the triplet code runs with compile-time register indices; each field
+// is OR-ed into the token's record in LDS at its bit offset, and the
+// records are stored word by word, 16 tokens (64 bytes) a store.
+constexpr int kTokTile = 16;                 // tokens of a wavefront tile
+constexpr int kEncWaves = 4;
+constexpr int kEncThreads = 64 * kEncWaves;  // 64 tokens per workgroup
+constexpr int kXRow = kHeadDim + 4;          // floats per token row of the exchange rows
+constexpr int kRecRow = 21;                  // record words per token row (W <= 19, odd pitch)
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4e __attribute__((ext_vector_type(4)));
+
+// bf16 bits of v rounded to nearest even (finite inputs)
+__device__ inline uint32_t bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// H_8 (Sylvester order, unnormalized) on eight registers.
+__device__ inline void wht8(float (&v)[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!(i & h)) {
+        const float p = v[i], q = v[i + h];
+        v[i] = p + q;
+        v[i + h] = p - q;
+      }
+}
+
+// y = H diag(s) x for the lane's token, coordinates 32 g + m in y[m]; the
+// input is given as bf16 terms: bterm(t, k_lo) returns the B operand
+// {x_(32 g + 8 e + k_lo) : e = 0..3} of term t.  amat[k_lo] holds the A
+// operands {H_16[L % 16][4 g + e] s_(32 g + 8 e + k_lo)}.
+template <int NT, class BTerm>
+__device__ inline void rotate16(const short4v (&amat)[8], BTerm&& bterm, float (&y)[32]) {
+  floatx4e d[8];
+#pragma unroll
+  for (int kl = 0; kl < 8; ++kl) {
+    d[kl] = floatx4e{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      d[kl] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(amat[kl], bterm(t, kl), d[kl], 0, 0, 0);
+  }
+  // rows r_hi = 4 g + r: the 8-point transform over k_lo
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float v[8];
+#pragma unroll
+    for (int kl = 0; kl < 8; ++kl) v[kl] = d[kl][r];
+    wht8(v);
+#pragma unroll
+    for (int rl = 0; rl < 8; ++rl) y[8 * r + rl] = v[rl];
+  }
+}
+
+// The three bf16 terms of an fp32 value: hi = bf16(x), mid = bf16(x - hi),
+// lo = bf16(x - hi - mid), whose sum is x to about 2^-24 relative.
+__device__ inline void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = bf16_rne(x);
+  const float r1 = x - __uint_as_float(hi << 16);
+  mid = bf16_rne(r1);
+  const float r2 = r1 - __uint_as_float(mid << 16);
+  lo = bf16_rne(r2);
+}
+
+// Sum of a value over the four lane groups of a token (lanes L, L ^ 16,
+// L ^ 32, L ^ 48), the same in all four.
+__device__ inline float groups_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+template <int BD, int BN, bool F32>
+__global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs a) {
+  constexpr int K = 1 << BD, R = 1 << BN;
+  constexpr int FWD = 2 * BD;                         // xi | eta << BD
+  constexpr int BT = FWD + BN;                        // + rho << 2 BD: one field per triplet
+  constexpr int WI = (kNTri * BT + 31) / 32;
+  static_assert(WI < kRecRow, "record row");
+
+  constexpr int KP = K + 2;                           // padded side of the direction table
+  // Direction table, padded by one cell on every side: entry (i, j), i, j in
+  // [-1, K], at (i + 1) + KP (j + 1) holds n(c_xi[i'], c_xi[j']) and the code
+  // pair i' | j' << BD of the clamped cell (i', j'), so the 3x3 neighbourhood
+  // of a seed is nine reads at constant offsets, and a clamped neighbour is
+  // the same candidate as the cell it clamps to.
+  __shared__ floatx4 lut[KP * KP];
+  __shared__ float cxi[K], midp[K + 1], crho[R], mid_rho[R];
+  __shared__ int guess_bad;
+  // per wavefront: the exchange rows and the records of its 16 tokens
+  __shared__ __attribute__((aligned(16))) float xrows[kEncWaves][kTokTile][kXRow];
+  __shared__ uint32_t recs[kEncWaves][kTokTile][kRecRow];
+
+  const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
+  const int col = L & 15, g = L >> 4;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const size_t plane = (size_t)b * a.H + h;
+  // the workgroup's 64 tokens: wavefront w takes tokens 16 w + (0..15)
+  const int t = blockIdx.x * (kEncWaves * kTokTile) + kTokTile * wave + col;
+  const bool valid = t < a.T;
+
+  // ---- signs of R (and R') as 128-bit masks; this lane group's 32 bits
+  const uint64_t sm0 = __ballot(splitmix_sign(a.seed, L) < 0.0f);
+  const uint64_t sm1 = __ballot(splitmix_sign(a.seed, L + 64) < 0.0f);
+  const uint64_t qm0 = __ballot(splitmix_sign(a.seed, kHeadDim + L) < 0.0f);
+  const uint64_t qm1 = __ballot(splitmix_sign(a.seed, kHeadDim + L + 64) < 0.0f);
+  // A operands of H diag(s) (and of H diag(s')):
+  // {H_16[col][4 g + e] s_(32 g + 8 e + k_lo)}, the signs the lane group's
+  // 32 bits of the mask
+  auto a_operands = [&](uint64_t m0, uint64_t m1, short4v (&am)[8]) __attribute__((always_inline)) {
+    const uint32_t sb = (uint32_t)((g < 2 ? m0 : m1) >> (32 * (g & 1)));
+#pragma unroll
+    for (int kl = 0; kl < 8; ++kl)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t neg = (__builtin_popcount(col & (4 * g + e)) ^ (sb >> (8 * e + kl))) & 1u;
+        am[kl][e] = (short)(neg ? 0xbf80 : 0x3f80);
+      }
+  };
+  short4v am[8];
+  a_operands(sm0, sm1, am);
+
+  // ---- the lane's 32 coordinates (bf16 input: words xw, pairs (2 j,
+  // 2 j + 1); fp32 input: xf), zeros past the last token, issued before the
+  // tables are built
+  uint32_t xw[F32 ? 1 : 16];
+  float xf[F32 ? 32 : 1];
+  {
+    const int64_t off = (int64_t)b * a.s0 + (int64_t)h * a.s1 + (int64_t)(valid ? t : 0) * a.s2 + 32 * g;
+    if constexpr (!F32) {
+      const uint16_t* row = static_cast<const uint16_t*>(a.x) + off;
+      if (a.vec16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint4 w = reinterpret_cast<const uint4*>(row)[k];
+          xw[4 * k] = valid ? w.x : 0u;
+          xw[4 * k + 1] = valid ? w.y : 0u;
+          xw[4 * k + 2] = valid ? w.z : 0u;
+          xw[4 * k + 3] = valid ? w.w : 0u;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          xw[j] = valid ? (uint32_t)row[2 * j] | ((uint32_t)row[2 * j + 1] << 16) : 0u;
+      }
+    } else {
+      const float* row = static_cast<const float*>(a.x) + off;
+      if (a.vec16) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float4 w = reinterpret_cast<const float4*>(row)[k];
+          xf[4 * k] = valid ? w.x : 0.0f;
+          xf[4 * k + 1] = valid ? w.y : 0.0f;
+          xf[4 * k + 2] = valid ? w.z : 0.0f;
+          xf[4 * k + 3] = valid ? w.w : 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) xf[j] = valid ? row[j] : 0.0f;
+      }
+    }
+  }
+
+  // ---- tables: codebooks, cell boundaries, decoded directions
+  if (tid < K) cxi[tid] = a.cb.xi[tid];
+  if (tid < R) crho[tid] = a.cb.rho[tid];
+  if (tid == 0) {
+    guess_bad = 0;
+    midp[0] = -INFINITY;
+    midp[K] = INFINITY;
+  }
+  __syncthreads();
+  if (tid < K - 1) {
+    const float m = 0.5f * (cxi[tid] + cxi[tid + 1]);
+    midp[tid + 1] = m;
+    // uniform grid boundaries b_k = -1 + 2 (k + 1) / K; the one-step
+    // correction is exact when b_(k-1) <= mid_k < b_(k+1) (with a margin
+    // for the rounding of the grid index)
+    const float lo = tid > 0 ? -1.0f + 2.0f * tid / K : -INFINITY;
+    const float hi = tid + 2 < K ? -1.0f + 2.0f * (tid + 2) / K : INFINITY;
+    if (!(m >= lo + 1e-5f && m < hi - 1e-5f)) guess_bad = 1;
+  }
+  if (tid < R - 1) mid_rho[tid] = 0.5f * (crho[tid] + crho[tid + 1]);
+  for (int e = tid; e < KP * KP; e += kEncThreads) {
+    // Eq. 6 with the fold of App. C.7, then normalization onto S^2.
+    const int ci = min(max(e % KP - 1, 0), K - 1), cj = min(max(e / KP - 1, 0), K - 1);
+    const float xi = cxi[ci], eta = cxi[cj];
+    const float z = 1.0f - fabsf(xi) - fabsf(eta);
+    float x = xi, y = eta;
+    if (z < 0.0f) {
+      x = (xi >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(eta));
+      y = (eta >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(xi));
+    }
+    const float n = fmaxf(sqrtf(x * x + y * y + z * z), kEps);
+    lut[e] = floatx4{x / n, y / n, z / n, __uint_as_float((uint32_t)(ci | (cj << BD)))};
+  }
+  __syncthreads();
+  // uniform: a scalar branch, not a masked one
+  const bool guess_ok = __builtin_amdgcn_readfirstlane(guess_bad) == 0;
+  float mr[R > 1 ? R - 1 : 1];
+#pragma unroll
+  for (int k = 0; k < R - 1; ++k) mr[k] = mid_rho[k];
+
+  float* xr = xrows[wave][col];
+  uint32_t* rec = recs[wave][col];
+  const bool scalar = a.rounding == OCTO_ROUND_SCALAR;     // kernel argument: uniform
+  const bool has_tail = g < 3;
+  // coordinate j of the lane's 32
+  auto xval = [&](int j) __attribute__((always_inline)) {
+    if constexpr (F32) return xf[j];
+    else return __uint_as_float(j & 1 ? xw[j >> 1] & 0xffff0000u : xw[j >> 1] << 16);
+  };
+  // the token records start empty
+  for (int i = L; i < kTokTile * kRecRow; i += 64) (&recs[wave][0][0])[i] = 0u;
+  // ---- gamma, rotation, scaling (Sec. 3.1)
+  float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 32; ++j) ss[j & 3] = fmaf(xval(j), xval(j), ss[j & 3]);
+  const float gamma = sqrtf(groups_sum((ss[0] + ss[1]) + (ss[2] + ss[3])));
+  float y[32];
+  if constexpr (!F32) {
+    rotate16<1>(am, [&](int, int kl) {
+      // {x_(8 e + kl)}: halves kl % 2 of words 4 e + kl / 2
+      const uint32_t sel = kl & 1 ? 0x07060302u : 0x05040100u;
+      const uint32_t p01 = __builtin_amdgcn_perm(xw[4 + (kl >> 1)], xw[kl >> 1], sel);
+      const uint32_t p23 = __builtin_amdgcn_perm(xw[12 + (kl >> 1)], xw[8 + (kl >> 1)], sel);
+      return __builtin_bit_cast(short4v, make_uint2(p01, p23));
+    }, y);
+  } else {
+    uint32_t tw[3][16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3(xf[2 * j], h0, m0, l0);
+      split3(xf[2 * j + 1], h1, m1, l1);
+      tw[0][j] = h0 | (h1 << 16);
+      tw[1][j] = m0 | (m1 << 16);
+      tw[2][j] = l0 | (l1 << 16);
+    }
+    rotate16<3>(am, [&](int tt, int kl) {
+      const uint32_t sel = kl & 1 ? 0x07060302u : 0x05040100u;
+      const uint32_t p01 = __builtin_amdgcn_perm(tw[tt][4 + (kl >> 1)], tw[tt][kl >> 1], sel);
+      const uint32_t p23 = __builtin_amdgcn_perm(tw[tt][12 + (kl >> 1)], tw[tt][8 + (kl >> 1)], sel);
+      return __builtin_bit_cast(short4v, make_uint2(p01, p23));
+    }, y);
+  }
+  const float scale = kInvSqrtD / fmaxf(gamma, kEps);
+
+  // ---- to the triplet layout: coordinates 30 g .. 30 g + 29 (triplets
+  // 10 g .. 10 g + 9) and 120 + 3 g .. 122 + 3 g (triplet 40 + g; the zero
+  // pad at 128)
+#pragma unroll
+  for (int j = 0; j < 32; j += 4)
+    *reinterpret_cast<floatx4*>(&xr[32 * g + j]) =
+        floatx4{y[j] * scale, y[j + 1] * scale, y[j + 2] * scale, y[j + 3] * scale};
+  if (g == 0) *reinterpret_cast<floatx4*>(&xr[kHeadDim]) = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float v[33];
+#pragma unroll
+  for (int j = 0; j < 30; j += 2) {
+    const float2 p = *reinterpret_cast<const float2*>(&xr[30 * g + j]);
+    v[j] = p.x;
+    v[j + 1] = p.y;
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) v[30 + j] = has_tail ? xr[120 + 3 * g + j] : 0.0f;
+
+  // ---- triplets: octahedral map, seeds, joint rounding, fields
+  StaticFor<0, 11>::run([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    // one triplet at a time: keeps the scheduler from interleaving the
+    // iterations (and their table reads) into a register spill
+    __builtin_amdgcn_sched_barrier(0);
+    if (m == 10 && !has_tail) return;
+    const int i = m < 10 ? 10 * g + m : 40 + g;          // the triplet
+    const float tx = v[3 * m], ty = v[3 * m + 1], tz = v[3 * m + 2];
+    // Eq. 5 on the L1-normalized direction, sign(0) = +1.
+    const float inv_l1 = __builtin_amdgcn_rcpf(fmaxf(fabsf(tx) + fabsf(ty) + fabsf(tz), kEps));
+    const float px = tx * inv_l1, py = ty * inv_l1, pz = tz * inv_l1;
+    float xi = px, eta = py;
+    if (pz < 0.0f) {
+      xi = (px >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(py));
+      eta = (py >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(px));
+    }
+    int sx, sy;
+    if (guess_ok) {
+      sx = seed_guess<K>(midp, xi);
+      sy = seed_guess<K>(midp, eta);
+    } else {
+      sx = seed_search<K>(midp, xi);
+      sy = seed_search<K>(midp, eta);
+    }
+    // corner (-1, -1) of the seed's neighbourhood; candidate (dx, dy) sits at
+    // offset (dx + 1) + KP (dy + 1)
+    const floatx4* nbh = &lut[sx + KP * sy];
+    floatx4 n0 = nbh[1 + KP];
+    pin(n0);
+    uint32_t code = __float_as_uint(n0.w);
+    int ir;
+    if (scalar) {
+      ir = rho_index<R>(mr, sqrtf(tx * tx + ty * ty + tz * tz));
+    } else {
+      // Seed first, then the other eight neighbours row-major (dx outer);
+      // only a strictly larger s replaces the incumbent.
+      float best = tx * n0.x + ty * n0.y + tz * n0.z;
+#pragma unroll
+      for (int dx = 0; dx < 3; ++dx)
+#pragma unroll
+        for (int dy = 0; dy < 3; ++dy) {
+          if (dx == 1 && dy == 1) continue;
+          floatx4 n = nbh[dx + KP * dy];
+          pin(n);
+          const float s = tx * n.x + ty * n.y + tz * n.z;
+          const bool up = s > best;
+          best = up ? s : best;
+          code = up ? __float_as_uint(n.w) : code;
+        }
+      ir = rho_index<R>(mr, best);
+    }
+    // the field at bit i B_tri of the record (LSB-first stream)
+    {
+      const uint32_t f = code | ((uint32_t)ir << FWD);
+      const int pos = i * BT, w = pos >> 5, sh = pos & 31;
+      __hip_atomic_fetch_or(&rec[w], f << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (sh + BT > 32)
+        __hip_atomic_fetch_or(&rec[w + 1], f >> (32 - sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (a.qjl) {
+      // rotated-frame residual r = u - u^ (Sec. 3.6), over the real coordinates
+      floatx4 nb = n0;
+      if (!scalar) {
+        nb = lut[(code & (K - 1)) + 1 + KP * ((code >> BD) + 1)];
+        pin(nb);
+      }
+      const float rho = crho[ir];
+      v[3 * m] = tx - rho * nb.x;
+      v[3 * m + 1] = ty - rho * nb.y;
+      v[3 * m + 2] = tz - rho * nb.z;
+    }
+  });
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // ---- stores: word w of 64 consecutive tokens is 256 contiguous bytes;
+  // lane group g stores words g, g + 4, .. of the 16 tokens
+  const int tc = a.token_offset + t;
+  if (valid) {
+#pragma unroll
+    for (int w0 = 0; w0 < WI; w0 += 4)
+      if (w0 + g < WI) a.idx[tile_word(plane, a.capacity, tc, w0 + g, WI)] = rec[w0 + g];
+    if (g == 0) a.gamma[plane * a.capacity + tc] = gamma;
+  }
+
+  // ---- QJL: sigma = sign(H diag(s') r), gamma_r = fp16(||r||)
+  if (a.qjl) {
+    // the residual back to coordinate order (the pad is not written)
+#pragma unroll
+    for (int j = 0; j < 30; j += 2) *reinterpret_cast<float2*>(&xr[30 * g + j]) = make_float2(v[j], v[j + 1]);
+    if (has_tail) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (120 + 3 * g + j < kHeadDim) xr[120 + 3 * g + j] = v[30 + j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float rv[32];
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) {
+      const floatx4 q = *reinterpret_cast<const floatx4*>(&xr[32 * g + j]);
+      rv[j] = q[0];
+      rv[j + 1] = q[1];
+      rv[j + 2] = q[2];
+      rv[j + 3] = q[3];
+    }
+    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) rs[j & 3] = fmaf(rv[j], rv[j], rs[j & 3]);
+    const float rn = sqrtf(groups_sum((rs[0] + rs[1]) + (rs[2] + rs[3])));
+    uint32_t tw[3][16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3(rv[2 * j], h0, m0, l0);
+      split3(rv[2 * j + 1], h1, m1, l1);
+      tw[0][j] = h0 | (h1 << 16);
+      tw[1][j] = m0 | (m1 << 16);
+      tw[2][j] = l0 | (l1 << 16);
+    }
+    short4v aq[8];
+    a_operands(qm0, qm1, aq);
+    float z[32];
+    rotate16<3>(aq, [&](int tt, int kl) {
+      const uint32_t sel = kl & 1 ? 0x07060302u : 0x05040100u;
+      const uint32_t p01 = __builtin_amdgcn_perm(tw[tt][4 + (kl >> 1)], tw[tt][kl >> 1], sel);
+      const uint32_t p23 = __builtin_amdgcn_perm(tw[tt][12 + (kl >> 1)], tw[tt][8 + (kl >> 1)], sel);
+      return __builtin_bit_cast(short4v, make_uint2(p01, p23));
+    }, z);
+    uint32_t sw = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) sw |= (uint32_t)(z[j] < 0.0f) << j;
+    if (valid) {
+      a.qjl_bits[tile_word(plane, a.capacity, tc, g, 4)] = sw;
+      if (g == 0) {
+        const _Float16 hr = (_Float16)rn;
+        a.gamma_r[plane * a.capacity + tc] = __builtin_bit_cast(uint16_t, hr);
+      }
+    }
+  }
+}
+
 // The group-wise value codec (group = 16 or 32): one lane per token, u = R x
 // in registers as above, then per group of GS coordinates the range, the
 // E4M3 step size, the BF16 zero-point and the codes (the quantizer of
@@ -434,10 +872,30 @@ __global__ __launch_bounds__(kThreads, 2) void group_encode_kernel(EncodeArgs a)
   }
 }
 
+// Which encoder.  The four-lanes-a-token kernel forms its rotations on the
+// matrix cores and has four times the wavefronts of the one-lane kernel for
+// the same tokens: it is faster for launches too small to fill the GPU with
+// one-lane wavefronts, for QJL keys (a second rotation per token) and for
+// b_dir <= 4 (measured on the 8192-, 32768- and 131072-token workloads:
+// equal at (4, 2), faster at (3, 1)).  With b_dir >= 5 its larger direction
+// table and register count make the one-lane kernel faster on large
+// launches (32768 tokens x 4 heads at (5, 3): 92 against 115 us for K and V).
+constexpr int64_t kPartMaxTokens = 100000;
+
 template <int BD, int BN>
 void launch(const EncodeArgs& a, hipStream_t st) {
-  dim3 grid((a.T + kThreads - 1) / kThreads, a.H, a.B);
-  hipLaunchKernelGGL((encode_kernel<BD, BN>), grid, dim3(kThreads), 0, st, a);
+  const int64_t n_tok = (int64_t)a.B * a.H * a.T;
+  if (BD <= 4 || a.qjl || n_tok < kPartMaxTokens) {
+    const void* fn = a.is_bf16 ? reinterpret_cast<const void*>(&encode_part_kernel<BD, BN, false>)
+                               : reinterpret_cast<const void*>(&encode_part_kernel<BD, BN, true>);
+    constexpr int kTok = kEncWaves * kTokTile;
+    EncodeArgs args = a;
+    void* kargs[] = {&args};
+    (void)hipLaunchKernel(fn, dim3((a.T + kTok - 1) / kTok, a.H, a.B), dim3(kEncThreads), kargs, 0, st);
+  } else {
+    dim3 grid((a.T + kThreads - 1) / kThreads, a.H, a.B);
+    hipLaunchKernelGGL((encode_row_kernel<BD, BN>), grid, dim3(kThreads), 0, st, a);
+  }
 }
 
 template <int VB, int GS>
@@ -501,6 +959,7 @@ extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, 
   a.gamma_r = dst->gamma_r;
   a.capacity = dst->capacity;
   a.token_offset = token_offset;
+
   if (c.group) {
     switch (c.bits * 100 + c.group) {
       case 216: launch_group<2, 16>(a, stream); break;
