@@ -14,14 +14,9 @@
 //                 gamma_r = fp16(||r||);
 //   Sec. 3        the indices of I_dir and I_nrm as one field per triplet
 //                 (xi | eta << b_dir | rho << 2 b_dir, B_tri bits).
-// Two kernels compute the same records (the choice is in launch()):
-//   encode_row_kernel   one lane a token, the row in 128 registers, the
-//                       Walsh-Hadamard transform the 7-stage butterfly in
-//                       registers, the fields packed at constant offsets;
-//                       a workgroup of 256 lanes takes 256 tokens;
-//   encode_part_kernel  four lanes a token, the rotation on the matrix cores
-//                       (see its section), a workgroup of 64 tokens.
-// group_encode_kernel encodes the group-wise value codec (one lane a token).
+// encode_part_kernel gives each token four lanes and forms the rotation on
+// the matrix cores (see its section).  group_encode_kernel encodes the
+// group-wise value codec, one lane a token with the row in 128 registers.
 // In the tile-64 layout word w of 64 consecutive tokens is 256 contiguous
 // bytes, so the word stores are coalesced.  LDS holds the codebooks, their
 // cell boundaries and, for every code pair, the decoded unit direction
@@ -54,6 +49,8 @@ struct EncodeArgs {
   uint32_t* qjl_bits;
   uint16_t* gamma_r;
   int capacity, token_offset;
+  // signs of R and R' (bit k % 32 of word k / 32: s_k < 0), from the seed
+  uint32_t smask[4], qmask[4];
 };
 
 // Nearest of the K sorted centroids of C_xi: the number of the K-1 cell
@@ -183,201 +180,7 @@ __device__ inline void load_row(const EncodeArgs& a, int b, int h, int t, bool v
   }
 }
 
-// One lane per token, the whole row in 128 registers: the rotation is the
-// 7-stage butterfly in registers.  Two wavefronts a SIMD.
-template <int BD, int BN>
-__global__ __launch_bounds__(kThreads, 2) void encode_row_kernel(EncodeArgs a) {
-  constexpr int K = 1 << BD, R = 1 << BN;
-  constexpr int FWD = 2 * BD;                         // xi | eta << BD
-  constexpr int BT = FWD + BN;                        // + rho << 2 BD: one field per triplet
-  constexpr int WI = (kNTri * BT + 31) / 32;
-
-  constexpr int KP = K + 2;                           // padded side of the direction table
-  // Direction table, padded by one cell on every side: entry (i, j), i, j in
-  // [-1, K], at (i + 1) + KP (j + 1) holds n(c_xi[i'], c_xi[j']) and the code
-  // pair i' | j' << BD of the clamped cell (i', j'), so the 3x3 neighbourhood
-  // of a seed is nine reads at constant offsets, and a clamped neighbour is
-  // the same candidate as the cell it clamps to.
-  __shared__ floatx4 lut[KP * KP];
-  __shared__ float cxi[K], midp[K + 1], crho[R], mid_rho[R];
-  __shared__ int guess_bad;
-
-  const int tid = threadIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int t = blockIdx.x * kThreads + tid;
-  const bool valid = t < a.T;
-  const size_t plane = (size_t)b * a.H + h;
-
-  // ---- signs of R (and R') as 128-bit masks, identical in every lane
-  const int ln = tid & 63;
-  const uint64_t sm0 = __ballot(splitmix_sign(a.seed, ln) < 0.0f);
-  const uint64_t sm1 = __ballot(splitmix_sign(a.seed, ln + 64) < 0.0f);
-  const uint64_t qm0 = __ballot(splitmix_sign(a.seed, kHeadDim + ln) < 0.0f);
-  const uint64_t qm1 = __ballot(splitmix_sign(a.seed, kHeadDim + ln + 64) < 0.0f);
-
-  // ---- the row of this token, issued before the tables are built
-  float v[128];
-  load_row(a, b, h, t, valid, v);
-
-  // ---- tables: codebooks, cell boundaries, decoded directions
-  if (tid < K) cxi[tid] = a.cb.xi[tid];
-  if (tid < R) crho[tid] = a.cb.rho[tid];
-  if (tid == 0) {
-    guess_bad = 0;
-    midp[0] = -INFINITY;
-    midp[K] = INFINITY;
-  }
-  __syncthreads();
-  if (tid < K - 1) {
-    const float m = 0.5f * (cxi[tid] + cxi[tid + 1]);
-    midp[tid + 1] = m;
-    // uniform grid boundaries b_k = -1 + 2 (k + 1) / K; the one-step
-    // correction is exact when b_(k-1) <= mid_k < b_(k+1) (with a margin
-    // for the rounding of the grid index)
-    const float lo = tid > 0 ? -1.0f + 2.0f * tid / K : -INFINITY;
-    const float hi = tid + 2 < K ? -1.0f + 2.0f * (tid + 2) / K : INFINITY;
-    if (!(m >= lo + 1e-5f && m < hi - 1e-5f)) guess_bad = 1;
-  }
-  if (tid < R - 1) mid_rho[tid] = 0.5f * (crho[tid] + crho[tid + 1]);
-  for (int e = tid; e < KP * KP; e += kThreads) {
-    // Eq. 6 with the fold of App. C.7, then normalization onto S^2.
-    const int ci = min(max(e % KP - 1, 0), K - 1), cj = min(max(e / KP - 1, 0), K - 1);
-    const float xi = cxi[ci], eta = cxi[cj];
-    const float z = 1.0f - fabsf(xi) - fabsf(eta);
-    float x = xi, y = eta;
-    if (z < 0.0f) {
-      x = (xi >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(eta));
-      y = (eta >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(xi));
-    }
-    const float n = fmaxf(sqrtf(x * x + y * y + z * z), kEps);
-    lut[e] = floatx4{x / n, y / n, z / n, __uint_as_float((uint32_t)(ci | (cj << BD)))};
-  }
-  __syncthreads();
-  // uniform: a scalar branch, not a masked one
-  const bool guess_ok = __builtin_amdgcn_readfirstlane(guess_bad) == 0;
-  float mr[R > 1 ? R - 1 : 1];
-#pragma unroll
-  for (int k = 0; k < R - 1; ++k) mr[k] = mid_rho[k];
-
-  // ---- gamma, sign flip, rotation (Sec. 3.1)
-  float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int j = 0; j < 128; ++j) ss[j & 3] = fmaf(v[j], v[j], ss[j & 3]);
-  const float gamma = sqrtf((ss[0] + ss[1]) + (ss[2] + ss[3]));
-  flip_signs(v, sm0, sm1);
-  wht128_regs(v);
-  const float scale = kInvSqrtD / fmaxf(gamma, kEps);
-#pragma unroll
-  for (int j = 0; j < 128; ++j) {
-    v[j] *= scale;
-    pin(v[j]);
-  }
-
-  // ---- triplets: octahedral map, seeds, joint rounding, packing
-  uint32_t iw[WI + 1];
-#pragma unroll
-  for (int w = 0; w <= WI; ++w) iw[w] = 0u;
-  const bool scalar = a.rounding == OCTO_ROUND_SCALAR;     // kernel argument: uniform
-  StaticFor<0, kNTri>::run([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    // one triplet at a time: keeps the scheduler from interleaving the 43
-    // iterations (and their table reads) into a register spill
-    __builtin_amdgcn_sched_barrier(0);
-    const float tx = v[3 * i], ty = v[3 * i + 1];
-    const float tz = 3 * i + 2 < kHeadDim ? v[3 * i + 2] : 0.0f;   // the zero pad
-    // Eq. 5 on the L1-normalized direction, sign(0) = +1.
-    const float inv_l1 = __builtin_amdgcn_rcpf(fmaxf(fabsf(tx) + fabsf(ty) + fabsf(tz), kEps));
-    const float px = tx * inv_l1, py = ty * inv_l1, pz = tz * inv_l1;
-    float xi = px, eta = py;
-    if (pz < 0.0f) {
-      xi = (px >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(py));
-      eta = (py >= 0.0f ? 1.0f : -1.0f) * (1.0f - fabsf(px));
-    }
-    int sx, sy;
-    if (guess_ok) {
-      sx = seed_guess<K>(midp, xi);
-      sy = seed_guess<K>(midp, eta);
-    } else {
-      sx = seed_search<K>(midp, xi);
-      sy = seed_search<K>(midp, eta);
-    }
-    // corner (-1, -1) of the seed's neighbourhood; candidate (dx, dy) sits at
-    // offset (dx + 1) + KP (dy + 1)
-    const floatx4* nbh = &lut[sx + KP * sy];
-    floatx4 n0 = nbh[1 + KP];
-    pin(n0);
-    uint32_t code = __float_as_uint(n0.w);
-    int ir;
-    if (scalar) {
-      ir = rho_index<R>(mr, sqrtf(tx * tx + ty * ty + tz * tz));
-    } else {
-      // Seed first, then the other eight neighbours row-major (dx outer);
-      // only a strictly larger s replaces the incumbent.
-      float best = tx * n0.x + ty * n0.y + tz * n0.z;
-#pragma unroll
-      for (int dx = 0; dx < 3; ++dx)
-#pragma unroll
-        for (int dy = 0; dy < 3; ++dy) {
-          if (dx == 1 && dy == 1) continue;
-          floatx4 n = nbh[dx + KP * dy];
-          pin(n);
-          const float s = tx * n.x + ty * n.y + tz * n.z;
-          const bool up = s > best;
-          best = up ? s : best;
-          code = up ? __float_as_uint(n.w) : code;
-        }
-      ir = rho_index<R>(mr, best);
-    }
-    // pack the triplet's field at its constant bit offset (LSB-first stream)
-    {
-      constexpr int pos = i * BT, w = pos >> 5, sh = pos & 31;
-      const uint32_t f = code | ((uint32_t)ir << FWD);
-      iw[w] |= f << sh;
-      if (sh + BT > 32) iw[w + 1] |= f >> ((32 - sh) & 31);
-    }
-    if (a.qjl) {
-      // rotated-frame residual r = u - u^ (Sec. 3.6), over the real coordinates
-      floatx4 nb = n0;
-      if (!scalar) {
-        nb = lut[(code & (K - 1)) + 1 + KP * ((code >> BD) + 1)];
-        pin(nb);
-      }
-      const float rho = crho[ir];
-      v[3 * i] = tx - rho * nb.x;
-      v[3 * i + 1] = ty - rho * nb.y;
-      if (3 * i + 2 < kHeadDim) v[3 * i + 2] = tz - rho * nb.z;
-    }
-  });
-
-  // ---- stores: word w of 64 consecutive tokens is 256 contiguous bytes
-  const int tc = a.token_offset + t;
-  if (valid) {
-#pragma unroll
-    for (int w = 0; w < WI; ++w) a.idx[tile_word(plane, a.capacity, tc, w, WI)] = iw[w];
-    a.gamma[plane * a.capacity + tc] = gamma;
-  }
-
-  // ---- QJL: sigma = sign(H diag(s') r), gamma_r = fp16(||r||)
-  if (a.qjl) {
-    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < 128; ++j) rs[j & 3] = fmaf(v[j], v[j], rs[j & 3]);
-    const float rn = sqrtf((rs[0] + rs[1]) + (rs[2] + rs[3]));
-    flip_signs(v, qm0, qm1);
-    wht128_regs(v);
-    uint32_t sw[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 128; ++j) sw[j >> 5] |= (uint32_t)(v[j] < 0.0f) << (j & 31);
-    if (valid) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) a.qjl_bits[tile_word(plane, a.capacity, tc, w, 4)] = sw[w];
-      const _Float16 hr = (_Float16)rn;
-      a.gamma_r[plane * a.capacity + tc] = __builtin_bit_cast(uint16_t, hr);
-    }
-  }
-}
-
-// ---------------------------------------------------------------- encoder, four lanes a token
+// ---------------------------------------------------------------- encoder
 // Four lanes per token.  A wavefront takes 16 tokens at a time (column col =
 // L % 16 of the matrix products) and lane group g = L / 16 of a token holds
 // its coordinates 32 g .. 32 g + 31.
@@ -469,7 +272,7 @@ __device__ inline float groups_sum(float x) {
   return x;
 }
 
-template <int BD, int BN, bool F32>
+template <int BD, int BN, bool F32, int TILES>
 __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs a) {
   constexpr int K = 1 << BD, R = 1 << BN;
   constexpr int FWD = 2 * BD;                         // xi | eta << BD
@@ -494,37 +297,37 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
   const int col = L & 15, g = L >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
   const size_t plane = (size_t)b * a.H + h;
-  // the workgroup's 64 tokens: wavefront w takes tokens 16 w + (0..15)
-  const int t = blockIdx.x * (kEncWaves * kTokTile) + kTokTile * wave + col;
-  const bool valid = t < a.T;
+  // the workgroup's 64 TILES tokens: tile it of wavefront w is tokens
+  // base + 16 (4 it + w) + (0..15)
+  const int base = blockIdx.x * (kEncWaves * kTokTile * TILES);
+  auto token_of = [&](int it) { return base + kTokTile * (kEncWaves * it + wave) + col; };
 
-  // ---- signs of R (and R') as 128-bit masks; this lane group's 32 bits
-  const uint64_t sm0 = __ballot(splitmix_sign(a.seed, L) < 0.0f);
-  const uint64_t sm1 = __ballot(splitmix_sign(a.seed, L + 64) < 0.0f);
-  const uint64_t qm0 = __ballot(splitmix_sign(a.seed, kHeadDim + L) < 0.0f);
-  const uint64_t qm1 = __ballot(splitmix_sign(a.seed, kHeadDim + L + 64) < 0.0f);
-  // A operands of H diag(s) (and of H diag(s')):
-  // {H_16[col][4 g + e] s_(32 g + 8 e + k_lo)}, the signs the lane group's
-  // 32 bits of the mask
-  auto a_operands = [&](uint64_t m0, uint64_t m1, short4v (&am)[8]) __attribute__((always_inline)) {
-    const uint32_t sb = (uint32_t)((g < 2 ? m0 : m1) >> (32 * (g & 1)));
+  // ---- A operands of H diag(s) (and of H diag(s')):
+  // {H_16[col][4 g + e] s_(32 g + 8 e + k_lo)} as bf16 +-1, from the lane
+  // group's 32 sign bits
+  auto a_operands = [&](const uint32_t (&mask)[4], short4v (&am)[8]) __attribute__((always_inline)) {
+    // bit 8 e + k_lo of x: the sign of entry e of the k_lo operand
+    uint32_t x = g == 0 ? mask[0] : g == 1 ? mask[1] : g == 2 ? mask[2] : mask[3];
 #pragma unroll
-    for (int kl = 0; kl < 8; ++kl)
+    for (int e = 0; e < 4; ++e) x ^= (uint32_t)(__builtin_popcount(col & (4 * g + e)) & 1) * (0xffu << (8 * e));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t neg = (__builtin_popcount(col & (4 * g + e)) ^ (sb >> (8 * e + kl))) & 1u;
-        am[kl][e] = (short)(neg ? 0xbf80 : 0x3f80);
-      }
+    for (int kl = 0; kl < 8; ++kl) {
+      const uint32_t y = x >> kl;
+      const uint32_t w0 = 0x3f803f80u | ((y << 15) & 0x8000u) | ((y << 23) & 0x80000000u);
+      const uint32_t w1 = 0x3f803f80u | ((y >> 1) & 0x8000u) | ((y << 7) & 0x80000000u);
+      am[kl] = __builtin_bit_cast(short4v, make_uint2(w0, w1));
+    }
   };
   short4v am[8];
-  a_operands(sm0, sm1, am);
+  a_operands(a.smask, am);
 
-  // ---- the lane's 32 coordinates (bf16 input: words xw, pairs (2 j,
-  // 2 j + 1); fp32 input: xf), zeros past the last token, issued before the
-  // tables are built
+  // ---- the lane's 32 coordinates of tile it (bf16 input: words xw, pairs
+  // (2 j, 2 j + 1); fp32 input: xf), zeros past the last token
   uint32_t xw[F32 ? 1 : 16];
   float xf[F32 ? 32 : 1];
-  {
+  auto load_x = [&](int it) __attribute__((always_inline)) {
+    const int t = token_of(it);
+    const bool valid = t < a.T;
     const int64_t off = (int64_t)b * a.s0 + (int64_t)h * a.s1 + (int64_t)(valid ? t : 0) * a.s2 + 32 * g;
     if constexpr (!F32) {
       const uint16_t* row = static_cast<const uint16_t*>(a.x) + off;
@@ -558,7 +361,8 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
         for (int j = 0; j < 32; ++j) xf[j] = valid ? row[j] : 0.0f;
       }
     }
-  }
+  };
+  load_x(0);                           // issued before the tables are built
 
   // ---- tables: codebooks, cell boundaries, decoded directions
   if (tid < K) cxi[tid] = a.cb.xi[tid];
@@ -609,6 +413,9 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
     if constexpr (F32) return xf[j];
     else return __uint_as_float(j & 1 ? xw[j >> 1] & 0xffff0000u : xw[j >> 1] << 16);
   };
+  for (int it = 0; it < TILES; ++it) {
+  const int t = token_of(it);
+  const bool valid = t < a.T;
   // the token records start empty
   for (int i = L; i < kTokTile * kRecRow; i += 64) (&recs[wave][0][0])[i] = 0u;
   // ---- gamma, rotation, scaling (Sec. 3.1)
@@ -644,6 +451,7 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
     }, y);
   }
   const float scale = kInvSqrtD / fmaxf(gamma, kEps);
+  if (it + 1 < TILES) load_x(it + 1);  // the next tile's coordinates
 
   // ---- to the triplet layout: coordinates 30 g .. 30 g + 29 (triplets
   // 10 g .. 10 g + 9) and 120 + 3 g .. 122 + 3 g (triplet 40 + g; the zero
@@ -790,7 +598,7 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
       tw[2][j] = l0 | (l1 << 16);
     }
     short4v aq[8];
-    a_operands(qm0, qm1, aq);
+    a_operands(a.qmask, aq);
     float z[32];
     rotate16<3>(aq, [&](int tt, int kl) {
       const uint32_t sel = kl & 1 ? 0x07060302u : 0x05040100u;
@@ -808,6 +616,13 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
         a.gamma_r[plane * a.capacity + tc] = __builtin_bit_cast(uint16_t, hr);
       }
     }
+  }
+  if (TILES > 1) {
+    // the rows and records are read before the next tile writes them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   }
 }
 
@@ -872,30 +687,18 @@ __global__ __launch_bounds__(kThreads, 2) void group_encode_kernel(EncodeArgs a)
   }
 }
 
-// Which encoder.  The four-lanes-a-token kernel forms its rotations on the
-// matrix cores and has four times the wavefronts of the one-lane kernel for
-// the same tokens: it is faster for launches too small to fill the GPU with
-// one-lane wavefronts, for QJL keys (a second rotation per token) and for
-// b_dir <= 4 (measured on the 8192-, 32768- and 131072-token workloads:
-// equal at (4, 2), faster at (3, 1)).  With b_dir >= 5 its larger direction
-// table and register count make the one-lane kernel faster on large
-// launches (32768 tokens x 4 heads at (5, 3): 92 against 115 us for K and V).
-constexpr int64_t kPartMaxTokens = 100000;
-
 template <int BD, int BN>
 void launch(const EncodeArgs& a, hipStream_t st) {
-  const int64_t n_tok = (int64_t)a.B * a.H * a.T;
-  if (BD <= 4 || a.qjl || n_tok < kPartMaxTokens) {
-    const void* fn = a.is_bf16 ? reinterpret_cast<const void*>(&encode_part_kernel<BD, BN, false>)
-                               : reinterpret_cast<const void*>(&encode_part_kernel<BD, BN, true>);
-    constexpr int kTok = kEncWaves * kTokTile;
-    EncodeArgs args = a;
-    void* kargs[] = {&args};
-    (void)hipLaunchKernel(fn, dim3((a.T + kTok - 1) / kTok, a.H, a.B), dim3(kEncThreads), kargs, 0, st);
-  } else {
-    dim3 grid((a.T + kThreads - 1) / kThreads, a.H, a.B);
-    hipLaunchKernelGGL((encode_row_kernel<BD, BN>), grid, dim3(kThreads), 0, st, a);
-  }
+  // b_dir >= 5: the direction table is large and the LDS allows two
+  // workgroups a compute unit anyway; each wavefront takes four tiles so
+  // that the table serves 256 tokens
+  constexpr int kTiles = BD >= 5 ? 4 : 1;
+  const void* fn = a.is_bf16 ? reinterpret_cast<const void*>(&encode_part_kernel<BD, BN, false, kTiles>)
+                             : reinterpret_cast<const void*>(&encode_part_kernel<BD, BN, true, kTiles>);
+  constexpr int kTok = kEncWaves * kTokTile * kTiles;
+  EncodeArgs args = a;
+  void* kargs[] = {&args};
+  (void)hipLaunchKernel(fn, dim3((a.T + kTok - 1) / kTok, a.H, a.B), dim3(kEncThreads), kargs, 0, st);
 }
 
 template <int VB, int GS>
@@ -959,6 +762,13 @@ extern "C" octo_status octo_encode(const octo_codec_desc* codec, const void* x, 
   a.gamma_r = dst->gamma_r;
   a.capacity = dst->capacity;
   a.token_offset = token_offset;
+  for (int w = 0; w < 4; ++w) {
+    a.smask[w] = a.qmask[w] = 0u;
+    for (int j = 0; j < 32; ++j) {
+      a.smask[w] |= (uint32_t)(splitmix_sign(c.seed, 32 * w + j) < 0.0f) << j;
+      a.qmask[w] |= (uint32_t)(splitmix_sign(c.seed, kHeadDim + 32 * w + j) < 0.0f) << j;
+    }
+  }
 
   if (c.group) {
     switch (c.bits * 100 + c.group) {

@@ -3,10 +3,9 @@
 Covers the five workload shapes at sizes the oracle finishes in seconds (with
 ragged tails), the full-size encodes on sampled tokens, appends at unaligned
 token offsets, zero vectors, the scalar rounding mode and the uniform (b, b)
-splits.  The library has two encoders (four lanes a token; one lane a token
-for b_dir >= 5 without QJL on launches of 100000 tokens or more): the small
-cases run the first, and test_encode_one_lane_kernel_paths runs the second's
-modes on launches above that size.
+splits; large launches of the b_dir >= 5 splits (the encoder takes four
+16-token tiles a wavefront there) in scalar rounding, fp32 input and two
+sweep splits.
 """
 import numpy as np
 import pytest
@@ -134,17 +133,17 @@ def test_encode_deterministic():
 @pytest.mark.parametrize("bits,b_dir,b_nrm,rounding,dtype", [
     (4, None, None, "scalar", torch.bfloat16), (4, None, None, "local3x3", torch.float32),
     (4, 6, 2, "local3x3", torch.bfloat16), (3, 5, 1, "local3x3", torch.bfloat16)])
-def test_encode_one_lane_kernel_paths(bits, b_dir, b_nrm, rounding, dtype):
-    """Launches of 4 x 25600 tokens with b_dir >= 5 and no QJL (the one-lane
-    encoder): scalar rounding, fp32 input and two sweep splits, on sampled
-    tokens of two planes."""
+def test_encode_large_launch_modes(bits, b_dir, b_nrm, rounding, dtype):
+    """Launches of 4 x 25600 tokens with b_dir >= 5 (four tiles a wavefront):
+    scalar rounding, fp32 input and two sweep splits, on sampled tokens of
+    two planes."""
     g = torch.Generator().manual_seed(11)
     x = torch.randn(1, 4, 25600, 128, generator=g).to(dtype)
     gc, hc = codecs(bits, b_dir=b_dir, b_nrm=b_nrm, rounding=rounding, seed=7)
-    say(f"one-lane encoder bits={bits} split=({b_dir},{b_nrm}) {rounding} {dtype}")
+    say(f"large encode bits={bits} split=({b_dir},{b_nrm}) {rounding} {dtype}")
     cache = encode_gpu(x, gc)
     rng = np.random.default_rng(2)
     tokens = np.sort(rng.choice(25600, size=256, replace=False))
     tokens[-1] = 25599
     assert_encode_ok(compare_encode(cache.to_host(), hc, x, planes=[(0, 0), (0, 3)], tokens=tokens),
-                     f"one-lane {bits} {b_dir} {b_nrm} {rounding} {dtype}")
+                     f"large {bits} {b_dir} {b_nrm} {rounding} {dtype}")
