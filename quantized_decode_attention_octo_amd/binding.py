@@ -120,17 +120,36 @@ def _check(status):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """torch's current stream on `device` as a raw handle."""
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _expect(t, name, shape, dtypes, contiguous=True):
     """Raises ValueError unless tensor t has exactly `shape` (None entries
     match any size) and one of `dtypes` and, if asked, is contiguous.  The library sees only pointers, so these checks
-    are the only guard against reads and writes past a buffer."""
+    are the only guard against reads and writes past a buffer.  The common
+    case (everything right) takes one comparison per property; the messages
+    come from the slow path."""
+    if type(t) is torch.Tensor and t.dtype in dtypes and (not contiguous or t.is_contiguous()):
+        sh = t.shape
+        if None in shape:
+            if len(sh) == len(shape) and all(e is None or e == n for e, n in zip(shape, sh)):
+                return
+        elif sh == shape:
+            return
+    _expect_failed(t, name, shape, dtypes, contiguous)
+
+
+def _expect_failed(t, name, shape, dtypes, contiguous):
     if not isinstance(t, torch.Tensor):
         raise ValueError(f"{name} must be a torch tensor")
     if t.dtype not in dtypes:
@@ -140,16 +159,20 @@ def _expect(t, name, shape, dtypes, contiguous=True):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want}")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    # a tensor subclass that passes every check is accepted
 
 
 def _on_device(device, **tensors):
     """Raises ValueError unless every tensor lives on `device`, a CUDA device
     (checked after the shapes, so that a shape error is named first)."""
+    idx = device.index if device.type == "cuda" else -2
     for name, t in tensors.items():
-        if t.device.type != "cuda":
-            raise ValueError(f"{name} is on {t.device}; the kernels need device memory")
-        if t.device != device:
+        if t.get_device() != idx:
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} is on {t.device}; the kernels need device memory")
             raise ValueError(f"{name} is on {t.device}, the cache on {device}")
+    if idx == -2:
+        raise ValueError(f"the cache is on {device}; the kernels need device memory")
 
 
 def _same_caches(k_cache, v_cache, k_codec, v_codec):
@@ -290,6 +313,17 @@ def octo_decode_workspace_bytes(k_codec, B, num_q_heads, kv_heads, max_seq_len):
     return n.value
 
 
+def _workspace_need(fn, k_codec, *sizes):
+    """fn(k_codec, *sizes), remembered per codec: the answer depends only on
+    the codec's layout and the sizes, and the query costs a library call."""
+    memo = k_codec.__dict__.setdefault("_ws_need", {})
+    key = (fn, sizes)
+    n = memo.get(key)
+    if n is None:
+        n = memo[key] = fn(k_codec, *sizes)
+    return n
+
+
 def workspace(nbytes, device):
     """A device buffer with at least nbytes from a 256-byte aligned start."""
     return torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
@@ -316,17 +350,18 @@ def octo_attend_decode(k_codec, v_codec, k_cache, v_cache, q, seq_lens, max_seq_
         out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
     _expect(out, "out", (B, Hq, d), (torch.float32,))
     _on_device(dev, q=q, seq_lens=seq_lens, out=out, k_cache=k_cache.idx, v_cache=v_cache.idx)
-    need = octo_decode_workspace_bytes(k_codec, B, Hq, k_cache.H, max_seq_len)
+    need = _workspace_need(octo_decode_workspace_bytes, k_codec, B, Hq, k_cache.H, max_seq_len)
     if ws is None or ws.numel() < need + 256:
         ws = workspace(need, dev)
     _expect(ws, "ws", (None,), (torch.uint8,))
-    _on_device(dev, ws=ws)
+    if ws.get_device() != q.get_device():
+        _on_device(dev, ws=ws)
     dt = DTYPE_F32 if q.dtype == torch.float32 else DTYPE_BF16
     _check(lib().octo_attend_decode(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
                                     ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
                                     _ptr(q), dt, Hq, _ptr(seq_lens), max_seq_len,
                                     float(softmax_scale), _ptr(out),
-                                    ctypes.c_void_p(_aligned_ptr(ws)), ws.numel() - 256,
+                                    _aligned_ptr(ws), ws.numel() - 256,
                                     _stream(q.device)))
     return out
 
@@ -391,18 +426,19 @@ def octo_decode_step(k_codec, v_codec, k_cache, v_cache, q, k_new, v_new, k_wind
     _on_device(dev, q=q, k_new=k_new, v_new=v_new, k_window=k_window, v_window=v_window,
                packed_lens=packed_lens, window_lens=window_lens, out=out,
                k_cache=k_cache.idx, v_cache=v_cache.idx)
-    need = octo_decode_step_workspace_bytes(k_codec, B, Hq, k_cache.H, max_packed_len)
+    need = _workspace_need(octo_decode_step_workspace_bytes, k_codec, B, Hq, k_cache.H, max_packed_len)
     if ws is None or ws.numel() < need + 256:
         ws = workspace(need, dev)
     _expect(ws, "ws", (None,), (torch.uint8,))
-    _on_device(dev, ws=ws)
+    if ws.get_device() != q.get_device():
+        _on_device(dev, ws=ws)
     dt = DTYPE_F32 if q.dtype == torch.float32 else DTYPE_BF16
     _check(lib().octo_decode_step(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
                                   ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
                                   _ptr(q), dt, Hq, _ptr(k_new), _ptr(v_new), _ptr(k_window),
                                   _ptr(v_window), W, _ptr(packed_lens), _ptr(window_lens),
                                   max_packed_len, float(softmax_scale), _ptr(out),
-                                  ctypes.c_void_p(_aligned_ptr(ws)), ws.numel() - 256,
+                                  _aligned_ptr(ws), ws.numel() - 256,
                                   _stream(q.device)))
     return out
 
@@ -436,15 +472,16 @@ def octo_attend_chunk(k_codec, v_codec, k_cache, v_cache, cached_tokens, q, k_cu
     _expect(out, "out", (B, Hq, Tq, d), (torch.float32,))
     _on_device(dev, q=q, k_cur=k_cur, v_cur=v_cur, out=out, k_cache=k_cache.idx,
                v_cache=v_cache.idx)
-    need = octo_chunk_workspace_bytes(k_codec, B, Hq, k_cache.H, Tq, cached_tokens, Tc, flags)
+    need = _workspace_need(octo_chunk_workspace_bytes, k_codec, B, Hq, k_cache.H, Tq, cached_tokens, Tc, flags)
     if ws is None or ws.numel() < need + 256:
         ws = workspace(need, dev)
     _expect(ws, "ws", (None,), (torch.uint8,))
-    _on_device(dev, ws=ws)
+    if ws.get_device() != q.get_device():
+        _on_device(dev, ws=ws)
     _check(lib().octo_attend_chunk(ctypes.byref(k_codec.desc), ctypes.byref(v_codec.desc),
                                    ctypes.byref(k_cache.view), ctypes.byref(v_cache.view),
                                    cached_tokens, _ptr(q), _ptr(k_cur), _ptr(v_cur), Hq, Tq, Tc,
                                    ctypes.c_float(softmax_scale), ctypes.c_uint32(flags), _ptr(out),
-                                   ctypes.c_void_p(_aligned_ptr(ws)), ws.numel() - 256,
+                                   _aligned_ptr(ws), ws.numel() - 256,
                                    _stream(q.device)))
     return out

@@ -55,8 +55,12 @@
 //
 // A second launch merges the splits by their log-sum-exp in split order and
 // applies R_v^T, so results do not depend on scheduling.  (Merging inside the
-// first launch needs device-scope fences, which on this chip write back and
-// invalidate a whole L2 per workgroup and cost far more than a launch.)
+// first launch, by the last workgroup of each plane to count itself in an
+// arrival counter, was slower on every workload: with device-scope fences,
+// which write back and invalidate a whole L2, the 32k call took twice as
+// long; with device-scope stores and loads of the partials instead, the
+// chain of round trips it adds at the end of the launch -- the stores, the
+// count, the loads -- still outlasted the second launch.)
 #include <math.h>
 
 #include <cstring>

@@ -180,6 +180,45 @@ def test_decode_reuses_workspace():
         assert np.abs(out.cpu().double().numpy() - ref).max() <= ATOL
 
 
+@pytest.mark.parametrize("key,B,T", [("gqa32k", 1, 1000), ("batch16", 32, 8192)])
+def test_decode_graph_replays(key, B, T):
+    """One call (scan and merge launches) captured in a HIP graph and
+    replayed four times, with an eager call on the same workspace between
+    replays: every replay matches the eager result bit for bit.  The 32k GQA
+    shape (b = 4: one eight-wave workgroup a CU) and 32 sequences of up to
+    8192 tokens (b = 3: two four-wave workgroups a CU)."""
+    w = workload(key, B=B)
+    inp = make_inputs(w, scale_T=T)
+    kc, _ = codecs(w.bits)
+    vc, _ = codecs(w.bits)
+    kcache = encode_gpu(inp["K"], kc)
+    vcache = encode_gpu(inp["V"], vc)
+    q, seq = inp["q"].cuda(), inp["seq_lens"].cuda()
+    max_len = int(inp["seq_lens"].max())
+    ws = octo.workspace(octo.octo_decode_workspace_bytes(kc, w.B, w.Hq, w.Hkv, max_len), "cuda")
+    out = torch.empty(w.B, w.Hq, 128, dtype=torch.float32, device="cuda")
+    ref = octo.octo_attend_decode(kc, vc, kcache, vcache, q, seq, max_len, ws=ws).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        octo.octo_attend_decode(kc, vc, kcache, vcache, q, seq, max_len, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        octo.octo_attend_decode(kc, vc, kcache, vcache, q, seq, max_len, out=out, ws=ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        say(f"decode graph replay {i}")
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
+        eager = octo.octo_attend_decode(kc, vc, kcache, vcache, q, seq, max_len, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref), f"eager call after replay {i}"
+
+
 def test_decode_max_len_zero():
     """max_seq_len = 0: every row is zero (the scan's speculative first-block
     loads read a zeroed device block instead of the cache)."""
