@@ -51,6 +51,7 @@ struct EncodeArgs {
   int capacity, token_offset;
   // signs of R and R' (bit k % 32 of word k / 32: s_k < 0), from the seed
   uint32_t smask[4], qmask[4];
+  int tiles;                      // 16-token tiles a wavefront (multi-tile kernels)
 };
 
 // Nearest of the K sorted centroids of C_xi: the number of the K-1 cell
@@ -204,7 +205,6 @@ constexpr int kTokTile = 16;                 // tokens of a wavefront tile
 constexpr int kEncWaves = 4;
 constexpr int kEncThreads = 64 * kEncWaves;  // 64 tokens per workgroup
 constexpr int kXRow = kHeadDim + 4;          // floats per token row of the exchange rows
-constexpr int kRecRow = 21;                  // record words per token row (W <= 19, odd pitch)
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4e __attribute__((ext_vector_type(4)));
@@ -272,13 +272,17 @@ __device__ inline float groups_sum(float x) {
   return x;
 }
 
-template <int BD, int BN, bool F32, int TILES>
-__global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs a) {
+// Three workgroups a CU for bf16 input at b_dir = 5 (LDS 52 KB each, at
+// most 168 registers a lane); smaller tables leave room for four by LDS.
+// MT: each wavefront takes a.tiles tiles, so that a large direction table
+// serves many tokens.
+template <int BD, int BN, bool F32, bool MT>
+__global__ __launch_bounds__(kEncThreads, BD == 5 && !F32 ? 3 : 2) void encode_part_kernel(EncodeArgs a) {
   constexpr int K = 1 << BD, R = 1 << BN;
   constexpr int FWD = 2 * BD;                         // xi | eta << BD
   constexpr int BT = FWD + BN;                        // + rho << 2 BD: one field per triplet
   constexpr int WI = (kNTri * BT + 31) / 32;
-  static_assert(WI < kRecRow, "record row");
+  static_assert(WI <= kXRow, "a record fits the first words of a token's row");
 
   constexpr int KP = K + 2;                           // padded side of the direction table
   // Direction table, padded by one cell on every side: entry (i, j), i, j in
@@ -289,17 +293,20 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
   __shared__ floatx4 lut[KP * KP];
   __shared__ float cxi[K], midp[K + 1], crho[R], mid_rho[R];
   __shared__ int guess_bad;
-  // per wavefront: the exchange rows and the records of its 16 tokens
+  // per wavefront: the exchange rows of its 16 tokens; once a tile's
+  // coordinates are in registers, the first words of a token's row hold its
+  // record (a separate array would keep the workgroup above a third of the
+  // CU's LDS)
   __shared__ __attribute__((aligned(16))) float xrows[kEncWaves][kTokTile][kXRow];
-  __shared__ uint32_t recs[kEncWaves][kTokTile][kRecRow];
 
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
   const int col = L & 15, g = L >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
   const size_t plane = (size_t)b * a.H + h;
-  // the workgroup's 64 TILES tokens: tile it of wavefront w is tokens
+  // the workgroup's 64 n_tiles tokens: tile it of wavefront w is tokens
   // base + 16 (4 it + w) + (0..15)
-  const int base = blockIdx.x * (kEncWaves * kTokTile * TILES);
+  const int n_tiles = MT ? a.tiles : 1;
+  const int base = blockIdx.x * (kEncWaves * kTokTile * n_tiles);
   auto token_of = [&](int it) { return base + kTokTile * (kEncWaves * it + wave) + col; };
 
   // ---- A operands of H diag(s) (and of H diag(s')):
@@ -405,7 +412,7 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
   for (int k = 0; k < R - 1; ++k) mr[k] = mid_rho[k];
 
   float* xr = xrows[wave][col];
-  uint32_t* rec = recs[wave][col];
+  uint32_t* rec = reinterpret_cast<uint32_t*>(xr);
   const bool scalar = a.rounding == OCTO_ROUND_SCALAR;     // kernel argument: uniform
   const bool has_tail = g < 3;
   // coordinate j of the lane's 32
@@ -413,11 +420,10 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
     if constexpr (F32) return xf[j];
     else return __uint_as_float(j & 1 ? xw[j >> 1] & 0xffff0000u : xw[j >> 1] << 16);
   };
-  for (int it = 0; it < TILES; ++it) {
+#pragma unroll 1
+  for (int it = 0; it < n_tiles; ++it) {
   const int t = token_of(it);
   const bool valid = t < a.T;
-  // the token records start empty
-  for (int i = L; i < kTokTile * kRecRow; i += 64) (&recs[wave][0][0])[i] = 0u;
   // ---- gamma, rotation, scaling (Sec. 3.1)
   float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -451,7 +457,7 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
     }, y);
   }
   const float scale = kInvSqrtD / fmaxf(gamma, kEps);
-  if (it + 1 < TILES) load_x(it + 1);  // the next tile's coordinates
+  if (it + 1 < n_tiles) load_x(it + 1);  // the next tile's coordinates
 
   // ---- to the triplet layout: coordinates 30 g .. 30 g + 29 (triplets
   // 10 g .. 10 g + 9) and 120 + 3 g .. 122 + 3 g (triplet 40 + g; the zero
@@ -473,6 +479,17 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
   }
 #pragma unroll
   for (int j = 0; j < 3; ++j) v[30 + j] = has_tail ? xr[120 + 3 * g + j] : 0.0f;
+  // the row's coordinates are read: its first WI words become the empty
+  // record (lane group g clears words g, g + 4, ..)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int w0 = 0; w0 < WI; w0 += 4)
+    if (w0 + g < WI) rec[w0 + g] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // ---- triplets: octahedral map, seeds, joint rounding, fields
   StaticFor<0, 11>::run([&](auto mc) {
@@ -563,6 +580,10 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
 
   // ---- QJL: sigma = sign(H diag(s') r), gamma_r = fp16(||r||)
   if (a.qjl) {
+    // the records are read (stored) before the rows take the residual
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // the residual back to coordinate order (the pad is not written)
 #pragma unroll
     for (int j = 0; j < 30; j += 2) *reinterpret_cast<float2*>(&xr[30 * g + j]) = make_float2(v[j], v[j + 1]);
@@ -617,7 +638,7 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode_part_kernel(EncodeArgs 
       }
     }
   }
-  if (TILES > 1) {
+  if (MT) {
     // the rows and records are read before the next tile writes them
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -687,18 +708,29 @@ __global__ __launch_bounds__(kThreads, 2) void group_encode_kernel(EncodeArgs a)
   }
 }
 
+constexpr int kCUs = 256;                     // compute units of the MI355X
+
 template <int BD, int BN>
 void launch(const EncodeArgs& a, hipStream_t st) {
-  // b_dir >= 5: the direction table is large and the LDS allows two
-  // workgroups a compute unit anyway; each wavefront takes four tiles so
-  // that the table serves 256 tokens
-  constexpr int kTiles = BD >= 5 ? 4 : 1;
-  const void* fn = a.is_bf16 ? reinterpret_cast<const void*>(&encode_part_kernel<BD, BN, false, kTiles>)
-                             : reinterpret_cast<const void*>(&encode_part_kernel<BD, BN, true, kTiles>);
-  constexpr int kTok = kEncWaves * kTokTile * kTiles;
+  // b_dir >= 5: the direction table is large and costs a workgroup as much
+  // as several tiles, so each wavefront takes as many tiles as fill the
+  // chip with one round of resident workgroups (three a CU with bf16 input
+  // at b_dir = 5, two with fp32 input, one at b_dir = 6, bound by the LDS
+  // and the registers)
+  constexpr bool kMT = BD >= 5;
   EncodeArgs args = a;
+  args.tiles = 1;
+  if (kMT) {
+    const int per_cu = BD >= 6 ? 1 : (a.is_bf16 ? 3 : 2);
+    const int64_t tok = (int64_t)a.T * a.H * a.B;
+    const int64_t slots = (int64_t)kCUs * per_cu * kEncWaves * kTokTile;
+    args.tiles = (int)std::max<int64_t>(1, (tok + slots - 1) / slots);
+  }
+  const void* fn = a.is_bf16 ? reinterpret_cast<const void*>(&encode_part_kernel<BD, BN, false, kMT>)
+                             : reinterpret_cast<const void*>(&encode_part_kernel<BD, BN, true, kMT>);
+  const int tok_wg = kEncWaves * kTokTile * args.tiles;
   void* kargs[] = {&args};
-  (void)hipLaunchKernel(fn, dim3((a.T + kTok - 1) / kTok, a.H, a.B), dim3(kEncThreads), kargs, 0, st);
+  (void)hipLaunchKernel(fn, dim3((a.T + tok_wg - 1) / tok_wg, a.H, a.B), dim3(kEncThreads), kargs, 0, st);
 }
 
 template <int VB, int GS>
