@@ -324,8 +324,9 @@ octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B
  * R_v v_cur and gamma u^ of the cached tokens (Eq. 13); the epilogue applies
  * R_v^T.  The cached window is decoded inside the attention kernel, tile by
  * tile, into on-chip memory: it is read once per query tile as packed words
- * and never written out.  The workspace receives only the fp16 rotated
- * queries and the fp16 rotated key and value rows of the current chunk.
+ * and never written out.  The queries are rotated inside the attention
+ * kernel too; the workspace receives only the fp16 rotated key and value
+ * rows of the current chunk, which every query tile of a plane reads.
  *   q          device bf16 [B, num_q_heads, Tq, d] contiguous, 16-byte aligned.
  *   k_cur,v_cur device bf16 [B, kv_heads, Tc, d] contiguous, 16-byte aligned
  *              (may be NULL if Tc == 0).

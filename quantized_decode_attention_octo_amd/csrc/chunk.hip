@@ -56,29 +56,21 @@ __host__ __device__ inline int part_coord(int pos) {
   return o < 30 ? 30 * p + o : 120 + 2 * p + (o - 30);
 }
 
-// ---------------------------------------------------------------- pre-passes
-// Rows t < T_out of a plane: fp16(post H diag(s) x_t), zero for t >= T (tile
-// padding); post = 1 / sqrt(d), times the softmax scale and log2(e) for the
-// queries, so that scores come out of the MFMA in log2 units.  Row out_off +
-// t of an [out_rows][stride] plane (stride >= 128 halves; the halves past 128
-// are not written), coordinates in part order (part_pos) when `perm` is set.
+// ---------------------------------------------------------------- pre-pass
+// Rows t < T_out of a plane of the current chunk's keys or values:
+// fp16(H diag(s) x_t / sqrt(d)), zero for t >= T (tile padding).  Row t of
+// an [out_rows][stride] plane (stride >= 128 halves; the halves past 128 are
+// not written), coordinates in part order (part_pos) when `perm` is set.
 // One workgroup takes 64 rows, sixteen lanes a row for the transform; the
 // part order is applied through LDS so that each lane still stores 16 bytes.
-//
-// With `feat` set (queries of the Jensen-bias correction), row t also gets
-// kFeat fp16 features: slot j < 128 / feat_gs holds feat_c ||(R x_t)_j||^2
-// over group j of the rotated coordinates, the other slots 0.
-constexpr int kFeat = 8;           // feature slots per row: groups of g >= 16
+// Every workgroup of a plane reads these rows, so they are transformed once
+// here; the queries are transformed inside the attention kernel.
 struct RotJob {
   const uint16_t* in;            // [planes][T][128] bf16
   int T, T_out;
   uint64_t seed;
-  float post;
   _Float16* out;
-  int out_rows, out_off, stride;
-  _Float16* feat;                // query features, or null
-  int feat_gs;
-  float feat_c;
+  int out_rows, stride;
   int tiles, planes;             // 64-row tiles per plane; planes (0: no job)
   int perm;                      // coordinates in part order
 };
@@ -89,12 +81,8 @@ __device__ inline void rotate_rows(const RotJob& jb, int tile_x, int plane, _Flo
   typedef _Float16 half8v __attribute__((ext_vector_type(8)));
   const uint16_t* __restrict__ in = jb.in;
   _Float16* __restrict__ out = jb.out;
-  const int T = jb.T, T_out = jb.T_out, out_rows = jb.out_rows, out_off = jb.out_off;
+  const int T = jb.T, T_out = jb.T_out, out_rows = jb.out_rows;
   const uint64_t seed = jb.seed;
-  const float post = jb.post;
-  _Float16* __restrict__ feat = jb.feat;
-  const int feat_gs = jb.feat_gs;
-  const float feat_c = jb.feat_c;
   // Sixteen lanes take a row, lane cl holding coordinates 8 cl .. 8 cl + 7
   // (one 16-byte load and store); a wavefront instruction covers 4 rows.
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -143,7 +131,7 @@ __device__ inline void rotate_rows(const RotJob& jb, int tile_x, int plane, _Flo
       }
     half8v o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (_Float16)(v[e] * post);
+    for (int e = 0; e < 8; ++e) o[e] = (_Float16)(v[e] * kInvSqrtD);
     if (jb.perm) {                                  // uniform branch
       // through the wavefront's own rows of the LDS tile
 #pragma unroll
@@ -154,40 +142,27 @@ __device__ inline void rotate_rows(const RotJob& jb, int tile_x, int plane, _Flo
       o = *reinterpret_cast<const half8v*>(&tile[k * kRotRow + 8 * cl]);
     }
     if (t < T_out)
-      *reinterpret_cast<half8v*>(out + ((size_t)plane * out_rows + out_off + t) * jb.stride + 8 * cl) = o;
-    if (feat != nullptr) {                          // uniform branch
-      // group sums of the squared rotated coordinates: a group of feat_gs
-      // coordinates is feat_gs / 8 consecutive lanes of the row
-      float sq = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sq = fmaf(v[e] * kInvSqrtD, v[e] * kInvSqrtD, sq);
-      const int lpg = feat_gs / 8;
-      for (int m = 1; m < lpg; m <<= 1) sq += __shfl_xor(sq, m, 64);
-      // slot cl < kFeat of the row's feature vector: group cl, or 0 past the groups
-      const int ng = kHeadDim / feat_gs;
-      const float f = __shfl(sq, 16 * sub + min(cl, ng - 1) * lpg, 64);
-      if (t < T && cl < kFeat) feat[((size_t)plane * T + t) * kFeat + cl] = (_Float16)(cl < ng ? feat_c * f : 0.0f);
-    }
+      *reinterpret_cast<half8v*>(out + ((size_t)plane * out_rows + t) * jb.stride + 8 * cl) = o;
   }
 }
 
-// The three row transforms of a chunk call (queries; current keys; current
-// values) in one launch, so that the loads of one overlap the stores of
-// another: workgroups [0, n0) take job 0, the next n1 job 1, the rest job 2,
-// where n_i = tiles_i planes_i.
-__global__ __launch_bounds__(256) void rotate_rows_kernel(RotJob q, RotJob k, RotJob v) {
+// The two row transforms of a chunk call (current keys; current values) in
+// one launch, so that the loads of one overlap the stores of the other:
+// workgroups [0, n0) take job 0, the rest job 1, where n0 = tiles_0 planes_0.
+__global__ __launch_bounds__(256) void rotate_rows_kernel(RotJob k, RotJob v) {
   __shared__ __attribute__((aligned(16))) _Float16 tile[64 * kRotRow];
-  const int n0 = q.tiles * q.planes, n1 = k.tiles * k.planes;
-  int id = blockIdx.x;
-  if (id < n0) {
-    rotate_rows(q, id % q.tiles, id / q.tiles, tile);
-  } else if ((id -= n0) < n1) {
+  const int n0 = k.tiles * k.planes;
+  const int id = blockIdx.x;
+  if (id < n0)
     rotate_rows(k, id % k.tiles, id / k.tiles, tile);
-  } else {
-    id -= n1;
-    rotate_rows(v, id % v.tiles, id / v.tiles, tile);
-  }
+  else
+    rotate_rows(v, (id - n0) % v.tiles, (id - n0) / v.tiles, tile);
 }
+
+// Query features of the Jensen-bias correction: kFeat fp16 slots per query
+// row; slot j < 128 / g holds feat_c ||(R q)_j||^2 over group j of the
+// rotated coordinates, the other slots 0.
+constexpr int kFeat = 8;           // feature slots per row: groups of g >= 16
 
 __device__ inline float4 oct_dir(float xi, float eta) {
   const float z = 1.0f - fabsf(xi) - fabsf(eta);
@@ -290,7 +265,12 @@ struct ChunkCodec {
 };
 
 struct ChunkArgs {
-  const _Float16* q;     // [B][Hq][Tq][128] rotated, times scale log2(e) / sqrt(d)
+  const uint16_t* q;     // [B][Hq][Tq][128] bf16, rotated in the kernel
+  uint64_t kseed;        // R of the keys (the queries' rotation)
+  float q_post;          // scale log2(e) / sqrt(d)
+  int kperm;             // queries in part order (OCTOPUS keys)
+  float feat_c;          // Jensen-bias correction: query feature factor
+  int feat_gs;           // ... and group size
   const _Float16* kc;    // current keys [B][Hkv][Tc_pad][128] rotated
   const _Float16* vc;    // current values [B][Hkv][Tc_pad][kVRowHalves] rotated
   float* out;            // [B][Hq][Tq][128]
@@ -302,7 +282,6 @@ struct ChunkArgs {
   int qb, n_blocks, bpp, packed;
   int cached, Tc, Tc_pad, capacity;
   uint64_t vseed;
-  const _Float16* qfeat; // Jensen-bias correction: query features [B][Hq][Tq][kFeat]
   const uint32_t *k_idx, *v_idx;
   const float *k_gamma, *v_gamma;
   ChunkCodec kcod, vcod;
@@ -661,6 +640,8 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   // argument block; then the tables
   constexpr int kCb = kMaxXi + kMaxRho;
   float* cbs = reinterpret_cast<float*>(tiles + kTilesBytes) - 2 * kCb;
+  static_assert(kCWaves * kQB * kHeadDim * 2 + 2 * kCb * 4 <= kTilesBytes,
+                "the query stagings and the codebooks share the tile area");
   {
     // constant indices into the argument block (a run-time index would put
     // a copy of it in private memory)
@@ -675,15 +656,79 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
       cbs[kCb + tid] = cv;
     }
   }
-  if constexpr (CORR) {
-    // each wavefront's 32 query feature rows (rows past Tq repeat the last)
-    if (L < kQB) {
-      const int qrow = min(q0 + L, a.Tq - 1);
-      *reinterpret_cast<half8*>(&qfs[(wave * kQB + L) * kFeat]) =
-          *reinterpret_cast<const half8*>(a.qfeat + ((size_t)bh * a.Tq + qrow) * kFeat);
+  // ---- the wavefront's 32 query rows (rows past Tq repeat the last):
+  // fp16(post H diag(s) q) in part order for OCTOPUS keys, staged in the
+  // wavefront's 8 KB of the tile area (free until the first tile; the
+  // codebooks sit past the eight stagings) with 16-byte chunk c of row r at
+  // chunk c ^ (r mod 16), then read back as the B fragments.  Sixteen lanes
+  // take a row, lane cl coordinates 8 cl .. 8 cl + 7: butterflies over bits
+  // 0..2 in registers, 3..6 across the row's lanes.  With the correction the
+  // group sums of the squared rotated coordinates give the query features.
+  half8 qf[kRG][4];
+  {
+    _Float16* stg = reinterpret_cast<_Float16*>(tiles) + wave * kQB * kHeadDim;
+    const int sub = L >> 4, cl = L & 15;
+    float sg[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sg[e] = splitmix_sign(a.kseed, 8 * cl + e);
+    uint4 raw[kQB / 4];
+#pragma unroll
+    for (int j = 0; j < kQB / 4; ++j) {
+      const int qrow = min(q0 + 4 * j + sub, a.Tq - 1);
+      raw[j] = *reinterpret_cast<const uint4*>(a.q + ((size_t)bh * a.Tq + qrow) * kHeadDim + 8 * cl);
     }
+#pragma unroll
+    for (int j = 0; j < kQB / 4; ++j) {
+      const int r = 4 * j + sub;
+      const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16)) * sg[e];
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!(e & m)) {
+            const float x = v[e], y = v[e | m];
+            v[e] = x + y;
+            v[e | m] = x - y;
+          }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __shfl_xor(v[e], m, 64);
+          v[e] = (cl & m) ? (pv - v[e]) : (v[e] + pv);
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pos = a.kperm ? part_pos(8 * cl + e) : 8 * cl + e;
+        stg[r * kHeadDim + ((((pos >> 3) ^ (r & 15)) << 3) | (pos & 7))] = (_Float16)(v[e] * a.q_post);
+      }
+      if constexpr (CORR) {
+        float sq = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq = fmaf(v[e] * kInvSqrtD, v[e] * kInvSqrtD, sq);
+        const int lpg = a.feat_gs / 8;                 // lanes of a group
+        for (int m = 1; m < lpg; m <<= 1) sq += __shfl_xor(sq, m, 64);
+        const int ng = kHeadDim / a.feat_gs;
+        const float f = __shfl(sq, 16 * sub + min(cl, ng - 1) * lpg, 64);
+        if (cl < kFeat) qfs[(wave * kQB + r) * kFeat + cl] = (_Float16)(cl < ng ? a.feat_c * f : 0.0f);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // query 16 rg + col, dims 32 s + 8 grp + e: chunk 4 s + grp of its row
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        qf[rg][s4] = *reinterpret_cast<const half8*>(
+            stg + (16 * rg + col) * kHeadDim + (((4 * s4 + grp) ^ col) << 3));
   }
-  __syncthreads();
+  __syncthreads();                     // the stagings are read before tile 0 lands
   {
     const float *cxk = cbs, *crk = cbs + kMaxXi, *cxv = cbs + kCb, *crv = cbs + kCb + kMaxXi;
     with_codec<KSEL>(a.kcod.sel, [&](auto cs) __attribute__((always_inline)) {
@@ -713,15 +758,6 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   }
   const int tstage = dten ? kVTileBytes : kKTileBytes;   // buffer 1 less buffer 0
 
-  // Q^T fragments (B operand): query q0 + 16 rg + col, dims 32 s + 8 grp + e.
-  half8 qf[kRG][4];
-#pragma unroll
-  for (int rg = 0; rg < kRG; ++rg) {
-    const int qrow = min(q0 + 16 * rg + col, a.Tq - 1);
-    const _Float16* src = a.q + ((size_t)bh * a.Tq + qrow) * kHeadDim;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qf[rg][s] = *reinterpret_cast<const half8*>(src + 32 * s + 8 * grp);
-  }
   floatx4 o[kRG][kOB];
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg)
@@ -1094,27 +1130,25 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
 
 struct ChunkPlan {
   int Tc_pad;
-  size_t q_off, k_off, v_off, qf_off, total;
+  size_t k_off, v_off, total;
 };
 
-// Workspace: fp16 rotated queries, the current chunk's rotated key rows and
-// value rows (padded to whole tiles; value rows of kVRowHalves), and with the
-// correction the query features.  Nothing of the cached window is staged.
+// Workspace: the current chunk's rotated key rows and value rows (padded to
+// whole tiles; value rows of kVRowHalves), which every workgroup of a plane
+// reads.  The queries are rotated inside the attention kernel, and nothing
+// of the cached window is staged.
 ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Tq, int Tc, bool corr) {
+  (void)Hq;
+  (void)Tq;
+  (void)corr;
   ChunkPlan p;
   p.Tc_pad = (Tc + kCurPad - 1) / kCurPad * kCurPad;
   const size_t row = kHeadDim * sizeof(_Float16);
   auto up = [](size_t n) { return (n + 255) / 256 * 256; };
-  p.q_off = 0;
-  p.k_off = up((size_t)B * Hq * Tq * row);
+  p.k_off = 0;
   const size_t kv = (size_t)B * Hkv * p.Tc_pad * row;
   p.v_off = p.k_off + up(kv);
-  p.total = p.v_off + up((size_t)B * Hkv * p.Tc_pad * kVRowBytes);
-  p.qf_off = 0;
-  if (corr) {
-    p.qf_off = p.total;
-    p.total += (size_t)B * Hq * Tq * kFeat * sizeof(_Float16);
-  }
+  p.total = std::max<size_t>(p.v_off + up((size_t)B * Hkv * p.Tc_pad * kVRowBytes), 256);
   return p;
 }
 
@@ -1234,35 +1268,37 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
     return fail(OCTO_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", what);
 
   char* ws = static_cast<char*>(workspace);
-  _Float16* qr = reinterpret_cast<_Float16*>(ws + p.q_off);
   _Float16* kr = reinterpret_cast<_Float16*>(ws + p.k_off);
   _Float16* vr = reinterpret_cast<_Float16*>(ws + p.v_off);
-  const int planes_q = B * num_q_heads, planes_kv = B * Hkv;
+  const int planes_kv = B * Hkv;
   // coordinates in part order for tensors in the OCTOPUS codec (queries and
   // current keys follow the keys' codec)
   const int kperm = kc.group ? 0 : 1, vperm = vc.group ? 0 : 1;
 
   const float tau = softmax_scale > 0.0f ? softmax_scale : kInvSqrtD;
   const float scale2 = tau * kLog2e;
-  _Float16* qf = corr ? reinterpret_cast<_Float16*>(ws + p.qf_off) : nullptr;
   // query features: minus 16 log2(e) tau^2 / 24 ||(R q)_j||^2 (the key
   // features carry Delta^2 / 16), so that their product is -b in log2 units
   const float feat_c = -16.0f * kLog2e * tau * tau / 24.0f;
-  RotJob jq{static_cast<const uint16_t*>(q), Tq, Tq, kc.seed, kInvSqrtD * scale2, qr, Tq, 0,
-            kHeadDim, qf, corr ? kc.group : 32, feat_c, (Tq + 63) / 64, planes_q, kperm};
+  // the pre-pass: the current keys and values
   const int cur_tiles = (p.Tc_pad + 63) / 64;
-  RotJob jk{static_cast<const uint16_t*>(k_cur), Tc, p.Tc_pad, kc.seed, kInvSqrtD, kr, p.Tc_pad,
-            0, kHeadDim, nullptr, 32, 0.0f, Tc > 0 ? cur_tiles : 0, planes_kv, kperm};
-  RotJob jv{static_cast<const uint16_t*>(v_cur), Tc, p.Tc_pad, vc.seed, kInvSqrtD, vr, p.Tc_pad,
-            0, kVRowHalves, nullptr, 32, 0.0f, Tc > 0 ? cur_tiles : 0, planes_kv, vperm};
-  const long rot_blocks = (long)jq.tiles * jq.planes + (long)jk.tiles * planes_kv * 2;
+  RotJob jk{static_cast<const uint16_t*>(k_cur), Tc, p.Tc_pad, kc.seed, kr, p.Tc_pad, kHeadDim,
+            cur_tiles, planes_kv, kperm};
+  RotJob jv{static_cast<const uint16_t*>(v_cur), Tc, p.Tc_pad, vc.seed, vr, p.Tc_pad, kVRowHalves,
+            cur_tiles, planes_kv, vperm};
+  const long rot_blocks = Tc > 0 ? (long)cur_tiles * planes_kv * 2 : 0;
   if (rot_blocks > 0)
-    hipLaunchKernelGGL(rotate_rows_kernel, dim3((unsigned)rot_blocks), dim3(256), 0, stream, jq, jk, jv);
+    hipLaunchKernelGGL(rotate_rows_kernel, dim3((unsigned)rot_blocks), dim3(256), 0, stream, jk, jv);
   if ((s = check_launch(what)) != OCTO_OK) return s;
 
   ChunkArgs a;
   std::memset(&a, 0, sizeof(a));
-  a.q = qr;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kseed = kc.seed;
+  a.q_post = kInvSqrtD * scale2;
+  a.kperm = kperm;
+  a.feat_c = feat_c;
+  a.feat_gs = corr ? kc.group : 32;
   a.kc = kr;
   a.vc = vr;
   a.out = out;
@@ -1280,7 +1316,6 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   a.Tc_pad = p.Tc_pad;
   a.capacity = k_cache->capacity;
   a.vseed = vc.seed;
-  a.qfeat = qf;
   a.k_idx = k_cache->idx;
   a.v_idx = v_cache->idx;
   a.k_gamma = k_cache->gamma;

@@ -230,17 +230,16 @@ def test_chunk_errors(L):
     n = ctypes.c_size_t()
     assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 0, ctypes.byref(n)) == 0
     need = n.value
-    # fp16 rotated queries [1, 2, 64, 128], the current chunk's key rows
-    # [1, 2, 64, 128] and value rows [1, 2, 64, 144] (padded rows); the
-    # cached window is decoded inside the kernel
-    assert need == (64 * 2 + 2 * 64) * 256 + 2 * 64 * 288
+    # the current chunk's rotated key rows [1, 2, 64, 128] and value rows
+    # [1, 2, 64, 144] (padded rows); the queries are rotated and the cached
+    # window decoded inside the kernel
+    assert need == 2 * 64 * 256 + 2 * 64 * 288
     # the same with 128 cached tokens more: nothing of the window is staged
     assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 256, 64, 0, ctypes.byref(n)) == 0
     assert n.value == need
-    # the correction adds 8 fp16 features per query row (the key features are
-    # formed in the kernel)
+    # the correction's query and key features are formed in the kernel
     assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 1, ctypes.byref(n)) == 0
-    assert n.value == need + 64 * 2 * 16
+    assert n.value == need
     assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 2, ctypes.byref(n)) == 1
 
     def ch(kd=kd, vd=vd, kv=kv, vv=vv, cached=128, Hq=2, Tq=64, Tc=64, ws=4096, ws_bytes=need,
