@@ -280,6 +280,14 @@ struct ChunkArgs {
   // (at most two KV planes, as a plane has bpp >= 8 blocks); else it takes
   // the bpp < 8 blocks of plane w.
   int qb, n_blocks, bpp, packed;
+  // Split tails (packed mode variant): a plane's bpp = 8 upp + r blocks go to
+  // upp workgroups of 8 whole blocks each, and the r leftover blocks are
+  // split by keys: workgroup k of the plane also scans tiles [k tt, (k+1) tt)
+  // for them (one wavefront a block) and writes unnormalized partials that a
+  // second launch merges.  No workgroup then spans two planes.
+  int tail, upp, tail_r, tail_tt;
+  float* tail_o;         // [planes][r][upp][32 rows][128] value sums (part order)
+  float2* tail_ml;       // [planes][r][upp][32 rows] (running maximum, normalizer)
   int cached, Tc, Tc_pad, capacity;
   uint64_t vseed;
   const uint32_t *k_idx, *v_idx;
@@ -613,8 +621,9 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   const int unit = xcd < full_xcds ? xcd * per_xcd + local
                                    : full_xcds * per_xcd + (xcd - full_xcds) * (per_xcd - 1) + local;
   // the workgroup's query blocks [start, start + count) and their planes
-  const int start = a.packed ? unit * kCWaves : unit * a.bpp;
-  const int count = a.packed ? min(kCWaves, a.n_blocks - start) : a.bpp;
+  const int start = a.tail ? (unit / a.upp) * a.bpp + (unit % a.upp) * kCWaves
+                           : (a.packed ? unit * kCWaves : unit * a.bpp);
+  const int count = a.tail ? kCWaves : (a.packed ? min(kCWaves, a.n_blocks - start) : a.bpp);
   const int gq = a.Hq / a.Hkv;
   auto plane_of = [&](int g) {
     const int bhq = g / a.qb;
@@ -623,10 +632,11 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   const int plane0 = plane_of(start), plane1 = plane_of(start + count - 1);
   const bool two = plane1 != plane0;
   // this wavefront's block (batch b, query head hq, queries q0 ..) and slot
-  const bool active = wave < count;
-  const int gb = start + min(wave, count - 1);
-  const int bh = gb / a.qb, q0 = (gb % a.qb) * kQB;
-  const int cslot = plane_of(gb) != plane0;
+  // (the first pass; a split tail's pass takes a leftover block)
+  bool active = wave < count;
+  int gb = start + min(wave, count - 1);
+  int bh = gb / a.qb, q0 = (gb % a.qb) * kQB;
+  int cslot = plane_of(gb) != plane0;
   // its decode task: slot, tensor (0 keys, 1 values), part parity
   const int dslot = wave >> 2, dten = (wave >> 1) & 1, dpar = wave & 1;
   const bool dact = dslot == 0 || two;
@@ -665,9 +675,13 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   // 0..2 in registers, 3..6 across the row's lanes.  With the correction the
   // group sums of the squared rotated coordinates give the query features.
   half8 qf[kRG][4];
-  {
+  auto stage_queries = [&]() __attribute__((always_inline)) {
     _Float16* stg = reinterpret_cast<_Float16*>(tiles) + wave * kQB * kHeadDim;
-    const int sub = L >> 4, cl = L & 15;
+    // from an opaque copy of the lane index, so that a later call forms its
+    // signs and offsets afresh instead of keeping the first call's live
+    int lq = L;
+    asm volatile("" : "+v"(lq));
+    const int sub = lq >> 4, cl = lq & 15;
     float sg[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sg[e] = splitmix_sign(a.kseed, 8 * cl + e);
@@ -721,13 +735,15 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // query 16 rg + col, dims 32 s + 8 grp + e: chunk 4 s + grp of its row
+    const int qcol = lq & 15, qgrp = lq >> 4;
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg)
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
         qf[rg][s4] = *reinterpret_cast<const half8*>(
-            stg + (16 * rg + col) * kHeadDim + (((4 * s4 + grp) ^ col) << 3));
-  }
+            stg + (16 * rg + qcol) * kHeadDim + (((4 * s4 + qgrp) ^ qcol) << 3));
+  };
+  stage_queries();
   __syncthreads();                     // the stagings are read before tile 0 lands
   {
     const float *cxk = cbs, *crk = cbs + kMaxXi, *cxv = cbs + kCb, *crv = cbs + kCb + kMaxXi;
@@ -742,6 +758,12 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
       });
     }
   }
+  // ---- passes: the workgroup's blocks over every tile; then, for a split
+  // tail, the plane's leftover blocks over this workgroup's share of tiles.
+  // Each pass forms its per-thread offsets afresh, so that none is kept
+  // live through the other's epilogue.
+  auto run_pass = [&](auto pass_c) __attribute__((always_inline)) {
+  constexpr int pass = decltype(pass_c)::value;
   // fp16 pair (1024, 1024) in a register (for the group codec's integers)
   uint32_t k1024;
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k1024));
@@ -759,18 +781,9 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   const int tstage = dten ? kVTileBytes : kKTileBytes;   // buffer 1 less buffer 0
 
   floatx4 o[kRG][kOB];
-#pragma unroll
-  for (int rg = 0; rg < kRG; ++rg)
-#pragma unroll
-    for (int c = 0; c < kOB; ++c) o[rg][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   // of query q0 + 16 rg + col: running maximum (log2 units; 0 until the
-  // first tile sets it), and this lane's part of the normalizer
+  // first tile of the pass sets it), and this lane's part of the normalizer
   float m_run[kRG], l_run[kRG];
-#pragma unroll
-  for (int rg = 0; rg < kRG; ++rg) {
-    m_run[rg] = 0.0f;
-    l_run[rg] = 0.0f;
-  }
 
   // the task's packed stream and gammas, and the current chunk's rows of the
   // task's plane (loads past a plane's range return zero)
@@ -791,6 +804,28 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
 
   const int n_ct = (a.cached + kBN - 1) / kBN, n_rt = (a.Tc + kBN - 1) / kBN;
   const int n_tiles = n_ct + n_rt;
+  int t_lo = 0, t_hi = n_tiles;        // the tiles of the current pass
+  if constexpr (pass == 1) {
+    const int k = unit % a.upp;
+    t_lo = min(n_tiles, k * a.tail_tt);
+    t_hi = min(n_tiles, t_lo + a.tail_tt);
+    active = wave < a.tail_r;
+    gb = plane0 * a.bpp + kCWaves * a.upp + min(wave, a.tail_r - 1);
+    bh = gb / a.qb;
+    q0 = (gb % a.qb) * kQB;
+    cslot = 0;
+    __syncthreads();                   // the first pass's epilogue rows are read
+    stage_queries();
+    __syncthreads();
+  }
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
+#pragma unroll
+    for (int c = 0; c < kOB; ++c) o[rg][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run[rg] = 0.0f;
+    l_run[rg] = 0.0f;
+  }
+
 
   // Words of the thread's row part of cached tile u into registers.
   auto load_words = [&](int u, uint32_t (&w)[NW]) __attribute__((always_inline)) {
@@ -886,7 +921,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   // serves every tile.)
   auto compute = [&](int u, auto stage) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
-    const bool cachedt = u < n_ct, first = u == 0;
+    const bool cachedt = u < n_ct, first = u == t_lo;
     const int nvalid = cachedt ? a.cached - u * kBN : a.Tc - (u - n_ct) * kBN;
     const char* ks = tiles + cslot * kSlotBytes + S * kKTileBytes;
     const char* vs = tiles + cslot * kSlotBytes + 2 * kKTileBytes + S * kVTileBytes;
@@ -1019,39 +1054,63 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     }
   };
 
-  // ---- the tile pipeline: the words of cached tile u in registers of
-  // stage u % 2, requested two tiles ahead
+  // ---- passes: the workgroup's blocks over every tile; then, for a split
+  // tail, the plane's leftover blocks over this workgroup's share of tiles
+  // ---- the tile pipeline over [t_lo, t_hi): the words of cached tile u in
+  // registers of stage (u - t_lo) % 2, requested two tiles ahead
+  const int c_hi = min(n_ct, t_hi);    // cached tiles of the pass end here
   uint32_t w0[NW] = {}, w1[NW] = {};
-  if (dact && n_ct > 0) load_words(0, w0);
-  if (dact && n_ct > 1) load_words(1, w1);
-  if (dact && n_ct == 0 && n_tiles > 0) request_rows(0, std::integral_constant<int, 0>{});
+  if (dact && t_lo < c_hi) load_words(t_lo, w0);
+  if (dact && t_lo + 1 < c_hi) load_words(t_lo + 1, w1);
+  if (dact && t_lo >= n_ct && t_lo < t_hi) request_rows(t_lo, std::integral_constant<int, 0>{});
   lds_barrier();                       // tables built
-  if (n_ct > 0) {
-    if (dact) decode(0, std::integral_constant<int, 0>{}, w0);
+  if (t_lo < c_hi) {
+    if (dact) decode(t_lo, std::integral_constant<int, 0>{}, w0);
   } else {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
   lds_barrier();
-  // iteration t, buffer and word stage S = t % 2
+  // iteration t, buffer and word stage S = (t - t_lo) % 2
   auto iter = [&](int t, auto stage, uint32_t (&wS)[NW], uint32_t (&wN)[NW]) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
     using Next = std::integral_constant<int, 1 - S>;
-    if (dact && t + 2 < n_ct) load_words(t + 2, wS);
-    const bool next_cur = t + 1 >= n_ct && t + 1 < n_tiles;
+    if (dact && t + 2 < c_hi) load_words(t + 2, wS);
+    const bool next_cur = t + 1 >= n_ct && t + 1 < t_hi;
     if (dact && next_cur) request_rows(t + 1, Next{});
     if (active) compute(t, stage);
-    if (t + 1 < n_ct) {
+    if (t + 1 < c_hi) {
       if (dact) decode(t + 1, Next{}, wN);
     } else if (next_cur) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
     tile_barrier();                    // tile t read by all; tile t + 1 in place
   };
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = t_lo; t < t_hi; t += 2) {
     iter(t, std::integral_constant<int, 0>{}, w0, w1);
-    if (t + 1 < n_tiles) iter(t + 1, std::integral_constant<int, 1>{}, w1, w0);
+    if (t + 1 < t_hi) iter(t + 1, std::integral_constant<int, 1>{}, w1, w0);
   }
 
+  if constexpr (pass == 1) {
+    // ---- a split tail's partial: per query row of the leftover block the
+    // running maximum (-inf for an empty share of tiles) and normalizer,
+    // and the unnormalized value sums in part order
+    if (active) {
+      const size_t row0 =
+          (((size_t)plane0 * a.tail_r + wave) * a.upp + unit % a.upp) * kQB;
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg) {
+        const float l_tot = rows_sum(l_run[rg]);
+        if (grp == 0)
+          a.tail_ml[row0 + 16 * rg + col] = make_float2(t_hi > t_lo ? m_run[rg] : -INFINITY, l_tot);
+#pragma unroll
+        for (int c = 0; c < kOB; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            a.tail_o[(row0 + 16 * rg + 4 * grp + r) * kHeadDim + 16 * c + col] = o[rg][c][r];
+      }
+    }
+    return;
+  }
   // ---- epilogue, one 16-query row group at a time: 1/l; value columns back
   // to coordinate order (OCTOPUS values, through the wavefront's own rows of
   // LDS); then R_v^T = diag(s_v) H / sqrt(d) on every query row.  Lane holds
@@ -1126,29 +1185,83 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
       for (int c = 0; c < 8; ++c) dst[16 * c + col] = v[c][r] * sv[c];
     }
   }
+  };
+  run_pass(std::integral_constant<int, 0>{});
+  if (a.tail) run_pass(std::integral_constant<int, 1>{});
+}
+
+// Merges a split tail's partials: one wavefront per query row of a
+// leftover block (plane p, leftover j, row), lane L holding coordinates L
+// and L + 64: the upp partials by their running maxima, 1/l, then
+// R_v^T = diag(s_v) H / sqrt(d).
+__global__ __launch_bounds__(256) void chunk_tail_merge_kernel(ChunkArgs a, int planes) {
+  const int L = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= planes * a.tail_r * kQB) return;
+  const int row = w % kQB, j = (w / kQB) % a.tail_r, p = w / (kQB * a.tail_r);
+  const int gb = p * a.bpp + kCWaves * a.upp + j;
+  const int bh = gb / a.qb, q = (gb % a.qb) * kQB + row;
+  if (q >= a.Tq) return;
+  const size_t r0 = ((size_t)p * a.tail_r + j) * a.upp;        // partial k: row (r0 + k) 32 + row
+  // every partial's maximum in one lane (upp <= 64 by the plan)
+  const float2 mlL = L < a.upp ? a.tail_ml[(r0 + L) * kQB + row] : make_float2(-INFINITY, 0.0f);
+  const float M = wave_max(mlL.x);
+  const int c0 = a.vperm ? part_pos(L) : L, c1 = a.vperm ? part_pos(L + 64) : L + 64;
+  float lsum = 0.0f, x0 = 0.0f, x1 = 0.0f;
+  if (M != -INFINITY) {                // the same in every lane
+    const float f = mlL.x == -INFINITY ? 0.0f : exp2f(mlL.x - M);
+    lsum = wave_sum(f * mlL.y);
+    for (int k = 0; k < a.upp; ++k) {
+      const float fk = __shfl(f, k, 64);
+      const float* o = a.tail_o + ((r0 + k) * kQB + row) * kHeadDim;
+      x0 = fmaf(fk, o[c0], x0);
+      x1 = fmaf(fk, o[c1], x1);
+    }
+  }
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  x0 *= inv;
+  x1 *= inv;
+  wht128(x0, x1);
+  float* dst = a.out + ((size_t)bh * a.Tq + q) * kHeadDim;
+  dst[L] = x0 * kInvSqrtD * splitmix_sign(a.vseed, L);
+  dst[L + 64] = x1 * kInvSqrtD * splitmix_sign(a.vseed, L + 64);
 }
 
 struct ChunkPlan {
   int Tc_pad;
-  size_t k_off, v_off, total;
+  int qb, bpp, packed;
+  int tail, upp, tail_r;               // split tails (see ChunkArgs)
+  size_t k_off, v_off, to_off, tml_off, total;
 };
 
-// Workspace: the current chunk's rotated key rows and value rows (padded to
-// whole tiles; value rows of kVRowHalves), which every workgroup of a plane
-// reads.  The queries are rotated inside the attention kernel, and nothing
-// of the cached window is staged.
+// The blocks of a call and their workgroups; the workspace: the current
+// chunk's rotated key rows and value rows (padded to whole tiles; value rows
+// of kVRowHalves), which every workgroup of a plane reads, and the split
+// tails' partials.  The queries are rotated inside the attention kernel, and
+// nothing of the cached window is staged.  Split tails are taken when a
+// plane has at least two workgroups of whole blocks and one to four blocks
+// over: a leftover block then adds a share of the tiles to each of the
+// plane's workgroups instead of a second plane's decoding to a workgroup
+// that spans two planes.
 ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Tq, int Tc, bool corr) {
-  (void)Hq;
-  (void)Tq;
   (void)corr;
   ChunkPlan p;
   p.Tc_pad = (Tc + kCurPad - 1) / kCurPad * kCurPad;
+  p.qb = (Tq + kQB - 1) / kQB;
+  p.bpp = (Hq / Hkv) * p.qb;
+  p.packed = p.bpp >= kCWaves;
+  p.upp = p.bpp / kCWaves;
+  p.tail_r = p.bpp % kCWaves;
+  p.tail = p.packed && p.upp >= 2 && p.upp <= 64 && p.tail_r >= 1 && p.tail_r <= 4;
   const size_t row = kHeadDim * sizeof(_Float16);
   auto up = [](size_t n) { return (n + 255) / 256 * 256; };
   p.k_off = 0;
   const size_t kv = (size_t)B * Hkv * p.Tc_pad * row;
   p.v_off = p.k_off + up(kv);
-  p.total = std::max<size_t>(p.v_off + up((size_t)B * Hkv * p.Tc_pad * kVRowBytes), 256);
+  p.to_off = p.v_off + up((size_t)B * Hkv * p.Tc_pad * kVRowBytes);
+  const size_t tail_rows = p.tail ? (size_t)B * Hkv * p.tail_r * p.upp * kQB : 0;
+  p.tml_off = p.to_off + up(tail_rows * kHeadDim * sizeof(float));
+  p.total = std::max<size_t>(p.tml_off + up(tail_rows * sizeof(float2)), 256);
   return p;
 }
 
@@ -1305,12 +1418,22 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   a.Hq = num_q_heads;
   a.Hkv = Hkv;
   a.Tq = Tq;
-  a.qb = (Tq + kQB - 1) / kQB;
+  a.qb = p.qb;
   const long long n_blocks = (long long)B * num_q_heads * a.qb;
   if (n_blocks > 0x7fffffffLL) return fail(OCTO_ERR_UNSUPPORTED, "%s: too many query blocks", what);
   a.n_blocks = (int)n_blocks;
-  a.bpp = (num_q_heads / Hkv) * a.qb;
-  a.packed = a.bpp >= kCWaves;
+  a.bpp = p.bpp;
+  a.packed = p.packed;
+  a.tail = p.tail;
+  a.upp = p.upp;
+  a.tail_r = p.tail_r;
+  a.tail_tt = 0;
+  if (p.tail) {
+    const int n_tiles = (cached_tokens + kBN - 1) / kBN + (Tc + kBN - 1) / kBN;
+    a.tail_tt = (n_tiles + p.upp - 1) / p.upp;
+    a.tail_o = reinterpret_cast<float*>(ws + p.to_off);
+    a.tail_ml = reinterpret_cast<float2*>(ws + p.tml_off);
+  }
   a.cached = cached_tokens;
   a.Tc = Tc;
   a.Tc_pad = p.Tc_pad;
@@ -1347,14 +1470,23 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
     }
   }
   const size_t dyn_bytes = (size_t)(off + 15) / 16 * 16;
-  const long long units = a.packed ? (n_blocks + kCWaves - 1) / kCWaves : (long long)B * Hkv;
+  const long long units = a.tail ? (long long)B * Hkv * a.upp
+                                 : a.packed ? (n_blocks + kCWaves - 1) / kCWaves : (long long)B * Hkv;
   const void* fn = chunk_kernel(corr, a.kcod.sel, a.vcod.sel);
   if (dyn_bytes > 65536) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_bytes);
     if (e != hipSuccess) return fail(OCTO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   }
   void* kargs[] = {&a};
-  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)units), dim3(kCThreads), kargs, dyn_bytes, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)units), dim3(kCThreads), kargs, dyn_bytes, stream);
   if (e != hipSuccess) return fail(OCTO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
-  return check_launch(what);
+  if ((s = check_launch(what)) != OCTO_OK) return s;
+  if (a.tail) {
+    // the leftover blocks' rows, four a workgroup
+    const long long rows = (long long)B * Hkv * a.tail_r * kQB;
+    hipLaunchKernelGGL(chunk_tail_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                       a, B * Hkv);
+    return check_launch(what);
+  }
+  return OCTO_OK;
 }

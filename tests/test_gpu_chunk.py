@@ -100,6 +100,21 @@ def test_chunk_full_size_sampled():
     assert err <= ATOL
 
 
+@pytest.mark.parametrize("Hq,Hkv,Tq,cached,tc", [(2, 2, 544, 300, 544), (4, 2, 280, 200, 280),
+                                                  (2, 2, 544, 0, 32), (1, 1, 1300, 700, 1300)])
+def test_chunk_split_tails(Hq, Hkv, Tq, cached, tc):
+    """Planes of 8 upp + r query blocks with upp >= 2 and r = 1..4 leftover
+    blocks: each of a plane's upp workgroups takes 8 whole blocks and a share
+    of the tiles for the leftover ones, whose partials a second launch
+    merges.  17 blocks a plane (r = 1), 2 x 9 blocks of a GQA plane (r = 2,
+    the last block ragged), one tile for two workgroups (the second's share
+    empty), and 41 blocks (upp = 5) over a ragged window."""
+    w = workload("chunk", Hq=Hq, Hkv=Hkv, T=max(cached, 64), chunk_q=Tq)
+    err, _ = run_chunk(w, cached=cached, tc=tc)
+    say(f"chunk split tails Hq={Hq} Hkv={Hkv} Tq={Tq} cached {cached} current {tc} err {err:.3e}")
+    assert err <= ATOL
+
+
 @pytest.mark.parametrize("cached,tc", [(0, 1), (5, 20), (20, 12), (31, 1), (32, 32), (40, 40), (64, 32),
                                        (40, 57)])
 def test_chunk_tile_counts(cached, tc):
