@@ -446,7 +446,8 @@ def run_chunk(w, steps, warmup):
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_FP16_PEAK_TFLOPS,
                      "traffic": recorded_traffic(w.key),
-                     "kernel": "octo_attend_chunk (rotate + decode pre-passes + MFMA attention)",
+                     "kernel": "octo_attend_chunk (current-row pre-pass, MFMA attention decoding "
+                               "the window tile by tile, leftover-block merge)",
                      "algorithmic_flops_per_launch": flops},
     }
     return res, (inp, kc, vc, kcache, vcache)
