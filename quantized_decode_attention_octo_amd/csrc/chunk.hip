@@ -13,12 +13,17 @@
 // R_v^T applied to the softmax-weighted rotated values.
 //
 // Launches on one stream:
-//   1. rotate_rows (x3): q, k_cur, v_cur -> fp16 rotated rows (coordinates in
-//      part order for tensors in the OCTOPUS codec, see part_pos)
-//   2. chunk_attn: fp16 MFMA flash attention (fp32 accumulation, online
-//      softmax) whose threads decode the cached window tile by tile from
-//      the packed records into LDS; epilogue 1/l and R_v^T; XCD-aware
-//      workgroup order.
+//   1. rotate_rows (x2): k_cur, v_cur -> fp16 rotated rows (coordinates in
+//      part order for tensors in the OCTOPUS codec, see part_pos), which
+//      every workgroup of a plane reads
+//   2. chunk_attn: each wavefront rotates its own query rows, then fp16 MFMA
+//      flash attention (fp32 accumulation, online softmax) whose threads
+//      decode the cached window tile by tile from the packed records into
+//      LDS; epilogue 1/l and R_v^T; XCD-aware workgroup order.  With split
+//      tails a second pass scans a share of the tiles for the plane's
+//      leftover query blocks and writes partials.
+//   3. chunk_tail_merge (split tails only): the leftover blocks' partials
+//      merged, 1/l and R_v^T.
 // The cached window is never written out: each query tile reads its packed
 // records (a few bytes a coordinate) and decodes them on chip.
 #include <math.h>
