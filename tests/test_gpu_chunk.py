@@ -36,14 +36,15 @@ def run_chunk(w, rows=None, heads=None, cached=None, tc=None):
     heads = heads or list(range(w.Hq))
     G = w.Hq // w.Hkv
     err = 0.0
-    for h in heads:
-        g = h // G
-        sub_k, sub_v = _plane(hkc, 0, g), _plane(hvc, 0, g)
-        ref = oatt.chunk_attention(q[:, h:h + 1].double().numpy(), sub_k, sub_v, hk, hv, cached,
-                                   kcur[:, g:g + 1].double().numpy(),
-                                   vcur[:, g:g + 1].double().numpy(), q_rows=rows)
-        r = np.arange(w.chunk_q) if rows is None else np.asarray(rows)
-        err = max(err, np.abs(out[0, h][r] - ref[0, 0][r]).max())
+    for b in range(w.B):
+        for h in heads:
+            g = h // G
+            sub_k, sub_v = _plane(hkc, b, g), _plane(hvc, b, g)
+            ref = oatt.chunk_attention(q[b:b + 1, h:h + 1].double().numpy(), sub_k, sub_v, hk, hv,
+                                       cached, kcur[b:b + 1, g:g + 1].double().numpy(),
+                                       vcur[b:b + 1, g:g + 1].double().numpy(), q_rows=rows)
+            r = np.arange(w.chunk_q) if rows is None else np.asarray(rows)
+            err = max(err, np.abs(out[b, h][r] - ref[0, 0][r]).max())
     return err, out
 
 
@@ -100,18 +101,20 @@ def test_chunk_full_size_sampled():
     assert err <= ATOL
 
 
-@pytest.mark.parametrize("Hq,Hkv,Tq,cached,tc", [(2, 2, 544, 300, 544), (4, 2, 280, 200, 280),
-                                                  (2, 2, 544, 0, 32), (1, 1, 1300, 700, 1300)])
-def test_chunk_split_tails(Hq, Hkv, Tq, cached, tc):
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,cached,tc", [(1, 2, 2, 544, 300, 544), (1, 4, 2, 280, 200, 280),
+                                                    (1, 2, 2, 544, 0, 32), (1, 1, 1, 1300, 700, 1300),
+                                                    (2, 4, 2, 280, 150, 200)])
+def test_chunk_split_tails(B, Hq, Hkv, Tq, cached, tc):
     """Planes of 8 upp + r query blocks with upp >= 2 and r = 1..4 leftover
     blocks: each of a plane's upp workgroups takes 8 whole blocks and a share
     of the tiles for the leftover ones, whose partials a second launch
     merges.  17 blocks a plane (r = 1), 2 x 9 blocks of a GQA plane (r = 2,
     the last block ragged), one tile for two workgroups (the second's share
-    empty), and 41 blocks (upp = 5) over a ragged window."""
-    w = workload("chunk", Hq=Hq, Hkv=Hkv, T=max(cached, 64), chunk_q=Tq)
+    empty), 41 blocks (upp = 5) over a ragged window, and two sequences of
+    GQA planes (the planes' blocks and partials indexed across the batch)."""
+    w = workload("chunk", B=B, Hq=Hq, Hkv=Hkv, T=max(cached, 64), chunk_q=Tq)
     err, _ = run_chunk(w, cached=cached, tc=tc)
-    say(f"chunk split tails Hq={Hq} Hkv={Hkv} Tq={Tq} cached {cached} current {tc} err {err:.3e}")
+    say(f"chunk split tails B={B} Hq={Hq} Hkv={Hkv} Tq={Tq} cached {cached} current {tc} err {err:.3e}")
     assert err <= ATOL
 
 
