@@ -933,8 +933,36 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     // scores of the tile's keys (log2 units): st[kt][rg][r] = key 16 kt + 4 grp + r
     floatx4 st[kBN / 16][kRG];
     const half8 zero8 = {};
+    if constexpr (!CORR) {
+      __builtin_amdgcn_sched_barrier(0);
+      half8 kf8[2][4];
+#pragma unroll
+      for (int kt = 0; kt < kBN / 16; ++kt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf8[kt][s] = *reinterpret_cast<const half8*>(ks + 16 * kt * 256 + kfr[s]);
+#pragma unroll
+      for (int kt = 0; kt < kBN / 16; ++kt) {
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int rg = 0; rg < kRG; ++rg)
+            st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf8[kt][s], qf[rg][s], st[kt][rg], 0, 0, 0);
+      }
+      // reads of slice 0 first; then each pair of products followed by one read
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int kt = 0; kt < kBN / 16; ++kt) {
+      if constexpr (CORR) {
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -943,6 +971,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg)
           st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[rg][s], st[kt][rg], 0, 0, 0);
+      }
       }
       if constexpr (CORR) {
         if (cachedt) {
