@@ -1034,44 +1034,16 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
       sh[rg] = up ? mx : 0.0f;
       any = any || __ballot(up) != 0;
     }
-    // P (and its sums), then O += P V (value fragments by the transposing
-    // read).  Written out on both sides of the (uniform) rescale branch, so
-    // that the accumulators stay in place on either side.
-    auto pv = [&](auto shifted) __attribute__((always_inline)) {
-      constexpr bool SH = decltype(shifted)::value;
-      half8 pf[kRG];
-#pragma unroll
-      for (int rg = 0; rg < kRG; ++rg) {
-        float ps = 0.0f;
-#pragma unroll
-        for (int e = 0; e < kBN / 4; ++e) {
-          // the raw exp2 (flushing results below the normal range to zero) is
-          // exact enough next to the row's largest terms (at least 1)
-          const float p = __builtin_amdgcn_exp2f(SH ? x[rg][e] - sh[rg] : x[rg][e]);
-          ps += p;
-          pf[rg][e] = (_Float16)p;
-        }
-        l_run[rg] += ps;               // this lane's keys; rows are summed at the end
-      }
-#pragma unroll
-      for (int c = 0; c < kOB; ++c) {
-        typedef __attribute__((address_space(3))) short4v lds_short4;
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vs + vtr + 32 * c));
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4*)(vs + vtr + 16 * kVRowBytes + 32 * c));
-        const half8 vf = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int rg = 0; rg < kRG; ++rg)
-          o[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg], vf, o[rg][c], 0, 0, 0);
-      }
-    };
+    // A rescale moves the rows' maxima, scales O and the sums by 2^-shift
+    // (on the first tile, both 0 and a shift of either sign, by at most 1)
+    // and shifts the scores, all in place; one chain of P V products then
+    // follows either way, so that each accumulator's only reader is its
+    // product and the product writes it in place.
     if (any) {
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) {
         m_run[rg] += sh[rg];
-        // O rows (queries q0 + 16 rg + 4 grp + r) and the sums scale by
-        // 2^-shift; on the first tile (both 0, shift of either sign) by at
-        // most 1
+        // O rows (queries q0 + 16 rg + 4 grp + r)
         const float alpha = __builtin_amdgcn_exp2f(-fmaxf(sh[rg], 0.0f));
         l_run[rg] *= alpha;
         float al[4];
@@ -1081,10 +1053,35 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
         for (int c = 0; c < kOB; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[rg][c][r] *= al[r];
+#pragma unroll
+        for (int e = 0; e < kBN / 4; ++e) x[rg][e] -= sh[rg];
       }
-      pv(std::true_type{});
-    } else {
-      pv(std::false_type{});
+    }
+    // P (and its sums), then O += P V (value fragments by the transposing read)
+    half8 pf[kRG];
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) {
+      float ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kBN / 4; ++e) {
+        // the raw exp2 (flushing results below the normal range to zero) is
+        // exact enough next to the row's largest terms (at least 1)
+        const float p = __builtin_amdgcn_exp2f(x[rg][e]);
+        ps += p;
+        pf[rg][e] = (_Float16)p;
+      }
+      l_run[rg] += ps;                 // this lane's keys; rows are summed at the end
+    }
+#pragma unroll
+    for (int c = 0; c < kOB; ++c) {
+      typedef __attribute__((address_space(3))) short4v lds_short4;
+      const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(vs + vtr + 32 * c));
+      const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(vs + vtr + 16 * kVRowBytes + 32 * c));
+      const half8 vf = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg)
+        o[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg], vf, o[rg][c], 0, 0, 0);
     }
   };
 
