@@ -187,10 +187,8 @@ __device__ inline float4 oct_dir(float xi, float eta) {
 // Each thread loads the packed words of one part of one cached row (keys and
 // values alike) straight into registers and writes that part as four
 // 16-byte chunks:
-//   - key rows: fp16 rho^ n^ (OCTOPUS keys, part order; gamma multiplies the
-//     fp32 scores) or Delta^ code + z^ (group keys, coordinate order);
-//   - value rows: fp16 gamma rho^ n^ (OCTOPUS values, part order) or Delta^
-//     code + z^ (group values, coordinate order).
+//   - key and value rows: fp16 gamma rho^ n^ (OCTOPUS, part order) or
+//     Delta^ code + z^ (group codec, coordinate order).
 // The current chunk's rows come from the pre-pass (rotate_rows) by direct
 // loads into the same tiles.  The value fragments of O = P V (eight keys of
 // one coordinate a lane) are read from the row-major value tile with the
@@ -446,13 +444,12 @@ __device__ inline void store_part(char* tile, const int (&cw)[4], const uint32_t
 // of three dwords, (x|y) of the first, (z of the first | x of the second),
 // (y|z) of the second; then the extra dword: part 0 (x|y) of triplet 40,
 // part 1 (z of 40 | x of 41), part 2 (y|z) of 41, part 3 (x|y) of 42.
-// Keys (VAL false): the scores take gamma in fp32, the threads of part 0
-// copy it to gk.  Values: every word times gamma.  `tab` is the lane's copy
-// of the table (entry e at tab + 8 C e).
-template <int BD, int BN, int PAR, bool VAL, int N>
+// Keys and values alike: every word times gamma (in fp16).  `tab` is the
+// lane's copy of the table (entry e at tab + 8 C e).
+template <int BD, int BN, int PAR, int N>
 __device__ __forceinline__ void dec_octo_row(const uint32_t (&w)[N], const char* tab,
                                              const char* rhotab, char* tile, const int (&cw)[4],
-                                             float* gk, int kk, int hi) {
+                                             int hi) {
   constexpr int BT = 2 * BD + BN, NWm = main_words(BT), NWe = tail_words(BT);
   constexpr int KK = 1 << (2 * BD);
   constexpr bool PRE = KK * (1 << BN) <= kMaxPre;
@@ -466,7 +463,6 @@ __device__ __forceinline__ void dec_octo_row(const uint32_t (&w)[N], const char*
   for (int i = 0; i < NWe; ++i) xe[i] = w[NWm + i];
   xe[NWe] = 0u;
   const uint32_t gam = w[NWm + NWe];
-  if (!VAL && pg == 0) gk[kk] = __uint_as_float(gam);
   const uint32_t* rhop = reinterpret_cast<const uint32_t*>(rhotab);
   auto entry = [&](uint32_t f) __attribute__((always_inline)) -> uint2 {
     if constexpr (PRE) {
@@ -495,11 +491,9 @@ __device__ __forceinline__ void dec_octo_row(const uint32_t (&w)[N], const char*
     const uint2 ea = entry(hi ? tail(42) : tail(40)), eb2 = entry(tail(41));
     d[15] = hi ? ea.x : pair_lo(ea.y, eb2.x);
   }
-  if constexpr (VAL) {
-    const uint32_t G = pack_rne(__uint_as_float(gam), __uint_as_float(gam));
+  const uint32_t G = pack_rne(__uint_as_float(gam), __uint_as_float(gam));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) d[i] = mul2(d[i], G);
-  }
+  for (int i = 0; i < 16; ++i) d[i] = mul2(d[i], G);
   store_part(tile, cw, d);
 }
 
@@ -520,14 +514,13 @@ __device__ inline uint32_t code_pair(uint32_t x2, uint32_t k1024) {
 }
 
 // Group row part: the 16 words (Delta^ code + z^) of coordinates 32 pg .. 32
-// pg + 31.  Keys: gamma 1 for the scores, and with CORR the key features
-// Delta^2 / 16 of the part's groups (zero in the unused slots).
+// pg + 31.  Keys with CORR: also the key features Delta^2 / 16 of the
+// part's groups (zero in the unused slots).
 template <int VB, int GS, bool CORR, bool VAL, int N>
 __device__ __forceinline__ void dec_group_row(const uint32_t (&w)[N], char* tile,
-                                              const int (&cw)[4], float* gk, _Float16* kf, int kk,
+                                              const int (&cw)[4], _Float16* kf, int kk,
                                               int pg, uint32_t k1024) {
   constexpr int G = kHeadDim / GS, NG = 32 / GS > 0 ? 32 / GS : 1;
-  if (!VAL && pg == 0) gk[kk] = 1.0f;
   uint32_t sc[NG], zz[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
@@ -609,7 +602,6 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   static_assert(KSEL == VSEL, "one codec for both tensors, or chosen at run time");
   constexpr int NW = row_words(KSEL);
   __shared__ __attribute__((aligned(1024))) char tiles[kTilesBytes];
-  __shared__ __attribute__((aligned(16))) float gks[kSlots][2][kBN];
   __shared__ __attribute__((aligned(16))) _Float16 kfs[kSlots][2][CORR ? kBN * kFeat : 8];
   __shared__ __attribute__((aligned(16))) _Float16 qfs[CORR ? kCWaves * kQB * kFeat : 8];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
@@ -786,9 +778,11 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   const int tstage = dten ? kVTileBytes : kKTileBytes;   // buffer 1 less buffer 0
 
   floatx4 o[kRG][kOB];
-  // of query q0 + 16 rg + col: running maximum (log2 units; 0 until the
-  // first tile of the pass sets it), and this lane's part of the normalizer
-  float m_run[kRG], l_run[kRG];
+  // nm: minus the running maximum of query q0 + 16 rg + col in all four
+  // slots (log2 units; 0 until the first tile of the pass sets it), the
+  // initial value of the tile's score products; ls: the normalizers of
+  // queries q0 + 16 rg + 4 grp + r, summed by the products P 1
+  floatx4 nm[kRG], ls[kRG];
 
   // the task's packed stream and gammas, and the current chunk's rows of the
   // task's plane (loads past a plane's range return zero)
@@ -827,8 +821,8 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   for (int rg = 0; rg < kRG; ++rg) {
 #pragma unroll
     for (int c = 0; c < kOB; ++c) o[rg][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    m_run[rg] = 0.0f;
-    l_run[rg] = 0.0f;
+    nm[rg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    ls[rg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
 
@@ -859,24 +853,18 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     asm volatile("" : "+v"(lt));
     const int kk = lt & 31, hi = (lt & 63) >> 5, pg = 2 * hi + dpar;
     char* tb = tiles + S * tstage;               // tw holds the slot's offsets
-    float* gk = gks[dslot][S];
     with_codec<KSEL>(dsel, [&](auto cs) __attribute__((always_inline)) {
       constexpr int C = decltype(cs)::value;
       if constexpr (C < 1000) {
         constexpr int BD = C / 10, BN = C % 10, NC = tab_copies(BD, BN);
         const char* tab = dyn + dtab + ((lt & (NC - 1)) << 3);
         const char* rt = dyn + drho;
-        if (dten) {
-          if (dpar) dec_octo_row<BD, BN, 1, true>(w, tab, rt, tb, tw, nullptr, kk, hi);
-          else dec_octo_row<BD, BN, 0, true>(w, tab, rt, tb, tw, nullptr, kk, hi);
-        } else {
-          if (dpar) dec_octo_row<BD, BN, 1, false>(w, tab, rt, tb, tw, gk, kk, hi);
-          else dec_octo_row<BD, BN, 0, false>(w, tab, rt, tb, tw, gk, kk, hi);
-        }
+        if (dpar) dec_octo_row<BD, BN, 1>(w, tab, rt, tb, tw, hi);
+        else dec_octo_row<BD, BN, 0>(w, tab, rt, tb, tw, hi);
       } else {
         constexpr int VB = (C - 1000) / 100, GS = C % 100;
-        if (dten) dec_group_row<VB, GS, false, true>(w, tb, tw, nullptr, nullptr, kk, pg, k1024);
-        else dec_group_row<VB, GS, CORR, false>(w, tb, tw, gk, kfs[dslot][S], kk, pg, k1024);
+        if (dten) dec_group_row<VB, GS, false, true>(w, tb, tw, nullptr, kk, pg, k1024);
+        else dec_group_row<VB, GS, CORR, false>(w, tb, tw, kfs[dslot][S], kk, pg, k1024);
       }
     });
   };
@@ -892,7 +880,6 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     uint32_t lx = L;
     asm volatile("" : "+v"(lx));
     const int lw = wave & 3;
-    if (lw == 0 && lx < kBN) gks[dslot][S][lx] = 1.0f;     // the scores take no gamma
     // key tile: lane L of load j fills stored chunk p = 64 j + L, row p / 16,
     // logical chunk (p % 16) ^ (row % 16)
 #pragma unroll
@@ -943,7 +930,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
 #pragma unroll
       for (int kt = 0; kt < kBN / 16; ++kt) {
 #pragma unroll
-        for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = nm[rg];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -964,7 +951,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     for (int kt = 0; kt < kBN / 16; ++kt) {
       if constexpr (CORR) {
 #pragma unroll
-      for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = nm[rg];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const half8 kf = *reinterpret_cast<const half8*>(ks + 16 * kt * 256 + kfr[s]);
@@ -989,23 +976,13 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
         }
       }
     }
-    // x = gamma s - m in log2 units relative to the running maximum (0
-    // before the first tile): gamma in fp32 from gks for OCTOPUS keys of the
-    // window (the tile holds rho^ n^), 1 for every other tile
+    // x = s - m in log2 units relative to the running maximum (0 before
+    // the first tile): the products started from -m
     float x[kRG][kBN / 4];
-    float4 g4[kBN / 16];
 #pragma unroll
-    for (int kt = 0; kt < kBN / 16; ++kt) g4[kt] = *reinterpret_cast<const float4*>(&gks[cslot][S][16 * kt + 4 * grp]);
+    for (int rg = 0; rg < kRG; ++rg)
 #pragma unroll
-    for (int rg = 0; rg < kRG; ++rg) {
-      const float mneg = -m_run[rg];
-#pragma unroll
-      for (int e = 0; e < kBN / 4; ++e) {
-        const int kt = e >> 2, r = e & 3;
-        const float g = r == 0 ? g4[kt].x : r == 1 ? g4[kt].y : r == 2 ? g4[kt].z : g4[kt].w;
-        x[rg][e] = fmaf(st[kt][rg][r], g, mneg);
-      }
-    }
+      for (int e = 0; e < kBN / 4; ++e) x[rg][e] = st[e >> 2][rg][e & 3];
     if (nvalid < kBN) {
       // keys 16 kt + 4 grp + r past the segment (an opaque lane offset, so
       // that no per-slot key index is kept in registers)
@@ -1042,13 +1019,15 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     if (any) {
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) {
-        m_run[rg] += sh[rg];
-        // O rows (queries q0 + 16 rg + 4 grp + r)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) nm[rg][r] -= sh[rg];
+        // O rows and normalizers (queries q0 + 16 rg + 4 grp + r)
         const float alpha = __builtin_amdgcn_exp2f(-fmaxf(sh[rg], 0.0f));
-        l_run[rg] *= alpha;
         float al[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ls[rg][r] *= al[r];
 #pragma unroll
         for (int c = 0; c < kOB; ++c)
 #pragma unroll
@@ -1057,20 +1036,18 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
         for (int e = 0; e < kBN / 4; ++e) x[rg][e] -= sh[rg];
       }
     }
-    // P (and its sums), then O += P V (value fragments by the transposing read)
+    // P and its row sums (P 1, of the fp16 P that the products take), then
+    // O += P V (value fragments by the transposing read)
     half8 pf[kRG];
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
-      float ps = 0.0f;
 #pragma unroll
-      for (int e = 0; e < kBN / 4; ++e) {
+      for (int e = 0; e < kBN / 4; ++e)
         // the raw exp2 (flushing results below the normal range to zero) is
         // exact enough next to the row's largest terms (at least 1)
-        const float p = __builtin_amdgcn_exp2f(x[rg][e]);
-        ps += p;
-        pf[rg][e] = (_Float16)p;
-      }
-      l_run[rg] += ps;                 // this lane's keys; rows are summed at the end
+        pf[rg][e] = (_Float16)__builtin_amdgcn_exp2f(x[rg][e]);
+      ls[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg], ones, ls[rg], 0, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < kOB; ++c) {
@@ -1130,9 +1107,12 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
           (((size_t)plane0 * a.tail_r + wave) * a.upp + unit % a.upp) * kQB;
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) {
-        const float l_tot = rows_sum(l_run[rg]);
-        if (grp == 0)
-          a.tail_ml[row0 + 16 * rg + col] = make_float2(t_hi > t_lo ? m_run[rg] : -INFINITY, l_tot);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float m = -__shfl(nm[rg][0], 4 * grp + r, 64);
+          if (col == 0)
+            a.tail_ml[row0 + 16 * rg + 4 * grp + r] = make_float2(t_hi > t_lo ? m : -INFINITY, ls[rg][r]);
+        }
 #pragma unroll
         for (int c = 0; c < kOB; ++c)
 #pragma unroll
@@ -1157,11 +1137,10 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   float* ob = reinterpret_cast<float*>(tiles) + wave * (16 * kORow);
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg) {
-    const float l_tot = rows_sum(l_run[rg]);   // the row's four lane groups
     float v[8][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float l = __shfl(l_tot, 4 * grp + r, 64);
+      const float l = ls[rg][r];
       const float li = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) v[c][r] = o[rg][c][r] * li;
