@@ -804,12 +804,17 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   const int n_ct = (a.cached + kBN - 1) / kBN, n_rt = (a.Tc + kBN - 1) / kBN;
   const int n_tiles = n_ct + n_rt;
   int t_lo = 0, t_hi = n_tiles;        // the tiles of the current pass
+  // a split tail's pass: leftover block tj of the plane is taken by
+  // wavefront 4 + tj, so that the wavefronts that compute (4 ..) and those
+  // that decode (0 .. 3) differ and a tile's products overlap the next
+  // tile's decoding
+  const int tj = wave - 4;
   if constexpr (pass == 1) {
     const int k = unit % a.upp;
     t_lo = min(n_tiles, k * a.tail_tt);
     t_hi = min(n_tiles, t_lo + a.tail_tt);
-    active = wave < a.tail_r;
-    gb = plane0 * a.bpp + kCWaves * a.upp + min(wave, a.tail_r - 1);
+    active = tj >= 0 && tj < a.tail_r;
+    gb = plane0 * a.bpp + kCWaves * a.upp + min(max(tj, 0), a.tail_r - 1);
     bh = gb / a.qb;
     q0 = (gb % a.qb) * kQB;
     cslot = 0;
@@ -1104,7 +1109,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     // and the unnormalized value sums in part order
     if (active) {
       const size_t row0 =
-          (((size_t)plane0 * a.tail_r + wave) * a.upp + unit % a.upp) * kQB;
+          (((size_t)plane0 * a.tail_r + tj) * a.upp + unit % a.upp) * kQB;
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) {
 #pragma unroll
