@@ -128,12 +128,11 @@ __device__ inline void rotate_rows(const RotJob& jb, int tile_x, int plane, _Flo
           v[e | m] = x - y;
         }
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
+    for (int m = 1; m < 16; m <<= 1) {
+      const float sgm = (cl & m) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __shfl_xor(v[e], m, 64);
-        v[e] = (cl & m) ? (p - v[e]) : (v[e] + p);
-      }
+      for (int e = 0; e < 8; ++e) v[e] = xbfly(v[e], lane_xor(v[e], m), sgm);
+    }
     half8v o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (_Float16)(v[e] * kInvSqrtD);
@@ -706,12 +705,11 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
             v[e | m] = x - y;
           }
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1)
+      for (int m = 1; m < 16; m <<= 1) {
+        const float sgm = (cl & m) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = __shfl_xor(v[e], m, 64);
-          v[e] = (cl & m) ? (pv - v[e]) : (v[e] + pv);
-        }
+        for (int e = 0; e < 8; ++e) v[e] = xbfly(v[e], lane_xor(v[e], m), sgm);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int pos = a.kperm ? part_pos(8 * cl + e) : 8 * cl + e;
@@ -1183,14 +1181,13 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
           }
         }
 #pragma unroll
-    for (int m = 8; m >= 1; m >>= 1)
+    for (int m = 8; m >= 1; m >>= 1) {
+      const float sgm = (col & m) ? -1.0f : 1.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __shfl_xor(v[c][r], m, 64);
-          v[c][r] = (col & m) ? (p - v[c][r]) : (v[c][r] + p);
-        }
+        for (int r = 0; r < 4; ++r) v[c][r] = xbfly(v[c][r], lane_xor(v[c][r], m), sgm);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int q = q0 + 16 * rg + 4 * grp + r;

@@ -93,6 +93,22 @@ __host__ __device__ inline float splitmix_sign(uint64_t seed, uint32_t j) {
   return (z >> 63) ? -1.0f : 1.0f;
 }
 
+// The value of lane L ^ m (m a power of two below 64, known after
+// unrolling): a DPP quad permutation for m = 1 and 2, a cross-lane read
+// otherwise.
+__device__ __forceinline__ float lane_xor(float v, int m) {
+  if (m == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  if (m == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  return __shfl_xor(v, m, 64);
+}
+
+// One cross-lane butterfly of a Walsh-Hadamard stage: v + p in the lane of
+// the pair with the stage's bit clear, p - v in its partner (p the other
+// lane's value), as one fused multiply-add by the lane's sign sg (+1 or
+// -1).  The product by +-1 is exact and the sum is rounded once, so the
+// result is the add or subtract itself.
+__device__ __forceinline__ float xbfly(float v, float p, float sg) { return fmaf(sg, v, p); }
+
 // Unnormalized Walsh-Hadamard transform of a 128-vector held by one
 // wavefront, lane l owning coordinates l (a) and l + 64 (b).  Natural
 // (Sylvester) order: H[i][j] = (-1)^popcount(i & j).  The stride-64 butterfly
@@ -104,11 +120,10 @@ __device__ inline void wht128(float& a, float& b) {
   b = t;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
-    float pa = __shfl_xor(a, m, 64);
-    float pb = __shfl_xor(b, m, 64);
-    const bool upper = lane & m;
-    a = upper ? (pa - a) : (a + pa);
-    b = upper ? (pb - b) : (b + pb);
+    const float pa = lane_xor(a, m), pb = lane_xor(b, m);
+    const float sg = (lane & m) ? -1.0f : 1.0f;
+    a = xbfly(a, pa, sg);
+    b = xbfly(b, pb, sg);
   }
 }
 
