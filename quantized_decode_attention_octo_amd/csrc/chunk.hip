@@ -285,11 +285,15 @@ struct ChunkArgs {
   // Split tails (packed mode variant): a plane's bpp = 8 upp + r blocks go to
   // upp workgroups of 8 whole blocks each, and the r leftover blocks are
   // split by keys: workgroup k of the plane also scans tiles [k tt, (k+1) tt)
-  // for them (one wavefront a block) and writes unnormalized partials that a
-  // second launch merges.  No workgroup then spans two planes.
-  int tail, upp, tail_r, tail_tt;
-  float* tail_o;         // [planes][r][upp][32 rows][128] value sums (part order)
-  float2* tail_ml;       // [planes][r][upp][32 rows] (running maximum, normalizer)
+  // for them and writes unnormalized partials that a second launch merges.
+  // No workgroup then spans two planes.  With r <= 2 (fold) the leftover
+  // blocks ride in the first pass: their 16-query row groups are taken by
+  // the wavefronts that do not decode (4 .. 7), each on every nsub-th tile of
+  // the share (nsub = 4 / (2 r)), giving upp nsub partials a row; otherwise a
+  // second pass over the share takes them, one wavefront a block.
+  int tail, upp, tail_r, tail_tt, fold, nsub;
+  float* tail_o;         // [planes][r][upp nsub][32 rows][128] value sums (part order)
+  float2* tail_ml;       // [planes][r][upp nsub][32 rows] (running maximum, normalizer)
   int cached, Tc, Tc_pad, capacity;
   uint64_t vseed;
   const uint32_t *k_idx, *v_idx;
@@ -602,7 +606,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   constexpr int NW = row_words(KSEL);
   __shared__ __attribute__((aligned(1024))) char tiles[kTilesBytes];
   __shared__ __attribute__((aligned(16))) _Float16 kfs[kSlots][2][CORR ? kBN * kFeat : 8];
-  __shared__ __attribute__((aligned(16))) _Float16 qfs[CORR ? kCWaves * kQB * kFeat : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 qfs[CORR ? (kCWaves * kQB + 64) * kFeat : 8];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
 
   const int tid = threadIdx.x, L = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -671,7 +675,11 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   // 0..2 in registers, 3..6 across the row's lanes.  With the correction the
   // group sums of the squared rotated coordinates give the query features.
   half8 qf[kRG][4];
-  auto stage_queries = [&]() __attribute__((always_inline)) {
+  // Stages 16 RG query rows q0_ .. of (batch, head) bh_ and reads back their
+  // fragments into dst; with the correction their features go to rows
+  // frow .. of qfs.
+  auto stage = [&](int bh_, int q0_, auto& dst, int frow) __attribute__((always_inline)) {
+    constexpr int RG = std::extent<std::remove_reference_t<decltype(dst)>>::value;
     _Float16* stg = reinterpret_cast<_Float16*>(tiles) + wave * kQB * kHeadDim;
     // from an opaque copy of the lane index, so that a later call forms its
     // signs and offsets afresh instead of keeping the first call's live
@@ -681,14 +689,14 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     float sg[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sg[e] = splitmix_sign(a.kseed, 8 * cl + e);
-    uint4 raw[kQB / 4];
+    uint4 raw[4 * RG];
 #pragma unroll
-    for (int j = 0; j < kQB / 4; ++j) {
-      const int qrow = min(q0 + 4 * j + sub, a.Tq - 1);
-      raw[j] = *reinterpret_cast<const uint4*>(a.q + ((size_t)bh * a.Tq + qrow) * kHeadDim + 8 * cl);
+    for (int j = 0; j < 4 * RG; ++j) {
+      const int qrow = min(q0_ + 4 * j + sub, a.Tq - 1);
+      raw[j] = *reinterpret_cast<const uint4*>(a.q + ((size_t)bh_ * a.Tq + qrow) * kHeadDim + 8 * cl);
     }
 #pragma unroll
-    for (int j = 0; j < kQB / 4; ++j) {
+    for (int j = 0; j < 4 * RG; ++j) {
       const int r = 4 * j + sub;
       const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
       float v[8];
@@ -723,7 +731,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
         for (int m = 1; m < lpg; m <<= 1) sq += __shfl_xor(sq, m, 64);
         const int ng = kHeadDim / a.feat_gs;
         const float f = __shfl(sq, 16 * sub + min(cl, ng - 1) * lpg, 64);
-        if (cl < kFeat) qfs[(wave * kQB + r) * kFeat + cl] = (_Float16)(cl < ng ? a.feat_c * f : 0.0f);
+        if (cl < kFeat) qfs[(frow + r) * kFeat + cl] = (_Float16)(cl < ng ? a.feat_c * f : 0.0f);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -732,13 +740,24 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     // query 16 rg + col, dims 32 s + 8 grp + e: chunk 4 s + grp of its row
     const int qcol = lq & 15, qgrp = lq >> 4;
 #pragma unroll
-    for (int rg = 0; rg < kRG; ++rg)
+    for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
-        qf[rg][s4] = *reinterpret_cast<const half8*>(
+        dst[rg][s4] = *reinterpret_cast<const half8*>(
             stg + (16 * rg + qcol) * kHeadDim + (((4 * s4 + qgrp) ^ qcol) << 3));
   };
-  stage_queries();
+  stage(bh, q0, qf, wave * kQB);
+  // fold mode: wavefront 4 + xw (which does not decode) also takes row group
+  // xrg of leftover block xj on tiles xsub, xsub + nsub, .. of the
+  // workgroup's share (its query features in rows 256 + 16 xw .. of qfs)
+  const int xw = wave - 4, x2r = 2 * max(a.tail_r, 1);
+  const bool xact = a.fold && xw >= 0;
+  const int xg = xact ? xw % x2r : 0, xj = xg >> 1, xrg = xg & 1, xsub = xact ? xw / x2r : 0;
+  half8 qx[1][4];
+  if (xact) {
+    const int gbx = plane0 * a.bpp + kCWaves * a.upp + xj;
+    stage(gbx / a.qb, (gbx % a.qb) * kQB + 16 * xrg, qx, kCWaves * kQB + 16 * xw);
+  }
   __syncthreads();                     // the stagings are read before tile 0 lands
   {
     const float *cxk = cbs, *crk = cbs + kMaxXi, *cxv = cbs + kCb, *crv = cbs + kCb + kMaxXi;
@@ -817,7 +836,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     q0 = (gb % a.qb) * kQB;
     cslot = 0;
     __syncthreads();                   // the first pass's epilogue rows are read
-    stage_queries();
+    stage(bh, q0, qf, wave * kQB);
     __syncthreads();
   }
 #pragma unroll
@@ -914,14 +933,16 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   // the ragged last tile of each segment masks keys.  (Both are uniform
   // branches on the scores alone, so that one copy of the MFMA chains
   // serves every tile.)
-  auto compute = [&](int u, auto stage) __attribute__((always_inline)) {
+  auto compute = [&](int u, auto stage, bool first, auto& qfa, auto& oa, auto& nma, auto& lsa, int frow)
+      __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
-    const bool cachedt = u < n_ct, first = u == t_lo;
+    constexpr int RG = std::extent<std::remove_reference_t<decltype(nma)>>::value;
+    const bool cachedt = u < n_ct;
     const int nvalid = cachedt ? a.cached - u * kBN : a.Tc - (u - n_ct) * kBN;
     const char* ks = tiles + cslot * kSlotBytes + S * kKTileBytes;
     const char* vs = tiles + cslot * kSlotBytes + 2 * kKTileBytes + S * kVTileBytes;
     // scores of the tile's keys (log2 units): st[kt][rg][r] = key 16 kt + 4 grp + r
-    floatx4 st[kBN / 16][kRG];
+    floatx4 st[kBN / 16][RG];
     const half8 zero8 = {};
     if constexpr (!CORR) {
       __builtin_amdgcn_sched_barrier(0);
@@ -933,12 +954,12 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
 #pragma unroll
       for (int kt = 0; kt < kBN / 16; ++kt) {
 #pragma unroll
-        for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = nm[rg];
+        for (int rg = 0; rg < RG; ++rg) st[kt][rg] = nma[rg];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int rg = 0; rg < kRG; ++rg)
-            st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf8[kt][s], qf[rg][s], st[kt][rg], 0, 0, 0);
+          for (int rg = 0; rg < RG; ++rg)
+            st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf8[kt][s], qfa[rg][s], st[kt][rg], 0, 0, 0);
       }
       // reads of slice 0 first; then each pair of products followed by one read
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -954,13 +975,13 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     for (int kt = 0; kt < kBN / 16; ++kt) {
       if constexpr (CORR) {
 #pragma unroll
-      for (int rg = 0; rg < kRG; ++rg) st[kt][rg] = nm[rg];
+      for (int rg = 0; rg < RG; ++rg) st[kt][rg] = nma[rg];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const half8 kf = *reinterpret_cast<const half8*>(ks + 16 * kt * 256 + kfr[s]);
 #pragma unroll
-        for (int rg = 0; rg < kRG; ++rg)
-          st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[rg][s], st[kt][rg], 0, 0, 0);
+        for (int rg = 0; rg < RG; ++rg)
+          st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qfa[rg][s], st[kt][rg], 0, 0, 0);
       }
       }
       if constexpr (CORR) {
@@ -970,10 +991,10 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
           half8 kf5 = zero8;
           if (grp == 0) kf5 = *reinterpret_cast<const half8*>(&kfs[cslot][S][(16 * kt + col) * kFeat]);
 #pragma unroll
-          for (int rg = 0; rg < kRG; ++rg) {
+          for (int rg = 0; rg < RG; ++rg) {
             half8 qf5 = zero8;
             if (grp == 0)
-              qf5 = *reinterpret_cast<const half8*>(&qfs[(wave * kQB + 16 * rg + col) * kFeat]);
+              qf5 = *reinterpret_cast<const half8*>(&qfs[(frow + 16 * rg + col) * kFeat]);
             st[kt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf5, qf5, st[kt][rg], 0, 0, 0);
           }
         }
@@ -981,9 +1002,9 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     }
     // x = s - m in log2 units relative to the running maximum (0 before
     // the first tile): the products started from -m
-    float x[kRG][kBN / 4];
+    float x[RG][kBN / 4];
 #pragma unroll
-    for (int rg = 0; rg < kRG; ++rg)
+    for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
       for (int e = 0; e < kBN / 4; ++e) x[rg][e] = st[e >> 2][rg][e & 3];
     if (nvalid < kBN) {
@@ -992,7 +1013,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
       int k4 = 4 * grp;
       asm volatile("" : "+v"(k4));
 #pragma unroll
-      for (int rg = 0; rg < kRG; ++rg)
+      for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
         for (int e = 0; e < kBN / 4; ++e)
           if (16 * (e >> 2) + k4 + (e & 3) >= nvalid) x[rg][e] = -INFINITY;
@@ -1002,10 +1023,10 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     // tile, which sets it -- so that nearly every tile skips the rescale;
     // probabilities then stay below 2^kLazyLog2, well inside fp16, and the
     // final 1/l cancels the shift.
-    float sh[kRG];
+    float sh[RG];
     bool any = false;
 #pragma unroll
-    for (int rg = 0; rg < kRG; ++rg) {
+    for (int rg = 0; rg < RG; ++rg) {
       float mx = x[rg][0];
 #pragma unroll
       for (int e = 1; e < kBN / 4; ++e) mx = fmaxf(mx, x[rg][e]);
@@ -1021,36 +1042,36 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     // product and the product writes it in place.
     if (any) {
 #pragma unroll
-      for (int rg = 0; rg < kRG; ++rg) {
+      for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) nm[rg][r] -= sh[rg];
+        for (int r = 0; r < 4; ++r) nma[rg][r] -= sh[rg];
         // O rows and normalizers (queries q0 + 16 rg + 4 grp + r)
         const float alpha = __builtin_amdgcn_exp2f(-fmaxf(sh[rg], 0.0f));
         float al[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ls[rg][r] *= al[r];
+        for (int r = 0; r < 4; ++r) lsa[rg][r] *= al[r];
 #pragma unroll
         for (int c = 0; c < kOB; ++c)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[rg][c][r] *= al[r];
+          for (int r = 0; r < 4; ++r) oa[rg][c][r] *= al[r];
 #pragma unroll
         for (int e = 0; e < kBN / 4; ++e) x[rg][e] -= sh[rg];
       }
     }
     // P and its row sums (P 1, of the fp16 P that the products take), then
     // O += P V (value fragments by the transposing read)
-    half8 pf[kRG];
+    half8 pf[RG];
     const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll
-    for (int rg = 0; rg < kRG; ++rg) {
+    for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
       for (int e = 0; e < kBN / 4; ++e)
         // the raw exp2 (flushing results below the normal range to zero) is
         // exact enough next to the row's largest terms (at least 1)
         pf[rg][e] = (_Float16)__builtin_amdgcn_exp2f(x[rg][e]);
-      ls[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg], ones, ls[rg], 0, 0, 0);
+      lsa[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg], ones, lsa[rg], 0, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < kOB; ++c) {
@@ -1060,11 +1081,21 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
           (lds_short4*)(vs + vtr + 16 * kVRowBytes + 32 * c));
       const half8 vf = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int rg = 0; rg < kRG; ++rg)
-        o[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg], vf, o[rg][c], 0, 0, 0);
+      for (int rg = 0; rg < RG; ++rg)
+        oa[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[rg], vf, oa[rg][c], 0, 0, 0);
     }
   };
 
+  // fold mode: the extra row group's share of tiles and softmax state
+  int x_lo = 0, x_hi = 0;
+  if (xact) {
+    x_lo = min(n_tiles, (unit % a.upp) * a.tail_tt);
+    x_hi = min(n_tiles, x_lo + a.tail_tt);
+  }
+  floatx4 ox[1][kOB], nmx[1], lsx[1];
+#pragma unroll
+  for (int c = 0; c < kOB; ++c) ox[0][c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  nmx[0] = lsx[0] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   // ---- passes: the workgroup's blocks over every tile; then, for a split
   // tail, the plane's leftover blocks over this workgroup's share of tiles
   // ---- the tile pipeline over [t_lo, t_hi): the words of cached tile u in
@@ -1088,7 +1119,11 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     if (dact && t + 2 < c_hi) load_words(t + 2, wS);
     const bool next_cur = t + 1 >= n_ct && t + 1 < t_hi;
     if (dact && next_cur) request_rows(t + 1, Next{});
-    if (active) compute(t, stage);
+    if (active) compute(t, stage, t == t_lo, qf, o, nm, ls, wave * kQB);
+    if constexpr (pass == 0) {
+      if (xact && t >= x_lo && t < x_hi && ((t - x_lo) & (a.nsub - 1)) == xsub)
+        compute(t, stage, t == x_lo + xsub, qx, ox, nmx, lsx, kCWaves * kQB + 16 * xw);
+    }
     if (t + 1 < c_hi) {
       if (dact) decode(t + 1, Next{}, wN);
     } else if (next_cur) {
@@ -1101,6 +1136,24 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
     if (t + 1 < t_hi) iter(t + 1, std::integral_constant<int, 1>{}, w1, w0);
   }
 
+  if constexpr (pass == 0) {
+    // ---- fold mode: the extra row group's partial (rows 16 xrg .. of
+    // leftover block xj; partial (unit % upp) nsub + xsub of the plane)
+    if (xact) {
+      const size_t row0 = (((size_t)plane0 * a.tail_r + xj) * (a.upp * a.nsub) +
+                           (unit % a.upp) * a.nsub + xsub) * kQB + 16 * xrg;
+      const bool any_tile = x_lo + xsub < x_hi;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m = -__shfl(nmx[0][0], 4 * grp + r, 64);
+        if (col == 0) a.tail_ml[row0 + 4 * grp + r] = make_float2(any_tile ? m : -INFINITY, lsx[0][r]);
+      }
+#pragma unroll
+      for (int c = 0; c < kOB; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a.tail_o[(row0 + 4 * grp + r) * kHeadDim + 16 * c + col] = ox[0][c][r];
+    }
+  }
   if constexpr (pass == 1) {
     // ---- a split tail's partial: per query row of the leftover block the
     // running maximum (-inf for an empty share of tiles) and normalizer,
@@ -1199,7 +1252,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
   }
   };
   run_pass(std::integral_constant<int, 0>{});
-  if (a.tail) run_pass(std::integral_constant<int, 1>{});
+  if (a.tail && !a.fold) run_pass(std::integral_constant<int, 1>{});
 }
 
 // Merges a split tail's partials: one wavefront per query row of a
@@ -1214,16 +1267,17 @@ __global__ __launch_bounds__(256) void chunk_tail_merge_kernel(ChunkArgs a, int 
   const int gb = p * a.bpp + kCWaves * a.upp + j;
   const int bh = gb / a.qb, q = (gb % a.qb) * kQB + row;
   if (q >= a.Tq) return;
-  const size_t r0 = ((size_t)p * a.tail_r + j) * a.upp;        // partial k: row (r0 + k) 32 + row
-  // every partial's maximum in one lane (upp <= 64 by the plan)
-  const float2 mlL = L < a.upp ? a.tail_ml[(r0 + L) * kQB + row] : make_float2(-INFINITY, 0.0f);
+  const int parts = a.upp * a.nsub;
+  const size_t r0 = ((size_t)p * a.tail_r + j) * parts;        // partial k: row (r0 + k) 32 + row
+  // every partial's maximum in one lane (upp nsub <= 64 by the plan)
+  const float2 mlL = L < parts ? a.tail_ml[(r0 + L) * kQB + row] : make_float2(-INFINITY, 0.0f);
   const float M = wave_max(mlL.x);
   const int c0 = a.vperm ? part_pos(L) : L, c1 = a.vperm ? part_pos(L + 64) : L + 64;
   float lsum = 0.0f, x0 = 0.0f, x1 = 0.0f;
   if (M != -INFINITY) {                // the same in every lane
     const float f = mlL.x == -INFINITY ? 0.0f : exp2f(mlL.x - M);
     lsum = wave_sum(f * mlL.y);
-    for (int k = 0; k < a.upp; ++k) {
+    for (int k = 0; k < parts; ++k) {
       const float fk = __shfl(f, k, 64);
       const float* o = a.tail_o + ((r0 + k) * kQB + row) * kHeadDim;
       x0 = fmaf(fk, o[c0], x0);
@@ -1242,7 +1296,7 @@ __global__ __launch_bounds__(256) void chunk_tail_merge_kernel(ChunkArgs a, int 
 struct ChunkPlan {
   int Tc_pad;
   int qb, bpp, packed;
-  int tail, upp, tail_r;               // split tails (see ChunkArgs)
+  int tail, upp, tail_r, fold, nsub;   // split tails (see ChunkArgs)
   size_t k_off, v_off, to_off, tml_off, total;
 };
 
@@ -1265,13 +1319,15 @@ ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Tq, int Tc, bool corr) {
   p.upp = p.bpp / kCWaves;
   p.tail_r = p.bpp % kCWaves;
   p.tail = p.packed && p.upp >= 2 && p.upp <= 64 && p.tail_r >= 1 && p.tail_r <= 4;
+  p.fold = p.tail && p.tail_r <= 2 && p.upp * (4 / (2 * p.tail_r)) <= 64;
+  p.nsub = p.fold ? 4 / (2 * p.tail_r) : 1;
   const size_t row = kHeadDim * sizeof(_Float16);
   auto up = [](size_t n) { return (n + 255) / 256 * 256; };
   p.k_off = 0;
   const size_t kv = (size_t)B * Hkv * p.Tc_pad * row;
   p.v_off = p.k_off + up(kv);
   p.to_off = p.v_off + up((size_t)B * Hkv * p.Tc_pad * kVRowBytes);
-  const size_t tail_rows = p.tail ? (size_t)B * Hkv * p.tail_r * p.upp * kQB : 0;
+  const size_t tail_rows = p.tail ? (size_t)B * Hkv * p.tail_r * p.upp * p.nsub * kQB : 0;
   p.tml_off = p.to_off + up(tail_rows * kHeadDim * sizeof(float));
   p.total = std::max<size_t>(p.tml_off + up(tail_rows * sizeof(float2)), 256);
   return p;
@@ -1439,6 +1495,8 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   a.tail = p.tail;
   a.upp = p.upp;
   a.tail_r = p.tail_r;
+  a.fold = p.fold;
+  a.nsub = p.nsub;
   a.tail_tt = 0;
   if (p.tail) {
     const int n_tiles = (cached_tokens + kBN - 1) / kBN + (Tc + kBN - 1) / kBN;
