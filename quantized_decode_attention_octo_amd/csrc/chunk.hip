@@ -20,8 +20,10 @@
 //      flash attention (fp32 accumulation, online softmax) whose threads
 //      decode the cached window tile by tile from the packed records into
 //      LDS; epilogue 1/l and R_v^T; XCD-aware workgroup order.  With split
-//      tails a second pass scans a share of the tiles for the plane's
-//      leftover query blocks and writes partials.
+//      tails each workgroup of a plane also takes the plane's leftover query
+//      blocks over a share of the tiles and writes partials: in the first
+//      pass, on the wavefronts that do not decode, for one or two leftover
+//      blocks; in a second pass over the share for three or four.
 //   3. chunk_tail_merge (split tails only): the leftover blocks' partials
 //      merged, 1/l and R_v^T.
 // The cached window is never written out: each query tile reads its packed
