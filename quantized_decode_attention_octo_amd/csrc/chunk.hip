@@ -1279,11 +1279,22 @@ __global__ __launch_bounds__(256) void chunk_tail_merge_kernel(ChunkArgs a, int 
   if (M != -INFINITY) {                // the same in every lane
     const float f = mlL.x == -INFINITY ? 0.0f : exp2f(mlL.x - M);
     lsum = wave_sum(f * mlL.y);
-    for (int k = 0; k < parts; ++k) {
-      const float fk = __shfl(f, k, 64);
-      const float* o = a.tail_o + ((r0 + k) * kQB + row) * kHeadDim;
-      x0 = fmaf(fk, o[c0], x0);
-      x1 = fmaf(fk, o[c1], x1);
+    // eight partials' loads in flight at a time (a partial past the last
+    // reads the last one again and is weighted by zero)
+    for (int k0 = 0; k0 < parts; k0 += 8) {
+      float v0[8], v1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* o = a.tail_o + ((r0 + min(k0 + u, parts - 1)) * kQB + row) * kHeadDim;
+        v0[u] = o[c0];
+        v1[u] = o[c1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float fk = k0 + u < parts ? __shfl(f, k0 + u, 64) : 0.0f;
+        x0 = fmaf(fk, v0[u], x0);
+        x1 = fmaf(fk, v1[u], x1);
+      }
     }
   }
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
