@@ -101,17 +101,22 @@ def test_chunk_full_size_sampled():
     assert err <= ATOL
 
 
+# leftover blocks a plane r = bpp mod 8: 1, 2, 1 (one tile in all, so that
+# shares and their halves are empty), 1, 2 (taken in the first pass), then 3
+# and 4 (a second pass over each workgroup's share)
 @pytest.mark.parametrize("B,Hq,Hkv,Tq,cached,tc", [(1, 2, 2, 544, 300, 544), (1, 4, 2, 280, 200, 280),
                                                     (1, 2, 2, 544, 0, 32), (1, 1, 1, 1300, 700, 1300),
-                                                    (2, 4, 2, 280, 150, 200)])
+                                                    (2, 4, 2, 280, 150, 200), (1, 2, 2, 608, 300, 300),
+                                                    (1, 2, 2, 640, 250, 100)])
 def test_chunk_split_tails(B, Hq, Hkv, Tq, cached, tc):
     """Planes of 8 upp + r query blocks with upp >= 2 and r = 1..4 leftover
     blocks: each of a plane's upp workgroups takes 8 whole blocks and a share
     of the tiles for the leftover ones, whose partials a second launch
     merges.  17 blocks a plane (r = 1), 2 x 9 blocks of a GQA plane (r = 2,
     the last block ragged), one tile for two workgroups (the second's share
-    empty), 41 blocks (upp = 5) over a ragged window, and two sequences of
-    GQA planes (the planes' blocks and partials indexed across the batch)."""
+    empty), 41 blocks (upp = 5) over a ragged window, two sequences of GQA
+    planes (the planes' blocks and partials indexed across the batch), and 19
+    and 20 blocks a plane (r = 3 and 4, which take a second pass)."""
     w = workload("chunk", B=B, Hq=Hq, Hkv=Hkv, T=max(cached, 64), chunk_q=Tq)
     err, _ = run_chunk(w, cached=cached, tc=tc)
     say(f"chunk split tails B={B} Hq={Hq} Hkv={Hkv} Tq={Tq} cached {cached} current {tc} err {err:.3e}")
