@@ -204,19 +204,26 @@ def test_group_chunk(group, cached, tc):
     assert err <= ATOL
 
 
-@pytest.mark.parametrize("kbits,kgroup,vbits,vgroup,correction,cached,tc", [
-    (2, 32, 2, 32, False, None, None),
-    (2, 32, 2, 32, True, None, None),
-    (3, 16, 3, 16, True, 57, None),
-    (4, 32, 2, 16, True, None, 0),
-    (2, 16, 2, 32, True, 0, None),
+@pytest.mark.parametrize("kbits,kgroup,vbits,vgroup,correction,cached,tc,hq,hkv,tq", [
+    (2, 32, 2, 32, False, None, None, 4, 2, 150),
+    (2, 32, 2, 32, True, None, None, 4, 2, 150),
+    (3, 16, 3, 16, True, 57, None, 4, 2, 150),
+    (4, 32, 2, 16, True, None, 0, 4, 2, 150),
+    (2, 16, 2, 32, True, 0, None, 4, 2, 150),
+    # split tails with the correction: r = 2 and 1 leftover blocks a plane
+    # (taken in the first pass, their query features in their own rows) and
+    # r = 3 (a second pass)
+    (2, 32, 2, 32, True, None, None, 4, 2, 280),
+    (2, 32, 2, 32, True, None, None, 2, 2, 544),
+    (2, 32, 2, 32, True, None, None, 2, 2, 608),
 ])
-def test_group_keys_chunk_and_jensen_correction(kbits, kgroup, vbits, vgroup, correction, cached, tc):
+def test_group_keys_chunk_and_jensen_correction(kbits, kgroup, vbits, vgroup, correction, cached, tc,
+                                                hq, hkv, tq):
     """Group-codec keys in the chunk path ("Quantized Keys Steal Attention"
     setting: group-wise round-to-nearest keys and values), with and without
     the Jensen-bias correction of cached logits (Eq. 15, its appendix on the
     rotation), against the oracle on the GPU-written caches."""
-    w = workload("chunk", Hq=4, Hkv=2, T=300, chunk_q=150)
+    w = workload("chunk", Hq=hq, Hkv=hkv, T=300, chunk_q=tq)
     inp = make_inputs(w)
     kc, hk = group_codecs(kbits, kgroup, seed=3)
     vc, hv = group_codecs(vbits, vgroup, seed=4)
