@@ -337,11 +337,11 @@ octo_status octo_chunk_workspace_bytes(const octo_codec_desc* k_codec, int32_t B
  * bias is one more MFMA k-slice per 16 keys, the product of fp16 query
  * features -16 log2(e) tau^2/24 ||(R q)_j||^2 and key features Delta_j^2/16,
  * so it shares the fp16 range limits below).  Operand range and precision:
- * the fp16 operands require |rotated entries| < 65504 (for cached values,
- * gamma rho^ < 65504) and round each operand to 11 significant bits, so this
+ * the fp16 operands require |rotated entries| < 65504 (for cached keys and
+ * values, gamma rho^ < 65504) and round each operand to 11 significant bits, so this
  * path is meant for inputs without large outlier channels (the decode path
  * computes in fp32).  Tq == 0 is a no-op; an empty window gives zero output
- * rows.  A plane whose current value rows (Tc rounded up to 32, times 288
+ * rows.  A plane whose current value rows (Tc rounded up to 32, times 256
  * bytes) or packed records (capacity times record bytes) exceed 2 GiB
  * returns OCTO_ERR_UNSUPPORTED.                                            */
 octo_status octo_attend_chunk(const octo_codec_desc* k_codec, const octo_codec_desc* v_codec,

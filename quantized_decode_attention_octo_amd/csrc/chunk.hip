@@ -213,7 +213,8 @@ constexpr int kKTileInsts = kBN * kKChunks / 64;    // 64-lane direct loads of a
 // four rows one transposing read serves at a time start 8 banks apart.
 // The current values come in rows of the same length.
 constexpr int kVRowBytes = 288;
-constexpr int kVRowHalves = kVRowBytes / 2;
+constexpr int kVRowChunks = kVRowBytes / 16;
+constexpr int kVSrcBytes = kHeadDim * 2;   // a value row in the workspace (unpadded)
 constexpr int kVTileBytes = kBN * kVRowBytes;
 constexpr int kVTileChunks = kVTileBytes / 16;
 constexpr int kVTileInsts = kVTileChunks / 64;      // 64-lane direct loads of a value tile
@@ -276,7 +277,7 @@ struct ChunkArgs {
   float feat_c;          // Jensen-bias correction: query feature factor
   int feat_gs;           // ... and group size
   const _Float16* kc;    // current keys [B][Hkv][Tc_pad][128] rotated
-  const _Float16* vc;    // current values [B][Hkv][Tc_pad][kVRowHalves] rotated
+  const _Float16* vc;    // current values [B][Hkv][Tc_pad][128] rotated
   float* out;            // [B][Hq][Tq][128]
   int Hq, Hkv, Tq;
   // 32-query blocks: qb a (batch, query head), n_blocks in all, in (batch,
@@ -817,8 +818,8 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
       const_cast<_Float16*>(a.kc + dplane * a.Tc_pad * kHeadDim), (short)0,
       a.Tc_pad * kHeadDim * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<_Float16*>(a.vc + dplane * a.Tc_pad * kVRowHalves), (short)0,
-      a.Tc_pad * kVRowBytes, kBufferWord3);
+      const_cast<_Float16*>(a.vc + dplane * a.Tc_pad * kHeadDim), (short)0,
+      a.Tc_pad * kVSrcBytes, kBufferWord3);
 
   const int n_ct = (a.cached + kBN - 1) / kBN, n_rt = (a.Tc + kBN - 1) / kBN;
   const int n_tiles = n_ct + n_rt;
@@ -914,13 +915,18 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_attn_kernel(ChunkArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, ks + 1024 * j, 16, (kr * kHeadDim + kc * 8) * 2,
                                                kt0 * kHeadDim * 2, 0, 0);
     }
-    // value tile: the padded rows as they are, chunk p = 64 j + L
+    // value tile: stored chunk p = 64 j + L is chunk p mod 18 of padded row
+    // p / 18, the 16 bytes at 16 (p mod 18) of that row (256 bytes in the
+    // workspace) for the first 16 chunks of a row; the two pad chunks read
+    // nothing
 #pragma unroll
     for (int i = 0; i < (kVTileInsts + 3) / 4; ++i) {
       const int j = 4 * i + lw;
+      const uint32_t p = 64 * j + lx, vr = p / kVRowChunks, vcn = p % kVRowChunks;
       if (j < kVTileInsts)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vs + 1024 * j, 16, (64 * j + lx) * 16,
-                                                 kt0 * kVRowBytes, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vs + 1024 * j, 16,
+                                                 vcn < 16 ? vr * kVSrcBytes + 16 * vcn : kOutOfRange,
+                                                 kt0 * kVSrcBytes, 0, 0);
     }
   };
   // per-lane offsets of the key fragments of slice s (row col, logical chunk
@@ -1314,8 +1320,8 @@ struct ChunkPlan {
 };
 
 // The blocks of a call and their workgroups; the workspace: the current
-// chunk's rotated key rows and value rows (padded to whole tiles; value rows
-// of kVRowHalves), which every workgroup of a plane reads, and the split
+// chunk's rotated key rows and value rows (padded to whole tiles), which
+// every workgroup of a plane reads, and the split
 // tails' partials.  The queries are rotated inside the attention kernel, and
 // nothing of the cached window is staged.  Split tails are taken when a
 // plane has at least two workgroups of whole blocks and one to four blocks
@@ -1339,7 +1345,7 @@ ChunkPlan chunk_plan(int B, int Hq, int Hkv, int Tq, int Tc, bool corr) {
   p.k_off = 0;
   const size_t kv = (size_t)B * Hkv * p.Tc_pad * row;
   p.v_off = p.k_off + up(kv);
-  p.to_off = p.v_off + up((size_t)B * Hkv * p.Tc_pad * kVRowBytes);
+  p.to_off = p.v_off + up(kv);
   const size_t tail_rows = p.tail ? (size_t)B * Hkv * p.tail_r * p.upp * p.nsub * kQB : 0;
   p.tml_off = p.to_off + up(tail_rows * kHeadDim * sizeof(float));
   p.total = std::max<size_t>(p.tml_off + up(tail_rows * sizeof(float2)), 256);
@@ -1452,7 +1458,7 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   const ChunkPlan p = chunk_plan(B, num_q_heads, Hkv, Tq, Tc, corr);
   // buffer descriptors address a plane's current rows and packed streams
   // with 32-bit byte ranges
-  if ((int64_t)p.Tc_pad * kVRowBytes > INT32_MAX ||
+  if ((int64_t)p.Tc_pad * kVSrcBytes > INT32_MAX ||
       (int64_t)k_cache->capacity * std::max(kc.w_idx, vc.w_idx) * 4 > INT32_MAX)
     return fail(OCTO_ERR_UNSUPPORTED, "%s: a plane's rows or packed streams exceed 2 GiB", what);
   if (!workspace || workspace_bytes < p.total)
@@ -1478,7 +1484,7 @@ extern "C" octo_status octo_attend_chunk(const octo_codec_desc* k_codec,
   const int cur_tiles = (p.Tc_pad + 63) / 64;
   RotJob jk{static_cast<const uint16_t*>(k_cur), Tc, p.Tc_pad, kc.seed, kr, p.Tc_pad, kHeadDim,
             cur_tiles, planes_kv, kperm};
-  RotJob jv{static_cast<const uint16_t*>(v_cur), Tc, p.Tc_pad, vc.seed, vr, p.Tc_pad, kVRowHalves,
+  RotJob jv{static_cast<const uint16_t*>(v_cur), Tc, p.Tc_pad, vc.seed, vr, p.Tc_pad, kHeadDim,
             cur_tiles, planes_kv, vperm};
   const long rot_blocks = Tc > 0 ? (long)cur_tiles * planes_kv * 2 : 0;
   if (rot_blocks > 0)

@@ -231,9 +231,9 @@ def test_chunk_errors(L):
     assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 128, 64, 0, ctypes.byref(n)) == 0
     need = n.value
     # the current chunk's rotated key rows [1, 2, 64, 128] and value rows
-    # [1, 2, 64, 144] (padded rows); the queries are rotated and the cached
-    # window decoded inside the kernel
-    assert need == 2 * 64 * 256 + 2 * 64 * 288
+    # [1, 2, 64, 128]; the queries are rotated and the cached window decoded
+    # inside the kernel
+    assert need == 2 * 64 * 256 + 2 * 64 * 256
     # the same with 128 cached tokens more: nothing of the window is staged
     assert L.octo_chunk_workspace_bytes(ctypes.byref(kd), 1, 2, 2, 64, 256, 64, 0, ctypes.byref(n)) == 0
     assert n.value == need
